@@ -1,0 +1,147 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/mtb.h declares, and rejects bad arguments before
+launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from transformer_layer_ln_amd import mtb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mtb.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"typedef[^;]*;", "", text)   # types, incl. function-pointer typedefs
+    return sorted(set(re.findall(r"\b(mtb_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = mtb.load()
+    decl = declared_functions()
+    assert set(decl) == set(mtb.EXPORTS), decl
+    for name in decl:
+        assert hasattr(lib, name), name
+
+
+def _cfg(**kw):
+    base = dict(batch=2, seq=128, hidden=256, q_heads=4, kv_heads=2, head_dim=64, ffn=512,
+                act="gelu", causal=False, dtype="bf16")
+    base.update(kw)
+    return mtb.make_cfg(**base)
+
+
+def test_size_queries_accept_valid_and_reject_invalid_configs():
+    assert mtb.saved_bytes(_cfg()) > 0
+    assert mtb.scratch_bytes(_cfg()) > 0
+    assert mtb.saved_bytes(_cfg(head_dim=32)) == 0          # bf16 needs d in {64, 128}
+    assert "head_dim" in mtb.last_error()
+    assert mtb.saved_bytes(_cfg(q_heads=3, kv_heads=2)) == 0
+    assert mtb.saved_bytes(_cfg(seq=100)) == 0
+    assert mtb.saved_bytes(_cfg(act="swiglu", ffn=520)) == 0
+    assert mtb.saved_bytes(_cfg(dtype="f32", head_dim=32, seq=100)) > 0   # fp32 path: any seq
+
+
+def test_saved_bytes_scale_with_tokens():
+    a = mtb.saved_bytes(_cfg(batch=1))
+    b = mtb.saved_bytes(_cfg(batch=4))
+    assert 3.5 * a < b < 4.5 * a
+
+
+class _FakePtr:
+    """Stands in for a tensor: only data_ptr() is used for argument checks."""
+
+    def __init__(self, p):
+        self.p = p
+
+    def data_ptr(self):
+        return self.p
+
+
+def _weights(p=0x10000):
+    return {k: _FakePtr(p + 0x1000 * i) for i, k in enumerate(("w_qkv", "w_o", "w_fc1", "w_fc2"))}
+
+
+def _status(fn, *args):
+    try:
+        fn(*args)
+    except mtb.MtbError as e:
+        return e.status, str(e)
+    return mtb.MTB_OK, ""
+
+
+class _S:
+    cuda_stream = None
+
+
+def test_block_calls_reject_bad_arguments_before_launch():
+    c = _cfg()
+    w = _weights()
+    buf = _FakePtr(0x100000)
+    st, msg = _status(mtb.block_fwd, c, w, mtb.PHASE_ALL, None, None, buf, buf, buf, None, _S())
+    assert st == mtb.MTB_EINVAL and "x is NULL" in msg
+    st, msg = _status(mtb.block_fwd, c, w, 7, buf, None, _FakePtr(0x200000), buf, buf, None, _S())
+    assert st == mtb.MTB_EINVAL and "phase" in msg
+    st, msg = _status(mtb.block_fwd, c, w, mtb.PHASE_ALL, _FakePtr(0x100004), None,
+                      _FakePtr(0x200000), buf, buf, None, _S())
+    assert st == mtb.MTB_EINVAL and "aligned" in msg
+    st, msg = _status(mtb.block_fwd, c, w, mtb.PHASE_SEG1, buf, None, _FakePtr(0x200000),
+                      _FakePtr(0x300000), _FakePtr(0x400000), None, _S())
+    assert st == mtb.MTB_EINVAL and "reduced_in" in msg
+    st, msg = _status(mtb.block_fwd, c, w, mtb.PHASE_ALL, buf, None, buf, _FakePtr(0x300000),
+                      _FakePtr(0x400000), None, _S())
+    assert st == mtb.MTB_EINVAL and "alias" in msg
+    w2 = dict(w)
+    w2["ln1_g"] = _FakePtr(0x500000)
+    st, msg = _status(mtb.block_fwd, c, w2, mtb.PHASE_ALL, buf, None, _FakePtr(0x200000),
+                      _FakePtr(0x300000), _FakePtr(0x400000), None, _S())
+    assert st == mtb.MTB_EINVAL and "together" in msg
+    st, msg = _status(mtb.block_fwd, _cfg(head_dim=96), w, mtb.PHASE_ALL, buf, None,
+                      _FakePtr(0x200000), _FakePtr(0x300000), _FakePtr(0x400000), None, _S())
+    assert st == mtb.MTB_EUNSUPPORTED
+    # a gradient for a weight that is absent
+    st, msg = _status(mtb.block_bwd, c, w, mtb.PHASE_ALL, buf, _FakePtr(0x300000), _FakePtr(0x600000),
+                      None, _FakePtr(0x200000), {"b_o": _FakePtr(0x700000)}, _FakePtr(0x400000),
+                      None, _S())
+    assert st == mtb.MTB_EINVAL and "absent" in msg
+
+
+def test_xent_rejects_bad_arguments_before_launch():
+    p = _FakePtr(0x100000)
+    st, msg = _status(mtb.vocab_xent, 0, 16, 0, mtb.BF16, mtb.XENT_PARTIAL, p, p, p, None, None,
+                      None, None, _S())
+    assert st == mtb.MTB_EINVAL
+    st, msg = _status(mtb.vocab_xent, 8, 16, 0, mtb.BF16, mtb.XENT_FINISH, p, p, p, None, None,
+                      _FakePtr(0x200000), None, _S())
+    assert st == mtb.MTB_EINVAL and "dloss" in msg
+    st, msg = _status(mtb.vocab_xent, 8, 16, 0, 5, mtb.XENT_PARTIAL, p, p, p, None, None, None,
+                      None, _S())
+    assert st == mtb.MTB_EINVAL and "dtype" in msg
+    st, msg = _status(mtb.vocab_xent_combine, 8, 0, p, p, None, _S())
+    assert st == mtb.MTB_EINVAL
+
+
+def test_struct_layout_matches_header():
+    # 10 int32 fields + 1 float
+    assert ctypes.sizeof(mtb.Cfg) == 44
+    assert ctypes.sizeof(mtb.Weights) == 12 * ctypes.sizeof(ctypes.c_void_p)
+    assert ctypes.sizeof(mtb.Comm) == 2 * ctypes.sizeof(ctypes.c_void_p)
+
+
+def test_product_path_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "transformer_layer_ln_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(from|import)\s+oracle\b", text, re.M), f
+                assert "oracle/" not in text, f
+    bench = open(os.path.join(ROOT, "bench.py")).read() if os.path.exists(os.path.join(ROOT, "bench.py")) else ""
+    # bench may use the oracle only inside its CPU-baseline leg
+    for line in bench.splitlines():
+        if re.match(r"^(from|import)\s+oracle", line):
+            pytest.fail("bench.py imports the oracle at module level")

@@ -1,0 +1,98 @@
+"""GPU parity of the block forward + backward (through the C ABI) against the
+fp64 oracle on identical seeded inputs.
+
+Tolerance (per output tensor, max |gpu - ref| / max |ref|): 2e-2 for bf16,
+1e-4 for fp32. The cotangent is a seeded N(0,1) tensor G (a row-constant
+cotangent such as mean(out)'s would leave part of the LayerNorm backward
+unexercised), plus one run with the listing's own loss = mean(out).
+"""
+import numpy as np
+import pytest
+
+from gpu_util import TOL, check_rank_vs_oracle, host, rel_err, run_rank, say, tdtype
+from oracle import block as ob
+from transformer_layer_ln_amd import inputs, mtb
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(cfg):
+    a = inputs.activations(cfg)
+    return inputs.shard_weights(cfg, 0), a["x"], a["g"]
+
+
+def test_c1_fp32_full_block():
+    cfg = inputs.C1
+    w, x, G = _case(cfg)
+    check_rank_vs_oracle(cfg, w, x, G)
+
+
+def test_c1_fp32_mean_loss():
+    """The listing's loss: out.mean(), cotangent 1/numel."""
+    cfg = inputs.C1
+    w, x, _ = _case(cfg)
+    G = np.full_like(x, 1.0 / x.size)
+    check_rank_vs_oracle(cfg, w, x, G, label="C1 mean(out)")
+
+
+@pytest.mark.parametrize("variant", [
+    dict(causal=True),
+    dict(act="swiglu", ffn=256, kv_heads=2),
+    dict(act="swiglu", ffn=256, kv_heads=1, causal=True, affine=True, bias=True),
+    dict(affine=True, bias=True, seq=40, head_dim=64, q_heads=2, kv_heads=2),
+])
+def test_fp32_variants(variant):
+    cfg = inputs.C1.with_(name="fp32-variant", **variant)
+    w, x, G = _case(cfg)
+    check_rank_vs_oracle(cfg, w, x, G)
+
+
+# bf16: shapes with ragged tails against the 128-wide GEMM tiles and the
+# 128-query attention tiles (seq 192, hidden 192/320, ffn 320, 3 heads)
+BF16_SMALL = [
+    dict(batch=3, seq=192, hidden=192, q_heads=2, kv_heads=2, head_dim=64, ffn=320),
+    dict(batch=2, seq=192, hidden=320, q_heads=3, kv_heads=1, head_dim=64, ffn=192, causal=True,
+         act="swiglu", affine=True, bias=True),
+    dict(batch=2, seq=256, hidden=256, q_heads=2, kv_heads=2, head_dim=128, ffn=384, causal=True),
+    dict(batch=1, seq=320, hidden=256, q_heads=4, kv_heads=2, head_dim=128, ffn=256, act="swiglu",
+         bias=True),
+    dict(batch=2, seq=64, hidden=128, q_heads=1, kv_heads=1, head_dim=64, ffn=64, causal=True),
+]
+
+
+@pytest.mark.parametrize("i", range(len(BF16_SMALL)))
+def test_bf16_small_shapes(i):
+    cfg = inputs.BlockConfig(f"bf16-small-{i}", dtype="bf16", tp=1, seed=2000 + i, **BF16_SMALL[i])
+    w, x, G = _case(cfg)
+    check_rank_vs_oracle(cfg, w, x, G)
+
+
+def test_c2_rank_share():
+    cfg = inputs.C2
+    w, x, G = _case(cfg)
+    check_rank_vs_oracle(cfg, w, x, G)
+
+
+def test_c4_rank_share_full_size():
+    """The seq-2048 causal TP=8 rank share at its full size, whole tensors."""
+    cfg = inputs.C4
+    w, x, G = _case(cfg)
+    check_rank_vs_oracle(cfg, w, x, G)
+
+
+def test_c5_swiglu_gqa_rank_share_full_size():
+    cfg = inputs.C5
+    w, x, G = _case(cfg)
+    check_rank_vs_oracle(cfg, w, x, G)
+
+
+def test_gpu_results_are_deterministic():
+    cfg = inputs.BlockConfig("det", batch=2, seq=256, hidden=256, q_heads=4, kv_heads=1, head_dim=64,
+                             ffn=256, act="swiglu", causal=True, seed=2100)
+    w, x, G = _case(cfg)
+    say("[gpu] determinism", cfg)
+    r1 = run_rank(cfg, w, x, G)
+    r2 = run_rank(cfg, w, x, G)
+    assert np.array_equal(r1[0], r2[0]) and np.array_equal(r1[1], r2[1])
+    for k in r1[2]:
+        assert np.array_equal(r1[2][k], r2[2][k]), k

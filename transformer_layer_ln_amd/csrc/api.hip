@@ -1,0 +1,496 @@
+// libmtb C ABI: argument validation, the layout of the caller-provided
+// `saved` / `scratch` buffers, and the order of kernel launches for the
+// forward and backward pass of one tensor-parallel rank's share of the block.
+//
+// Block structure: [Lab06] sec. 2 listing steps (2)-(8) in its pre-LN order;
+// sharding and the reduction points: [TP-block] sec. 1-2 (column-parallel
+// QKV and fc1, row-parallel projection and fc2, two all-reduces forward and
+// two backward); vocab-parallel cross-entropy: [TP-block] sec. 4.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "kernels.h"
+#include "mtb.h"
+
+using namespace mtb;
+
+namespace {
+
+thread_local std::string g_err;
+
+mtb_status fail(mtb_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+#define MTB_HIP(call)                                                                       \
+  do {                                                                                      \
+    hipError_t e_ = (call);                                                                 \
+    if (e_ != hipSuccess)                                                                   \
+      return fail(MTB_EHIP, "%s failed: %s", #call, hipGetErrorString(e_));                 \
+  } while (0)
+
+struct Dims {
+  int64_t B, S, H, nq, nkv, d, F, Fu, Nqkv, T, NO;
+  int64_t es;  // element size
+  int dt;      // MTB_F32 / MTB_BF16
+  int act, causal;
+  float eps;
+};
+
+mtb_status check_cfg(const mtb_cfg* c, Dims& d) {
+  if (!c) return fail(MTB_EINVAL, "cfg is NULL");
+  if (c->batch <= 0 || c->seq <= 0 || c->hidden <= 0 || c->q_heads <= 0 || c->kv_heads <= 0 ||
+      c->head_dim <= 0 || c->ffn <= 0)
+    return fail(MTB_EINVAL, "cfg sizes must be positive");
+  if (c->q_heads % c->kv_heads)
+    return fail(MTB_EINVAL, "q_heads (%d) must be a multiple of kv_heads (%d)", c->q_heads,
+                c->kv_heads);
+  if (c->act != MTB_ACT_GELU && c->act != MTB_ACT_SWIGLU)
+    return fail(MTB_EINVAL, "act must be MTB_ACT_GELU or MTB_ACT_SWIGLU");
+  if (c->causal != 0 && c->causal != 1) return fail(MTB_EINVAL, "causal must be 0 or 1");
+  if (c->dtype != MTB_F32 && c->dtype != MTB_BF16) return fail(MTB_EINVAL, "bad dtype %d", c->dtype);
+  if (!(c->ln_eps > 0.f) || c->ln_eps > 1.f) return fail(MTB_EINVAL, "ln_eps must be in (0, 1]");
+  d.B = c->batch; d.S = c->seq; d.H = c->hidden; d.nq = c->q_heads; d.nkv = c->kv_heads;
+  d.d = c->head_dim; d.F = c->ffn; d.act = c->act; d.causal = c->causal; d.dt = c->dtype;
+  d.eps = c->ln_eps;
+  d.Fu = d.act == MTB_ACT_SWIGLU ? 2 * d.F : d.F;
+  d.Nqkv = (d.nq + 2 * d.nkv) * d.d;
+  d.T = d.B * d.S;
+  d.NO = d.nq * d.d;
+  d.es = d.dt == MTB_BF16 ? 2 : 4;
+  if (d.T > (1 << 30) || d.H > 8192 || d.Nqkv > (1 << 20) || d.Fu > (1 << 24))
+    return fail(MTB_EUNSUPPORTED, "sizes beyond this build's limits (T <= 2^30, hidden <= 8192)");
+  if (d.act == MTB_ACT_SWIGLU && d.F % 16)
+    return fail(MTB_EUNSUPPORTED, "SwiGLU needs ffn %% 16 == 0 (gate/up interleave of 16)");
+  if (d.dt == MTB_BF16) {
+    if (d.d != 64 && d.d != 128)
+      return fail(MTB_EUNSUPPORTED, "bf16 path supports head_dim 64 or 128, got %d", c->head_dim);
+    if (d.S % 64 || d.H % 64 || d.F % 64 || d.NO % 64)
+      return fail(MTB_EUNSUPPORTED,
+                  "bf16 path needs seq, hidden, ffn and q_heads*head_dim multiples of 64");
+  } else {
+    if (d.d != 32 && d.d != 64 && d.d != 128)
+      return fail(MTB_EUNSUPPORTED, "fp32 path supports head_dim 32, 64 or 128, got %d",
+                  c->head_dim);
+    if (d.H % 8 || d.F % 8) return fail(MTB_EUNSUPPORTED, "fp32 path needs hidden, ffn %% 8 == 0");
+  }
+  return MTB_OK;
+}
+
+size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Saved {
+  size_t a, mu1, rs1, qkv, qkvT, O, lse, h, mu2, rs2, c, u, m, total;
+};
+Saved saved_layout(const Dims& d) {
+  Saved s;
+  size_t o = 0;
+  const size_t e = d.es, T = d.T;
+  s.a = o; o += al(T * d.H * e);
+  s.mu1 = o; o += al(T * 4);
+  s.rs1 = o; o += al(T * 4);
+  s.qkv = o; o += al(T * d.Nqkv * e);
+  s.qkvT = o; o += d.dt == MTB_BF16 ? al(T * d.Nqkv * e) : 0;
+  s.O = o; o += al(T * d.NO * e);
+  s.lse = o; o += al((size_t)d.B * d.nq * d.S * 4);
+  s.h = o; o += al(T * d.H * e);
+  s.mu2 = o; o += al(T * 4);
+  s.rs2 = o; o += al(T * 4);
+  s.c = o; o += al(T * d.H * e);
+  s.u = o; o += al(T * d.Fu * e);
+  s.m = o; o += al(T * d.F * e);
+  s.total = o;
+  return s;
+}
+
+struct Scratch {
+  size_t dh, p, du, dm, dO, dOT, Dbuf, dqkv, part, red, total;
+};
+Scratch scratch_layout(const Dims& d) {
+  Scratch s;
+  size_t o = 0;
+  const size_t e = d.es, T = d.T;
+  s.dh = o; o += al(T * d.H * e);       // persists from backward SEG1 to SEG2
+  s.p = o; o += al(T * d.H * e);        // partial sums (p_attn, p_mlp, dc, da)
+  s.du = o; o += al(T * d.Fu * e);
+  s.dm = o; o += d.dt == MTB_F32 ? al(T * d.F * e) : 0;
+  s.dO = o; o += al(T * d.NO * e);
+  s.dOT = o; o += d.dt == MTB_BF16 ? al(T * d.NO * e) : 0;
+  s.Dbuf = o; o += al((size_t)d.B * d.nq * d.S * 4);
+  s.dqkv = o; o += al(T * d.Nqkv * e);
+  s.part = o; o += (d.dt == MTB_BF16 && d.nq != d.nkv) ? al((size_t)d.B * d.nq * d.S * 2 * d.d * 4) : 0;
+  int64_t nmax = d.H > d.Fu ? d.H : d.Fu;
+  if (d.Nqkv > nmax) nmax = d.Nqkv;
+  s.red = o; o += al((size_t)colsum_splits((int)d.T) * nmax * 4);
+  s.total = o;
+  return s;
+}
+
+bool misaligned(const void* p) { return ((uintptr_t)p & 15) != 0; }
+
+#define MTB_REQ(p, name)                                                             \
+  do {                                                                               \
+    if (!(p)) return fail(MTB_EINVAL, "%s is NULL", name);                           \
+    if (misaligned(p)) return fail(MTB_EINVAL, "%s is not 16-byte aligned", name);   \
+  } while (0)
+#define MTB_OPT(p, name)                                                             \
+  do {                                                                               \
+    if ((p) && misaligned(p)) return fail(MTB_EINVAL, "%s is not 16-byte aligned", name); \
+  } while (0)
+
+mtb_status check_weights(const mtb_weights* w) {
+  if (!w) return fail(MTB_EINVAL, "weights is NULL");
+  MTB_REQ(w->w_qkv, "w_qkv");
+  MTB_REQ(w->w_o, "w_o");
+  MTB_REQ(w->w_fc1, "w_fc1");
+  MTB_REQ(w->w_fc2, "w_fc2");
+  MTB_OPT(w->b_qkv, "b_qkv"); MTB_OPT(w->b_o, "b_o"); MTB_OPT(w->b_fc1, "b_fc1");
+  MTB_OPT(w->b_fc2, "b_fc2"); MTB_OPT(w->ln1_g, "ln1_g"); MTB_OPT(w->ln1_b, "ln1_b");
+  MTB_OPT(w->ln2_g, "ln2_g"); MTB_OPT(w->ln2_b, "ln2_b");
+  if ((!w->ln1_g) != (!w->ln1_b) || (!w->ln2_g) != (!w->ln2_b))
+    return fail(MTB_EINVAL, "LayerNorm gain and shift must be given together");
+  return MTB_OK;
+}
+
+mtb_status call_hook(const mtb_comm* comm, void* buf, int64_t count, int dt, int op, hipStream_t st) {
+  if (!comm || !comm->allreduce) return MTB_OK;
+  const mtb_status s = comm->allreduce(buf, count, dt, op, (void*)st, comm->user);
+  if (s != MTB_OK) return fail(MTB_ECOMM, "reduction hook returned %d", (int)s);
+  return MTB_OK;
+}
+
+char* P(void* base, size_t off) { return (char*)base + off; }
+
+// benchmark trace (see mtb_trace_arm)
+struct Trace {
+  int what = MTB_TRACE_NONE;
+  void* const* b = nullptr;
+  void* const* e = nullptr;
+  int n = 0, i = 0;
+};
+Trace g_trace;
+
+void trace_begin(int what, hipStream_t st) {
+  if (g_trace.what == what && g_trace.i < g_trace.n) hipEventRecord((hipEvent_t)g_trace.b[g_trace.i], st);
+}
+void trace_end(int what, hipStream_t st) {
+  if (g_trace.what == what && g_trace.i < g_trace.n) hipEventRecord((hipEvent_t)g_trace.e[g_trace.i++], st);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mtb_last_error(void) { return g_err.c_str(); }
+
+mtb_status mtb_trace_arm(int32_t what, void* const* begin_events, void* const* end_events, int32_t n) {
+  if (what < MTB_TRACE_NONE || what > MTB_TRACE_FC2_WGRAD || n < 0)
+    return fail(MTB_EINVAL, "bad trace request");
+  if (n > 0 && (!begin_events || !end_events)) return fail(MTB_EINVAL, "trace events are NULL");
+  g_trace.what = what;
+  g_trace.b = begin_events;
+  g_trace.e = end_events;
+  g_trace.n = n;
+  g_trace.i = 0;
+  return MTB_OK;
+}
+
+int32_t mtb_trace_disarm(void) {
+  const int32_t k = g_trace.i;
+  g_trace = Trace();
+  return k;
+}
+
+size_t mtb_block_saved_bytes(const mtb_cfg* cfg) {
+  Dims d;
+  if (check_cfg(cfg, d) != MTB_OK) return 0;
+  return saved_layout(d).total;
+}
+
+size_t mtb_block_scratch_bytes(const mtb_cfg* cfg) {
+  Dims d;
+  if (check_cfg(cfg, d) != MTB_OK) return 0;
+  return scratch_layout(d).total;
+}
+
+mtb_status mtb_block_fwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase, const void* x,
+                         const void* reduced_in, void* out, void* saved, void* scratch,
+                         const mtb_comm* comm, void* hip_stream) {
+  Dims d;
+  mtb_status s = check_cfg(cfg, d);
+  if (s != MTB_OK) return s;
+  if (phase < MTB_PHASE_ALL || phase > MTB_PHASE_SEG2) return fail(MTB_EINVAL, "bad phase %d", phase);
+  if ((s = check_weights(w)) != MTB_OK) return s;
+  MTB_REQ(x, "x");
+  MTB_REQ(out, "out");
+  MTB_REQ(saved, "saved");
+  MTB_REQ(scratch, "scratch");
+  if (phase == MTB_PHASE_SEG1 || phase == MTB_PHASE_SEG2) MTB_REQ(reduced_in, "reduced_in");
+  if (out == x || out == reduced_in || out == saved || out == scratch)
+    return fail(MTB_EINVAL, "out may not alias an input or a work buffer");
+
+  hipStream_t st = (hipStream_t)hip_stream;
+  const Saved L = saved_layout(d);
+  const Scratch Z = scratch_layout(d);
+  const int dt = d.dt;
+  const int T = (int)d.T, H = (int)d.H, Nq = (int)d.Nqkv, NO = (int)d.NO, F = (int)d.F,
+            Fu = (int)d.Fu, S = (int)d.S;
+  const bool bf = dt == MTB_BF16;
+  const bool fused = phase == MTB_PHASE_ALL && !(comm && comm->allreduce);
+  void* a = P(saved, L.a); float* mu1 = (float*)P(saved, L.mu1); float* rs1 = (float*)P(saved, L.rs1);
+  void* qkv = P(saved, L.qkv); void* qkvT = bf ? P(saved, L.qkvT) : nullptr;
+  void* O = P(saved, L.O); float* lse = (float*)P(saved, L.lse);
+  void* h = P(saved, L.h); float* mu2 = (float*)P(saved, L.mu2); float* rs2 = (float*)P(saved, L.rs2);
+  void* c = P(saved, L.c); void* u = P(saved, L.u); void* m = P(saved, L.m);
+  void* p = P(scratch, Z.p);
+
+  if (phase == MTB_PHASE_ALL || phase == MTB_PHASE_SEG0) {
+    // (2) input LayerNorm
+    trace_begin(MTB_TRACE_LN1_FWD, st);
+    MTB_HIP(ln_fwd(dt, T, H, x, nullptr, nullptr, w->ln1_g, w->ln1_b, nullptr, a, mu1, rs1, d.eps, st));
+    trace_end(MTB_TRACE_LN1_FWD, st);
+    // column-parallel QKV; the bf16 path also keeps a per-batch transpose for attention
+    Epi e;
+    e.out = qkv; e.ldo = Nq; e.bias = w->b_qkv; e.outT = qkvT; e.S = S;
+    MTB_HIP(gemm(dt, T, Nq, H, a, H, true, w->w_qkv, H, true, e, st));
+    // per-head attention over the local heads
+    trace_begin(MTB_TRACE_ATTN_FWD, st);
+    MTB_HIP(attn_fwd(dt, (int)d.B, S, (int)d.nq, (int)d.nkv, (int)d.d, d.causal, qkv, qkvT, O, lse, st));
+    trace_end(MTB_TRACE_ATTN_FWD, st);
+    // row-parallel projection: a partial sum, reduced at g1
+    Epi ep;
+    if (fused) {  // identity reduction: fuse (4) residual and the bias
+      ep.out = h; ep.ldo = H; ep.bias = w->b_o; ep.resid = x; ep.ldr = H;
+    } else {
+      ep.out = phase == MTB_PHASE_SEG0 ? out : p; ep.ldo = H;
+    }
+    MTB_HIP(gemm(dt, T, H, NO, O, NO, true, w->w_o, NO, true, ep, st));
+    if (phase == MTB_PHASE_SEG0) return MTB_OK;
+    if (fused) {
+      MTB_HIP(ln_fwd(dt, T, H, h, nullptr, nullptr, w->ln2_g, w->ln2_b, nullptr, c, mu2, rs2, d.eps, st));
+    } else {
+      if ((s = call_hook(comm, p, d.T * d.H, dt, MTB_OP_SUM, st)) != MTB_OK) return s;
+      MTB_HIP(ln_fwd(dt, T, H, x, p, w->b_o, w->ln2_g, w->ln2_b, h, c, mu2, rs2, d.eps, st));
+    }
+  } else if (phase == MTB_PHASE_SEG1) {
+    // g1 done by the caller: h = x + sum(p_attn) + b_o, then (5) LN2
+    MTB_HIP(ln_fwd(dt, T, H, x, reduced_in, w->b_o, w->ln2_g, w->ln2_b, h, c, mu2, rs2, d.eps, st));
+  }
+
+  if (phase == MTB_PHASE_ALL || phase == MTB_PHASE_SEG1) {
+    // column-parallel fc1 + activation
+    if (bf) {
+      Epi e;
+      e.kind = d.act == MTB_ACT_GELU ? EPI_GELU : EPI_SWIGLU;
+      e.out = u; e.ldo = Fu; e.out2 = m; e.ldo2 = F; e.bias = w->b_fc1;
+      trace_begin(MTB_TRACE_FC1_FWD, st);
+      MTB_HIP(gemm(dt, T, Fu, H, c, H, true, w->w_fc1, H, true, e, st));
+      trace_end(MTB_TRACE_FC1_FWD, st);
+    } else {
+      Epi e;
+      e.out = u; e.ldo = Fu; e.bias = w->b_fc1;
+      MTB_HIP(gemm(dt, T, Fu, H, c, H, true, w->w_fc1, H, true, e, st));
+      MTB_HIP(act_fwd(dt, d.act, T, F, u, m, st));
+    }
+    // (6) row-parallel fc2: a partial sum, reduced at g2; (7) residual
+    Epi e;
+    if (fused) {
+      e.out = out; e.ldo = H; e.bias = w->b_fc2; e.resid = h; e.ldr = H;
+    } else {
+      e.out = phase == MTB_PHASE_SEG1 ? out : p; e.ldo = H;
+    }
+    MTB_HIP(gemm(dt, T, H, F, m, F, true, w->w_fc2, F, true, e, st));
+    if (fused || phase == MTB_PHASE_SEG1) return MTB_OK;
+    if ((s = call_hook(comm, p, d.T * d.H, dt, MTB_OP_SUM, st)) != MTB_OK) return s;
+    MTB_HIP(add3(dt, T, H, h, p, w->b_fc2, out, st));
+    return MTB_OK;
+  }
+  // SEG2: out = h + sum(p_mlp) + b2
+  MTB_HIP(add3(dt, T, H, h, reduced_in, w->b_fc2, out, st));
+  return MTB_OK;
+}
+
+mtb_status mtb_block_bwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase, const void* x,
+                         const void* saved, const void* dout, const void* reduced_in, void* dx,
+                         const mtb_grads* grads, void* scratch, const mtb_comm* comm,
+                         void* hip_stream) {
+  Dims d;
+  mtb_status s = check_cfg(cfg, d);
+  if (s != MTB_OK) return s;
+  if (phase < MTB_PHASE_ALL || phase > MTB_PHASE_SEG2) return fail(MTB_EINVAL, "bad phase %d", phase);
+  if ((s = check_weights(w)) != MTB_OK) return s;
+  MTB_REQ(x, "x");
+  MTB_REQ(saved, "saved");
+  MTB_REQ(dout, "dout");
+  MTB_REQ(dx, "dx");
+  MTB_REQ(scratch, "scratch");
+  if (phase == MTB_PHASE_SEG1 || phase == MTB_PHASE_SEG2) MTB_REQ(reduced_in, "reduced_in");
+  if (dx == x || dx == dout || dx == reduced_in || dx == saved || dx == scratch)
+    return fail(MTB_EINVAL, "dx may not alias an input or a work buffer");
+  mtb_grads g0 = {};
+  const mtb_grads& g = grads ? *grads : g0;
+  {
+    const void* gp[12] = {g.ln1_g, g.ln1_b, g.w_qkv, g.b_qkv, g.w_o, g.b_o,
+                          g.ln2_g, g.ln2_b, g.w_fc1, g.b_fc1, g.w_fc2, g.b_fc2};
+    const void* wp[12] = {w->ln1_g, w->ln1_b, w->w_qkv, w->b_qkv, w->w_o, w->b_o,
+                          w->ln2_g, w->ln2_b, w->w_fc1, w->b_fc1, w->w_fc2, w->b_fc2};
+    for (int i = 0; i < 12; ++i) {
+      if (gp[i] && misaligned(gp[i])) return fail(MTB_EINVAL, "gradient %d is not 16-byte aligned", i);
+      if (gp[i] && !wp[i]) return fail(MTB_EINVAL, "gradient %d requested for an absent weight", i);
+    }
+  }
+
+  hipStream_t st = (hipStream_t)hip_stream;
+  const Saved L = saved_layout(d);
+  const Scratch Z = scratch_layout(d);
+  const int dt = d.dt;
+  const int T = (int)d.T, H = (int)d.H, Nq = (int)d.Nqkv, NO = (int)d.NO, F = (int)d.F,
+            Fu = (int)d.Fu, S = (int)d.S;
+  const bool bf = dt == MTB_BF16;
+  char* sv = (char*)saved;
+  const void* a = sv + L.a; const float* mu1 = (const float*)(sv + L.mu1);
+  const float* rs1 = (const float*)(sv + L.rs1);
+  const void* qkv = sv + L.qkv; const void* qkvT = bf ? sv + L.qkvT : nullptr;
+  const void* O = sv + L.O; const float* lse = (const float*)(sv + L.lse);
+  const void* h = sv + L.h; const float* mu2 = (const float*)(sv + L.mu2);
+  const float* rs2 = (const float*)(sv + L.rs2);
+  const void* c = sv + L.c; const void* u = sv + L.u; const void* m = sv + L.m;
+  void* dh = P(scratch, Z.dh); void* p = P(scratch, Z.p); void* du = P(scratch, Z.du);
+  void* dm = P(scratch, Z.dm); void* dO = P(scratch, Z.dO); void* dOT = bf ? P(scratch, Z.dOT) : nullptr;
+  float* Dbuf = (float*)P(scratch, Z.Dbuf); void* dqkv = P(scratch, Z.dqkv);
+  float* part = (float*)P(scratch, Z.part); float* red = (float*)P(scratch, Z.red);
+  const void* G = dout;
+
+  if (phase == MTB_PHASE_ALL || phase == MTB_PHASE_SEG0) {
+    // fc2 backward: dm = G W2 with the activation's derivative fused (bf16)
+    if (bf) {
+      Epi e;
+      e.kind = d.act == MTB_ACT_GELU ? EPI_DGELU : EPI_DSWIGLU;
+      e.out = du; e.ldo = Fu; e.aux = u; e.ldaux = Fu;
+      MTB_HIP(gemm(dt, T, F, H, G, H, true, w->w_fc2, F, false, e, st));
+    } else {
+      Epi e;
+      e.out = dm; e.ldo = F;
+      MTB_HIP(gemm(dt, T, F, H, G, H, true, w->w_fc2, F, false, e, st));
+      MTB_HIP(act_bwd(dt, d.act, T, F, dm, u, du, st));
+    }
+    if (g.w_fc2) {
+      Epi e;
+      e.out = g.w_fc2; e.ldo = F;
+      trace_begin(MTB_TRACE_FC2_WGRAD, st);
+      MTB_HIP(gemm(dt, H, F, T, G, H, false, m, F, false, e, st));
+      trace_end(MTB_TRACE_FC2_WGRAD, st);
+    }
+    if (g.b_fc2) MTB_HIP(colsum(dt, T, H, G, H, nullptr, nullptr, nullptr, g.b_fc2, red, st));
+    if (g.w_fc1) {
+      Epi e;
+      e.out = g.w_fc1; e.ldo = H;
+      MTB_HIP(gemm(dt, Fu, H, T, du, Fu, false, c, H, false, e, st));
+    }
+    if (g.b_fc1) MTB_HIP(colsum(dt, T, Fu, du, Fu, nullptr, nullptr, nullptr, g.b_fc1, red, st));
+    // fc1 input gradient: partial over ranks, summed at f1
+    Epi e;
+    e.out = phase == MTB_PHASE_SEG0 ? dx : p; e.ldo = H;
+    MTB_HIP(gemm(dt, T, H, Fu, du, Fu, true, w->w_fc1, H, false, e, st));
+    if (phase == MTB_PHASE_SEG0) return MTB_OK;
+    if ((s = call_hook(comm, p, d.T * d.H, dt, MTB_OP_SUM, st)) != MTB_OK) return s;
+  }
+
+  if (phase == MTB_PHASE_ALL || phase == MTB_PHASE_SEG1) {
+    const void* dc = phase == MTB_PHASE_SEG1 ? reduced_in : p;
+    // LN2 backward + residual: dh = G + LN2^T(dc)
+    MTB_HIP(ln_bwd(dt, T, H, dc, h, mu2, rs2, w->ln2_g, G, dh, st));
+    if (g.ln2_g) MTB_HIP(colsum(dt, T, H, dc, H, h, mu2, rs2, g.ln2_g, red, st));
+    if (g.ln2_b) MTB_HIP(colsum(dt, T, H, dc, H, nullptr, nullptr, nullptr, g.ln2_b, red, st));
+    // projection backward (row-parallel: g1's backward is the identity)
+    {
+      Epi e;
+      e.out = dO; e.ldo = NO; e.outT = dOT; e.S = S;
+      MTB_HIP(gemm(dt, T, NO, H, dh, H, true, w->w_o, NO, false, e, st));
+    }
+    if (g.w_o) {
+      Epi e;
+      e.out = g.w_o; e.ldo = NO;
+      MTB_HIP(gemm(dt, H, NO, T, dh, H, false, O, NO, false, e, st));
+    }
+    if (g.b_o) MTB_HIP(colsum(dt, T, H, dh, H, nullptr, nullptr, nullptr, g.b_o, red, st));
+    // attention backward
+    MTB_HIP(attn_bwd(dt, (int)d.B, S, (int)d.nq, (int)d.nkv, (int)d.d, d.causal, qkv, qkvT, O, dO,
+                     dOT, lse, Dbuf, dqkv, part, st));
+    if (g.w_qkv) {
+      Epi e;
+      e.out = g.w_qkv; e.ldo = H;
+      MTB_HIP(gemm(dt, Nq, H, T, dqkv, Nq, false, a, H, false, e, st));
+    }
+    if (g.b_qkv) MTB_HIP(colsum(dt, T, Nq, dqkv, Nq, nullptr, nullptr, nullptr, g.b_qkv, red, st));
+    // QKV input gradient: partial over ranks, summed at f2
+    Epi e;
+    e.out = phase == MTB_PHASE_SEG1 ? dx : p; e.ldo = H;
+    MTB_HIP(gemm(dt, T, H, Nq, dqkv, Nq, true, w->w_qkv, H, false, e, st));
+    if (phase == MTB_PHASE_SEG1) return MTB_OK;
+    if ((s = call_hook(comm, p, d.T * d.H, dt, MTB_OP_SUM, st)) != MTB_OK) return s;
+  }
+
+  // LN1 backward + residual: dx = dh + LN1^T(da)
+  const void* da = phase == MTB_PHASE_SEG2 ? reduced_in : p;
+  MTB_HIP(ln_bwd(dt, T, H, da, x, mu1, rs1, w->ln1_g, dh, dx, st));
+  if (g.ln1_g) MTB_HIP(colsum(dt, T, H, da, H, x, mu1, rs1, g.ln1_g, red, st));
+  if (g.ln1_b) MTB_HIP(colsum(dt, T, H, da, H, nullptr, nullptr, nullptr, g.ln1_b, red, st));
+  return MTB_OK;
+}
+
+mtb_status mtb_vocab_xent(int64_t n, int64_t v, int64_t v0, int32_t dtype, int32_t phase,
+                          const void* logits, const int64_t* target, float* stats, float* loss,
+                          const float* dloss, void* dlogits, const mtb_comm* comm,
+                          void* hip_stream) {
+  if (n <= 0 || v <= 0 || v0 < 0) return fail(MTB_EINVAL, "n_tokens, v_local must be > 0, v_start >= 0");
+  if (n > 0x7fffffff) return fail(MTB_EUNSUPPORTED, "n_tokens beyond 2^31");
+  if (dtype != MTB_F32 && dtype != MTB_BF16) return fail(MTB_EINVAL, "bad dtype %d", dtype);
+  if (phase < MTB_XENT_ALL || phase > MTB_XENT_FINISH) return fail(MTB_EINVAL, "bad phase %d", phase);
+  MTB_REQ(target, "target");
+  MTB_REQ(stats, "stats");
+  if (phase != MTB_XENT_FINISH || dlogits) MTB_REQ(logits, "logits");
+  MTB_OPT(loss, "loss");
+  MTB_OPT(dloss, "dloss");
+  MTB_OPT(dlogits, "dlogits");
+  if (dlogits && !dloss) return fail(MTB_EINVAL, "dlogits requested without dloss");
+  hipStream_t st = (hipStream_t)hip_stream;
+  mtb_status s;
+  if (phase == MTB_XENT_PARTIAL) {
+    MTB_HIP(xent_partial(dtype, n, v, v0, logits, target, stats, nullptr, st));
+    return MTB_OK;
+  }
+  if (phase == MTB_XENT_ALL) {
+    const bool hook = comm && comm->allreduce;
+    MTB_HIP(xent_partial(dtype, n, v, v0, logits, target, stats, hook ? stats + 3 * n : nullptr, st));
+    if (hook) {
+      if ((s = call_hook(comm, stats, n, MTB_F32, MTB_OP_MAX, st)) != MTB_OK) return s;
+      MTB_HIP(xent_rescale(n, stats, stats + 3 * n, st));
+      if ((s = call_hook(comm, stats + n, n, MTB_F32, MTB_OP_SUM, st)) != MTB_OK) return s;
+      if ((s = call_hook(comm, stats + 2 * n, n, MTB_F32, MTB_OP_SUM, st)) != MTB_OK) return s;
+    }
+  }
+  if (loss || dlogits)
+    MTB_HIP(xent_finish(dtype, n, v, v0, logits, target, stats, loss, dloss, dlogits, st));
+  return MTB_OK;
+}
+
+mtb_status mtb_vocab_xent_combine(int64_t n, int32_t n_shards, const float* shard_stats,
+                                  float* stats, float* loss, void* hip_stream) {
+  if (n <= 0 || n_shards <= 0) return fail(MTB_EINVAL, "n_tokens and n_shards must be > 0");
+  MTB_REQ(shard_stats, "shard_stats");
+  MTB_REQ(stats, "stats");
+  MTB_OPT(loss, "loss");
+  MTB_HIP(xent_combine(n, n_shards, shard_stats, stats, loss, (hipStream_t)hip_stream));
+  return MTB_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,115 @@
+// Shared device helpers for the gfx950 kernels: bf16 storage, vector
+// types, wavefront (64-lane) reductions.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef uint16_t bf16_t;  // bf16 storage (upper half of an fp32)
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define MTB_DEV __device__ __forceinline__
+
+MTB_DEV float bf2f(bf16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
+// fp32 -> bf16, round to nearest even (finite inputs; NaN stays NaN).
+MTB_DEV bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u) return (bf16_t)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+// two fp32 -> packed bf16 pair (lo in bits 0..15)
+MTB_DEV uint32_t pack2(float lo, float hi) {
+  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+MTB_DEV float lo_f(uint32_t p) { return __uint_as_float(p << 16); }
+MTB_DEV float hi_f(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
+
+// element access by dtype
+template <typename T> MTB_DEV float ld_f(const T* p);
+template <> MTB_DEV float ld_f<float>(const float* p) { return *p; }
+template <> MTB_DEV float ld_f<bf16_t>(const bf16_t* p) { return bf2f(*p); }
+template <typename T> MTB_DEV void st_f(T* p, float v);
+template <> MTB_DEV void st_f<float>(float* p, float v) { *p = v; }
+template <> MTB_DEV void st_f<bf16_t>(bf16_t* p, float v) { *p = f2bf(v); }
+
+// 8 consecutive elements <-> 8 floats
+template <typename T> MTB_DEV void ld8(const T* p, float (&v)[8]);
+template <> MTB_DEV void ld8<bf16_t>(const bf16_t* p, float (&v)[8]) {
+  u32x4 q = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { v[2 * i] = lo_f(q[i]); v[2 * i + 1] = hi_f(q[i]); }
+}
+template <> MTB_DEV void ld8<float>(const float* p, float (&v)[8]) {
+  f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
+}
+template <typename T> MTB_DEV void st8(T* p, const float (&v)[8]);
+template <> MTB_DEV void st8<bf16_t>(bf16_t* p, const float (&v)[8]) {
+  u32x4 q;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) q[i] = pack2(v[2 * i], v[2 * i + 1]);
+  *reinterpret_cast<u32x4*>(p) = q;
+}
+template <> MTB_DEV void st8<float>(float* p, const float (&v)[8]) {
+  f32x4 a, b;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { a[i] = v[i]; b[i] = v[4 + i]; }
+  *reinterpret_cast<f32x4*>(p) = a;
+  *reinterpret_cast<f32x4*>(p + 4) = b;
+}
+
+// 4 consecutive elements <-> 4 floats
+template <typename T> MTB_DEV void ld4(const T* p, float (&v)[4]);
+template <> MTB_DEV void ld4<bf16_t>(const bf16_t* p, float (&v)[4]) {
+  u32x2 q = *reinterpret_cast<const u32x2*>(p);
+  v[0] = lo_f(q[0]); v[1] = hi_f(q[0]); v[2] = lo_f(q[1]); v[3] = hi_f(q[1]);
+}
+template <> MTB_DEV void ld4<float>(const float* p, float (&v)[4]) {
+  f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+}
+template <typename T> MTB_DEV void st4(T* p, const float (&v)[4]);
+template <> MTB_DEV void st4<bf16_t>(bf16_t* p, const float (&v)[4]) {
+  u32x2 q;
+  q[0] = pack2(v[0], v[1]);
+  q[1] = pack2(v[2], v[3]);
+  *reinterpret_cast<u32x2*>(p) = q;
+}
+template <> MTB_DEV void st4<float>(float* p, const float (&v)[4]) {
+  f32x4 a = {v[0], v[1], v[2], v[3]};
+  *reinterpret_cast<f32x4*>(p) = a;
+}
+
+// full-wavefront (64 lanes) butterfly reductions
+MTB_DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+MTB_DEV float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// e^x through the hardware base-2 exponential
+MTB_DEV float exp_fast(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+MTB_DEV float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// exact GELU u * Phi(u), with the device erf
+MTB_DEV float gelu_f(float u) { return 0.5f * u * (1.0f + erff(u * 0.70710678118654752f)); }
+MTB_DEV float gelu_grad_f(float u) {
+  float cdf = 0.5f * (1.0f + erff(u * 0.70710678118654752f));
+  float pdf = 0.39894228040143268f * expf(-0.5f * u * u);
+  return cdf + u * pdf;
+}
+MTB_DEV float sigmoid_f(float u) { return 1.0f / (1.0f + expf(-u)); }

@@ -1,0 +1,404 @@
+// GEMMs of the block: C[m][n] = sum_k A(m,k) B(n,k) with fused epilogues.
+//
+// bf16 path: gfx950 MFMA v_mfma_f32_32x32x16_bf16, 256 threads = 2x2
+// wavefronts, block tile BM x BN x 64, LDS double-buffered (one barrier per
+// k-step: the next tile is fetched into registers while the current one is
+// multiplied, then written to the other LDS buffer). Both operands sit in LDS
+// as [row][k] with k contiguous and 16-byte chunks XOR-swizzled by row, so a
+// fragment is one ds_read_b128 per lane. An operand whose contraction index
+// is not the contiguous one (dgrad's weight, both wgrad operands) is
+// transposed in registers on its way to LDS: a thread reads four k-rows of
+// eight contiguous elements and writes eight rows of four k-values.
+//
+// The MFMA is issued as (B-fragment, A-fragment), i.e. it computes C^T, so
+// that each lane ends up holding 4 consecutive n of one row m: stores are
+// 8-byte (bf16) vectors and gate/up pairs of the SwiGLU interleave land in
+// the same lane.
+//
+// Uses in the block ([TP-block] sec. 1-2; [MLM-notes] Column/RowParallelLinear):
+//   forward   Y = X W^T         A = X [T][in],  B = W [out][in]     (k-contig both)
+//   dgrad     dX = dY W         A = dY [T][out], B = W [out][in]    (B transposed)
+//   wgrad     dW = dY^T X       A = dY [T][out], B = X [T][in]      (both transposed)
+#include <type_traits>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace mtb {
+namespace {
+
+constexpr int BK = 64;
+
+MTB_DEV int swz(int row) { return (row ^ (row >> 3)) & 7; }
+
+// operand tile ROWS x BK from a matrix stored [rows][K] (k contiguous)
+template <int ROWS>
+struct TileKc {
+  static constexpr int NCH = ROWS * BK / 8 / 256;  // 16-byte chunks per thread
+  u32x4 r[NCH];
+  MTB_DEV void load(const bf16_t* __restrict__ p, int ld, int row0, int rowmax, int k0, int tid) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int q = tid + 256 * i, row = q >> 3, c = q & 7;
+      const int gr = min(row0 + row, rowmax - 1);
+      r[i] = *reinterpret_cast<const u32x4*>(p + (size_t)gr * ld + k0 + c * 8);
+    }
+  }
+  MTB_DEV void store(bf16_t* s, int tid) const {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int q = tid + 256 * i, row = q >> 3, c = q & 7;
+      *reinterpret_cast<u32x4*>(s + row * BK + ((c ^ swz(row)) << 3)) = r[i];
+    }
+  }
+};
+
+// operand tile ROWS x BK from a matrix stored [K][rows] (rows contiguous):
+// 4 (k) x 8 (rows) register blocks, transposed on the way to LDS
+template <int ROWS>
+struct TileMn {
+  static constexpr int IT = (ROWS / 8) * (BK / 4) / 256;
+  u32x4 r[IT][4];
+  MTB_DEV void load(const bf16_t* __restrict__ p, int ld, int row0, int rowmax, int k0, int tid) {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int idx = tid + 256 * it;
+      const int mc = idx % (ROWS / 8), k4 = idx / (ROWS / 8);
+      const int gm = min(row0 + mc * 8, rowmax - 8);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        r[it][j] = *reinterpret_cast<const u32x4*>(p + (size_t)(k0 + k4 * 4 + j) * ld + gm);
+    }
+  }
+  MTB_DEV void store(bf16_t* s, int tid) const {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int idx = tid + 256 * it;
+      const int mc = idx % (ROWS / 8), k4 = idx / (ROWS / 8);
+      const int c = k4 >> 1, half = k4 & 1;
+#pragma unroll
+      for (int mm = 0; mm < 8; ++mm) {
+        const int p = mm >> 1;
+        uint32_t w0, w1;
+        if (mm & 1) {
+          w0 = (r[it][0][p] >> 16) | (r[it][1][p] & 0xffff0000u);
+          w1 = (r[it][2][p] >> 16) | (r[it][3][p] & 0xffff0000u);
+        } else {
+          w0 = (r[it][0][p] & 0xffffu) | (r[it][1][p] << 16);
+          w1 = (r[it][2][p] & 0xffffu) | (r[it][3][p] << 16);
+        }
+        const int row = mc * 8 + mm;
+        u32x2 w = {w0, w1};
+        *reinterpret_cast<u32x2*>(s + row * BK + ((c ^ swz(row)) << 3) + half * 4) = w;
+      }
+    }
+  }
+};
+
+template <typename T>
+MTB_DEV void ld4g(const void* p, size_t off, float (&v)[4]) {
+  ld4(reinterpret_cast<const T*>(p) + off, v);
+}
+
+// epilogue for 4 consecutive columns n..n+3 of row m
+template <typename T, int EPI>
+MTB_DEV void epi4(const Epi& e, int m, int n, int N, float (&v)[4]) {
+  if constexpr (EPI == EPI_STORE || EPI == EPI_GELU) {
+    if (e.bias) {
+      float b[4];
+      ld4g<T>(e.bias, n, b);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] += b[r];
+    }
+  }
+  if constexpr (EPI == EPI_STORE) {
+    if (e.resid) {
+      float b[4];
+      ld4g<T>(e.resid, (size_t)m * e.ldr + n, b);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] += b[r];
+    }
+    st4(reinterpret_cast<T*>(e.out) + (size_t)m * e.ldo + n, v);
+    if (e.outT) {
+      const int bb = m / e.S, s = m % e.S;
+      T* o = reinterpret_cast<T*>(e.outT) + ((size_t)bb * N + n) * e.S + s;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st_f(o + (size_t)r * e.S, v[r]);
+    }
+  } else if constexpr (EPI == EPI_GELU) {
+    st4(reinterpret_cast<T*>(e.out) + (size_t)m * e.ldo + n, v);
+    float a[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) a[r] = gelu_f(v[r]);
+    st4(reinterpret_cast<T*>(e.out2) + (size_t)m * e.ldo2 + n, a);
+  } else if constexpr (EPI == EPI_DGELU) {
+    float u[4];
+    ld4g<T>(e.aux, (size_t)m * e.ldaux + n, u);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] *= gelu_grad_f(u[r]);
+    st4(reinterpret_cast<T*>(e.out) + (size_t)m * e.ldo + n, v);
+  } else if constexpr (EPI == EPI_DSWIGLU) {
+    // v = dm at features n..n+3; gate/up positions in the interleaved layout
+    const int gp = (n >> 4) * 32 + (n & 15);
+    float ug[4], uu[4], dg[4], du[4];
+    ld4g<T>(e.aux, (size_t)m * e.ldaux + gp, ug);
+    ld4g<T>(e.aux, (size_t)m * e.ldaux + gp + 16, uu);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float s = sigmoid_f(ug[r]);
+      dg[r] = v[r] * uu[r] * s * (1.0f + ug[r] * (1.0f - s));
+      du[r] = v[r] * ug[r] * s;
+    }
+    st4(reinterpret_cast<T*>(e.out) + (size_t)m * e.ldo + gp, dg);
+    st4(reinterpret_cast<T*>(e.out) + (size_t)m * e.ldo + gp + 16, du);
+  }
+}
+
+template <int BM, int BN, bool AKC, bool BKC, int EPI>
+__global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(int M, int N, int K,
+                                                           const bf16_t* __restrict__ A, int lda,
+                                                           const bf16_t* __restrict__ B, int ldb,
+                                                           Epi ep) {
+  constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
+  __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * BK];
+  __shared__ __attribute__((aligned(16))) bf16_t sB[2][BN * BK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // block -> tile: blocks i, i+8, i+16, ... share an XCD (and its L2), so
+  // give each XCD a contiguous run of tiles, then walk GROUP tile-rows at a
+  // time so that concurrently running tiles share A and B panels.
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  int bid = blockIdx.x;
+  const int nb = gridDim.x;
+  if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+  constexpr int GROUP = 8;
+  const int per_group = GROUP * tiles_n;
+  const int first_m = (bid / per_group) * GROUP;
+  const int gsz = min(tiles_m - first_m, GROUP);
+  const int tm = first_m + (bid % per_group) % gsz, tn = (bid % per_group) / gsz;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  using LA = typename std::conditional<AKC, TileKc<BM>, TileMn<BM>>::type;
+  using LB = typename std::conditional<BKC, TileKc<BN>, TileMn<BN>>::type;
+  LA la;
+  LB lb;
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int KT = K / BK;
+  la.load(A, lda, m0, M, 0, tid);
+  lb.load(B, ldb, n0, N, 0, tid);
+  la.store(sA[0], tid);
+  lb.store(sB[0], tid);
+  __syncthreads();
+
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < KT) {
+      la.load(A, lda, m0, M, (kt + 1) * BK, tid);
+      lb.load(B, ldb, n0, N, (kt + 1) * BK, tid);
+    }
+    const bf16_t* as = sA[cur];
+    const bf16_t* bs = sB[cur];
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const int c = kk * 2 + (lane >> 5);
+      bf16x8 af[FM], bf[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int row = wm * WM + i * 32 + (lane & 31);
+        af[i] = *reinterpret_cast<const bf16x8*>(as + row * BK + ((c ^ swz(row)) << 3));
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int row = wn * WN + j * 32 + (lane & 31);
+        bf[j] = *reinterpret_cast<const bf16x8*>(bs + row * BK + ((c ^ swz(row)) << 3));
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < KT) {
+      la.store(sA[cur ^ 1], tid);
+      lb.store(sB[cur ^ 1], tid);
+    }
+    __syncthreads();
+  }
+
+  // lane holds C[m][n..n+3] with m = (lane & 31), n = 8*i + 4*(lane >> 5) inside each 32x32 fragment
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int m = m0 + wm * WM + i * 32 + (lane & 31);
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int nf = n0 + wn * WN + j * 32;
+      if constexpr (EPI == EPI_SWIGLU) {
+        // columns nf..nf+15 are gate features f0..f0+15, nf+16..nf+31 the matching up features
+        if (nf >= N) continue;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int n = nf + 8 * q + 4 * (lane >> 5);
+          float g[4], u[4], o[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            g[r] = acc[i][j][4 * q + r];
+            u[r] = acc[i][j][4 * (q + 2) + r];
+          }
+          if (ep.bias) {
+            float bg[4], bu[4];
+            ld4g<bf16_t>(ep.bias, n, bg);
+            ld4g<bf16_t>(ep.bias, n + 16, bu);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) { g[r] += bg[r]; u[r] += bu[r]; }
+          }
+          // keep the stored pre-activations and the activation consistent
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            g[r] = bf2f(f2bf(g[r]));
+            u[r] = bf2f(f2bf(u[r]));
+            o[r] = g[r] * sigmoid_f(g[r]) * u[r];
+          }
+          bf16_t* uo = reinterpret_cast<bf16_t*>(ep.out) + (size_t)m * ep.ldo;
+          st4(uo + n, g);
+          st4(uo + n + 16, u);
+          const int f = (nf >> 1) + 8 * q + 4 * (lane >> 5);
+          st4(reinterpret_cast<bf16_t*>(ep.out2) + (size_t)m * ep.ldo2 + f, o);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = nf + 8 * q + 4 * (lane >> 5);
+          if (n >= N) continue;
+          float v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r];
+          if constexpr (EPI == EPI_GELU) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              if (ep.bias) v[r] += bf2f(reinterpret_cast<const bf16_t*>(ep.bias)[n + r]);
+              v[r] = bf2f(f2bf(v[r]));
+            }
+            Epi e2 = ep;
+            e2.bias = nullptr;
+            epi4<bf16_t, EPI>(e2, m, n, N, v);
+          } else {
+            epi4<bf16_t, EPI>(ep, m, n, N, v);
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 path: plain 64x64 register-blocked FMA GEMM (correctness-size problems)
+// ---------------------------------------------------------------------------
+template <bool AKC, bool BKC>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(int M, int N, int K,
+                                                       const float* __restrict__ A, int lda,
+                                                       const float* __restrict__ B, int ldb,
+                                                       Epi ep) {
+  __shared__ float sA[16][68];
+  __shared__ float sB[16][68];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += 16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid + 256 * i;
+      int row, kk;
+      if (AKC) { row = e >> 4; kk = e & 15; } else { kk = e >> 6; row = e & 63; }
+      const int gm = m0 + row, gk = k0 + kk;
+      float va = 0.f;
+      if (gm < M && gk < K) va = AKC ? A[(size_t)gm * lda + gk] : A[(size_t)gk * lda + gm];
+      sA[kk][row] = va;
+      if (BKC) { row = e >> 4; kk = e & 15; } else { kk = e >> 6; row = e & 63; }
+      const int gn = n0 + row, gk2 = k0 + kk;
+      float vb = 0.f;
+      if (gn < N && gk2 < K) vb = BKC ? B[(size_t)gn * ldb + gk2] : B[(size_t)gk2 * ldb + gn];
+      sB[kk][row] = vb;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { a[i] = sA[kk][ty * 4 + i]; b[i] = sB[kk][tx * 4 + i]; }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+  const int n = n0 + tx * 4;
+  if (n >= N) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + ty * 4 + i;
+    if (m >= M) continue;
+    float v[4] = {acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
+    epi4<float, EPI_STORE>(ep, m, n, N, v);
+  }
+}
+
+template <int BM, int BN, bool AKC, bool BKC, int EPI>
+hipError_t launch_bf16(int M, int N, int K, const void* A, int lda, const void* B, int ldb,
+                       const Epi& e, hipStream_t st) {
+  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, AKC, BKC, EPI>), dim3(tiles), dim3(256), 0, st, M,
+                     N, K, (const bf16_t*)A, lda, (const bf16_t*)B, ldb, e);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t gemm(int dtype, int M, int N, int K, const void* A, int lda, bool a_kc, const void* B,
+                int ldb, bool b_kc, const Epi& e, hipStream_t st) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (dtype == 0) {
+    if (e.kind != EPI_STORE) return hipErrorInvalidValue;
+    dim3 grid((N + 63) / 64, (M + 63) / 64);
+#define MTB_F32G(AK, BKc)                                                                   \
+  hipLaunchKernelGGL((gemm_f32_kernel<AK, BKc>), grid, dim3(256), 0, st, M, N, K,          \
+                     (const float*)A, lda, (const float*)B, ldb, e)
+    if (a_kc && b_kc) MTB_F32G(true, true);
+    else if (a_kc) MTB_F32G(true, false);
+    else if (b_kc) MTB_F32G(false, true);
+    else MTB_F32G(false, false);
+#undef MTB_F32G
+    return hipGetLastError();
+  }
+  // bf16: K % 64 == 0, M % 8 == 0, N % 8 == 0 (checked by the caller)
+  if (a_kc && b_kc) {
+    switch (e.kind) {
+      case EPI_STORE: return launch_bf16<128, 128, true, true, EPI_STORE>(M, N, K, A, lda, B, ldb, e, st);
+      case EPI_GELU: return launch_bf16<128, 128, true, true, EPI_GELU>(M, N, K, A, lda, B, ldb, e, st);
+      case EPI_SWIGLU: return launch_bf16<128, 128, true, true, EPI_SWIGLU>(M, N, K, A, lda, B, ldb, e, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (a_kc && !b_kc) {
+    switch (e.kind) {
+      case EPI_STORE: return launch_bf16<128, 128, true, false, EPI_STORE>(M, N, K, A, lda, B, ldb, e, st);
+      case EPI_DGELU: return launch_bf16<128, 128, true, false, EPI_DGELU>(M, N, K, A, lda, B, ldb, e, st);
+      case EPI_DSWIGLU: return launch_bf16<128, 128, true, false, EPI_DSWIGLU>(M, N, K, A, lda, B, ldb, e, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (!a_kc && !b_kc && e.kind == EPI_STORE)
+    return launch_bf16<128, 128, false, false, EPI_STORE>(M, N, K, A, lda, B, ldb, e, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mtb

@@ -1,0 +1,82 @@
+// Host-side launchers of the gfx950 kernels (internal to libmtb).
+// dtype is MTB_F32 (0) or MTB_BF16 (1) as in mtb.h.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mtb {
+
+// GEMM epilogues. The product is C[m][n] = sum_k A(m,k) B(n,k).
+enum EpiKind {
+  EPI_STORE = 0,    // out = C (+bias[n]) (+resid[m][n]); optional per-batch transpose outT
+  EPI_GELU = 1,     // u = C (+bias): out = u, out2 = GELU(u)
+  EPI_SWIGLU = 2,   // u = C (+bias) over interleaved gate/up columns: out = u [M][2F],
+                    // out2[m][f] = silu(gate) * up  [M][F]
+  EPI_DGELU = 3,    // out = C * GELU'(aux[m][n])
+  EPI_DSWIGLU = 4,  // C = dm [M][F]; aux = u [M][2F] interleaved: out [M][2F] = (d gate, d up)
+};
+
+struct Epi {
+  int kind = EPI_STORE;
+  void* out = nullptr;         // [M][ldo]
+  int ldo = 0;
+  void* out2 = nullptr;        // [M][ldo2]
+  int ldo2 = 0;
+  const void* bias = nullptr;  // [N]
+  const void* resid = nullptr; // [M][ldr]
+  int ldr = 0;
+  const void* aux = nullptr;   // [M][ldaux]
+  int ldaux = 0;
+  void* outT = nullptr;        // [M/S][N][S]: per-batch transpose (tokens contiguous)
+  int S = 1;
+};
+
+// C = A . B^T-style product with operand majorness:
+//   a_kc: A stored [M][K] (k contiguous) else [K][M];
+//   b_kc: B stored [N][K] (k contiguous) else [K][N].
+hipError_t gemm(int dtype, int M, int N, int K, const void* A, int lda, bool a_kc,
+                const void* B, int ldb, bool b_kc, const Epi& e, hipStream_t st);
+
+// LayerNorm over rows of width H: hsum = x (+resid) (+bias) rounded to dtype;
+// y = (hsum - mu) * rstd (* g + b). h_out (optional) receives hsum.
+hipError_t ln_fwd(int dtype, int rows, int H, const void* x, const void* resid, const void* bias,
+                  const void* g, const void* b, void* h_out, void* y, float* mu, float* rstd,
+                  float eps, hipStream_t st);
+// dx = dres + LN backward of dy at xhat = (hin - mu) * rstd, gain g (optional).
+hipError_t ln_bwd(int dtype, int rows, int H, const void* dy, const void* hin, const float* mu,
+                  const float* rstd, const void* g, const void* dres, void* dx, hipStream_t st);
+// column sums over rows: out[n] = sum_r y[r][n] (*xhat[r][n] if hin != NULL), written in dtype.
+// part: rows_split * N floats of scratch.
+hipError_t colsum(int dtype, int rows, int N, const void* y, int ldy, const void* hin,
+                  const float* mu, const float* rstd, void* out, float* part, hipStream_t st);
+// number of row splits colsum uses for `rows` rows (part holds splits * N floats)
+int colsum_splits(int rows);
+// out = a + b (+bias[n]) elementwise over [rows][H]
+hipError_t add3(int dtype, int rows, int H, const void* a, const void* b, const void* bias,
+                void* out, hipStream_t st);
+// activation forward / backward as separate passes (fp32 path)
+hipError_t act_fwd(int dtype, int act, int rows, int F, const void* u, void* m, hipStream_t st);
+hipError_t act_bwd(int dtype, int act, int rows, int F, const void* dm, const void* u, void* du,
+                   hipStream_t st);
+
+// Attention. qkv [T][Nqkv] token-major ([Q heads | K heads | V heads]);
+// qkvT [B][Nqkv][S] (bf16 path only); O [T][nq*d]; lse [B][nq][S] (natural log).
+hipError_t attn_fwd(int dtype, int B, int S, int nq, int nkv, int d, int causal, const void* qkv,
+                    const void* qkvT, void* O, float* lse, hipStream_t st);
+// dO [T][nq*d], dOT [B][nq*d][S] (bf16 only); Dbuf [B][nq][S] fp32 scratch;
+// dqkv [T][Nqkv] output; part: fp32 scratch of B*nq*S*2*d floats (GQA, bf16).
+hipError_t attn_bwd(int dtype, int B, int S, int nq, int nkv, int d, int causal, const void* qkv,
+                    const void* qkvT, const void* O, const void* dO, const void* dOT,
+                    const float* lse, float* Dbuf, void* dqkv, float* part, hipStream_t st);
+
+// Vocab-sharded cross-entropy.
+hipError_t xent_partial(int dtype, int64_t n, int64_t v, int64_t v0, const void* z,
+                        const int64_t* tgt, float* stats, float* mloc, hipStream_t st);
+hipError_t xent_rescale(int64_t n, float* stats, const float* mloc, hipStream_t st);
+hipError_t xent_combine(int64_t n, int R, const float* shard_stats, float* stats, float* loss,
+                        hipStream_t st);
+hipError_t xent_finish(int dtype, int64_t n, int64_t v, int64_t v0, const void* z,
+                       const int64_t* tgt, const float* stats, float* loss, const float* dloss,
+                       void* dz, hipStream_t st);
+
+}  // namespace mtb

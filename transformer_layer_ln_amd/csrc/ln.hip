@@ -1,0 +1,374 @@
+// LayerNorm forward/backward and the small elementwise / column-reduction
+// kernels of the block. All are HBM-bound: one 64-lane wavefront owns one
+// row, holds it in registers (16-byte vector loads, coalesced across lanes)
+// and reduces with wavefront butterflies.
+//
+// LayerNorm: [Lab06] sec. 2 steps (2) and (5) -- F.layer_norm over the hidden
+// dimension: per-token mean and biased variance, (x - mean) / sqrt(var + eps),
+// optional gain/shift.
+#include "common.h"
+#include "kernels.h"
+
+namespace mtb {
+namespace {
+
+constexpr int kRowsPerBlock = 4;  // 4 wavefronts, one row each
+
+// NC = number of 8-element chunks per lane (H <= 512 * NC)
+template <typename T, int NC>
+__global__ __launch_bounds__(256) void ln_fwd_kernel(int rows, int H, const T* __restrict__ x,
+                                                     const T* __restrict__ resid,
+                                                     const T* __restrict__ bias,
+                                                     const T* __restrict__ g,
+                                                     const T* __restrict__ b, T* __restrict__ h_out,
+                                                     T* __restrict__ y, float* __restrict__ mu_out,
+                                                     float* __restrict__ rstd_out, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const size_t base = (size_t)row * H;
+  float v[NC][8];
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int col = (c * 64 + lane) * 8;
+    if (col < H) {
+      ld8(x + base + col, v[c]);
+      if (resid) {
+        float r[8];
+        ld8(resid + base + col, r);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[c][e] += r[e];
+      }
+      if (bias) {
+        float r[8];
+        ld8(bias + col, r);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[c][e] += r[e];
+      }
+      if (resid || bias) {
+        // the stored residual stream and the statistics see the same values
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          T t;
+          st_f(&t, v[c][e]);
+          v[c][e] = ld_f(&t);
+        }
+        if (h_out) st8(h_out + base + col, v[c]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += v[c][e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[c][e] = 0.f;
+    }
+  }
+  const float inv_h = 1.0f / (float)H;
+  const float mean = wave_sum(s) * inv_h;
+  float q = 0.f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int col = (c * 64 + lane) * 8;
+    if (col < H) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float d = v[c][e] - mean;
+        q += d * d;
+      }
+    }
+  }
+  const float var = wave_sum(q) * inv_h;
+  const float rstd = 1.0f / sqrtf(var + eps);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int col = (c * 64 + lane) * 8;
+    if (col < H) {
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = (v[c][e] - mean) * rstd;
+      if (g) {
+        float gg[8], bb[8];
+        ld8(g + col, gg);
+        ld8(b + col, bb);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = o[e] * gg[e] + bb[e];
+      }
+      st8(y + base + col, o);
+    }
+  }
+  if (lane == 0) {
+    mu_out[row] = mean;
+    rstd_out[row] = rstd;
+  }
+}
+
+// dx = dres + rstd * (gh - mean(gh) - xhat * mean(gh * xhat)), gh = dy * g
+template <typename T, int NC>
+__global__ __launch_bounds__(256) void ln_bwd_kernel(int rows, int H, const T* __restrict__ dy,
+                                                     const T* __restrict__ hin,
+                                                     const float* __restrict__ mu,
+                                                     const float* __restrict__ rstd,
+                                                     const T* __restrict__ g,
+                                                     const T* __restrict__ dres,
+                                                     T* __restrict__ dx) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const size_t base = (size_t)row * H;
+  const float m = mu[row], r = rstd[row];
+  float gh[NC][8], xh[NC][8];
+  float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int col = (c * 64 + lane) * 8;
+    if (col < H) {
+      float hv[8];
+      ld8(dy + base + col, gh[c]);
+      ld8(hin + base + col, hv);
+      if (g) {
+        float gg[8];
+        ld8(g + col, gg);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gh[c][e] *= gg[e];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        xh[c][e] = (hv[e] - m) * r;
+        s1 += gh[c][e];
+        s2 += gh[c][e] * xh[c][e];
+      }
+    }
+  }
+  const float inv_h = 1.0f / (float)H;
+  const float mg = wave_sum(s1) * inv_h;
+  const float mgx = wave_sum(s2) * inv_h;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int col = (c * 64 + lane) * 8;
+    if (col < H) {
+      float o[8], d0[8];
+      ld8(dres + base + col, d0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = d0[e] + r * (gh[c][e] - mg - xh[c][e] * mgx);
+      st8(dx + base + col, o);
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void colsum_part_kernel(int rows, int N, int rows_per,
+                                                          const T* __restrict__ y, int ldy,
+                                                          const T* __restrict__ hin,
+                                                          const float* __restrict__ mu,
+                                                          const float* __restrict__ rstd,
+                                                          float* __restrict__ part) {
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= N) return;
+  const int r0 = blockIdx.y * rows_per;
+  const int r1 = min(rows, r0 + rows_per);
+  float acc = 0.f;
+  for (int r = r0; r < r1; ++r) {
+    float v = ld_f(y + (size_t)r * ldy + n);
+    if (hin) v *= (ld_f(hin + (size_t)r * N + n) - mu[r]) * rstd[r];
+    acc += v;
+  }
+  part[(size_t)blockIdx.y * N + n] = acc;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void colsum_fin_kernel(int N, int splits,
+                                                         const float* __restrict__ part,
+                                                         T* __restrict__ out) {
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= N) return;
+  float acc = 0.f;
+  for (int s = 0; s < splits; ++s) acc += part[(size_t)s * N + n];
+  st_f(out + n, acc);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void add3_kernel(size_t total8, int H, const T* __restrict__ a,
+                                                   const T* __restrict__ b,
+                                                   const T* __restrict__ bias,
+                                                   T* __restrict__ out) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total8) return;
+  const size_t e0 = i * 8;
+  float va[8], vb[8];
+  ld8(a + e0, va);
+  ld8(b + e0, vb);
+  if (bias) {
+    float vc[8];
+    ld8(bias + (int)(e0 % H), vc);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vb[e] += vc[e];
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) va[e] += vb[e];
+  st8(out + e0, va);
+}
+
+// GELU: u [rows][F] -> m. SwiGLU: u [rows][2F] (gate/up interleaved by 16) -> m [rows][F].
+template <typename T>
+__global__ __launch_bounds__(256) void act_fwd_kernel(int act, size_t total, int F,
+                                                      const T* __restrict__ u, T* __restrict__ m) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  if (act == 0) {
+    st_f(m + i, gelu_f(ld_f(u + i)));
+  } else {
+    const size_t r = i / F;
+    const int f = (int)(i % F);
+    const size_t gp = r * 2 * F + (f >> 4) * 32 + (f & 15);
+    const float ug = ld_f(u + gp), uu = ld_f(u + gp + 16);
+    st_f(m + i, ug * sigmoid_f(ug) * uu);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void act_bwd_kernel(int act, size_t total, int F,
+                                                      const T* __restrict__ dm,
+                                                      const T* __restrict__ u,
+                                                      T* __restrict__ du) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const float d = ld_f(dm + i);
+  if (act == 0) {
+    st_f(du + i, d * gelu_grad_f(ld_f(u + i)));
+  } else {
+    const size_t r = i / F;
+    const int f = (int)(i % F);
+    const size_t gp = r * 2 * F + (f >> 4) * 32 + (f & 15);
+    const float ug = ld_f(u + gp), uu = ld_f(u + gp + 16);
+    const float s = sigmoid_f(ug);
+    st_f(du + gp, d * uu * s * (1.0f + ug * (1.0f - s)));
+    st_f(du + gp + 16, d * ug * s);
+  }
+}
+
+template <typename T, int NC>
+hipError_t ln_fwd_t(int rows, int H, const void* x, const void* resid, const void* bias,
+                    const void* g, const void* b, void* h_out, void* y, float* mu, float* rstd,
+                    float eps, hipStream_t st) {
+  dim3 grid((rows + kRowsPerBlock - 1) / kRowsPerBlock);
+  hipLaunchKernelGGL((ln_fwd_kernel<T, NC>), grid, dim3(256), 0, st, rows, H, (const T*)x,
+                     (const T*)resid, (const T*)bias, (const T*)g, (const T*)b, (T*)h_out, (T*)y,
+                     mu, rstd, eps);
+  return hipGetLastError();
+}
+
+template <typename T, int NC>
+hipError_t ln_bwd_t(int rows, int H, const void* dy, const void* hin, const float* mu,
+                    const float* rstd, const void* g, const void* dres, void* dx, hipStream_t st) {
+  dim3 grid((rows + kRowsPerBlock - 1) / kRowsPerBlock);
+  hipLaunchKernelGGL((ln_bwd_kernel<T, NC>), grid, dim3(256), 0, st, rows, H, (const T*)dy,
+                     (const T*)hin, mu, rstd, (const T*)g, (const T*)dres, (T*)dx);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t ln_fwd_dispatch(int rows, int H, const void* x, const void* resid, const void* bias,
+                           const void* g, const void* b, void* h_out, void* y, float* mu,
+                           float* rstd, float eps, hipStream_t st) {
+  const int nc = (H + 511) / 512;
+#define MTB_LNF(N) return ln_fwd_t<T, N>(rows, H, x, resid, bias, g, b, h_out, y, mu, rstd, eps, st)
+  if (nc <= 1) MTB_LNF(1);
+  if (nc <= 2) MTB_LNF(2);
+  if (nc <= 4) MTB_LNF(4);
+  if (nc <= 8) MTB_LNF(8);
+  if (nc <= 16) MTB_LNF(16);
+#undef MTB_LNF
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t ln_bwd_dispatch(int rows, int H, const void* dy, const void* hin, const float* mu,
+                           const float* rstd, const void* g, const void* dres, void* dx,
+                           hipStream_t st) {
+  const int nc = (H + 511) / 512;
+#define MTB_LNB(N) return ln_bwd_t<T, N>(rows, H, dy, hin, mu, rstd, g, dres, dx, st)
+  if (nc <= 1) MTB_LNB(1);
+  if (nc <= 2) MTB_LNB(2);
+  if (nc <= 4) MTB_LNB(4);
+  if (nc <= 8) MTB_LNB(8);
+  if (nc <= 16) MTB_LNB(16);
+#undef MTB_LNB
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t ln_fwd(int dtype, int rows, int H, const void* x, const void* resid, const void* bias,
+                  const void* g, const void* b, void* h_out, void* y, float* mu, float* rstd,
+                  float eps, hipStream_t st) {
+  if (dtype == 1)
+    return ln_fwd_dispatch<bf16_t>(rows, H, x, resid, bias, g, b, h_out, y, mu, rstd, eps, st);
+  return ln_fwd_dispatch<float>(rows, H, x, resid, bias, g, b, h_out, y, mu, rstd, eps, st);
+}
+
+hipError_t ln_bwd(int dtype, int rows, int H, const void* dy, const void* hin, const float* mu,
+                  const float* rstd, const void* g, const void* dres, void* dx, hipStream_t st) {
+  if (dtype == 1) return ln_bwd_dispatch<bf16_t>(rows, H, dy, hin, mu, rstd, g, dres, dx, st);
+  return ln_bwd_dispatch<float>(rows, H, dy, hin, mu, rstd, g, dres, dx, st);
+}
+
+int colsum_splits(int rows) { return rows < 64 ? 1 : (rows + 63) / 64 < 128 ? (rows + 63) / 64 : 128; }
+
+hipError_t colsum(int dtype, int rows, int N, const void* y, int ldy, const void* hin,
+                  const float* mu, const float* rstd, void* out, float* part, hipStream_t st) {
+  const int splits = colsum_splits(rows);
+  const int rows_per = (rows + splits - 1) / splits;
+  dim3 g1((N + 255) / 256, splits), g2((N + 255) / 256);
+  if (dtype == 1) {
+    hipLaunchKernelGGL(colsum_part_kernel<bf16_t>, g1, dim3(256), 0, st, rows, N, rows_per,
+                       (const bf16_t*)y, ldy, (const bf16_t*)hin, mu, rstd, part);
+    hipLaunchKernelGGL(colsum_fin_kernel<bf16_t>, g2, dim3(256), 0, st, N, splits, part,
+                       (bf16_t*)out);
+  } else {
+    hipLaunchKernelGGL(colsum_part_kernel<float>, g1, dim3(256), 0, st, rows, N, rows_per,
+                       (const float*)y, ldy, (const float*)hin, mu, rstd, part);
+    hipLaunchKernelGGL(colsum_fin_kernel<float>, g2, dim3(256), 0, st, N, splits, part,
+                       (float*)out);
+  }
+  return hipGetLastError();
+}
+
+hipError_t add3(int dtype, int rows, int H, const void* a, const void* b, const void* bias,
+                void* out, hipStream_t st) {
+  const size_t total8 = (size_t)rows * H / 8;
+  dim3 grid((unsigned)((total8 + 255) / 256));
+  if (dtype == 1)
+    hipLaunchKernelGGL(add3_kernel<bf16_t>, grid, dim3(256), 0, st, total8, H, (const bf16_t*)a,
+                       (const bf16_t*)b, (const bf16_t*)bias, (bf16_t*)out);
+  else
+    hipLaunchKernelGGL(add3_kernel<float>, grid, dim3(256), 0, st, total8, H, (const float*)a,
+                       (const float*)b, (const float*)bias, (float*)out);
+  return hipGetLastError();
+}
+
+hipError_t act_fwd(int dtype, int act, int rows, int F, const void* u, void* m, hipStream_t st) {
+  const size_t total = (size_t)rows * F;
+  dim3 grid((unsigned)((total + 255) / 256));
+  if (dtype == 1)
+    hipLaunchKernelGGL(act_fwd_kernel<bf16_t>, grid, dim3(256), 0, st, act, total, F,
+                       (const bf16_t*)u, (bf16_t*)m);
+  else
+    hipLaunchKernelGGL(act_fwd_kernel<float>, grid, dim3(256), 0, st, act, total, F,
+                       (const float*)u, (float*)m);
+  return hipGetLastError();
+}
+
+hipError_t act_bwd(int dtype, int act, int rows, int F, const void* dm, const void* u, void* du,
+                   hipStream_t st) {
+  const size_t total = (size_t)rows * F;
+  dim3 grid((unsigned)((total + 255) / 256));
+  if (dtype == 1)
+    hipLaunchKernelGGL(act_bwd_kernel<bf16_t>, grid, dim3(256), 0, st, act, total, F,
+                       (const bf16_t*)dm, (const bf16_t*)u, (bf16_t*)du);
+  else
+    hipLaunchKernelGGL(act_bwd_kernel<float>, grid, dim3(256), 0, st, act, total, F,
+                       (const float*)dm, (const float*)u, (float*)du);
+  return hipGetLastError();
+}
+
+}  // namespace mtb
