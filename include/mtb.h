@@ -21,8 +21,9 @@
  *   never allocates device memory; the sizes of the caller-provided `saved`
  *   and `scratch` buffers come from the *_bytes queries.
  * Layout: row-major, contiguous. Activations are [B, S, H] (token-major,
- *   T = B*S rows). Weights are [out, in]. Every pointer must be 16-byte
- *   aligned.
+ *   T = B*S rows). Weights are [out, in]. Tensor pointers must be 16-byte
+ *   aligned; the cross-entropy's per-token vectors (target, stats, loss,
+ *   dloss) need only their element type's alignment.
  * Dtype: MTB_BF16 -- every tensor (activations, weights, biases, LN
  *   parameters, gradients, partial sums) is bf16, with fp32 accumulation
  *   inside; MTB_F32 -- everything fp32. LayerNorm statistics, the attention

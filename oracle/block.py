@@ -251,7 +251,9 @@ def block_backward(G, cache):
     Returns (dx [B, S, H], grads) with grads holding the unsharded gradient
     of every weight present (shard slices concatenated back), plus the
     per-shard partials at the two backward reduction points under
-    grads["_dc_partials"] and grads["_da_partials"]."""
+    grads["_dc_partials"] and grads["_da_partials"], and the per-token key
+    gradients (whose column sums give the key-bias gradient) under
+    grads["_dk_tokens"]."""
     R, B, S, H = cache["R"], cache["B"], cache["S"], cache["H"]
     nq, nkv, d = cache["nq"], cache["nkv"], cache["d"]
     T = B * S
@@ -292,6 +294,7 @@ def block_backward(G, cache):
 
     # attention: projection (row-parallel), per-head attention, QKV (column-parallel)
     da_parts = []
+    dk_tok = []
     for r in range(R):
         sh = cache["shards"][r]
         ws = sh["w"]
@@ -308,6 +311,7 @@ def block_backward(G, cache):
         if "bq" in ws:
             g["bq"], g["bk"], g["bv"] = dq2.sum(0), dk2.sum(0), dv2.sum(0)
         da_parts.append(dq2 @ ws["wq"] + dk2 @ ws["wk"] + dv2 @ ws["wv"])
+        dk_tok.append(dk2)
     if "bo" in w:
         dbo = dh.sum(0)
 
@@ -330,6 +334,7 @@ def block_backward(G, cache):
     grads["_dc_partials"] = dc_parts
     grads["_da_partials"] = da_parts
     grads["_dh"] = dh
+    grads["_dk_tokens"] = np.concatenate(dk_tok, axis=1)   # [T, nkv*d] per-token key gradients
     return dx.reshape(B, S, H), grads
 
 

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import TOL, host, oracle_kw, rel_err, run_rank, say, split_grads, tdtype
+from gpu_util import TOL, host, oracle_kw, rel_err, run_rank, say, split_grads, tdtype, zero_sum_err
 from oracle import block as ob
 from transformer_layer_ln_amd import inputs, mtb
 
@@ -99,7 +99,8 @@ def _check_tp(cfg):
             got = res["grads"][0][k]
         else:
             got = np.concatenate([res["grads"][r][k] for r in range(cfg.tp)], axis=axis)
-        errs["d" + k] = rel_err(got, ref_g[k])
+        errs["d" + k] = (rel_err(got, ref_g[k]) if k != "bk"
+                         else zero_sum_err(got, ref_g["_dk_tokens"]))
     say("   errors:", {k: f"{v:.2e}" for k, v in errs.items()})
     bad = {k: v for k, v in errs.items() if not v <= tol}
     assert not bad, f"above tolerance {tol}: {bad}"

@@ -134,7 +134,7 @@ Scratch scratch_layout(const Dims& d) {
   return s;
 }
 
-bool misaligned(const void* p) { return ((uintptr_t)p & 15) != 0; }
+bool misaligned(const void* p, uintptr_t a = 16) { return ((uintptr_t)p & (a - 1)) != 0; }
 
 #define MTB_REQ(p, name)                                                             \
   do {                                                                               \
@@ -144,6 +144,16 @@ bool misaligned(const void* p) { return ((uintptr_t)p & 15) != 0; }
 #define MTB_OPT(p, name)                                                             \
   do {                                                                               \
     if ((p) && misaligned(p)) return fail(MTB_EINVAL, "%s is not 16-byte aligned", name); \
+  } while (0)
+// small per-token vectors: natural alignment of their element type
+#define MTB_REQ_A(p, name, a)                                                        \
+  do {                                                                               \
+    if (!(p)) return fail(MTB_EINVAL, "%s is NULL", name);                           \
+    if (misaligned(p, a)) return fail(MTB_EINVAL, "%s is not %d-byte aligned", name, (int)(a)); \
+  } while (0)
+#define MTB_OPT_A(p, name, a)                                                        \
+  do {                                                                               \
+    if ((p) && misaligned(p, a)) return fail(MTB_EINVAL, "%s is not %d-byte aligned", name, (int)(a)); \
   } while (0)
 
 mtb_status check_weights(const mtb_weights* w) {
@@ -455,11 +465,11 @@ mtb_status mtb_vocab_xent(int64_t n, int64_t v, int64_t v0, int32_t dtype, int32
   if (n > 0x7fffffff) return fail(MTB_EUNSUPPORTED, "n_tokens beyond 2^31");
   if (dtype != MTB_F32 && dtype != MTB_BF16) return fail(MTB_EINVAL, "bad dtype %d", dtype);
   if (phase < MTB_XENT_ALL || phase > MTB_XENT_FINISH) return fail(MTB_EINVAL, "bad phase %d", phase);
-  MTB_REQ(target, "target");
-  MTB_REQ(stats, "stats");
+  MTB_REQ_A(target, "target", 8);
+  MTB_REQ_A(stats, "stats", 4);
   if (phase != MTB_XENT_FINISH || dlogits) MTB_REQ(logits, "logits");
-  MTB_OPT(loss, "loss");
-  MTB_OPT(dloss, "dloss");
+  MTB_OPT_A(loss, "loss", 4);
+  MTB_OPT_A(dloss, "dloss", 4);
   MTB_OPT(dlogits, "dlogits");
   if (dlogits && !dloss) return fail(MTB_EINVAL, "dlogits requested without dloss");
   hipStream_t st = (hipStream_t)hip_stream;
@@ -486,9 +496,9 @@ mtb_status mtb_vocab_xent(int64_t n, int64_t v, int64_t v0, int32_t dtype, int32
 mtb_status mtb_vocab_xent_combine(int64_t n, int32_t n_shards, const float* shard_stats,
                                   float* stats, float* loss, void* hip_stream) {
   if (n <= 0 || n_shards <= 0) return fail(MTB_EINVAL, "n_tokens and n_shards must be > 0");
-  MTB_REQ(shard_stats, "shard_stats");
-  MTB_REQ(stats, "stats");
-  MTB_OPT(loss, "loss");
+  MTB_REQ_A(shard_stats, "shard_stats", 4);
+  MTB_REQ_A(stats, "stats", 4);
+  MTB_OPT_A(loss, "loss", 4);
   MTB_HIP(xent_combine(n, n_shards, shard_stats, stats, loss, (hipStream_t)hip_stream));
   return MTB_OK;
 }
