@@ -7,6 +7,11 @@ share (hidden 4096, 4 local heads x 128, ffn chunk 2048, batch 4, causal,
 GELU). Prints ONE JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--workload seq2048|seq512|seq4096]
+
+The default workload is the seq-2048 rank share (the metric's target
+configuration); --workload seq512 times the seq-512 TP=4 share (hidden 1024,
+4 heads x 64, ffn chunk 1024, batch 8) and seq4096 the SwiGLU/GQA share.
 """
 from __future__ import annotations
 
@@ -21,6 +26,15 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+
+WORKLOADS = {
+    "seq2048": ("C4", "TP=8 rank share of a hidden-4096 block: 4 local heads x 128, ffn chunk 2048, "
+                      "batch 4, seq 2048, causal, GELU", "one tp8 rank share"),
+    "seq512": ("C2", "TP=4 rank share of a hidden-1024 block: 4 local heads x 64, ffn chunk 1024, "
+                     "batch 8, seq 512, GELU", "one tp4 rank share"),
+    "seq4096": ("C5", "TP=8 rank share of a hidden-4096 SwiGLU/GQA block: 4 q / 1 kv heads x 128, "
+                      "ffn chunk 1792 (gate+up 3584), batch 2, seq 4096", "one tp8 rank share"),
+}
 
 
 def model_flops(cfg) -> float:
@@ -131,6 +145,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--workload", default="seq2048", choices=sorted(WORKLOADS))
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share; --gpus {args.gpus} is not supported "
@@ -140,28 +155,26 @@ def main():
 
     from transformer_layer_ln_amd import inputs, mtb
 
-    cfg = inputs.C4
+    key, desc, par = WORKLOADS[args.workload]
+    cfg = inputs.CONFIGS[key]
     flops = model_flops(cfg)
     ms, wall, kern = run_gpu(cfg, args.steps, args.warmup,
                              trace_what=[mtb.TRACE_FC1_FWD, mtb.TRACE_LN1_FWD, mtb.TRACE_ATTN_FWD])
     tflops = flops / (ms * 1e-3) / 1e12
 
-    # the seq-512 TP=4 rank share, for the metric's second sequence length
-    ms512, _, _ = run_gpu(inputs.C2, args.steps, args.warmup)
-    tf512 = model_flops(inputs.C2) / (ms512 * 1e-3) / 1e12
-
     T, H, F = cfg.tokens, cfg.hidden, cfg.ffn
-    fc1_flops = 2.0 * T * H * F
+    Fu = 2 * F if cfg.act == "swiglu" else F
+    fc1_flops = 2.0 * T * H * Fu
     fc1_ms = kern[mtb.TRACE_FC1_FWD]
     achieved = fc1_flops / (fc1_ms * 1e-3) / 1e12
     ln_bytes = T * H * 2 * 2 + T * 8          # read x, write a (bf16), write mu/rstd
     ln_ms = kern[mtb.TRACE_LN1_FWD]
-    attn_pairs = cfg.seq * (cfg.seq + 1) // 2
+    attn_pairs = cfg.seq * (cfg.seq + 1) // 2 if cfg.causal else cfg.seq * cfg.seq
     attn_flops = 4.0 * cfg.head_dim * attn_pairs * cfg.batch * cfg.q_heads
     attn_ms = kern[mtb.TRACE_ATTN_FWD]
 
     res = {
-        "metric": "block fwd+bwd TFLOP/s (one TP-rank shard, bf16) at seq 2048",
+        "metric": f"block fwd+bwd TFLOP/s (one TP-rank shard, bf16) at seq {cfg.seq}",
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -173,18 +186,14 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic: seeded N(0,1) x, N(0,1/fan_in) weights, dout = 1/numel",
-        "config": {"workload": "TP=8 rank share of a hidden-4096 block: 4 local heads x 128, "
-                               "ffn chunk 2048, batch 4, seq 2048, causal, GELU",
-                   "batch": cfg.batch, "seq_len": cfg.seq, "hidden": cfg.hidden,
-                   "local_heads": cfg.q_heads, "head_dim": cfg.head_dim, "ffn_chunk": cfg.ffn,
-                   "parallelism": "one tp8 rank share"},
+        "config": {"workload": desc, "batch": cfg.batch, "seq_len": cfg.seq,
+                   "hidden": cfg.hidden, "local_q_heads": cfg.q_heads,
+                   "local_kv_heads": cfg.kv_heads, "head_dim": cfg.head_dim,
+                   "ffn_chunk": cfg.ffn, "parallelism": par},
         "model_flops_per_step": flops,
         "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "tokens_per_s": round(cfg.tokens / (ms * 1e-3), 1),
-        "seq512": {"workload": "TP=4 rank share, hidden 1024, 4 heads x 64, ffn chunk 1024, "
-                               "batch 8, seq 512", "ms_per_step": round(ms512, 4),
-                   "tflops": round(tf512, 2)},
-        "roofline": {"kernel": "fc1 forward GEMM + GELU epilogue (8192 x 2048 x 4096)",
+        "roofline": {"kernel": f"fc1 forward GEMM + {cfg.act} epilogue ({T} x {Fu} x {H})",
                      "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": None, "avg_ms": round(fc1_ms, 5)},

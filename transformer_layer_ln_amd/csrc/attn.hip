@@ -3,21 +3,22 @@
 // keys, times V; [TP-block] sec. 2: heads are independent, so one rank runs
 // its local heads with no communication; GQA: q head i reads kv head i / g).
 //
-// bf16 path (gfx950 MFMA 32x32x16):
-//  * forward: a workgroup = 4 wavefronts x 32 queries of one (batch, q head).
-//    K and V^T tiles of 64 keys are staged in LDS and shared by the 4
-//    wavefronts. Each wavefront computes S^T = K Q^T so that a lane owns one
-//    query column: the online-softmax row max/sum is 16 values in-lane plus
-//    one cross-lane exchange (lane ^ 32), and the rescale of the O^T
-//    accumulator is a per-lane scalar. P^T feeds the second MFMA
-//    (O^T += V^T P^T) straight from registers. Only O and the row
-//    log-sum-exp are written.
+// bf16 path (gfx950 MFMA 32x32x16). Every kernel works on 64-row tiles of one
+// (batch, head) with 4 wavefronts arranged 2 x 2: each wavefront takes 32 rows
+// of its own side and one 32-row half of the other side's tile, and the two
+// halves are combined through LDS at the end. That gives S/64 * B * heads
+// workgroups (two resident per CU at 2 wavefronts per SIMD); causal grids pair
+// heavy and light tiles.
+//  * forward: S^T = K Q^T puts one query per lane, so the online-softmax row
+//    max is 16 in-lane values plus one exchange with lane ^ 32, the running
+//    sum stays per lane until the end, and the O^T accumulator is rescaled
+//    only when some row's max moved. P^T feeds O^T += V^T P^T from registers.
+//    K and V^T tiles are fetched one step ahead into registers, double-
+//    buffered in LDS. Only O and the row log-sum-exp are written.
 //  * backward: P is recomputed from the saved log-sum-exp.
-//    dK/dV: a workgroup owns 128 keys (4 x 32) of one q head and walks all
-//    query tiles; S = Q K^T puts a key per lane so that dV^T += dO^T P^T and
-//    dK^T += Q^T dS^T take P and dS straight from registers. With GQA the
-//    per-q-head contributions are summed over the group by a second pass.
-//    dQ: a workgroup owns 128 queries and walks the key tiles (S^T layout).
+//    dK/dV: S = Q K^T puts a key per lane, so P and dS feed dV^T += dO^T P^T
+//    and dK^T += Q^T dS^T from registers; with GQA the q-head contributions
+//    of a kv head are summed by a second pass. dQ: S^T layout, dQ^T += K^T dS^T.
 //    No atomics: every output element has exactly one writer.
 // Layout inputs: qkv [T][Nqkv] token-major and its per-batch transpose
 // qkvT [B][Nqkv][S]; dO [T][nq*d] and dOT [B][nq*d][S].
@@ -71,40 +72,101 @@ MTB_DEV bf16x8 frag(const bf16_t* s, int row, int c) {
   return *reinterpret_cast<const bf16x8*>(s + row * W + ((c ^ swz(row)) << 3));
 }
 
-MTB_DEV __bf16 to_bf(float f) { return __builtin_bit_cast(__bf16, f2bf(f)); }
-
-// B operand for a 16-key (or 16-query) k-step t from a pair of 32x32
-// accumulators: lane group g holds rows 8i + 4g + r; step t uses i = 2(t&1), 2(t&1)+1.
-MTB_DEV bf16x8 pack_step(const f32x16 (&a)[2], int t) {
-  const int f = t >> 1, i0 = 2 * (t & 1);
-  bf16x8 p;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    p[r] = to_bf(a[f][4 * i0 + r]);
-    p[4 + r] = to_bf(a[f][4 * (i0 + 1) + r]);
+// linear workgroup id -> (tile along the sequence, batch*head). Causal
+// workloads put heavy tiles in the first half of the grid (heaviest first)
+// and light tiles in the second half (lightest first): the two workgroups a
+// CU holds together then carry about the same total work.
+// heavy_high: the heavy tiles are the high-numbered ones (queries at the end
+// see the most keys); otherwise the low-numbered ones (keys at the start are
+// seen by the most queries).
+MTB_DEV void tile_order(int L, int ntile, int nbh, bool causal, bool heavy_high, int& tile, int& bh) {
+  bh = L % nbh;
+  const int j = L / nbh;
+  int rank;  // 0 = heaviest
+  if (!causal) {
+    tile = j;
+    return;
   }
-  return p;
+  if (ntile % 2 == 0) {
+    const int h = ntile / 2;
+    rank = j < h ? j : ntile - 1 - (j - h);
+  } else {
+    rank = j;
+  }
+  tile = heavy_high ? ntile - 1 - rank : rank;
 }
 
+// K tile (64 keys x D, rows of qkv) and V^T tile (D x 64 keys, rows of qkvT),
+// fetched into registers one step ahead of their use
+template <int D>
+struct KVFetch {
+  static constexpr int NK = 64 * D / 8 / 256, NV = D * 8 / 256;
+  u32x4 k[NK], v[NV];
+  MTB_DEV void load(const bf16_t* __restrict__ kp, size_t ldq, const bf16_t* __restrict__ vtp,
+                    size_t S, int tid) {
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int q = tid + 256 * i, row = q / (D / 8), c = q % (D / 8);
+      k[i] = *reinterpret_cast<const u32x4*>(kp + (size_t)row * ldq + c * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int q = tid + 256 * i, row = q >> 3, c = q & 7;
+      v[i] = *reinterpret_cast<const u32x4*>(vtp + (size_t)row * S + c * 8);
+    }
+  }
+  MTB_DEV void store(bf16_t* sK, bf16_t* sV, int tid) const {
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int q = tid + 256 * i, row = q / (D / 8), c = q % (D / 8);
+      *reinterpret_cast<u32x4*>(sK + row * D + ((c ^ swz(row)) << 3)) = k[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int q = tid + 256 * i, row = q >> 3, c = q & 7;
+      const int p1 = (c >> 1) * 16 + (c & 1) * 4, p2 = p1 + 8;
+      u32x2 lo = {v[i][0], v[i][1]}, hi = {v[i][2], v[i][3]};
+      *reinterpret_cast<u32x2*>(sV + row * 64 + (((p1 >> 3) ^ swz(row)) << 3) + (p1 & 7)) = lo;
+      *reinterpret_cast<u32x2*>(sV + row * 64 + (((p2 >> 3) ^ swz(row)) << 3) + (p2 & 7)) = hi;
+    }
+  }
+};
+
+// two 16-row k-steps of a 32x32 accumulator as bf16 B operands:
+// step 0 = rows {4lg..4lg+3, 8+4lg..}, step 1 = rows {16+4lg.., 24+4lg..}
+MTB_DEV void pack_half(const float (&a)[16], bf16x8& p0, bf16x8& p1) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    p0[r] = (__bf16)a[r];
+    p0[4 + r] = (__bf16)a[4 + r];
+    p1[r] = (__bf16)a[8 + r];
+    p1[4 + r] = (__bf16)a[12 + r];
+  }
+}
+
+// Forward. Workgroup = 64 queries of one (batch, q head); wavefront w takes
+// query half w & 1 and key half w >> 1 of every 64-key tile, keeps its own
+// online-softmax state, and the two key halves are merged at the end.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void attn_fwd_kernel(int S, int nq, int nkv, int ldq,
-                                                       const bf16_t* __restrict__ qkv,
-                                                       const bf16_t* __restrict__ qkvT,
-                                                       bf16_t* __restrict__ O,
-                                                       float* __restrict__ lse, float sl2) {
-  __shared__ __attribute__((aligned(16))) bf16_t sK[64 * D];
-  __shared__ __attribute__((aligned(16))) bf16_t sV[D * 64];
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(int S, int nq, int nkv, int ldq,
+                                                          const bf16_t* __restrict__ qkv,
+                                                          const bf16_t* __restrict__ qkvT,
+                                                          bf16_t* __restrict__ O,
+                                                          float* __restrict__ lse, float sl2) {
+  __shared__ __attribute__((aligned(16))) bf16_t smem[4 * 64 * D];  // 2 stages of K, V^T
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lg = lane >> 5;
-  const int qb = CAUSAL ? (gridDim.x - 1 - blockIdx.x) : blockIdx.x;  // heavy tiles first
-  const int hq = blockIdx.y, b = blockIdx.z, hk = hq / (nq / nkv);
-  const int q0 = qb * 128 + wave * 32;
-  const bool active = q0 < S;
-  const size_t tok0 = (size_t)b * S;
+  const int qh = wave & 1, kh = wave >> 1;
+  const int ntile = S / 64, nbh = gridDim.x / ntile;
+  int qb, bh;
+  tile_order(blockIdx.x, ntile, nbh, CAUSAL, true, qb, bh);
+  const int b = bh / nq, hq = bh % nq, hk = hq / (nq / nkv);
+  const int q0 = qb * 64 + qh * 32;
   const int qi = q0 + (lane & 31);
+  const size_t tok0 = (size_t)b * S;
 
   bf16x8 qf[D / 16];
   {
-    const bf16_t* qp = qkv + (tok0 + min(qi, S - 1)) * ldq + hq * D + 8 * lg;
+    const bf16_t* qp = qkv + (tok0 + qi) * ldq + hq * D + 8 * lg;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qp + kk * 16);
   }
@@ -113,88 +175,112 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(int S, int nq, int nkv, i
   for (int i = 0; i < D / 32; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
-  float m_i = kNegInf, l_i = 0.f;
+  float m_i = kNegInf, l_i = 0.f;  // l_i: this lane's keys only, summed with lane ^ 32 at the end
 
   const bf16_t* kbase = qkv + tok0 * ldq + (size_t)(nq + hk) * D;
   const bf16_t* vtbase = qkvT + ((size_t)b * ldq + (size_t)(nq + nkv + hk) * D) * S;
-  const int kend = CAUSAL ? min(S, qb * 128 + 128) : S;
-  const int qlast = q0 + 31;
+  const int ntk = CAUSAL ? qb + 1 : ntile;
+  KVFetch<D> pf;
+  pf.load(kbase, ldq, vtbase, S, tid);
+  pf.store(smem, smem + 64 * D, tid);
+  __syncthreads();
 
-  for (int k0 = 0; k0 < kend; k0 += 64) {
-    __syncthreads();
-    lds_rows<64, D>(sK, kbase + (size_t)k0 * ldq, ldq, tid);
-    lds_tposed<D>(sV, vtbase + k0, S, tid);
-    __syncthreads();
-    if (!active || (CAUSAL && k0 > qlast)) continue;
-
-    f32x16 s[2];
+  for (int t = 0; t < ntk; ++t) {
+    bf16_t* sK = smem + (t & 1) * 128 * D;
+    bf16_t* sV = sK + 64 * D;
+    if (t + 1 < ntk) pf.load(kbase + (size_t)(t + 1) * 64 * ldq, ldq, vtbase + (t + 1) * 64, S, tid);
+    const int ks = t * 64 + kh * 32;
+    if (!CAUSAL || ks <= q0 + 31) {
+      f32x16 sa, sb;
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
+      for (int r = 0; r < 16; ++r) { sa[r] = 0.f; sb[r] = 0.f; }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[f][r] = 0.f;
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const bf16x8 kf = frag<D>(sK, kh * 32 + (lane & 31), 2 * kk + lg);
+        if (kk & 1) sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sb, 0, 0, 0);
+        else sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sa, 0, 0, 0);
+      }
+      // s[j]: key ks + 8(j>>2) + 4lg + (j&3), query qi
+      float s[16];
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
+      for (int j = 0; j < 16; ++j) s[j] = sa[j] + sb[j];
+      if (CAUSAL && ks + 31 > q0) {
 #pragma unroll
-      for (int f = 0; f < 2; ++f)
-        s[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            frag<D>(sK, f * 32 + (lane & 31), 2 * kk + lg), qf[kk], s[f], 0, 0, 0);
-
-    // s[f][j]: key k0 + 32f + 8(j>>2) + 4lg + (j&3), query qi
-    float mx = kNegInf;
+        for (int j = 0; j < 16; ++j)
+          if (ks + 8 * (j >> 2) + 4 * lg + (j & 3) > qi) s[j] = kNegInf;
+      }
+      float mx = s[0];
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
+      for (int j = 1; j < 16; ++j) mx = fmaxf(mx, s[j]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mnew = fmaxf(m_i, mx * sl2);
+      const float mref = mnew == kNegInf ? 0.f : mnew;
+      const float alpha = exp2_fast(m_i - mref);
+      float ls = 0.f;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        float z = s[f][j] * sl2;
-        if (CAUSAL) {
-          const int key = k0 + 32 * f + 8 * (j >> 2) + 4 * lg + (j & 3);
-          if (key > qi) z = kNegInf;
-        }
-        s[f][j] = z;
-        mx = fmaxf(mx, z);
+        s[j] = exp2_fast(fmaf(s[j], sl2, -mref));
+        ls += s[j];
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mnew = fmaxf(m_i, mx);
-    const float alpha = (m_i == kNegInf) ? 0.f : exp2_fast(m_i - mnew);
-    float ls = 0.f;
+      l_i = l_i * alpha + ls;
+      m_i = mnew;
+      if (__any(alpha != 1.0f)) {
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
+        for (int i = 0; i < D / 32; ++i)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float p = exp2_fast(s[f][j] - mnew);
-        s[f][j] = p;
-        ls += p;
+          for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
       }
-    ls += __shfl_xor(ls, 32, 64);
-    l_i = l_i * alpha + ls;
-    m_i = mnew;
+      bf16x8 p0, p1;
+      pack_half(s, p0, p1);
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
-
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const bf16x8 pf = pack_step(s, t);
-#pragma unroll
-      for (int df = 0; df < D / 32; ++df)
-        oacc[df] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            frag<64>(sV, df * 32 + (lane & 31), 2 * t + lg), pf, oacc[df], 0, 0, 0);
+      for (int df = 0; df < D / 32; ++df) {
+        const int row = df * 32 + (lane & 31);
+        oacc[df] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<64>(sV, row, 4 * kh + lg), p0,
+                                                           oacc[df], 0, 0, 0);
+        oacc[df] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<64>(sV, row, 4 * kh + 2 + lg), p1,
+                                                           oacc[df], 0, 0, 0);
+      }
     }
+    if (t + 1 < ntk) {
+      bf16_t* nK = smem + ((t + 1) & 1) * 128 * D;
+      pf.store(nK, nK + 64 * D, tid);
+    }
+    __syncthreads();
   }
-  if (!active || qi >= S) return;
-  const float inv = 1.0f / l_i;
-  bf16_t* op = O + (tok0 + qi) * (size_t)(nq * D) + hq * D;
+  l_i += __shfl_xor(l_i, 32, 64);
+
+  // merge the key halves: kh = 1 hands (m, l, O^T) to kh = 0 through LDS
+  constexpr int NR = D / 2;  // accumulator floats per lane
+  float* xo = reinterpret_cast<float*>(smem);
+  float* xm = xo + 2 * NR * 64;
+  if (kh == 1) {
 #pragma unroll
-  for (int df = 0; df < D / 32; ++df)
+    for (int df = 0; df < D / 32; ++df)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float v[4];
+      for (int r = 0; r < 16; ++r) xo[(qh * NR + df * 16 + r) * 64 + lane] = oacc[df][r];
+    xm[qh * 64 + lane] = m_i;
+    xm[128 + qh * 64 + lane] = l_i;
+  }
+  __syncthreads();
+  if (kh == 0) {
+    const float m1 = xm[qh * 64 + lane], l1 = xm[128 + qh * 64 + lane];
+    const float M = fmaxf(m_i, m1);
+    const float a0 = exp2_fast(m_i - M), a1 = exp2_fast(m1 - M);
+    const float L = l_i * a0 + l1 * a1;
+    const float inv = 1.0f / L;
+    bf16_t* op = O + (tok0 + qi) * (size_t)(nq * D) + hq * D;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = oacc[df][4 * i + r] * inv;
-      st4(op + df * 32 + 8 * i + 4 * lg, v);
-    }
-  if (lg == 0) lse[((size_t)b * nq + hq) * S + qi] = (m_i + __log2f(l_i)) * kLn2;
+    for (int df = 0; df < D / 32; ++df)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          v[r] = (oacc[df][4 * i + r] * a0 + xo[(qh * NR + df * 16 + 4 * i + r) * 64 + lane] * a1) * inv;
+        st4(op + df * 32 + 8 * i + 4 * lg, v);
+      }
+    if (lg == 0) lse[((size_t)b * nq + hq) * S + qi] = (M + __log2f(L)) * kLn2;
+  }
 }
 
 // D_i = sum_d dO[i][d] * O[i][d] per (token, head); lanes of a group of d/8
@@ -224,43 +310,44 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(int rows, int S, int 
   }
 }
 
+// dK, dV. Workgroup = 64 keys of one (batch, q head); wavefront w takes key
+// half w & 1 and query half w >> 1 of every 64-query tile. S = Q K^T puts a
+// key per lane, so P and dS feed dV^T += dO^T P^T and dK^T += Q^T dS^T
+// straight from registers; the two query halves are summed at the end.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
+__global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(
     int S, int nq, int nkv, int ldq, const bf16_t* __restrict__ qkv,
     const bf16_t* __restrict__ qkvT, const bf16_t* __restrict__ dO,
     const bf16_t* __restrict__ dOT, const float* __restrict__ lse,
     const float* __restrict__ Dbuf, bf16_t* __restrict__ dqkv, float* __restrict__ part, float sl2,
     float scale) {
-  __shared__ __attribute__((aligned(16))) bf16_t sQ[64 * D];
-  __shared__ __attribute__((aligned(16))) bf16_t sdO[64 * D];
-  __shared__ __attribute__((aligned(16))) bf16_t sQT[D * 64];
-  __shared__ __attribute__((aligned(16))) bf16_t sdOT[D * 64];
-  __shared__ __attribute__((aligned(16))) bf16_t sKw[128 * D];  // this workgroup's keys
-  __shared__ __attribute__((aligned(16))) bf16_t sVw[128 * D];
-  __shared__ float sL[64], sD[64];
+  __shared__ __attribute__((aligned(16))) bf16_t smem[4 * 64 * D];  // Q, dO, Q^T, dO^T tiles
+  __shared__ __attribute__((aligned(16))) float sL[64], sD[64];
+  bf16_t* sQ = smem;
+  bf16_t* sdO = smem + 64 * D;
+  bf16_t* sQT = smem + 128 * D;
+  bf16_t* sdOT = smem + 192 * D;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lg = lane >> 5;
-  const int kb = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
+  const int kh = wave & 1, qh = wave >> 1;
+  const int ntile = S / 64, nbh = gridDim.x / ntile;
+  int kb, bh;
+  tile_order(blockIdx.x, ntile, nbh, CAUSAL, false, kb, bh);
+  const int b = bh / nq, hq = bh % nq;
   const int g = nq / nkv, hk = hq / g;
-  const int kw0 = kb * 128 + wave * 32;
-  const bool active = kw0 < S;
-  const int key = kw0 + (lane & 31);
+  const int k0 = kb * 64 + kh * 32;
+  const int key = k0 + (lane & 31);
   const size_t tok0 = (size_t)b * S;
   const int ldo = nq * D;
 
-  // K and V rows of the workgroup's 128 keys (rows past S repeat the last key)
+  bf16x8 kf[D / 16], vf[D / 16];
   {
-    constexpr int CH = D / 8, N = 128 * CH / 256;
+    const size_t kr = (tok0 + key) * ldq + 8 * lg;
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int q = tid + 256 * i, row = q / CH, c = q % CH;
-      const size_t tr = (tok0 + min(kb * 128 + row, S - 1)) * ldq + c * 8;
-      const u32x4 kv = *reinterpret_cast<const u32x4*>(qkv + tr + (size_t)(nq + hk) * D);
-      const u32x4 vv = *reinterpret_cast<const u32x4*>(qkv + tr + (size_t)(nq + nkv + hk) * D);
-      *reinterpret_cast<u32x4*>(sKw + row * D + ((c ^ swz(row)) << 3)) = kv;
-      *reinterpret_cast<u32x4*>(sVw + row * D + ((c ^ swz(row)) << 3)) = vv;
+    for (int kk = 0; kk < D / 16; ++kk) {
+      kf[kk] = *reinterpret_cast<const bf16x8*>(qkv + kr + (size_t)(nq + hk) * D + kk * 16);
+      vf[kk] = *reinterpret_cast<const bf16x8*>(qkv + kr + (size_t)(nq + nkv + hk) * D + kk * 16);
     }
   }
-  const int krow = wave * 32 + (lane & 31);
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i)
@@ -273,96 +360,96 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
   const bf16_t* dotbase = dOT + ((size_t)b * ldo + (size_t)hq * D) * S;
   const float* lrow = lse + ((size_t)b * nq + hq) * S;
   const float* drow = Dbuf + ((size_t)b * nq + hq) * S;
-  const int qstart = CAUSAL ? kb * 128 : 0;
 
-  for (int q0 = qstart; q0 < S; q0 += 64) {
+  for (int qt = CAUSAL ? kb : 0; qt < ntile; ++qt) {
+    const int qt0 = qt * 64;
     __syncthreads();
-    lds_rows<64, D>(sQ, qbase + (size_t)q0 * ldq, ldq, tid);
-    lds_rows<64, D>(sdO, dobase + (size_t)q0 * ldo, ldo, tid);
-    lds_tposed<D>(sQT, qtbase + q0, S, tid);
-    lds_tposed<D>(sdOT, dotbase + q0, S, tid);
+    lds_rows<64, D>(sQ, qbase + (size_t)qt0 * ldq, ldq, tid);
+    lds_rows<64, D>(sdO, dobase + (size_t)qt0 * ldo, ldo, tid);
+    lds_tposed<D>(sQT, qtbase + qt0, S, tid);
+    lds_tposed<D>(sdOT, dotbase + qt0, S, tid);
     if (tid < 64) {
-      sL[tid] = lrow[q0 + tid] * kLog2e;
-      sD[tid] = drow[q0 + tid];
+      sL[tid] = lrow[qt0 + tid] * kLog2e;
+      sD[tid] = drow[qt0 + tid];
     }
     __syncthreads();
-    if (!active || (CAUSAL && q0 + 63 < kw0)) continue;
+    const int qw0 = qt0 + qh * 32;
+    if (CAUSAL && qw0 + 31 < k0) continue;
 
-    f32x16 s[2], dp[2];
+    f32x16 s, dp;
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) { s[f][r] = 0.f; dp[f][r] = 0.f; }
+    for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      const bf16x8 kf = frag<D>(sKw, krow, 2 * kk + lg);
-      const bf16x8 vf = frag<D>(sVw, krow, 2 * kk + lg);
+      const int row = qh * 32 + (lane & 31);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<D>(sQ, row, 2 * kk + lg), kf[kk], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<D>(sdO, row, 2 * kk + lg), vf[kk], dp, 0, 0, 0);
+    }
+    // element j: query qw0 + 8(j>>2) + 4lg + (j&3), key `key`
+    float p[16], ds[16];
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        s[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<D>(sQ, f * 32 + (lane & 31), 2 * kk + lg),
-                                                       kf, s[f], 0, 0, 0);
-        dp[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            frag<D>(sdO, f * 32 + (lane & 31), 2 * kk + lg), vf, dp[f], 0, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      const int ql = qh * 32 + 8 * i + 4 * lg;
+      const f32x4 L4 = *reinterpret_cast<const f32x4*>(sL + ql);
+      const f32x4 D4 = *reinterpret_cast<const f32x4*>(sD + ql);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 4 * i + r;
+        float pv = exp2_fast(fmaf(s[j], sl2, -L4[r]));
+        if (CAUSAL && key > qt0 + ql + r) pv = 0.f;
+        p[j] = pv;
+        ds[j] = pv * (dp[j] - D4[r]);
       }
     }
-    // s[f][j]: query q0 + 32f + 8(j>>2) + 4lg + (j&3), key `key`
-#pragma unroll
-    for (int f = 0; f < 2; ++f)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int ql = 32 * f + 8 * (j >> 2) + 4 * lg + (j & 3);
-        float p = exp2_fast(s[f][j] * sl2 - sL[ql]);
-        if (CAUSAL && key > q0 + ql) p = 0.f;
-        s[f][j] = p;
-        dp[f][j] = p * (dp[f][j] - sD[ql]);
-      }
-    bf16x8 pf[4], sf[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      pf[t] = pack_step(s, t);
-      sf[t] = pack_step(dp, t);
-    }
+    bf16x8 p0, p1, d0, d1;
+    pack_half(p, p0, p1);
+    pack_half(ds, d0, d1);
 #pragma unroll
     for (int df = 0; df < D / 32; ++df) {
       const int row = df * 32 + (lane & 31);
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        dv[df] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<64>(sdOT, row, 2 * t + lg), pf[t],
-                                                         dv[df], 0, 0, 0);
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        dk[df] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<64>(sQT, row, 2 * t + lg), sf[t],
-                                                         dk[df], 0, 0, 0);
+      dv[df] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<64>(sdOT, row, 4 * qh + lg), p0, dv[df], 0, 0, 0);
+      dv[df] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<64>(sdOT, row, 4 * qh + 2 + lg), p1, dv[df], 0, 0, 0);
+      dk[df] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<64>(sQT, row, 4 * qh + lg), d0, dk[df], 0, 0, 0);
+      dk[df] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<64>(sQT, row, 4 * qh + 2 + lg), d1, dk[df], 0, 0, 0);
     }
   }
-  if (!active || key >= S) return;
-  // dk[df][4i + r]: d = 32 df + 8i + 4lg + r for key `key`
-  if (g == 1) {
-    bf16_t* dkp = dqkv + (tok0 + key) * ldq + (size_t)(nq + hk) * D;
-    bf16_t* dvp = dqkv + (tok0 + key) * ldq + (size_t)(nq + nkv + hk) * D;
+  // sum the two query halves: qh = 1 hands its accumulators to qh = 0
+  __syncthreads();
+  constexpr int NR = D / 2;
+  float* xo = reinterpret_cast<float*>(smem);  // [kh][dk|dv][NR][64]
+  if (qh == 1) {
 #pragma unroll
     for (int df = 0; df < D / 32; ++df)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float a[4], c[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) { a[r] = dk[df][4 * i + r] * scale; c[r] = dv[df][4 * i + r]; }
-        st4(dkp + df * 32 + 8 * i + 4 * lg, a);
-        st4(dvp + df * 32 + 8 * i + 4 * lg, c);
-      }
-  } else {
-    float* pp = part + (((size_t)b * nq + hq) * S + key) * (2 * D);
-#pragma unroll
-    for (int df = 0; df < D / 32; ++df)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float a[4], c[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) { a[r] = dk[df][4 * i + r] * scale; c[r] = dv[df][4 * i + r]; }
-        st4(pp + df * 32 + 8 * i + 4 * lg, a);
-        st4(pp + D + df * 32 + 8 * i + 4 * lg, c);
+      for (int r = 0; r < 16; ++r) {
+        xo[((kh * 2 + 0) * NR + df * 16 + r) * 64 + lane] = dk[df][r];
+        xo[((kh * 2 + 1) * NR + df * 16 + r) * 64 + lane] = dv[df][r];
       }
   }
+  __syncthreads();
+  if (qh == 1) return;
+  // dk[df][4i + r]: d = 32 df + 8i + 4lg + r for key `key`
+#pragma unroll
+  for (int df = 0; df < D / 32; ++df)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float a[4], c[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = df * 16 + 4 * i + r;
+        a[r] = (dk[df][4 * i + r] + xo[((kh * 2 + 0) * NR + j) * 64 + lane]) * scale;
+        c[r] = dv[df][4 * i + r] + xo[((kh * 2 + 1) * NR + j) * 64 + lane];
+      }
+      const int d = df * 32 + 8 * i + 4 * lg;
+      if (g == 1) {
+        st4(dqkv + (tok0 + key) * ldq + (size_t)(nq + hk) * D + d, a);
+        st4(dqkv + (tok0 + key) * ldq + (size_t)(nq + nkv + hk) * D + d, c);
+      } else {
+        float* pp = part + (((size_t)b * nq + hq) * S + key) * (2 * D);
+        st4(pp + d, a);
+        st4(pp + D + d, c);
+      }
+    }
 }
 
 // sum the g q-head contributions of each kv head (GQA) into dqkv
@@ -394,37 +481,42 @@ __global__ __launch_bounds__(256) void attn_dkv_reduce_kernel(int B, int S, int 
   st8(dqkv + ((size_t)b * S + s) * ldq + col, acc);
 }
 
+// dQ. Workgroup = 64 queries of one (batch, q head); wavefront w takes query
+// half w & 1 and key half w >> 1 of every 64-key tile (S^T layout: a query
+// per lane); the key halves are summed at the end.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     int S, int nq, int nkv, int ldq, const bf16_t* __restrict__ qkv,
     const bf16_t* __restrict__ qkvT, const bf16_t* __restrict__ dO,
     const float* __restrict__ lse, const float* __restrict__ Dbuf, bf16_t* __restrict__ dqkv,
     float sl2, float scale) {
-  __shared__ __attribute__((aligned(16))) bf16_t sK[64 * D];
-  __shared__ __attribute__((aligned(16))) bf16_t sV[64 * D];
-  __shared__ __attribute__((aligned(16))) bf16_t sKT[D * 64];
+  __shared__ __attribute__((aligned(16))) bf16_t smem[3 * 64 * D];  // K, V, K^T tiles
+  bf16_t* sK = smem;
+  bf16_t* sV = smem + 64 * D;
+  bf16_t* sKT = smem + 128 * D;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lg = lane >> 5;
-  const int qb = CAUSAL ? (gridDim.x - 1 - blockIdx.x) : blockIdx.x;
-  const int hq = blockIdx.y, b = blockIdx.z, hk = hq / (nq / nkv);
-  const int q0 = qb * 128 + wave * 32;
-  const bool active = q0 < S;
+  const int qh = wave & 1, kh = wave >> 1;
+  const int ntile = S / 64, nbh = gridDim.x / ntile;
+  int qb, bh;
+  tile_order(blockIdx.x, ntile, nbh, CAUSAL, true, qb, bh);
+  const int b = bh / nq, hq = bh % nq, hk = hq / (nq / nkv);
+  const int q0 = qb * 64 + qh * 32;
   const int qi = q0 + (lane & 31);
-  const int qc = min(qi, S - 1);
   const size_t tok0 = (size_t)b * S;
   const int ldo = nq * D;
 
   bf16x8 qf[D / 16], of[D / 16];
   {
-    const bf16_t* qp = qkv + (tok0 + qc) * ldq + hq * D + 8 * lg;
-    const bf16_t* dp = dO + (tok0 + qc) * ldo + hq * D + 8 * lg;
+    const bf16_t* qp = qkv + (tok0 + qi) * ldq + hq * D + 8 * lg;
+    const bf16_t* gp = dO + (tok0 + qi) * ldo + hq * D + 8 * lg;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       qf[kk] = *reinterpret_cast<const bf16x8*>(qp + kk * 16);
-      of[kk] = *reinterpret_cast<const bf16x8*>(dp + kk * 16);
+      of[kk] = *reinterpret_cast<const bf16x8*>(gp + kk * 16);
     }
   }
-  const float Lq = lse[((size_t)b * nq + hq) * S + qc] * kLog2e;
-  const float Dq = Dbuf[((size_t)b * nq + hq) * S + qc];
+  const float Lq = lse[((size_t)b * nq + hq) * S + qi] * kLog2e;
+  const float Dq = Dbuf[((size_t)b * nq + hq) * S + qi];
   f32x16 dq[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i)
@@ -434,52 +526,56 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   const bf16_t* kbase = qkv + tok0 * ldq + (size_t)(nq + hk) * D;
   const bf16_t* vbase = qkv + tok0 * ldq + (size_t)(nq + nkv + hk) * D;
   const bf16_t* ktbase = qkvT + ((size_t)b * ldq + (size_t)(nq + hk) * D) * S;
-  const int kend = CAUSAL ? min(S, qb * 128 + 128) : S;
-  const int qlast = q0 + 31;
+  const int ntk = CAUSAL ? qb + 1 : ntile;
 
-  for (int k0 = 0; k0 < kend; k0 += 64) {
+  for (int t = 0; t < ntk; ++t) {
+    const int k0 = t * 64;
     __syncthreads();
     lds_rows<64, D>(sK, kbase + (size_t)k0 * ldq, ldq, tid);
     lds_rows<64, D>(sV, vbase + (size_t)k0 * ldq, ldq, tid);
     lds_tposed<D>(sKT, ktbase + k0, S, tid);
     __syncthreads();
-    if (!active || (CAUSAL && k0 > qlast)) continue;
+    const int ks = k0 + kh * 32;
+    if (CAUSAL && ks > q0 + 31) continue;
 
-    f32x16 s[2], dp[2];
+    f32x16 s, dp;
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
+    for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) { s[f][r] = 0.f; dp[f][r] = 0.f; }
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const int row = kh * 32 + (lane & 31);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<D>(sK, row, 2 * kk + lg), qf[kk], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<D>(sV, row, 2 * kk + lg), of[kk], dp, 0, 0, 0);
+    }
+    // element j: key ks + 8(j>>2) + 4lg + (j&3), query qi
+    float ds[16];
+    const bool diag = CAUSAL && ks + 31 > q0;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
+    for (int j = 0; j < 16; ++j) {
+      float pv = exp2_fast(fmaf(s[j], sl2, -Lq));
+      if (diag && ks + 8 * (j >> 2) + 4 * lg + (j & 3) > qi) pv = 0.f;
+      ds[j] = pv * (dp[j] - Dq);
+    }
+    bf16x8 d0, d1;
+    pack_half(ds, d0, d1);
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        s[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<D>(sK, f * 32 + (lane & 31), 2 * kk + lg),
-                                                       qf[kk], s[f], 0, 0, 0);
-        dp[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            frag<D>(sV, f * 32 + (lane & 31), 2 * kk + lg), of[kk], dp[f], 0, 0, 0);
-      }
-#pragma unroll
-    for (int f = 0; f < 2; ++f)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        float p = exp2_fast(s[f][j] * sl2 - Lq);
-        if (CAUSAL) {
-          const int key = k0 + 32 * f + 8 * (j >> 2) + 4 * lg + (j & 3);
-          if (key > qi) p = 0.f;
-        }
-        dp[f][j] = p * (dp[f][j] - Dq);
-      }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const bf16x8 sf = pack_step(dp, t);
-#pragma unroll
-      for (int df = 0; df < D / 32; ++df)
-        dq[df] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<64>(sKT, df * 32 + (lane & 31), 2 * t + lg),
-                                                         sf, dq[df], 0, 0, 0);
+    for (int df = 0; df < D / 32; ++df) {
+      const int row = df * 32 + (lane & 31);
+      dq[df] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<64>(sKT, row, 4 * kh + lg), d0, dq[df], 0, 0, 0);
+      dq[df] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<64>(sKT, row, 4 * kh + 2 + lg), d1, dq[df], 0, 0, 0);
     }
   }
-  if (!active || qi >= S) return;
+  __syncthreads();
+  constexpr int NR = D / 2;
+  float* xo = reinterpret_cast<float*>(smem);  // [qh][NR][64]
+  if (kh == 1) {
+#pragma unroll
+    for (int df = 0; df < D / 32; ++df)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xo[(qh * NR + df * 16 + r) * 64 + lane] = dq[df][r];
+  }
+  __syncthreads();
+  if (kh == 1) return;
   bf16_t* op = dqkv + (tok0 + qi) * ldq + (size_t)hq * D;
 #pragma unroll
   for (int df = 0; df < D / 32; ++df)
@@ -487,7 +583,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
     for (int i = 0; i < 4; ++i) {
       float v[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = dq[df][4 * i + r] * scale;
+      for (int r = 0; r < 4; ++r)
+        v[r] = (dq[df][4 * i + r] + xo[(qh * NR + df * 16 + 4 * i + r) * 64 + lane]) * scale;
       st4(op + df * 32 + 8 * i + 4 * lg, v);
     }
 }
@@ -612,7 +709,7 @@ template <int D>
 hipError_t attn_fwd_bf16(int B, int S, int nq, int nkv, int causal, const void* qkv,
                          const void* qkvT, void* O, float* lse, hipStream_t st) {
   const int ldq = (nq + 2 * nkv) * D;
-  dim3 grid((S + 127) / 128, nq, B);
+  dim3 grid((S / 64) * B * nq);
   const float sl2 = kLog2e / sqrtf((float)D);
   if (causal)
     hipLaunchKernelGGL((attn_fwd_kernel<D, true>), grid, dim3(256), 0, st, S, nq, nkv, ldq,
@@ -632,7 +729,7 @@ hipError_t attn_bwd_bf16(int B, int S, int nq, int nkv, int causal, const void* 
   const int rows = B * S * nq;
   hipLaunchKernelGGL((attn_bwd_pre_kernel<bf16_t, D>), dim3((rows * (D / 8) + 255) / 256),
                      dim3(256), 0, st, rows, S, nq, (const bf16_t*)O, (const bf16_t*)dO, Dbuf);
-  dim3 grid((S + 127) / 128, nq, B);
+  dim3 grid((S / 64) * B * nq);
 #define MTB_BWD(C)                                                                            \
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, C>), grid, dim3(256), 0, st, S, nq, nkv, ldq,  \
                      (const bf16_t*)qkv, (const bf16_t*)qkvT, (const bf16_t*)dO,             \

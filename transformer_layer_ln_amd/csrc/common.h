@@ -16,17 +16,16 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 MTB_DEV float bf2f(bf16_t v) { return __uint_as_float((uint32_t)v << 16); }
 
-// fp32 -> bf16, round to nearest even (finite inputs; NaN stays NaN).
-MTB_DEV bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u) return (bf16_t)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
-}
+// fp32 -> bf16, round to nearest even (gfx950: one v_cvt_pk_bf16_f32)
+MTB_DEV bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 
 // two fp32 -> packed bf16 pair (lo in bits 0..15)
 MTB_DEV uint32_t pack2(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  bf16x2_t v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
 }
 MTB_DEV float lo_f(uint32_t p) { return __uint_as_float(p << 16); }
 MTB_DEV float hi_f(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }

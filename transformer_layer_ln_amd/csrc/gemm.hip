@@ -1,7 +1,7 @@
 // GEMMs of the block: C[m][n] = sum_k A(m,k) B(n,k) with fused epilogues.
 //
-// bf16 path: gfx950 MFMA v_mfma_f32_32x32x16_bf16, 256 threads = 2x2
-// wavefronts, block tile BM x BN x 64, LDS double-buffered (one barrier per
+// bf16 path: gfx950 MFMA v_mfma_f32_32x32x16_bf16, a grid of 2x2, 2x4 or
+// 4x2 wavefronts per block, block tile BM x BN x 64, LDS double-buffered (one barrier per
 // k-step: the next tile is fetched into registers while the current one is
 // multiplied, then written to the other LDS buffer). Both operands sit in LDS
 // as [row][k] with k contiguous and 16-byte chunks XOR-swizzled by row, so a
@@ -31,15 +31,17 @@ constexpr int BK = 64;
 
 MTB_DEV int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
-// operand tile ROWS x BK from a matrix stored [rows][K] (k contiguous)
-template <int ROWS>
+// operand tile ROWS x BK from a matrix stored [rows][K] (k contiguous),
+// NT threads, 16-byte chunks
+template <int ROWS, int NT>
 struct TileKc {
-  static constexpr int NCH = ROWS * BK / 8 / 256;  // 16-byte chunks per thread
+  static constexpr int NCH = ROWS * BK / 8 / NT;
+  static_assert(ROWS * BK / 8 % NT == 0, "tile must split evenly over the threads");
   u32x4 r[NCH];
   MTB_DEV void load(const bf16_t* __restrict__ p, int ld, int row0, int rowmax, int k0, int tid) {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int q = tid + 256 * i, row = q >> 3, c = q & 7;
+      const int q = tid + NT * i, row = q >> 3, c = q & 7;
       const int gr = min(row0 + row, rowmax - 1);
       r[i] = *reinterpret_cast<const u32x4*>(p + (size_t)gr * ld + k0 + c * 8);
     }
@@ -47,7 +49,7 @@ struct TileKc {
   MTB_DEV void store(bf16_t* s, int tid) const {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int q = tid + 256 * i, row = q >> 3, c = q & 7;
+      const int q = tid + NT * i, row = q >> 3, c = q & 7;
       *reinterpret_cast<u32x4*>(s + row * BK + ((c ^ swz(row)) << 3)) = r[i];
     }
   }
@@ -55,14 +57,16 @@ struct TileKc {
 
 // operand tile ROWS x BK from a matrix stored [K][rows] (rows contiguous):
 // 4 (k) x 8 (rows) register blocks, transposed on the way to LDS
-template <int ROWS>
+template <int ROWS, int NT>
 struct TileMn {
-  static constexpr int IT = (ROWS / 8) * (BK / 4) / 256;
+  static constexpr int TOT = (ROWS / 8) * (BK / 4);  // 4x8 blocks in the tile
+  static constexpr int IT = (TOT + NT - 1) / NT;     // (threads past TOT idle)
   u32x4 r[IT][4];
   MTB_DEV void load(const bf16_t* __restrict__ p, int ld, int row0, int rowmax, int k0, int tid) {
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-      const int idx = tid + 256 * it;
+      const int idx = tid + NT * it;
+      if (TOT % NT != 0 && idx >= TOT) break;
       const int mc = idx % (ROWS / 8), k4 = idx / (ROWS / 8);
       const int gm = min(row0 + mc * 8, rowmax - 8);
 #pragma unroll
@@ -73,7 +77,8 @@ struct TileMn {
   MTB_DEV void store(bf16_t* s, int tid) const {
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-      const int idx = tid + 256 * it;
+      const int idx = tid + NT * it;
+      if (TOT % NT != 0 && idx >= TOT) break;
       const int mc = idx % (ROWS / 8), k4 = idx / (ROWS / 8);
       const int c = k4 >> 1, half = k4 & 1;
 #pragma unroll
@@ -154,16 +159,19 @@ MTB_DEV void epi4(const Epi& e, int m, int n, int N, float (&v)[4]) {
   }
 }
 
-template <int BM, int BN, bool AKC, bool BKC, int EPI>
-__global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(int M, int N, int K,
+// BM x BN block tile, WGM x WGN wavefronts (each WM x WN = FM x FN 32x32
+// fragments), OCC = wavefronts per SIMD the register budget must allow
+template <int BM, int BN, int WGM, int WGN, int OCC, bool AKC, bool BKC, int EPI>
+__global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(int M, int N, int K,
                                                            const bf16_t* __restrict__ A, int lda,
                                                            const bf16_t* __restrict__ B, int ldb,
                                                            Epi ep) {
-  constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
+  constexpr int NT = 64 * WGM * WGN;
+  constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32;
   __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * BK];
   __shared__ __attribute__((aligned(16))) bf16_t sB[2][BN * BK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
 
   // block -> tile: blocks i, i+8, i+16, ... share an XCD (and its L2), so
   // give each XCD a contiguous run of tiles, then walk GROUP tile-rows at a
@@ -179,8 +187,8 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(int M, int N, int K,
   const int tm = first_m + (bid % per_group) % gsz, tn = (bid % per_group) / gsz;
   const int m0 = tm * BM, n0 = tn * BN;
 
-  using LA = typename std::conditional<AKC, TileKc<BM>, TileMn<BM>>::type;
-  using LB = typename std::conditional<BKC, TileKc<BN>, TileMn<BN>>::type;
+  using LA = typename std::conditional<AKC, TileKc<BM, NT>, TileMn<BM, NT>>::type;
+  using LB = typename std::conditional<BKC, TileKc<BN, NT>, TileMn<BN, NT>>::type;
   LA la;
   LB lb;
   f32x16 acc[FM][FN];
@@ -352,13 +360,33 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(int M, int N, int K,
   }
 }
 
-template <int BM, int BN, bool AKC, bool BKC, int EPI>
+template <int BM, int BN, int WGM, int WGN, int OCC, bool AKC, bool BKC, int EPI>
+hipError_t launch_cfg(int M, int N, int K, const void* A, int lda, const void* B, int ldb,
+                      const Epi& e, hipStream_t st) {
+  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, OCC, AKC, BKC, EPI>), dim3(tiles),
+                     dim3(64 * WGM * WGN), 0, st, M, N, K, (const bf16_t*)A, lda,
+                     (const bf16_t*)B, ldb, e);
+  return hipGetLastError();
+}
+
+// Tile shape per problem (measured on MI355X over the block's GEMM shapes):
+// 256x256 with 2x4 wavefronts when the problem is large and deep enough to
+// fill the chip; for the weight gradients (both operands transposed in LDS)
+// 256x128 with 4x2 wavefronts; 128x128 with 2x2 wavefronts otherwise.
+template <bool AKC, bool BKC, int EPI>
 hipError_t launch_bf16(int M, int N, int K, const void* A, int lda, const void* B, int ldb,
                        const Epi& e, hipStream_t st) {
-  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, AKC, BKC, EPI>), dim3(tiles), dim3(256), 0, st, M,
-                     N, K, (const bf16_t*)A, lda, (const bf16_t*)B, ldb, e);
-  return hipGetLastError();
+  const long t256 = (long)((M + 255) / 256) * ((N + 255) / 256);
+  const long t256x128 = (long)((M + 255) / 256) * ((N + 127) / 128);
+  if constexpr (!AKC && !BKC) {
+    if (t256x128 >= 256 && K >= 1024)
+      return launch_cfg<256, 128, 4, 2, 1, AKC, BKC, EPI>(M, N, K, A, lda, B, ldb, e, st);
+  } else {
+    if (t256 >= 128 && K >= 1024)
+      return launch_cfg<256, 256, 2, 4, 1, AKC, BKC, EPI>(M, N, K, A, lda, B, ldb, e, st);
+  }
+  return launch_cfg<128, 128, 2, 2, 2, AKC, BKC, EPI>(M, N, K, A, lda, B, ldb, e, st);
 }
 
 }  // namespace
@@ -382,22 +410,22 @@ hipError_t gemm(int dtype, int M, int N, int K, const void* A, int lda, bool a_k
   // bf16: K % 64 == 0, M % 8 == 0, N % 8 == 0 (checked by the caller)
   if (a_kc && b_kc) {
     switch (e.kind) {
-      case EPI_STORE: return launch_bf16<128, 128, true, true, EPI_STORE>(M, N, K, A, lda, B, ldb, e, st);
-      case EPI_GELU: return launch_bf16<128, 128, true, true, EPI_GELU>(M, N, K, A, lda, B, ldb, e, st);
-      case EPI_SWIGLU: return launch_bf16<128, 128, true, true, EPI_SWIGLU>(M, N, K, A, lda, B, ldb, e, st);
+      case EPI_STORE: return launch_bf16<true, true, EPI_STORE>(M, N, K, A, lda, B, ldb, e, st);
+      case EPI_GELU: return launch_bf16<true, true, EPI_GELU>(M, N, K, A, lda, B, ldb, e, st);
+      case EPI_SWIGLU: return launch_bf16<true, true, EPI_SWIGLU>(M, N, K, A, lda, B, ldb, e, st);
       default: return hipErrorInvalidValue;
     }
   }
   if (a_kc && !b_kc) {
     switch (e.kind) {
-      case EPI_STORE: return launch_bf16<128, 128, true, false, EPI_STORE>(M, N, K, A, lda, B, ldb, e, st);
-      case EPI_DGELU: return launch_bf16<128, 128, true, false, EPI_DGELU>(M, N, K, A, lda, B, ldb, e, st);
-      case EPI_DSWIGLU: return launch_bf16<128, 128, true, false, EPI_DSWIGLU>(M, N, K, A, lda, B, ldb, e, st);
+      case EPI_STORE: return launch_bf16<true, false, EPI_STORE>(M, N, K, A, lda, B, ldb, e, st);
+      case EPI_DGELU: return launch_bf16<true, false, EPI_DGELU>(M, N, K, A, lda, B, ldb, e, st);
+      case EPI_DSWIGLU: return launch_bf16<true, false, EPI_DSWIGLU>(M, N, K, A, lda, B, ldb, e, st);
       default: return hipErrorInvalidValue;
     }
   }
   if (!a_kc && !b_kc && e.kind == EPI_STORE)
-    return launch_bf16<128, 128, false, false, EPI_STORE>(M, N, K, A, lda, B, ldb, e, st);
+    return launch_bf16<false, false, EPI_STORE>(M, N, K, A, lda, B, ldb, e, st);
   return hipErrorInvalidValue;
 }
 
