@@ -8,14 +8,21 @@ GELU). Prints ONE JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                     [--workload seq2048|seq512|seq4096]
+    python bench.py --calibrate-copy MIB
 
 The default workload is the seq-2048 rank share (the metric's target
 configuration); --workload seq512 times the seq-512 TP=4 share (hidden 1024,
 4 heads x 64, ffn chunk 1024, batch 8) and seq4096 the SwiGLU/GQA share.
+
+--calibrate-copy runs only a plain device-to-device copy of MIB MiB, five
+times, so that rocprofv3's FETCH_SIZE / WRITE_SIZE counters can be scaled
+against a kernel whose HBM traffic is known (MIB MiB read + MIB MiB written
+per launch).
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -26,6 +33,53 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+
+# HBM bytes per fc1 launch from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE)
+# scaled by the same counters on a copy of known size; valid only while the
+# GEMM source is the one the counters were taken on.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fc1_gemm_gelu_seq2048_traffic.txt")
+GEMM_SOURCES = [os.path.join(ROOT, "transformer_layer_ln_amd", "csrc", f)
+                for f in ("gemm.hip", "common.h", "kernels.h")]
+
+
+def gemm_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """traffic_bytes_per_launch from the committed counter summary, or None
+    when there is none for this workload or the GEMM source has changed."""
+    if workload != "seq2048" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith(" "):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("gemm_source_sha256") != gemm_source_hash():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def calibrate_copy(mib):
+    import torch
+
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_mib": mib, "launches": 5, "bytes_read_per_launch": n * 4,
+                      "bytes_written_per_launch": n * 4}), flush=True)
 
 WORKLOADS = {
     "seq2048": ("C4", "TP=8 rank share of a hidden-4096 block: 4 local heads x 128, ffn chunk 2048, "
@@ -146,7 +200,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--workload", default="seq2048", choices=sorted(WORKLOADS))
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share; --gpus {args.gpus} is not supported "
               "(the other tensor-parallel ranks run the same kernels on their own GPUs)",
@@ -196,7 +254,8 @@ def main():
         "roofline": {"kernel": f"fc1 forward GEMM + {cfg.act} epilogue ({T} x {Fu} x {H})",
                      "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "avg_ms": round(fc1_ms, 5)},
+                     "traffic": measured_traffic(args.workload), "traffic_unit": "bytes/launch",
+                     "algorithmic_flops_per_launch": fc1_flops, "avg_ms": round(fc1_ms, 5)},
         "other_kernels": {
             "ln1_fwd": {"bound": "hbm", "avg_ms": round(ln_ms, 5),
                         "achieved_GBs": round(ln_bytes / (ln_ms * 1e-3) / 1e9, 1),

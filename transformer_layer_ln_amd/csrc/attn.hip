@@ -47,11 +47,11 @@ MTB_DEV void lds_rows(bf16_t* s, const bf16_t* __restrict__ g, size_t ld, int ti
   }
 }
 
-// D x 64 tile of a transposed matrix (D rows, 64 consecutive tokens each,
-// row pitch ld) -> LDS [d][64 keys] with the keys of every 16-group stored in
-// the order 0-3, 8-11, 4-7, 12-15: lane group g of an MFMA k-step then reads
-// keys {4g..4g+3, 8+4g..8+4g+3} -- the keys its accumulator layout holds --
-// as one 16-byte chunk.
+// D x 64 tile of a transposed matrix (D rows of 64 tokens, row pitch ld) ->
+// LDS [d][64 keys]. The tokens arrive already in the order 0-3, 8-11, 4-7,
+// 12-15 inside every 16 (the GEMM epilogue writes them so): lane group g of
+// an MFMA k-step then reads keys {4g..4g+3, 8+4g..8+4g+3} -- the keys its
+// accumulator layout holds -- as one 16-byte chunk.
 template <int D>
 MTB_DEV void lds_tposed(bf16_t* s, const bf16_t* __restrict__ g, size_t ld, int tid) {
   constexpr int N = D * 8 / 256;
@@ -59,10 +59,28 @@ MTB_DEV void lds_tposed(bf16_t* s, const bf16_t* __restrict__ g, size_t ld, int 
   for (int i = 0; i < N; ++i) {
     const int q = tid + 256 * i, row = q >> 3, c = q & 7;
     const u32x4 v = *reinterpret_cast<const u32x4*>(g + (size_t)row * ld + c * 8);
-    const int p1 = (c >> 1) * 16 + (c & 1) * 4, p2 = p1 + 8;
-    u32x2 lo = {v[0], v[1]}, hi = {v[2], v[3]};
-    *reinterpret_cast<u32x2*>(s + row * 64 + (((p1 >> 3) ^ swz(row)) << 3) + (p1 & 7)) = lo;
-    *reinterpret_cast<u32x2*>(s + row * 64 + (((p2 >> 3) ^ swz(row)) << 3) + (p2 & 7)) = hi;
+    *reinterpret_cast<u32x4*>(s + row * 64 + ((c ^ swz(row)) << 3)) = v;
+  }
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Direct-to-LDS copy of a ROWS x (CH 16-byte chunks) tile (row pitch ld
+// elements) into LDS [row][CH chunks] with the chunk index XOR-swizzled by
+// row, issued by the 4 wavefronts of the workgroup. Each load instruction
+// fills one contiguous KB of LDS (lane l -> bytes 16l..16l+15), so every
+// lane fetches the global chunk that belongs at its LDS position.
+template <int ROWS, int CH>
+MTB_DEV void dma_tile(bf16_t* lds, const bf16_t* __restrict__ g, size_t ld, int wave, int lane) {
+  constexpr int BLK = ROWS * CH / 64, PERW = BLK / 4, RPB = 64 / CH;
+  static_assert(BLK % 4 == 0, "tile must split over 4 wavefronts");
+#pragma unroll
+  for (int i = 0; i < PERW; ++i) {
+    const int b = wave * PERW + i;
+    const int row = b * RPB + lane / CH, pc = lane % CH;
+    const int c = pc ^ swz(row);
+    __builtin_amdgcn_global_load_lds((const void*)(g + (size_t)row * ld + c * 8),
+                                     (lds_ptr_t)(lds + b * 512), 16, 0, 0);
   }
 }
 
@@ -124,10 +142,7 @@ struct KVFetch {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int q = tid + 256 * i, row = q >> 3, c = q & 7;
-      const int p1 = (c >> 1) * 16 + (c & 1) * 4, p2 = p1 + 8;
-      u32x2 lo = {v[i][0], v[i][1]}, hi = {v[i][2], v[i][3]};
-      *reinterpret_cast<u32x2*>(sV + row * 64 + (((p1 >> 3) ^ swz(row)) << 3) + (p1 & 7)) = lo;
-      *reinterpret_cast<u32x2*>(sV + row * 64 + (((p2 >> 3) ^ swz(row)) << 3) + (p2 & 7)) = hi;
+      *reinterpret_cast<u32x4*>(sV + row * 64 + ((c ^ swz(row)) << 3)) = v[i];
     }
   }
 };

@@ -11,9 +11,17 @@
 // eight contiguous elements and writes eight rows of four k-values.
 //
 // The MFMA is issued as (B-fragment, A-fragment), i.e. it computes C^T, so
-// that each lane ends up holding 4 consecutive n of one row m: stores are
-// 8-byte (bf16) vectors and gate/up pairs of the SwiGLU interleave land in
-// the same lane.
+// that each lane ends up holding 4 consecutive n of one row m.
+//
+// Epilogue: the fp32 accumulator tile is staged in LDS (a chunk of rows at a
+// time, reusing the operand buffers) and then read back row-wise, so that
+// every global access of the epilogue -- bias, residual and derivative
+// inputs, the stored outputs -- is 16 bytes per lane over whole rows. Storing
+// straight from the MFMA layout touches 32 rows per instruction with 16 bytes
+// each; on MI355X those partial-line writes reach HBM several times over
+// (measured 3.5x the output bytes for the two-output GELU epilogue). The
+// per-batch transposed copy that attention reads is written from the same
+// staged tile by columns, 128 contiguous bytes per output row.
 //
 // Uses in the block ([TP-block] sec. 1-2; [MLM-notes] Column/RowParallelLinear):
 //   forward   Y = X W^T         A = X [T][in],  B = W [out][in]     (k-contig both)
@@ -105,57 +113,165 @@ MTB_DEV void ld4g(const void* p, size_t off, float (&v)[4]) {
   ld4(reinterpret_cast<const T*>(p) + off, v);
 }
 
-// epilogue for 4 consecutive columns n..n+3 of row m
-template <typename T, int EPI>
-MTB_DEV void epi4(const Epi& e, int m, int n, int N, float (&v)[4]) {
-  if constexpr (EPI == EPI_STORE || EPI == EPI_GELU) {
-    if (e.bias) {
-      float b[4];
-      ld4g<T>(e.bias, n, b);
+// fp32 path epilogue (plain store, optional bias and residual) for 4
+// consecutive columns n..n+3 of row m
+MTB_DEV void epi4_f32(const Epi& e, int m, int n, float (&v)[4]) {
+  if (e.bias) {
+    float b[4];
+    ld4g<float>(e.bias, n, b);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] += b[r];
+    for (int r = 0; r < 4; ++r) v[r] += b[r];
+  }
+  if (e.resid) {
+    float b[4];
+    ld4g<float>(e.resid, (size_t)m * e.ldr + n, b);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] += b[r];
+  }
+  st4(reinterpret_cast<float*>(e.out) + (size_t)m * e.ldo + n, v);
+}
+
+// 8 bf16 values at p + off -> floats, added to v
+MTB_DEV void add8(const void* p, size_t off, float (&v)[8]) {
+  float b[8];
+  ld8(reinterpret_cast<const bf16_t*>(p) + off, b);
+#pragma unroll
+  for (int r = 0; r < 8; ++r) v[r] += b[r];
+}
+MTB_DEV void out8(void* p, size_t off, const float (&v)[8]) {
+  st8(reinterpret_cast<bf16_t*>(p) + off, v);
+}
+
+// rows of the tile staged per epilogue chunk: BM halved until the fp32 chunk
+// fits the operand buffers (max_rows = their size in fp32 rows)
+constexpr int stage_rows(int bm, int max_rows) { return bm <= max_rows ? bm : stage_rows(bm / 2, max_rows); }
+
+// Staged fp32 tile: CR rows x BN columns, 16-byte chunks XOR-swizzled by row.
+template <int BN>
+struct Staged {
+  static constexpr int NCH = BN / 4;  // 16-byte chunks per row
+  float* s;
+  MTB_DEV int off(int r, int n) const { return r * BN + ((((n >> 2) ^ r) & (NCH - 1)) << 2) + (n & 3); }
+  MTB_DEV void put4(int r, int n, const f32x4& v) const { *reinterpret_cast<f32x4*>(s + off(r, n)) = v; }
+  MTB_DEV void get8(int r, int n, float (&v)[8]) const {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(s + off(r, n));
+    const f32x4 b = *reinterpret_cast<const f32x4*>(s + off(r, n + 4));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
+  }
+  MTB_DEV float get(int r, int n) const { return s[off(r, n)]; }
+};
+
+// Row phase of the epilogue for rows [0, CR) of the staged chunk whose first
+// row is global row mc: each work item is 8 consecutive columns of one row
+// (for SwiGLU, the 8 gate and the matching 8 up columns).
+template <int EPI, int BN, int CR, int NT>
+MTB_DEV void epi_rows(const Epi& e, const Staged<BN>& st, int M, int N, int mc, int n0, int tid) {
+  if constexpr (EPI == EPI_SWIGLU) {
+    // columns 32k..32k+15 are gate features 16k.., 32k+16..32k+31 the matching up features
+    constexpr int IPR = BN / 16;
+    for (int it = tid; it < CR * IPR; it += NT) {
+      const int r = it / IPR, c = it % IPR;
+      const int m = mc + r, nl = (c >> 1) * 32 + (c & 1) * 8, n = n0 + nl;
+      if (m >= M || n >= N) continue;
+      float g[8], u[8], o[8];
+      st.get8(r, nl, g);
+      st.get8(r, nl + 16, u);
+      if (e.bias) {
+        add8(e.bias, n, g);
+        add8(e.bias, n + 16, u);
+      }
+      // keep the stored pre-activations and the activation consistent
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        g[i] = bf2f(f2bf(g[i]));
+        u[i] = bf2f(f2bf(u[i]));
+        o[i] = g[i] * sigmoid_f(g[i]) * u[i];
+      }
+      const size_t ro = (size_t)m * e.ldo;
+      out8(e.out, ro + n, g);
+      out8(e.out, ro + n + 16, u);
+      out8(e.out2, (size_t)m * e.ldo2 + (n >> 5) * 16 + (n & 15), o);
+    }
+  } else {
+    constexpr int IPR = BN / 8;
+    for (int it = tid; it < CR * IPR; it += NT) {
+      const int r = it / IPR, nl = (it % IPR) * 8;
+      const int m = mc + r, n = n0 + nl;
+      if (m >= M || n >= N) continue;
+      float v[8];
+      st.get8(r, nl, v);
+      if constexpr (EPI == EPI_STORE) {
+        if (e.bias) add8(e.bias, n, v);
+        if (e.resid) add8(e.resid, (size_t)m * e.ldr + n, v);
+        out8(e.out, (size_t)m * e.ldo + n, v);
+      } else if constexpr (EPI == EPI_GELU) {
+        if (e.bias) add8(e.bias, n, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = bf2f(f2bf(v[i]));
+        out8(e.out, (size_t)m * e.ldo + n, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = gelu_f(v[i]);
+        out8(e.out2, (size_t)m * e.ldo2 + n, v);
+      } else if constexpr (EPI == EPI_DGELU) {
+        float u[8];
+        ld8(reinterpret_cast<const bf16_t*>(e.aux) + (size_t)m * e.ldaux + n, u);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] *= gelu_grad_f(u[i]);
+        out8(e.out, (size_t)m * e.ldo + n, v);
+      } else if constexpr (EPI == EPI_DSWIGLU) {
+        // v = dm at features n..n+7; their gate/up columns in the interleaved layout
+        const int gp = (n >> 4) * 32 + (n & 15);
+        float ug[8], uu[8], dg[8], du[8];
+        ld8(reinterpret_cast<const bf16_t*>(e.aux) + (size_t)m * e.ldaux + gp, ug);
+        ld8(reinterpret_cast<const bf16_t*>(e.aux) + (size_t)m * e.ldaux + gp + 16, uu);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float sg = sigmoid_f(ug[i]);
+          dg[i] = v[i] * uu[i] * sg * (1.0f + ug[i] * (1.0f - sg));
+          du[i] = v[i] * ug[i] * sg;
+        }
+        out8(e.out, (size_t)m * e.ldo + gp, dg);
+        out8(e.out, (size_t)m * e.ldo + gp + 16, du);
+      }
     }
   }
-  if constexpr (EPI == EPI_STORE) {
+}
+
+// Column phase: the per-batch transposed copy outT[b][n][s] of the stored
+// values. Inside every 16 tokens the order is 0-3, 8-11, 4-7, 12-15 (bits 2
+// and 3 of the token index swapped), the key order the attention kernels'
+// MFMA operands consume. 8 lanes cover 64 consecutive positions (128 bytes)
+// of one output row; each lane writes 8 positions = tokens {4h..4h+3,
+// 8+4h..8+4h+3} of one 16-token block.
+template <int BN, int CR, int NT>
+MTB_DEV void epi_cols(const Epi& e, const Staged<BN>& st, int M, int N, int mc, int n0, int tid) {
+  static_assert(CR % 64 == 0, "whole 64-token groups per chunk");
+  for (int it = tid; it < BN * CR / 8; it += NT) {
+    const int l8 = it & 7, nl = (it >> 3) % BN, g = (it >> 3) / BN;
+    const int n = n0 + nl, blk = g * 64 + (l8 >> 1) * 16, h = l8 & 1;
+    const int m = mc + blk;  // first token of the 16-token block
+    if (m >= M || n >= N) continue;
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = st.get(blk + 4 * h + i, nl);
+      v[4 + i] = st.get(blk + 8 + 4 * h + i, nl);
+    }
+    if (e.bias) {
+      const float b = bf2f(reinterpret_cast<const bf16_t*>(e.bias)[n]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] += b;
+    }
     if (e.resid) {
-      float b[4];
-      ld4g<T>(e.resid, (size_t)m * e.ldr + n, b);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] += b[r];
+      for (int i = 0; i < 4; ++i) {
+        v[i] += bf2f(reinterpret_cast<const bf16_t*>(e.resid)[(size_t)(m + 4 * h + i) * e.ldr + n]);
+        v[4 + i] += bf2f(reinterpret_cast<const bf16_t*>(e.resid)[(size_t)(m + 8 + 4 * h + i) * e.ldr + n]);
+      }
     }
-    st4(reinterpret_cast<T*>(e.out) + (size_t)m * e.ldo + n, v);
-    if (e.outT) {
-      const int bb = m / e.S, s = m % e.S;
-      T* o = reinterpret_cast<T*>(e.outT) + ((size_t)bb * N + n) * e.S + s;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) st_f(o + (size_t)r * e.S, v[r]);
-    }
-  } else if constexpr (EPI == EPI_GELU) {
-    st4(reinterpret_cast<T*>(e.out) + (size_t)m * e.ldo + n, v);
-    float a[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) a[r] = gelu_f(v[r]);
-    st4(reinterpret_cast<T*>(e.out2) + (size_t)m * e.ldo2 + n, a);
-  } else if constexpr (EPI == EPI_DGELU) {
-    float u[4];
-    ld4g<T>(e.aux, (size_t)m * e.ldaux + n, u);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) v[r] *= gelu_grad_f(u[r]);
-    st4(reinterpret_cast<T*>(e.out) + (size_t)m * e.ldo + n, v);
-  } else if constexpr (EPI == EPI_DSWIGLU) {
-    // v = dm at features n..n+3; gate/up positions in the interleaved layout
-    const int gp = (n >> 4) * 32 + (n & 15);
-    float ug[4], uu[4], dg[4], du[4];
-    ld4g<T>(e.aux, (size_t)m * e.ldaux + gp, ug);
-    ld4g<T>(e.aux, (size_t)m * e.ldaux + gp + 16, uu);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float s = sigmoid_f(ug[r]);
-      dg[r] = v[r] * uu[r] * s * (1.0f + ug[r] * (1.0f - s));
-      du[r] = v[r] * ug[r] * s;
-    }
-    st4(reinterpret_cast<T*>(e.out) + (size_t)m * e.ldo + gp, dg);
-    st4(reinterpret_cast<T*>(e.out) + (size_t)m * e.ldo + gp + 16, du);
+    const int bb = m / e.S, s = m % e.S + 8 * h;
+    out8(e.outT, ((size_t)bb * N + n) * e.S + s, v);
   }
 }
 
@@ -168,8 +284,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(int M, i
                                                            Epi ep) {
   constexpr int NT = 64 * WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32;
-  __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * BK];
-  __shared__ __attribute__((aligned(16))) bf16_t sB[2][BN * BK];
+  // operand double buffers; reused by the epilogue for the staged fp32 tile
+  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * (BM + BN) * BK];
+  auto sA = [&](int i) { return smem + i * (BM * BK); };
+  auto sB = [&](int i) { return smem + 2 * BM * BK + i * (BN * BK); };
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
 
@@ -202,8 +320,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(int M, i
   const int KT = K / BK;
   la.load(A, lda, m0, M, 0, tid);
   lb.load(B, ldb, n0, N, 0, tid);
-  la.store(sA[0], tid);
-  lb.store(sB[0], tid);
+  la.store(sA(0), tid);
+  lb.store(sB(0), tid);
   __syncthreads();
 
   for (int kt = 0; kt < KT; ++kt) {
@@ -212,8 +330,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(int M, i
       la.load(A, lda, m0, M, (kt + 1) * BK, tid);
       lb.load(B, ldb, n0, N, (kt + 1) * BK, tid);
     }
-    const bf16_t* as = sA[cur];
-    const bf16_t* bs = sB[cur];
+    const bf16_t* as = sA(cur);
+    const bf16_t* bs = sB(cur);
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       const int c = kk * 2 + (lane >> 5);
@@ -235,74 +353,41 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(int M, i
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
     }
     if (kt + 1 < KT) {
-      la.store(sA[cur ^ 1], tid);
-      lb.store(sB[cur ^ 1], tid);
+      la.store(sA(cur ^ 1), tid);
+      lb.store(sB(cur ^ 1), tid);
     }
     __syncthreads();
   }
 
-  // lane holds C[m][n..n+3] with m = (lane & 31), n = 8*i + 4*(lane >> 5) inside each 32x32 fragment
+  // Epilogue. lane holds C[m][n..n+3] with m = (lane & 31), n = 8q + 4(lane >> 5)
+  // inside each 32x32 fragment (register 4q + r -> column n + r). The tile
+  // goes through LDS CR rows at a time (the last k-step ended with a barrier,
+  // so the operand buffers are free).
+  constexpr int CR = stage_rows(BM, 2 * (BM + BN) * BK / 2 / BN);
+  static_assert(CR >= WM && BM % CR == 0 && CR % 64 == 0, "staging chunk");
+  const Staged<BN> st{reinterpret_cast<float*>(smem)};
+#pragma unroll 1
+  for (int c0 = 0; c0 < BM; c0 += CR) {
+    if (c0 > 0) __syncthreads();
+    if (wm * WM >= c0 && wm * WM < c0 + CR) {
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int m = m0 + wm * WM + i * 32 + (lane & 31);
-    if (m >= M) continue;
+      for (int i = 0; i < FM; ++i) {
+        const int r = wm * WM - c0 + i * 32 + (lane & 31);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int nf = n0 + wn * WN + j * 32;
-      if constexpr (EPI == EPI_SWIGLU) {
-        // columns nf..nf+15 are gate features f0..f0+15, nf+16..nf+31 the matching up features
-        if (nf >= N) continue;
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const int n = nf + 8 * q + 4 * (lane >> 5);
-          float g[4], u[4], o[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            g[r] = acc[i][j][4 * q + r];
-            u[r] = acc[i][j][4 * (q + 2) + r];
+          for (int q = 0; q < 4; ++q) {
+            const int n = wn * WN + j * 32 + 8 * q + 4 * (lane >> 5);
+            const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                             acc[i][j][4 * q + 3]};
+            st.put4(r, n, v);
           }
-          if (ep.bias) {
-            float bg[4], bu[4];
-            ld4g<bf16_t>(ep.bias, n, bg);
-            ld4g<bf16_t>(ep.bias, n + 16, bu);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) { g[r] += bg[r]; u[r] += bu[r]; }
-          }
-          // keep the stored pre-activations and the activation consistent
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            g[r] = bf2f(f2bf(g[r]));
-            u[r] = bf2f(f2bf(u[r]));
-            o[r] = g[r] * sigmoid_f(g[r]) * u[r];
-          }
-          bf16_t* uo = reinterpret_cast<bf16_t*>(ep.out) + (size_t)m * ep.ldo;
-          st4(uo + n, g);
-          st4(uo + n + 16, u);
-          const int f = (nf >> 1) + 8 * q + 4 * (lane >> 5);
-          st4(reinterpret_cast<bf16_t*>(ep.out2) + (size_t)m * ep.ldo2 + f, o);
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = nf + 8 * q + 4 * (lane >> 5);
-          if (n >= N) continue;
-          float v[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r];
-          if constexpr (EPI == EPI_GELU) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              if (ep.bias) v[r] += bf2f(reinterpret_cast<const bf16_t*>(ep.bias)[n + r]);
-              v[r] = bf2f(f2bf(v[r]));
-            }
-            Epi e2 = ep;
-            e2.bias = nullptr;
-            epi4<bf16_t, EPI>(e2, m, n, N, v);
-          } else {
-            epi4<bf16_t, EPI>(ep, m, n, N, v);
-          }
-        }
       }
+    }
+    __syncthreads();
+    epi_rows<EPI, BN, CR, NT>(ep, st, M, N, m0 + c0, n0, tid);
+    if constexpr (EPI == EPI_STORE) {
+      if (ep.outT) epi_cols<BN, CR, NT>(ep, st, M, N, m0 + c0, n0, tid);
     }
   }
 }
@@ -356,7 +441,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(int M, int N, int K,
     const int m = m0 + ty * 4 + i;
     if (m >= M) continue;
     float v[4] = {acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
-    epi4<float, EPI_STORE>(ep, m, n, N, v);
+    epi4_f32(ep, m, n, v);
   }
 }
 

@@ -27,7 +27,8 @@ struct Epi {
   int ldr = 0;
   const void* aux = nullptr;   // [M][ldaux]
   int ldaux = 0;
-  void* outT = nullptr;        // [M/S][N][S]: per-batch transpose (tokens contiguous)
+  void* outT = nullptr;        // [M/S][N][S]: per-batch transpose (tokens contiguous, bits 2
+                               // and 3 of the token index swapped: see gemm.hip)
   int S = 1;
 };
 
@@ -60,7 +61,8 @@ hipError_t act_bwd(int dtype, int act, int rows, int F, const void* dm, const vo
                    hipStream_t st);
 
 // Attention. qkv [T][Nqkv] token-major ([Q heads | K heads | V heads]);
-// qkvT [B][Nqkv][S] (bf16 path only); O [T][nq*d]; lse [B][nq][S] (natural log).
+// qkvT [B][Nqkv][S] (bf16 path only; tokens in the within-16 order the GEMM
+// epilogue writes); O [T][nq*d]; lse [B][nq][S] (natural log).
 hipError_t attn_fwd(int dtype, int B, int S, int nq, int nkv, int d, int causal, const void* qkv,
                     const void* qkvT, void* O, float* lse, hipStream_t st);
 // dO [T][nq*d], dOT [B][nq*d][S] (bf16 only); Dbuf [B][nq][S] fp32 scratch;
