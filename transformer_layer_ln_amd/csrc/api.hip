@@ -112,7 +112,7 @@ Saved saved_layout(const Dims& d) {
 }
 
 struct Scratch {
-  size_t dh, p, du, dm, dO, dOT, Dbuf, dqkv, part, red, total;
+  size_t dh, p, du, dm, dO, dOT, Dbuf, dqkv, part, red, ws, total;
 };
 Scratch scratch_layout(const Dims& d) {
   Scratch s;
@@ -130,6 +130,16 @@ Scratch scratch_layout(const Dims& d) {
   int64_t nmax = d.H > d.Fu ? d.H : d.Fu;
   if (d.Nqkv > nmax) nmax = d.Nqkv;
   s.red = o; o += al((size_t)colsum_splits((int)d.T) * nmax * 4);
+  // split-contraction partial tiles of the weight gradients (one at a time)
+  const int dt = d.dt, T32 = (int)d.T, H = (int)d.H;
+  size_t ws = gemm_ws_bytes(dt, (int)d.Nqkv, H, T32, false, false, EPI_STORE);
+  const size_t wo = gemm_ws_bytes(dt, H, (int)d.NO, T32, false, false, EPI_STORE);
+  const size_t w1 = gemm_ws_bytes(dt, (int)d.Fu, H, T32, false, false, EPI_STORE);
+  const size_t w2 = gemm_ws_bytes(dt, H, (int)d.F, T32, false, false, EPI_STORE);
+  if (wo > ws) ws = wo;
+  if (w1 > ws) ws = w1;
+  if (w2 > ws) ws = w2;
+  s.ws = o; o += al(ws);
   s.total = o;
   return s;
 }
@@ -377,6 +387,7 @@ mtb_status mtb_block_bwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
   void* dm = P(scratch, Z.dm); void* dO = P(scratch, Z.dO); void* dOT = bf ? P(scratch, Z.dOT) : nullptr;
   float* Dbuf = (float*)P(scratch, Z.Dbuf); void* dqkv = P(scratch, Z.dqkv);
   float* part = (float*)P(scratch, Z.part); float* red = (float*)P(scratch, Z.red);
+  void* ws = Z.total > Z.ws ? P(scratch, Z.ws) : nullptr;
   const void* G = dout;
 
   if (phase == MTB_PHASE_ALL || phase == MTB_PHASE_SEG0) {
@@ -394,7 +405,7 @@ mtb_status mtb_block_bwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
     }
     if (g.w_fc2) {
       Epi e;
-      e.out = g.w_fc2; e.ldo = F;
+      e.out = g.w_fc2; e.ldo = F; e.ws = ws;
       trace_begin(MTB_TRACE_FC2_WGRAD, st);
       MTB_HIP(gemm(dt, H, F, T, G, H, false, m, F, false, e, st));
       trace_end(MTB_TRACE_FC2_WGRAD, st);
@@ -402,7 +413,7 @@ mtb_status mtb_block_bwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
     if (g.b_fc2) MTB_HIP(colsum(dt, T, H, G, H, nullptr, nullptr, nullptr, g.b_fc2, red, st));
     if (g.w_fc1) {
       Epi e;
-      e.out = g.w_fc1; e.ldo = H;
+      e.out = g.w_fc1; e.ldo = H; e.ws = ws;
       MTB_HIP(gemm(dt, Fu, H, T, du, Fu, false, c, H, false, e, st));
     }
     if (g.b_fc1) MTB_HIP(colsum(dt, T, Fu, du, Fu, nullptr, nullptr, nullptr, g.b_fc1, red, st));
@@ -428,7 +439,7 @@ mtb_status mtb_block_bwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
     }
     if (g.w_o) {
       Epi e;
-      e.out = g.w_o; e.ldo = NO;
+      e.out = g.w_o; e.ldo = NO; e.ws = ws;
       MTB_HIP(gemm(dt, H, NO, T, dh, H, false, O, NO, false, e, st));
     }
     if (g.b_o) MTB_HIP(colsum(dt, T, H, dh, H, nullptr, nullptr, nullptr, g.b_o, red, st));
@@ -437,7 +448,7 @@ mtb_status mtb_block_bwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
                      dOT, lse, Dbuf, dqkv, part, st));
     if (g.w_qkv) {
       Epi e;
-      e.out = g.w_qkv; e.ldo = H;
+      e.out = g.w_qkv; e.ldo = H; e.ws = ws;
       MTB_HIP(gemm(dt, Nq, H, T, dqkv, Nq, false, a, H, false, e, st));
     }
     if (g.b_qkv) MTB_HIP(colsum(dt, T, Nq, dqkv, Nq, nullptr, nullptr, nullptr, g.b_qkv, red, st));

@@ -36,6 +36,7 @@ namespace mtb {
 namespace {
 
 constexpr int BK = 64;
+constexpr int EPI_PARTIAL = 100;  // internal: fp32 partial tile of a split contraction
 
 MTB_DEV int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
@@ -238,6 +239,40 @@ MTB_DEV void epi_rows(const Epi& e, const Staged<BN>& st, int M, int N, int mc, 
   }
 }
 
+// Row phase of a split contraction: the fp32 partial tile to ws [M][N]
+template <int BN, int CR, int NT>
+MTB_DEV void epi_partial(float* ws, const Staged<BN>& st, int M, int N, int mc, int n0, int tid) {
+  constexpr int IPR = BN / 8;
+  for (int it = tid; it < CR * IPR; it += NT) {
+    const int r = it / IPR, nl = (it % IPR) * 8;
+    const int m = mc + r, n = n0 + nl;
+    if (m >= M || n >= N) continue;
+    float v[8];
+    st.get8(r, nl, v);
+    st8(ws + (size_t)m * N + n, v);
+  }
+}
+
+// out[m][n] = sum over s = 0 .. splits-1 of ws[s][m][n], rounded once; 8
+// elements per thread (N % 8 == 0)
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(int M, int N, int splits,
+                                                            const float* __restrict__ ws,
+                                                            bf16_t* __restrict__ out, int ldo) {
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  const size_t MN = (size_t)M * N;
+  if (i >= MN) return;
+  float v[8];
+  ld8(ws + i, v);
+  for (int s = 1; s < splits; ++s) {
+    float w[8];
+    ld8(ws + (size_t)s * MN + i, w);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) v[r] += w[r];
+  }
+  const size_t m = i / N, n = i % N;
+  st8(out + m * ldo + n, v);
+}
+
 // Column phase: the per-batch transposed copy outT[b][n][s] of the stored
 // values. Inside every 16 tokens the order is 0-3, 8-11, 4-7, 12-15 (bits 2
 // and 3 of the token index swapped), the key order the attention kernels'
@@ -281,7 +316,7 @@ template <int BM, int BN, int WGM, int WGN, int OCC, bool AKC, bool BKC, int EPI
 __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(int M, int N, int K,
                                                            const bf16_t* __restrict__ A, int lda,
                                                            const bf16_t* __restrict__ B, int ldb,
-                                                           Epi ep) {
+                                                           Epi ep, int ksplit) {
   constexpr int NT = 64 * WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32;
   // operand double buffers; reused by the epilogue for the staged fp32 tile
@@ -298,6 +333,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(int M, i
   int bid = blockIdx.x;
   const int nb = gridDim.x;
   if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+  // split contraction: blocks [s * tiles, (s + 1) * tiles) take k-range s
+  const int split = bid / (tiles_m * tiles_n);
+  bid -= split * (tiles_m * tiles_n);
+  const int kspan = K / ksplit, kbeg = split * kspan;
   constexpr int GROUP = 8;
   const int per_group = GROUP * tiles_n;
   const int first_m = (bid / per_group) * GROUP;
@@ -317,9 +356,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(int M, i
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int KT = K / BK;
-  la.load(A, lda, m0, M, 0, tid);
-  lb.load(B, ldb, n0, N, 0, tid);
+  const int KT = kspan / BK;
+  la.load(A, lda, m0, M, kbeg, tid);
+  lb.load(B, ldb, n0, N, kbeg, tid);
   la.store(sA(0), tid);
   lb.store(sB(0), tid);
   __syncthreads();
@@ -327,8 +366,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(int M, i
   for (int kt = 0; kt < KT; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < KT) {
-      la.load(A, lda, m0, M, (kt + 1) * BK, tid);
-      lb.load(B, ldb, n0, N, (kt + 1) * BK, tid);
+      la.load(A, lda, m0, M, kbeg + (kt + 1) * BK, tid);
+      lb.load(B, ldb, n0, N, kbeg + (kt + 1) * BK, tid);
     }
     const bf16_t* as = sA(cur);
     const bf16_t* bs = sB(cur);
@@ -385,7 +424,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(int M, i
       }
     }
     __syncthreads();
-    epi_rows<EPI, BN, CR, NT>(ep, st, M, N, m0 + c0, n0, tid);
+    if constexpr (EPI == EPI_PARTIAL)
+      epi_partial<BN, CR, NT>(reinterpret_cast<float*>(ep.ws) + (size_t)split * M * N, st, M, N,
+                              m0 + c0, n0, tid);
+    else
+      epi_rows<EPI, BN, CR, NT>(ep, st, M, N, m0 + c0, n0, tid);
     if constexpr (EPI == EPI_STORE) {
       if (ep.outT) epi_cols<BN, CR, NT>(ep, st, M, N, m0 + c0, n0, tid);
     }
@@ -447,25 +490,52 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(int M, int N, int K,
 
 template <int BM, int BN, int WGM, int WGN, int OCC, bool AKC, bool BKC, int EPI>
 hipError_t launch_cfg(int M, int N, int K, const void* A, int lda, const void* B, int ldb,
-                      const Epi& e, hipStream_t st) {
+                      const Epi& e, hipStream_t st, int ksplit = 1) {
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, OCC, AKC, BKC, EPI>), dim3(tiles),
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, OCC, AKC, BKC, EPI>), dim3(tiles * ksplit),
                      dim3(64 * WGM * WGN), 0, st, M, N, K, (const bf16_t*)A, lda,
-                     (const bf16_t*)B, ldb, e);
+                     (const bf16_t*)B, ldb, e, ksplit);
   return hipGetLastError();
+}
+
+constexpr int kCUs = 256;
+
+// Split count for a weight gradient (both operands transposed) on 256x128
+// tiles: only when the tiles would leave at least half the CUs idle, the
+// smallest power of two that gives 3/4 of a wave of kCUs blocks, each split
+// at least 1024 deep; 1 = no split. (More splits cost 8 bytes per output
+// element each in partial-tile traffic.)
+int wgrad_splits(int M, int N, int K) {
+  const long tiles = (long)((M + 255) / 256) * ((N + 127) / 128);
+  if (tiles > kCUs / 2) return 1;
+  int s = 1;
+  while (s < 8 && tiles * s * 4 < 3L * kCUs && K % (2 * s * BK) == 0 && K / (2 * s) >= 1024) s *= 2;
+  return s;
 }
 
 // Tile shape per problem (measured on MI355X over the block's GEMM shapes):
 // 256x256 with 2x4 wavefronts when the problem is large and deep enough to
 // fill the chip; for the weight gradients (both operands transposed in LDS)
-// 256x128 with 4x2 wavefronts; 128x128 with 2x2 wavefronts otherwise.
+// 256x128 with 4x2 wavefronts, the contraction split over several blocks
+// when there are too few tiles (given a workspace); 128x128 with 2x2
+// wavefronts otherwise.
 template <bool AKC, bool BKC, int EPI>
 hipError_t launch_bf16(int M, int N, int K, const void* A, int lda, const void* B, int ldb,
                        const Epi& e, hipStream_t st) {
   const long t256 = (long)((M + 255) / 256) * ((N + 255) / 256);
   const long t256x128 = (long)((M + 255) / 256) * ((N + 127) / 128);
-  if constexpr (!AKC && !BKC) {
-    if (t256x128 >= 256 && K >= 1024)
+  if constexpr (!AKC && !BKC && EPI == EPI_STORE) {
+    const int ks = e.ws ? wgrad_splits(M, N, K) : 1;
+    if (ks > 1) {
+      hipError_t r = launch_cfg<256, 128, 4, 2, 1, AKC, BKC, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, e,
+                                                                           st, ks);
+      if (r != hipSuccess) return r;
+      const size_t n8 = (size_t)M * N / 8;
+      hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st,
+                         M, N, ks, (const float*)e.ws, (bf16_t*)e.out, e.ldo);
+      return hipGetLastError();
+    }
+    if (t256x128 >= kCUs && K >= 1024)
       return launch_cfg<256, 128, 4, 2, 1, AKC, BKC, EPI>(M, N, K, A, lda, B, ldb, e, st);
   } else {
     if (t256 >= 128 && K >= 1024)
@@ -475,6 +545,12 @@ hipError_t launch_bf16(int M, int N, int K, const void* A, int lda, const void* 
 }
 
 }  // namespace
+
+size_t gemm_ws_bytes(int dtype, int M, int N, int K, bool a_kc, bool b_kc, int kind) {
+  if (dtype == 0 || a_kc || b_kc || kind != EPI_STORE || M <= 0 || N <= 0) return 0;
+  const int ks = wgrad_splits(M, N, K);
+  return ks > 1 ? (size_t)ks * M * N * 4 : 0;
+}
 
 hipError_t gemm(int dtype, int M, int N, int K, const void* A, int lda, bool a_kc, const void* B,
                 int ldb, bool b_kc, const Epi& e, hipStream_t st) {

@@ -27,6 +27,7 @@ struct Epi {
   int ldr = 0;
   const void* aux = nullptr;   // [M][ldaux]
   int ldaux = 0;
+  void* ws = nullptr;          // fp32 workspace for split-K partial tiles (gemm_ws_bytes), or null
   void* outT = nullptr;        // [M/S][N][S]: per-batch transpose (tokens contiguous, bits 2
                                // and 3 of the token index swapped: see gemm.hip)
   int S = 1;
@@ -37,6 +38,11 @@ struct Epi {
 //   b_kc: B stored [N][K] (k contiguous) else [K][N].
 hipError_t gemm(int dtype, int M, int N, int K, const void* A, int lda, bool a_kc,
                 const void* B, int ldb, bool b_kc, const Epi& e, hipStream_t st);
+// Bytes of Epi::ws that gemm() uses to split the contraction of this product
+// over several workgroups per output tile (0: it does not split). Only weight
+// gradients (both operands transposed, plain store) with too few tiles to fill
+// the chip are split; the partial tiles are summed in a fixed order.
+size_t gemm_ws_bytes(int dtype, int M, int N, int K, bool a_kc, bool b_kc, int kind);
 
 // LayerNorm over rows of width H: hsum = x (+resid) (+bias) rounded to dtype;
 // y = (hsum - mu) * rstd (* g + b). h_out (optional) receives hsum.
