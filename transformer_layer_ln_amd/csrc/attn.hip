@@ -329,6 +329,9 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(int rows, int S, int 
 // half w & 1 and query half w >> 1 of every 64-query tile. S = Q K^T puts a
 // key per lane, so P and dS feed dV^T += dO^T P^T and dK^T += Q^T dS^T
 // straight from registers; the two query halves are summed at the end.
+// The Q, dO, Q^T, dO^T tiles and the tile's log-sum-exp and D values are
+// copied global -> LDS directly, double-buffered: tile t+1 streams in while
+// tile t is used.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(
     int S, int nq, int nkv, int ldq, const bf16_t* __restrict__ qkv,
@@ -336,13 +339,11 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(
     const bf16_t* __restrict__ dOT, const float* __restrict__ lse,
     const float* __restrict__ Dbuf, bf16_t* __restrict__ dqkv, float* __restrict__ part, float sl2,
     float scale) {
-  __shared__ __attribute__((aligned(16))) bf16_t smem[4 * 64 * D];  // Q, dO, Q^T, dO^T tiles
-  __shared__ __attribute__((aligned(16))) float sL[64], sD[64];
-  bf16_t* sQ = smem;
-  bf16_t* sdO = smem + 64 * D;
-  bf16_t* sQT = smem + 128 * D;
-  bf16_t* sdOT = smem + 192 * D;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lg = lane >> 5;
+  constexpr int TILE = 64 * D;              // elements of one 64 x D (or D x 64) tile
+  constexpr int STAGE = 4 * TILE + 512;  // Q, dO, Q^T, dO^T, then lse and D (64 floats each), 1-KB aligned
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[2 * STAGE];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lg = lane >> 5;
   const int kh = wave & 1, qh = wave >> 1;
   const int ntile = S / 64, nbh = gridDim.x / ntile;
   int kb, bh;
@@ -376,60 +377,103 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(
   const float* lrow = lse + ((size_t)b * nq + hq) * S;
   const float* drow = Dbuf + ((size_t)b * nq + hq) * S;
 
-  for (int qt = CAUSAL ? kb : 0; qt < ntile; ++qt) {
+  auto fetch = [&](int qt) {
+    bf16_t* st = smem + (qt & 1) * STAGE;
     const int qt0 = qt * 64;
-    __syncthreads();
-    lds_rows<64, D>(sQ, qbase + (size_t)qt0 * ldq, ldq, tid);
-    lds_rows<64, D>(sdO, dobase + (size_t)qt0 * ldo, ldo, tid);
-    lds_tposed<D>(sQT, qtbase + qt0, S, tid);
-    lds_tposed<D>(sdOT, dotbase + qt0, S, tid);
-    if (tid < 64) {
-      sL[tid] = lrow[qt0 + tid] * kLog2e;
-      sD[tid] = drow[qt0 + tid];
+    dma_tile<64, D / 8>(st, qbase + (size_t)qt0 * ldq, ldq, wave, lane);
+    dma_tile<64, D / 8>(st + TILE, dobase + (size_t)qt0 * ldo, ldo, wave, lane);
+    dma_tile<D, 8>(st + 2 * TILE, qtbase + qt0, S, wave, lane);
+    dma_tile<D, 8>(st + 3 * TILE, dotbase + qt0, S, wave, lane);
+    if (wave == 0) {
+      __builtin_amdgcn_global_load_lds((const void*)(lrow + qt0 + lane), (lds_ptr_t)(st + 4 * TILE), 4, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(drow + qt0 + lane), (lds_ptr_t)(st + 4 * TILE + 128), 4, 0,
+                                       0);
     }
-    __syncthreads();
-    const int qw0 = qt0 + qh * 32;
-    if (CAUSAL && qw0 + 31 < k0) continue;
+  };
 
-    f32x16 s, dp;
+  const int qfirst = CAUSAL ? kb : 0;
+  fetch(qfirst);
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+  __syncthreads();
+  for (int qt = qfirst; qt < ntile; ++qt) {
+    if (qt + 1 < ntile) fetch(qt + 1);   // into the stage every wave finished with last iteration
+    const bf16_t* st = smem + (qt & 1) * STAGE;
+    const bf16_t* sQ = st;
+    const bf16_t* sdO = st + TILE;
+    const bf16_t* sQT = st + 2 * TILE;
+    const bf16_t* sdOT = st + 3 * TILE;
+    const float* sL = reinterpret_cast<const float*>(st + 4 * TILE);
+    const float* sD = sL + 64;
+    const int qt0 = qt * 64;
+    const int qw0 = qt0 + qh * 32;
+    if (!CAUSAL || qw0 + 31 >= k0) {
+      // all of this tile's Q / dO fragments first, so the LDS reads overlap
+      bf16x8 qa[D / 16], oa[D / 16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const int row = qh * 32 + (lane & 31);
+        qa[kk] = frag<D>(sQ, row, 2 * kk + lg);
+        oa[kk] = frag<D>(sdO, row, 2 * kk + lg);
+      }
+      f32x16 s, dp;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      const int row = qh * 32 + (lane & 31);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<D>(sQ, row, 2 * kk + lg), kf[kk], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<D>(sdO, row, 2 * kk + lg), vf[kk], dp, 0, 0, 0);
-    }
-    // element j: query qw0 + 8(j>>2) + 4lg + (j&3), key `key`
-    float p[16], ds[16];
+      for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ql = qh * 32 + 8 * i + 4 * lg;
-      const f32x4 L4 = *reinterpret_cast<const f32x4*>(sL + ql);
-      const f32x4 D4 = *reinterpret_cast<const f32x4*>(sD + ql);
+      for (int kk = 0; kk < D / 16; ++kk) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kk], kf[kk], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[kk], vf[kk], dp, 0, 0, 0);
+      }
+      // the dO^T / Q^T fragments of the second pair of products, read under the first
+      bf16x8 ot[D / 32][2], qt2[D / 32][2];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = 4 * i + r;
-        float pv = exp2_fast(fmaf(s[j], sl2, -L4[r]));
-        if (CAUSAL && key > qt0 + ql + r) pv = 0.f;
-        p[j] = pv;
-        ds[j] = pv * (dp[j] - D4[r]);
+      for (int df = 0; df < D / 32; ++df) {
+        const int row = df * 32 + (lane & 31);
+        ot[df][0] = frag<64>(sdOT, row, 4 * qh + lg);
+        ot[df][1] = frag<64>(sdOT, row, 4 * qh + 2 + lg);
+        qt2[df][0] = frag<64>(sQT, row, 4 * qh + lg);
+        qt2[df][1] = frag<64>(sQT, row, 4 * qh + 2 + lg);
+      }
+      // issue order: the Q / dO reads, then each S / dP MFMA followed by one
+      // of the dO^T / Q^T reads (the scheduler would otherwise sink every
+      // read next to its use)
+      __builtin_amdgcn_sched_group_barrier(0x100, D / 8, 0);
+#pragma unroll
+      for (int i = 0; i < D / 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      // element j: query qw0 + 8(j>>2) + 4lg + (j&3), key `key`
+      float p[16], ds[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ql = qh * 32 + 8 * i + 4 * lg;
+        const f32x4 L4 = *reinterpret_cast<const f32x4*>(sL + ql);
+        const f32x4 D4 = *reinterpret_cast<const f32x4*>(sD + ql);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = 4 * i + r;
+          float pv = exp2_fast(fmaf(s[j], sl2, -(L4[r] * kLog2e)));
+          if (CAUSAL && key > qt0 + ql + r) pv = 0.f;
+          p[j] = pv;
+          ds[j] = pv * (dp[j] - D4[r]);
+        }
+      }
+      bf16x8 p0, p1, d0, d1;
+      pack_half(p, p0, p1);
+      pack_half(ds, d0, d1);
+#pragma unroll
+      for (int df = 0; df < D / 32; ++df) {
+        dv[df] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ot[df][0], p0, dv[df], 0, 0, 0);
+        dv[df] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ot[df][1], p1, dv[df], 0, 0, 0);
+        dk[df] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt2[df][0], d0, dk[df], 0, 0, 0);
+        dk[df] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt2[df][1], d1, dk[df], 0, 0, 0);
       }
     }
-    bf16x8 p0, p1, d0, d1;
-    pack_half(p, p0, p1);
-    pack_half(ds, d0, d1);
-#pragma unroll
-    for (int df = 0; df < D / 32; ++df) {
-      const int row = df * 32 + (lane & 31);
-      dv[df] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<64>(sdOT, row, 4 * qh + lg), p0, dv[df], 0, 0, 0);
-      dv[df] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<64>(sdOT, row, 4 * qh + 2 + lg), p1, dv[df], 0, 0, 0);
-      dk[df] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<64>(sQT, row, 4 * qh + lg), d0, dk[df], 0, 0, 0);
-      dk[df] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<64>(sQT, row, 4 * qh + 2 + lg), d1, dk[df], 0, 0, 0);
-    }
+    // tile qt+1 landed, and every wave is done with stage qt & 1
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+    __syncthreads();
   }
   // sum the two query halves: qh = 1 hands its accumulators to qh = 0
-  __syncthreads();
   constexpr int NR = D / 2;
   float* xo = reinterpret_cast<float*>(smem);  // [kh][dk|dv][NR][64]
   if (qh == 1) {
