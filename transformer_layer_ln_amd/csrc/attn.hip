@@ -7,21 +7,25 @@
 // (batch, head) with 4 wavefronts arranged 2 x 2: each wavefront takes 32 rows
 // of its own side and one 32-row half of the other side's tile, and the two
 // halves are combined through LDS at the end. That gives S/64 * B * heads
-// workgroups (two resident per CU at 2 wavefronts per SIMD); causal grids pair
-// heavy and light tiles.
+// workgroups; causal grids pair heavy and light tiles. The other side's
+// tiles stream global -> LDS with direct-to-LDS loads, double-buffered (tile
+// t+1 is in flight while tile t is used); each wavefront reads a tile's
+// fragments in bulk ahead of the MFMAs that use them.
 //  * forward: S^T = K Q^T puts one query per lane, so the online-softmax row
 //    max is 16 in-lane values plus one exchange with lane ^ 32, the running
 //    sum stays per lane until the end, and the O^T accumulator is rescaled
 //    only when some row's max moved. P^T feeds O^T += V^T P^T from registers.
-//    K and V^T tiles are fetched one step ahead into registers, double-
-//    buffered in LDS. Only O and the row log-sum-exp are written.
+//    Only O and the row log-sum-exp are written.
 //  * backward: P is recomputed from the saved log-sum-exp.
 //    dK/dV: S = Q K^T puts a key per lane, so P and dS feed dV^T += dO^T P^T
 //    and dK^T += Q^T dS^T from registers; with GQA the q-head contributions
 //    of a kv head are summed by a second pass. dQ: S^T layout, dQ^T += K^T dS^T.
 //    No atomics: every output element has exactly one writer.
 // Layout inputs: qkv [T][Nqkv] token-major and its per-batch transpose
-// qkvT [B][Nqkv][S]; dO [T][nq*d] and dOT [B][nq*d][S].
+// qkvT [B][Nqkv][S]; dO [T][nq*d] and dOT [B][nq*d][S]. In the transposed
+// copies the tokens of every 16 are stored in the order 0-3, 8-11, 4-7, 12-15,
+// so that an MFMA k-step's 16 keys -- the lane group g holds keys 4g..4g+3 and
+// 8+4g..8+4g+3 of its accumulator layout -- are one 16-byte chunk.
 #include "common.h"
 #include "kernels.h"
 
@@ -33,35 +37,6 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
 
 MTB_DEV int swz(int row) { return (row ^ (row >> 3)) & 7; }
-
-// ROWS x D tile of a row-major matrix (row pitch ld elements) -> LDS [row][D],
-// 16-byte chunks XOR-swizzled by row.
-template <int ROWS, int D>
-MTB_DEV void lds_rows(bf16_t* s, const bf16_t* __restrict__ g, size_t ld, int tid) {
-  constexpr int CH = D / 8, N = ROWS * CH / 256;
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const int q = tid + 256 * i, row = q / CH, c = q % CH;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(g + (size_t)row * ld + c * 8);
-    *reinterpret_cast<u32x4*>(s + row * D + ((c ^ swz(row)) << 3)) = v;
-  }
-}
-
-// D x 64 tile of a transposed matrix (D rows of 64 tokens, row pitch ld) ->
-// LDS [d][64 keys]. The tokens arrive already in the order 0-3, 8-11, 4-7,
-// 12-15 inside every 16 (the GEMM epilogue writes them so): lane group g of
-// an MFMA k-step then reads keys {4g..4g+3, 8+4g..8+4g+3} -- the keys its
-// accumulator layout holds -- as one 16-byte chunk.
-template <int D>
-MTB_DEV void lds_tposed(bf16_t* s, const bf16_t* __restrict__ g, size_t ld, int tid) {
-  constexpr int N = D * 8 / 256;
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const int q = tid + 256 * i, row = q >> 3, c = q & 7;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(g + (size_t)row * ld + c * 8);
-    *reinterpret_cast<u32x4*>(s + row * 64 + ((c ^ swz(row)) << 3)) = v;
-  }
-}
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -114,39 +89,6 @@ MTB_DEV void tile_order(int L, int ntile, int nbh, bool causal, bool heavy_high,
   tile = heavy_high ? ntile - 1 - rank : rank;
 }
 
-// K tile (64 keys x D, rows of qkv) and V^T tile (D x 64 keys, rows of qkvT),
-// fetched into registers one step ahead of their use
-template <int D>
-struct KVFetch {
-  static constexpr int NK = 64 * D / 8 / 256, NV = D * 8 / 256;
-  u32x4 k[NK], v[NV];
-  MTB_DEV void load(const bf16_t* __restrict__ kp, size_t ldq, const bf16_t* __restrict__ vtp,
-                    size_t S, int tid) {
-#pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      const int q = tid + 256 * i, row = q / (D / 8), c = q % (D / 8);
-      k[i] = *reinterpret_cast<const u32x4*>(kp + (size_t)row * ldq + c * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int q = tid + 256 * i, row = q >> 3, c = q & 7;
-      v[i] = *reinterpret_cast<const u32x4*>(vtp + (size_t)row * S + c * 8);
-    }
-  }
-  MTB_DEV void store(bf16_t* sK, bf16_t* sV, int tid) const {
-#pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      const int q = tid + 256 * i, row = q / (D / 8), c = q % (D / 8);
-      *reinterpret_cast<u32x4*>(sK + row * D + ((c ^ swz(row)) << 3)) = k[i];
-    }
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int q = tid + 256 * i, row = q >> 3, c = q & 7;
-      *reinterpret_cast<u32x4*>(sV + row * 64 + ((c ^ swz(row)) << 3)) = v[i];
-    }
-  }
-};
-
 // two 16-row k-steps of a 32x32 accumulator as bf16 B operands:
 // step 0 = rows {4lg..4lg+3, 8+4lg..}, step 1 = rows {16+4lg.., 24+4lg..}
 MTB_DEV void pack_half(const float (&a)[16], bf16x8& p0, bf16x8& p1) {
@@ -168,8 +110,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(int S, int nq, int nkv
                                                           const bf16_t* __restrict__ qkvT,
                                                           bf16_t* __restrict__ O,
                                                           float* __restrict__ lse, float sl2) {
-  __shared__ __attribute__((aligned(16))) bf16_t smem[4 * 64 * D];  // 2 stages of K, V^T
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lg = lane >> 5;
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[4 * 64 * D];  // 2 stages of K, V^T
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lg = lane >> 5;
   const int qh = wave & 1, kh = wave >> 1;
   const int ntile = S / 64, nbh = gridDim.x / ntile;
   int qb, bh;
@@ -195,25 +138,44 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(int S, int nq, int nkv
   const bf16_t* kbase = qkv + tok0 * ldq + (size_t)(nq + hk) * D;
   const bf16_t* vtbase = qkvT + ((size_t)b * ldq + (size_t)(nq + nkv + hk) * D) * S;
   const int ntk = CAUSAL ? qb + 1 : ntile;
-  KVFetch<D> pf;
-  pf.load(kbase, ldq, vtbase, S, tid);
-  pf.store(smem, smem + 64 * D, tid);
+  auto fetch = [&](int t) {
+    bf16_t* st = smem + (t & 1) * 128 * D;
+    dma_tile<64, D / 8>(st, kbase + (size_t)t * 64 * ldq, ldq, wave, lane);
+    dma_tile<D, 8>(st + 64 * D, vtbase + t * 64, S, wave, lane);
+  };
+  fetch(0);
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
   __syncthreads();
 
   for (int t = 0; t < ntk; ++t) {
-    bf16_t* sK = smem + (t & 1) * 128 * D;
-    bf16_t* sV = sK + 64 * D;
-    if (t + 1 < ntk) pf.load(kbase + (size_t)(t + 1) * 64 * ldq, ldq, vtbase + (t + 1) * 64, S, tid);
+    if (t + 1 < ntk) fetch(t + 1);   // into the stage every wave finished with last iteration
+    const bf16_t* sK = smem + (t & 1) * 128 * D;
+    const bf16_t* sV = sK + 64 * D;
     const int ks = t * 64 + kh * 32;
     if (!CAUSAL || ks <= q0 + 31) {
+      bf16x8 kf[D / 16], vt[D / 32][2];
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) kf[kk] = frag<D>(sK, kh * 32 + (lane & 31), 2 * kk + lg);
+#pragma unroll
+      for (int df = 0; df < D / 32; ++df) {
+        const int row = df * 32 + (lane & 31);
+        vt[df][0] = frag<64>(sV, row, 4 * kh + lg);
+        vt[df][1] = frag<64>(sV, row, 4 * kh + 2 + lg);
+      }
       f32x16 sa, sb;
 #pragma unroll
       for (int r = 0; r < 16; ++r) { sa[r] = 0.f; sb[r] = 0.f; }
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
-        const bf16x8 kf = frag<D>(sK, kh * 32 + (lane & 31), 2 * kk + lg);
-        if (kk & 1) sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sb, 0, 0, 0);
-        else sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sa, 0, 0, 0);
+        if (kk & 1) sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], sb, 0, 0, 0);
+        else sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], sa, 0, 0, 0);
+      }
+      // issue order: the K reads, then each S^T MFMA followed by one V^T read
+      __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 0);
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
       // s[j]: key ks + 8(j>>2) + 4lg + (j&3), query qi
       float s[16];
@@ -249,17 +211,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(int S, int nq, int nkv
       pack_half(s, p0, p1);
 #pragma unroll
       for (int df = 0; df < D / 32; ++df) {
-        const int row = df * 32 + (lane & 31);
-        oacc[df] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<64>(sV, row, 4 * kh + lg), p0,
-                                                           oacc[df], 0, 0, 0);
-        oacc[df] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<64>(sV, row, 4 * kh + 2 + lg), p1,
-                                                           oacc[df], 0, 0, 0);
+        oacc[df] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt[df][0], p0, oacc[df], 0, 0, 0);
+        oacc[df] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt[df][1], p1, oacc[df], 0, 0, 0);
       }
     }
-    if (t + 1 < ntk) {
-      bf16_t* nK = smem + ((t + 1) & 1) * 128 * D;
-      pf.store(nK, nK + 64 * D, tid);
-    }
+    // tile t+1 landed, and every wave is done with stage t & 1
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
     __syncthreads();
   }
   l_i += __shfl_xor(l_i, 32, 64);
@@ -542,18 +499,21 @@ __global__ __launch_bounds__(256) void attn_dkv_reduce_kernel(int B, int S, int 
 
 // dQ. Workgroup = 64 queries of one (batch, q head); wavefront w takes query
 // half w & 1 and key half w >> 1 of every 64-key tile (S^T layout: a query
-// per lane); the key halves are summed at the end.
+// per lane); the key halves are summed at the end. K, V and K^T tiles are
+// copied global -> LDS directly into one buffer: two workgroups share a CU
+// and cover each other's loads (measured faster than double-buffering at one
+// workgroup per CU).
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     int S, int nq, int nkv, int ldq, const bf16_t* __restrict__ qkv,
     const bf16_t* __restrict__ qkvT, const bf16_t* __restrict__ dO,
     const float* __restrict__ lse, const float* __restrict__ Dbuf, bf16_t* __restrict__ dqkv,
     float sl2, float scale) {
-  __shared__ __attribute__((aligned(16))) bf16_t smem[3 * 64 * D];  // K, V, K^T tiles
-  bf16_t* sK = smem;
-  bf16_t* sV = smem + 64 * D;
-  bf16_t* sKT = smem + 128 * D;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lg = lane >> 5;
+  constexpr int TILE = 64 * D;
+  constexpr int STAGE = 3 * TILE;  // K, V, K^T
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[STAGE];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lg = lane >> 5;
   const int qh = wave & 1, kh = wave >> 1;
   const int ntile = S / 64, nbh = gridDim.x / ntile;
   int qb, bh;
@@ -586,45 +546,50 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
   const bf16_t* vbase = qkv + tok0 * ldq + (size_t)(nq + nkv + hk) * D;
   const bf16_t* ktbase = qkvT + ((size_t)b * ldq + (size_t)(nq + hk) * D) * S;
   const int ntk = CAUSAL ? qb + 1 : ntile;
-
-  for (int t = 0; t < ntk; ++t) {
+  auto fetch = [&](int t) {
     const int k0 = t * 64;
+    dma_tile<64, D / 8>(smem, kbase + (size_t)k0 * ldq, ldq, wave, lane);
+    dma_tile<64, D / 8>(smem + TILE, vbase + (size_t)k0 * ldq, ldq, wave, lane);
+    dma_tile<D, 8>(smem + 2 * TILE, ktbase + k0, S, wave, lane);
+  };
+  for (int t = 0; t < ntk; ++t) {
+    fetch(t);
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
     __syncthreads();
-    lds_rows<64, D>(sK, kbase + (size_t)k0 * ldq, ldq, tid);
-    lds_rows<64, D>(sV, vbase + (size_t)k0 * ldq, ldq, tid);
-    lds_tposed<D>(sKT, ktbase + k0, S, tid);
-    __syncthreads();
-    const int ks = k0 + kh * 32;
-    if (CAUSAL && ks > q0 + 31) continue;
-
-    f32x16 s, dp;
+    const bf16_t* sK = smem;
+    const bf16_t* sV = sK + TILE;
+    const bf16_t* sKT = sK + 2 * TILE;
+    const int ks = t * 64 + kh * 32;
+    if (!CAUSAL || ks <= q0 + 31) {
+      f32x16 s, dp;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
+      for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      const int row = kh * 32 + (lane & 31);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<D>(sK, row, 2 * kk + lg), qf[kk], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<D>(sV, row, 2 * kk + lg), of[kk], dp, 0, 0, 0);
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const int row = kh * 32 + (lane & 31);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<D>(sK, row, 2 * kk + lg), qf[kk], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<D>(sV, row, 2 * kk + lg), of[kk], dp, 0, 0, 0);
+      }
+      // element j: key ks + 8(j>>2) + 4lg + (j&3), query qi
+      float ds[16];
+      const bool diag = CAUSAL && ks + 31 > q0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        float pv = exp2_fast(fmaf(s[j], sl2, -Lq));
+        if (diag && ks + 8 * (j >> 2) + 4 * lg + (j & 3) > qi) pv = 0.f;
+        ds[j] = pv * (dp[j] - Dq);
+      }
+      bf16x8 d0, d1;
+      pack_half(ds, d0, d1);
+#pragma unroll
+      for (int df = 0; df < D / 32; ++df) {
+        const int row = df * 32 + (lane & 31);
+        dq[df] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<64>(sKT, row, 4 * kh + lg), d0, dq[df], 0, 0, 0);
+        dq[df] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<64>(sKT, row, 4 * kh + 2 + lg), d1, dq[df], 0, 0, 0);
+      }
     }
-    // element j: key ks + 8(j>>2) + 4lg + (j&3), query qi
-    float ds[16];
-    const bool diag = CAUSAL && ks + 31 > q0;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      float pv = exp2_fast(fmaf(s[j], sl2, -Lq));
-      if (diag && ks + 8 * (j >> 2) + 4 * lg + (j & 3) > qi) pv = 0.f;
-      ds[j] = pv * (dp[j] - Dq);
-    }
-    bf16x8 d0, d1;
-    pack_half(ds, d0, d1);
-#pragma unroll
-    for (int df = 0; df < D / 32; ++df) {
-      const int row = df * 32 + (lane & 31);
-      dq[df] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<64>(sKT, row, 4 * kh + lg), d0, dq[df], 0, 0, 0);
-      dq[df] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<64>(sKT, row, 4 * kh + 2 + lg), d1, dq[df], 0, 0, 0);
-    }
+    __syncthreads();  // every wave is done with the tile before the next one lands
   }
-  __syncthreads();
   constexpr int NR = D / 2;
   float* xo = reinterpret_cast<float*>(smem);  // [qh][NR][64]
   if (kh == 1) {
