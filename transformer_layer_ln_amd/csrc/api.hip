@@ -136,6 +136,8 @@ Scratch scratch_layout(const Dims& d) {
   const size_t wo = gemm_ws_bytes(dt, H, (int)d.NO, T32, false, false, EPI_STORE);
   const size_t w1 = gemm_ws_bytes(dt, (int)d.Fu, H, T32, false, false, EPI_STORE);
   const size_t w2 = gemm_ws_bytes(dt, H, (int)d.F, T32, false, false, EPI_STORE);
+  const size_t wd = gemm_ws_bytes(dt, T32, (int)d.NO, H, true, false, EPI_STORE);  // projection dgrad
+  if (wd > ws) ws = wd;
   if (wo > ws) ws = wo;
   if (w1 > ws) ws = w1;
   if (w2 > ws) ws = w2;
@@ -434,7 +436,7 @@ mtb_status mtb_block_bwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
     // projection backward (row-parallel: g1's backward is the identity)
     {
       Epi e;
-      e.out = dO; e.ldo = NO; e.outT = dOT; e.S = S;
+      e.out = dO; e.ldo = NO; e.outT = dOT; e.S = S; e.ws = ws;
       MTB_HIP(gemm(dt, T, NO, H, dh, H, true, w->w_o, NO, false, e, st));
     }
     if (g.w_o) {

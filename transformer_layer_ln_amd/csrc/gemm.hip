@@ -41,16 +41,17 @@ constexpr int EPI_PARTIAL = 100;  // internal: fp32 partial tile of a split cont
 MTB_DEV int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
 // operand tile ROWS x BK from a matrix stored [rows][K] (k contiguous),
-// NT threads, 16-byte chunks
+// NT threads, 16-byte chunks (threads past the last chunk idle)
 template <int ROWS, int NT>
 struct TileKc {
-  static constexpr int NCH = ROWS * BK / 8 / NT;
-  static_assert(ROWS * BK / 8 % NT == 0, "tile must split evenly over the threads");
+  static constexpr int TOT = ROWS * BK / 8;
+  static constexpr int NCH = (TOT + NT - 1) / NT;
   u32x4 r[NCH];
   MTB_DEV void load(const bf16_t* __restrict__ p, int ld, int row0, int rowmax, int k0, int tid) {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int q = tid + NT * i, row = q >> 3, c = q & 7;
+      if (TOT % NT != 0 && q >= TOT) break;
       const int gr = min(row0 + row, rowmax - 1);
       r[i] = *reinterpret_cast<const u32x4*>(p + (size_t)gr * ld + k0 + c * 8);
     }
@@ -59,6 +60,7 @@ struct TileKc {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int q = tid + NT * i, row = q >> 3, c = q & 7;
+      if (TOT % NT != 0 && q >= TOT) break;
       *reinterpret_cast<u32x4*>(s + row * BK + ((c ^ swz(row)) << 3)) = r[i];
     }
   }
@@ -143,16 +145,23 @@ MTB_DEV void out8(void* p, size_t off, const float (&v)[8]) {
   st8(reinterpret_cast<bf16_t*>(p) + off, v);
 }
 
-// rows of the tile staged per epilogue chunk: BM halved until the fp32 chunk
-// fits the operand buffers (max_rows = their size in fp32 rows)
-constexpr int stage_rows(int bm, int max_rows) { return bm <= max_rows ? bm : stage_rows(bm / 2, max_rows); }
+// rows of the tile staged per epilogue chunk: the largest multiple of the
+// wavefront tile height wm that divides bm and fits the operand buffers
+// (max_rows = their size in fp32 rows)
+constexpr int stage_rows(int bm, int wm, int max_rows, int c) {
+  return c <= wm ? wm : (bm % c == 0 && c <= max_rows ? c : stage_rows(bm, wm, max_rows, c - wm));
+}
 
 // Staged fp32 tile: CR rows x BN columns, 16-byte chunks XOR-swizzled by row.
 template <int BN>
 struct Staged {
-  static constexpr int NCH = BN / 4;  // 16-byte chunks per row
+  static constexpr int NCH = BN / 4;      // 16-byte chunks per row
+  static constexpr int G = NCH & -NCH;    // XOR-swizzle within aligned groups of G chunks
   float* s;
-  MTB_DEV int off(int r, int n) const { return r * BN + ((((n >> 2) ^ r) & (NCH - 1)) << 2) + (n & 3); }
+  MTB_DEV int off(int r, int n) const {
+    const int c = n >> 2;
+    return r * BN + (((c & ~(G - 1)) | ((c ^ r) & (G - 1))) << 2) + (n & 3);
+  }
   MTB_DEV void put4(int r, int n, const f32x4& v) const { *reinterpret_cast<f32x4*>(s + off(r, n)) = v; }
   MTB_DEV void get8(int r, int n, float (&v)[8]) const {
     const f32x4 a = *reinterpret_cast<const f32x4*>(s + off(r, n));
@@ -310,6 +319,46 @@ MTB_DEV void epi_cols(const Epi& e, const Staged<BN>& st, int M, int N, int mc, 
   }
 }
 
+// Epilogue of a split contraction with a fused epilogue: sums the fp32
+// partial tiles of ws [splits][M][N] in split order into the staged tile, then
+// runs the same row (and column) phases as the GEMM kernel. One block per
+// BM x BN output tile.
+template <int BM, int BN, int NT, int EPI>
+__global__ __launch_bounds__(NT) void splitk_epi_kernel(int M, int N, int splits,
+                                                        const float* __restrict__ ws, Epi ep) {
+  constexpr int CR = BM * BN * 4 <= 65536 ? BM : 65536 / (BN * 4);
+  static_assert(BM % CR == 0 && CR % 64 == 0, "staging chunk");
+  __shared__ __attribute__((aligned(16))) float smem[CR * BN];
+  const Staged<BN> st{smem};
+  const int tid = threadIdx.x, tiles_n = (N + BN - 1) / BN;
+  const int m0 = (blockIdx.x / tiles_n) * BM, n0 = (blockIdx.x % tiles_n) * BN;
+  const size_t MN = (size_t)M * N;
+  for (int c0 = 0; c0 < BM; c0 += CR) {
+    if (c0 > 0) __syncthreads();
+    for (int it = tid; it < CR * BN / 8; it += NT) {
+      const int r = it / (BN / 8), nl = (it % (BN / 8)) * 8;
+      const int m = m0 + c0 + r, n = n0 + nl;
+      float v[8] = {};
+      if (m < M && n < N) {
+        const float* p = ws + (size_t)m * N + n;
+        for (int sp = 0; sp < splits; ++sp) {
+          float w[8];
+          ld8(p + sp * MN, w);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) v[q] += w[q];
+        }
+      }
+      st.put4(r, nl, f32x4{v[0], v[1], v[2], v[3]});
+      st.put4(r, nl + 4, f32x4{v[4], v[5], v[6], v[7]});
+    }
+    __syncthreads();
+    epi_rows<EPI, BN, CR, NT>(ep, st, M, N, m0 + c0, n0, tid);
+    if constexpr (EPI == EPI_STORE) {
+      if (ep.outT) epi_cols<BN, CR, NT>(ep, st, M, N, m0 + c0, n0, tid);
+    }
+  }
+}
+
 // BM x BN block tile, WGM x WGN wavefronts (each WM x WN = FM x FN 32x32
 // fragments), OCC = wavefronts per SIMD the register budget must allow
 template <int BM, int BN, int WGM, int WGN, int OCC, bool AKC, bool BKC, int EPI>
@@ -402,8 +451,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(int M, i
   // inside each 32x32 fragment (register 4q + r -> column n + r). The tile
   // goes through LDS CR rows at a time (the last k-step ended with a barrier,
   // so the operand buffers are free).
-  constexpr int CR = stage_rows(BM, 2 * (BM + BN) * BK / 2 / BN);
-  static_assert(CR >= WM && BM % CR == 0 && CR % 64 == 0, "staging chunk");
+  constexpr int CR = stage_rows(BM, WM, 2 * (BM + BN) * BK / 2 / BN, BM);
+  static_assert(CR >= WM && BM % CR == 0 && CR * BN <= (BM + BN) * BK, "staging chunk");
+  // the per-batch transposed copy (token-major left operand only) needs whole 64-token groups
+  constexpr bool COLS = EPI == EPI_STORE && AKC;
+  static_assert(!COLS || CR % 64 == 0, "transposed copy needs whole 64-token groups per chunk");
   const Staged<BN> st{reinterpret_cast<float*>(smem)};
 #pragma unroll 1
   for (int c0 = 0; c0 < BM; c0 += CR) {
@@ -429,7 +481,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(int M, i
                               m0 + c0, n0, tid);
     else
       epi_rows<EPI, BN, CR, NT>(ep, st, M, N, m0 + c0, n0, tid);
-    if constexpr (EPI == EPI_STORE) {
+    if constexpr (COLS) {
       if (ep.outT) epi_cols<BN, CR, NT>(ep, st, M, N, m0 + c0, n0, tid);
     }
   }
@@ -513,17 +565,41 @@ int wgrad_splits(int M, int N, int K) {
   return s;
 }
 
-// Tile shape per problem (measured on MI355X over the block's GEMM shapes):
-// 256x256 with 2x4 wavefronts when the problem is large and deep enough to
-// fill the chip; for the weight gradients (both operands transposed in LDS)
-// 256x128 with 4x2 wavefronts, the contraction split over several blocks
-// when there are too few tiles (given a workspace); 128x128 with 2x2
-// wavefronts otherwise.
+// Split count for a product with a token-major left operand and a plain or
+// transposed-copy store whose 128x128 tiles fill at most half of the chip's
+// two-per-CU block slots: doubled until they fill them, each split at least
+// 1024 deep; 1 = no split.
+int store_splits(int M, int N, int K) {
+  const long tiles = (long)((M + 127) / 128) * ((N + 127) / 128);
+  if (tiles > kCUs || (long)((M + 255) / 256) * ((N + 255) / 256) >= kCUs) return 1;
+  int s = 1;
+  while (s < 4 && tiles * s < 2L * kCUs && K % (2 * s * BK) == 0 && K / (2 * s) >= 1024) s *= 2;
+  return s;
+}
+
+// Fraction of the chip's block slots that `tiles` blocks keep busy over their
+// waves (slots = kCUs * blocks per CU).
+double fill(long tiles, int per_cu) {
+  const long slots = (long)kCUs * per_cu, waves = (tiles + slots - 1) / slots;
+  return (double)tiles / (double)(waves * slots);
+}
+
+// Tile shape per problem: each candidate's relative per-tile rate (measured
+// on MI355X over the block's GEMM shapes) times the fraction of the chip its
+// tile count fills; 256x256 (2x4 wavefronts) and 128x128 (2x2, two blocks
+// per CU) for the products with a k-contiguous left operand, plus 256x192
+// (4x2) when N splits into 192-wide tiles; for the weight gradients (both
+// operands transposed in LDS) 256x128 (4x2) when it fills the chip, the
+// contraction split over several blocks when too few tiles remain (given a
+// workspace), else 128x128.
+// (Tiles for 6 wavefronts fill the chip better at N = 1536 but leave two of
+// a CU's four SIMDs with twice the work: measured slower.)
 template <bool AKC, bool BKC, int EPI>
 hipError_t launch_bf16(int M, int N, int K, const void* A, int lda, const void* B, int ldb,
                        const Epi& e, hipStream_t st) {
-  const long t256 = (long)((M + 255) / 256) * ((N + 255) / 256);
-  const long t256x128 = (long)((M + 255) / 256) * ((N + 127) / 128);
+  auto tl = [&](int bm, int bn) { return (long)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+  const double f128 = 0.85 * fill(tl(128, 128), 2);
+  if (!AKC && e.outT) return hipErrorInvalidValue;  // the transposed copy is token-major only
   if constexpr (!AKC && !BKC && EPI == EPI_STORE) {
     const int ks = e.ws ? wgrad_splits(M, N, K) : 1;
     if (ks > 1) {
@@ -535,11 +611,33 @@ hipError_t launch_bf16(int M, int N, int K, const void* A, int lda, const void* 
                          M, N, ks, (const float*)e.ws, (bf16_t*)e.out, e.ldo);
       return hipGetLastError();
     }
-    if (t256x128 >= kCUs && K >= 1024)
+    // 256x128 only when it fills the chip: at two blocks per CU, 128x128
+    // tiles beat a partly filled 256x128 grid (measured 158 vs 175 us for the
+    // 1536 x 4096 x 8192 QKV weight gradient)
+    if (K >= 1024 && tl(256, 128) >= kCUs)
       return launch_cfg<256, 128, 4, 2, 1, AKC, BKC, EPI>(M, N, K, A, lda, B, ldb, e, st);
   } else {
-    if (t256 >= 128 && K >= 1024)
-      return launch_cfg<256, 256, 2, 4, 1, AKC, BKC, EPI>(M, N, K, A, lda, B, ldb, e, st);
+    if constexpr (AKC && EPI == EPI_STORE) {
+      const int ks = e.ws ? store_splits(M, N, K) : 1;
+      if (ks > 1) {
+        hipError_t r = launch_cfg<128, 128, 2, 2, 2, AKC, BKC, EPI_PARTIAL>(M, N, K, A, lda, B, ldb,
+                                                                             e, st, ks);
+        if (r != hipSuccess) return r;
+        hipLaunchKernelGGL((splitk_epi_kernel<128, 128, 256, EPI_STORE>), dim3((unsigned)tl(128, 128)),
+                           dim3(256), 0, st, M, N, ks, (const float*)e.ws, e);
+        return hipGetLastError();
+      }
+    }
+    if (K >= 512) {
+      const double f256 = 1.0 * fill(tl(256, 256), 1);
+      double f192 = 0.0;
+      if constexpr (AKC && BKC && EPI == EPI_STORE) f192 = N % 192 == 0 ? 0.95 * fill(tl(256, 192), 1) : 0.0;
+      if constexpr (AKC && BKC && EPI == EPI_STORE)
+        if (f192 > f256 && f192 > f128)
+          return launch_cfg<256, 192, 4, 2, 1, AKC, BKC, EPI>(M, N, K, A, lda, B, ldb, e, st);
+      if (f256 >= f128)
+        return launch_cfg<256, 256, 2, 4, 1, AKC, BKC, EPI>(M, N, K, A, lda, B, ldb, e, st);
+    }
   }
   return launch_cfg<128, 128, 2, 2, 2, AKC, BKC, EPI>(M, N, K, A, lda, B, ldb, e, st);
 }
@@ -547,8 +645,10 @@ hipError_t launch_bf16(int M, int N, int K, const void* A, int lda, const void* 
 }  // namespace
 
 size_t gemm_ws_bytes(int dtype, int M, int N, int K, bool a_kc, bool b_kc, int kind) {
-  if (dtype == 0 || a_kc || b_kc || kind != EPI_STORE || M <= 0 || N <= 0) return 0;
-  const int ks = wgrad_splits(M, N, K);
+  if (dtype == 0 || kind != EPI_STORE || M <= 0 || N <= 0) return 0;
+  int ks = 1;
+  if (!a_kc && !b_kc) ks = wgrad_splits(M, N, K);
+  else if (a_kc) ks = store_splits(M, N, K);
   return ks > 1 ? (size_t)ks * M * N * 4 : 0;
 }
 

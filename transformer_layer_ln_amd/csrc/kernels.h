@@ -39,9 +39,10 @@ struct Epi {
 hipError_t gemm(int dtype, int M, int N, int K, const void* A, int lda, bool a_kc,
                 const void* B, int ldb, bool b_kc, const Epi& e, hipStream_t st);
 // Bytes of Epi::ws that gemm() uses to split the contraction of this product
-// over several workgroups per output tile (0: it does not split). Only weight
-// gradients (both operands transposed, plain store) with too few tiles to fill
-// the chip are split; the partial tiles are summed in a fixed order.
+// over several workgroups per output tile (0: it does not split). Plain-store
+// products (weight gradients; token-major products, also with the transposed
+// copy) with too few tiles to fill the chip are split; the partial tiles are
+// summed in a fixed order.
 size_t gemm_ws_bytes(int dtype, int M, int N, int K, bool a_kc, bool b_kc, int kind);
 
 // LayerNorm over rows of width H: hsum = x (+resid) (+bias) rounded to dtype;
