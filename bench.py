@@ -14,6 +14,12 @@ The default workload is the seq-2048 rank share (the metric's target
 configuration); --workload seq512 times the seq-512 TP=4 share (hidden 1024,
 4 heads x 64, ffn chunk 1024, batch 8) and seq4096 the SwiGLU/GQA share.
 
+Besides the headline step it reports per-step median/p10/p90, the pages'
+attention / FFN / backward segment times (library segment events), LN
+forward/backward and attention-forward kernel rates, and the vocab-parallel
+cross-entropy (partial + loss + gradient) on one [8192 x 16032] vocab shard
+against HBM bandwidth.
+
 --calibrate-copy runs only a plain device-to-device copy of MIB MiB, five
 times, so that rocprofv3's FETCH_SIZE / WRITE_SIZE counters can be scaled
 against a kernel whose HBM traffic is known (MIB MiB read + MIB MiB written
@@ -75,11 +81,19 @@ def calibrate_copy(mib):
     n = mib * (1 << 20) // 4
     src = torch.ones(n, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
-    for _ in range(5):
+    st = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    dst.copy_(src)
+    e0.record(st)
+    for _ in range(4):
         dst.copy_(src)
+    e1.record(st)
     torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 4
     print(json.dumps({"copy_mib": mib, "launches": 5, "bytes_read_per_launch": n * 4,
-                      "bytes_written_per_launch": n * 4}), flush=True)
+                      "bytes_written_per_launch": n * 4, "avg_ms": round(ms, 4),
+                      "GBs_read_plus_write": round(2 * n * 4 / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 WORKLOADS = {
     "seq2048": ("C4", "TP=8 rank share of a hidden-4096 block: 4 local heads x 128, ffn chunk 2048, "
@@ -103,6 +117,10 @@ def model_flops(cfg) -> float:
 
 
 def run_gpu(cfg, steps, warmup, trace_what=None):
+    """Times `steps` fwd+bwd steps (one event pair around the whole timed
+    region and one per step); returns (mean ms, per-step ms list, wall s,
+    {trace: mean ms}). The first trace is armed during the timed steps, the
+    others during extra passes outside the timed region."""
     import torch
 
     from transformer_layer_ln_amd import inputs, mtb
@@ -126,28 +144,23 @@ def run_gpu(cfg, steps, warmup, trace_what=None):
         step()
     torch.cuda.synchronize()
     st = torch.cuda.current_stream()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    traces = {}
-    ctx = []
-    for what in (trace_what or []):
-        traces[what] = mtb.Trace(what, steps)
-    # one trace can be armed at a time: time the step with the first, then
-    # run extra armed passes for the others outside the timed region
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    traces = {what: mtb.Trace(what, steps) for what in (trace_what or [])}
     first = next(iter(traces.values()), None)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     if first is not None:
         first.__enter__()
-    t0.record(st)
-    for _ in range(steps):
+    ev[0].record(st)
+    for i in range(steps):
         step()
-    t1.record(st)
+        ev[i + 1].record(st)
     if first is not None:
         first.__exit__(None, None, None)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms = t0.elapsed_time(t1) / steps
+    ms = ev[0].elapsed_time(ev[steps]) / steps
+    per_step = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
     kern = {}
     for what, tr in traces.items():
         if tr is not first:
@@ -156,7 +169,42 @@ def run_gpu(cfg, steps, warmup, trace_what=None):
                     step()
         kern[what] = tr.mean_ms()
     assert torch.isfinite(out.float()).all() and torch.isfinite(dx.float()).all()
-    return ms, wall, kern
+    return ms, per_step, wall, kern
+
+
+def run_xent(xcfg, steps, warmup):
+    """X1-X3 on one vocab shard: mtb_vocab_xent(MTB_XENT_ALL) with the
+    identity reduction (one shard's statistics are final), loss and the
+    logit gradient into a separate buffer. Returns mean ms per call."""
+    import torch
+
+    from transformer_layer_ln_amd import inputs, mtb
+
+    dev = torch.device("cuda")
+    n, v = xcfg.n_tokens, xcfg.v_local
+    z = torch.as_tensor(inputs.xent_logits(xcfg, 0)).to(dev, torch.bfloat16)
+    y = torch.as_tensor(inputs.xent_targets(xcfg)).to(dev)
+    dl = torch.as_tensor(inputs.xent_dloss(xcfg)).to(dev)
+    stats = torch.empty(4 * n, dtype=torch.float32, device=dev)
+    loss = torch.empty(n, dtype=torch.float32, device=dev)
+    dz = torch.empty_like(z)
+
+    def call():
+        mtb.vocab_xent(n, v, 0, mtb.BF16, mtb.XENT_ALL, z, y, stats, loss, dl, dz)
+
+    for _ in range(warmup):
+        call()
+    st = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(st)
+    for _ in range(steps):
+        call()
+    e1.record(st)
+    torch.cuda.synchronize()
+    assert torch.isfinite(loss).all()
+    return e0.elapsed_time(e1) / steps
 
 
 def cpu_baseline(cfg, budget_s=20.0):
@@ -216,9 +264,13 @@ def main():
     key, desc, par = WORKLOADS[args.workload]
     cfg = inputs.CONFIGS[key]
     flops = model_flops(cfg)
-    ms, wall, kern = run_gpu(cfg, args.steps, args.warmup,
-                             trace_what=[mtb.TRACE_FC1_FWD, mtb.TRACE_LN1_FWD, mtb.TRACE_ATTN_FWD])
+    ms, per_step, wall, kern = run_gpu(
+        cfg, args.steps, args.warmup,
+        trace_what=[mtb.TRACE_FC1_FWD, mtb.TRACE_LN1_FWD, mtb.TRACE_ATTN_FWD, mtb.TRACE_ATTN_SEG,
+                    mtb.TRACE_FFN_SEG, mtb.TRACE_BWD, mtb.TRACE_LN1_BWD])
     tflops = flops / (ms * 1e-3) / 1e12
+    srt = sorted(per_step)
+    pct = lambda q: srt[min(len(srt) - 1, int(q * (len(srt) - 1) + 0.5))]
 
     T, H, F = cfg.tokens, cfg.hidden, cfg.ffn
     Fu = 2 * F if cfg.act == "swiglu" else F
@@ -230,6 +282,11 @@ def main():
     attn_pairs = cfg.seq * (cfg.seq + 1) // 2 if cfg.causal else cfg.seq * cfg.seq
     attn_flops = 4.0 * cfg.head_dim * attn_pairs * cfg.batch * cfg.q_heads
     attn_ms = kern[mtb.TRACE_ATTN_FWD]
+    lnb_bytes = T * H * 2 * 4 + T * 8          # read dy, x, dres, write dx (bf16), read mu/rstd
+    lnb_ms = kern[mtb.TRACE_LN1_BWD]
+    xcfg = inputs.C5_XENT
+    xent_ms = run_xent(xcfg, args.steps, args.warmup)
+    xent_bytes = 6 * xcfg.n_tokens * xcfg.v_local   # X1 reads 2 B/logit, X3 reads 2 + writes 2
 
     res = {
         "metric": f"block fwd+bwd TFLOP/s (one TP-rank shard, bf16) at seq {cfg.seq}",
@@ -239,6 +296,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_median": round(pct(0.5), 4),
+        "ms_per_step_p10": round(pct(0.1), 4),
+        "ms_per_step_p90": round(pct(0.9), 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -262,7 +322,24 @@ def main():
                         "peak_GBs": PEAK_HBM_GBS},
             "attn_fwd": {"bound": "mfma", "avg_ms": round(attn_ms, 5),
                          "achieved_TFLOPs": round(attn_flops / (attn_ms * 1e-3) / 1e12, 1)},
+            "ln1_bwd": {"bound": "hbm", "avg_ms": round(lnb_ms, 5),
+                        "achieved_GBs": round(lnb_bytes / (lnb_ms * 1e-3) / 1e9, 1),
+                        "peak_GBs": PEAK_HBM_GBS},
+            "vocab_xent": {"bound": "hbm", "workload": (
+                               f"one vocab shard [{xcfg.n_tokens} x {xcfg.v_local}] bf16 of "
+                               f"V={xcfg.vocab} over TP={xcfg.tp}: partial (max, sum exp, target "
+                               "logit) + loss + logit gradient, identity reduction"),
+                           "avg_ms": round(xent_ms, 5),
+                           "achieved_GBs": round(xent_bytes / (xent_ms * 1e-3) / 1e9, 1),
+                           "peak_GBs": PEAK_HBM_GBS},
         },
+        # the pages' breakdown (attention / FFN / backward), timed by the
+        # library's segment events; the pages' own figures are context only
+        "segments_ms": {"attention_fwd": round(kern[mtb.TRACE_ATTN_SEG], 4),
+                        "ffn_fwd": round(kern[mtb.TRACE_FFN_SEG], 4),
+                        "backward": round(kern[mtb.TRACE_BWD], 4)},
+        "context_pages": ("seq 512 on 4 unspecified GPUs, PyTorch eager: attention 18.42 ms, "
+                          "FFN 21.76 ms, backward 40.35 ms per step"),
         "wall_s_timed": round(wall, 3),
     }
     if not args.no_cpu_baseline:

@@ -246,6 +246,12 @@ mtb_status mtb_vocab_xent_combine(int64_t n_tokens, int32_t n_shards, const floa
 #define MTB_TRACE_ATTN_FWD 2  /* attention forward */
 #define MTB_TRACE_LN1_FWD 3   /* input LayerNorm forward */
 #define MTB_TRACE_FC2_WGRAD 4 /* fc2 weight-gradient GEMM */
+/* Segments of MTB_PHASE_ALL calls (the attention / FFN / backward breakdown
+ * of [Lab06] sec. 4): */
+#define MTB_TRACE_ATTN_SEG 5  /* forward LN1 .. projection (with the fused residual) */
+#define MTB_TRACE_FFN_SEG 6   /* forward LN2 .. fc2 (with the residual) */
+#define MTB_TRACE_BWD 7       /* the whole backward call */
+#define MTB_TRACE_LN1_BWD 8   /* input LayerNorm backward + residual-gradient add */
 mtb_status mtb_trace_arm(int32_t what, void *const *begin_events, void *const *end_events, int32_t n);
 int32_t mtb_trace_disarm(void);
 

@@ -214,7 +214,7 @@ extern "C" {
 const char* mtb_last_error(void) { return g_err.c_str(); }
 
 mtb_status mtb_trace_arm(int32_t what, void* const* begin_events, void* const* end_events, int32_t n) {
-  if (what < MTB_TRACE_NONE || what > MTB_TRACE_FC2_WGRAD || n < 0)
+  if (what < MTB_TRACE_NONE || what > MTB_TRACE_LN1_BWD || n < 0)
     return fail(MTB_EINVAL, "bad trace request");
   if (n > 0 && (!begin_events || !end_events)) return fail(MTB_EINVAL, "trace events are NULL");
   g_trace.what = what;
@@ -274,7 +274,9 @@ mtb_status mtb_block_fwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
   void* c = P(saved, L.c); void* u = P(saved, L.u); void* m = P(saved, L.m);
   void* p = P(scratch, Z.p);
 
+  const bool all = phase == MTB_PHASE_ALL;
   if (phase == MTB_PHASE_ALL || phase == MTB_PHASE_SEG0) {
+    if (all) trace_begin(MTB_TRACE_ATTN_SEG, st);
     // (2) input LayerNorm
     trace_begin(MTB_TRACE_LN1_FWD, st);
     MTB_HIP(ln_fwd(dt, T, H, x, nullptr, nullptr, w->ln1_g, w->ln1_b, nullptr, a, mu1, rs1, d.eps, st));
@@ -297,9 +299,13 @@ mtb_status mtb_block_fwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
     MTB_HIP(gemm(dt, T, H, NO, O, NO, true, w->w_o, NO, true, ep, st));
     if (phase == MTB_PHASE_SEG0) return MTB_OK;
     if (fused) {
+      trace_end(MTB_TRACE_ATTN_SEG, st);
+      trace_begin(MTB_TRACE_FFN_SEG, st);
       MTB_HIP(ln_fwd(dt, T, H, h, nullptr, nullptr, w->ln2_g, w->ln2_b, nullptr, c, mu2, rs2, d.eps, st));
     } else {
       if ((s = call_hook(comm, p, d.T * d.H, dt, MTB_OP_SUM, st)) != MTB_OK) return s;
+      trace_end(MTB_TRACE_ATTN_SEG, st);
+      trace_begin(MTB_TRACE_FFN_SEG, st);
       MTB_HIP(ln_fwd(dt, T, H, x, p, w->b_o, w->ln2_g, w->ln2_b, h, c, mu2, rs2, d.eps, st));
     }
   } else if (phase == MTB_PHASE_SEG1) {
@@ -330,9 +336,11 @@ mtb_status mtb_block_fwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
       e.out = phase == MTB_PHASE_SEG1 ? out : p; e.ldo = H;
     }
     MTB_HIP(gemm(dt, T, H, F, m, F, true, w->w_fc2, F, true, e, st));
+    if (fused) trace_end(MTB_TRACE_FFN_SEG, st);
     if (fused || phase == MTB_PHASE_SEG1) return MTB_OK;
     if ((s = call_hook(comm, p, d.T * d.H, dt, MTB_OP_SUM, st)) != MTB_OK) return s;
     MTB_HIP(add3(dt, T, H, h, p, w->b_fc2, out, st));
+    trace_end(MTB_TRACE_FFN_SEG, st);
     return MTB_OK;
   }
   // SEG2: out = h + sum(p_mlp) + b2
@@ -391,6 +399,8 @@ mtb_status mtb_block_bwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
   float* part = (float*)P(scratch, Z.part); float* red = (float*)P(scratch, Z.red);
   void* ws = Z.total > Z.ws ? P(scratch, Z.ws) : nullptr;
   const void* G = dout;
+  const bool all = phase == MTB_PHASE_ALL;
+  if (all) trace_begin(MTB_TRACE_BWD, st);
 
   if (phase == MTB_PHASE_ALL || phase == MTB_PHASE_SEG0) {
     // fc2 backward: dm = G W2 with the activation's derivative fused (bf16)
@@ -464,9 +474,12 @@ mtb_status mtb_block_bwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
 
   // LN1 backward + residual: dx = dh + LN1^T(da)
   const void* da = phase == MTB_PHASE_SEG2 ? reduced_in : p;
+  trace_begin(MTB_TRACE_LN1_BWD, st);
   MTB_HIP(ln_bwd(dt, T, H, da, x, mu1, rs1, w->ln1_g, dh, dx, st));
+  trace_end(MTB_TRACE_LN1_BWD, st);
   if (g.ln1_g) MTB_HIP(colsum(dt, T, H, da, H, x, mu1, rs1, g.ln1_g, red, st));
   if (g.ln1_b) MTB_HIP(colsum(dt, T, H, da, H, nullptr, nullptr, nullptr, g.ln1_b, red, st));
+  if (all) trace_end(MTB_TRACE_BWD, st);
   return MTB_OK;
 }
 

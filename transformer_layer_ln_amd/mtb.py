@@ -29,6 +29,7 @@ EXPORTS = ("mtb_block_saved_bytes", "mtb_block_scratch_bytes", "mtb_block_fwd", 
            "mtb_vocab_xent", "mtb_vocab_xent_combine", "mtb_trace_arm", "mtb_trace_disarm",
            "mtb_last_error")
 TRACE_NONE, TRACE_FC1_FWD, TRACE_ATTN_FWD, TRACE_LN1_FWD, TRACE_FC2_WGRAD = 0, 1, 2, 3, 4
+TRACE_ATTN_SEG, TRACE_FFN_SEG, TRACE_BWD, TRACE_LN1_BWD = 5, 6, 7, 8
 
 
 class MtbError(RuntimeError):
