@@ -9,6 +9,7 @@ GELU). Prints ONE JSON line.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                     [--workload seq2048|seq512|seq4096]
     python bench.py --calibrate-copy MIB
+    python bench.py --sweep
 
 The default workload is the seq-2048 rank share (the metric's target
 configuration); --workload seq512 times the seq-512 TP=4 share (hidden 1024,
@@ -19,6 +20,9 @@ attention / FFN / backward segment times (library segment events), LN
 forward/backward and attention-forward kernel rates, and the vocab-parallel
 cross-entropy (partial + loss + gradient) on one [8192 x 16032] vocab shard
 against HBM bandwidth.
+
+--sweep times the seq-512 share at seq 128/256/512/1024 and fits the
+log-log slopes of the attention / FFN / backward times against seq.
 
 --calibrate-copy runs only a plain device-to-device copy of MIB MiB, five
 times, so that rocprofv3's FETCH_SIZE / WRITE_SIZE counters can be scaled
@@ -102,7 +106,50 @@ WORKLOADS = {
                      "batch 8, seq 512, GELU", "one tp4 rank share"),
     "seq4096": ("C5", "TP=8 rank share of a hidden-4096 SwiGLU/GQA block: 4 q / 1 kv heads x 128, "
                       "ffn chunk 1792 (gate+up 3584), batch 2, seq 4096", "one tp8 rank share"),
+    "seq4096-causal": ("C5c", "TP=8 rank share of a hidden-4096 SwiGLU/GQA block: 4 q / 1 kv heads x "
+                              "128, ffn chunk 1792 (gate+up 3584), batch 2, seq 4096, causal",
+                       "one tp8 rank share"),
 }
+
+
+def workload_cfg(key):
+    from transformer_layer_ln_amd import inputs
+
+    if key == "C5c":
+        return inputs.C5.with_(name="C5-tp8-s4096-swiglu-gqa-causal", causal=True)
+    return inputs.CONFIGS[key]
+
+
+def seq_sweep(steps, warmup):
+    """The seq-512 TP=4 share at seq 128/256/512/1024 (batch 8): the pages'
+    attention / FFN / backward segments per seq, and their log-log slopes
+    against seq (attention kernel ~ s^2, FFN ~ s)."""
+    import numpy as np
+
+    from transformer_layer_ln_amd import inputs, mtb
+
+    pts = []
+    for sq in inputs.C3_SEQS:
+        cfg = inputs.C3(sq)
+        ms_e, _, _, kern, graph = run_gpu(cfg, steps, warmup,
+                                          trace_what=[mtb.TRACE_ATTN_FWD, mtb.TRACE_ATTN_SEG,
+                                                      mtb.TRACE_FFN_SEG, mtb.TRACE_BWD],
+                                          graph_steps=steps)
+        ms = graph[0]
+        pts.append({"seq": sq, "tokens": cfg.tokens, "ms_per_step": round(ms, 4),
+                    "ms_per_step_eager": round(ms_e, 4),
+                    "attention_kernel_ms": round(kern[mtb.TRACE_ATTN_FWD], 5),
+                    "attention_segment_ms": round(kern[mtb.TRACE_ATTN_SEG], 5),
+                    "ffn_segment_ms": round(kern[mtb.TRACE_FFN_SEG], 5),
+                    "backward_ms": round(kern[mtb.TRACE_BWD], 5),
+                    "TFLOPs": round(model_flops(cfg) / (ms * 1e-3) / 1e12, 2)})
+    ls = np.log([p["seq"] for p in pts])
+    slope = lambda k: round(float(np.polyfit(ls, np.log([p[k] for p in pts]), 1)[0]), 3)
+    return {"sweep": "seq", "workload": ("TP=4 rank share of a hidden-1024 block: 4 local heads x 64, "
+                                         "ffn chunk 1024, batch 8, GELU, seq 128/256/512/1024"),
+            "steps": steps, "warmup": warmup, "points": pts,
+            "loglog_slope_vs_seq": {k: slope(k) for k in ("attention_kernel_ms", "attention_segment_ms",
+                                                           "ffn_segment_ms", "backward_ms")}}
 
 
 def model_flops(cfg) -> float:
@@ -116,11 +163,13 @@ def model_flops(cfg) -> float:
     return 3.0 * fwd
 
 
-def run_gpu(cfg, steps, warmup, trace_what=None):
+def run_gpu(cfg, steps, warmup, trace_what=None, graph_steps=0):
     """Times `steps` fwd+bwd steps (one event pair around the whole timed
     region and one per step); returns (mean ms, per-step ms list, wall s,
-    {trace: mean ms}). The first trace is armed during the timed steps, the
-    others during extra passes outside the timed region."""
+    {trace: mean ms}, graph) with graph = (mean ms, per-step ms) of
+    `graph_steps` replays of the step captured in a HIP graph, or None. The
+    first trace is armed during the timed eager steps, the others during
+    extra passes."""
     import torch
 
     from transformer_layer_ln_amd import inputs, mtb
@@ -169,7 +218,26 @@ def run_gpu(cfg, steps, warmup, trace_what=None):
                     step()
         kern[what] = tr.mean_ms()
     assert torch.isfinite(out.float()).all() and torch.isfinite(dx.float()).all()
-    return ms, per_step, wall, kern
+    graph = None
+    if graph_steps:
+        # the same step captured once in a HIP graph and replayed: the kernels
+        # and buffers are identical, only the per-launch host work is gone
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(warmup):
+            g.replay()
+        gev = [torch.cuda.Event(enable_timing=True) for _ in range(graph_steps + 1)]
+        torch.cuda.synchronize()
+        gev[0].record(st)
+        for i in range(graph_steps):
+            g.replay()
+            gev[i + 1].record(st)
+        torch.cuda.synchronize()
+        graph = (gev[0].elapsed_time(gev[graph_steps]) / graph_steps,
+                 [gev[i].elapsed_time(gev[i + 1]) for i in range(graph_steps)])
+        assert torch.isfinite(out.float()).all() and torch.isfinite(dx.float()).all()
+    return ms, per_step, wall, kern, graph
 
 
 def run_xent(xcfg, steps, warmup):
@@ -249,6 +317,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--workload", default="seq2048", choices=sorted(WORKLOADS))
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB")
+    ap.add_argument("--sweep", action="store_true", help="seq 128..1024 sweep of the seq-512 share")
+    ap.add_argument("--eager", action="store_true", help="time eager library calls, not graph replays")
     args = ap.parse_args()
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
@@ -261,13 +331,18 @@ def main():
 
     from transformer_layer_ln_amd import inputs, mtb
 
+    if args.sweep:
+        print(json.dumps(seq_sweep(args.steps, args.warmup)), flush=True)
+        return
     key, desc, par = WORKLOADS[args.workload]
-    cfg = inputs.CONFIGS[key]
+    cfg = workload_cfg(key)
     flops = model_flops(cfg)
-    ms, per_step, wall, kern = run_gpu(
+    ms_eager, per_step_eager, wall, kern, graph = run_gpu(
         cfg, args.steps, args.warmup,
         trace_what=[mtb.TRACE_FC1_FWD, mtb.TRACE_LN1_FWD, mtb.TRACE_ATTN_FWD, mtb.TRACE_ATTN_SEG,
-                    mtb.TRACE_FFN_SEG, mtb.TRACE_BWD, mtb.TRACE_LN1_BWD])
+                    mtb.TRACE_FFN_SEG, mtb.TRACE_BWD, mtb.TRACE_LN1_BWD],
+        graph_steps=0 if args.eager else args.steps)
+    ms, per_step = (ms_eager, per_step_eager) if graph is None else graph
     tflops = flops / (ms * 1e-3) / 1e12
     srt = sorted(per_step)
     pct = lambda q: srt[min(len(srt) - 1, int(q * (len(srt) - 1) + 0.5))]
@@ -299,6 +374,9 @@ def main():
         "ms_per_step_median": round(pct(0.5), 4),
         "ms_per_step_p10": round(pct(0.1), 4),
         "ms_per_step_p90": round(pct(0.9), 4),
+        "launch": ("eager: one library call per fwd and per bwd" if graph is None else
+                   "HIP graph: one fwd+bwd step captured once, replayed per step"),
+        "ms_per_step_eager": round(ms_eager, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

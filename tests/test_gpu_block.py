@@ -96,3 +96,52 @@ def test_gpu_results_are_deterministic():
     assert np.array_equal(r1[0], r2[0]) and np.array_equal(r1[1], r2[1])
     for k in r1[2]:
         assert np.array_equal(r1[2][k], r2[2][k]), k
+
+
+def _graph_case(cfg):
+    """Eager fwd+bwd, then the same step captured in a HIP graph and replayed
+    three times with eager work and synchronisations in between; every replay
+    must reproduce the eager results bit for bit."""
+    import torch
+
+    w_split, x, G = _case(cfg)
+    dev = torch.device("cuda")
+    dt = torch.bfloat16
+    blk = mtb.BlockShard(mtb.cfg_from(cfg), mtb.device_weights(w_split, cfg.act, dt, dev), dev)
+    xd = torch.as_tensor(x).to(dev, dt)
+    Gd = torch.as_tensor(G).to(dev, dt)
+    out = torch.empty_like(xd)
+    dx = torch.empty_like(xd)
+    grads = blk.grad_buffers()
+    blk.fwd(xd, out)
+    blk.bwd(xd, Gd, dx, grads)
+    torch.cuda.synchronize()
+    ref = [out.clone(), dx.clone()] + [grads[k].clone() for k in sorted(grads)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        blk.fwd(xd, out)
+        blk.bwd(xd, Gd, dx, grads)
+    for rep in range(3):
+        for t in [out, dx] + list(grads.values()):
+            t.fill_(float("nan"))            # eager work between the replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [out, dx] + [grads[k] for k in sorted(grads)]
+        for i, (a, b) in enumerate(zip(got, ref)):
+            assert torch.equal(a, b), f"replay {rep}, tensor {i}"
+    say(f"   3 graph replays equal the eager step ({len(ref)} tensors)")
+
+
+@pytest.mark.gpu
+def test_graph_replay_matches_eager_step():
+    cfg = inputs.BlockConfig("graph", batch=2, seq=256, hidden=512, q_heads=4, kv_heads=2,
+                             head_dim=64, ffn=512, act="swiglu", causal=True, seed=2200)
+    say("[gpu] graph replay", cfg)
+    _graph_case(cfg)
+
+
+@pytest.mark.gpu
+def test_graph_replay_matches_eager_step_seq512_share():
+    say("[gpu] graph replay, seq-512 TP=4 share")
+    _graph_case(inputs.C2)

@@ -130,17 +130,27 @@ Scratch scratch_layout(const Dims& d) {
   int64_t nmax = d.H > d.Fu ? d.H : d.Fu;
   if (d.Nqkv > nmax) nmax = d.Nqkv;
   s.red = o; o += al((size_t)colsum_splits((int)d.T) * nmax * 4);
-  // split-contraction partial tiles of the weight gradients (one at a time)
-  const int dt = d.dt, T32 = (int)d.T, H = (int)d.H;
-  size_t ws = gemm_ws_bytes(dt, (int)d.Nqkv, H, T32, false, false, EPI_STORE);
-  const size_t wo = gemm_ws_bytes(dt, H, (int)d.NO, T32, false, false, EPI_STORE);
-  const size_t w1 = gemm_ws_bytes(dt, (int)d.Fu, H, T32, false, false, EPI_STORE);
-  const size_t w2 = gemm_ws_bytes(dt, H, (int)d.F, T32, false, false, EPI_STORE);
-  const size_t wd = gemm_ws_bytes(dt, T32, (int)d.NO, H, true, false, EPI_STORE);  // projection dgrad
-  if (wd > ws) ws = wd;
-  if (wo > ws) ws = wo;
-  if (w1 > ws) ws = w1;
-  if (w2 > ws) ws = w2;
+  // split-contraction partial tiles (one GEMM at a time): the largest any
+  // GEMM of the block asks for
+  const int dt = d.dt, T32 = (int)d.T, H = (int)d.H, Nq = (int)d.Nqkv, NO = (int)d.NO,
+            F = (int)d.F, Fu = (int)d.Fu;
+  const int act_f = d.act == MTB_ACT_GELU ? EPI_GELU : EPI_SWIGLU;
+  const int act_b = d.act == MTB_ACT_GELU ? EPI_DGELU : EPI_DSWIGLU;
+  const size_t need[] = {
+      gemm_ws_bytes(dt, T32, Nq, H, true, true, EPI_STORE),    // QKV
+      gemm_ws_bytes(dt, T32, H, NO, true, true, EPI_STORE),    // projection
+      gemm_ws_bytes(dt, T32, Fu, H, true, true, act_f),        // fc1
+      gemm_ws_bytes(dt, T32, H, F, true, true, EPI_STORE),     // fc2
+      gemm_ws_bytes(dt, T32, F, H, true, false, act_b),        // fc2 dgrad
+      gemm_ws_bytes(dt, T32, H, Fu, true, false, EPI_STORE),   // fc1 dgrad
+      gemm_ws_bytes(dt, T32, NO, H, true, false, EPI_STORE),   // projection dgrad
+      gemm_ws_bytes(dt, T32, H, Nq, true, false, EPI_STORE),   // QKV dgrad
+      gemm_ws_bytes(dt, H, F, T32, false, false, EPI_STORE),   // weight gradients
+      gemm_ws_bytes(dt, Fu, H, T32, false, false, EPI_STORE),
+      gemm_ws_bytes(dt, H, NO, T32, false, false, EPI_STORE),
+      gemm_ws_bytes(dt, Nq, H, T32, false, false, EPI_STORE)};
+  size_t ws = 0;
+  for (size_t v : need) ws = v > ws ? v : ws;
   s.ws = o; o += al(ws);
   s.total = o;
   return s;
@@ -273,6 +283,7 @@ mtb_status mtb_block_fwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
   void* h = P(saved, L.h); float* mu2 = (float*)P(saved, L.mu2); float* rs2 = (float*)P(saved, L.rs2);
   void* c = P(saved, L.c); void* u = P(saved, L.u); void* m = P(saved, L.m);
   void* p = P(scratch, Z.p);
+  void* ws = Z.total > Z.ws ? P(scratch, Z.ws) : nullptr;
 
   const bool all = phase == MTB_PHASE_ALL;
   if (phase == MTB_PHASE_ALL || phase == MTB_PHASE_SEG0) {
@@ -283,7 +294,7 @@ mtb_status mtb_block_fwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
     trace_end(MTB_TRACE_LN1_FWD, st);
     // column-parallel QKV; the bf16 path also keeps a per-batch transpose for attention
     Epi e;
-    e.out = qkv; e.ldo = Nq; e.bias = w->b_qkv; e.outT = qkvT; e.S = S;
+    e.out = qkv; e.ldo = Nq; e.bias = w->b_qkv; e.outT = qkvT; e.S = S; e.ws = ws;
     MTB_HIP(gemm(dt, T, Nq, H, a, H, true, w->w_qkv, H, true, e, st));
     // per-head attention over the local heads
     trace_begin(MTB_TRACE_ATTN_FWD, st);
@@ -291,6 +302,7 @@ mtb_status mtb_block_fwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
     trace_end(MTB_TRACE_ATTN_FWD, st);
     // row-parallel projection: a partial sum, reduced at g1
     Epi ep;
+    ep.ws = ws;
     if (fused) {  // identity reduction: fuse (4) residual and the bias
       ep.out = h; ep.ldo = H; ep.bias = w->b_o; ep.resid = x; ep.ldr = H;
     } else {
@@ -318,7 +330,7 @@ mtb_status mtb_block_fwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
     if (bf) {
       Epi e;
       e.kind = d.act == MTB_ACT_GELU ? EPI_GELU : EPI_SWIGLU;
-      e.out = u; e.ldo = Fu; e.out2 = m; e.ldo2 = F; e.bias = w->b_fc1;
+      e.out = u; e.ldo = Fu; e.out2 = m; e.ldo2 = F; e.bias = w->b_fc1; e.ws = ws;
       trace_begin(MTB_TRACE_FC1_FWD, st);
       MTB_HIP(gemm(dt, T, Fu, H, c, H, true, w->w_fc1, H, true, e, st));
       trace_end(MTB_TRACE_FC1_FWD, st);
@@ -330,6 +342,7 @@ mtb_status mtb_block_fwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
     }
     // (6) row-parallel fc2: a partial sum, reduced at g2; (7) residual
     Epi e;
+    e.ws = ws;
     if (fused) {
       e.out = out; e.ldo = H; e.bias = w->b_fc2; e.resid = h; e.ldr = H;
     } else {
@@ -407,7 +420,7 @@ mtb_status mtb_block_bwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
     if (bf) {
       Epi e;
       e.kind = d.act == MTB_ACT_GELU ? EPI_DGELU : EPI_DSWIGLU;
-      e.out = du; e.ldo = Fu; e.aux = u; e.ldaux = Fu;
+      e.out = du; e.ldo = Fu; e.aux = u; e.ldaux = Fu; e.ws = ws;
       MTB_HIP(gemm(dt, T, F, H, G, H, true, w->w_fc2, F, false, e, st));
     } else {
       Epi e;
@@ -431,7 +444,7 @@ mtb_status mtb_block_bwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
     if (g.b_fc1) MTB_HIP(colsum(dt, T, Fu, du, Fu, nullptr, nullptr, nullptr, g.b_fc1, red, st));
     // fc1 input gradient: partial over ranks, summed at f1
     Epi e;
-    e.out = phase == MTB_PHASE_SEG0 ? dx : p; e.ldo = H;
+    e.out = phase == MTB_PHASE_SEG0 ? dx : p; e.ldo = H; e.ws = ws;
     MTB_HIP(gemm(dt, T, H, Fu, du, Fu, true, w->w_fc1, H, false, e, st));
     if (phase == MTB_PHASE_SEG0) return MTB_OK;
     if ((s = call_hook(comm, p, d.T * d.H, dt, MTB_OP_SUM, st)) != MTB_OK) return s;
@@ -466,7 +479,7 @@ mtb_status mtb_block_bwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
     if (g.b_qkv) MTB_HIP(colsum(dt, T, Nq, dqkv, Nq, nullptr, nullptr, nullptr, g.b_qkv, red, st));
     // QKV input gradient: partial over ranks, summed at f2
     Epi e;
-    e.out = phase == MTB_PHASE_SEG1 ? dx : p; e.ldo = H;
+    e.out = phase == MTB_PHASE_SEG1 ? dx : p; e.ldo = H; e.ws = ws;
     MTB_HIP(gemm(dt, T, H, Nq, dqkv, Nq, true, w->w_qkv, H, false, e, st));
     if (phase == MTB_PHASE_SEG1) return MTB_OK;
     if ((s = call_hook(comm, p, d.T * d.H, dt, MTB_OP_SUM, st)) != MTB_OK) return s;

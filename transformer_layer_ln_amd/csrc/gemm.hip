@@ -552,31 +552,6 @@ hipError_t launch_cfg(int M, int N, int K, const void* A, int lda, const void* B
 
 constexpr int kCUs = 256;
 
-// Split count for a weight gradient (both operands transposed) on 256x128
-// tiles: only when the tiles would leave at least half the CUs idle, the
-// smallest power of two that gives 3/4 of a wave of kCUs blocks, each split
-// at least 1024 deep; 1 = no split. (More splits cost 8 bytes per output
-// element each in partial-tile traffic.)
-int wgrad_splits(int M, int N, int K) {
-  const long tiles = (long)((M + 255) / 256) * ((N + 127) / 128);
-  if (tiles > kCUs / 2) return 1;
-  int s = 1;
-  while (s < 8 && tiles * s * 4 < 3L * kCUs && K % (2 * s * BK) == 0 && K / (2 * s) >= 1024) s *= 2;
-  return s;
-}
-
-// Split count for a product with a token-major left operand and a plain or
-// transposed-copy store whose 128x128 tiles fill at most half of the chip's
-// two-per-CU block slots: doubled until they fill them, each split at least
-// 1024 deep; 1 = no split.
-int store_splits(int M, int N, int K) {
-  const long tiles = (long)((M + 127) / 128) * ((N + 127) / 128);
-  if (tiles > kCUs || (long)((M + 255) / 256) * ((N + 255) / 256) >= kCUs) return 1;
-  int s = 1;
-  while (s < 4 && tiles * s < 2L * kCUs && K % (2 * s * BK) == 0 && K / (2 * s) >= 1024) s *= 2;
-  return s;
-}
-
 // Fraction of the chip's block slots that `tiles` blocks keep busy over their
 // waves (slots = kCUs * blocks per CU).
 double fill(long tiles, int per_cu) {
@@ -584,60 +559,97 @@ double fill(long tiles, int per_cu) {
   return (double)tiles / (double)(waves * slots);
 }
 
-// Tile shape per problem: each candidate's relative per-tile rate (measured
-// on MI355X over the block's GEMM shapes) times the fraction of the chip its
-// tile count fills; 256x256 (2x4 wavefronts) and 128x128 (2x2, two blocks
-// per CU) for the products with a k-contiguous left operand, plus 256x192
-// (4x2) when N splits into 192-wide tiles; for the weight gradients (both
-// operands transposed in LDS) 256x128 (4x2) when it fills the chip, the
-// contraction split over several blocks when too few tiles remain (given a
-// workspace), else 128x128.
-// (Tiles for 6 wavefronts fill the chip better at N = 1536 but leave two of
-// a CU's four SIMDs with twice the work: measured slower.)
+enum Tile { T256x256, T256x192, T256x128, T128x128 };
+struct Plan {
+  Tile tile;
+  int splits;  // > 1: the contraction is split over that many blocks per tile
+};
+
+// Tile shape and contraction split per problem, the one decision both the
+// launch and the workspace query use. Candidates (relative per-tile rates
+// measured on MI355X over the block's GEMM shapes, times the fraction of the
+// chip their tile count fills): 256x256 (2x4 wavefronts), 256x192 (4x2) when
+// N splits into 192-wide tiles (plain store), 128x128 (2x2, two blocks per
+// CU); for weight gradients (both operands transposed in LDS) 256x128 (4x2)
+// when it fills the chip, else 128x128 (at two blocks per CU those beat a
+// partly filled 256x128 grid: 158 vs 175 us for the 1536 x 4096 x 8192 QKV
+// weight gradient). Tiles for 6 wavefronts fill the chip better at N = 1536
+// but leave two of a CU's four SIMDs with twice the work: measured slower.
+//
+// Split contraction (needs a workspace, `split_ok`; plain stores only): a
+// deep product whose tiles leave at least half of the chip's block slots idle
+// gets its contraction split into 2, 4 or 8 parts at least 1024 deep -- weight
+// gradients on 256x128 tiles up to 3/4 of a wave, token-major products on
+// 128x128 tiles up to both blocks per CU -- and the fp32 partial tiles are
+// summed in a fixed order by a second pass that also runs the epilogue. Each
+// extra split costs 8 bytes per output element of partial-tile traffic. (At
+// the seq-512 share, where every GEMM is 4096 x <=1024 x <=4096, splitting
+// down to 512-deep parts made the step slower, 0.356 -> 0.401 ms: a block's
+// fixed costs, not its k-loop, dominate there.)
+Plan plan(int M, int N, int K, bool a_kc, bool b_kc, int kind, bool split_ok) {
+  auto tl = [&](int bm, int bn) { return (long)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+  auto depth_ok = [&](int s) { return K % (s * BK) == 0 && K / s >= 1024; };
+  if (!a_kc && !b_kc) {
+    const long t2 = tl(256, 128);
+    if (split_ok && kind == EPI_STORE && t2 <= kCUs / 2) {
+      int s = 1;
+      while (s < 8 && t2 * s * 4 < 3L * kCUs && depth_ok(2 * s)) s *= 2;
+      if (s > 1) return {T256x128, s};
+    }
+    if (K >= 1024 && t2 >= kCUs) return {T256x128, 1};
+    return {T128x128, 1};
+  }
+  const long t256 = tl(256, 256), t128 = tl(128, 128);
+  if (split_ok && a_kc && kind == EPI_STORE && t128 <= kCUs && t256 < kCUs) {
+    int s = 1;
+    while (s < 4 && t128 * s < 2L * kCUs && depth_ok(2 * s)) s *= 2;
+    if (s > 1) return {T128x128, s};
+  }
+  const double f128 = 0.85 * fill(t128, 2);
+  if (K >= 512) {
+    const double f256 = 1.0 * fill(t256, 1);
+    const double f192 = (a_kc && b_kc && kind == EPI_STORE && N % 192 == 0) ? 0.95 * fill(tl(256, 192), 1)
+                                                                            : 0.0;
+    if (f192 > f256 && f192 > f128) return {T256x192, 1};
+    if (f256 >= f128) return {T256x256, 1};
+  }
+  return {T128x128, 1};
+}
+
 template <bool AKC, bool BKC, int EPI>
 hipError_t launch_bf16(int M, int N, int K, const void* A, int lda, const void* B, int ldb,
                        const Epi& e, hipStream_t st) {
-  auto tl = [&](int bm, int bn) { return (long)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-  const double f128 = 0.85 * fill(tl(128, 128), 2);
   if (!AKC && e.outT) return hipErrorInvalidValue;  // the transposed copy is token-major only
-  if constexpr (!AKC && !BKC && EPI == EPI_STORE) {
-    const int ks = e.ws ? wgrad_splits(M, N, K) : 1;
-    if (ks > 1) {
-      hipError_t r = launch_cfg<256, 128, 4, 2, 1, AKC, BKC, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, e,
-                                                                           st, ks);
+  const Plan pl = plan(M, N, K, AKC, BKC, EPI, e.ws != nullptr);
+  if (pl.splits > 1) {
+    hipError_t r;
+    if constexpr (!AKC && !BKC) {
+      if (pl.tile == T256x128)
+        r = launch_cfg<256, 128, 4, 2, 1, AKC, BKC, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, e, st, pl.splits);
+      else
+        r = launch_cfg<128, 128, 2, 2, 2, AKC, BKC, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, e, st, pl.splits);
       if (r != hipSuccess) return r;
       const size_t n8 = (size_t)M * N / 8;
       hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st,
-                         M, N, ks, (const float*)e.ws, (bf16_t*)e.out, e.ldo);
-      return hipGetLastError();
+                         M, N, pl.splits, (const float*)e.ws, (bf16_t*)e.out, e.ldo);
+    } else {
+      r = launch_cfg<128, 128, 2, 2, 2, AKC, BKC, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, e, st, pl.splits);
+      if (r != hipSuccess) return r;
+      const unsigned tiles = (unsigned)(((M + 127) / 128) * ((N + 127) / 128));
+      hipLaunchKernelGGL((splitk_epi_kernel<128, 128, 256, EPI>), dim3(tiles), dim3(256), 0, st, M, N,
+                         pl.splits, (const float*)e.ws, e);
     }
-    // 256x128 only when it fills the chip: at two blocks per CU, 128x128
-    // tiles beat a partly filled 256x128 grid (measured 158 vs 175 us for the
-    // 1536 x 4096 x 8192 QKV weight gradient)
-    if (K >= 1024 && tl(256, 128) >= kCUs)
+    return hipGetLastError();
+  }
+  if constexpr (!AKC && !BKC) {
+    if (pl.tile == T256x128)
       return launch_cfg<256, 128, 4, 2, 1, AKC, BKC, EPI>(M, N, K, A, lda, B, ldb, e, st);
   } else {
-    if constexpr (AKC && EPI == EPI_STORE) {
-      const int ks = e.ws ? store_splits(M, N, K) : 1;
-      if (ks > 1) {
-        hipError_t r = launch_cfg<128, 128, 2, 2, 2, AKC, BKC, EPI_PARTIAL>(M, N, K, A, lda, B, ldb,
-                                                                             e, st, ks);
-        if (r != hipSuccess) return r;
-        hipLaunchKernelGGL((splitk_epi_kernel<128, 128, 256, EPI_STORE>), dim3((unsigned)tl(128, 128)),
-                           dim3(256), 0, st, M, N, ks, (const float*)e.ws, e);
-        return hipGetLastError();
-      }
-    }
-    if (K >= 512) {
-      const double f256 = 1.0 * fill(tl(256, 256), 1);
-      double f192 = 0.0;
-      if constexpr (AKC && BKC && EPI == EPI_STORE) f192 = N % 192 == 0 ? 0.95 * fill(tl(256, 192), 1) : 0.0;
-      if constexpr (AKC && BKC && EPI == EPI_STORE)
-        if (f192 > f256 && f192 > f128)
-          return launch_cfg<256, 192, 4, 2, 1, AKC, BKC, EPI>(M, N, K, A, lda, B, ldb, e, st);
-      if (f256 >= f128)
-        return launch_cfg<256, 256, 2, 4, 1, AKC, BKC, EPI>(M, N, K, A, lda, B, ldb, e, st);
-    }
+    if constexpr (AKC && BKC && EPI == EPI_STORE)
+      if (pl.tile == T256x192)
+        return launch_cfg<256, 192, 4, 2, 1, AKC, BKC, EPI>(M, N, K, A, lda, B, ldb, e, st);
+    if (pl.tile == T256x256)
+      return launch_cfg<256, 256, 2, 4, 1, AKC, BKC, EPI>(M, N, K, A, lda, B, ldb, e, st);
   }
   return launch_cfg<128, 128, 2, 2, 2, AKC, BKC, EPI>(M, N, K, A, lda, B, ldb, e, st);
 }
@@ -645,11 +657,9 @@ hipError_t launch_bf16(int M, int N, int K, const void* A, int lda, const void* 
 }  // namespace
 
 size_t gemm_ws_bytes(int dtype, int M, int N, int K, bool a_kc, bool b_kc, int kind) {
-  if (dtype == 0 || kind != EPI_STORE || M <= 0 || N <= 0) return 0;
-  int ks = 1;
-  if (!a_kc && !b_kc) ks = wgrad_splits(M, N, K);
-  else if (a_kc) ks = store_splits(M, N, K);
-  return ks > 1 ? (size_t)ks * M * N * 4 : 0;
+  if (dtype == 0 || M <= 0 || N <= 0 || K <= 0) return 0;
+  const Plan pl = plan(M, N, K, a_kc, b_kc, kind, true);
+  return pl.splits > 1 ? (size_t)pl.splits * M * N * 4 : 0;
 }
 
 hipError_t gemm(int dtype, int M, int N, int K, const void* A, int lda, bool a_kc, const void* B,
