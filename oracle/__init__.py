@@ -14,7 +14,9 @@ against the pages by eye:
   evaluated as R tensor-parallel shards whose partial sums are added at the
   two reduction points (R = 1 is the unsharded block);
 * ``xent``   -- cross-entropy over vocab-sharded logits, following the
-  three-reduction scheme (global max, target logit, sum of exponentials).
+  three-reduction scheme (global max, target logit, sum of exponentials);
+* ``embed``  -- the vocab-parallel input embedding: masked lookup per shard,
+  summed over shards, and its adjoint (scatter-add into the shard's rows).
 
 Pages cited (short key -> page):
 
@@ -33,4 +35,4 @@ Parity status: every function here is pinned by the ``-m "not gpu"`` tests in
 forms, brute force on tiny inputs, an independent float64 autograd
 cross-check). No function is "parity unpinned".
 """
-from . import block, xent  # noqa: F401
+from . import block, embed, xent  # noqa: F401
