@@ -17,9 +17,10 @@ configuration); --workload seq512 times the seq-512 TP=4 share (hidden 1024,
 
 Besides the headline step it reports per-step median/p10/p90, the pages'
 attention / FFN / backward segment times (library segment events), LN
-forward/backward and attention-forward kernel rates, and the vocab-parallel
-cross-entropy (partial + loss + gradient) on one [8192 x 16032] vocab shard
-against HBM bandwidth.
+forward/backward and attention-forward kernel rates, and, against HBM
+bandwidth, the vocab-parallel cross-entropy (partial + loss + gradient) on
+one [8192 x 16032] vocab shard and the vocab-parallel input embedding
+(forward lookup, backward scatter-add) on one [16032 x 4096] table shard.
 
 --sweep times the seq-512 share at seq 128/256/512/1024 and fits the
 log-log slopes of the attention / FFN / backward times against seq.
@@ -240,6 +241,42 @@ def run_gpu(cfg, steps, warmup, trace_what=None, graph_steps=0):
     return ms, per_step, wall, kern, graph
 
 
+def run_embed(ecfg, steps, warmup):
+    """Vocab-parallel embedding forward and backward on vocab shard 0.
+    Returns (fwd ms, bwd ms, tokens whose id lies in the shard)."""
+    import torch
+
+    from transformer_layer_ln_amd import inputs, mtb
+
+    dev = torch.device("cuda")
+    n, h, vl = ecfg.n_tokens, ecfg.hidden, ecfg.v_local
+    ids_h = inputs.embed_ids(ecfg)
+    ids = torch.as_tensor(ids_h).to(dev)
+    table = torch.as_tensor(inputs.embed_table(ecfg, 0)).to(dev, torch.bfloat16)
+    dout = torch.as_tensor(inputs.embed_dout(ecfg)).to(dev, torch.bfloat16)
+    out = torch.empty(n, h, dtype=torch.bfloat16, device=dev)
+    dtab = torch.empty_like(table)
+    ws = torch.empty(mtb.vocab_embed_bwd_workspace_bytes(n, vl), dtype=torch.uint8, device=dev)
+    fwd = lambda: mtb.vocab_embed_fwd(n, vl, 0, h, mtb.BF16, ids, table, out)
+    bwd = lambda: mtb.vocab_embed_bwd(n, vl, 0, h, mtb.BF16, ids, dout, dtab, ws)
+    st = torch.cuda.current_stream()
+    res = []
+    for call in (fwd, bwd):
+        for _ in range(warmup):
+            call()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(st)
+        for _ in range(steps):
+            call()
+        e1.record(st)
+        torch.cuda.synchronize()
+        res.append(e0.elapsed_time(e1) / steps)
+    own = int(((ids_h >= 0) & (ids_h < vl)).sum())
+    return res[0], res[1], own
+
+
 def run_xent(xcfg, steps, warmup):
     """X1-X3 on one vocab shard: mtb_vocab_xent(MTB_XENT_ALL) with the
     identity reduction (one shard's statistics are final), loss and the
@@ -362,6 +399,12 @@ def main():
     xcfg = inputs.C5_XENT
     xent_ms = run_xent(xcfg, args.steps, args.warmup)
     xent_bytes = 6 * xcfg.n_tokens * xcfg.v_local   # X1 reads 2 B/logit, X3 reads 2 + writes 2
+    ecfg = inputs.C5_EMBED
+    emb_f_ms, emb_b_ms, emb_own = run_embed(ecfg, args.steps, args.warmup)
+    # forward: read the in-shard rows, write every output row; backward: read
+    # the in-shard tokens' gradient rows, write every table row (+ 8 B ids)
+    emb_f_bytes = (emb_own + ecfg.n_tokens) * ecfg.hidden * 2 + 8 * ecfg.n_tokens
+    emb_b_bytes = (emb_own + ecfg.v_local) * ecfg.hidden * 2 + 8 * ecfg.n_tokens
 
     res = {
         "metric": f"block fwd+bwd TFLOP/s (one TP-rank shard, bf16) at seq {cfg.seq}",
@@ -410,6 +453,15 @@ def main():
                            "avg_ms": round(xent_ms, 5),
                            "achieved_GBs": round(xent_bytes / (xent_ms * 1e-3) / 1e9, 1),
                            "peak_GBs": PEAK_HBM_GBS},
+            "vocab_embed": {"bound": "hbm", "workload": (
+                                f"one vocab shard [{ecfg.v_local} x {ecfg.hidden}] bf16 of "
+                                f"V={ecfg.vocab} over TP={ecfg.tp}, {ecfg.n_tokens} token ids "
+                                f"({emb_own} in the shard)"),
+                            "fwd_avg_ms": round(emb_f_ms, 5),
+                            "fwd_achieved_GBs": round(emb_f_bytes / (emb_f_ms * 1e-3) / 1e9, 1),
+                            "bwd_avg_ms": round(emb_b_ms, 5),
+                            "bwd_achieved_GBs": round(emb_b_bytes / (emb_b_ms * 1e-3) / 1e9, 1),
+                            "peak_GBs": PEAK_HBM_GBS},
         },
         # the pages' breakdown (attention / FFN / backward), timed by the
         # library's segment events; the pages' own figures are context only

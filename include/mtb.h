@@ -235,6 +235,36 @@ mtb_status mtb_vocab_xent(int64_t n_tokens, int64_t v_local, int64_t v_start, in
 mtb_status mtb_vocab_xent_combine(int64_t n_tokens, int32_t n_shards, const float *shard_stats,
                                   float *stats, float *loss, void *hip_stream);
 
+/* Vocab-parallel input embedding ([TP-block] sec. 3) on one vocab shard:
+ * this rank holds rows [v_start, v_start + v_local) of the [vocab, hidden]
+ * table.
+ *   ids [n_tokens] int64 GLOBAL token ids (any value: ids outside this
+ *     shard's range, negative or beyond the vocab, select nothing here);
+ *   table [v_local][hidden] (dtype), out [n_tokens][hidden] (dtype).
+ * Forward: out[t] = table[ids[t] - v_start] when the id lies in the shard,
+ * else a zero row; then, with a hook, out is all-reduced (SUM) over the
+ * shards -- the masks make exactly one shard contribute each token's row.
+ * NULL comm: identity (one shard). hidden % 8 == 0; table, out 16-byte and
+ * ids 8-byte aligned; n_tokens, v_local < 2^31. */
+mtb_status mtb_vocab_embed_fwd(int64_t n_tokens, int64_t v_local, int64_t v_start, int64_t hidden,
+                               int32_t dtype, const int64_t *ids, const void *table, void *out,
+                               const mtb_comm *comm, void *hip_stream);
+
+/* Device workspace (bytes, caller-owned) that mtb_vocab_embed_bwd needs:
+ * 8 bytes per table row of the shard (a token count and a first token);
+ * 0 when n_tokens or v_local is outside 1 .. 2^31 - 1. */
+size_t mtb_vocab_embed_bwd_workspace_bytes(int64_t n_tokens, int64_t v_local);
+
+/* Backward of the embedding: the all-reduce's backward is the identity, so
+ * dout [n_tokens][hidden] is the full (replicated) gradient of out. Writes
+ * dtable[v] = sum of dout[t] over the tokens t with ids[t] == v_start + v,
+ * accumulated in fp32 in increasing t (deterministic), rounded once; rows no
+ * token selects are written as zeros. Same layout and alignment rules as the
+ * forward; workspace 16-byte aligned. */
+mtb_status mtb_vocab_embed_bwd(int64_t n_tokens, int64_t v_local, int64_t v_start, int64_t hidden,
+                               int32_t dtype, const int64_t *ids, const void *dout, void *dtable,
+                               void *workspace, void *hip_stream);
+
 /* Benchmark instrumentation (not for concurrent use; process-wide state).
  * While armed, every launch of the kernel class `what` records
  * begin_events[i] before it and end_events[i] after it on the launch's

@@ -125,6 +125,28 @@ def test_xent_rejects_bad_arguments_before_launch():
     assert st == mtb.MTB_EINVAL
 
 
+def test_embed_rejects_bad_arguments_before_launch():
+    p, q, r = _FakePtr(0x100000), _FakePtr(0x200000), _FakePtr(0x300000)
+    st, msg = _status(mtb.vocab_embed_fwd, 8, 16, 0, 64, mtb.BF16, None, q, r, None, _S())
+    assert st == mtb.MTB_EINVAL and "ids is NULL" in msg
+    st, msg = _status(mtb.vocab_embed_fwd, 8, 16, 0, 60, mtb.BF16, p, q, r, None, _S())
+    assert st == mtb.MTB_EUNSUPPORTED and "multiple of 8" in msg
+    st, msg = _status(mtb.vocab_embed_fwd, 8, 16, -1, 64, mtb.BF16, p, q, r, None, _S())
+    assert st == mtb.MTB_EINVAL
+    st, msg = _status(mtb.vocab_embed_fwd, 8, 16, 0, 64, mtb.BF16, p, _FakePtr(0x200008), r, None,
+                      _S())
+    assert st == mtb.MTB_EINVAL and "aligned" in msg
+    st, msg = _status(mtb.vocab_embed_bwd, 8, 16, 0, 64, mtb.BF16, p, q, r, None, _S())
+    assert st == mtb.MTB_EINVAL and "workspace" in msg
+
+
+def test_embed_workspace_query():
+    assert mtb.vocab_embed_bwd_workspace_bytes(0, 16) == 0
+    assert mtb.vocab_embed_bwd_workspace_bytes(8, 0) == 0
+    assert mtb.vocab_embed_bwd_workspace_bytes(8192, 16032) == 16032 * 8
+    assert mtb.vocab_embed_bwd_workspace_bytes(1 << 20, 10) == 80
+
+
 def test_struct_layout_matches_header():
     # 10 int32 fields + 1 float
     assert ctypes.sizeof(mtb.Cfg) == 44

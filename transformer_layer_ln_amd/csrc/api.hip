@@ -219,6 +219,18 @@ void trace_end(int what, hipStream_t st) {
 
 }  // namespace
 
+namespace {
+mtb_status check_embed(int64_t n, int64_t v, int64_t v0, int64_t h, int32_t dtype) {
+  if (n <= 0 || v <= 0 || v0 < 0 || h <= 0)
+    return fail(MTB_EINVAL, "n_tokens, v_local, hidden must be > 0 and v_start >= 0");
+  if (dtype != MTB_F32 && dtype != MTB_BF16) return fail(MTB_EINVAL, "bad dtype %d", dtype);
+  if (h % 8 != 0) return fail(MTB_EUNSUPPORTED, "hidden %lld is not a multiple of 8", (long long)h);
+  if (n > 0x7fffffff || v > 0x7fffffff || h > 0x7fffffff)
+    return fail(MTB_EUNSUPPORTED, "n_tokens, v_local and hidden must be below 2^31");
+  return MTB_OK;
+}
+}  // namespace
+
 extern "C" {
 
 const char* mtb_last_error(void) { return g_err.c_str(); }
@@ -539,6 +551,37 @@ mtb_status mtb_vocab_xent_combine(int64_t n, int32_t n_shards, const float* shar
   MTB_REQ_A(stats, "stats", 4);
   MTB_OPT_A(loss, "loss", 4);
   MTB_HIP(xent_combine(n, n_shards, shard_stats, stats, loss, (hipStream_t)hip_stream));
+  return MTB_OK;
+}
+
+mtb_status mtb_vocab_embed_fwd(int64_t n, int64_t v, int64_t v0, int64_t h, int32_t dtype,
+                               const int64_t* ids, const void* table, void* out,
+                               const mtb_comm* comm, void* hip_stream) {
+  mtb_status s = check_embed(n, v, v0, h, dtype);
+  if (s != MTB_OK) return s;
+  MTB_REQ_A(ids, "ids", 8);
+  MTB_REQ(table, "table");
+  MTB_REQ(out, "out");
+  hipStream_t st = (hipStream_t)hip_stream;
+  MTB_HIP(embed_fwd(dtype, n, v, v0, (int)h, ids, table, out, st));
+  return call_hook(comm, out, n * h, dtype, MTB_OP_SUM, st);
+}
+
+size_t mtb_vocab_embed_bwd_workspace_bytes(int64_t n, int64_t v) {
+  if (n <= 0 || n > 0x7fffffff || v <= 0 || v > 0x7fffffff) return 0;
+  return embed_ws_bytes(v);
+}
+
+mtb_status mtb_vocab_embed_bwd(int64_t n, int64_t v, int64_t v0, int64_t h, int32_t dtype,
+                               const int64_t* ids, const void* dout, void* dtable,
+                               void* workspace, void* hip_stream) {
+  mtb_status s = check_embed(n, v, v0, h, dtype);
+  if (s != MTB_OK) return s;
+  MTB_REQ_A(ids, "ids", 8);
+  MTB_REQ(dout, "dout");
+  MTB_REQ(dtable, "dtable");
+  MTB_REQ(workspace, "workspace");
+  MTB_HIP(embed_bwd(dtype, n, v, v0, (int)h, ids, dout, dtable, workspace, (hipStream_t)hip_stream));
   return MTB_OK;
 }
 

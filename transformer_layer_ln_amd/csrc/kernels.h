@@ -88,4 +88,12 @@ hipError_t xent_finish(int dtype, int64_t n, int64_t v, int64_t v0, const void* 
                        const int64_t* tgt, const float* stats, float* loss, const float* dloss,
                        void* dz, hipStream_t st);
 
+// Vocab-parallel embedding (one vocab shard [v0, v0 + vl) of the table).
+// Backward workspace: per table row, an int32 token count and first token.
+size_t embed_ws_bytes(int64_t vl);
+hipError_t embed_fwd(int dtype, int64_t n, int64_t vl, int64_t v0, int H, const int64_t* ids,
+                     const void* table, void* out, hipStream_t st);
+hipError_t embed_bwd(int dtype, int64_t n, int64_t vl, int64_t v0, int H, const int64_t* ids,
+                     const void* dout, void* dtable, void* workspace, hipStream_t st);
+
 }  // namespace mtb

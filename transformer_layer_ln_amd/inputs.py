@@ -37,6 +37,7 @@ _TAG = {
     "bq": 20, "bk": 21, "bv": 22, "bo": 23, "b1": 24, "bg": 25, "bu": 26, "b2": 27,
     "ln1_g": 30, "ln1_b": 31, "ln2_g": 32, "ln2_b": 33,
     "logits": 40, "targets": 41,
+    "embed_table": 50, "embed_ids": 51, "embed_dout": 52,
 }
 
 
@@ -96,6 +97,25 @@ class XentConfig:
         return self.vocab // self.tp
 
 
+@dataclass(frozen=True)
+class EmbedConfig:
+    """Vocab-parallel input embedding: a [vocab, hidden] table split by vocab
+    over tp ranks; n_tokens token ids. repeat > 0 draws the ids from only
+    `repeat` distinct values (heavy rows for the scatter-add)."""
+    name: str
+    n_tokens: int
+    vocab: int
+    hidden: int
+    tp: int
+    dtype: str = "bf16"
+    seed: int = 1005
+    repeat: int = 0
+
+    @property
+    def v_local(self) -> int:
+        return self.vocab // self.tp
+
+
 # The five workloads. C1 is the small fp32 correctness case; C2-C5 are one
 # rank's share of the tensor-parallel layers the pages describe.
 C1 = BlockConfig("C1-fp32-full", batch=1, seq=64, hidden=128, q_heads=4, kv_heads=4,
@@ -114,6 +134,9 @@ C4 = BlockConfig("C4-tp8-s2048-causal", batch=4, seq=2048, hidden=4096, q_heads=
 C5 = BlockConfig("C5-tp8-s4096-swiglu-gqa", batch=2, seq=4096, hidden=4096, q_heads=4, kv_heads=1,
                  head_dim=128, ffn=1792, act="swiglu", causal=False, dtype="bf16", tp=8, seed=1005)
 C5_XENT = XentConfig("C5-xent-v128256-tp8", n_tokens=8192, vocab=128256, tp=8, dtype="bf16", seed=1005)
+# the input-side counterpart of C5's vocab shard: ids of the seq-4096 share's
+# 8192 tokens, one [16032 x 4096] shard of the 128256-row table
+C5_EMBED = EmbedConfig("C5-embed-v128256-h4096-tp8", n_tokens=8192, vocab=128256, hidden=4096, tp=8)
 
 CONFIGS = {"C1": C1, "C2": C2, "C4": C4, "C5": C5}
 
@@ -222,3 +245,22 @@ def xent_targets(cfg: XentConfig) -> np.ndarray:
 def xent_dloss(cfg: XentConfig) -> np.ndarray:
     """Per-token loss cotangent for a mean over tokens: 1/N each (float32)."""
     return np.full(cfg.n_tokens, 1.0 / cfg.n_tokens, dtype=np.float32)
+
+
+def embed_table(cfg: EmbedConfig, rank: int) -> np.ndarray:
+    """Vocab shard ``rank``'s table rows [V_local, hidden], N(0,1)."""
+    return _normal(cfg.seed, "embed_table", rank, (cfg.v_local, cfg.hidden), 1.0, cfg.dtype)
+
+
+def embed_ids(cfg: EmbedConfig) -> np.ndarray:
+    """Token ids [N] int64, uniform in [0, vocab) (or over `repeat` values)."""
+    r = _rng(cfg.seed, "embed_ids")
+    if cfg.repeat:
+        pool = r.integers(0, cfg.vocab, size=cfg.repeat, dtype=np.int64)
+        return pool[r.integers(0, cfg.repeat, size=cfg.n_tokens)]
+    return r.integers(0, cfg.vocab, size=cfg.n_tokens, dtype=np.int64)
+
+
+def embed_dout(cfg: EmbedConfig) -> np.ndarray:
+    """Gradient of the embedding output [N, hidden], N(0,1)."""
+    return _normal(cfg.seed, "embed_dout", 0, (cfg.n_tokens, cfg.hidden), 1.0, cfg.dtype)
