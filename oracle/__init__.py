@@ -16,7 +16,9 @@ against the pages by eye:
 * ``xent``   -- cross-entropy over vocab-sharded logits, following the
   three-reduction scheme (global max, target logit, sum of exponentials);
 * ``embed``  -- the vocab-parallel input embedding: masked lookup per shard,
-  summed over shards, and its adjoint (scatter-add into the shard's rows).
+  summed over shards, and its adjoint (scatter-add into the shard's rows);
+* ``lmhead`` -- the vocab-parallel output layer feeding ``xent``: logits slice
+  z_r = h W_r^T per shard, and the gradients dW_r and sum_r dz_r W_r.
 
 Pages cited (short key -> page):
 
@@ -35,4 +37,4 @@ Parity status: every function here is pinned by the ``-m "not gpu"`` tests in
 forms, brute force on tiny inputs, an independent float64 autograd
 cross-check). No function is "parity unpinned".
 """
-from . import block, embed, xent  # noqa: F401
+from . import block, embed, lmhead, xent  # noqa: F401
