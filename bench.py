@@ -277,6 +277,44 @@ def run_embed(ecfg, steps, warmup):
     return res[0], res[1], own
 
 
+def run_lmhead(lcfg, steps, warmup):
+    """Fused LM head + cross-entropy on the last vocab shard, no reduction
+    hook (the shard's statistics are final). Returns (fwd ms, bwd ms)."""
+    import torch
+
+    from transformer_layer_ln_amd import inputs, mtb
+
+    dev = torch.device("cuda")
+    n, H, vl = lcfg.n_tokens, lcfg.hidden, lcfg.v_local
+    v0 = (lcfg.tp - 1) * vl
+    h = torch.as_tensor(inputs.lmhead_h(lcfg)).to(dev, torch.bfloat16)
+    w = torch.as_tensor(inputs.lmhead_w(lcfg, lcfg.tp - 1)).to(dev, torch.bfloat16)
+    t = torch.as_tensor(v0 + inputs.lmhead_targets(lcfg) % vl).to(dev)
+    dl = torch.full((n,), 1.0 / n, dtype=torch.float32, device=dev)
+    stats = torch.empty(4, n, dtype=torch.float32, device=dev)
+    loss = torch.empty(n, dtype=torch.float32, device=dev)
+    dh = torch.empty_like(h)
+    dw = torch.empty_like(w)
+    ws = torch.empty(mtb.lmhead_xent_workspace_bytes(n, H, vl), dtype=torch.uint8, device=dev)
+    fwd = lambda: mtb.lmhead_xent_fwd(n, H, vl, v0, mtb.BF16, h, w, t, stats, loss, ws)
+    bwd = lambda: mtb.lmhead_xent_bwd(n, H, vl, v0, mtb.BF16, h, w, t, stats, dl, dh, dw, ws)
+    st = torch.cuda.current_stream()
+    res = []
+    for call in (fwd, bwd):
+        for _ in range(warmup):
+            call()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(st)
+        for _ in range(steps):
+            call()
+        e1.record(st)
+        torch.cuda.synchronize()
+        res.append(e0.elapsed_time(e1) / steps)
+    return res[0], res[1]
+
+
 def run_xent(xcfg, steps, warmup):
     """X1-X3 on one vocab shard: mtb_vocab_xent(MTB_XENT_ALL) with the
     identity reduction (one shard's statistics are final), loss and the
@@ -405,6 +443,9 @@ def main():
     # the in-shard tokens' gradient rows, write every table row (+ 8 B ids)
     emb_f_bytes = (emb_own + ecfg.n_tokens) * ecfg.hidden * 2 + 8 * ecfg.n_tokens
     emb_b_bytes = (emb_own + ecfg.v_local) * ecfg.hidden * 2 + 8 * ecfg.n_tokens
+    lcfg = inputs.C5_LMHEAD
+    lm_f_ms, lm_b_ms = run_lmhead(lcfg, args.steps, args.warmup)
+    lm_flops = 2.0 * lcfg.n_tokens * lcfg.hidden * lcfg.v_local   # one [n x V_r x H] product
 
     res = {
         "metric": f"block fwd+bwd TFLOP/s (one TP-rank shard, bf16) at seq {cfg.seq}",
@@ -462,6 +503,18 @@ def main():
                             "bwd_avg_ms": round(emb_b_ms, 5),
                             "bwd_achieved_GBs": round(emb_b_bytes / (emb_b_ms * 1e-3) / 1e9, 1),
                             "peak_GBs": PEAK_HBM_GBS},
+            "lmhead_xent": {"bound": "mfma", "workload": (
+                                f"LM head + cross-entropy on one vocab shard: [{lcfg.n_tokens} x "
+                                f"{lcfg.hidden}] x [{lcfg.v_local} x {lcfg.hidden}]^T bf16 of "
+                                f"V={lcfg.vocab} over TP={lcfg.tp}; forward = logits GEMM with "
+                                "the loss statistics in its epilogue; backward = logits "
+                                "recomputed with the gradient epilogue, then dh and dW GEMMs"),
+                            "fwd_avg_ms": round(lm_f_ms, 5),
+                            "fwd_achieved_TFLOPs": round(lm_flops / (lm_f_ms * 1e-3) / 1e12, 1),
+                            "bwd_avg_ms": round(lm_b_ms, 5),
+                            "bwd_achieved_TFLOPs": round(3 * lm_flops / (lm_b_ms * 1e-3) / 1e12,
+                                                         1),
+                            "peak_TFLOPs": PEAK_BF16_TFLOPS},
         },
         # the pages' breakdown (attention / FFN / backward), timed by the
         # library's segment events; the pages' own figures are context only

@@ -235,6 +235,38 @@ mtb_status mtb_vocab_xent(int64_t n_tokens, int64_t v_local, int64_t v_start, in
 mtb_status mtb_vocab_xent_combine(int64_t n_tokens, int32_t n_shards, const float *shard_stats,
                                   float *stats, float *loss, void *hip_stream);
 
+/* Vocab-parallel output layer (LM head) fused with the vocab-parallel
+ * cross-entropy ([TP-block] sec. 4 computes the loss from vocab-sharded
+ * logits; here they come from this rank's vocab slice of the [V, hidden]
+ * output embedding, rows [v_start, v_start + v_local), as z = h w^T, a
+ * column-parallel linear). bf16 only; n_tokens, hidden, v_local multiples of
+ * 8; h [n_tokens][hidden], w [v_local][hidden], 16-byte aligned.
+ *
+ * Forward: the logits are computed tile by tile and each tile is reduced in
+ * the GEMM epilogue to per-token (max, sum exp, target logit); the
+ * [n_tokens, v_local] logits are never stored. Then, exactly as
+ * mtb_vocab_xent(MTB_XENT_ALL): stats [4][n_tokens] ends up holding the
+ * combined (M, S, T) over the shards (the hook's MAX, local rescale, SUM,
+ * SUM; NULL comm: one shard), and loss[n] = log S + M - T if loss != NULL.
+ *
+ * Backward, with the combined stats of the forward and dloss [n_tokens]:
+ * recomputes the logits in a GEMM whose epilogue writes
+ * dz = (exp(z - M)/S - onehot(target)) * dloss (bf16, in the workspace), then
+ * dw = dz^T h [v_local][hidden] (if dw != NULL) and dh = dz w
+ * [n_tokens][hidden] (if dh != NULL) -- this shard's partial of the input
+ * gradient, summed over the shards by the hook (SUM, bf16). At least one of
+ * dh, dw. Workspace: mtb_lmhead_xent_workspace_bytes (device, caller-owned,
+ * 16-byte aligned; the same size serves both calls). */
+size_t mtb_lmhead_xent_workspace_bytes(int64_t n_tokens, int64_t hidden, int64_t v_local);
+mtb_status mtb_lmhead_xent_fwd(int64_t n_tokens, int64_t hidden, int64_t v_local, int64_t v_start,
+                               int32_t dtype, const void *h, const void *w, const int64_t *target,
+                               float *stats, float *loss, void *workspace, const mtb_comm *comm,
+                               void *hip_stream);
+mtb_status mtb_lmhead_xent_bwd(int64_t n_tokens, int64_t hidden, int64_t v_local, int64_t v_start,
+                               int32_t dtype, const void *h, const void *w, const int64_t *target,
+                               const float *stats, const float *dloss, void *dh, void *dw,
+                               void *workspace, const mtb_comm *comm, void *hip_stream);
+
 /* Vocab-parallel input embedding ([TP-block] sec. 3) on one vocab shard:
  * this rank holds rows [v_start, v_start + v_local) of the [vocab, hidden]
  * table.

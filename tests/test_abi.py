@@ -167,3 +167,34 @@ def test_product_path_does_not_import_the_oracle():
     for line in bench.splitlines():
         if re.match(r"^(from|import)\s+oracle", line):
             pytest.fail("bench.py imports the oracle at module level")
+
+
+def test_lmhead_rejects_bad_arguments_before_launch():
+    p, q, r, s = _FakePtr(0x100000), _FakePtr(0x200000), _FakePtr(0x300000), _FakePtr(0x400000)
+    ws = _FakePtr(0x500000)
+    st, msg = _status(mtb.lmhead_xent_fwd, 8, 64, 16, 0, mtb.F32, p, q, r, s, None, ws, None, _S())
+    assert st == mtb.MTB_EUNSUPPORTED and "bf16" in msg
+    st, msg = _status(mtb.lmhead_xent_fwd, 8, 60, 16, 0, mtb.BF16, p, q, r, s, None, ws, None, _S())
+    assert st == mtb.MTB_EUNSUPPORTED and "multiples of 8" in msg
+    st, msg = _status(mtb.lmhead_xent_fwd, 8, 64, 16, -8, mtb.BF16, p, q, r, s, None, ws, None,
+                      _S())
+    assert st == mtb.MTB_EINVAL
+    st, msg = _status(mtb.lmhead_xent_fwd, 8, 64, 16, 0, mtb.BF16, p, q, _FakePtr(0x300004), s,
+                      None, ws, None, _S())
+    assert st == mtb.MTB_EINVAL and "aligned" in msg
+    st, msg = _status(mtb.lmhead_xent_fwd, 8, 64, 16, 0, mtb.BF16, p, q, r, s, None, None, None,
+                      _S())
+    assert st == mtb.MTB_EINVAL and "workspace" in msg
+    st, msg = _status(mtb.lmhead_xent_bwd, 8, 64, 16, 0, mtb.BF16, p, q, r, s, ws, None, None,
+                      _FakePtr(0x600000), None, _S())
+    assert st == mtb.MTB_EINVAL and "dh" in msg
+    st, msg = _status(mtb.lmhead_xent_bwd, 8, 64, 16, 0, mtb.BF16, p, q, r, s, None,
+                      _FakePtr(0x700000), None, _FakePtr(0x600000), None, _S())
+    assert st == mtb.MTB_EINVAL and "dloss" in msg
+
+
+def test_lmhead_workspace_query():
+    assert mtb.lmhead_xent_workspace_bytes(0, 64, 16) == 0
+    # the backward's bf16 [n, v_local] gradient of the logits dominates
+    assert mtb.lmhead_xent_workspace_bytes(8192, 4096, 16032) == 8192 * 16032 * 2
+    assert mtb.lmhead_xent_workspace_bytes(64, 4096, 8) == 64 * 8 * 2

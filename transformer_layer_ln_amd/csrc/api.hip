@@ -229,6 +229,23 @@ mtb_status check_embed(int64_t n, int64_t v, int64_t v0, int64_t h, int32_t dtyp
     return fail(MTB_EUNSUPPORTED, "n_tokens, v_local and hidden must be below 2^31");
   return MTB_OK;
 }
+mtb_status check_lmhead(int64_t n, int64_t h, int64_t v, int64_t v0, int32_t dtype) {
+  if (n <= 0 || h <= 0 || v <= 0 || v0 < 0)
+    return fail(MTB_EINVAL, "n_tokens, hidden, v_local must be > 0 and v_start >= 0");
+  if (dtype != MTB_BF16)
+    return fail(dtype == MTB_F32 ? MTB_EUNSUPPORTED : MTB_EINVAL, "the LM head runs in bf16 only");
+  if (n % 8 || h % 8 || v % 8)
+    return fail(MTB_EUNSUPPORTED, "n_tokens, hidden and v_local must be multiples of 8");
+  if (n > 0x7fffffff || h > 0x7fffffff || v > 0x7fffffff)
+    return fail(MTB_EUNSUPPORTED, "n_tokens, hidden and v_local must be below 2^31");
+  return MTB_OK;
+}
+
+int lmhead_tiles(int64_t n, int64_t h, int64_t v) {
+  const int bn = gemm_tile_n((int)n, (int)v, (int)h, true, true, EPI_XENT_STATS);
+  return (int)((v + bn - 1) / bn);
+}
+
 }  // namespace
 
 extern "C" {
@@ -582,6 +599,92 @@ mtb_status mtb_vocab_embed_bwd(int64_t n, int64_t v, int64_t v0, int64_t h, int3
   MTB_REQ(dtable, "dtable");
   MTB_REQ(workspace, "workspace");
   MTB_HIP(embed_bwd(dtype, n, v, v0, (int)h, ids, dout, dtable, workspace, (hipStream_t)hip_stream));
+  return MTB_OK;
+}
+
+size_t mtb_lmhead_xent_workspace_bytes(int64_t n, int64_t h, int64_t v) {
+  if (n <= 0 || h <= 0 || v <= 0 || n > 0x7fffffff || h > 0x7fffffff || v > 0x7fffffff) return 0;
+  const size_t parts = (size_t)n * lmhead_tiles(n, h, v) * 3 * sizeof(float);
+  const size_t dz = (size_t)n * v * 2;
+  return parts > dz ? parts : dz;
+}
+
+mtb_status mtb_lmhead_xent_fwd(int64_t n, int64_t h, int64_t v, int64_t v0, int32_t dtype,
+                               const void* hid, const void* w, const int64_t* target,
+                               float* stats, float* loss, void* workspace, const mtb_comm* comm,
+                               void* hip_stream) {
+  mtb_status s = check_lmhead(n, h, v, v0, dtype);
+  if (s != MTB_OK) return s;
+  MTB_REQ(hid, "h");
+  MTB_REQ(w, "w");
+  MTB_REQ_A(target, "target", 8);
+  MTB_REQ_A(stats, "stats", 4);
+  MTB_OPT_A(loss, "loss", 4);
+  MTB_REQ(workspace, "workspace");
+  hipStream_t st = (hipStream_t)hip_stream;
+  // logits tile by tile, reduced in the epilogue: the [n, v] logits are never stored
+  Epi e;
+  e.kind = EPI_XENT_STATS;
+  e.out = workspace;
+  e.target = target;
+  e.col0 = v0;
+  MTB_HIP(gemm(MTB_BF16, (int)n, (int)v, (int)h, hid, (int)h, true, w, (int)h, true, e, st));
+  const bool hook = comm && comm->allreduce;
+  MTB_HIP(lmhead_combine(n, lmhead_tiles(n, h, v), (const float*)workspace, stats,
+                         hook ? stats + 3 * n : nullptr, st));
+  if (hook) {
+    if ((s = call_hook(comm, stats, n, MTB_F32, MTB_OP_MAX, st)) != MTB_OK) return s;
+    MTB_HIP(xent_rescale(n, stats, stats + 3 * n, st));
+    if ((s = call_hook(comm, stats + n, n, MTB_F32, MTB_OP_SUM, st)) != MTB_OK) return s;
+    if ((s = call_hook(comm, stats + 2 * n, n, MTB_F32, MTB_OP_SUM, st)) != MTB_OK) return s;
+  }
+  if (loss)
+    MTB_HIP(xent_finish(MTB_BF16, n, v, v0, nullptr, target, stats, loss, nullptr, nullptr, st));
+  return MTB_OK;
+}
+
+mtb_status mtb_lmhead_xent_bwd(int64_t n, int64_t h, int64_t v, int64_t v0, int32_t dtype,
+                               const void* hid, const void* w, const int64_t* target,
+                               const float* stats, const float* dloss, void* dh, void* dw,
+                               void* workspace, const mtb_comm* comm, void* hip_stream) {
+  mtb_status s = check_lmhead(n, h, v, v0, dtype);
+  if (s != MTB_OK) return s;
+  MTB_REQ(hid, "h");
+  MTB_REQ(w, "w");
+  MTB_REQ_A(target, "target", 8);
+  MTB_REQ_A(stats, "stats", 4);
+  MTB_REQ_A(dloss, "dloss", 4);
+  MTB_OPT(dh, "dh");
+  MTB_OPT(dw, "dw");
+  if (!dh && !dw) return fail(MTB_EINVAL, "neither dh nor dw requested");
+  MTB_REQ(workspace, "workspace");
+  hipStream_t st = (hipStream_t)hip_stream;
+  // dz = (softmax - onehot) * dloss from recomputed logits, bf16 [n][v]
+  void* dz = workspace;
+  {
+    Epi e;
+    e.kind = EPI_XENT_GRAD;
+    e.out = dz;
+    e.ldo = (int)v;
+    e.target = target;
+    e.col0 = v0;
+    e.rowstat = stats;
+    e.rowscale = dloss;
+    MTB_HIP(gemm(MTB_BF16, (int)n, (int)v, (int)h, hid, (int)h, true, w, (int)h, true, e, st));
+  }
+  if (dw) {  // dW = dz^T h: both operands token-major
+    Epi e;
+    e.out = dw;
+    e.ldo = (int)h;
+    MTB_HIP(gemm(MTB_BF16, (int)v, (int)h, (int)n, dz, (int)v, false, hid, (int)h, false, e, st));
+  }
+  if (dh) {  // dh = dz W: this shard's partial of the column-parallel input's gradient
+    Epi e;
+    e.out = dh;
+    e.ldo = (int)h;
+    MTB_HIP(gemm(MTB_BF16, (int)n, (int)h, (int)v, dz, (int)v, true, w, (int)h, false, e, st));
+    if ((s = call_hook(comm, dh, n * h, MTB_BF16, MTB_OP_SUM, st)) != MTB_OK) return s;
+  }
   return MTB_OK;
 }
 

@@ -47,13 +47,16 @@ struct TileKc {
   static constexpr int TOT = ROWS * BK / 8;
   static constexpr int NCH = (TOT + NT - 1) / NT;
   u32x4 r[NCH];
-  MTB_DEV void load(const bf16_t* __restrict__ p, int ld, int row0, int rowmax, int k0, int tid) {
+  MTB_DEV void load(const bf16_t* __restrict__ p, int ld, int row0, int rowmax, int k0, int kmax,
+                    int tid) {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int q = tid + NT * i, row = q >> 3, c = q & 7;
       if (TOT % NT != 0 && q >= TOT) break;
       const int gr = min(row0 + row, rowmax - 1);
-      r[i] = *reinterpret_cast<const u32x4*>(p + (size_t)gr * ld + k0 + c * 8);
+      // past the contraction's end (K % 64 != 0): zeros
+      r[i] = k0 + c * 8 < kmax ? *reinterpret_cast<const u32x4*>(p + (size_t)gr * ld + k0 + c * 8)
+                               : u32x4{0u, 0u, 0u, 0u};
     }
   }
   MTB_DEV void store(bf16_t* s, int tid) const {
@@ -73,7 +76,8 @@ struct TileMn {
   static constexpr int TOT = (ROWS / 8) * (BK / 4);  // 4x8 blocks in the tile
   static constexpr int IT = (TOT + NT - 1) / NT;     // (threads past TOT idle)
   u32x4 r[IT][4];
-  MTB_DEV void load(const bf16_t* __restrict__ p, int ld, int row0, int rowmax, int k0, int tid) {
+  MTB_DEV void load(const bf16_t* __restrict__ p, int ld, int row0, int rowmax, int k0, int kmax,
+                    int tid) {
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
       const int idx = tid + NT * it;
@@ -81,8 +85,11 @@ struct TileMn {
       const int mc = idx % (ROWS / 8), k4 = idx / (ROWS / 8);
       const int gm = min(row0 + mc * 8, rowmax - 8);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        r[it][j] = *reinterpret_cast<const u32x4*>(p + (size_t)(k0 + k4 * 4 + j) * ld + gm);
+      for (int j = 0; j < 4; ++j) {
+        const int k = k0 + k4 * 4 + j;  // past the contraction's end: zeros
+        r[it][j] = k < kmax ? *reinterpret_cast<const u32x4*>(p + (size_t)k * ld + gm)
+                            : u32x4{0u, 0u, 0u, 0u};
+      }
     }
   }
   MTB_DEV void store(bf16_t* s, int tid) const {
@@ -243,8 +250,50 @@ MTB_DEV void epi_rows(const Epi& e, const Staged<BN>& st, int M, int N, int mc, 
         }
         out8(e.out, (size_t)m * e.ldo + gp, dg);
         out8(e.out, (size_t)m * e.ldo + gp + 16, du);
+      } else if constexpr (EPI == EPI_XENT_GRAD) {
+        // dz = softmax - onehot(target), scaled by the token's loss cotangent
+        const float Mx = e.rowstat[m], sc = e.rowscale[m] / e.rowstat[M + m];
+        const int64_t lt = e.target[m] - e.col0 - n;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = exp_fast(v[i] - Mx) * sc;
+        if (lt >= 0 && lt < 8) v[lt] -= e.rowscale[m];
+        out8(e.out, (size_t)m * e.ldo + n, v);
       }
     }
+  }
+}
+
+// Row statistics of a logits tile for the vocab cross-entropy: per row of
+// the staged chunk, over this tile's valid columns, (max, sum exp(z - max),
+// z at the row's target or 0) into out [M][tiles_n][3]. NT / CR threads per
+// row, each over a contiguous run of columns, merged by lane shuffles.
+template <int BN, int CR, int NT>
+MTB_DEV void epi_xent_stats(const Epi& e, const Staged<BN>& st, int M, int N, int mc, int n0, int tn,
+                            int tiles_n, int tid) {
+  constexpr int TPR = NT / CR, CPT = BN / TPR;
+  static_assert(TPR * CR == NT && TPR <= 64 && (TPR & (TPR - 1)) == 0, "threads per row");
+  const int r = tid / TPR, part = tid % TPR, m = mc + r;
+  const int c0 = part * CPT, cend = min(CPT, N - n0 - c0);   // valid columns of this run
+  float mx = -__builtin_huge_valf(), sum = 0.f, tz = 0.f;
+  int64_t lt = -1;
+  if (m < M) lt = e.target[m] - e.col0 - n0 - c0;
+  for (int c = 0; c < cend; ++c) mx = fmaxf(mx, st.get(r, c0 + c));
+  for (int c = 0; c < cend; ++c) sum += exp_fast(st.get(r, c0 + c) - mx);
+  if (lt >= 0 && lt < cend) tz = st.get(r, c0 + (int)lt);
+#pragma unroll
+  for (int o = 1; o < TPR; o <<= 1) {
+    const float m2 = __shfl_xor(mx, o, 64), s2 = __shfl_xor(sum, o, 64);
+    tz += __shfl_xor(tz, o, 64);
+    const float Mx = fmaxf(mx, m2);
+    sum = (mx == -__builtin_huge_valf() ? 0.f : sum * exp_fast(mx - Mx)) +
+          (m2 == -__builtin_huge_valf() ? 0.f : s2 * exp_fast(m2 - Mx));
+    mx = Mx;
+  }
+  if (part == 0 && m < M) {
+    float* o = reinterpret_cast<float*>(e.out) + ((size_t)m * tiles_n + tn) * 3;
+    o[0] = mx;
+    o[1] = sum;
+    o[2] = tz;
   }
 }
 
@@ -405,9 +454,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(int M, i
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int KT = kspan / BK;
-  la.load(A, lda, m0, M, kbeg, tid);
-  lb.load(B, ldb, n0, N, kbeg, tid);
+  const int KT = (kspan + BK - 1) / BK, kend = kbeg + kspan;
+  la.load(A, lda, m0, M, kbeg, kend, tid);
+  lb.load(B, ldb, n0, N, kbeg, kend, tid);
   la.store(sA(0), tid);
   lb.store(sB(0), tid);
   __syncthreads();
@@ -415,8 +464,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(int M, i
   for (int kt = 0; kt < KT; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < KT) {
-      la.load(A, lda, m0, M, kbeg + (kt + 1) * BK, tid);
-      lb.load(B, ldb, n0, N, kbeg + (kt + 1) * BK, tid);
+      la.load(A, lda, m0, M, kbeg + (kt + 1) * BK, kend, tid);
+      lb.load(B, ldb, n0, N, kbeg + (kt + 1) * BK, kend, tid);
     }
     const bf16_t* as = sA(cur);
     const bf16_t* bs = sB(cur);
@@ -479,6 +528,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(int M, i
     if constexpr (EPI == EPI_PARTIAL)
       epi_partial<BN, CR, NT>(reinterpret_cast<float*>(ep.ws) + (size_t)split * M * N, st, M, N,
                               m0 + c0, n0, tid);
+    else if constexpr (EPI == EPI_XENT_STATS)
+      epi_xent_stats<BN, CR, NT>(ep, st, M, N, m0 + c0, n0, tn, tiles_n, tid);
     else
       epi_rows<EPI, BN, CR, NT>(ep, st, M, N, m0 + c0, n0, tid);
     if constexpr (COLS) {
@@ -591,7 +642,7 @@ Plan plan(int M, int N, int K, bool a_kc, bool b_kc, int kind, bool split_ok) {
   auto depth_ok = [&](int s) { return K % (s * BK) == 0 && K / s >= 1024; };
   if (!a_kc && !b_kc) {
     const long t2 = tl(256, 128);
-    if (split_ok && kind == EPI_STORE && t2 <= kCUs / 2) {
+    if (split_ok && kind == EPI_STORE && t2 <= kCUs / 2 && K % BK == 0) {
       int s = 1;
       while (s < 8 && t2 * s * 4 < 3L * kCUs && depth_ok(2 * s)) s *= 2;
       if (s > 1) return {T256x128, s};
@@ -600,7 +651,7 @@ Plan plan(int M, int N, int K, bool a_kc, bool b_kc, int kind, bool split_ok) {
     return {T128x128, 1};
   }
   const long t256 = tl(256, 256), t128 = tl(128, 128);
-  if (split_ok && a_kc && kind == EPI_STORE && t128 <= kCUs && t256 < kCUs) {
+  if (split_ok && a_kc && kind == EPI_STORE && t128 <= kCUs && t256 < kCUs && K % BK == 0) {
     int s = 1;
     while (s < 4 && t128 * s < 2L * kCUs && depth_ok(2 * s)) s *= 2;
     if (s > 1) return {T128x128, s};
@@ -656,6 +707,14 @@ hipError_t launch_bf16(int M, int N, int K, const void* A, int lda, const void* 
 
 }  // namespace
 
+int gemm_tile_n(int M, int N, int K, bool a_kc, bool b_kc, int kind) {
+  switch (plan(M, N, K, a_kc, b_kc, kind, false).tile) {
+    case T256x256: return 256;
+    case T256x192: return 192;
+    default: return 128;
+  }
+}
+
 size_t gemm_ws_bytes(int dtype, int M, int N, int K, bool a_kc, bool b_kc, int kind) {
   if (dtype == 0 || M <= 0 || N <= 0 || K <= 0) return 0;
   const Plan pl = plan(M, N, K, a_kc, b_kc, kind, true);
@@ -678,12 +737,17 @@ hipError_t gemm(int dtype, int M, int N, int K, const void* A, int lda, bool a_k
 #undef MTB_F32G
     return hipGetLastError();
   }
-  // bf16: K % 64 == 0, M % 8 == 0, N % 8 == 0 (checked by the caller)
+  // bf16: K % 8 == 0 (a partial last k-tile is zero-filled), M % 8 == 0, N % 8 == 0 (checked by
+  // the caller)
   if (a_kc && b_kc) {
     switch (e.kind) {
       case EPI_STORE: return launch_bf16<true, true, EPI_STORE>(M, N, K, A, lda, B, ldb, e, st);
       case EPI_GELU: return launch_bf16<true, true, EPI_GELU>(M, N, K, A, lda, B, ldb, e, st);
       case EPI_SWIGLU: return launch_bf16<true, true, EPI_SWIGLU>(M, N, K, A, lda, B, ldb, e, st);
+      case EPI_XENT_STATS:
+        return launch_bf16<true, true, EPI_XENT_STATS>(M, N, K, A, lda, B, ldb, e, st);
+      case EPI_XENT_GRAD:
+        return launch_bf16<true, true, EPI_XENT_GRAD>(M, N, K, A, lda, B, ldb, e, st);
       default: return hipErrorInvalidValue;
     }
   }

@@ -14,6 +14,11 @@ enum EpiKind {
                     // out2[m][f] = silu(gate) * up  [M][F]
   EPI_DGELU = 3,    // out = C * GELU'(aux[m][n])
   EPI_DSWIGLU = 4,  // C = dm [M][F]; aux = u [M][2F] interleaved: out [M][2F] = (d gate, d up)
+  EPI_XENT_STATS = 5,  // C = logits [M][N] (vocab columns from col0): per row and BN-wide column
+                       // tile, (max, sum exp(C - max), C at the row's target or 0) to
+                       // out (float) [M][tiles_n][3]; nothing else is stored
+  EPI_XENT_GRAD = 6,   // out = (exp(C - M_r) / S_r - [col0 + n == target_r]) * dloss_r with
+                       // M_r = rowstat[r], S_r = rowstat[M + r], dloss_r = rowscale[r]
 };
 
 struct Epi {
@@ -28,6 +33,10 @@ struct Epi {
   const void* aux = nullptr;   // [M][ldaux]
   int ldaux = 0;
   void* ws = nullptr;          // fp32 workspace for split-K partial tiles (gemm_ws_bytes), or null
+  const int64_t* target = nullptr;  // EPI_XENT_*: [M] global target ids
+  int64_t col0 = 0;                 // EPI_XENT_*: global vocab id of column 0
+  const float* rowstat = nullptr;   // EPI_XENT_GRAD: [2][M] (max, sum exp)
+  const float* rowscale = nullptr;  // EPI_XENT_GRAD: [M] loss cotangent
   void* outT = nullptr;        // [M/S][N][S]: per-batch transpose (tokens contiguous, bits 2
                                // and 3 of the token index swapped: see gemm.hip)
   int S = 1;
@@ -44,6 +53,9 @@ hipError_t gemm(int dtype, int M, int N, int K, const void* A, int lda, bool a_k
 // copy) with too few tiles to fill the chip are split; the partial tiles are
 // summed in a fixed order.
 size_t gemm_ws_bytes(int dtype, int M, int N, int K, bool a_kc, bool b_kc, int kind);
+// Column-tile width the bf16 GEMM uses for this problem (the tiles_n of
+// EPI_XENT_STATS is ceil(N / it)).
+int gemm_tile_n(int M, int N, int K, bool a_kc, bool b_kc, int kind);
 
 // LayerNorm over rows of width H: hsum = x (+resid) (+bias) rounded to dtype;
 // y = (hsum - mu) * rstd (* g + b). h_out (optional) receives hsum.
@@ -87,6 +99,10 @@ hipError_t xent_combine(int64_t n, int R, const float* shard_stats, float* stats
 hipError_t xent_finish(int dtype, int64_t n, int64_t v, int64_t v0, const void* z,
                        const int64_t* tgt, const float* stats, float* loss, const float* dloss,
                        void* dz, hipStream_t st);
+
+// LM head: merge per-column-tile logits statistics [n][tiles][3] into [3][n].
+hipError_t lmhead_combine(int64_t n, int tiles, const float* parts, float* stats, float* mloc,
+                          hipStream_t st);
 
 // Vocab-parallel embedding (one vocab shard [v0, v0 + vl) of the table).
 // Backward workspace: per table row, an int32 token count and first token.

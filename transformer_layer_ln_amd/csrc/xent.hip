@@ -144,6 +144,26 @@ __global__ __launch_bounds__(256) void xent_finish_kernel(int64_t n, int64_t v, 
   }
 }
 
+// per token: merge the (max, sum exp, target logit) of the logits' column
+// tiles [n][tiles][3] into stats [3][n] (+ the max into mloc if given)
+__global__ __launch_bounds__(256) void lmhead_combine_kernel(int64_t n, int tiles,
+                                                             const float* __restrict__ parts,
+                                                             float* __restrict__ stats,
+                                                             float* __restrict__ mloc) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const float* p = parts + (size_t)i * tiles * 3;
+  float m = kNegInf, s = 0.f, t = 0.f;
+  for (int k = 0; k < tiles; ++k) {
+    ms_merge(m, s, p[3 * k], p[3 * k + 1]);
+    t += p[3 * k + 2];
+  }
+  stats[i] = m;
+  stats[n + i] = s;
+  stats[2 * n + i] = t;
+  if (mloc) mloc[i] = m;
+}
+
 template <typename T>
 hipError_t partial_t(int64_t n, int64_t v, int64_t v0, const void* z, const int64_t* tgt,
                      float* stats, float* mloc, hipStream_t st) {
@@ -174,6 +194,13 @@ hipError_t xent_partial(int dtype, int64_t n, int64_t v, int64_t v0, const void*
                         const int64_t* tgt, float* stats, float* mloc, hipStream_t st) {
   return dtype == 1 ? partial_t<bf16_t>(n, v, v0, z, tgt, stats, mloc, st)
                     : partial_t<float>(n, v, v0, z, tgt, stats, mloc, st);
+}
+
+hipError_t lmhead_combine(int64_t n, int tiles, const float* parts, float* stats, float* mloc,
+                          hipStream_t st) {
+  hipLaunchKernelGGL(lmhead_combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, n,
+                     tiles, parts, stats, mloc);
+  return hipGetLastError();
 }
 
 hipError_t xent_rescale(int64_t n, float* stats, const float* mloc, hipStream_t st) {

@@ -38,6 +38,7 @@ _TAG = {
     "ln1_g": 30, "ln1_b": 31, "ln2_g": 32, "ln2_b": 33,
     "logits": 40, "targets": 41,
     "embed_table": 50, "embed_ids": 51, "embed_dout": 52,
+    "lmhead_h": 60, "lmhead_w": 61, "lmhead_targets": 62,
 }
 
 
@@ -116,6 +117,25 @@ class EmbedConfig:
         return self.vocab // self.tp
 
 
+@dataclass(frozen=True)
+class LmheadConfig:
+    """Vocab-parallel output layer + cross-entropy: final hidden states
+    [n_tokens, hidden] (N(0,1), what a LayerNorm with unit gain hands over),
+    a [vocab, hidden] output embedding split by vocab over tp ranks (N(0,
+    w_std^2), the usual 0.02 initialisation), uniform targets in [0, vocab)."""
+    name: str
+    n_tokens: int
+    vocab: int
+    hidden: int
+    tp: int
+    seed: int = 1006
+    w_std: float = 0.02
+
+    @property
+    def v_local(self) -> int:
+        return self.vocab // self.tp
+
+
 # The five workloads. C1 is the small fp32 correctness case; C2-C5 are one
 # rank's share of the tensor-parallel layers the pages describe.
 C1 = BlockConfig("C1-fp32-full", batch=1, seq=64, hidden=128, q_heads=4, kv_heads=4,
@@ -137,6 +157,10 @@ C5_XENT = XentConfig("C5-xent-v128256-tp8", n_tokens=8192, vocab=128256, tp=8, d
 # the input-side counterpart of C5's vocab shard: ids of the seq-4096 share's
 # 8192 tokens, one [16032 x 4096] shard of the 128256-row table
 C5_EMBED = EmbedConfig("C5-embed-v128256-h4096-tp8", n_tokens=8192, vocab=128256, hidden=4096, tp=8)
+# the output layer of the same model: the seq-4096 share's final hidden
+# states against one vocab shard of the [128256, 4096] output embedding
+C5_LMHEAD = LmheadConfig("C5-lmhead-v128256-h4096-tp8", n_tokens=8192, vocab=128256, hidden=4096,
+                         tp=8)
 
 CONFIGS = {"C1": C1, "C2": C2, "C4": C4, "C5": C5}
 
@@ -264,3 +288,18 @@ def embed_ids(cfg: EmbedConfig) -> np.ndarray:
 def embed_dout(cfg: EmbedConfig) -> np.ndarray:
     """Gradient of the embedding output [N, hidden], N(0,1)."""
     return _normal(cfg.seed, "embed_dout", 0, (cfg.n_tokens, cfg.hidden), 1.0, cfg.dtype)
+
+
+def lmhead_h(cfg: LmheadConfig) -> np.ndarray:
+    """Final hidden states [N, hidden] (bf16-exact float32)."""
+    return _normal(cfg.seed, "lmhead_h", 0, (cfg.n_tokens, cfg.hidden), 1.0, "bf16")
+
+
+def lmhead_w(cfg: LmheadConfig, rank: int) -> np.ndarray:
+    """Vocab shard ``rank``'s output-embedding rows [V_local, hidden]."""
+    return _normal(cfg.seed, "lmhead_w", rank, (cfg.v_local, cfg.hidden), cfg.w_std, "bf16")
+
+
+def lmhead_targets(cfg: LmheadConfig) -> np.ndarray:
+    return _rng(cfg.seed, "lmhead_targets").integers(0, cfg.vocab, size=cfg.n_tokens,
+                                                     dtype=np.int64)

@@ -26,7 +26,8 @@ WEIGHT_FIELDS = ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_o", "b_o",
 
 # the functions include/mtb.h declares
 EXPORTS = ("mtb_block_saved_bytes", "mtb_block_scratch_bytes", "mtb_block_fwd", "mtb_block_bwd",
-           "mtb_vocab_xent", "mtb_vocab_xent_combine", "mtb_vocab_embed_fwd",
+           "mtb_vocab_xent", "mtb_vocab_xent_combine", "mtb_lmhead_xent_workspace_bytes",
+           "mtb_lmhead_xent_fwd", "mtb_lmhead_xent_bwd", "mtb_vocab_embed_fwd",
            "mtb_vocab_embed_bwd_workspace_bytes", "mtb_vocab_embed_bwd", "mtb_trace_arm",
            "mtb_trace_disarm", "mtb_last_error")
 TRACE_NONE, TRACE_FC1_FWD, TRACE_ATTN_FWD, TRACE_LN1_FWD, TRACE_FC2_WGRAD = 0, 1, 2, 3, 4
@@ -89,6 +90,16 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mtb_vocab_xent.restype = c_int32
     lib.mtb_vocab_xent_combine.argtypes = [c_int64, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]
     lib.mtb_vocab_xent_combine.restype = c_int32
+    lib.mtb_lmhead_xent_workspace_bytes.argtypes = [c_int64, c_int64, c_int64]
+    lib.mtb_lmhead_xent_workspace_bytes.restype = c_size_t
+    lib.mtb_lmhead_xent_fwd.argtypes = [c_int64, c_int64, c_int64, c_int64, c_int32, c_void_p,
+                                        c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                        c_void_p]
+    lib.mtb_lmhead_xent_fwd.restype = c_int32
+    lib.mtb_lmhead_xent_bwd.argtypes = [c_int64, c_int64, c_int64, c_int64, c_int32, c_void_p,
+                                        c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                        c_void_p, c_void_p, c_void_p]
+    lib.mtb_lmhead_xent_bwd.restype = c_int32
     lib.mtb_vocab_embed_fwd.argtypes = [c_int64, c_int64, c_int64, c_int64, c_int32, c_void_p,
                                         c_void_p, c_void_p, c_void_p, c_void_p]
     lib.mtb_vocab_embed_fwd.restype = c_int32
@@ -183,6 +194,25 @@ def vocab_xent(n_tokens, v_local, v_start, dtype, phase, logits, target, stats, 
 def vocab_xent_combine(n_tokens, n_shards, shard_stats, stats, loss=None, stream=None):
     _check(load().mtb_vocab_xent_combine(n_tokens, n_shards, _ptr(shard_stats), _ptr(stats),
                                          _ptr(loss), _stream(stream)))
+
+
+def lmhead_xent_workspace_bytes(n_tokens, hidden, v_local):
+    return load().mtb_lmhead_xent_workspace_bytes(n_tokens, hidden, v_local)
+
+
+def lmhead_xent_fwd(n_tokens, hidden, v_local, v_start, dtype, h, w, target, stats, loss,
+                    workspace, comm=None, stream=None):
+    _check(load().mtb_lmhead_xent_fwd(n_tokens, hidden, v_local, v_start, dtype, _ptr(h), _ptr(w),
+                                      _ptr(target), _ptr(stats), _ptr(loss), _ptr(workspace),
+                                      byref(comm) if comm is not None else None, _stream(stream)))
+
+
+def lmhead_xent_bwd(n_tokens, hidden, v_local, v_start, dtype, h, w, target, stats, dloss, dh, dw,
+                    workspace, comm=None, stream=None):
+    _check(load().mtb_lmhead_xent_bwd(n_tokens, hidden, v_local, v_start, dtype, _ptr(h), _ptr(w),
+                                      _ptr(target), _ptr(stats), _ptr(dloss), _ptr(dh), _ptr(dw),
+                                      _ptr(workspace), byref(comm) if comm is not None else None,
+                                      _stream(stream)))
 
 
 def vocab_embed_fwd(n_tokens, v_local, v_start, hidden, dtype, ids, table, out, comm=None,
