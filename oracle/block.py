@@ -12,6 +12,15 @@ Structure ([Lab06] sec. 2 listing, steps (2)-(8); [TP-block] sec. 1-2):
     m   = GELU(c W1^T + b1)  or  silu(c Wg^T + bg) * (c Wu^T + bu)
     out = h + sum_r m_r W2_r^T + b2   row-parallel partials, reduction point g2  (6)(7)
 
+Post-LN variant ([Lab06] sec. 2 notes (2)(5) and sec. 5: the residual is
+added first and the sum is normalised, as in the original Transformer):
+
+    r1  = x + attn(x)          h   = LN1(r1)
+    r2  = h + mlp(h)           out = LN2(r2)
+
+with the same attention and MLP (and the same reduction points); the
+attention reads x itself and the MLP reads h.
+
 The backward follows the conjugate placement of the reductions: a
 row-parallel output is summed in the forward and passed through in the
 backward; a column-parallel input is passed through in the forward and its
@@ -176,14 +185,19 @@ def _lin(x, w, b=None):
 
 
 def block_forward(x, w, *, q_heads, kv_heads, head_dim, act="gelu", causal=False,
-                  eps=1e-5, R=1):
+                  eps=1e-5, R=1, norm="pre"):
     """Forward of the unsharded block given as R shards.
 
     x [B, S, H]; w the unsharded weights (keys as in the inputs module:
     wq [nq*d, H], wk, wv [nkv*d, H], wo [H, nq*d], w1 [F, H] or wg, wu [F, H],
     w2 [H, F], optional biases and LN gain/shift). q_heads, kv_heads are the
     unsharded head counts; each of the R shards takes q_heads/R and
-    kv_heads/R whole heads and ffn/R MLP columns. Returns (out, cache)."""
+    kv_heads/R whole heads and ffn/R MLP columns. norm = "pre" (LN before
+    each sublayer) or "post" (LN after each residual sum). Returns
+    (out, cache)."""
+    if norm not in ("pre", "post"):
+        raise ValueError(norm)
+    post = norm == "post"
     x = np.asarray(x, F64)
     w = {k: np.asarray(v, F64) for k, v in w.items()}
     B, S, H = x.shape
@@ -192,11 +206,15 @@ def block_forward(x, w, *, q_heads, kv_heads, head_dim, act="gelu", causal=False
     nq, nkv = q_heads // R, kv_heads // R
     x2 = x.reshape(T, H)
     cache = {"R": R, "B": B, "S": S, "H": H, "nq": nq, "nkv": nkv, "d": d,
-             "act": act, "causal": causal, "x": x2, "w": w, "shards": []}
+             "act": act, "causal": causal, "x": x2, "w": w, "shards": [], "post": post}
 
-    # (2) input LayerNorm, replicated on every rank
-    a, xhat1, rstd1 = layer_norm_fwd(x2, w.get("ln1_g"), w.get("ln1_b"), eps)
-    cache.update(a=a, xhat1=xhat1, rstd1=rstd1)
+    if post:
+        a = x2          # post-LN: attention reads the block input itself
+    else:
+        # (2) input LayerNorm, replicated on every rank
+        a, xhat1, rstd1 = layer_norm_fwd(x2, w.get("ln1_g"), w.get("ln1_b"), eps)
+        cache.update(xhat1=xhat1, rstd1=rstd1)
+    cache["a"] = a
 
     # attention: each shard owns whole heads; its projection is a partial sum
     p_attn = []
@@ -215,10 +233,16 @@ def block_forward(x, w, *, q_heads, kv_heads, head_dim, act="gelu", causal=False
     attn = sum(p_attn)
     if "bo" in w:
         attn = attn + w["bo"]
-    h = x2 + attn
-    # (5) second LayerNorm
-    c, xhat2, rstd2 = layer_norm_fwd(h, w.get("ln2_g"), w.get("ln2_b"), eps)
-    cache.update(h=h, c=c, xhat2=xhat2, rstd2=rstd2)
+    if post:
+        # residual first, then the first LayerNorm; the MLP reads its output
+        h, xhat1, rstd1 = layer_norm_fwd(x2 + attn, w.get("ln1_g"), w.get("ln1_b"), eps)
+        c = h
+        cache.update(h=h, c=c, xhat1=xhat1, rstd1=rstd1)
+    else:
+        h = x2 + attn
+        # (5) second LayerNorm
+        c, xhat2, rstd2 = layer_norm_fwd(h, w.get("ln2_g"), w.get("ln2_b"), eps)
+        cache.update(h=h, c=c, xhat2=xhat2, rstd2=rstd2)
 
     # MLP: column-parallel fc1 + activation, row-parallel fc2 partials
     p_mlp = []
@@ -241,7 +265,11 @@ def block_forward(x, w, *, q_heads, kv_heads, head_dim, act="gelu", causal=False
     y = sum(p_mlp)
     if "b2" in w:
         y = y + w["b2"]
-    out = h + y
+    if post:
+        out, xhat2, rstd2 = layer_norm_fwd(h + y, w.get("ln2_g"), w.get("ln2_b"), eps)
+        cache.update(xhat2=xhat2, rstd2=rstd2)
+    else:
+        out = h + y
     return out.reshape(B, S, H), cache
 
 
@@ -259,16 +287,24 @@ def block_backward(G, cache):
     T = B * S
     w = cache["w"]
     G2 = np.asarray(G, F64).reshape(T, H)
+    post = cache["post"]
     sg = {}
+    if post:
+        # post-LN: the output LayerNorm first; its input gradient feeds both
+        # the MLP branch and the residual into h
+        up, dg2, db2n = layer_norm_bwd(G2, cache["xhat2"], cache["rstd2"], w.get("ln2_g"))
+    else:
+        up = G2
 
-    # fc2 (row-parallel): g2's backward passes G unchanged to every shard
+    # fc2 (row-parallel): g2's backward passes its upstream gradient unchanged
+    # to every shard
     dc_parts = []
     for r in range(R):
         sh = cache["shards"][r]
         ws = sh["w"]
         g = {}
-        dm = G2 @ ws["w2"]
-        g["w2"] = G2.T @ sh["m"]
+        dm = up @ ws["w2"]
+        g["w2"] = up.T @ sh["m"]
         if cache["act"] == "gelu":
             du = dm * gelu_grad(sh["u"])
             g["w1"] = du.T @ cache["c"]
@@ -285,12 +321,17 @@ def block_backward(G, cache):
             dc_parts.append(dug @ ws["wg"] + duu @ ws["wu"])
         sg[r] = g
     if "b2" in w:
-        db2 = G2.sum(0)
+        db2 = up.sum(0)
 
     # column-parallel fc1 input: its gradient is summed over shards (f's backward)
     dc = sum(dc_parts)
-    dh_ln, dg2, db2n = layer_norm_bwd(dc, cache["xhat2"], cache["rstd2"], w.get("ln2_g"))
-    dh = G2 + dh_ln
+    if post:
+        dh = up + dc                        # at h = LN1(r1): residual + MLP input
+        up_attn, dg1, db1n = layer_norm_bwd(dh, cache["xhat1"], cache["rstd1"], w.get("ln1_g"))
+    else:
+        dh_ln, dg2, db2n = layer_norm_bwd(dc, cache["xhat2"], cache["rstd2"], w.get("ln2_g"))
+        dh = G2 + dh_ln
+        up_attn = dh
 
     # attention: projection (row-parallel), per-head attention, QKV (column-parallel)
     da_parts = []
@@ -299,8 +340,8 @@ def block_backward(G, cache):
         sh = cache["shards"][r]
         ws = sh["w"]
         g = sg[r]
-        do_tok = dh @ ws["wo"]
-        g["wo"] = dh.T @ sh["o"]
+        do_tok = up_attn @ ws["wo"]
+        g["wo"] = up_attn.T @ sh["o"]
         do = do_tok.reshape(B, S, nq, d).transpose(0, 2, 1, 3)
         dq, dk, dv = attention_bwd(sh["q"], sh["k"], sh["v"], do, cache["causal"])
         dq2 = dq.transpose(0, 2, 1, 3).reshape(T, nq * d)
@@ -313,11 +354,14 @@ def block_backward(G, cache):
         da_parts.append(dq2 @ ws["wq"] + dk2 @ ws["wk"] + dv2 @ ws["wv"])
         dk_tok.append(dk2)
     if "bo" in w:
-        dbo = dh.sum(0)
+        dbo = up_attn.sum(0)
 
     da = sum(da_parts)
-    dx_ln, dg1, db1n = layer_norm_bwd(da, cache["xhat1"], cache["rstd1"], w.get("ln1_g"))
-    dx = dh + dx_ln
+    if post:
+        dx = up_attn + da                   # attention read x itself
+    else:
+        dx_ln, dg1, db1n = layer_norm_bwd(da, cache["xhat1"], cache["rstd1"], w.get("ln1_g"))
+        dx = dh + dx_ln
 
     grads = {}
     for k in sg[0]:

@@ -40,25 +40,27 @@ def _rand_weights(rng, H, nq, nkv, d, F, act, bias, affine):
 
 
 VARIANTS = [
-    # act, causal, bias, affine, nq, nkv, R
-    ("gelu", False, False, False, 2, 2, 1),
-    ("gelu", True, True, True, 2, 2, 2),
-    ("swiglu", True, True, True, 4, 2, 2),    # GQA: 2 q heads per kv head
-    ("swiglu", False, False, False, 4, 1, 1),  # MQA-like: 4 q heads share 1 kv head
+    # act, causal, bias, affine, nq, nkv, R, norm
+    ("gelu", False, False, False, 2, 2, 1, "pre"),
+    ("gelu", True, True, True, 2, 2, 2, "pre"),
+    ("swiglu", True, True, True, 4, 2, 2, "pre"),    # GQA: 2 q heads per kv head
+    ("swiglu", False, False, False, 4, 1, 1, "pre"),  # MQA-like: 4 q heads share 1 kv head
+    ("gelu", True, True, True, 2, 2, 2, "post"),      # post-LN ([Lab06] sec. 2 (2)(5))
+    ("swiglu", False, False, False, 4, 2, 1, "post"),
 ]
 
 
 def _fwd(x, w, v, R=None):
-    act, causal, _, _, nq, nkv, r = v
+    act, causal, _, _, nq, nkv, r, norm = v
     return ob.block_forward(x, w, q_heads=nq, kv_heads=nkv, head_dim=4, act=act,
-                            causal=causal, R=r if R is None else R)
+                            causal=causal, R=r if R is None else R, norm=norm)
 
 
-@pytest.mark.parametrize("v", VARIANTS, ids=lambda v: f"{v[0]}-c{int(v[1])}-b{int(v[2])}-a{int(v[3])}-q{v[4]}kv{v[5]}-R{v[6]}")
+@pytest.mark.parametrize("v", VARIANTS, ids=lambda v: f"{v[0]}-c{int(v[1])}-b{int(v[2])}-a{int(v[3])}-q{v[4]}kv{v[5]}-R{v[6]}-{v[7]}")
 def test_block_backward_matches_central_differences(v):
     """Every gradient (dx and all weights) against central differences of
     L = sum(out * G), step 1e-6, on B=2, S=5, H=8, d=4, F=6."""
-    act, causal, bias, affine, nq, nkv, R = v
+    act, causal, bias, affine, nq, nkv, R, _ = v
     rng = np.random.default_rng(7)
     B, S, H, d, F = 2, 5, 8, 4, 6
     x = rng.normal(size=(B, S, H))
@@ -90,7 +92,8 @@ def test_block_backward_matches_central_differences(v):
         assert err <= 1e-6 * max(1.0, np.max(np.abs(grads[k]))), (k, err)
 
 
-def test_shard_sum_identity_forward_and_backward():
+@pytest.mark.parametrize("norm", ["pre", "post"])
+def test_shard_sum_identity_forward_and_backward(norm):
     """Splitting the layer over R = 4 ranks (whole heads, ffn/R columns) and
     summing the row-parallel partials reproduces the unsharded block, its
     input gradient and every weight gradient ([TP-block] sec. 1-2)."""
@@ -100,7 +103,7 @@ def test_shard_sum_identity_forward_and_backward():
         w = _rand_weights(rng, H, nq, nkv, d, F, act, True, True)
         x = rng.normal(size=(B, S, H))
         G = rng.normal(size=(B, S, H))
-        kw = dict(q_heads=nq, kv_heads=nkv, head_dim=d, act=act, causal=True)
+        kw = dict(q_heads=nq, kv_heads=nkv, head_dim=d, act=act, causal=True, norm=norm)
         o1, c1 = ob.block_forward(x, w, R=1, **kw)
         o4, c4 = ob.block_forward(x, w, R=4, **kw)
         dx1, g1 = ob.block_backward(G, c1)
@@ -219,22 +222,26 @@ def test_identical_keys_give_prefix_means():
     assert np.max(np.abs(o[0, 0] - pref)) < 1e-14
 
 
-def test_against_independent_float64_autograd():
-    """The same block written with torch float64 CPU ops and autograd."""
+@pytest.mark.parametrize("norm", ["pre", "post"])
+def test_against_independent_float64_autograd(norm):
+    """The same block written with torch float64 CPU ops and autograd
+    (post-LN: LN(x + attention(x)), then LN(h + MLP(h)))."""
     torch = pytest.importorskip("torch")
     F_ = torch.nn.functional
     rng = np.random.default_rng(21)
     B, S, H, nq, nkv, d, F = 2, 7, 16, 4, 2, 4, 12
+    post = norm == "post"
     for act, causal in (("gelu", False), ("swiglu", True)):
         w = _rand_weights(rng, H, nq, nkv, d, F, act, True, True)
         x = rng.normal(size=(B, S, H))
         G = rng.normal(size=(B, S, H))
-        out, c = ob.block_forward(x, w, q_heads=nq, kv_heads=nkv, head_dim=d, act=act, causal=causal)
+        out, c = ob.block_forward(x, w, q_heads=nq, kv_heads=nkv, head_dim=d, act=act, causal=causal,
+                                  norm=norm)
         dx, grads = ob.block_backward(G, c)
 
         tw = {k: torch.tensor(v, dtype=torch.float64, requires_grad=True) for k, v in w.items()}
         tx = torch.tensor(x, dtype=torch.float64, requires_grad=True)
-        a = F_.layer_norm(tx, (H,), tw["ln1_g"], tw["ln1_b"], 1e-5)
+        a = tx if post else F_.layer_norm(tx, (H,), tw["ln1_g"], tw["ln1_b"], 1e-5)
         q = F_.linear(a, tw["wq"], tw["bq"]).view(B, S, nq, d).permute(0, 2, 1, 3)
         k = F_.linear(a, tw["wk"], tw["bk"]).view(B, S, nkv, d).permute(0, 2, 1, 3)
         v = F_.linear(a, tw["wv"], tw["bv"]).view(B, S, nkv, d).permute(0, 2, 1, 3)
@@ -245,12 +252,18 @@ def test_against_independent_float64_autograd():
             sc = sc.masked_fill(torch.ones(S, S, dtype=torch.bool).triu(1), float("-inf"))
         o = torch.matmul(torch.softmax(sc, -1), v).permute(0, 2, 1, 3).reshape(B, S, nq * d)
         hh = tx + F_.linear(o, tw["wo"], tw["bo"])
-        cc = F_.layer_norm(hh, (H,), tw["ln2_g"], tw["ln2_b"], 1e-5)
+        if post:
+            hh = F_.layer_norm(hh, (H,), tw["ln1_g"], tw["ln1_b"], 1e-5)
+            cc = hh
+        else:
+            cc = F_.layer_norm(hh, (H,), tw["ln2_g"], tw["ln2_b"], 1e-5)
         if act == "gelu":
             m = F_.gelu(F_.linear(cc, tw["w1"], tw["b1"]))
         else:
             m = F_.silu(F_.linear(cc, tw["wg"], tw["bg"])) * F_.linear(cc, tw["wu"], tw["bu"])
         to = hh + F_.linear(m, tw["w2"], tw["b2"])
+        if post:
+            to = F_.layer_norm(to, (H,), tw["ln2_g"], tw["ln2_b"], 1e-5)
         (to * torch.tensor(G)).sum().backward()
         assert np.max(np.abs(to.detach().numpy() - out)) < 1e-12
         assert np.max(np.abs(tx.grad.numpy() - dx)) < 1e-11
@@ -267,3 +280,42 @@ def test_mean_loss_cotangent_leaves_layernorm_grad_zero_without_affine():
     _, xhat, rstd = ob.layer_norm_fwd(x)
     dx, _, _ = ob.layer_norm_bwd(np.full((3, 10), 0.01), xhat, rstd)
     assert np.max(np.abs(dx)) < 1e-15
+
+
+def test_post_ln_closed_form_with_zero_projections():
+    """Post-LN with Wo = W2 = 0 and no biases: out = LN(LN(x)) row by row.
+    Written out: y = (x - mean) / sqrt(var + eps) has variance
+    var / (var + eps), so out = y / sqrt(var / (var + eps) + eps). Its input
+    gradient (through two gain-free LayerNorms) has zero row sums."""
+    rng = np.random.default_rng(29)
+    H, nq, nkv, d, F = 12, 2, 2, 4, 8
+    w = _rand_weights(rng, H, nq, nkv, d, F, "gelu", False, False)
+    w["wo"] = np.zeros_like(w["wo"])
+    w["w2"] = np.zeros_like(w["w2"])
+    x = rng.normal(size=(2, 5, H)) * 3.0 + 1.0
+    G = rng.normal(size=(2, 5, H))
+    out, c = ob.block_forward(x, w, q_heads=nq, kv_heads=nkv, head_dim=d, causal=True, norm="post")
+    eps = 1e-5
+    mu = x.mean(-1, keepdims=True)
+    var = x.var(-1, keepdims=True)
+    ref = (x - mu) / np.sqrt(var + eps) / np.sqrt(var / (var + eps) + eps)
+    assert np.max(np.abs(out - ref)) < 1e-13
+    dx, _ = ob.block_backward(G, c)
+    assert np.max(np.abs(dx.sum(-1))) < 1e-13
+
+
+def test_post_ln_output_rows_are_normalised():
+    """Whatever the weights, a gain-free post-LN block's output rows have
+    mean 0 and variance v / (v + eps) (v: the row variance of r2 = h + mlp),
+    so strictly inside (0, 1) and close to 1 for unit-scale rows."""
+    rng = np.random.default_rng(31)
+    H, nq, nkv, d, F = 16, 4, 2, 4, 12
+    for act in ("gelu", "swiglu"):
+        w = _rand_weights(rng, H, nq, nkv, d, F, act, True, False)
+        x = rng.normal(size=(2, 6, H))
+        out, c = ob.block_forward(x, w, q_heads=nq, kv_heads=nkv, head_dim=d, act=act, norm="post")
+        assert np.max(np.abs(out.mean(-1))) < 1e-14
+        v = out.var(-1)
+        assert np.all(v < 1.0) and np.all(v > 0.999)
+        # and the MLP read the first LayerNorm's output, itself normalised
+        assert np.max(np.abs(c["c"].mean(-1))) < 1e-14
