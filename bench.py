@@ -7,7 +7,7 @@ share (hidden 4096, 4 local heads x 128, ffn chunk 2048, batch 4, causal,
 GELU). Prints ONE JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--workload seq2048|seq512|seq4096]
+                    [--workload seq2048|seq512|seq4096|seq4096-causal|seq2048-post]
     python bench.py --calibrate-copy MIB
     python bench.py --sweep
 
@@ -110,6 +110,9 @@ WORKLOADS = {
     "seq4096-causal": ("C5c", "TP=8 rank share of a hidden-4096 SwiGLU/GQA block: 4 q / 1 kv heads x "
                               "128, ffn chunk 1792 (gate+up 3584), batch 2, seq 4096, causal",
                        "one tp8 rank share"),
+    "seq2048-post": ("C4p", "TP=8 rank share of a hidden-4096 block in post-LN order: 4 local heads "
+                            "x 128, ffn chunk 2048, batch 4, seq 2048, causal, GELU",
+                     "one tp8 rank share"),
 }
 
 
@@ -118,6 +121,8 @@ def workload_cfg(key):
 
     if key == "C5c":
         return inputs.C5.with_(name="C5-tp8-s4096-swiglu-gqa-causal", causal=True)
+    if key == "C4p":
+        return inputs.C4.with_(name="C4-tp8-s2048-post-ln", norm="post")
     return inputs.CONFIGS[key]
 
 
@@ -479,14 +484,15 @@ def main():
                      "traffic": measured_traffic(args.workload), "traffic_unit": "bytes/launch",
                      "algorithmic_flops_per_launch": fc1_flops, "avg_ms": round(fc1_ms, 5)},
         "other_kernels": {
-            "ln1_fwd": {"bound": "hbm", "avg_ms": round(ln_ms, 5),
-                        "achieved_GBs": round(ln_bytes / (ln_ms * 1e-3) / 1e9, 1),
-                        "peak_GBs": PEAK_HBM_GBS},
+            # the input LayerNorm's kernels (pre-LN order only: post-LN has none)
+            "ln1_fwd": None if cfg.norm == "post" else {
+                "bound": "hbm", "avg_ms": round(ln_ms, 5),
+                "achieved_GBs": round(ln_bytes / (ln_ms * 1e-3) / 1e9, 1), "peak_GBs": PEAK_HBM_GBS},
             "attn_fwd": {"bound": "mfma", "avg_ms": round(attn_ms, 5),
                          "achieved_TFLOPs": round(attn_flops / (attn_ms * 1e-3) / 1e12, 1)},
-            "ln1_bwd": {"bound": "hbm", "avg_ms": round(lnb_ms, 5),
-                        "achieved_GBs": round(lnb_bytes / (lnb_ms * 1e-3) / 1e9, 1),
-                        "peak_GBs": PEAK_HBM_GBS},
+            "ln1_bwd": None if cfg.norm == "post" else {
+                "bound": "hbm", "avg_ms": round(lnb_ms, 5),
+                "achieved_GBs": round(lnb_bytes / (lnb_ms * 1e-3) / 1e9, 1), "peak_GBs": PEAK_HBM_GBS},
             "vocab_xent": {"bound": "hbm", "workload": (
                                f"one vocab shard [{xcfg.n_tokens} x {xcfg.v_local}] bf16 of "
                                f"V={xcfg.vocab} over TP={xcfg.tp}: partial (max, sum exp, target "

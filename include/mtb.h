@@ -66,6 +66,14 @@ typedef int32_t mtb_status;
 #define MTB_ACT_GELU 0
 #define MTB_ACT_SWIGLU 1
 
+/* LayerNorm placement. PRE ([Lab06] sec. 2 listing, (2) and (5)): each
+ * sublayer reads LN(stream) and adds to the un-normalised stream. POST (the
+ * order the same notes, (2)(5) and sec. 5, call post-LN: residual first,
+ * then LayerNorm, as in the original Transformer): h = LN1(x + attn(x)),
+ * out = LN2(h + mlp(h)). */
+#define MTB_NORM_PRE 0
+#define MTB_NORM_POST 1
+
 /* reduction ops of the communication hook */
 #define MTB_OP_SUM 0
 #define MTB_OP_MAX 1
@@ -87,7 +95,8 @@ typedef int32_t mtb_status;
  *     q head i reads kv head i / (q_heads / kv_heads), [TP-block] sec. 2 GQA);
  *   head_dim: d;  ffn: local MLP width F;
  *   act: MTB_ACT_*;  causal: 0/1 (key s' > query s masked);
- *   dtype: MTB_F32 / MTB_BF16;  ln_eps: LayerNorm epsilon (e.g. 1e-5).
+ *   dtype: MTB_F32 / MTB_BF16;  ln_eps: LayerNorm epsilon (e.g. 1e-5);
+ *   norm: MTB_NORM_PRE / MTB_NORM_POST.
  * Supported shapes (else MTB_EUNSUPPORTED):
  *   MTB_BF16: head_dim in {64, 128}; seq, hidden, ffn and q_heads*head_dim
  *     multiples of 64 (tokens, hidden and ffn need not be multiples of the
@@ -103,6 +112,7 @@ typedef struct mtb_cfg {
   int32_t causal;
   int32_t dtype;
   float ln_eps;
+  int32_t norm;
 } mtb_cfg;
 
 /* Weights of one rank's share, all [out, in] row-major, dtype of the cfg.
@@ -167,6 +177,8 @@ size_t mtb_block_scratch_bytes(const mtb_cfg *cfg);
  *   (causal optional, GQA by head groups); p_attn = O Wo^T  [reduction g1];
  *   h = x + sum(p_attn) + b_o; c = LN2(h); m = GELU(c W1^T + b1) or
  *   silu(gate)*up; p_mlp = m W2^T  [reduction g2]; out = h + sum(p_mlp) + b2.
+ * MTB_NORM_POST: qkv from x itself; h = LN1(x + sum(p_attn) + b_o) is the MLP
+ *   input; out = LN2(h + sum(p_mlp) + b2). Same phases and reduction points.
  * Arguments:
  *   x [B,S,H]           block input (read in SEG0, SEG1; must be unchanged
  *                       between the phases of one pass)
@@ -195,10 +207,15 @@ mtb_status mtb_block_fwd(const mtb_cfg *cfg, const mtb_weights *w, int32_t phase
  *         attention and QKV backward -> dx := this rank's da partial
  *   SEG2: reduced_in = sum of da; LN1 backward + residual -> dx
  *   ALL:  the whole pass, hook at the two points -> dx
+ * MTB_NORM_POST: SEG0 starts with LN2's backward; SEG1 runs LN1's backward
+ *   of (residual + sum of dc) before the attention; SEG2 adds the sum of da
+ *   to LN1's input gradient -> dx. LN2 gradients are written in SEG0, LN1's
+ *   in SEG1.
  * x and saved are those of the matching mtb_block_fwd; dout must be
- * unchanged across the phases. Weight gradients are written in the phase
- * that computes them (fc1/fc2 in SEG0; LN2, projection, QKV in SEG1; LN1 in
- * SEG2). dx may not alias any input. */
+ * unchanged across the phases, and the same scratch passed to all of them.
+ * Weight gradients are written in the phase that computes them (fc1/fc2 in
+ * SEG0; LN2, projection, QKV in SEG1; LN1 in SEG2). dx may not alias any
+ * input. */
 mtb_status mtb_block_bwd(const mtb_cfg *cfg, const mtb_weights *w, int32_t phase,
                          const void *x, const void *saved, const void *dout,
                          const void *reduced_in, void *dx, const mtb_grads *grads,

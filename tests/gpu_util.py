@@ -47,7 +47,7 @@ def host(t):
 
 def oracle_kw(cfg):
     return dict(q_heads=cfg.q_heads, kv_heads=cfg.kv_heads, head_dim=cfg.head_dim, act=cfg.act,
-                causal=cfg.causal, eps=cfg.ln_eps)
+                causal=cfg.causal, eps=cfg.ln_eps, norm=cfg.norm)
 
 
 def split_grads(g: dict, cfg) -> dict:
@@ -109,7 +109,7 @@ def check_rank_vs_oracle(cfg, w_split, x, G, tol=None, comm=None, label=""):
     tol = TOL[cfg.dtype] if tol is None else tol
     say(f"[gpu] {label or cfg.name}: B={cfg.batch} S={cfg.seq} H={cfg.hidden} nq={cfg.q_heads} "
         f"nkv={cfg.kv_heads} d={cfg.head_dim} F={cfg.ffn} act={cfg.act} causal={cfg.causal} "
-        f"dtype={cfg.dtype}")
+        f"dtype={cfg.dtype} norm={cfg.norm}")
     out, dx, grads = run_rank(cfg, w_split, x, G, comm=comm)
     ref_out, cache = ob.block_forward(x, w_split, R=1, **oracle_kw(cfg))
     ref_dx, ref_g = ob.block_backward(G, cache)

@@ -44,6 +44,11 @@ def test_size_queries_accept_valid_and_reject_invalid_configs():
     assert mtb.saved_bytes(_cfg(seq=100)) == 0
     assert mtb.saved_bytes(_cfg(act="swiglu", ffn=520)) == 0
     assert mtb.saved_bytes(_cfg(dtype="f32", head_dim=32, seq=100)) > 0   # fp32 path: any seq
+    assert mtb.saved_bytes(_cfg(norm="post")) == mtb.saved_bytes(_cfg())
+    assert mtb.scratch_bytes(_cfg(norm="post")) > mtb.scratch_bytes(_cfg())
+    bad = _cfg()
+    bad.norm = 2
+    assert mtb.saved_bytes(bad) == 0 and "norm" in mtb.last_error()
 
 
 def test_saved_bytes_scale_with_tokens():
@@ -148,8 +153,8 @@ def test_embed_workspace_query():
 
 
 def test_struct_layout_matches_header():
-    # 10 int32 fields + 1 float
-    assert ctypes.sizeof(mtb.Cfg) == 44
+    # 10 int32 fields + 1 float + 1 int32
+    assert ctypes.sizeof(mtb.Cfg) == 48
     assert ctypes.sizeof(mtb.Weights) == 12 * ctypes.sizeof(ctypes.c_void_p)
     assert ctypes.sizeof(mtb.Comm) == 2 * ctypes.sizeof(ctypes.c_void_p)
 

@@ -145,3 +145,38 @@ def test_graph_replay_matches_eager_step():
 def test_graph_replay_matches_eager_step_seq512_share():
     say("[gpu] graph replay, seq-512 TP=4 share")
     _graph_case(inputs.C2)
+
+
+# post-LN ([Lab06] sec. 2 notes (2)(5)): residual first, then LayerNorm
+@pytest.mark.parametrize("variant", [
+    dict(),
+    dict(act="swiglu", ffn=256, kv_heads=2, causal=True, affine=True, bias=True),
+])
+def test_fp32_post_ln(variant):
+    cfg = inputs.C1.with_(name="fp32-post", norm="post", **variant)
+    w, x, G = _case(cfg)
+    check_rank_vs_oracle(cfg, w, x, G)
+
+
+@pytest.mark.parametrize("i", [0, 1, 3])
+def test_bf16_post_ln_small_shapes(i):
+    cfg = inputs.BlockConfig(f"bf16-post-{i}", dtype="bf16", tp=1, seed=2500 + i, norm="post",
+                             **BF16_SMALL[i])
+    w, x, G = _case(cfg)
+    check_rank_vs_oracle(cfg, w, x, G)
+
+
+def test_c4_post_ln_rank_share_full_size():
+    """The seq-2048 causal TP=8 rank share in post-LN order, whole tensors."""
+    cfg = inputs.C4.with_(name="C4-post", norm="post")
+    w, x, G = _case(cfg)
+    check_rank_vs_oracle(cfg, w, x, G)
+
+
+@pytest.mark.gpu
+def test_graph_replay_matches_eager_step_post_ln():
+    cfg = inputs.BlockConfig("graph-post", batch=2, seq=256, hidden=512, q_heads=4, kv_heads=2,
+                             head_dim=64, ffn=512, act="swiglu", causal=True, seed=2600, norm="post",
+                             affine=True, bias=True)
+    say("[gpu] graph replay, post-LN", cfg)
+    _graph_case(cfg)

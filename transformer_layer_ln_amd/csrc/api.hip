@@ -2,7 +2,8 @@
 // `saved` / `scratch` buffers, and the order of kernel launches for the
 // forward and backward pass of one tensor-parallel rank's share of the block.
 //
-// Block structure: [Lab06] sec. 2 listing steps (2)-(8) in its pre-LN order;
+// Block structure: [Lab06] sec. 2 listing steps (2)-(8) in its pre-LN order,
+// or the post-LN order its notes (2)(5) describe (residual first, then LN);
 // sharding and the reduction points: [TP-block] sec. 1-2 (column-parallel
 // QKV and fc1, row-parallel projection and fc2, two all-reduces forward and
 // two backward); vocab-parallel cross-entropy: [TP-block] sec. 4.
@@ -43,6 +44,7 @@ struct Dims {
   int dt;      // MTB_F32 / MTB_BF16
   int act, causal;
   float eps;
+  bool post;   // post-LN order
 };
 
 mtb_status check_cfg(const mtb_cfg* c, Dims& d) {
@@ -58,9 +60,12 @@ mtb_status check_cfg(const mtb_cfg* c, Dims& d) {
   if (c->causal != 0 && c->causal != 1) return fail(MTB_EINVAL, "causal must be 0 or 1");
   if (c->dtype != MTB_F32 && c->dtype != MTB_BF16) return fail(MTB_EINVAL, "bad dtype %d", c->dtype);
   if (!(c->ln_eps > 0.f) || c->ln_eps > 1.f) return fail(MTB_EINVAL, "ln_eps must be in (0, 1]");
+  if (c->norm != MTB_NORM_PRE && c->norm != MTB_NORM_POST)
+    return fail(MTB_EINVAL, "norm must be MTB_NORM_PRE or MTB_NORM_POST");
   d.B = c->batch; d.S = c->seq; d.H = c->hidden; d.nq = c->q_heads; d.nkv = c->kv_heads;
   d.d = c->head_dim; d.F = c->ffn; d.act = c->act; d.causal = c->causal; d.dt = c->dtype;
   d.eps = c->ln_eps;
+  d.post = c->norm == MTB_NORM_POST;
   d.Fu = d.act == MTB_ACT_SWIGLU ? 2 * d.F : d.F;
   d.Nqkv = (d.nq + 2 * d.nkv) * d.d;
   d.T = d.B * d.S;
@@ -87,6 +92,9 @@ mtb_status check_cfg(const mtb_cfg* c, Dims& d) {
 
 size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Saved activations. Pre-LN: a = LN1(x), h = x + attn, c = LN2(h).
+// Post-LN: h = r1 = x + attn, c = LN1(r1) (the MLP input), a = r2 = c + mlp
+// (the second LayerNorm's input); mu/rstd 1 and 2 belong to LN1 and LN2.
 struct Saved {
   size_t a, mu1, rs1, qkv, qkvT, O, lse, h, mu2, rs2, c, u, m, total;
 };
@@ -112,13 +120,14 @@ Saved saved_layout(const Dims& d) {
 }
 
 struct Scratch {
-  size_t dh, p, du, dm, dO, dOT, Dbuf, dqkv, part, red, ws, total;
+  size_t dh, dr, p, du, dm, dO, dOT, Dbuf, dqkv, part, red, ws, total;
 };
 Scratch scratch_layout(const Dims& d) {
   Scratch s;
   size_t o = 0;
   const size_t e = d.es, T = d.T;
-  s.dh = o; o += al(T * d.H * e);       // persists from backward SEG1 to SEG2
+  s.dh = o; o += al(T * d.H * e);       // pre: dh, SEG1 -> SEG2; post: dr2, SEG0 -> SEG1
+  s.dr = o; o += d.post ? al(T * d.H * e) : 0;   // post: dr1, SEG1 -> SEG2
   s.p = o; o += al(T * d.H * e);        // partial sums (p_attn, p_mlp, dc, da)
   s.du = o; o += al(T * d.Fu * e);
   s.dm = o; o += d.dt == MTB_F32 ? al(T * d.F * e) : 0;
@@ -315,16 +324,26 @@ mtb_status mtb_block_fwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
   void* ws = Z.total > Z.ws ? P(scratch, Z.ws) : nullptr;
 
   const bool all = phase == MTB_PHASE_ALL;
+  const bool post = d.post;
+  // the LayerNorm after the attention residual: LN2 (pre-LN) or LN1 (post-LN)
+  const void* lnA_g = post ? w->ln1_g : w->ln2_g;
+  const void* lnA_b = post ? w->ln1_b : w->ln2_b;
+  float* muA = post ? mu1 : mu2;
+  float* rsA = post ? rs1 : rs2;
+  void* r2 = a;  // post-LN: the second LayerNorm's input
   if (phase == MTB_PHASE_ALL || phase == MTB_PHASE_SEG0) {
     if (all) trace_begin(MTB_TRACE_ATTN_SEG, st);
-    // (2) input LayerNorm
-    trace_begin(MTB_TRACE_LN1_FWD, st);
-    MTB_HIP(ln_fwd(dt, T, H, x, nullptr, nullptr, w->ln1_g, w->ln1_b, nullptr, a, mu1, rs1, d.eps, st));
-    trace_end(MTB_TRACE_LN1_FWD, st);
-    // column-parallel QKV; the bf16 path also keeps a per-batch transpose for attention
+    if (!post) {
+      // (2) input LayerNorm
+      trace_begin(MTB_TRACE_LN1_FWD, st);
+      MTB_HIP(ln_fwd(dt, T, H, x, nullptr, nullptr, w->ln1_g, w->ln1_b, nullptr, a, mu1, rs1, d.eps, st));
+      trace_end(MTB_TRACE_LN1_FWD, st);
+    }
+    // column-parallel QKV on LN1(x) (pre-LN) or x (post-LN); the bf16 path
+    // also keeps a per-batch transpose for attention
     Epi e;
     e.out = qkv; e.ldo = Nq; e.bias = w->b_qkv; e.outT = qkvT; e.S = S; e.ws = ws;
-    MTB_HIP(gemm(dt, T, Nq, H, a, H, true, w->w_qkv, H, true, e, st));
+    MTB_HIP(gemm(dt, T, Nq, H, post ? x : a, H, true, w->w_qkv, H, true, e, st));
     // per-head attention over the local heads
     trace_begin(MTB_TRACE_ATTN_FWD, st);
     MTB_HIP(attn_fwd(dt, (int)d.B, S, (int)d.nq, (int)d.nkv, (int)d.d, d.causal, qkv, qkvT, O, lse, st));
@@ -342,16 +361,17 @@ mtb_status mtb_block_fwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
     if (fused) {
       trace_end(MTB_TRACE_ATTN_SEG, st);
       trace_begin(MTB_TRACE_FFN_SEG, st);
-      MTB_HIP(ln_fwd(dt, T, H, h, nullptr, nullptr, w->ln2_g, w->ln2_b, nullptr, c, mu2, rs2, d.eps, st));
+      MTB_HIP(ln_fwd(dt, T, H, h, nullptr, nullptr, lnA_g, lnA_b, nullptr, c, muA, rsA, d.eps, st));
     } else {
       if ((s = call_hook(comm, p, d.T * d.H, dt, MTB_OP_SUM, st)) != MTB_OK) return s;
       trace_end(MTB_TRACE_ATTN_SEG, st);
       trace_begin(MTB_TRACE_FFN_SEG, st);
-      MTB_HIP(ln_fwd(dt, T, H, x, p, w->b_o, w->ln2_g, w->ln2_b, h, c, mu2, rs2, d.eps, st));
+      MTB_HIP(ln_fwd(dt, T, H, x, p, w->b_o, lnA_g, lnA_b, h, c, muA, rsA, d.eps, st));
     }
   } else if (phase == MTB_PHASE_SEG1) {
-    // g1 done by the caller: h = x + sum(p_attn) + b_o, then (5) LN2
-    MTB_HIP(ln_fwd(dt, T, H, x, reduced_in, w->b_o, w->ln2_g, w->ln2_b, h, c, mu2, rs2, d.eps, st));
+    // g1 done by the caller: h = x + sum(p_attn) + b_o, then (5) LN2 (pre-LN)
+    // or LN1 (post-LN) of it
+    MTB_HIP(ln_fwd(dt, T, H, x, reduced_in, w->b_o, lnA_g, lnA_b, h, c, muA, rsA, d.eps, st));
   }
 
   if (phase == MTB_PHASE_ALL || phase == MTB_PHASE_SEG1) {
@@ -369,24 +389,37 @@ mtb_status mtb_block_fwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
       MTB_HIP(gemm(dt, T, Fu, H, c, H, true, w->w_fc1, H, true, e, st));
       MTB_HIP(act_fwd(dt, d.act, T, F, u, m, st));
     }
-    // (6) row-parallel fc2: a partial sum, reduced at g2; (7) residual
+    // (6) row-parallel fc2: a partial sum, reduced at g2; (7) residual onto
+    // h (pre-LN) or onto the MLP input (post-LN, then LN2)
     Epi e;
     e.ws = ws;
     if (fused) {
-      e.out = out; e.ldo = H; e.bias = w->b_fc2; e.resid = h; e.ldr = H;
+      e.out = post ? r2 : out; e.ldo = H; e.bias = w->b_fc2; e.resid = post ? c : h; e.ldr = H;
     } else {
       e.out = phase == MTB_PHASE_SEG1 ? out : p; e.ldo = H;
     }
     MTB_HIP(gemm(dt, T, H, F, m, F, true, w->w_fc2, F, true, e, st));
-    if (fused) trace_end(MTB_TRACE_FFN_SEG, st);
+    if (fused) {
+      if (post)
+        MTB_HIP(ln_fwd(dt, T, H, r2, nullptr, nullptr, w->ln2_g, w->ln2_b, nullptr, out, mu2, rs2,
+                       d.eps, st));
+      trace_end(MTB_TRACE_FFN_SEG, st);
+    }
     if (fused || phase == MTB_PHASE_SEG1) return MTB_OK;
     if ((s = call_hook(comm, p, d.T * d.H, dt, MTB_OP_SUM, st)) != MTB_OK) return s;
-    MTB_HIP(add3(dt, T, H, h, p, w->b_fc2, out, st));
+    if (post)
+      MTB_HIP(ln_fwd(dt, T, H, c, p, w->b_fc2, w->ln2_g, w->ln2_b, r2, out, mu2, rs2, d.eps, st));
+    else
+      MTB_HIP(add3(dt, T, H, h, p, w->b_fc2, out, st));
     trace_end(MTB_TRACE_FFN_SEG, st);
     return MTB_OK;
   }
-  // SEG2: out = h + sum(p_mlp) + b2
-  MTB_HIP(add3(dt, T, H, h, reduced_in, w->b_fc2, out, st));
+  // SEG2: out = h + sum(p_mlp) + b2 (pre-LN), or LN2(c + sum(p_mlp) + b2)
+  if (post)
+    MTB_HIP(ln_fwd(dt, T, H, c, reduced_in, w->b_fc2, w->ln2_g, w->ln2_b, r2, out, mu2, rs2, d.eps,
+                   st));
+  else
+    MTB_HIP(add3(dt, T, H, h, reduced_in, w->b_fc2, out, st));
   return MTB_OK;
 }
 
@@ -436,15 +469,26 @@ mtb_status mtb_block_bwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
   const float* rs2 = (const float*)(sv + L.rs2);
   const void* c = sv + L.c; const void* u = sv + L.u; const void* m = sv + L.m;
   void* dh = P(scratch, Z.dh); void* p = P(scratch, Z.p); void* du = P(scratch, Z.du);
+  void* dr = d.post ? P(scratch, Z.dr) : nullptr;
   void* dm = P(scratch, Z.dm); void* dO = P(scratch, Z.dO); void* dOT = bf ? P(scratch, Z.dOT) : nullptr;
   float* Dbuf = (float*)P(scratch, Z.Dbuf); void* dqkv = P(scratch, Z.dqkv);
   float* part = (float*)P(scratch, Z.part); float* red = (float*)P(scratch, Z.red);
   void* ws = Z.total > Z.ws ? P(scratch, Z.ws) : nullptr;
-  const void* G = dout;
   const bool all = phase == MTB_PHASE_ALL;
+  const bool post = d.post;
+  const bool fused = all && !(comm && comm->allreduce);
+  // upstream gradient of the MLP branch: dout (pre-LN) or LN2's input
+  // gradient dr2 (post-LN, kept in the dh buffer until SEG1)
+  const void* G = post ? dh : dout;
   if (all) trace_begin(MTB_TRACE_BWD, st);
 
   if (phase == MTB_PHASE_ALL || phase == MTB_PHASE_SEG0) {
+    if (post) {
+      // post-LN: out = LN2(r2), r2 kept in the `a` slot
+      MTB_HIP(ln_bwd(dt, T, H, dout, nullptr, a, mu2, rs2, w->ln2_g, nullptr, dh, st));
+      if (g.ln2_g) MTB_HIP(colsum(dt, T, H, dout, nullptr, H, a, mu2, rs2, g.ln2_g, red, st));
+      if (g.ln2_b) MTB_HIP(colsum(dt, T, H, dout, nullptr, H, nullptr, nullptr, nullptr, g.ln2_b, red, st));
+    }
     // fc2 backward: dm = G W2 with the activation's derivative fused (bf16)
     if (bf) {
       Epi e;
@@ -464,13 +508,13 @@ mtb_status mtb_block_bwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
       MTB_HIP(gemm(dt, H, F, T, G, H, false, m, F, false, e, st));
       trace_end(MTB_TRACE_FC2_WGRAD, st);
     }
-    if (g.b_fc2) MTB_HIP(colsum(dt, T, H, G, H, nullptr, nullptr, nullptr, g.b_fc2, red, st));
+    if (g.b_fc2) MTB_HIP(colsum(dt, T, H, G, nullptr, H, nullptr, nullptr, nullptr, g.b_fc2, red, st));
     if (g.w_fc1) {
       Epi e;
       e.out = g.w_fc1; e.ldo = H; e.ws = ws;
       MTB_HIP(gemm(dt, Fu, H, T, du, Fu, false, c, H, false, e, st));
     }
-    if (g.b_fc1) MTB_HIP(colsum(dt, T, Fu, du, Fu, nullptr, nullptr, nullptr, g.b_fc1, red, st));
+    if (g.b_fc1) MTB_HIP(colsum(dt, T, Fu, du, nullptr, Fu, nullptr, nullptr, nullptr, g.b_fc1, red, st));
     // fc1 input gradient: partial over ranks, summed at f1
     Epi e;
     e.out = phase == MTB_PHASE_SEG0 ? dx : p; e.ldo = H; e.ws = ws;
@@ -481,46 +525,70 @@ mtb_status mtb_block_bwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
 
   if (phase == MTB_PHASE_ALL || phase == MTB_PHASE_SEG1) {
     const void* dc = phase == MTB_PHASE_SEG1 ? reduced_in : p;
-    // LN2 backward + residual: dh = G + LN2^T(dc)
-    MTB_HIP(ln_bwd(dt, T, H, dc, h, mu2, rs2, w->ln2_g, G, dh, st));
-    if (g.ln2_g) MTB_HIP(colsum(dt, T, H, dc, H, h, mu2, rs2, g.ln2_g, red, st));
-    if (g.ln2_b) MTB_HIP(colsum(dt, T, H, dc, H, nullptr, nullptr, nullptr, g.ln2_b, red, st));
+    // upstream gradient of the attention branch
+    const void* dA;
+    if (post) {
+      // LN1 backward of the gradient at h = LN1(r1): residual dr2 + MLP input dc
+      MTB_HIP(ln_bwd(dt, T, H, dc, dh, h, mu1, rs1, w->ln1_g, nullptr, dr, st));
+      if (g.ln1_g) MTB_HIP(colsum(dt, T, H, dc, dh, H, h, mu1, rs1, g.ln1_g, red, st));
+      if (g.ln1_b) MTB_HIP(colsum(dt, T, H, dc, dh, H, nullptr, nullptr, nullptr, g.ln1_b, red, st));
+      dA = dr;
+    } else {
+      // LN2 backward + residual: dh = G + LN2^T(dc)
+      MTB_HIP(ln_bwd(dt, T, H, dc, nullptr, h, mu2, rs2, w->ln2_g, G, dh, st));
+      if (g.ln2_g) MTB_HIP(colsum(dt, T, H, dc, nullptr, H, h, mu2, rs2, g.ln2_g, red, st));
+      if (g.ln2_b) MTB_HIP(colsum(dt, T, H, dc, nullptr, H, nullptr, nullptr, nullptr, g.ln2_b, red, st));
+      dA = dh;
+    }
     // projection backward (row-parallel: g1's backward is the identity)
     {
       Epi e;
       e.out = dO; e.ldo = NO; e.outT = dOT; e.S = S; e.ws = ws;
-      MTB_HIP(gemm(dt, T, NO, H, dh, H, true, w->w_o, NO, false, e, st));
+      MTB_HIP(gemm(dt, T, NO, H, dA, H, true, w->w_o, NO, false, e, st));
     }
     if (g.w_o) {
       Epi e;
       e.out = g.w_o; e.ldo = NO; e.ws = ws;
-      MTB_HIP(gemm(dt, H, NO, T, dh, H, false, O, NO, false, e, st));
+      MTB_HIP(gemm(dt, H, NO, T, dA, H, false, O, NO, false, e, st));
     }
-    if (g.b_o) MTB_HIP(colsum(dt, T, H, dh, H, nullptr, nullptr, nullptr, g.b_o, red, st));
+    if (g.b_o) MTB_HIP(colsum(dt, T, H, dA, nullptr, H, nullptr, nullptr, nullptr, g.b_o, red, st));
     // attention backward
     MTB_HIP(attn_bwd(dt, (int)d.B, S, (int)d.nq, (int)d.nkv, (int)d.d, d.causal, qkv, qkvT, O, dO,
                      dOT, lse, Dbuf, dqkv, part, st));
     if (g.w_qkv) {
       Epi e;
       e.out = g.w_qkv; e.ldo = H; e.ws = ws;
-      MTB_HIP(gemm(dt, Nq, H, T, dqkv, Nq, false, a, H, false, e, st));
+      MTB_HIP(gemm(dt, Nq, H, T, dqkv, Nq, false, post ? x : a, H, false, e, st));
     }
-    if (g.b_qkv) MTB_HIP(colsum(dt, T, Nq, dqkv, Nq, nullptr, nullptr, nullptr, g.b_qkv, red, st));
-    // QKV input gradient: partial over ranks, summed at f2
+    if (g.b_qkv) MTB_HIP(colsum(dt, T, Nq, dqkv, nullptr, Nq, nullptr, nullptr, nullptr, g.b_qkv, red, st));
+    // QKV input gradient: partial over ranks, summed at f2 (post-LN with the
+    // identity reduction: dx = dr1 + da straight from the epilogue)
     Epi e;
     e.out = phase == MTB_PHASE_SEG1 ? dx : p; e.ldo = H; e.ws = ws;
+    if (post && fused) {
+      e.out = dx; e.resid = dr; e.ldr = H;
+    }
     MTB_HIP(gemm(dt, T, H, Nq, dqkv, Nq, true, w->w_qkv, H, false, e, st));
     if (phase == MTB_PHASE_SEG1) return MTB_OK;
+    if (post && fused) {
+      trace_end(MTB_TRACE_BWD, st);
+      return MTB_OK;
+    }
     if ((s = call_hook(comm, p, d.T * d.H, dt, MTB_OP_SUM, st)) != MTB_OK) return s;
   }
 
-  // LN1 backward + residual: dx = dh + LN1^T(da)
   const void* da = phase == MTB_PHASE_SEG2 ? reduced_in : p;
-  trace_begin(MTB_TRACE_LN1_BWD, st);
-  MTB_HIP(ln_bwd(dt, T, H, da, x, mu1, rs1, w->ln1_g, dh, dx, st));
-  trace_end(MTB_TRACE_LN1_BWD, st);
-  if (g.ln1_g) MTB_HIP(colsum(dt, T, H, da, H, x, mu1, rs1, g.ln1_g, red, st));
-  if (g.ln1_b) MTB_HIP(colsum(dt, T, H, da, H, nullptr, nullptr, nullptr, g.ln1_b, red, st));
+  if (post) {
+    // the attention read x itself: dx = dr1 + da
+    MTB_HIP(add3(dt, T, H, dr, da, nullptr, dx, st));
+  } else {
+    // LN1 backward + residual: dx = dh + LN1^T(da)
+    trace_begin(MTB_TRACE_LN1_BWD, st);
+    MTB_HIP(ln_bwd(dt, T, H, da, nullptr, x, mu1, rs1, w->ln1_g, dh, dx, st));
+    trace_end(MTB_TRACE_LN1_BWD, st);
+    if (g.ln1_g) MTB_HIP(colsum(dt, T, H, da, nullptr, H, x, mu1, rs1, g.ln1_g, red, st));
+    if (g.ln1_b) MTB_HIP(colsum(dt, T, H, da, nullptr, H, nullptr, nullptr, nullptr, g.ln1_b, red, st));
+  }
   if (all) trace_end(MTB_TRACE_BWD, st);
   return MTB_OK;
 }

@@ -62,13 +62,16 @@ int gemm_tile_n(int M, int N, int K, bool a_kc, bool b_kc, int kind);
 hipError_t ln_fwd(int dtype, int rows, int H, const void* x, const void* resid, const void* bias,
                   const void* g, const void* b, void* h_out, void* y, float* mu, float* rstd,
                   float eps, hipStream_t st);
-// dx = dres + LN backward of dy at xhat = (hin - mu) * rstd, gain g (optional).
-hipError_t ln_bwd(int dtype, int rows, int H, const void* dy, const void* hin, const float* mu,
-                  const float* rstd, const void* g, const void* dres, void* dx, hipStream_t st);
-// column sums over rows: out[n] = sum_r y[r][n] (*xhat[r][n] if hin != NULL), written in dtype.
-// part: rows_split * N floats of scratch.
-hipError_t colsum(int dtype, int rows, int N, const void* y, int ldy, const void* hin,
-                  const float* mu, const float* rstd, void* out, float* part, hipStream_t st);
+// dx = dres + LN backward of (dy + dy2) at xhat = (hin - mu) * rstd, gain g;
+// dy2, dres, g optional.
+hipError_t ln_bwd(int dtype, int rows, int H, const void* dy, const void* dy2, const void* hin,
+                  const float* mu, const float* rstd, const void* g, const void* dres, void* dx,
+                  hipStream_t st);
+// column sums over rows: out[n] = sum_r (y + y2)[r][n] (*xhat[r][n] if hin != NULL), written
+// in dtype; y2 optional, same leading dimension. part: rows_split * N floats of scratch.
+hipError_t colsum(int dtype, int rows, int N, const void* y, const void* y2, int ldy,
+                  const void* hin, const float* mu, const float* rstd, void* out, float* part,
+                  hipStream_t st);
 // number of row splits colsum uses for `rows` rows (part holds splits * N floats)
 int colsum_splits(int rows);
 // out = a + b (+bias[n]) elementwise over [rows][H]

@@ -102,9 +102,11 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(int rows, int H, const T* _
   }
 }
 
-// dx = dres + rstd * (gh - mean(gh) - xhat * mean(gh * xhat)), gh = dy * g
+// dx = dres + rstd * (gh - mean(gh) - xhat * mean(gh * xhat)), gh = (dy + dy2) * g;
+// dy2 and dres optional
 template <typename T, int NC>
 __global__ __launch_bounds__(256) void ln_bwd_kernel(int rows, int H, const T* __restrict__ dy,
+                                                     const T* __restrict__ dy2,
                                                      const T* __restrict__ hin,
                                                      const float* __restrict__ mu,
                                                      const float* __restrict__ rstd,
@@ -124,6 +126,12 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(int rows, int H, const T* _
     if (col < H) {
       float hv[8];
       ld8(dy + base + col, gh[c]);
+      if (dy2) {
+        float d2[8];
+        ld8(dy2 + base + col, d2);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gh[c][e] += d2[e];
+      }
       ld8(hin + base + col, hv);
       if (g) {
         float gg[8];
@@ -146,8 +154,8 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(int rows, int H, const T* _
   for (int c = 0; c < NC; ++c) {
     const int col = (c * 64 + lane) * 8;
     if (col < H) {
-      float o[8], d0[8];
-      ld8(dres + base + col, d0);
+      float o[8], d0[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      if (dres) ld8(dres + base + col, d0);
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = d0[e] + r * (gh[c][e] - mg - xh[c][e] * mgx);
       st8(dx + base + col, o);
@@ -157,7 +165,8 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(int rows, int H, const T* _
 
 template <typename T>
 __global__ __launch_bounds__(256) void colsum_part_kernel(int rows, int N, int rows_per,
-                                                          const T* __restrict__ y, int ldy,
+                                                          const T* __restrict__ y,
+                                                          const T* __restrict__ y2, int ldy,
                                                           const T* __restrict__ hin,
                                                           const float* __restrict__ mu,
                                                           const float* __restrict__ rstd,
@@ -169,6 +178,7 @@ __global__ __launch_bounds__(256) void colsum_part_kernel(int rows, int N, int r
   float acc = 0.f;
   for (int r = r0; r < r1; ++r) {
     float v = ld_f(y + (size_t)r * ldy + n);
+    if (y2) v += ld_f(y2 + (size_t)r * ldy + n);
     if (hin) v *= (ld_f(hin + (size_t)r * N + n) - mu[r]) * rstd[r];
     acc += v;
   }
@@ -258,11 +268,12 @@ hipError_t ln_fwd_t(int rows, int H, const void* x, const void* resid, const voi
 }
 
 template <typename T, int NC>
-hipError_t ln_bwd_t(int rows, int H, const void* dy, const void* hin, const float* mu,
-                    const float* rstd, const void* g, const void* dres, void* dx, hipStream_t st) {
+hipError_t ln_bwd_t(int rows, int H, const void* dy, const void* dy2, const void* hin,
+                    const float* mu, const float* rstd, const void* g, const void* dres, void* dx,
+                    hipStream_t st) {
   dim3 grid((rows + kRowsPerBlock - 1) / kRowsPerBlock);
   hipLaunchKernelGGL((ln_bwd_kernel<T, NC>), grid, dim3(256), 0, st, rows, H, (const T*)dy,
-                     (const T*)hin, mu, rstd, (const T*)g, (const T*)dres, (T*)dx);
+                     (const T*)dy2, (const T*)hin, mu, rstd, (const T*)g, (const T*)dres, (T*)dx);
   return hipGetLastError();
 }
 
@@ -282,11 +293,11 @@ hipError_t ln_fwd_dispatch(int rows, int H, const void* x, const void* resid, co
 }
 
 template <typename T>
-hipError_t ln_bwd_dispatch(int rows, int H, const void* dy, const void* hin, const float* mu,
-                           const float* rstd, const void* g, const void* dres, void* dx,
-                           hipStream_t st) {
+hipError_t ln_bwd_dispatch(int rows, int H, const void* dy, const void* dy2, const void* hin,
+                           const float* mu, const float* rstd, const void* g, const void* dres,
+                           void* dx, hipStream_t st) {
   const int nc = (H + 511) / 512;
-#define MTB_LNB(N) return ln_bwd_t<T, N>(rows, H, dy, hin, mu, rstd, g, dres, dx, st)
+#define MTB_LNB(N) return ln_bwd_t<T, N>(rows, H, dy, dy2, hin, mu, rstd, g, dres, dx, st)
   if (nc <= 1) MTB_LNB(1);
   if (nc <= 2) MTB_LNB(2);
   if (nc <= 4) MTB_LNB(4);
@@ -306,27 +317,32 @@ hipError_t ln_fwd(int dtype, int rows, int H, const void* x, const void* resid, 
   return ln_fwd_dispatch<float>(rows, H, x, resid, bias, g, b, h_out, y, mu, rstd, eps, st);
 }
 
-hipError_t ln_bwd(int dtype, int rows, int H, const void* dy, const void* hin, const float* mu,
-                  const float* rstd, const void* g, const void* dres, void* dx, hipStream_t st) {
-  if (dtype == 1) return ln_bwd_dispatch<bf16_t>(rows, H, dy, hin, mu, rstd, g, dres, dx, st);
-  return ln_bwd_dispatch<float>(rows, H, dy, hin, mu, rstd, g, dres, dx, st);
+hipError_t ln_bwd(int dtype, int rows, int H, const void* dy, const void* dy2, const void* hin,
+                  const float* mu, const float* rstd, const void* g, const void* dres, void* dx,
+                  hipStream_t st) {
+  if (dtype == 1)
+    return ln_bwd_dispatch<bf16_t>(rows, H, dy, dy2, hin, mu, rstd, g, dres, dx, st);
+  return ln_bwd_dispatch<float>(rows, H, dy, dy2, hin, mu, rstd, g, dres, dx, st);
 }
 
 int colsum_splits(int rows) { return rows < 64 ? 1 : (rows + 63) / 64 < 128 ? (rows + 63) / 64 : 128; }
 
-hipError_t colsum(int dtype, int rows, int N, const void* y, int ldy, const void* hin,
-                  const float* mu, const float* rstd, void* out, float* part, hipStream_t st) {
+hipError_t colsum(int dtype, int rows, int N, const void* y, const void* y2, int ldy,
+                  const void* hin, const float* mu, const float* rstd, void* out, float* part,
+                  hipStream_t st) {
   const int splits = colsum_splits(rows);
   const int rows_per = (rows + splits - 1) / splits;
   dim3 g1((N + 255) / 256, splits), g2((N + 255) / 256);
   if (dtype == 1) {
     hipLaunchKernelGGL(colsum_part_kernel<bf16_t>, g1, dim3(256), 0, st, rows, N, rows_per,
-                       (const bf16_t*)y, ldy, (const bf16_t*)hin, mu, rstd, part);
+                       (const bf16_t*)y, (const bf16_t*)y2, ldy, (const bf16_t*)hin, mu, rstd,
+                       part);
     hipLaunchKernelGGL(colsum_fin_kernel<bf16_t>, g2, dim3(256), 0, st, N, splits, part,
                        (bf16_t*)out);
   } else {
     hipLaunchKernelGGL(colsum_part_kernel<float>, g1, dim3(256), 0, st, rows, N, rows_per,
-                       (const float*)y, ldy, (const float*)hin, mu, rstd, part);
+                       (const float*)y, (const float*)y2, ldy, (const float*)hin, mu, rstd,
+                       part);
     hipLaunchKernelGGL(colsum_fin_kernel<float>, g2, dim3(256), 0, st, N, splits, part,
                        (float*)out);
   }

@@ -65,6 +65,7 @@ class BlockConfig:
     affine: bool = False       # LayerNorm gain/shift present
     bias: bool = False         # linear biases present
     ln_eps: float = 1e-5
+    norm: str = "pre"          # "pre" | "post": LayerNorm before each sublayer or after each residual
 
     @property
     def tokens(self) -> int:

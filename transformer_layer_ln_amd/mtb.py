@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(HERE, "libmtb.so")
 MTB_OK, MTB_EINVAL, MTB_EUNSUPPORTED, MTB_EHIP, MTB_ECOMM = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
 ACT_GELU, ACT_SWIGLU = 0, 1
+NORM_PRE, NORM_POST = 0, 1
 OP_SUM, OP_MAX = 0, 1
 PHASE_ALL, PHASE_SEG0, PHASE_SEG1, PHASE_SEG2 = 0, 1, 2, 3
 XENT_ALL, XENT_PARTIAL, XENT_FINISH = 0, 1, 2
@@ -44,7 +45,7 @@ class Cfg(ctypes.Structure):
     _fields_ = [("batch", c_int32), ("seq", c_int32), ("hidden", c_int32),
                 ("q_heads", c_int32), ("kv_heads", c_int32), ("head_dim", c_int32),
                 ("ffn", c_int32), ("act", c_int32), ("causal", c_int32), ("dtype", c_int32),
-                ("ln_eps", c_float)]
+                ("ln_eps", c_float), ("norm", c_int32)]
 
 
 class Weights(ctypes.Structure):
@@ -138,16 +139,16 @@ def _stream(stream=None):
 
 
 def make_cfg(batch, seq, hidden, q_heads, kv_heads, head_dim, ffn, act="gelu", causal=False,
-             dtype="bf16", ln_eps=1e-5) -> Cfg:
+             dtype="bf16", ln_eps=1e-5, norm="pre") -> Cfg:
     return Cfg(batch, seq, hidden, q_heads, kv_heads, head_dim, ffn,
                ACT_GELU if act == "gelu" else ACT_SWIGLU, int(bool(causal)),
-               BF16 if dtype == "bf16" else F32, ln_eps)
+               BF16 if dtype == "bf16" else F32, ln_eps, NORM_POST if norm == "post" else NORM_PRE)
 
 
 def cfg_from(c) -> Cfg:
     """Cfg from an object with the BlockConfig attribute names."""
     return make_cfg(c.batch, c.seq, c.hidden, c.q_heads, c.kv_heads, c.head_dim, c.ffn,
-                    c.act, c.causal, c.dtype, c.ln_eps)
+                    c.act, c.causal, c.dtype, c.ln_eps, getattr(c, "norm", "pre"))
 
 
 def saved_bytes(cfg: Cfg) -> int:
