@@ -18,7 +18,9 @@ against the pages by eye:
 * ``embed``  -- the vocab-parallel input embedding: masked lookup per shard,
   summed over shards, and its adjoint (scatter-add into the shard's rows);
 * ``lmhead`` -- the vocab-parallel output layer feeding ``xent``: logits slice
-  z_r = h W_r^T per shard, and the gradients dW_r and sum_r dz_r W_r.
+  z_r = h W_r^T per shard, and the gradients dW_r and sum_r dz_r W_r;
+* ``dropout`` -- counter-based dropout masks (Philox4x32-10 from its published
+  definition) with the tensor-parallel seed scheme, used by ``block``.
 
 Pages cited (short key -> page):
 

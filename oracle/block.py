@@ -21,6 +21,13 @@ added first and the sum is normalised, as in the original Transformer):
 with the same attention and MLP (and the same reduction points); the
 attention reads x itself and the MLP reads h.
 
+Dropout ([TP-block] sec. 5), optional: on the attention probabilities of each
+local head (inside the TP region: rank r draws with seed + 2718 + r), and on
+the hidden state after the attention block and after the MLP, i.e. on
+sum(partials) + bias before the residual add (outside the TP region: every
+rank draws the same mask from the seed itself). Masks come from the
+counter-based generator in ``dropout``; a kept value is scaled by 1/(1-p).
+
 The backward follows the conjugate placement of the reductions: a
 row-parallel output is summed in the forward and passed through in the
 backward; a column-parallel input is passed through in the forward and its
@@ -41,6 +48,8 @@ import math
 
 import numpy as np
 from scipy.special import erf
+
+from . import dropout as odrop
 
 F64 = np.float64
 
@@ -120,23 +129,26 @@ def attention_probs(qi, kj, causal):
     return p / p.sum(axis=-1, keepdims=True)
 
 
-def attention_fwd(q, k, v, causal):
-    """q [B, nq, S, d]; k, v [B, nkv, S, d]; q head i reads kv head i // g."""
+def attention_fwd(q, k, v, causal, mult=None):
+    """q [B, nq, S, d]; k, v [B, nkv, S, d]; q head i reads kv head i // g.
+    mult [B, nq, S, S] (optional): dropout multipliers applied to P."""
     b_, nq, s, d = q.shape
     g = nq // k.shape[1]
     o = np.empty_like(q)
     for b in range(b_):
         for i in range(nq):
             p = attention_probs(q[b, i], k[b, i // g], causal)
+            if mult is not None:
+                p = p * mult[b, i]
             o[b, i] = p @ v[b, i // g]
     return o
 
 
-def attention_bwd(q, k, v, do, causal):
-    """Gradients of O = P V with P = softmax(Z), Z = Q K^T / sqrt(d):
-    dV += P^T dO, dP = dO V^T, dZ = P o (dP - rowsum(dP o P)),
-    dQ = dZ K / sqrt(d), dK += dZ^T Q / sqrt(d). kv gradients are summed over
-    the q heads that share the kv head."""
+def attention_bwd(q, k, v, do, causal, mult=None):
+    """Gradients of O = P~ V with P~ = P o mult (mult = 1 without dropout),
+    P = softmax(Z), Z = Q K^T / sqrt(d): dV += P~^T dO, dP = (dO V^T) o mult,
+    dZ = P o (dP - rowsum(dP o P)), dQ = dZ K / sqrt(d), dK += dZ^T Q / sqrt(d).
+    kv gradients are summed over the q heads that share the kv head."""
     b_, nq, s, d = q.shape
     g = nq // k.shape[1]
     dq = np.zeros_like(q)
@@ -147,8 +159,11 @@ def attention_bwd(q, k, v, do, causal):
         for i in range(nq):
             j = i // g
             p = attention_probs(q[b, i], k[b, j], causal)
-            dv[b, j] += p.T @ do[b, i]
+            pm = p if mult is None else p * mult[b, i]
+            dv[b, j] += pm.T @ do[b, i]
             dp = do[b, i] @ v[b, j].T
+            if mult is not None:
+                dp = dp * mult[b, i]
             dz = p * (dp - (dp * p).sum(axis=-1, keepdims=True))
             dq[b, i] = dz @ k[b, j] * sc
             dk[b, j] += dz.T @ q[b, i] * sc
@@ -185,7 +200,7 @@ def _lin(x, w, b=None):
 
 
 def block_forward(x, w, *, q_heads, kv_heads, head_dim, act="gelu", causal=False,
-                  eps=1e-5, R=1, norm="pre"):
+                  eps=1e-5, R=1, norm="pre", dropout=None, tp_rank=0):
     """Forward of the unsharded block given as R shards.
 
     x [B, S, H]; w the unsharded weights (keys as in the inputs module:
@@ -194,10 +209,12 @@ def block_forward(x, w, *, q_heads, kv_heads, head_dim, act="gelu", causal=False
     unsharded head counts; each of the R shards takes q_heads/R and
     kv_heads/R whole heads and ffn/R MLP columns. norm = "pre" (LN before
     each sublayer) or "post" (LN after each residual sum). Returns
-    (out, cache)."""
+    (out, cache). dropout: None or dict(p_attn, p_hidden, seed, offset); shard
+    r of the R is tensor-parallel rank tp_rank + r (its attention seed)."""
     if norm not in ("pre", "post"):
         raise ValueError(norm)
     post = norm == "post"
+    dr = dict(p_attn=0.0, p_hidden=0.0, seed=0, offset=0) if dropout is None else dict(dropout)
     x = np.asarray(x, F64)
     w = {k: np.asarray(v, F64) for k, v in w.items()}
     B, S, H = x.shape
@@ -223,16 +240,28 @@ def block_forward(x, w, *, q_heads, kv_heads, head_dim, act="gelu", causal=False
         q = _lin(a, ws["wq"], ws.get("bq")).reshape(B, S, nq, d).transpose(0, 2, 1, 3)
         k = _lin(a, ws["wk"], ws.get("bk")).reshape(B, S, nkv, d).transpose(0, 2, 1, 3)
         v = _lin(a, ws["wv"], ws.get("bv")).reshape(B, S, nkv, d).transpose(0, 2, 1, 3)
-        o = attention_fwd(q, k, v, causal)
+        mult = None
+        if dr["p_attn"] > 0.0:
+            mult = odrop.multiplier((B, nq, S, S), odrop.SITE_ATTN,
+                                    odrop.attn_seed(dr["seed"], tp_rank + r), dr["offset"],
+                                    dr["p_attn"])
+        o = attention_fwd(q, k, v, causal, mult)
         o_tok = o.transpose(0, 2, 1, 3).reshape(T, nq * d)
         p_attn.append(o_tok @ ws["wo"].T)
-        cache["shards"].append({"w": ws, "q": q, "k": k, "v": v, "o": o_tok})
+        cache["shards"].append({"w": ws, "q": q, "k": k, "v": v, "o": o_tok, "mult": mult})
     cache["p_attn"] = p_attn
 
     # reduction point g1 (sum of partials), bias once, (4) residual
     attn = sum(p_attn)
     if "bo" in w:
         attn = attn + w["bo"]
+    # hidden dropout outside the TP region: the same mask on every rank
+    mult_h1 = odrop.multiplier((T, H), odrop.SITE_HIDDEN_ATTN, dr["seed"], dr["offset"],
+                               dr["p_hidden"])
+    mult_h2 = odrop.multiplier((T, H), odrop.SITE_HIDDEN_MLP, dr["seed"], dr["offset"],
+                               dr["p_hidden"])
+    cache.update(mult_h1=mult_h1, mult_h2=mult_h2)
+    attn = attn * mult_h1
     if post:
         # residual first, then the first LayerNorm; the MLP reads its output
         h, xhat1, rstd1 = layer_norm_fwd(x2 + attn, w.get("ln1_g"), w.get("ln1_b"), eps)
@@ -265,6 +294,7 @@ def block_forward(x, w, *, q_heads, kv_heads, head_dim, act="gelu", causal=False
     y = sum(p_mlp)
     if "b2" in w:
         y = y + w["b2"]
+    y = y * mult_h2
     if post:
         out, xhat2, rstd2 = layer_norm_fwd(h + y, w.get("ln2_g"), w.get("ln2_b"), eps)
         cache.update(xhat2=xhat2, rstd2=rstd2)
@@ -295,6 +325,7 @@ def block_backward(G, cache):
         up, dg2, db2n = layer_norm_bwd(G2, cache["xhat2"], cache["rstd2"], w.get("ln2_g"))
     else:
         up = G2
+    upm = up * cache["mult_h2"]     # through the MLP output's dropout
 
     # fc2 (row-parallel): g2's backward passes its upstream gradient unchanged
     # to every shard
@@ -303,8 +334,8 @@ def block_backward(G, cache):
         sh = cache["shards"][r]
         ws = sh["w"]
         g = {}
-        dm = up @ ws["w2"]
-        g["w2"] = up.T @ sh["m"]
+        dm = upm @ ws["w2"]
+        g["w2"] = upm.T @ sh["m"]
         if cache["act"] == "gelu":
             du = dm * gelu_grad(sh["u"])
             g["w1"] = du.T @ cache["c"]
@@ -321,7 +352,7 @@ def block_backward(G, cache):
             dc_parts.append(dug @ ws["wg"] + duu @ ws["wu"])
         sg[r] = g
     if "b2" in w:
-        db2 = up.sum(0)
+        db2 = upm.sum(0)
 
     # column-parallel fc1 input: its gradient is summed over shards (f's backward)
     dc = sum(dc_parts)
@@ -332,6 +363,7 @@ def block_backward(G, cache):
         dh_ln, dg2, db2n = layer_norm_bwd(dc, cache["xhat2"], cache["rstd2"], w.get("ln2_g"))
         dh = G2 + dh_ln
         up_attn = dh
+    upa = up_attn * cache["mult_h1"]  # through the attention output's dropout
 
     # attention: projection (row-parallel), per-head attention, QKV (column-parallel)
     da_parts = []
@@ -340,10 +372,10 @@ def block_backward(G, cache):
         sh = cache["shards"][r]
         ws = sh["w"]
         g = sg[r]
-        do_tok = up_attn @ ws["wo"]
-        g["wo"] = up_attn.T @ sh["o"]
+        do_tok = upa @ ws["wo"]
+        g["wo"] = upa.T @ sh["o"]
         do = do_tok.reshape(B, S, nq, d).transpose(0, 2, 1, 3)
-        dq, dk, dv = attention_bwd(sh["q"], sh["k"], sh["v"], do, cache["causal"])
+        dq, dk, dv = attention_bwd(sh["q"], sh["k"], sh["v"], do, cache["causal"], sh["mult"])
         dq2 = dq.transpose(0, 2, 1, 3).reshape(T, nq * d)
         dk2 = dk.transpose(0, 2, 1, 3).reshape(T, nkv * d)
         dv2 = dv.transpose(0, 2, 1, 3).reshape(T, nkv * d)
@@ -354,7 +386,7 @@ def block_backward(G, cache):
         da_parts.append(dq2 @ ws["wq"] + dk2 @ ws["wk"] + dv2 @ ws["wv"])
         dk_tok.append(dk2)
     if "bo" in w:
-        dbo = up_attn.sum(0)
+        dbo = upa.sum(0)
 
     da = sum(da_parts)
     if post:
