@@ -7,7 +7,7 @@ share (hidden 4096, 4 local heads x 128, ffn chunk 2048, batch 4, causal,
 GELU). Prints ONE JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--workload seq2048|seq512|seq4096|seq4096-causal|seq2048-post]
+                    [--workload seq2048|seq512|seq4096|seq4096-causal|seq2048-post|seq2048-dropout]
     python bench.py --calibrate-copy MIB
     python bench.py --sweep
 
@@ -110,6 +110,10 @@ WORKLOADS = {
     "seq4096-causal": ("C5c", "TP=8 rank share of a hidden-4096 SwiGLU/GQA block: 4 q / 1 kv heads x "
                               "128, ffn chunk 1792 (gate+up 3584), batch 2, seq 4096, causal",
                        "one tp8 rank share"),
+    "seq2048-dropout": ("C4d", "TP=8 rank share of a hidden-4096 block: 4 local heads x 128, ffn chunk "
+                               "2048, batch 4, seq 2048, causal, GELU, dropout 0.1 on the attention "
+                               "probabilities and on the hidden state (counter-based masks)",
+                        "one tp8 rank share"),
     "seq2048-post": ("C4p", "TP=8 rank share of a hidden-4096 block in post-LN order: 4 local heads "
                             "x 128, ffn chunk 2048, batch 4, seq 2048, causal, GELU",
                      "one tp8 rank share"),
@@ -123,6 +127,9 @@ def workload_cfg(key):
         return inputs.C5.with_(name="C5-tp8-s4096-swiglu-gqa-causal", causal=True)
     if key == "C4p":
         return inputs.C4.with_(name="C4-tp8-s2048-post-ln", norm="post")
+    if key == "C4d":
+        return inputs.C4.with_(name="C4-tp8-s2048-dropout", p_attn=0.1, p_hidden=0.1,
+                               drop_seed=1234, drop_offset=0)
     return inputs.CONFIGS[key]
 
 
@@ -368,7 +375,10 @@ def cpu_baseline(cfg, budget_s=20.0):
     a = inputs.activations(sample)
     w = inputs.shard_weights(sample, 0)
     kw = dict(q_heads=sample.q_heads, kv_heads=sample.kv_heads, head_dim=sample.head_dim,
-              act=sample.act, causal=sample.causal)
+              act=sample.act, causal=sample.causal, norm=sample.norm)
+    if sample.p_attn or sample.p_hidden:
+        kw["dropout"] = dict(p_attn=sample.p_attn, p_hidden=sample.p_hidden,
+                             seed=sample.drop_seed, offset=sample.drop_offset)
     times = []
     t_start = time.perf_counter()
     while True:

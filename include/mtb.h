@@ -74,6 +74,26 @@ typedef int32_t mtb_status;
 #define MTB_NORM_PRE 0
 #define MTB_NORM_POST 1
 
+/* Dropout ([TP-block] sec. 5). Inside the tensor-parallel region (the
+ * attention probabilities of the local heads) every rank needs its own mask
+ * stream: seed + MTB_TP_SEED_OFFSET + tp_rank. Outside it (the hidden state
+ * after the attention block and after the MLP, replicated on every rank) all
+ * ranks must draw the same mask: the seed itself. The mask is counter-based,
+ * a pure function of (stream, site, element, rng_offset), so the backward
+ * regenerates the forward's mask and a recomputation reproduces it:
+ *   word = Philox4x32-10 (Salmon et al., SC 2011) with counter
+ *          (i / 4 low 32 bits, i / 4 high 32 bits, site, rng_offset) and key
+ *          (stream low 32 bits, stream high 32 bits), output word i % 4;
+ *   dropped iff word < floor(p * 2^32) (p the float in mtb_cfg); a kept value
+ *   is scaled by 1 / (1 - p).
+ * Element index i: attention ((b * q_heads + h) * seq + query) * seq + key
+ * over the LOCAL heads; hidden token * hidden + column. The hidden dropout
+ * applies to sum(partials) + bias before the residual add. */
+#define MTB_TP_SEED_OFFSET 2718
+#define MTB_DROP_SITE_ATTN 0
+#define MTB_DROP_SITE_HIDDEN_ATTN 1
+#define MTB_DROP_SITE_HIDDEN_MLP 2
+
 /* reduction ops of the communication hook */
 #define MTB_OP_SUM 0
 #define MTB_OP_MAX 1
@@ -96,7 +116,11 @@ typedef int32_t mtb_status;
  *   head_dim: d;  ffn: local MLP width F;
  *   act: MTB_ACT_*;  causal: 0/1 (key s' > query s masked);
  *   dtype: MTB_F32 / MTB_BF16;  ln_eps: LayerNorm epsilon (e.g. 1e-5);
- *   norm: MTB_NORM_PRE / MTB_NORM_POST.
+ *   norm: MTB_NORM_PRE / MTB_NORM_POST;
+ *   attn_dropout, hidden_dropout: probabilities in [0, 1) (0: off);
+ *   tp_rank: this rank's index in its tensor-parallel group (>= 0);
+ *   rng_offset: counter word 3 of every mask (advance it per layer / step);
+ *   seed: the 64-bit seed shared by the tensor-parallel group.
  * Supported shapes (else MTB_EUNSUPPORTED):
  *   MTB_BF16: head_dim in {64, 128}; seq, hidden, ffn and q_heads*head_dim
  *     multiples of 64 (tokens, hidden and ffn need not be multiples of the
@@ -113,6 +137,10 @@ typedef struct mtb_cfg {
   int32_t dtype;
   float ln_eps;
   int32_t norm;
+  float attn_dropout, hidden_dropout;
+  int32_t tp_rank;
+  uint32_t rng_offset;
+  uint64_t seed;
 } mtb_cfg;
 
 /* Weights of one rank's share, all [out, in] row-major, dtype of the cfg.

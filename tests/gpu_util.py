@@ -46,8 +46,12 @@ def host(t):
 
 
 def oracle_kw(cfg):
-    return dict(q_heads=cfg.q_heads, kv_heads=cfg.kv_heads, head_dim=cfg.head_dim, act=cfg.act,
-                causal=cfg.causal, eps=cfg.ln_eps, norm=cfg.norm)
+    kw = dict(q_heads=cfg.q_heads, kv_heads=cfg.kv_heads, head_dim=cfg.head_dim, act=cfg.act,
+              causal=cfg.causal, eps=cfg.ln_eps, norm=cfg.norm)
+    if cfg.p_attn or cfg.p_hidden:
+        kw["dropout"] = dict(p_attn=cfg.p_attn, p_hidden=cfg.p_hidden, seed=cfg.drop_seed,
+                             offset=cfg.drop_offset)
+    return kw
 
 
 def split_grads(g: dict, cfg) -> dict:
@@ -86,12 +90,12 @@ def split_grads(g: dict, cfg) -> dict:
     return out
 
 
-def run_rank(cfg, w_split, x, G, comm=None):
+def run_rank(cfg, w_split, x, G, comm=None, tp_rank=0):
     """Forward + backward of one rank's share with MTB_PHASE_ALL.
     Returns (out, dx, grads-in-oracle-names) on the host."""
     dev = torch.device("cuda")
     dt = tdtype(cfg)
-    c = mtb.cfg_from(cfg)
+    c = mtb.cfg_from(cfg, tp_rank)
     w = mtb.device_weights(w_split, cfg.act, dt, dev)
     blk = mtb.BlockShard(c, w, dev)
     xd = torch.as_tensor(x).to(dev, dt).contiguous()
@@ -105,13 +109,13 @@ def run_rank(cfg, w_split, x, G, comm=None):
     return host(out), host(dx), split_grads(grads, cfg)
 
 
-def check_rank_vs_oracle(cfg, w_split, x, G, tol=None, comm=None, label=""):
+def check_rank_vs_oracle(cfg, w_split, x, G, tol=None, comm=None, label="", tp_rank=0):
     tol = TOL[cfg.dtype] if tol is None else tol
     say(f"[gpu] {label or cfg.name}: B={cfg.batch} S={cfg.seq} H={cfg.hidden} nq={cfg.q_heads} "
         f"nkv={cfg.kv_heads} d={cfg.head_dim} F={cfg.ffn} act={cfg.act} causal={cfg.causal} "
-        f"dtype={cfg.dtype} norm={cfg.norm}")
-    out, dx, grads = run_rank(cfg, w_split, x, G, comm=comm)
-    ref_out, cache = ob.block_forward(x, w_split, R=1, **oracle_kw(cfg))
+        f"dtype={cfg.dtype} norm={cfg.norm} dropout={cfg.p_attn}/{cfg.p_hidden} rank={tp_rank}")
+    out, dx, grads = run_rank(cfg, w_split, x, G, comm=comm, tp_rank=tp_rank)
+    ref_out, cache = ob.block_forward(x, w_split, R=1, tp_rank=tp_rank, **oracle_kw(cfg))
     ref_dx, ref_g = ob.block_backward(G, cache)
     errs = {"out": rel_err(out, ref_out), "dx": rel_err(dx, ref_dx)}
     for k in w_split:

@@ -49,6 +49,16 @@ def test_size_queries_accept_valid_and_reject_invalid_configs():
     bad = _cfg()
     bad.norm = 2
     assert mtb.saved_bytes(bad) == 0 and "norm" in mtb.last_error()
+    for field, val in (("attn_dropout", 1.0), ("hidden_dropout", -0.1), ("attn_dropout", float("nan"))):
+        bad = _cfg()
+        setattr(bad, field, val)
+        assert mtb.saved_bytes(bad) == 0 and "dropout" in mtb.last_error()
+    bad = _cfg()
+    bad.tp_rank = -1
+    assert mtb.saved_bytes(bad) == 0 and "tp_rank" in mtb.last_error()
+    # hidden dropout needs one more [T, H] buffer for the masked upstream gradient
+    assert mtb.scratch_bytes(_cfg(hidden_dropout=0.1)) > mtb.scratch_bytes(_cfg())
+    assert mtb.scratch_bytes(_cfg(attn_dropout=0.1)) == mtb.scratch_bytes(_cfg())
 
 
 def test_saved_bytes_scale_with_tokens():
@@ -153,8 +163,9 @@ def test_embed_workspace_query():
 
 
 def test_struct_layout_matches_header():
-    # 10 int32 fields + 1 float + 1 int32
-    assert ctypes.sizeof(mtb.Cfg) == 48
+    # 10 int32 + float + int32 + 2 float + int32 + uint32 + uint64
+    assert ctypes.sizeof(mtb.Cfg) == 72
+    assert mtb.Cfg.seed.offset == 64
     assert ctypes.sizeof(mtb.Weights) == 12 * ctypes.sizeof(ctypes.c_void_p)
     assert ctypes.sizeof(mtb.Comm) == 2 * ctypes.sizeof(ctypes.c_void_p)
 

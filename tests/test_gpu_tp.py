@@ -29,14 +29,13 @@ def emulate_tp(cfg):
     dev = torch.device("cuda")
     dt = tdtype(cfg)
     R = cfg.tp
-    c = mtb.cfg_from(cfg)
     a = inputs.activations(cfg)
     x = torch.as_tensor(a["x"]).to(dev, dt).contiguous()
     G = torch.as_tensor(a["g"]).to(dev, dt).contiguous()
     shards = []
     for r in range(R):
         w = mtb.device_weights(inputs.shard_weights(cfg, r), cfg.act, dt, dev)
-        shards.append(mtb.BlockShard(c, w, dev))
+        shards.append(mtb.BlockShard(mtb.cfg_from(cfg, tp_rank=r), w, dev))
     buf = lambda: torch.full_like(x, float("nan"))
     # forward: SEG0 -> sum -> SEG1 -> sum -> SEG2
     p_attn = [buf() for _ in range(R)]
@@ -134,6 +133,16 @@ def test_tp_emulation_post_ln_swiglu_gqa_affine_fp32_and_bf16():
     _check_tp(cfg)
     _check_tp(inputs.C1.with_(name="tp2-fp32-post", q_heads=2, kv_heads=2, ffn=256, tp=2,
                               bias=True, affine=True, norm="post"))
+
+
+def test_tp_emulation_with_dropout():
+    """[TP-block] sec. 5 across shards: each shard's attention masks come
+    from its own rank's stream, the hidden masks (applied after the sums) are
+    shared; the sum over shards must equal the oracle's R-shard block."""
+    drop = dict(p_attn=0.25, p_hidden=0.125, drop_seed=77, drop_offset=1)
+    _check_tp(inputs.C3(128).with_(name="C3-tp4-s128-dropout", **drop))
+    _check_tp(inputs.C1.with_(name="tp2-fp32-dropout-post", q_heads=2, kv_heads=2, ffn=256, tp=2,
+                              bias=True, norm="post", **drop))
 
 
 class _Hook:

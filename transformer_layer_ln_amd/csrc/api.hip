@@ -7,6 +7,7 @@
 // sharding and the reduction points: [TP-block] sec. 1-2 (column-parallel
 // QKV and fc1, row-parallel projection and fc2, two all-reduces forward and
 // two backward); vocab-parallel cross-entropy: [TP-block] sec. 4.
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -45,7 +46,25 @@ struct Dims {
   int act, causal;
   float eps;
   bool post;   // post-LN order
+  // dropout ([TP-block] sec. 5): attention probabilities (this rank's
+  // stream), hidden state after the attention and after the MLP (the stream
+  // every rank shares)
+  Drop dattn, dh1, dh2;
 };
+
+Drop make_drop(float p, uint64_t key, uint32_t site, uint32_t offset) {
+  Drop d;
+  if (p > 0.f) {
+    const double t = floor((double)p * 4294967296.0);
+    d.thr = t >= 4294967295.0 ? 0xffffffffu : (uint32_t)t;
+    d.scale = (float)(1.0 / (1.0 - (double)p));
+  }
+  d.k0 = (uint32_t)key;
+  d.k1 = (uint32_t)(key >> 32);
+  d.site = site;
+  d.offset = offset;
+  return d;
+}
 
 mtb_status check_cfg(const mtb_cfg* c, Dims& d) {
   if (!c) return fail(MTB_EINVAL, "cfg is NULL");
@@ -62,10 +81,18 @@ mtb_status check_cfg(const mtb_cfg* c, Dims& d) {
   if (!(c->ln_eps > 0.f) || c->ln_eps > 1.f) return fail(MTB_EINVAL, "ln_eps must be in (0, 1]");
   if (c->norm != MTB_NORM_PRE && c->norm != MTB_NORM_POST)
     return fail(MTB_EINVAL, "norm must be MTB_NORM_PRE or MTB_NORM_POST");
+  if (!(c->attn_dropout >= 0.f && c->attn_dropout < 1.f) ||
+      !(c->hidden_dropout >= 0.f && c->hidden_dropout < 1.f))
+    return fail(MTB_EINVAL, "dropout probabilities must be in [0, 1)");
+  if (c->tp_rank < 0) return fail(MTB_EINVAL, "tp_rank must be >= 0");
   d.B = c->batch; d.S = c->seq; d.H = c->hidden; d.nq = c->q_heads; d.nkv = c->kv_heads;
   d.d = c->head_dim; d.F = c->ffn; d.act = c->act; d.causal = c->causal; d.dt = c->dtype;
   d.eps = c->ln_eps;
   d.post = c->norm == MTB_NORM_POST;
+  d.dattn = make_drop(c->attn_dropout, c->seed + MTB_TP_SEED_OFFSET + (uint64_t)c->tp_rank,
+                      MTB_DROP_SITE_ATTN, c->rng_offset);
+  d.dh1 = make_drop(c->hidden_dropout, c->seed, MTB_DROP_SITE_HIDDEN_ATTN, c->rng_offset);
+  d.dh2 = make_drop(c->hidden_dropout, c->seed, MTB_DROP_SITE_HIDDEN_MLP, c->rng_offset);
   d.Fu = d.act == MTB_ACT_SWIGLU ? 2 * d.F : d.F;
   d.Nqkv = (d.nq + 2 * d.nkv) * d.d;
   d.T = d.B * d.S;
@@ -120,7 +147,7 @@ Saved saved_layout(const Dims& d) {
 }
 
 struct Scratch {
-  size_t dh, dr, p, du, dm, dO, dOT, Dbuf, dqkv, part, red, ws, total;
+  size_t dh, dr, gm, p, du, dm, dO, dOT, Dbuf, dqkv, part, red, ws, total;
 };
 Scratch scratch_layout(const Dims& d) {
   Scratch s;
@@ -128,6 +155,7 @@ Scratch scratch_layout(const Dims& d) {
   const size_t e = d.es, T = d.T;
   s.dh = o; o += al(T * d.H * e);       // pre: dh, SEG1 -> SEG2; post: dr2, SEG0 -> SEG1
   s.dr = o; o += d.post ? al(T * d.H * e) : 0;   // post: dr1, SEG1 -> SEG2
+  s.gm = o; o += d.dh1.thr ? al(T * d.H * e) : 0;  // hidden dropout: masked upstream gradient
   s.p = o; o += al(T * d.H * e);        // partial sums (p_attn, p_mlp, dc, da)
   s.du = o; o += al(T * d.Fu * e);
   s.dm = o; o += d.dt == MTB_F32 ? al(T * d.F * e) : 0;
@@ -346,13 +374,14 @@ mtb_status mtb_block_fwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
     MTB_HIP(gemm(dt, T, Nq, H, post ? x : a, H, true, w->w_qkv, H, true, e, st));
     // per-head attention over the local heads
     trace_begin(MTB_TRACE_ATTN_FWD, st);
-    MTB_HIP(attn_fwd(dt, (int)d.B, S, (int)d.nq, (int)d.nkv, (int)d.d, d.causal, qkv, qkvT, O, lse, st));
+    MTB_HIP(attn_fwd(dt, (int)d.B, S, (int)d.nq, (int)d.nkv, (int)d.d, d.causal, qkv, qkvT, O, lse, st,
+                     d.dattn));
     trace_end(MTB_TRACE_ATTN_FWD, st);
     // row-parallel projection: a partial sum, reduced at g1
     Epi ep;
     ep.ws = ws;
-    if (fused) {  // identity reduction: fuse (4) residual and the bias
-      ep.out = h; ep.ldo = H; ep.bias = w->b_o; ep.resid = x; ep.ldr = H;
+    if (fused) {  // identity reduction: fuse (4) residual, the bias and the dropout
+      ep.out = h; ep.ldo = H; ep.bias = w->b_o; ep.resid = x; ep.ldr = H; ep.drop = d.dh1;
     } else {
       ep.out = phase == MTB_PHASE_SEG0 ? out : p; ep.ldo = H;
     }
@@ -366,12 +395,12 @@ mtb_status mtb_block_fwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
       if ((s = call_hook(comm, p, d.T * d.H, dt, MTB_OP_SUM, st)) != MTB_OK) return s;
       trace_end(MTB_TRACE_ATTN_SEG, st);
       trace_begin(MTB_TRACE_FFN_SEG, st);
-      MTB_HIP(ln_fwd(dt, T, H, x, p, w->b_o, lnA_g, lnA_b, h, c, muA, rsA, d.eps, st));
+      MTB_HIP(ln_fwd(dt, T, H, x, p, w->b_o, lnA_g, lnA_b, h, c, muA, rsA, d.eps, st, d.dh1));
     }
   } else if (phase == MTB_PHASE_SEG1) {
-    // g1 done by the caller: h = x + sum(p_attn) + b_o, then (5) LN2 (pre-LN)
-    // or LN1 (post-LN) of it
-    MTB_HIP(ln_fwd(dt, T, H, x, reduced_in, w->b_o, lnA_g, lnA_b, h, c, muA, rsA, d.eps, st));
+    // g1 done by the caller: h = x + dropout(sum(p_attn) + b_o), then (5) LN2
+    // (pre-LN) or LN1 (post-LN) of it
+    MTB_HIP(ln_fwd(dt, T, H, x, reduced_in, w->b_o, lnA_g, lnA_b, h, c, muA, rsA, d.eps, st, d.dh1));
   }
 
   if (phase == MTB_PHASE_ALL || phase == MTB_PHASE_SEG1) {
@@ -395,6 +424,7 @@ mtb_status mtb_block_fwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
     e.ws = ws;
     if (fused) {
       e.out = post ? r2 : out; e.ldo = H; e.bias = w->b_fc2; e.resid = post ? c : h; e.ldr = H;
+      e.drop = d.dh2;
     } else {
       e.out = phase == MTB_PHASE_SEG1 ? out : p; e.ldo = H;
     }
@@ -408,18 +438,19 @@ mtb_status mtb_block_fwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
     if (fused || phase == MTB_PHASE_SEG1) return MTB_OK;
     if ((s = call_hook(comm, p, d.T * d.H, dt, MTB_OP_SUM, st)) != MTB_OK) return s;
     if (post)
-      MTB_HIP(ln_fwd(dt, T, H, c, p, w->b_fc2, w->ln2_g, w->ln2_b, r2, out, mu2, rs2, d.eps, st));
+      MTB_HIP(ln_fwd(dt, T, H, c, p, w->b_fc2, w->ln2_g, w->ln2_b, r2, out, mu2, rs2, d.eps, st,
+                     d.dh2));
     else
-      MTB_HIP(add3(dt, T, H, h, p, w->b_fc2, out, st));
+      MTB_HIP(add3(dt, T, H, h, p, w->b_fc2, out, st, d.dh2));
     trace_end(MTB_TRACE_FFN_SEG, st);
     return MTB_OK;
   }
   // SEG2: out = h + sum(p_mlp) + b2 (pre-LN), or LN2(c + sum(p_mlp) + b2)
   if (post)
     MTB_HIP(ln_fwd(dt, T, H, c, reduced_in, w->b_fc2, w->ln2_g, w->ln2_b, r2, out, mu2, rs2, d.eps,
-                   st));
+                   st, d.dh2));
   else
-    MTB_HIP(add3(dt, T, H, h, reduced_in, w->b_fc2, out, st));
+    MTB_HIP(add3(dt, T, H, h, reduced_in, w->b_fc2, out, st, d.dh2));
   return MTB_OK;
 }
 
@@ -470,6 +501,7 @@ mtb_status mtb_block_bwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
   const void* c = sv + L.c; const void* u = sv + L.u; const void* m = sv + L.m;
   void* dh = P(scratch, Z.dh); void* p = P(scratch, Z.p); void* du = P(scratch, Z.du);
   void* dr = d.post ? P(scratch, Z.dr) : nullptr;
+  void* gm = d.dh1.thr ? P(scratch, Z.gm) : nullptr;
   void* dm = P(scratch, Z.dm); void* dO = P(scratch, Z.dO); void* dOT = bf ? P(scratch, Z.dOT) : nullptr;
   float* Dbuf = (float*)P(scratch, Z.Dbuf); void* dqkv = P(scratch, Z.dqkv);
   float* part = (float*)P(scratch, Z.part); float* red = (float*)P(scratch, Z.red);
@@ -480,6 +512,8 @@ mtb_status mtb_block_bwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
   // upstream gradient of the MLP branch: dout (pre-LN) or LN2's input
   // gradient dr2 (post-LN, kept in the dh buffer until SEG1)
   const void* G = post ? dh : dout;
+  // the MLP branch's own gradient: G through the dropout of the MLP output
+  const void* Gm = d.dh2.thr ? gm : G;
   if (all) trace_begin(MTB_TRACE_BWD, st);
 
   if (phase == MTB_PHASE_ALL || phase == MTB_PHASE_SEG0) {
@@ -489,26 +523,27 @@ mtb_status mtb_block_bwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
       if (g.ln2_g) MTB_HIP(colsum(dt, T, H, dout, nullptr, H, a, mu2, rs2, g.ln2_g, red, st));
       if (g.ln2_b) MTB_HIP(colsum(dt, T, H, dout, nullptr, H, nullptr, nullptr, nullptr, g.ln2_b, red, st));
     }
+    if (d.dh2.thr) MTB_HIP(drop_apply(dt, (size_t)d.T * d.H, G, gm, d.dh2, st));
     // fc2 backward: dm = G W2 with the activation's derivative fused (bf16)
     if (bf) {
       Epi e;
       e.kind = d.act == MTB_ACT_GELU ? EPI_DGELU : EPI_DSWIGLU;
       e.out = du; e.ldo = Fu; e.aux = u; e.ldaux = Fu; e.ws = ws;
-      MTB_HIP(gemm(dt, T, F, H, G, H, true, w->w_fc2, F, false, e, st));
+      MTB_HIP(gemm(dt, T, F, H, Gm, H, true, w->w_fc2, F, false, e, st));
     } else {
       Epi e;
       e.out = dm; e.ldo = F;
-      MTB_HIP(gemm(dt, T, F, H, G, H, true, w->w_fc2, F, false, e, st));
+      MTB_HIP(gemm(dt, T, F, H, Gm, H, true, w->w_fc2, F, false, e, st));
       MTB_HIP(act_bwd(dt, d.act, T, F, dm, u, du, st));
     }
     if (g.w_fc2) {
       Epi e;
       e.out = g.w_fc2; e.ldo = F; e.ws = ws;
       trace_begin(MTB_TRACE_FC2_WGRAD, st);
-      MTB_HIP(gemm(dt, H, F, T, G, H, false, m, F, false, e, st));
+      MTB_HIP(gemm(dt, H, F, T, Gm, H, false, m, F, false, e, st));
       trace_end(MTB_TRACE_FC2_WGRAD, st);
     }
-    if (g.b_fc2) MTB_HIP(colsum(dt, T, H, G, nullptr, H, nullptr, nullptr, nullptr, g.b_fc2, red, st));
+    if (g.b_fc2) MTB_HIP(colsum(dt, T, H, Gm, nullptr, H, nullptr, nullptr, nullptr, g.b_fc2, red, st));
     if (g.w_fc1) {
       Epi e;
       e.out = g.w_fc1; e.ldo = H; e.ws = ws;
@@ -540,6 +575,11 @@ mtb_status mtb_block_bwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
       if (g.ln2_b) MTB_HIP(colsum(dt, T, H, dc, nullptr, H, nullptr, nullptr, nullptr, g.ln2_b, red, st));
       dA = dh;
     }
+    // the attention branch's own gradient: through the attention output's dropout
+    if (d.dh1.thr) {
+      MTB_HIP(drop_apply(dt, (size_t)d.T * d.H, dA, gm, d.dh1, st));
+      dA = gm;
+    }
     // projection backward (row-parallel: g1's backward is the identity)
     {
       Epi e;
@@ -554,7 +594,7 @@ mtb_status mtb_block_bwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
     if (g.b_o) MTB_HIP(colsum(dt, T, H, dA, nullptr, H, nullptr, nullptr, nullptr, g.b_o, red, st));
     // attention backward
     MTB_HIP(attn_bwd(dt, (int)d.B, S, (int)d.nq, (int)d.nkv, (int)d.d, d.causal, qkv, qkvT, O, dO,
-                     dOT, lse, Dbuf, dqkv, part, st));
+                     dOT, lse, Dbuf, dqkv, part, st, d.dattn));
     if (g.w_qkv) {
       Epi e;
       e.out = g.w_qkv; e.ldo = H; e.ws = ws;

@@ -21,12 +21,19 @@
 //    and dK^T += Q^T dS^T from registers; with GQA the q-head contributions
 //    of a kv head are summed by a second pass. dQ: S^T layout, dQ^T += K^T dS^T.
 //    No atomics: every output element has exactly one writer.
+//  * dropout on the probabilities ([TP-block] sec. 5, inside the TP region):
+//    element (batch b, local q head h, query q, key k) has flat index
+//    ((b * nq + h) * S + q) * S + k; the forward scales P by the mask after
+//    the row sums are taken (the normaliser sees every key), and the
+//    backward uses the mask on P for dV and on dP = dO V^T for dS. D =
+//    rowsum(dO o O) is unchanged.
 // Layout inputs: qkv [T][Nqkv] token-major and its per-batch transpose
 // qkvT [B][Nqkv][S]; dO [T][nq*d] and dOT [B][nq*d][S]. In the transposed
 // copies the tokens of every 16 are stored in the order 0-3, 8-11, 4-7, 12-15,
 // so that an MFMA k-step's 16 keys -- the lane group g holds keys 4g..4g+3 and
 // 8+4g..8+4g+3 of its accumulator layout -- are one 16-byte chunk.
 #include "common.h"
+#include "drop.h"
 #include "kernels.h"
 
 namespace mtb {
@@ -104,12 +111,13 @@ MTB_DEV void pack_half(const float (&a)[16], bf16x8& p0, bf16x8& p1) {
 // Forward. Workgroup = 64 queries of one (batch, q head); wavefront w takes
 // query half w & 1 and key half w >> 1 of every 64-key tile, keeps its own
 // online-softmax state, and the two key halves are merged at the end.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(int S, int nq, int nkv, int ldq,
                                                           const bf16_t* __restrict__ qkv,
                                                           const bf16_t* __restrict__ qkvT,
                                                           bf16_t* __restrict__ O,
-                                                          float* __restrict__ lse, float sl2) {
+                                                          float* __restrict__ lse, float sl2,
+                                                          Drop drop) {
   __shared__ __attribute__((aligned(1024))) bf16_t smem[4 * 64 * D];  // 2 stages of K, V^T
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lg = lane >> 5;
@@ -201,6 +209,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(int S, int nq, int nkv
       }
       l_i = l_i * alpha + ls;
       m_i = mnew;
+      if constexpr (DROP) {
+        const uint64_t row = ((uint64_t)bh * S + qi) * S;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float km[4];
+          drop_mul4(drop, (row + ks + 8 * i + 4 * lg) >> 2, km);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) s[4 * i + r] *= km[r];
+        }
+      }
       if (__any(alpha != 1.0f)) {
 #pragma unroll
         for (int i = 0; i < D / 32; ++i)
@@ -289,13 +307,13 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(int rows, int S, int 
 // The Q, dO, Q^T, dO^T tiles and the tile's log-sum-exp and D values are
 // copied global -> LDS directly, double-buffered: tile t+1 streams in while
 // tile t is used.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(
     int S, int nq, int nkv, int ldq, const bf16_t* __restrict__ qkv,
     const bf16_t* __restrict__ qkvT, const bf16_t* __restrict__ dO,
     const bf16_t* __restrict__ dOT, const float* __restrict__ lse,
     const float* __restrict__ Dbuf, bf16_t* __restrict__ dqkv, float* __restrict__ part, float sl2,
-    float scale) {
+    float scale, Drop drop) {
   constexpr int TILE = 64 * D;              // elements of one 64 x D (or D x 64) tile
   constexpr int STAGE = 4 * TILE + 512;  // Q, dO, Q^T, dO^T, then lse and D (64 floats each), 1-KB aligned
   __shared__ __attribute__((aligned(1024))) bf16_t smem[2 * STAGE];
@@ -401,6 +419,25 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(
       }
       // element j: query qw0 + 8(j>>2) + 4lg + (j&3), key `key`
       float p[16], ds[16];
+      // dropout keep bits: one generator call covers 4 keys of one query, and
+      // the 4 lanes of an aligned key group hold the same 4 queries, so lane
+      // c of the group draws for query c and the group shares the 16 bits
+      // (bit 4r + c' = keep(query r, key c'))
+      uint32_t kbits[4];
+      if constexpr (DROP) {
+        const int c = lane & 3;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int qq = qt0 + qh * 32 + 8 * i + 4 * lg + c;
+          const u32x4 w = drop_words(drop, (((uint64_t)bh * S + qq) * S + (key & ~3)) >> 2);
+          uint32_t v = (uint32_t)(w[0] >= drop.thr) | ((uint32_t)(w[1] >= drop.thr) << 1) |
+                       ((uint32_t)(w[2] >= drop.thr) << 2) | ((uint32_t)(w[3] >= drop.thr) << 3);
+          v <<= 4 * c;
+          v |= (uint32_t)__shfl_xor((int)v, 1, 64);
+          v |= (uint32_t)__shfl_xor((int)v, 2, 64);
+          kbits[i] = v;
+        }
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int ql = qh * 32 + 8 * i + 4 * lg;
@@ -411,8 +448,14 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(
           const int j = 4 * i + r;
           float pv = exp2_fast(fmaf(s[j], sl2, -(L4[r] * kLog2e)));
           if (CAUSAL && key > qt0 + ql + r) pv = 0.f;
-          p[j] = pv;
-          ds[j] = pv * (dp[j] - D4[r]);
+          if constexpr (DROP) {
+            const float km = (kbits[i] >> (4 * r + (lane & 3))) & 1u ? drop.scale : 0.f;
+            p[j] = pv * km;
+            ds[j] = pv * (dp[j] * km - D4[r]);
+          } else {
+            p[j] = pv;
+            ds[j] = pv * (dp[j] - D4[r]);
+          }
         }
       }
       bf16x8 p0, p1, d0, d1;
@@ -503,12 +546,12 @@ __global__ __launch_bounds__(256) void attn_dkv_reduce_kernel(int B, int S, int 
 // copied global -> LDS directly into one buffer: two workgroups share a CU
 // and cover each other's loads (measured faster than double-buffering at one
 // workgroup per CU).
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     int S, int nq, int nkv, int ldq, const bf16_t* __restrict__ qkv,
     const bf16_t* __restrict__ qkvT, const bf16_t* __restrict__ dO,
     const float* __restrict__ lse, const float* __restrict__ Dbuf, bf16_t* __restrict__ dqkv,
-    float sl2, float scale) {
+    float sl2, float scale, Drop drop) {
   constexpr int TILE = 64 * D;
   constexpr int STAGE = 3 * TILE;  // K, V, K^T
   __shared__ __attribute__((aligned(1024))) bf16_t smem[STAGE];
@@ -573,6 +616,16 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
       // element j: key ks + 8(j>>2) + 4lg + (j&3), query qi
       float ds[16];
       const bool diag = CAUSAL && ks + 31 > q0;
+      if constexpr (DROP) {
+        const uint64_t row = ((uint64_t)bh * S + qi) * S;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float km[4];
+          drop_mul4(drop, (row + ks + 8 * i + 4 * lg) >> 2, km);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dp[4 * i + r] *= km[r];
+        }
+      }
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         float pv = exp2_fast(fmaf(s[j], sl2, -Lq));
@@ -622,7 +675,8 @@ __global__ __launch_bounds__(128) void attn_fwd_f32_kernel(int B, int S, int nq,
                                                            int causal,
                                                            const float* __restrict__ qkv,
                                                            float* __restrict__ O,
-                                                           float* __restrict__ lse, float scale) {
+                                                           float* __restrict__ lse, float scale,
+                                                           Drop drop) {
   const int gid = blockIdx.x * 128 + threadIdx.x;
   if (gid >= B * nq * S) return;
   const int s = gid % S, hq = (gid / S) % nq, b = gid / (S * nq);
@@ -644,8 +698,9 @@ __global__ __launch_bounds__(128) void attn_fwd_f32_kernel(int B, int S, int nq,
     const float a = (m == kNegInf) ? 0.f : expf(m - mn);
     const float p = expf(z - mn);
     l = l * a + p;
+    const float pk = drop.thr ? p * drop_mul(drop, ((uint64_t)(b * nq + hq) * S + s) * S + t) : p;
 #pragma unroll
-    for (int e = 0; e < D; ++e) o[e] = o[e] * a + p * vr[e];
+    for (int e = 0; e < D; ++e) o[e] = o[e] * a + pk * vr[e];
     m = mn;
   }
   const float inv = 1.0f / l;
@@ -658,7 +713,7 @@ template <int D>
 __global__ __launch_bounds__(128) void attn_bwd_dq_f32_kernel(
     int B, int S, int nq, int nkv, int ldq, int causal, const float* __restrict__ qkv,
     const float* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dbuf,
-    float* __restrict__ dqkv, float scale) {
+    float* __restrict__ dqkv, float scale, Drop drop) {
   const int gid = blockIdx.x * 128 + threadIdx.x;
   if (gid >= B * nq * S) return;
   const int s = gid % S, hq = (gid / S) % nq, b = gid / (S * nq);
@@ -681,6 +736,7 @@ __global__ __launch_bounds__(128) void attn_bwd_dq_f32_kernel(
 #pragma unroll
     for (int e = 0; e < D; ++e) { z = fmaf(q[e], kr[e], z); dpv = fmaf(go[e], vr[e], dpv); }
     const float p = expf(z * scale - L);
+    if (drop.thr) dpv *= drop_mul(drop, ((uint64_t)(b * nq + hq) * S + s) * S + t);
     const float ds = p * (dpv - Dq);
 #pragma unroll
     for (int e = 0; e < D; ++e) dq[e] = fmaf(ds, kr[e], dq[e]);
@@ -693,7 +749,7 @@ template <int D>
 __global__ __launch_bounds__(128) void attn_bwd_dkdv_f32_kernel(
     int B, int S, int nq, int nkv, int ldq, int causal, const float* __restrict__ qkv,
     const float* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dbuf,
-    float* __restrict__ dqkv, float scale) {
+    float* __restrict__ dqkv, float scale, Drop drop) {
   const int gid = blockIdx.x * 128 + threadIdx.x;
   if (gid >= B * nkv * S) return;
   const int t = gid % S, hk = (gid / S) % nkv, b = gid / (S * nkv);
@@ -717,9 +773,11 @@ __global__ __launch_bounds__(128) void attn_bwd_dkdv_f32_kernel(
 #pragma unroll
       for (int e = 0; e < D; ++e) { z = fmaf(qr[e], k[e], z); dpv = fmaf(gr[e], v[e], dpv); }
       const float p = expf(z * scale - lse[((size_t)b * nq + hq) * S + s]);
-      const float ds = p * (dpv - Dbuf[((size_t)b * nq + hq) * S + s]);
+      const float km = drop.thr ? drop_mul(drop, ((uint64_t)(b * nq + hq) * S + s) * S + t) : 1.f;
+      const float ds = p * (dpv * km - Dbuf[((size_t)b * nq + hq) * S + s]);
+      const float pk = p * km;
 #pragma unroll
-      for (int e = 0; e < D; ++e) { dv[e] = fmaf(p, gr[e], dv[e]); dk[e] = fmaf(ds, qr[e], dk[e]); }
+      for (int e = 0; e < D; ++e) { dv[e] = fmaf(pk, gr[e], dv[e]); dk[e] = fmaf(ds, qr[e], dk[e]); }
     }
   }
 #pragma unroll
@@ -731,37 +789,46 @@ __global__ __launch_bounds__(128) void attn_bwd_dkdv_f32_kernel(
 
 template <int D>
 hipError_t attn_fwd_bf16(int B, int S, int nq, int nkv, int causal, const void* qkv,
-                         const void* qkvT, void* O, float* lse, hipStream_t st) {
+                         const void* qkvT, void* O, float* lse, const Drop& drop,
+                         hipStream_t st) {
   const int ldq = (nq + 2 * nkv) * D;
   dim3 grid((S / 64) * B * nq);
   const float sl2 = kLog2e / sqrtf((float)D);
-  if (causal)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, true>), grid, dim3(256), 0, st, S, nq, nkv, ldq,
-                       (const bf16_t*)qkv, (const bf16_t*)qkvT, (bf16_t*)O, lse, sl2);
-  else
-    hipLaunchKernelGGL((attn_fwd_kernel<D, false>), grid, dim3(256), 0, st, S, nq, nkv, ldq,
-                       (const bf16_t*)qkv, (const bf16_t*)qkvT, (bf16_t*)O, lse, sl2);
+#define MTB_FWD(C, DR)                                                                        \
+  hipLaunchKernelGGL((attn_fwd_kernel<D, C, DR>), grid, dim3(256), 0, st, S, nq, nkv, ldq,    \
+                     (const bf16_t*)qkv, (const bf16_t*)qkvT, (bf16_t*)O, lse, sl2, drop)
+  if (causal) {
+    if (drop.thr) MTB_FWD(true, true); else MTB_FWD(true, false);
+  } else {
+    if (drop.thr) MTB_FWD(false, true); else MTB_FWD(false, false);
+  }
+#undef MTB_FWD
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t attn_bwd_bf16(int B, int S, int nq, int nkv, int causal, const void* qkv,
                          const void* qkvT, const void* O, const void* dO, const void* dOT,
-                         const float* lse, float* Dbuf, void* dqkv, float* part, hipStream_t st) {
+                         const float* lse, float* Dbuf, void* dqkv, float* part,
+                         const Drop& drop, hipStream_t st) {
   const int ldq = (nq + 2 * nkv) * D;
   const float sl2 = kLog2e / sqrtf((float)D), scale = 1.0f / sqrtf((float)D);
   const int rows = B * S * nq;
   hipLaunchKernelGGL((attn_bwd_pre_kernel<bf16_t, D>), dim3((rows * (D / 8) + 255) / 256),
                      dim3(256), 0, st, rows, S, nq, (const bf16_t*)O, (const bf16_t*)dO, Dbuf);
   dim3 grid((S / 64) * B * nq);
-#define MTB_BWD(C)                                                                            \
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, C>), grid, dim3(256), 0, st, S, nq, nkv, ldq,  \
-                     (const bf16_t*)qkv, (const bf16_t*)qkvT, (const bf16_t*)dO,             \
-                     (const bf16_t*)dOT, lse, Dbuf, (bf16_t*)dqkv, part, sl2, scale);        \
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<D, C>), grid, dim3(256), 0, st, S, nq, nkv, ldq,    \
+#define MTB_BWD(C, DR)                                                                        \
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, C, DR>), grid, dim3(256), 0, st, S, nq, nkv,   \
+                     ldq, (const bf16_t*)qkv, (const bf16_t*)qkvT, (const bf16_t*)dO,        \
+                     (const bf16_t*)dOT, lse, Dbuf, (bf16_t*)dqkv, part, sl2, scale, drop);  \
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<D, C, DR>), grid, dim3(256), 0, st, S, nq, nkv, ldq,\
                      (const bf16_t*)qkv, (const bf16_t*)qkvT, (const bf16_t*)dO, lse, Dbuf,  \
-                     (bf16_t*)dqkv, sl2, scale)
-  if (causal) { MTB_BWD(true); } else { MTB_BWD(false); }
+                     (bf16_t*)dqkv, sl2, scale, drop)
+  if (causal) {
+    if (drop.thr) { MTB_BWD(true, true); } else { MTB_BWD(true, false); }
+  } else {
+    if (drop.thr) { MTB_BWD(false, true); } else { MTB_BWD(false, false); }
+  }
 #undef MTB_BWD
   if (nq != nkv) {
     const size_t total = (size_t)B * nkv * S * (2 * D / 8);
@@ -773,19 +840,19 @@ hipError_t attn_bwd_bf16(int B, int S, int nq, int nkv, int causal, const void* 
 
 template <int D>
 hipError_t attn_fwd_f32(int B, int S, int nq, int nkv, int causal, const void* qkv, void* O,
-                        float* lse, hipStream_t st) {
+                        float* lse, const Drop& drop, hipStream_t st) {
   const int ldq = (nq + 2 * nkv) * D;
   const int n = B * nq * S;
   hipLaunchKernelGGL((attn_fwd_f32_kernel<D>), dim3((n + 127) / 128), dim3(128), 0, st, B, S, nq,
                      nkv, ldq, causal, (const float*)qkv, (float*)O, lse,
-                     1.0f / sqrtf((float)D));
+                     1.0f / sqrtf((float)D), drop);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t attn_bwd_f32(int B, int S, int nq, int nkv, int causal, const void* qkv, const void* O,
                         const void* dO, const float* lse, float* Dbuf, void* dqkv,
-                        hipStream_t st) {
+                        const Drop& drop, hipStream_t st) {
   const int ldq = (nq + 2 * nkv) * D;
   const int rows = B * S * nq;
   const float scale = 1.0f / sqrtf((float)D);
@@ -794,41 +861,44 @@ hipError_t attn_bwd_f32(int B, int S, int nq, int nkv, int causal, const void* q
   const int nqs = B * nq * S, nks = B * nkv * S;
   hipLaunchKernelGGL((attn_bwd_dq_f32_kernel<D>), dim3((nqs + 127) / 128), dim3(128), 0, st, B, S,
                      nq, nkv, ldq, causal, (const float*)qkv, (const float*)dO, lse, Dbuf,
-                     (float*)dqkv, scale);
+                     (float*)dqkv, scale, drop);
   hipLaunchKernelGGL((attn_bwd_dkdv_f32_kernel<D>), dim3((nks + 127) / 128), dim3(128), 0, st, B,
                      S, nq, nkv, ldq, causal, (const float*)qkv, (const float*)dO, lse, Dbuf,
-                     (float*)dqkv, scale);
+                     (float*)dqkv, scale, drop);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t attn_fwd(int dtype, int B, int S, int nq, int nkv, int d, int causal, const void* qkv,
-                    const void* qkvT, void* O, float* lse, hipStream_t st) {
+                    const void* qkvT, void* O, float* lse, hipStream_t st, const Drop& drop) {
   if (dtype == 1) {
-    if (d == 64) return attn_fwd_bf16<64>(B, S, nq, nkv, causal, qkv, qkvT, O, lse, st);
-    if (d == 128) return attn_fwd_bf16<128>(B, S, nq, nkv, causal, qkv, qkvT, O, lse, st);
+    if (d == 64) return attn_fwd_bf16<64>(B, S, nq, nkv, causal, qkv, qkvT, O, lse, drop, st);
+    if (d == 128) return attn_fwd_bf16<128>(B, S, nq, nkv, causal, qkv, qkvT, O, lse, drop, st);
     return hipErrorInvalidValue;
   }
-  if (d == 32) return attn_fwd_f32<32>(B, S, nq, nkv, causal, qkv, O, lse, st);
-  if (d == 64) return attn_fwd_f32<64>(B, S, nq, nkv, causal, qkv, O, lse, st);
-  if (d == 128) return attn_fwd_f32<128>(B, S, nq, nkv, causal, qkv, O, lse, st);
+  if (d == 32) return attn_fwd_f32<32>(B, S, nq, nkv, causal, qkv, O, lse, drop, st);
+  if (d == 64) return attn_fwd_f32<64>(B, S, nq, nkv, causal, qkv, O, lse, drop, st);
+  if (d == 128) return attn_fwd_f32<128>(B, S, nq, nkv, causal, qkv, O, lse, drop, st);
   return hipErrorInvalidValue;
 }
 
 hipError_t attn_bwd(int dtype, int B, int S, int nq, int nkv, int d, int causal, const void* qkv,
                     const void* qkvT, const void* O, const void* dO, const void* dOT,
-                    const float* lse, float* Dbuf, void* dqkv, float* part, hipStream_t st) {
+                    const float* lse, float* Dbuf, void* dqkv, float* part, hipStream_t st,
+                    const Drop& drop) {
   if (dtype == 1) {
     if (d == 64)
-      return attn_bwd_bf16<64>(B, S, nq, nkv, causal, qkv, qkvT, O, dO, dOT, lse, Dbuf, dqkv, part, st);
+      return attn_bwd_bf16<64>(B, S, nq, nkv, causal, qkv, qkvT, O, dO, dOT, lse, Dbuf, dqkv, part,
+                               drop, st);
     if (d == 128)
-      return attn_bwd_bf16<128>(B, S, nq, nkv, causal, qkv, qkvT, O, dO, dOT, lse, Dbuf, dqkv, part, st);
+      return attn_bwd_bf16<128>(B, S, nq, nkv, causal, qkv, qkvT, O, dO, dOT, lse, Dbuf, dqkv,
+                                part, drop, st);
     return hipErrorInvalidValue;
   }
-  if (d == 32) return attn_bwd_f32<32>(B, S, nq, nkv, causal, qkv, O, dO, lse, Dbuf, dqkv, st);
-  if (d == 64) return attn_bwd_f32<64>(B, S, nq, nkv, causal, qkv, O, dO, lse, Dbuf, dqkv, st);
-  if (d == 128) return attn_bwd_f32<128>(B, S, nq, nkv, causal, qkv, O, dO, lse, Dbuf, dqkv, st);
+  if (d == 32) return attn_bwd_f32<32>(B, S, nq, nkv, causal, qkv, O, dO, lse, Dbuf, dqkv, drop, st);
+  if (d == 64) return attn_bwd_f32<64>(B, S, nq, nkv, causal, qkv, O, dO, lse, Dbuf, dqkv, drop, st);
+  if (d == 128) return attn_bwd_f32<128>(B, S, nq, nkv, causal, qkv, O, dO, lse, Dbuf, dqkv, drop, st);
   return hipErrorInvalidValue;
 }
 

@@ -112,3 +112,24 @@ MTB_DEV float gelu_grad_f(float u) {
   return cdf + u * pdf;
 }
 MTB_DEV float sigmoid_f(float u) { return 1.0f / (1.0f + expf(-u)); }
+
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
+// easy as 1, 2, 3", SC 2011): ten rounds; each multiplies counter words 0 and
+// 2 by fixed constants and feeds the high halves, xor-ed with the key and the
+// other two words, into the next counter; the key advances by two Weyl
+// constants between rounds.
+MTB_DEV u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                            uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
+    const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+    c0 = hi1 ^ c1 ^ k0;
+    c1 = lo1;
+    c2 = hi0 ^ c3 ^ k1;
+    c3 = lo0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return u32x4{c0, c1, c2, c3};
+}

@@ -29,6 +29,8 @@
 //   wgrad     dW = dY^T X       A = dY [T][out], B = X [T][in]      (both transposed)
 #include <type_traits>
 
+#include "drop.h"
+
 #include "common.h"
 #include "kernels.h"
 
@@ -125,12 +127,18 @@ MTB_DEV void ld4g(const void* p, size_t off, float (&v)[4]) {
 
 // fp32 path epilogue (plain store, optional bias and residual) for 4
 // consecutive columns n..n+3 of row m
-MTB_DEV void epi4_f32(const Epi& e, int m, int n, float (&v)[4]) {
+MTB_DEV void epi4_f32(const Epi& e, int m, int n, int N, float (&v)[4]) {
   if (e.bias) {
     float b[4];
     ld4g<float>(e.bias, n, b);
 #pragma unroll
     for (int r = 0; r < 4; ++r) v[r] += b[r];
+  }
+  if (e.drop.thr) {  // dropout of (C + bias) before the residual add
+    float k[4];
+    drop_mul4(e.drop, ((uint64_t)m * N + n) >> 2, k);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] *= k[r];
   }
   if (e.resid) {
     float b[4];
@@ -220,6 +228,7 @@ MTB_DEV void epi_rows(const Epi& e, const Staged<BN>& st, int M, int N, int mc, 
       st.get8(r, nl, v);
       if constexpr (EPI == EPI_STORE) {
         if (e.bias) add8(e.bias, n, v);
+        if (e.drop.thr) drop_apply8(e.drop, (uint64_t)m * N + n, v);
         if (e.resid) add8(e.resid, (size_t)m * e.ldr + n, v);
         out8(e.out, (size_t)m * e.ldo + n, v);
       } else if constexpr (EPI == EPI_GELU) {
@@ -587,7 +596,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(int M, int N, int K,
     const int m = m0 + ty * 4 + i;
     if (m >= M) continue;
     float v[4] = {acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
-    epi4_f32(ep, m, n, v);
+    epi4_f32(ep, m, n, N, v);
   }
 }
 

@@ -6,6 +6,18 @@
 
 namespace mtb {
 
+// Dropout of one site ([TP-block] sec. 5): a counter-based mask, a pure
+// function of (key, site, offset, flat element index i): the 32-bit word
+// i & 3 of Philox4x32-10(counter = (i >> 2 as two 32-bit words, site,
+// offset), key); the element is dropped when that word is below thr, and a
+// kept element is scaled by `scale` = 1 / (1 - p).
+struct Drop {
+  uint32_t thr = 0;          // floor(p * 2^32); 0: no dropout at this site
+  float scale = 1.0f;
+  uint32_t k0 = 0, k1 = 0;   // seed, low and high 32 bits
+  uint32_t site = 0, offset = 0;
+};
+
 // GEMM epilogues. The product is C[m][n] = sum_k A(m,k) B(n,k).
 enum EpiKind {
   EPI_STORE = 0,    // out = C (+bias[n]) (+resid[m][n]); optional per-batch transpose outT
@@ -37,6 +49,8 @@ struct Epi {
   int64_t col0 = 0;                 // EPI_XENT_*: global vocab id of column 0
   const float* rowstat = nullptr;   // EPI_XENT_GRAD: [2][M] (max, sum exp)
   const float* rowscale = nullptr;  // EPI_XENT_GRAD: [M] loss cotangent
+  Drop drop;                   // EPI_STORE: out = resid + dropout(C + bias), element index
+                               // m * N + n (the [T][H] hidden state)
   void* outT = nullptr;        // [M/S][N][S]: per-batch transpose (tokens contiguous, bits 2
                                // and 3 of the token index swapped: see gemm.hip)
   int S = 1;
@@ -57,11 +71,12 @@ size_t gemm_ws_bytes(int dtype, int M, int N, int K, bool a_kc, bool b_kc, int k
 // EPI_XENT_STATS is ceil(N / it)).
 int gemm_tile_n(int M, int N, int K, bool a_kc, bool b_kc, int kind);
 
-// LayerNorm over rows of width H: hsum = x (+resid) (+bias) rounded to dtype;
-// y = (hsum - mu) * rstd (* g + b). h_out (optional) receives hsum.
+// LayerNorm over rows of width H: hsum = x + dropout((resid) (+bias)) rounded
+// to dtype (element index row * H + col); y = (hsum - mu) * rstd (* g + b).
+// h_out (optional) receives hsum.
 hipError_t ln_fwd(int dtype, int rows, int H, const void* x, const void* resid, const void* bias,
                   const void* g, const void* b, void* h_out, void* y, float* mu, float* rstd,
-                  float eps, hipStream_t st);
+                  float eps, hipStream_t st, const Drop& drop = Drop());
 // dx = dres + LN backward of (dy + dy2) at xhat = (hin - mu) * rstd, gain g;
 // dy2, dres, g optional.
 hipError_t ln_bwd(int dtype, int rows, int H, const void* dy, const void* dy2, const void* hin,
@@ -74,9 +89,12 @@ hipError_t colsum(int dtype, int rows, int N, const void* y, const void* y2, int
                   hipStream_t st);
 // number of row splits colsum uses for `rows` rows (part holds splits * N floats)
 int colsum_splits(int rows);
-// out = a + b (+bias[n]) elementwise over [rows][H]
+// out = a + dropout(b (+bias[n])) elementwise over [rows][H]
 hipError_t add3(int dtype, int rows, int H, const void* a, const void* b, const void* bias,
-                void* out, hipStream_t st);
+                void* out, hipStream_t st, const Drop& drop = Drop());
+// out = in * dropout multiplier over n elements (n % 8 == 0; element index from 0)
+hipError_t drop_apply(int dtype, size_t n, const void* in, void* out, const Drop& drop,
+                      hipStream_t st);
 // activation forward / backward as separate passes (fp32 path)
 hipError_t act_fwd(int dtype, int act, int rows, int F, const void* u, void* m, hipStream_t st);
 hipError_t act_bwd(int dtype, int act, int rows, int F, const void* dm, const void* u, void* du,
@@ -86,12 +104,14 @@ hipError_t act_bwd(int dtype, int act, int rows, int F, const void* dm, const vo
 // qkvT [B][Nqkv][S] (bf16 path only; tokens in the within-16 order the GEMM
 // epilogue writes); O [T][nq*d]; lse [B][nq][S] (natural log).
 hipError_t attn_fwd(int dtype, int B, int S, int nq, int nkv, int d, int causal, const void* qkv,
-                    const void* qkvT, void* O, float* lse, hipStream_t st);
+                    const void* qkvT, void* O, float* lse, hipStream_t st,
+                    const Drop& drop = Drop());
 // dO [T][nq*d], dOT [B][nq*d][S] (bf16 only); Dbuf [B][nq][S] fp32 scratch;
 // dqkv [T][Nqkv] output; part: fp32 scratch of B*nq*S*2*d floats (GQA, bf16).
 hipError_t attn_bwd(int dtype, int B, int S, int nq, int nkv, int d, int causal, const void* qkv,
                     const void* qkvT, const void* O, const void* dO, const void* dOT,
-                    const float* lse, float* Dbuf, void* dqkv, float* part, hipStream_t st);
+                    const float* lse, float* Dbuf, void* dqkv, float* part, hipStream_t st,
+                    const Drop& drop = Drop());
 
 // Vocab-sharded cross-entropy.
 hipError_t xent_partial(int dtype, int64_t n, int64_t v, int64_t v0, const void* z,

@@ -7,6 +7,7 @@
 // dimension: per-token mean and biased variance, (x - mean) / sqrt(var + eps),
 // optional gain/shift.
 #include "common.h"
+#include "drop.h"
 #include "kernels.h"
 
 namespace mtb {
@@ -22,7 +23,8 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(int rows, int H, const T* _
                                                      const T* __restrict__ g,
                                                      const T* __restrict__ b, T* __restrict__ h_out,
                                                      T* __restrict__ y, float* __restrict__ mu_out,
-                                                     float* __restrict__ rstd_out, float eps) {
+                                                     float* __restrict__ rstd_out, float eps,
+                                                     Drop drop) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   if (row >= rows) return;
@@ -34,19 +36,19 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(int rows, int H, const T* _
     const int col = (c * 64 + lane) * 8;
     if (col < H) {
       ld8(x + base + col, v[c]);
-      if (resid) {
-        float r[8];
-        ld8(resid + base + col, r);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[c][e] += r[e];
-      }
-      if (bias) {
-        float r[8];
-        ld8(bias + col, r);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[c][e] += r[e];
-      }
       if (resid || bias) {
+        // x + dropout(resid + bias)
+        float r[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (resid) ld8(resid + base + col, r);
+        if (bias) {
+          float bb[8];
+          ld8(bias + col, bb);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) r[e] += bb[e];
+        }
+        if (drop.thr) drop_apply8(drop, (uint64_t)base + col, r);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[c][e] += r[e];
         // the stored residual stream and the statistics see the same values
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -200,7 +202,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void add3_kernel(size_t total8, int H, const T* __restrict__ a,
                                                    const T* __restrict__ b,
                                                    const T* __restrict__ bias,
-                                                   T* __restrict__ out) {
+                                                   T* __restrict__ out, Drop drop) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= total8) return;
   const size_t e0 = i * 8;
@@ -213,9 +215,22 @@ __global__ __launch_bounds__(256) void add3_kernel(size_t total8, int H, const T
 #pragma unroll
     for (int e = 0; e < 8; ++e) vb[e] += vc[e];
   }
+  if (drop.thr) drop_apply8(drop, e0, vb);
 #pragma unroll
   for (int e = 0; e < 8; ++e) va[e] += vb[e];
   st8(out + e0, va);
+}
+
+// out = in * dropout multiplier, element by element (8 per thread)
+template <typename T>
+__global__ __launch_bounds__(256) void drop_apply_kernel(size_t total8, const T* __restrict__ in,
+                                                         T* __restrict__ out, Drop drop) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total8) return;
+  float v[8];
+  ld8(in + i * 8, v);
+  drop_apply8(drop, i * 8, v);
+  st8(out + i * 8, v);
 }
 
 // GELU: u [rows][F] -> m. SwiGLU: u [rows][2F] (gate/up interleaved by 16) -> m [rows][F].
@@ -259,11 +274,11 @@ __global__ __launch_bounds__(256) void act_bwd_kernel(int act, size_t total, int
 template <typename T, int NC>
 hipError_t ln_fwd_t(int rows, int H, const void* x, const void* resid, const void* bias,
                     const void* g, const void* b, void* h_out, void* y, float* mu, float* rstd,
-                    float eps, hipStream_t st) {
+                    float eps, const Drop& drop, hipStream_t st) {
   dim3 grid((rows + kRowsPerBlock - 1) / kRowsPerBlock);
   hipLaunchKernelGGL((ln_fwd_kernel<T, NC>), grid, dim3(256), 0, st, rows, H, (const T*)x,
                      (const T*)resid, (const T*)bias, (const T*)g, (const T*)b, (T*)h_out, (T*)y,
-                     mu, rstd, eps);
+                     mu, rstd, eps, drop);
   return hipGetLastError();
 }
 
@@ -280,9 +295,10 @@ hipError_t ln_bwd_t(int rows, int H, const void* dy, const void* dy2, const void
 template <typename T>
 hipError_t ln_fwd_dispatch(int rows, int H, const void* x, const void* resid, const void* bias,
                            const void* g, const void* b, void* h_out, void* y, float* mu,
-                           float* rstd, float eps, hipStream_t st) {
+                           float* rstd, float eps, const Drop& drop, hipStream_t st) {
   const int nc = (H + 511) / 512;
-#define MTB_LNF(N) return ln_fwd_t<T, N>(rows, H, x, resid, bias, g, b, h_out, y, mu, rstd, eps, st)
+#define MTB_LNF(N) \
+  return ln_fwd_t<T, N>(rows, H, x, resid, bias, g, b, h_out, y, mu, rstd, eps, drop, st)
   if (nc <= 1) MTB_LNF(1);
   if (nc <= 2) MTB_LNF(2);
   if (nc <= 4) MTB_LNF(4);
@@ -311,10 +327,11 @@ hipError_t ln_bwd_dispatch(int rows, int H, const void* dy, const void* dy2, con
 
 hipError_t ln_fwd(int dtype, int rows, int H, const void* x, const void* resid, const void* bias,
                   const void* g, const void* b, void* h_out, void* y, float* mu, float* rstd,
-                  float eps, hipStream_t st) {
+                  float eps, hipStream_t st, const Drop& drop) {
   if (dtype == 1)
-    return ln_fwd_dispatch<bf16_t>(rows, H, x, resid, bias, g, b, h_out, y, mu, rstd, eps, st);
-  return ln_fwd_dispatch<float>(rows, H, x, resid, bias, g, b, h_out, y, mu, rstd, eps, st);
+    return ln_fwd_dispatch<bf16_t>(rows, H, x, resid, bias, g, b, h_out, y, mu, rstd, eps, drop,
+                                   st);
+  return ln_fwd_dispatch<float>(rows, H, x, resid, bias, g, b, h_out, y, mu, rstd, eps, drop, st);
 }
 
 hipError_t ln_bwd(int dtype, int rows, int H, const void* dy, const void* dy2, const void* hin,
@@ -350,15 +367,28 @@ hipError_t colsum(int dtype, int rows, int N, const void* y, const void* y2, int
 }
 
 hipError_t add3(int dtype, int rows, int H, const void* a, const void* b, const void* bias,
-                void* out, hipStream_t st) {
+                void* out, hipStream_t st, const Drop& drop) {
   const size_t total8 = (size_t)rows * H / 8;
   dim3 grid((unsigned)((total8 + 255) / 256));
   if (dtype == 1)
     hipLaunchKernelGGL(add3_kernel<bf16_t>, grid, dim3(256), 0, st, total8, H, (const bf16_t*)a,
-                       (const bf16_t*)b, (const bf16_t*)bias, (bf16_t*)out);
+                       (const bf16_t*)b, (const bf16_t*)bias, (bf16_t*)out, drop);
   else
     hipLaunchKernelGGL(add3_kernel<float>, grid, dim3(256), 0, st, total8, H, (const float*)a,
-                       (const float*)b, (const float*)bias, (float*)out);
+                       (const float*)b, (const float*)bias, (float*)out, drop);
+  return hipGetLastError();
+}
+
+hipError_t drop_apply(int dtype, size_t n, const void* in, void* out, const Drop& drop,
+                      hipStream_t st) {
+  const size_t total8 = n / 8;
+  dim3 grid((unsigned)((total8 + 255) / 256));
+  if (dtype == 1)
+    hipLaunchKernelGGL(drop_apply_kernel<bf16_t>, grid, dim3(256), 0, st, total8,
+                       (const bf16_t*)in, (bf16_t*)out, drop);
+  else
+    hipLaunchKernelGGL(drop_apply_kernel<float>, grid, dim3(256), 0, st, total8, (const float*)in,
+                       (float*)out, drop);
   return hipGetLastError();
 }
 

@@ -145,23 +145,33 @@ __global__ __launch_bounds__(256) void xent_finish_kernel(int64_t n, int64_t v, 
 }
 
 // per token: merge the (max, sum exp, target logit) of the logits' column
-// tiles [n][tiles][3] into stats [3][n] (+ the max into mloc if given)
+// tiles [n][tiles][3] into stats [3][n] (+ the max into mloc if given); one
+// wavefront per token, lanes over the tiles, then a butterfly merge
 __global__ __launch_bounds__(256) void lmhead_combine_kernel(int64_t n, int tiles,
                                                              const float* __restrict__ parts,
                                                              float* __restrict__ stats,
                                                              float* __restrict__ mloc) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   if (i >= n) return;
   const float* p = parts + (size_t)i * tiles * 3;
   float m = kNegInf, s = 0.f, t = 0.f;
-  for (int k = 0; k < tiles; ++k) {
+  for (int k = lane; k < tiles; k += 64) {
     ms_merge(m, s, p[3 * k], p[3 * k + 1]);
     t += p[3 * k + 2];
   }
-  stats[i] = m;
-  stats[n + i] = s;
-  stats[2 * n + i] = t;
-  if (mloc) mloc[i] = m;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
+    ms_merge(m, s, m2, s2);
+    t += __shfl_xor(t, o, 64);
+  }
+  if (lane == 0) {
+    stats[i] = m;
+    stats[n + i] = s;
+    stats[2 * n + i] = t;
+    if (mloc) mloc[i] = m;
+  }
 }
 
 template <typename T>
@@ -198,7 +208,7 @@ hipError_t xent_partial(int dtype, int64_t n, int64_t v, int64_t v0, const void*
 
 hipError_t lmhead_combine(int64_t n, int tiles, const float* parts, float* stats, float* mloc,
                           hipStream_t st) {
-  hipLaunchKernelGGL(lmhead_combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, n,
+  hipLaunchKernelGGL(lmhead_combine_kernel, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, st, n,
                      tiles, parts, stats, mloc);
   return hipGetLastError();
 }

@@ -66,6 +66,10 @@ class BlockConfig:
     bias: bool = False         # linear biases present
     ln_eps: float = 1e-5
     norm: str = "pre"          # "pre" | "post": LayerNorm before each sublayer or after each residual
+    p_attn: float = 0.0        # dropout on the attention probabilities
+    p_hidden: float = 0.0      # dropout on the hidden state after attention and after the MLP
+    drop_seed: int = 0
+    drop_offset: int = 0
 
     @property
     def tokens(self) -> int:

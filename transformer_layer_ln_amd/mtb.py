@@ -45,7 +45,9 @@ class Cfg(ctypes.Structure):
     _fields_ = [("batch", c_int32), ("seq", c_int32), ("hidden", c_int32),
                 ("q_heads", c_int32), ("kv_heads", c_int32), ("head_dim", c_int32),
                 ("ffn", c_int32), ("act", c_int32), ("causal", c_int32), ("dtype", c_int32),
-                ("ln_eps", c_float), ("norm", c_int32)]
+                ("ln_eps", c_float), ("norm", c_int32), ("attn_dropout", c_float),
+                ("hidden_dropout", c_float), ("tp_rank", c_int32), ("rng_offset", ctypes.c_uint32),
+                ("seed", ctypes.c_uint64)]
 
 
 class Weights(ctypes.Structure):
@@ -139,16 +141,21 @@ def _stream(stream=None):
 
 
 def make_cfg(batch, seq, hidden, q_heads, kv_heads, head_dim, ffn, act="gelu", causal=False,
-             dtype="bf16", ln_eps=1e-5, norm="pre") -> Cfg:
+             dtype="bf16", ln_eps=1e-5, norm="pre", attn_dropout=0.0, hidden_dropout=0.0,
+             tp_rank=0, rng_offset=0, seed=0) -> Cfg:
     return Cfg(batch, seq, hidden, q_heads, kv_heads, head_dim, ffn,
                ACT_GELU if act == "gelu" else ACT_SWIGLU, int(bool(causal)),
-               BF16 if dtype == "bf16" else F32, ln_eps, NORM_POST if norm == "post" else NORM_PRE)
+               BF16 if dtype == "bf16" else F32, ln_eps, NORM_POST if norm == "post" else NORM_PRE,
+               attn_dropout, hidden_dropout, tp_rank, rng_offset, seed)
 
 
-def cfg_from(c) -> Cfg:
-    """Cfg from an object with the BlockConfig attribute names."""
+def cfg_from(c, tp_rank=0) -> Cfg:
+    """Cfg from an object with the BlockConfig attribute names (tp_rank: the
+    rank whose share this is, for the attention dropout stream)."""
     return make_cfg(c.batch, c.seq, c.hidden, c.q_heads, c.kv_heads, c.head_dim, c.ffn,
-                    c.act, c.causal, c.dtype, c.ln_eps, getattr(c, "norm", "pre"))
+                    c.act, c.causal, c.dtype, c.ln_eps, getattr(c, "norm", "pre"),
+                    getattr(c, "p_attn", 0.0), getattr(c, "p_hidden", 0.0), tp_rank,
+                    getattr(c, "drop_offset", 0), getattr(c, "drop_seed", 0))
 
 
 def saved_bytes(cfg: Cfg) -> int:
