@@ -3,12 +3,13 @@
 // bf16 path: gfx950 MFMA v_mfma_f32_32x32x16_bf16, a grid of 2x2, 2x4 or
 // 4x2 wavefronts per block, block tile BM x BN x 64, LDS double-buffered (one barrier per
 // k-step: the next tile is fetched into registers while the current one is
-// multiplied, then written to the other LDS buffer). Both operands sit in LDS
-// as [row][k] with k contiguous and 16-byte chunks XOR-swizzled by row, so a
+// multiplied, then written to the other LDS buffer). A k-contiguous operand
+// sits in LDS as [row][k] with 16-byte chunks XOR-swizzled by row, so a
 // fragment is one ds_read_b128 per lane. An operand whose contraction index
-// is not the contiguous one (dgrad's weight, both wgrad operands) is
-// transposed in registers on its way to LDS: a thread reads four k-rows of
-// eight contiguous elements and writes eight rows of four k-values.
+// is not the contiguous one (dgrad's weight, both wgrad operands) is copied
+// as it is, [k][row], and its fragments come from two LDS transpose reads
+// (ds_read_b64_tr_b16) per lane: no register transposes (measured 6 % faster
+// on the weight gradients than transposing in registers on the way to LDS).
 //
 // The MFMA is issued as (B-fragment, A-fragment), i.e. it computes C^T, so
 // that each lane ends up holding 4 consecutive n of one row m.
@@ -71,54 +72,60 @@ struct TileKc {
   }
 };
 
-// operand tile ROWS x BK from a matrix stored [K][rows] (rows contiguous):
-// 4 (k) x 8 (rows) register blocks, transposed on the way to LDS
+// operand tile ROWS x BK from a matrix stored [K][rows] (rows contiguous),
+// kept in that layout in LDS: [BK][ROWS], 16-byte chunks of a k row permuted
+// by chunk ^ 4 (k mod 4). The MFMA fragments are read with the LDS transpose
+// read (64 bits per lane: within each 16-lane group, lane i receives element
+// i mod 4 of the 8 bytes addressed by lanes 4j + i / 4, j = 0..3), so the
+// tile is copied as it is and never transposed in registers.
+MTB_DEV int swt(int k) { return (k & 3) << 2; }
+
 template <int ROWS, int NT>
-struct TileMn {
-  static constexpr int TOT = (ROWS / 8) * (BK / 4);  // 4x8 blocks in the tile
-  static constexpr int IT = (TOT + NT - 1) / NT;     // (threads past TOT idle)
-  u32x4 r[IT][4];
+struct TileMnT {
+  static_assert(ROWS == 128 || ROWS == 256, "chunk permutation needs 16 or 32 chunks per row");
+  static constexpr int CPR = ROWS / 8;  // 16-byte chunks per k row
+  static constexpr int TOT = BK * CPR;
+  static constexpr int NCH = (TOT + NT - 1) / NT;
+  u32x4 r[NCH];
   MTB_DEV void load(const bf16_t* __restrict__ p, int ld, int row0, int rowmax, int k0, int kmax,
                     int tid) {
 #pragma unroll
-    for (int it = 0; it < IT; ++it) {
-      const int idx = tid + NT * it;
-      if (TOT % NT != 0 && idx >= TOT) break;
-      const int mc = idx % (ROWS / 8), k4 = idx / (ROWS / 8);
-      const int gm = min(row0 + mc * 8, rowmax - 8);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int k = k0 + k4 * 4 + j;  // past the contraction's end: zeros
-        r[it][j] = k < kmax ? *reinterpret_cast<const u32x4*>(p + (size_t)k * ld + gm)
-                            : u32x4{0u, 0u, 0u, 0u};
-      }
+    for (int i = 0; i < NCH; ++i) {
+      const int q = tid + NT * i, k = q / CPR, c = q % CPR;
+      if (TOT % NT != 0 && q >= TOT) break;
+      const int gm = min(row0 + c * 8, rowmax - 8);
+      // past the contraction's end: zeros
+      r[i] = k0 + k < kmax ? *reinterpret_cast<const u32x4*>(p + (size_t)(k0 + k) * ld + gm)
+                           : u32x4{0u, 0u, 0u, 0u};
     }
   }
   MTB_DEV void store(bf16_t* s, int tid) const {
 #pragma unroll
-    for (int it = 0; it < IT; ++it) {
-      const int idx = tid + NT * it;
-      if (TOT % NT != 0 && idx >= TOT) break;
-      const int mc = idx % (ROWS / 8), k4 = idx / (ROWS / 8);
-      const int c = k4 >> 1, half = k4 & 1;
-#pragma unroll
-      for (int mm = 0; mm < 8; ++mm) {
-        const int p = mm >> 1;
-        uint32_t w0, w1;
-        if (mm & 1) {
-          w0 = (r[it][0][p] >> 16) | (r[it][1][p] & 0xffff0000u);
-          w1 = (r[it][2][p] >> 16) | (r[it][3][p] & 0xffff0000u);
-        } else {
-          w0 = (r[it][0][p] & 0xffffu) | (r[it][1][p] << 16);
-          w1 = (r[it][2][p] & 0xffffu) | (r[it][3][p] << 16);
-        }
-        const int row = mc * 8 + mm;
-        u32x2 w = {w0, w1};
-        *reinterpret_cast<u32x2*>(s + row * BK + ((c ^ swz(row)) << 3) + half * 4) = w;
-      }
+    for (int i = 0; i < NCH; ++i) {
+      const int q = tid + NT * i, k = q / CPR, c = q % CPR;
+      if (TOT % NT != 0 && q >= TOT) break;
+      *reinterpret_cast<u32x4*>(s + k * ROWS + ((c ^ swt(k)) << 3)) = r[i];
     }
   }
 };
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4* lds_i16x4_t;
+
+// MFMA fragment (rows r0 .. r0+31, k = 16 kk .. 16 kk + 15; lane: row r0 + lane % 32,
+// k 8 (lane / 32) .. +7) of a [BK][ROWS] tile: two transpose reads of 4 k each
+template <int ROWS>
+MTB_DEV bf16x8 frag_tr(const bf16_t* s, int r0, int kk, int lane) {
+  const int g = lane >> 4, sl = lane & 15;
+  const int m = r0 + 16 * (g & 1) + 4 * (sl & 3);
+  const int k = kk * 16 + 8 * (g >> 1) + (sl >> 2);
+  const int off = ((m >> 3) ^ swt(k)) * 8 + (m & 7);
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t)(s + k * ROWS + off));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t)(s + (k + 4) * ROWS + off));
+  const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
 
 template <typename T>
 MTB_DEV void ld4g(const void* p, size_t off, float (&v)[4]) {
@@ -451,8 +458,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(int M, i
   const int tm = first_m + (bid % per_group) % gsz, tn = (bid % per_group) / gsz;
   const int m0 = tm * BM, n0 = tn * BN;
 
-  using LA = typename std::conditional<AKC, TileKc<BM, NT>, TileMn<BM, NT>>::type;
-  using LB = typename std::conditional<BKC, TileKc<BN, NT>, TileMn<BN, NT>>::type;
+  using LA = typename std::conditional<AKC, TileKc<BM, NT>, TileMnT<BM, NT>>::type;
+  using LB = typename std::conditional<BKC, TileKc<BN, NT>, TileMnT<BN, NT>>::type;
   LA la;
   LB lb;
   f32x16 acc[FM][FN];
@@ -485,12 +492,18 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(int M, i
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int row = wm * WM + i * 32 + (lane & 31);
-        af[i] = *reinterpret_cast<const bf16x8*>(as + row * BK + ((c ^ swz(row)) << 3));
+        if constexpr (AKC)
+          af[i] = *reinterpret_cast<const bf16x8*>(as + row * BK + ((c ^ swz(row)) << 3));
+        else
+          af[i] = frag_tr<BM>(as, wm * WM + i * 32, kk, lane);
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const int row = wn * WN + j * 32 + (lane & 31);
-        bf[j] = *reinterpret_cast<const bf16x8*>(bs + row * BK + ((c ^ swz(row)) << 3));
+        if constexpr (BKC)
+          bf[j] = *reinterpret_cast<const bf16x8*>(bs + row * BK + ((c ^ swz(row)) << 3));
+        else
+          bf[j] = frag_tr<BN>(bs, wn * WN + j * 32, kk, lane);
       }
 #pragma unroll
       for (int i = 0; i < FM; ++i)

@@ -105,8 +105,9 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(int rows, int H, const T* _
 }
 
 // dx = dres + rstd * (gh - mean(gh) - xhat * mean(gh * xhat)), gh = (dy + dy2) * g;
-// dy2 and dres optional
-template <typename T, int NC>
+// dy2 (DY2) and dres (DRES) optional: separate instantiations keep each
+// variant's loads straight-line
+template <typename T, int NC, bool DY2, bool DRES>
 __global__ __launch_bounds__(256) void ln_bwd_kernel(int rows, int H, const T* __restrict__ dy,
                                                      const T* __restrict__ dy2,
                                                      const T* __restrict__ hin,
@@ -128,7 +129,7 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(int rows, int H, const T* _
     if (col < H) {
       float hv[8];
       ld8(dy + base + col, gh[c]);
-      if (dy2) {
+      if constexpr (DY2) {
         float d2[8];
         ld8(dy2 + base + col, d2);
 #pragma unroll
@@ -157,7 +158,7 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(int rows, int H, const T* _
     const int col = (c * 64 + lane) * 8;
     if (col < H) {
       float o[8], d0[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      if (dres) ld8(dres + base + col, d0);
+      if constexpr (DRES) ld8(dres + base + col, d0);
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = d0[e] + r * (gh[c][e] - mg - xh[c][e] * mgx);
       st8(dx + base + col, o);
@@ -287,8 +288,15 @@ hipError_t ln_bwd_t(int rows, int H, const void* dy, const void* dy2, const void
                     const float* mu, const float* rstd, const void* g, const void* dres, void* dx,
                     hipStream_t st) {
   dim3 grid((rows + kRowsPerBlock - 1) / kRowsPerBlock);
-  hipLaunchKernelGGL((ln_bwd_kernel<T, NC>), grid, dim3(256), 0, st, rows, H, (const T*)dy,
-                     (const T*)dy2, (const T*)hin, mu, rstd, (const T*)g, (const T*)dres, (T*)dx);
+#define MTB_LNBK(A2, R)                                                                      \
+  hipLaunchKernelGGL((ln_bwd_kernel<T, NC, A2, R>), grid, dim3(256), 0, st, rows, H, (const T*)dy, \
+                     (const T*)dy2, (const T*)hin, mu, rstd, (const T*)g, (const T*)dres, (T*)dx)
+  if (dy2) {
+    if (dres) MTB_LNBK(true, true); else MTB_LNBK(true, false);
+  } else {
+    if (dres) MTB_LNBK(false, true); else MTB_LNBK(false, false);
+  }
+#undef MTB_LNBK
   return hipGetLastError();
 }
 
