@@ -44,6 +44,10 @@ def test_size_queries_accept_valid_and_reject_invalid_configs():
     assert mtb.saved_bytes(_cfg(seq=100)) == 0
     assert mtb.saved_bytes(_cfg(act="swiglu", ffn=520)) == 0
     assert mtb.saved_bytes(_cfg(dtype="f32", head_dim=32, seq=100)) > 0   # fp32 path: any seq
+    assert mtb.saved_bytes(_cfg(batch=0)) == 0 and "positive" in mtb.last_error()
+    assert mtb.saved_bytes(_cfg(seq=0)) == 0
+    assert mtb.saved_bytes(_cfg(hidden=8192)) > 0                 # the largest hidden
+    assert mtb.saved_bytes(_cfg(hidden=8256)) == 0 and "8192" in mtb.last_error()
     assert mtb.saved_bytes(_cfg(norm="post")) == mtb.saved_bytes(_cfg())
     assert mtb.scratch_bytes(_cfg(norm="post")) > mtb.scratch_bytes(_cfg())
     bad = _cfg()

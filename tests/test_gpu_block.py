@@ -180,3 +180,25 @@ def test_graph_replay_matches_eager_step_post_ln():
                              affine=True, bias=True)
     say("[gpu] graph replay, post-LN", cfg)
     _graph_case(cfg)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_largest_supported_hidden(dtype):
+    """hidden = 8192, the largest the LayerNorm kernels hold in registers (16
+    chunks of 8 per lane), with a short sequence so the oracle stays fast."""
+    extra = dict(head_dim=64, q_heads=2, kv_heads=2) if dtype == "bf16" else dict(head_dim=32,
+                                                                                  q_heads=2,
+                                                                                  kv_heads=1)
+    cfg = inputs.BlockConfig(f"hidden8192-{dtype}", batch=1, seq=64, hidden=8192, ffn=128,
+                             dtype=dtype, causal=True, affine=True, bias=True, seed=2990, **extra)
+    w, x, G = _case(cfg)
+    check_rank_vs_oracle(cfg, w, x, G)
+
+
+@pytest.mark.parametrize("seq", [1, 3])
+def test_fp32_degenerate_sequences(seq):
+    """One or three tokens per sequence (fp32 path: any seq): softmax over a
+    single key, causal triangle of three."""
+    cfg = inputs.C1.with_(name=f"fp32-seq{seq}", seq=seq, batch=3, causal=True, bias=True)
+    w, x, G = _case(cfg)
+    check_rank_vs_oracle(cfg, w, x, G)
