@@ -301,16 +301,24 @@ mtb_status mtb_vocab_xent_combine(int64_t n_tokens, int32_t n_shards, const floa
  * [n_tokens][hidden] (if dh != NULL) -- this shard's partial of the input
  * gradient, summed over the shards by the hook (SUM, bf16). At least one of
  * dh, dw. Workspace: mtb_lmhead_xent_workspace_bytes (device, caller-owned,
- * 16-byte aligned; the same size serves both calls). */
+ * 16-byte aligned; the same size serves both calls).
+ *
+ * logits (optional, bf16 [n_tokens][v_local]): trades memory for the
+ * backward's recompute. Given to the forward, the logits are stored there
+ * (rounded to bf16, and the statistics are those of the stored values, as
+ * mtb_vocab_xent would see them); given to the backward (the same buffer),
+ * no logits GEMM runs: dz is formed in place in `logits` (which it
+ * overwrites) and the workspace may be NULL. NULL in both: the logits are
+ * never stored. */
 size_t mtb_lmhead_xent_workspace_bytes(int64_t n_tokens, int64_t hidden, int64_t v_local);
 mtb_status mtb_lmhead_xent_fwd(int64_t n_tokens, int64_t hidden, int64_t v_local, int64_t v_start,
                                int32_t dtype, const void *h, const void *w, const int64_t *target,
-                               float *stats, float *loss, void *workspace, const mtb_comm *comm,
-                               void *hip_stream);
+                               float *stats, float *loss, void *logits, void *workspace,
+                               const mtb_comm *comm, void *hip_stream);
 mtb_status mtb_lmhead_xent_bwd(int64_t n_tokens, int64_t hidden, int64_t v_local, int64_t v_start,
                                int32_t dtype, const void *h, const void *w, const int64_t *target,
-                               const float *stats, const float *dloss, void *dh, void *dw,
-                               void *workspace, const mtb_comm *comm, void *hip_stream);
+                               const float *stats, const float *dloss, void *logits, void *dh,
+                               void *dw, void *workspace, const mtb_comm *comm, void *hip_stream);
 
 /* Vocab-parallel input embedding ([TP-block] sec. 3) on one vocab shard:
  * this rank holds rows [v_start, v_start + v_local) of the [vocab, hidden]

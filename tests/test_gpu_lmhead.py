@@ -29,20 +29,26 @@ def _dev_inputs(h, w, target, dloss):
             torch.as_tensor(target).to(dev), torch.as_tensor(dloss).to(dev, torch.float32))
 
 
-def _run_one(h, w, target, v0, dloss, comm=None, want=("loss", "dh", "dw")):
-    """One shard through the C ABI -> host dict(loss, stats, dh, dw)."""
+def _run_one(h, w, target, v0, dloss, comm=None, want=("loss", "dh", "dw"), store=False):
+    """One shard through the C ABI -> host dict(loss, stats, dh, dw); store:
+    the forward keeps the logits and the backward uses them (no workspace)."""
     n, H = h.shape
     vl = w.shape[0]
     hd, wd, td, dl = _dev_inputs(h, w, target, dloss)
     ws = torch.empty(mtb.lmhead_xent_workspace_bytes(n, H, vl), dtype=torch.uint8, device=hd.device)
     stats = torch.full((4, n), float("nan"), device=hd.device)
     loss = torch.full((n,), float("nan"), device=hd.device) if "loss" in want else None
-    mtb.lmhead_xent_fwd(n, H, vl, v0, mtb.BF16, hd, wd, td, stats, loss, ws, comm=comm)
+    z = torch.full((n, vl), float("nan"), dtype=torch.bfloat16, device=hd.device) if store else None
+    mtb.lmhead_xent_fwd(n, H, vl, v0, mtb.BF16, hd, wd, td, stats, loss, ws, comm=comm, logits=z)
+    zhost = host(z) if store else None
     dh = torch.full_like(hd, float("nan")) if "dh" in want else None
     dw = torch.full_like(wd, float("nan")) if "dw" in want else None
-    mtb.lmhead_xent_bwd(n, H, vl, v0, mtb.BF16, hd, wd, td, stats, dl, dh, dw, ws, comm=comm)
+    mtb.lmhead_xent_bwd(n, H, vl, v0, mtb.BF16, hd, wd, td, stats, dl, dh, dw,
+                        None if store else ws, comm=comm, logits=z)
     torch.cuda.synchronize()
     out = dict(stats=host(stats))
+    if store:
+        out["logits"] = zhost
     for k, t in (("loss", loss), ("dh", dh), ("dw", dw)):
         if t is not None:
             out[k] = host(t)
@@ -257,3 +263,26 @@ def test_seq4096_vocab_shard_full_size():
     assert e[0] <= TOL["f32"] and e[1] <= TOL["f32"]
     assert max(e[2:]) <= TOL["bf16"]
     assert np.all(np.isfinite(got["dh"])) and np.all(np.isfinite(got["dw"]))
+
+
+@pytest.mark.parametrize("n,H,V", [(264, 200, 1000), (1032, 1032, 2056)])
+def test_stored_logits_mode(n, H, V):
+    """Logits kept by the forward (bf16) and used by the backward in place of
+    the recompute: the stored logits are the product rounded once, the loss
+    is that of the stored logits (bf16-level agreement with the fp64 oracle),
+    and the gradients match the oracle and the recompute path."""
+    cfg = inputs.LmheadConfig("lmhead-store", n_tokens=n, vocab=V, hidden=H, tp=1, seed=3600 + n,
+                              w_std=0.5 / np.sqrt(H))
+    say(f"[gpu] LM head, stored logits: n={n} hidden={H} vocab={V}")
+    h, w, t = inputs.lmhead_h(cfg), inputs.lmhead_w(cfg, 0), inputs.lmhead_targets(cfg)
+    dloss = np.full(n, 1.0 / n, np.float32)
+    got = _run_one(h, w, t, 0, dloss, store=True)
+    ref = _oracle_full(h, [w], t, [0], dloss)
+    z_ref = ol.logits(h, w)
+    assert rel_err(got["logits"], z_ref) <= TOL["bf16"]
+    e = {k: rel_err(got[k], ref[k]) for k in ("loss", "dh")}
+    e["dW"] = rel_err(got["dw"], ref["dws"][0])
+    say("   " + "  ".join(f"{k} {v:.2e}" for k, v in e.items()))
+    assert max(e.values()) <= TOL["bf16"]
+    rec = _run_one(h, w, t, 0, dloss)
+    assert rel_err(got["dh"], rec["dh"]) <= 1e-2 and rel_err(got["dw"], rec["dw"]) <= 1e-2

@@ -719,8 +719,8 @@ size_t mtb_lmhead_xent_workspace_bytes(int64_t n, int64_t h, int64_t v) {
 
 mtb_status mtb_lmhead_xent_fwd(int64_t n, int64_t h, int64_t v, int64_t v0, int32_t dtype,
                                const void* hid, const void* w, const int64_t* target,
-                               float* stats, float* loss, void* workspace, const mtb_comm* comm,
-                               void* hip_stream) {
+                               float* stats, float* loss, void* logits, void* workspace,
+                               const mtb_comm* comm, void* hip_stream) {
   mtb_status s = check_lmhead(n, h, v, v0, dtype);
   if (s != MTB_OK) return s;
   MTB_REQ(hid, "h");
@@ -728,12 +728,15 @@ mtb_status mtb_lmhead_xent_fwd(int64_t n, int64_t h, int64_t v, int64_t v0, int3
   MTB_REQ_A(target, "target", 8);
   MTB_REQ_A(stats, "stats", 4);
   MTB_OPT_A(loss, "loss", 4);
+  MTB_OPT(logits, "logits");
   MTB_REQ(workspace, "workspace");
   hipStream_t st = (hipStream_t)hip_stream;
-  // logits tile by tile, reduced in the epilogue: the [n, v] logits are never stored
+  // logits tile by tile, reduced in the epilogue; stored only if asked for
   Epi e;
   e.kind = EPI_XENT_STATS;
   e.out = workspace;
+  e.out2 = logits;
+  e.ldo2 = (int)v;
   e.target = target;
   e.col0 = v0;
   MTB_HIP(gemm(MTB_BF16, (int)n, (int)v, (int)h, hid, (int)h, true, w, (int)h, true, e, st));
@@ -753,8 +756,9 @@ mtb_status mtb_lmhead_xent_fwd(int64_t n, int64_t h, int64_t v, int64_t v0, int3
 
 mtb_status mtb_lmhead_xent_bwd(int64_t n, int64_t h, int64_t v, int64_t v0, int32_t dtype,
                                const void* hid, const void* w, const int64_t* target,
-                               const float* stats, const float* dloss, void* dh, void* dw,
-                               void* workspace, const mtb_comm* comm, void* hip_stream) {
+                               const float* stats, const float* dloss, void* logits, void* dh,
+                               void* dw, void* workspace, const mtb_comm* comm,
+                               void* hip_stream) {
   mtb_status s = check_lmhead(n, h, v, v0, dtype);
   if (s != MTB_OK) return s;
   MTB_REQ(hid, "h");
@@ -765,11 +769,15 @@ mtb_status mtb_lmhead_xent_bwd(int64_t n, int64_t h, int64_t v, int64_t v0, int3
   MTB_OPT(dh, "dh");
   MTB_OPT(dw, "dw");
   if (!dh && !dw) return fail(MTB_EINVAL, "neither dh nor dw requested");
-  MTB_REQ(workspace, "workspace");
+  MTB_OPT(logits, "logits");
+  if (!logits) MTB_REQ(workspace, "workspace");
   hipStream_t st = (hipStream_t)hip_stream;
-  // dz = (softmax - onehot) * dloss from recomputed logits, bf16 [n][v]
-  void* dz = workspace;
-  {
+  // dz = (softmax - onehot) * dloss, bf16 [n][v]: from the stored logits, in
+  // place, or from logits recomputed by a GEMM whose epilogue forms it
+  void* dz = logits ? logits : workspace;
+  if (logits) {
+    MTB_HIP(xent_finish(MTB_BF16, n, v, v0, logits, target, stats, nullptr, dloss, dz, st));
+  } else {
     Epi e;
     e.kind = EPI_XENT_GRAD;
     e.out = dz;

@@ -282,7 +282,9 @@ MTB_DEV void epi_rows(const Epi& e, const Staged<BN>& st, int M, int N, int mc, 
 // Row statistics of a logits tile for the vocab cross-entropy: per row of
 // the staged chunk, over this tile's valid columns, (max, sum exp(z - max),
 // z at the row's target or 0) into out [M][tiles_n][3]. NT / CR threads per
-// row, each over a contiguous run of columns, merged by lane shuffles.
+// row, each over a contiguous run of columns, merged by lane shuffles. With
+// out2 the logits are also stored (bf16 [M][ldo2]) and the statistics taken
+// from those stored values.
 template <int BN, int CR, int NT>
 MTB_DEV void epi_xent_stats(const Epi& e, const Staged<BN>& st, int M, int N, int mc, int n0, int tn,
                             int tiles_n, int tid) {
@@ -293,9 +295,22 @@ MTB_DEV void epi_xent_stats(const Epi& e, const Staged<BN>& st, int M, int N, in
   float mx = -__builtin_huge_valf(), sum = 0.f, tz = 0.f;
   int64_t lt = -1;
   if (m < M) lt = e.target[m] - e.col0 - n0 - c0;
-  for (int c = 0; c < cend; ++c) mx = fmaxf(mx, st.get(r, c0 + c));
-  for (int c = 0; c < cend; ++c) sum += exp_fast(st.get(r, c0 + c) - mx);
-  if (lt >= 0 && lt < cend) tz = st.get(r, c0 + (int)lt);
+  const bool keep = e.out2 != nullptr;
+  auto z = [&](int c) {
+    const float v = st.get(r, c0 + c);
+    return keep ? bf2f(f2bf(v)) : v;
+  };
+  if (keep && m < M) {
+    static_assert(CPT % 8 == 0, "stored logits go out 8 at a time");
+    for (int c = 0; c < cend; c += 8) {  // cend is a multiple of 8 (N % 8 == 0)
+      float v[8];
+      st.get8(r, c0 + c, v);
+      out8(e.out2, (size_t)m * e.ldo2 + n0 + c0 + c, v);
+    }
+  }
+  for (int c = 0; c < cend; ++c) mx = fmaxf(mx, z(c));
+  for (int c = 0; c < cend; ++c) sum += exp_fast(z(c) - mx);
+  if (lt >= 0 && lt < cend) tz = z((int)lt);
 #pragma unroll
   for (int o = 1; o < TPR; o <<= 1) {
     const float m2 = __shfl_xor(mx, o, 64), s2 = __shfl_xor(sum, o, 64);

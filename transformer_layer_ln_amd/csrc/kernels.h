@@ -28,7 +28,8 @@ enum EpiKind {
   EPI_DSWIGLU = 4,  // C = dm [M][F]; aux = u [M][2F] interleaved: out [M][2F] = (d gate, d up)
   EPI_XENT_STATS = 5,  // C = logits [M][N] (vocab columns from col0): per row and BN-wide column
                        // tile, (max, sum exp(C - max), C at the row's target or 0) to
-                       // out (float) [M][tiles_n][3]; nothing else is stored
+                       // out (float) [M][tiles_n][3]; with out2 the logits are also stored
+                       // (bf16 [M][ldo2]) and the statistics are those of the stored values
   EPI_XENT_GRAD = 6,   // out = (exp(C - M_r) / S_r - [col0 + n == target_r]) * dloss_r with
                        // M_r = rowstat[r], S_r = rowstat[M + r], dloss_r = rowscale[r]
 };

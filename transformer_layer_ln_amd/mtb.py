@@ -97,11 +97,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mtb_lmhead_xent_workspace_bytes.restype = c_size_t
     lib.mtb_lmhead_xent_fwd.argtypes = [c_int64, c_int64, c_int64, c_int64, c_int32, c_void_p,
                                         c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
-                                        c_void_p]
+                                        c_void_p, c_void_p]
     lib.mtb_lmhead_xent_fwd.restype = c_int32
     lib.mtb_lmhead_xent_bwd.argtypes = [c_int64, c_int64, c_int64, c_int64, c_int32, c_void_p,
                                         c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
-                                        c_void_p, c_void_p, c_void_p]
+                                        c_void_p, c_void_p, c_void_p, c_void_p]
     lib.mtb_lmhead_xent_bwd.restype = c_int32
     lib.mtb_vocab_embed_fwd.argtypes = [c_int64, c_int64, c_int64, c_int64, c_int32, c_void_p,
                                         c_void_p, c_void_p, c_void_p, c_void_p]
@@ -209,18 +209,19 @@ def lmhead_xent_workspace_bytes(n_tokens, hidden, v_local):
 
 
 def lmhead_xent_fwd(n_tokens, hidden, v_local, v_start, dtype, h, w, target, stats, loss,
-                    workspace, comm=None, stream=None):
+                    workspace, comm=None, stream=None, logits=None):
     _check(load().mtb_lmhead_xent_fwd(n_tokens, hidden, v_local, v_start, dtype, _ptr(h), _ptr(w),
-                                      _ptr(target), _ptr(stats), _ptr(loss), _ptr(workspace),
-                                      byref(comm) if comm is not None else None, _stream(stream)))
+                                      _ptr(target), _ptr(stats), _ptr(loss), _ptr(logits),
+                                      _ptr(workspace), byref(comm) if comm is not None else None,
+                                      _stream(stream)))
 
 
 def lmhead_xent_bwd(n_tokens, hidden, v_local, v_start, dtype, h, w, target, stats, dloss, dh, dw,
-                    workspace, comm=None, stream=None):
+                    workspace, comm=None, stream=None, logits=None):
     _check(load().mtb_lmhead_xent_bwd(n_tokens, hidden, v_local, v_start, dtype, _ptr(h), _ptr(w),
-                                      _ptr(target), _ptr(stats), _ptr(dloss), _ptr(dh), _ptr(dw),
-                                      _ptr(workspace), byref(comm) if comm is not None else None,
-                                      _stream(stream)))
+                                      _ptr(target), _ptr(stats), _ptr(dloss), _ptr(logits), _ptr(dh),
+                                      _ptr(dw), _ptr(workspace),
+                                      byref(comm) if comm is not None else None, _stream(stream)))
 
 
 def vocab_embed_fwd(n_tokens, v_local, v_start, hidden, dtype, ids, table, out, comm=None,
