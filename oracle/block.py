@@ -242,9 +242,8 @@ def block_forward(x, w, *, q_heads, kv_heads, head_dim, act="gelu", causal=False
         v = _lin(a, ws["wv"], ws.get("bv")).reshape(B, S, nkv, d).transpose(0, 2, 1, 3)
         mult = None
         if dr["p_attn"] > 0.0:
-            mult = odrop.multiplier((B, nq, S, S), odrop.SITE_ATTN,
-                                    odrop.attn_seed(dr["seed"], tp_rank + r), dr["offset"],
-                                    dr["p_attn"])
+            mult = odrop.AttnMult(B, nq, S, odrop.attn_seed(dr["seed"], tp_rank + r),
+                                  dr["offset"], dr["p_attn"])
         o = attention_fwd(q, k, v, causal, mult)
         o_tok = o.transpose(0, 2, 1, 3).reshape(T, nq * d)
         p_attn.append(o_tok @ ws["wo"].T)

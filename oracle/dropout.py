@@ -41,12 +41,13 @@ def philox4x32_10(c0, c1, c2, c3, k0, k1):
     c0, c1, c2, c3 = (np.asarray(v, np.uint64) & MASK32 for v in (c0, c1, c2, c3))
     k0 = np.uint64(k0) & MASK32
     k1 = np.uint64(k1) & MASK32
+    s32 = np.uint64(32)
     for _ in range(10):
-        p0 = _M0 * c0
+        p0 = _M0 * c0          # 32 x 32 -> 64-bit products
         p1 = _M1 * c2
-        hi0, lo0 = p0 >> np.uint64(32), p0 & MASK32
-        hi1, lo1 = p1 >> np.uint64(32), p1 & MASK32
-        c0, c1, c2, c3 = (hi1 ^ c1 ^ k0) & MASK32, lo1, (hi0 ^ c3 ^ k1) & MASK32, lo0
+        # new words: (hi(p1) ^ c1 ^ k0, lo(p1), hi(p0) ^ c3 ^ k1, lo(p0)); every
+        # operand is below 2^32, so the xors need no mask
+        c0, c1, c2, c3 = (p1 >> s32) ^ c1 ^ k0, p1 & MASK32, (p0 >> s32) ^ c3 ^ k1, p0 & MASK32
         k0 = (k0 + _W0) & MASK32
         k1 = (k1 + _W1) & MASK32
     return c0, c1, c2, c3
@@ -87,3 +88,32 @@ def multiplier(shape, site, seed, offset, p):
 
 def attn_seed(seed, tp_rank):
     return seed + TP_SEED_OFFSET + tp_rank
+
+
+def multiplier_range(start, count, site, seed, offset, p):
+    """keep / (1 - p) of the flat elements start .. start + count - 1."""
+    if p == 0.0:
+        return np.ones(count)
+    idx = np.arange(start, start + count, dtype=np.uint64)
+    return (words(idx, site, seed, offset) >= np.uint64(threshold(p))) / (1.0 - p)
+
+
+class AttnMult:
+    """Dropout multipliers of the attention probabilities [B, nq, S, S]
+    (flat index ((b * nq + h) * S + q) * S + k), made one (batch, head)
+    slice at a time: mult[b, h] is the [S, S] slice; np.asarray gives all."""
+
+    def __init__(self, B, nq, S, seed, offset, p):
+        self.B, self.nq, self.S = B, nq, S
+        self.seed, self.offset, self.p = seed, offset, p
+        self.shape = (B, nq, S, S)
+
+    def __getitem__(self, bh):
+        b, h = bh
+        S = self.S
+        return multiplier_range((b * self.nq + h) * S * S, S * S, SITE_ATTN, self.seed,
+                                self.offset, self.p).reshape(S, S)
+
+    def __array__(self, dtype=None, copy=None):
+        a = np.stack([np.stack([self[b, h] for h in range(self.nq)]) for b in range(self.B)])
+        return a if dtype is None else a.astype(dtype)

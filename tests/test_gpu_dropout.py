@@ -96,3 +96,16 @@ def test_dropout_hook_path_matches_fused_path():
             if k != "bk":
                 assert rel_err(g_h[k], g[k]) < 1e-2, k
     assert len(calls) == 8
+
+
+@pytest.mark.timeout(400)
+def test_seq2048_share_with_dropout_full_size():
+    """The workload `bench.py --workload seq2048-dropout` times: the seq-2048
+    causal TP=8 rank share with dropout 0.1 on all three sites, whole
+    tensors. p is taken as its float32 value on both sides (the device
+    threshold comes from the float in mtb_cfg). The oracle's masks alone are
+    ~10^8 generator words: tens of seconds on the CPU."""
+    p = float(np.float32(0.1))
+    cfg = inputs.C4.with_(name="C4-dropout", p_attn=p, p_hidden=p, drop_seed=1234, drop_offset=0)
+    w, x, G = _case(cfg)
+    check_rank_vs_oracle(cfg, w, x, G, tp_rank=3)

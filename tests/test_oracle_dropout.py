@@ -128,12 +128,16 @@ def test_tensor_parallel_seeds():
     x = rng.normal(size=(1, 8, H))
     kw = _kw(nq, nkv, "gelu", False, "pre")
     _, c = ob.block_forward(x, w, R=R, dropout=DROP, **kw)
-    m0, m1 = c["shards"][0]["mult"], c["shards"][1]["mult"]
+    m0, m1 = np.asarray(c["shards"][0]["mult"]), np.asarray(c["shards"][1]["mult"])
     assert m0.shape == m1.shape and (m0 != m1).mean() > 0.3
     # rank 1 of two = shard 0 of a one-shard run at tp_rank 1
     _, c1 = ob.block_forward(x, ob.shard(w, R, 1, d), R=1, dropout=DROP, tp_rank=1,
                              **dict(kw, q_heads=nq // R, kv_heads=nkv // R))
-    assert np.array_equal(c1["shards"][0]["mult"], m1)
+    assert np.array_equal(np.asarray(c1["shards"][0]["mult"]), m1)
+    # the per-(batch, head) slices are the full-array mask's slices
+    full = od.keep_mask((1, nq // R, 8, 8), od.SITE_ATTN, od.attn_seed(DROP["seed"], 1),
+                        DROP["offset"], DROP["p_attn"]) / (1 - DROP["p_attn"])
+    assert np.array_equal(full, m1)
     _, c0 = ob.block_forward(x, ob.shard(w, R, 0, d), R=1, dropout=DROP, tp_rank=0,
                              **dict(kw, q_heads=nq // R, kv_heads=nkv // R))
     assert np.array_equal(c0["mult_h1"], c1["mult_h1"]) and np.array_equal(c0["mult_h2"], c1["mult_h2"])
@@ -196,7 +200,7 @@ def test_masked_block_against_float64_autograd():
     v = v.repeat_interleave(nq // nkv, dim=1)
     sc = torch.matmul(q, k.transpose(-1, -2)) / d ** 0.5
     sc = sc.masked_fill(torch.ones(S, S, dtype=torch.bool).triu(1), float("-inf"))
-    pm = torch.softmax(sc, -1) * torch.tensor(c["shards"][0]["mult"])
+    pm = torch.softmax(sc, -1) * torch.tensor(np.asarray(c["shards"][0]["mult"]))
     o = torch.matmul(pm, v).permute(0, 2, 1, 3).reshape(B, S, nq * d)
     m1 = torch.tensor(c["mult_h1"].reshape(B, S, H))
     m2 = torch.tensor(c["mult_h2"].reshape(B, S, H))
