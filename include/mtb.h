@@ -35,7 +35,7 @@
  *   different streams with different buffers may run concurrently.
  * Errors: argument checks run before any launch; on failure nothing is
  *   launched and MTB_EINVAL (bad pointer, size or alignment) or
- *   MTB_EUNSUPPORTED (a valid shape this build has no kernel for) is
+ *   MTB_EUNSUPPORTED (a valid shape the library has no kernel for) is
  *   returned. MTB_EHIP reports a failed launch, MTB_ECOMM a failed
  *   reduction hook (nothing further is launched after it).
  *   mtb_last_error() gives a message for the last non-OK status of the

@@ -99,7 +99,7 @@ mtb_status check_cfg(const mtb_cfg* c, Dims& d) {
   d.NO = d.nq * d.d;
   d.es = d.dt == MTB_BF16 ? 2 : 4;
   if (d.T > (1 << 30) || d.H > 8192 || d.Nqkv > (1 << 20) || d.Fu > (1 << 24))
-    return fail(MTB_EUNSUPPORTED, "sizes beyond this build's limits (T <= 2^30, hidden <= 8192)");
+    return fail(MTB_EUNSUPPORTED, "sizes beyond the library's limits (T <= 2^30, hidden <= 8192)");
   if (d.act == MTB_ACT_SWIGLU && d.F % 16)
     return fail(MTB_EUNSUPPORTED, "SwiGLU needs ffn %% 16 == 0 (gate/up interleave of 16)");
   if (d.dt == MTB_BF16) {
