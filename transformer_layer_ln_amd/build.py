@@ -2,7 +2,7 @@
 
     python -m transformer_layer_ln_amd.build
 
-Compiles every ``csrc/*.hip`` to an object in ``_build/`` (in parallel) and
+Regenerates ``csrc/gemm_loop.inc``, compiles every ``csrc/*.hip`` to an object in ``_build/`` (in parallel) and
 links the shared library. Always recompiles: it is the "does it build" check.
 """
 from __future__ import annotations
@@ -38,6 +38,11 @@ def _run(cmd):
 
 def build(verbose: bool = False, jobs: int = 8) -> str:
     os.makedirs(BUILD, exist_ok=True)
+    # the GEMM main loop is generated (csrc/gen_gemm_loop.py -> csrc/gemm_loop.inc)
+    rc, out = _run([sys.executable, os.path.join(CSRC, "gen_gemm_loop.py")])
+    if rc != 0:
+        print(out)
+        raise RuntimeError("libmtb: generating gemm_loop.inc failed")
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     objs = [os.path.join(BUILD, os.path.basename(s)[:-4] + ".o") for s in srcs]
     cmds = [[HIPCC, *CFLAGS, "-c", s, "-o", o] for s, o in zip(srcs, objs)]

@@ -31,6 +31,7 @@
 #include <type_traits>
 
 #include "drop.h"
+#include "gemm_loop.inc"
 
 #include "common.h"
 #include "kernels.h"
@@ -439,6 +440,77 @@ __global__ __launch_bounds__(NT) void splitk_epi_kernel(int M, int N, int splits
   }
 }
 
+// Block -> (tile row, tile column, contraction split). Blocks i, i+8, i+16,
+// ... share an XCD (and its L2), so each XCD gets a contiguous run of tiles,
+// walked GROUP tile-rows at a time so that concurrently running tiles share A
+// and B panels. Split s of the contraction takes blocks [s * tiles, (s + 1) *
+// tiles).
+struct BlockTile {
+  int tm, tn, split, tiles_n;
+};
+template <int BM, int BN>
+MTB_DEV BlockTile block_tile(int M, int N) {
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  int bid = blockIdx.x;
+  const int nb = gridDim.x;
+  if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+  const int split = bid / (tiles_m * tiles_n);
+  bid -= split * (tiles_m * tiles_n);
+  constexpr int GROUP = 8;
+  const int per_group = GROUP * tiles_n;
+  const int first_m = (bid / per_group) * GROUP;
+  const int gsz = min(tiles_m - first_m, GROUP);
+  return {first_m + (bid % per_group) % gsz, (bid % per_group) / gsz, split, tiles_n};
+}
+
+// Epilogue. lane holds C[m][n..n+3] with m = (lane & 31), n = 8q + 4(lane >> 5)
+// inside each 32x32 fragment (register 4q + r -> column n + r). The tile goes
+// through LDS CR rows at a time, reusing the operand buffers (SMEM_F floats;
+// the caller has synchronised after the last operand read).
+template <int BM, int BN, int WGM, int WGN, int SMEM_F, bool AKC, int EPI>
+MTB_DEV void gemm_epilogue(const f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32], void* smem,
+                           const Epi& ep, int M, int N, int m0, int n0, const BlockTile& bt,
+                           int wm, int wn, int lane, int tid) {
+  constexpr int NT = 64 * WGM * WGN;
+  constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32;
+  constexpr int CR = stage_rows(BM, WM, SMEM_F / BN, BM);
+  static_assert(CR >= WM && BM % CR == 0 && CR * BN <= SMEM_F, "staging chunk");
+  // the per-batch transposed copy (token-major left operand only) needs whole 64-token groups
+  constexpr bool COLS = EPI == EPI_STORE && AKC;
+  static_assert(!COLS || CR % 64 == 0, "transposed copy needs whole 64-token groups per chunk");
+  const Staged<BN> st{reinterpret_cast<float*>(smem)};
+#pragma unroll 1
+  for (int c0 = 0; c0 < BM; c0 += CR) {
+    if (c0 > 0) __syncthreads();
+    if (wm * WM >= c0 && wm * WM < c0 + CR) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int r = wm * WM - c0 + i * 32 + (lane & 31);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int n = wn * WN + j * 32 + 8 * q + 4 * (lane >> 5);
+            const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                             acc[i][j][4 * q + 3]};
+            st.put4(r, n, v);
+          }
+      }
+    }
+    __syncthreads();
+    if constexpr (EPI == EPI_PARTIAL)
+      epi_partial<BN, CR, NT>(reinterpret_cast<float*>(ep.ws) + (size_t)bt.split * M * N, st, M, N,
+                              m0 + c0, n0, tid);
+    else if constexpr (EPI == EPI_XENT_STATS)
+      epi_xent_stats<BN, CR, NT>(ep, st, M, N, m0 + c0, n0, bt.tn, bt.tiles_n, tid);
+    else
+      epi_rows<EPI, BN, CR, NT>(ep, st, M, N, m0 + c0, n0, tid);
+    if constexpr (COLS) {
+      if (ep.outT) epi_cols<BN, CR, NT>(ep, st, M, N, m0 + c0, n0, tid);
+    }
+  }
+}
+
 // BM x BN block tile, WGM x WGN wavefronts (each WM x WN = FM x FN 32x32
 // fragments), OCC = wavefronts per SIMD the register budget must allow
 template <int BM, int BN, int WGM, int WGN, int OCC, bool AKC, bool BKC, int EPI>
@@ -455,23 +527,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(int M, i
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
 
-  // block -> tile: blocks i, i+8, i+16, ... share an XCD (and its L2), so
-  // give each XCD a contiguous run of tiles, then walk GROUP tile-rows at a
-  // time so that concurrently running tiles share A and B panels.
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  int bid = blockIdx.x;
-  const int nb = gridDim.x;
-  if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
-  // split contraction: blocks [s * tiles, (s + 1) * tiles) take k-range s
-  const int split = bid / (tiles_m * tiles_n);
-  bid -= split * (tiles_m * tiles_n);
-  const int kspan = K / ksplit, kbeg = split * kspan;
-  constexpr int GROUP = 8;
-  const int per_group = GROUP * tiles_n;
-  const int first_m = (bid / per_group) * GROUP;
-  const int gsz = min(tiles_m - first_m, GROUP);
-  const int tm = first_m + (bid % per_group) % gsz, tn = (bid % per_group) / gsz;
-  const int m0 = tm * BM, n0 = tn * BN;
+  const BlockTile bt = block_tile<BM, BN>(M, N);
+  const int kspan = K / ksplit, kbeg = bt.split * kspan;
+  const int m0 = bt.tm * BM, n0 = bt.tn * BN;
 
   using LA = typename std::conditional<AKC, TileKc<BM, NT>, TileMnT<BM, NT>>::type;
   using LB = typename std::conditional<BKC, TileKc<BN, NT>, TileMnT<BN, NT>>::type;
@@ -533,46 +591,127 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(int M, i
     __syncthreads();
   }
 
-  // Epilogue. lane holds C[m][n..n+3] with m = (lane & 31), n = 8q + 4(lane >> 5)
-  // inside each 32x32 fragment (register 4q + r -> column n + r). The tile
-  // goes through LDS CR rows at a time (the last k-step ended with a barrier,
-  // so the operand buffers are free).
-  constexpr int CR = stage_rows(BM, WM, 2 * (BM + BN) * BK / 2 / BN, BM);
-  static_assert(CR >= WM && BM % CR == 0 && CR * BN <= (BM + BN) * BK, "staging chunk");
-  // the per-batch transposed copy (token-major left operand only) needs whole 64-token groups
-  constexpr bool COLS = EPI == EPI_STORE && AKC;
-  static_assert(!COLS || CR % 64 == 0, "transposed copy needs whole 64-token groups per chunk");
-  const Staged<BN> st{reinterpret_cast<float*>(smem)};
-#pragma unroll 1
-  for (int c0 = 0; c0 < BM; c0 += CR) {
-    if (c0 > 0) __syncthreads();
-    if (wm * WM >= c0 && wm * WM < c0 + CR) {
+  gemm_epilogue<BM, BN, WGM, WGN, (BM + BN) * BK, AKC, EPI>(acc, smem, ep, M, N, m0, n0, bt, wm, wn,
+                                                            lane, tid);
+}
+
+// 256 x 256 tile, 4 wavefronts (2 x 2) of 128 x 128 each, with the hand-scheduled
+// main loop of gemm_loop.inc (schedule and LDS layout: gen_gemm_loop.py).
+// Needs each split's contraction to be a multiple of 128 and every operand
+// byte offset below 2^32 (sched_ok).
+constexpr int SBK = 32, SSTAGES = 4;
+
+template <bool AKC, bool BKC, int EPI>
+__global__ __launch_bounds__(256, 1) void gemm_bf16_sched_kernel(int M, int N, int K,
+                                                                 const bf16_t* __restrict__ A, int lda,
+                                                                 const bf16_t* __restrict__ B, int ldb,
+                                                                 Epi ep, int ksplit) {
+  constexpr int BM = 256, BN = 256;
+  constexpr uint32_t B_OFF = BM * SBK * 2;  // operand B follows A inside a stage (bytes)
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[SSTAGES * (BM + BN) * SBK];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const BlockTile bt = block_tile<BM, BN>(M, N);
+  const int kspan = K / ksplit, kbeg = bt.split * kspan;
+  const int m0 = bt.tm * BM, n0 = bt.tn * BN;
+  const uint32_t lds = (uint32_t)(uintptr_t)smem;
+
+  // Copies: this wavefront's blocks 4 wave + q (q = 0..3) of 1 KB per operand
+  // and k-tile; lane l writes bytes [16 l, 16 l + 16) of its block.
+  // k-contiguous: block = 16 rows x 64 bytes; row r's chunk c sits at c ^ ((r >> 2) & 3).
+  // otherwise:    block = 2 k-rows x 512 bytes; k-row k's chunk c sits at c ^ ((k & 3) << 2).
+  auto copy_off = [&](bool kc, int q, int row0, int rows, int ld) -> uint32_t {
+    const int b = 4 * wave + q;
+    if (kc) {
+      const int r = 16 * b + (lane >> 2), c = (lane & 3) ^ ((r >> 2) & 3);
+      return ((uint32_t)min(row0 + r, rows - 1) * (uint32_t)ld + c * 8) * 2u;
+    }
+    const int k = 2 * b + (lane >> 5), c = (lane & 31) ^ ((k & 3) << 2);
+    return ((uint32_t)k * (uint32_t)ld + (uint32_t)min(row0 + c * 8, rows - 8)) * 2u;
+  };
+  uint32_t voA[4], voB[4];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int r = wm * WM - c0 + i * 32 + (lane & 31);
+  for (int q = 0; q < 4; ++q) {
+    voA[q] = copy_off(AKC, q, m0, M, lda);
+    voB[q] = copy_off(BKC, q, n0, N, ldb);
+  }
+  const uint64_t sbA = (uint64_t)(A + (AKC ? (size_t)kbeg : (size_t)kbeg * lda));
+  const uint64_t sbB = (uint64_t)(B + (BKC ? (size_t)kbeg : (size_t)kbeg * ldb));
+  const uint32_t ksA = AKC ? SBK * 2 : SBK * 2 * (uint32_t)lda;
+  const uint32_t ksB = BKC ? SBK * 2 : SBK * 2 * (uint32_t)ldb;
+  const uint32_t ldsA = __builtin_amdgcn_readfirstlane(lds + wave * 4096);
+  const uint32_t ldsB = __builtin_amdgcn_readfirstlane(lds + B_OFF + wave * 4096);
+
+  // Fragment base addresses (stages 2 and 3 from the second set, 64 KB on,
+  // past the reach of the 16-bit read offset).
+  // k-contiguous: f[2 hi + kk] for step kk (fragment i is 2 KB further);
+  // otherwise: f[4 hi + i] for fragment i (step kk is 8 KB further).
+  auto frag_bases = [&](bool kc, int w, uint32_t off, uint32_t (&f)[8]) {
+    if (kc) {
+      const int r = w * 128 + (lane & 31);
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+      for (int kk = 0; kk < 2; ++kk) {
+        const int c = 2 * kk + (lane >> 5);
+        f[kk] = lds + off + r * 64 + ((c ^ ((r >> 2) & 3)) << 4);
+        f[2 + kk] = f[kk] + 65536;
+        f[4 + kk] = f[kk];
+        f[6 + kk] = f[2 + kk];
+      }
+    } else {
+      const int g = lane >> 4, sl = lane & 15, k = 8 * (g >> 1) + (sl >> 2);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int n = wn * WN + j * 32 + 8 * q + 4 * (lane >> 5);
-            const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                             acc[i][j][4 * q + 3]};
-            st.put4(r, n, v);
-          }
+      for (int i = 0; i < 4; ++i) {
+        const int m = w * 128 + 32 * i + 16 * (g & 1) + 4 * (sl & 3);
+        f[i] = lds + off + (k * 256 + ((m >> 3) ^ ((k & 3) << 2)) * 8 + (m & 7)) * 2;
+        f[4 + i] = f[i] + 65536;
       }
     }
-    __syncthreads();
-    if constexpr (EPI == EPI_PARTIAL)
-      epi_partial<BN, CR, NT>(reinterpret_cast<float*>(ep.ws) + (size_t)split * M * N, st, M, N,
-                              m0 + c0, n0, tid);
-    else if constexpr (EPI == EPI_XENT_STATS)
-      epi_xent_stats<BN, CR, NT>(ep, st, M, N, m0 + c0, n0, tn, tiles_n, tid);
-    else
-      epi_rows<EPI, BN, CR, NT>(ep, st, M, N, m0 + c0, n0, tid);
-    if constexpr (COLS) {
-      if (ep.outT) epi_cols<BN, CR, NT>(ep, st, M, N, m0 + c0, n0, tid);
-    }
-  }
+  };
+  uint32_t fa[8], fb[8];
+  frag_bases(AKC, wm, 0, fa);
+  frag_bases(BKC, wn, B_OFF, fb);
+
+  const int KT = kspan / SBK;
+  int rem = KT - 1, iters = KT / SSTAGES;
+  uint32_t ta, tb;
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+#define MTB_LOOP_OPERANDS                                                                          \
+  : [c00] "+a"(acc[0][0]), [c01] "+a"(acc[0][1]), [c02] "+a"(acc[0][2]), [c03] "+a"(acc[0][3]),    \
+    [c10] "+a"(acc[1][0]), [c11] "+a"(acc[1][1]), [c12] "+a"(acc[1][2]), [c13] "+a"(acc[1][3]),    \
+    [c20] "+a"(acc[2][0]), [c21] "+a"(acc[2][1]), [c22] "+a"(acc[2][2]), [c23] "+a"(acc[2][3]),    \
+    [c30] "+a"(acc[3][0]), [c31] "+a"(acc[3][1]), [c32] "+a"(acc[3][2]), [c33] "+a"(acc[3][3]),    \
+    [voA0] "+v"(voA[0]), [voA1] "+v"(voA[1]), [voA2] "+v"(voA[2]), [voA3] "+v"(voA[3]),            \
+    [voB0] "+v"(voB[0]), [voB1] "+v"(voB[1]), [voB2] "+v"(voB[2]), [voB3] "+v"(voB[3]),            \
+    [rem] "+s"(rem), [iters] "+s"(iters), [ta] "=&s"(ta), [tb] "=&s"(tb)                           \
+  : [ldsA] "s"(ldsA), [ldsB] "s"(ldsB), [sbA] "s"(sbA), [sbB] "s"(sbB), [ksA] "s"(ksA),            \
+    [ksB] "s"(ksB), [fa0] "v"(fa[0]), [fa1] "v"(fa[1]), [fa2] "v"(fa[2]), [fa3] "v"(fa[3]),        \
+    [fa4] "v"(fa[4]), [fa5] "v"(fa[5]), [fa6] "v"(fa[6]), [fa7] "v"(fa[7]), [fb0] "v"(fb[0]),      \
+    [fb1] "v"(fb[1]), [fb2] "v"(fb[2]), [fb3] "v"(fb[3]), [fb4] "v"(fb[4]), [fb5] "v"(fb[5]),      \
+    [fb6] "v"(fb[6]), [fb7] "v"(fb[7])                                                             \
+  : "memory", "m0", "scc", MTB_GEMM_LOOP_CLOBBERS
+  // The loop writes M0 (the LDS address of its copies) before every use; no
+  // code around it keeps a value in M0, so its clobber is declared without
+  // the compiler's warning about reserved registers.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  if constexpr (AKC && BKC)
+    asm volatile(MTB_GEMM_LOOP_NT MTB_LOOP_OPERANDS);
+  else if constexpr (AKC)
+    asm volatile(MTB_GEMM_LOOP_NN MTB_LOOP_OPERANDS);
+  else
+    asm volatile(MTB_GEMM_LOOP_TN MTB_LOOP_OPERANDS);
+#pragma clang diagnostic pop
+#undef MTB_LOOP_OPERANDS
+  __syncthreads();
+  gemm_epilogue<BM, BN, 2, 2, SSTAGES * (BM + BN) * SBK / 2, AKC, EPI>(acc, smem, ep, M, N, m0, n0, bt,
+                                                                      wm, wn, lane, tid);
 }
 
 // ---------------------------------------------------------------------------
@@ -647,7 +786,7 @@ double fill(long tiles, int per_cu) {
   return (double)tiles / (double)(waves * slots);
 }
 
-enum Tile { T256x256, T256x192, T256x128, T128x128 };
+enum Tile { T256x256, T256x192, T256x128, T128x128, TSCHED };
 struct Plan {
   Tile tile;
   int splits;  // > 1: the contraction is split over that many blocks per tile
@@ -656,28 +795,39 @@ struct Plan {
 // Tile shape and contraction split per problem, the one decision both the
 // launch and the workspace query use. Candidates (relative per-tile rates
 // measured on MI355X over the block's GEMM shapes, times the fraction of the
-// chip their tile count fills): 256x256 (2x4 wavefronts), 256x192 (4x2) when
-// N splits into 192-wide tiles (plain store), 128x128 (2x2, two blocks per
-// CU); for weight gradients (both operands transposed in LDS) 256x128 (4x2)
-// when it fills the chip, else 128x128 (at two blocks per CU those beat a
-// partly filled 256x128 grid: 158 vs 175 us for the 1536 x 4096 x 8192 QKV
-// weight gradient). Tiles for 6 wavefronts fill the chip better at N = 1536
-// but leave two of a CU's four SIMDs with twice the work: measured slower.
+// chip their tile count fills): the scheduled 256x256 kernel (4 wavefronts,
+// gen_gemm_loop.py) when the contraction is a multiple of 128, 1.2-1.5x the
+// 2x4-wavefront 256x256 kernel; 256x192 (4x2 wavefronts) when N splits into
+// 192-wide tiles (plain store); 128x128 (2x2, two blocks per CU). Weight
+// gradients (both operands transposed in LDS) take the scheduled kernel with
+// the contraction split until the blocks fill 3/4 of the chip; without it,
+// 256x128 (4x2) when it fills the chip, else 128x128 (at two blocks per CU
+// those beat a partly filled 256x128 grid: 158 vs 175 us for the 1536 x 4096
+// x 8192 QKV weight gradient). Tiles for 6 wavefronts fill the chip better at
+// N = 1536 but leave two of a CU's four SIMDs with twice the work: measured
+// slower.
 //
 // Split contraction (needs a workspace, `split_ok`; plain stores only): a
 // deep product whose tiles leave at least half of the chip's block slots idle
-// gets its contraction split into 2, 4 or 8 parts at least 1024 deep -- weight
-// gradients on 256x128 tiles up to 3/4 of a wave, token-major products on
-// 128x128 tiles up to both blocks per CU -- and the fp32 partial tiles are
-// summed in a fixed order by a second pass that also runs the epilogue. Each
-// extra split costs 8 bytes per output element of partial-tile traffic. (At
-// the seq-512 share, where every GEMM is 4096 x <=1024 x <=4096, splitting
-// down to 512-deep parts made the step slower, 0.356 -> 0.401 ms: a block's
-// fixed costs, not its k-loop, dominate there.)
+// gets its contraction split into 2, 4 or 8 parts at least 1024 deep --
+// token-major products on 128x128 tiles up to both blocks per CU -- and the
+// fp32 partial tiles are summed in a fixed order by a second pass that also
+// runs the epilogue. Each extra split costs 8 bytes per output element of
+// partial-tile traffic. (At the seq-512 share, where every GEMM is 4096 x
+// <=1024 x <=4096, splitting down to 512-deep parts made the step slower,
+// 0.356 -> 0.401 ms: a block's fixed costs, not its k-loop, dominate there.)
 Plan plan(int M, int N, int K, bool a_kc, bool b_kc, int kind, bool split_ok) {
   auto tl = [&](int bm, int bn) { return (long)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
   auto depth_ok = [&](int s) { return K % (s * BK) == 0 && K / s >= 1024; };
+  auto sched_depth = [&](int s) { return K % (s * SSTAGES * SBK) == 0 && K / s >= 1024; };
+  const long t256 = tl(256, 256);
   if (!a_kc && !b_kc) {
+    if (K % (SSTAGES * SBK) == 0) {
+      int s = 1;
+      if (split_ok && kind == EPI_STORE)
+        while (s < 8 && t256 * s * 4 < 3L * kCUs && sched_depth(2 * s)) s *= 2;
+      if (t256 * s * 2 >= kCUs) return {TSCHED, s};
+    }
     const long t2 = tl(256, 128);
     if (split_ok && kind == EPI_STORE && t2 <= kCUs / 2 && K % BK == 0) {
       int s = 1;
@@ -687,7 +837,7 @@ Plan plan(int M, int N, int K, bool a_kc, bool b_kc, int kind, bool split_ok) {
     if (K >= 1024 && t2 >= kCUs) return {T256x128, 1};
     return {T128x128, 1};
   }
-  const long t256 = tl(256, 256), t128 = tl(128, 128);
+  const long t128 = tl(128, 128);
   if (split_ok && a_kc && kind == EPI_STORE && t128 <= kCUs && t256 < kCUs && K % BK == 0) {
     int s = 1;
     while (s < 4 && t128 * s < 2L * kCUs && depth_ok(2 * s)) s *= 2;
@@ -695,13 +845,34 @@ Plan plan(int M, int N, int K, bool a_kc, bool b_kc, int kind, bool split_ok) {
   }
   const double f128 = 0.85 * fill(t128, 2);
   if (K >= 512) {
-    const double f256 = 1.0 * fill(t256, 1);
+    const double f256 = (K % (SSTAGES * SBK) == 0 ? 1.3 : 1.0) * fill(t256, 1);
     const double f192 = (a_kc && b_kc && kind == EPI_STORE && N % 192 == 0) ? 0.95 * fill(tl(256, 192), 1)
                                                                             : 0.0;
     if (f192 > f256 && f192 > f128) return {T256x192, 1};
-    if (f256 >= f128) return {T256x256, 1};
+    if (f256 >= f128) return {K % (SSTAGES * SBK) == 0 ? TSCHED : T256x256, 1};
   }
   return {T128x128, 1};
+}
+
+// The scheduled 256 x 256 kernel takes a problem when each split's
+// contraction is a multiple of 128 and every byte offset into an operand
+// fits in 32 bits.
+bool sched_ok(int M, int N, int K, bool a_kc, int lda, bool b_kc, int ldb, int splits) {
+  if (K % splits != 0 || (K / splits) % (SSTAGES * SBK) != 0) return false;
+  auto fits = [&](bool kc, int rows, int ld) {
+    const size_t last = kc ? (size_t)(rows - 1) * ld + K : (size_t)(K - 1) * ld + rows;
+    return last * 2 < (size_t(1) << 32);
+  };
+  return M >= 8 && N >= 8 && fits(a_kc, M, lda) && fits(b_kc, N, ldb);
+}
+
+template <bool AKC, bool BKC, int EPI>
+hipError_t launch_sched(int M, int N, int K, const void* A, int lda, const void* B, int ldb,
+                        const Epi& e, hipStream_t st, int ksplit = 1) {
+  const int tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  hipLaunchKernelGGL((gemm_bf16_sched_kernel<AKC, BKC, EPI>), dim3(tiles * ksplit), dim3(256), 0, st,
+                     M, N, K, (const bf16_t*)A, lda, (const bf16_t*)B, ldb, e, ksplit);
+  return hipGetLastError();
 }
 
 template <bool AKC, bool BKC, int EPI>
@@ -709,6 +880,26 @@ hipError_t launch_bf16(int M, int N, int K, const void* A, int lda, const void* 
                        const Epi& e, hipStream_t st) {
   if (!AKC && e.outT) return hipErrorInvalidValue;  // the transposed copy is token-major only
   const Plan pl = plan(M, N, K, AKC, BKC, EPI, e.ws != nullptr);
+  if (pl.tile == TSCHED) {
+    // operands past the 32-bit offsets: the 2x4-wavefront kernel on the same tiles
+    const bool ok = sched_ok(M, N, K, AKC, lda, BKC, ldb, pl.splits);
+    if constexpr (!AKC && !BKC && EPI == EPI_STORE) {
+      if (pl.splits > 1) {
+        const hipError_t r =
+            ok ? launch_sched<AKC, BKC, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, e, st, pl.splits)
+               : launch_cfg<256, 256, 2, 4, 1, AKC, BKC, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, e, st,
+                                                                       pl.splits);
+        if (r != hipSuccess) return r;
+        const size_t n8 = (size_t)M * N / 8;
+        hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st,
+                           M, N, pl.splits, (const float*)e.ws, (bf16_t*)e.out, e.ldo);
+        return hipGetLastError();
+      }
+    }
+    if (pl.splits > 1) return hipErrorInvalidValue;  // only weight gradients split on these tiles
+    return ok ? launch_sched<AKC, BKC, EPI>(M, N, K, A, lda, B, ldb, e, st)
+              : launch_cfg<256, 256, 2, 4, 1, AKC, BKC, EPI>(M, N, K, A, lda, B, ldb, e, st);
+  }
   if (pl.splits > 1) {
     hipError_t r;
     if constexpr (!AKC && !BKC) {
@@ -746,7 +937,8 @@ hipError_t launch_bf16(int M, int N, int K, const void* A, int lda, const void* 
 
 int gemm_tile_n(int M, int N, int K, bool a_kc, bool b_kc, int kind) {
   switch (plan(M, N, K, a_kc, b_kc, kind, false).tile) {
-    case T256x256: return 256;
+    case T256x256:
+    case TSCHED: return 256;
     case T256x192: return 192;
     default: return 128;
   }
