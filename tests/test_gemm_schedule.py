@@ -1,0 +1,268 @@
+"""Host-side checks of the hand-scheduled GEMM main loop (the inline assembly
+that csrc/gen_gemm_loop.py writes to csrc/gemm_loop.inc).
+
+1. The committed include is what the generator produces.
+2. A symbolic execution of one wavefront's instruction stream (the four
+   wavefronts of a block run the same stream, so what holds for one holds for
+   all) over several contraction lengths, per operand layout, checks:
+   - every MFMA multiplies an A and a B fragment of the same k-tile and
+     16-deep step, both landed (their LDS reads retired by an s_waitcnt), and
+     every accumulator sums each (k-tile, step) exactly once, in order;
+   - an LDS read sees a stage only when the stage's last copy completed on
+     every lane (vmcnt) before a barrier, and reads the fragment its
+     destination registers are meant for;
+   - a copy into a stage is issued only when every read of the stage's
+     previous tile retired before a barrier (no wavefront still reads it);
+   - the copies fetch k-tiles 0, 1, ..., KT-1 in order and then re-fetch the
+     last one; M0 is written, with a wait state, before every copy;
+   - wait counts fit their fields, LDS read offsets fit 16 bits, copy
+     destinations stay inside the 128 KB of stages.
+"""
+import importlib.util
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "transformer_layer_ln_amd", "csrc")
+
+
+def _gen():
+    spec = importlib.util.spec_from_file_location("gen_gemm_loop", os.path.join(CSRC, "gen_gemm_loop.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+GEN = _gen()
+STAGE = GEN.STAGE_BYTES
+
+
+def test_committed_include_matches_generator():
+    with open(os.path.join(CSRC, "gemm_loop.inc")) as f:
+        assert f.read() == GEN.render()
+
+
+class ScheduleError(AssertionError):
+    pass
+
+
+class Wave:
+    """Symbolic state of one wavefront running the loop for KT k-tiles."""
+
+    def __init__(self, layouts, KT):
+        self.lay = layouts                 # {"a": "kc"|"mn", "b": ...}
+        self.KT = KT
+        self.iters = KT // GEN.STAGES
+        self.rem = KT - 1
+        self.src = {(x, q): 0 for x in "AB" for q in range(4)}   # k-tile the copy offset points at
+        self.copied = {(x, q): [] for x in "AB" for q in range(4)}
+        self.t = {"ta": None, "tb": None}
+        self.scc = None
+        self.m0 = None
+        self.lgkm = []       # outstanding LDS reads, oldest first: (regs, content, stage)
+        self.vm = []         # outstanding copies: (stage, x, q)
+        self.regs = {}       # first VGPR of a 2-register half -> (content, landed)
+        self.epoch = 0       # barriers passed
+        self.visible = {s: None for s in range(GEN.STAGES)}       # k-tile readable in a stage
+        self.blocks = {s: {} for s in range(GEN.STAGES)}          # (x, q) -> [tile, complete]
+        self.reads_done = {s: [] for s in range(GEN.STAGES)}      # epochs of retired reads
+        self.reads_open = {s: 0 for s in range(GEN.STAGES)}
+        self.acc = {(i, j): [] for i in range(4) for j in range(4)}
+        self.prev = []       # the last two instructions (M0 hazard check)
+
+    def fail(self, msg):
+        raise ScheduleError(msg)
+
+    # --- memory counters
+    def retire_lgkm(self, n):
+        while len(self.lgkm) > n:
+            regs, content, stage = self.lgkm.pop(0)
+            for r in regs:
+                self.regs[r] = (content, True)
+            self.reads_open[stage] -= 1
+            self.reads_done[stage].append(self.epoch)
+
+    def retire_vm(self, n):
+        while len(self.vm) > n:
+            stage, x, q = self.vm.pop(0)
+            self.blocks[stage][(x, q)][1] = True
+
+    def barrier(self):
+        self.epoch += 1
+        for s, blk in self.blocks.items():
+            tiles = {t for t, _ in blk.values()}
+            if len(blk) == 8 and len(tiles) == 1 and all(c for _, c in blk.values()):
+                self.visible[s] = tiles.pop()
+
+    # --- instructions
+    def ds_read(self, kind, reg, base, off):
+        if off > 65535:
+            self.fail(f"LDS read offset {off} does not fit 16 bits")
+        x, n = base[0], int(base[1:])
+        op = "ab".index(x)
+        hi = n // 2 if self.lay[x] == "kc" else n // 4
+        stage = 2 * hi + off // STAGE
+        if self.lay[x] == "kc":
+            if kind != "ds_read_b128":
+                self.fail("k-contiguous operand read with " + kind)
+            kk, idx, half = n % 2, (off % STAGE) // 2048, None
+            regs = [reg, reg + 2]
+        else:
+            if kind != "ds_read_b64_tr_b16":
+                self.fail("transposed operand read with " + kind)
+            idx, kk, half = n % 4, (off % STAGE) // 8192, (off % 8192) // 2048
+            regs = [reg] if half == 0 else [reg - 2]
+        tile = self.visible[stage]
+        if tile is None:
+            self.fail(f"read of stage {stage} before its copy completed behind a barrier")
+        r0 = regs[0]
+        exp = GEN.freg((r0 - 128) // 64, kk, op, idx)
+        if r0 != exp:
+            self.fail(f"fragment (kk {kk}, op {x}, {idx}) read into v{r0}, expected v{exp}")
+        content = (tile, kk, op, idx)
+        dest = regs if half is None else [reg]
+        for r in dest:
+            self.regs[r] = (content, False)
+        self.lgkm.append((dest, content, stage))
+        self.reads_open[stage] += 1
+
+    def copy(self, x, q):
+        if len(self.prev) < 2 or self.prev[-1] != "s_nop" or self.prev[-2] != "m0":
+            self.fail("copy not preceded by an M0 write and one wait state")
+        mx, moff = self.m0
+        stage, mq = moff // STAGE, (moff % STAGE) // 1024
+        # the last wavefront's block ends at M0 + its 3 * 4 KB + 1 KB
+        if mx != x or mq != q or moff % 1024 or moff + (GEN.B_OFFSET if x == "B" else 0) + 3 * 4096 + 1024 > GEN.STAGES * STAGE:
+            self.fail(f"M0 {self.m0} does not address block {q} of operand {x}")
+        if self.reads_open[stage] or any(e >= self.epoch for e in self.reads_done[stage]):
+            self.fail(f"copy into stage {stage} while a read of its previous tile may be in flight")
+        self.reads_done[stage] = []
+        tile = self.src[(x, q)]
+        self.copied[(x, q)].append(tile)
+        self.visible[stage] = None
+        self.blocks[stage][(x, q)] = [tile, False]
+        self.vm.append((stage, x, q))
+
+    def mfma(self, i, j, rb, ra):
+        ca, cb = [], []
+        for r, out in ((ra, ca), (rb, cb)):
+            for h in (r, r + 2):
+                if h not in self.regs or not self.regs[h][1]:
+                    self.fail(f"MFMA c{i}{j} reads v{h} before its LDS read retired")
+                out.append(self.regs[h][0])
+        if ca[0] != ca[1] or cb[0] != cb[1]:
+            self.fail(f"MFMA c{i}{j}: fragment halves from different reads {ca} {cb}")
+        (ta, ka, oa, ia), (tb, kb, ob, jb) = ca[0], cb[0]
+        if (oa, ob, ia, jb) != (0, 1, i, j) or ta != tb or ka != kb:
+            self.fail(f"MFMA c{i}{j} multiplies A {ca[0]} with B {cb[0]}")
+        self.acc[(i, j)].append((ta, ka))
+
+    def run(self, lines):
+        labels = {l[:-1]: k for k, l in enumerate(lines) if l.endswith(":")}
+        pc, steps = 0, 0
+        while pc < len(lines):
+            steps += 1
+            if steps > 10 ** 6:
+                self.fail("no exit from the loop")
+            line = lines[pc]
+            pc += 1
+            tag = self.step(line)
+            if tag == "branch":
+                pc = labels[line.split()[-1]]
+            self.prev = (self.prev + [tag or line.split()[0]])[-2:]
+
+    def step(self, line):
+        f = line.replace(",", " ").split()
+        op = f[0]
+        if line.endswith(":"):
+            return "label"
+        if op in ("ds_read_b128", "ds_read_b64_tr_b16"):
+            reg = int(re.match(r"v\[(\d+):", f[1]).group(1))
+            base = re.match(r"%\[f([ab]\d)\]", f[2]).group(1)
+            self.ds_read(op, reg, base, int(f[3].split(":")[1]))
+        elif op == "v_mfma_f32_32x32x16_bf16":
+            i, j = int(f[1][3]), int(f[1][4])
+            rb = int(re.match(r"v\[(\d+):", f[2]).group(1))
+            ra = int(re.match(r"v\[(\d+):", f[3]).group(1))
+            self.mfma(i, j, rb, ra)
+        elif op == "s_waitcnt":
+            for part in f[1:]:
+                name, n = re.match(r"(\w+)\((\d+)\)", part).groups()
+                n = int(n)
+                if name == "lgkmcnt":
+                    if n > 15:
+                        self.fail("lgkmcnt field is 4 bits")
+                    self.retire_lgkm(n)
+                else:
+                    if n > 63:
+                        self.fail("vmcnt field is 6 bits")
+                    self.retire_vm(n)
+        elif op == "s_barrier":
+            self.barrier()
+        elif op == "s_add_u32" and f[1] == "m0":
+            self.m0 = (re.match(r"%\[lds([AB])\]", f[2]).group(1), int(f[3]))
+            return "m0"
+        elif op == "s_nop":
+            return "s_nop"
+        elif op == "global_load_lds_dwordx4":
+            x, q = re.match(r"%\[vo([AB])(\d)\]", f[1]).groups()
+            self.copy(x, int(q))
+        elif op == "s_cmp_gt_i32":
+            self.scc = (self.rem if f[1] == "%[rem]" else self.iters) > 0
+        elif op == "s_cselect_b32":
+            self.t[f[1][2:-1]] = 1 if self.scc else 0
+        elif op == "s_sub_i32":
+            if f[1] == "%[rem]":
+                self.rem -= 1
+            else:
+                self.iters -= 1
+        elif op == "v_add_u32":
+            x, q = re.match(r"%\[vo([AB])(\d)\]", f[1]).groups()
+            self.src[(x, int(q))] += self.t[f[2][2:-1]]
+        elif op == "s_cbranch_scc1":
+            return "branch" if self.scc else "fallthrough"
+        else:
+            self.fail("unmodelled instruction: " + line)
+        return None
+
+
+@pytest.mark.parametrize("name,la,lb", GEN.LAYOUTS)
+@pytest.mark.parametrize("KT", [4, 8, 12, 32])
+def test_schedule_symbolic_execution(name, la, lb, KT):
+    lines = GEN.loop(la, lb)
+    assert lines[0] == "s_nop 4" and lines[-3:] == ["s_nop 7"] * 3   # accumulator hazards
+    w = Wave({"a": la, "b": lb}, KT)
+    w.run(lines)
+    assert not w.lgkm and not w.vm, "memory operations outstanding at the end"
+    want = [(t, kk) for t in range(KT) for kk in (0, 1)]
+    for ij, got in w.acc.items():
+        assert got == want, f"accumulator c{ij[0]}{ij[1]}"
+    for key, tiles in w.copied.items():
+        n = len(tiles)
+        assert tiles == list(range(KT)) + [KT - 1] * (n - KT), f"copy sequence of {key}: {tiles}"
+
+
+def test_symbolic_execution_catches_a_short_wait():
+    """The checker itself: dropping the wait before the second step's MFMAs
+    (an MFMA would use fragments still in flight) must be reported."""
+    la, lb = "kc", "kc"
+    lines = GEN.loop(la, lb)
+    waits = [k for k, l in enumerate(lines) if l.startswith("s_waitcnt lgkmcnt")]
+    bad = lines[:waits[2]] + lines[waits[2] + 1:]
+    with pytest.raises(ScheduleError, match="before its LDS read retired"):
+        Wave({"a": la, "b": lb}, 8).run(bad)
+
+
+def test_symbolic_execution_catches_an_early_copy():
+    """Moving a barrier behind the copies of a tile (a wavefront could still
+    read the stage being overwritten, or read a stage whose copy has not
+    landed) must be reported."""
+    la, lb = "kc", "mn"
+    lines = GEN.loop(la, lb)
+    loop_start = lines.index("L%=_ktile:")
+    k = lines.index("s_barrier", loop_start)
+    bad = lines[:k] + lines[k + 1:]
+    with pytest.raises(ScheduleError):
+        Wave({"a": la, "b": lb}, 8).run(bad)

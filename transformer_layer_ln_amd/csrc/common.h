@@ -104,12 +104,29 @@ MTB_DEV float wave_max(float v) {
 MTB_DEV float exp_fast(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 MTB_DEV float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// exact GELU u * Phi(u), with the device erf
-MTB_DEV float gelu_f(float u) { return 0.5f * u * (1.0f + erff(u * 0.70710678118654752f)); }
+// erf(x) from Abramowitz & Stegun, Handbook of Mathematical Functions, eq.
+// 7.1.26 (absolute error <= 1.5e-7): for x >= 0, 1 - (a1 t + a2 t^2 + a3 t^3 +
+// a4 t^4 + a5 t^5) exp(-x^2) with t = 1 / (1 + p x); odd in x. One branch-free
+// path (hardware reciprocal and exp2), so the GEMM epilogues that apply GELU
+// to every output element stay cheap. Also returns e = exp(-x^2).
+MTB_DEV float erf_as(float x, float& e) {
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, fabsf(x), 1.0f));
+  e = __builtin_amdgcn_exp2f(-x * x * 1.4426950408889634f);
+  const float poly =
+      t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, 1.061405429f, -1.453152027f), 1.421413741f), -0.284496736f),
+               0.254829592f);
+  return copysignf(1.0f - poly * e, x);
+}
+// exact-form GELU u * Phi(u), Phi(u) = (1 + erf(u / sqrt 2)) / 2
+MTB_DEV float gelu_f(float u) {
+  float e;
+  return 0.5f * u * (1.0f + erf_as(u * 0.70710678118654752f, e));
+}
+// GELU'(u) = Phi(u) + u phi(u); phi(u) = exp(-u^2 / 2) / sqrt(2 pi) is the e of erf_as
 MTB_DEV float gelu_grad_f(float u) {
-  float cdf = 0.5f * (1.0f + erff(u * 0.70710678118654752f));
-  float pdf = 0.39894228040143268f * expf(-0.5f * u * u);
-  return cdf + u * pdf;
+  float e;
+  const float cdf = 0.5f * (1.0f + erf_as(u * 0.70710678118654752f, e));
+  return cdf + u * 0.39894228040143268f * e;
 }
 MTB_DEV float sigmoid_f(float u) { return 1.0f / (1.0f + expf(-u)); }
 

@@ -844,12 +844,15 @@ Plan plan(int M, int N, int K, bool a_kc, bool b_kc, int kind, bool split_ok) {
     if (s > 1) return {T128x128, s};
   }
   const double f128 = 0.85 * fill(t128, 2);
+  // the scheduled kernel's fixed per-block costs (one wavefront per SIMD to hide the first copies
+  // and the epilogue) outweigh its faster loop below 1024-deep contractions
+  const bool sk = K % (SSTAGES * SBK) == 0 && K >= 1024;
   if (K >= 512) {
-    const double f256 = (K % (SSTAGES * SBK) == 0 ? 1.3 : 1.0) * fill(t256, 1);
+    const double f256 = (sk ? 1.3 : 1.0) * fill(t256, 1);
     const double f192 = (a_kc && b_kc && kind == EPI_STORE && N % 192 == 0) ? 0.95 * fill(tl(256, 192), 1)
                                                                             : 0.0;
     if (f192 > f256 && f192 > f128) return {T256x192, 1};
-    if (f256 >= f128) return {K % (SSTAGES * SBK) == 0 ? TSCHED : T256x256, 1};
+    if (f256 >= f128) return {sk ? TSCHED : T256x256, 1};
   }
   return {T128x128, 1};
 }

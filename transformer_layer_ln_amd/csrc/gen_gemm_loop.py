@@ -130,7 +130,11 @@ def interleave(a, b):
     return out
 
 
-def loop(la, lb):
+def loop(la, lb, reads_first=False, copies_step=0):
+    """the asm lines for operand layouts la, lb ("kc" / "mn"). The defaults are
+    the schedule described above; reads_first issues a step's fragment reads
+    right after its first MFMA instead of spreading them, copies_step = 1 moves
+    the copies into the second step (measurement variants)."""
     nread = sum(4 if l == "kc" else 8 for l in (la, lb))   # LDS reads per 16-deep step
     wait_step = f"s_waitcnt lgkmcnt({min(nread, 15)})"
     L = ["s_nop 4"]   # accumulator initialisation (VALU/AGPR writes) -> MFMA
@@ -150,29 +154,42 @@ def loop(la, lb):
         L.append(f"s_waitcnt vmcnt({8 * (STAGES - 3)})")
         L.append("s_barrier")
         L.append(wait_step)
-        r0 = reads(la, 0, Y, nxt, 0) + reads(lb, 1, Y, nxt, 0)
-        L += spread([mfma(X, 0, i, j) for i, j in pairs], interleave(r0, copies(dst)) + [advance()])
-        L.append(wait_step)
-        r1 = reads(la, 0, Y, nxt, 1) + reads(lb, 1, Y, nxt, 1)
-        L += spread([mfma(X, 1, i, j) for i, j in pairs], r1)
+        for kk in range(2):
+            r = reads(la, 0, Y, nxt, kk) + reads(lb, 1, Y, nxt, kk)
+            c = copies(dst) + [advance()] if kk == copies_step else []
+            m = [mfma(X, kk, i, j) for i, j in pairs]
+            if reads_first:
+                L += [m[0]] + [x for u in r for x in u] + spread(m[1:], c)
+            else:
+                L += spread(m, interleave(r, c[:-1]) + c[-1:] if c else r)
+            if kk == 0:
+                L.append(wait_step)
     L += ["s_sub_i32 %[iters], %[iters], 1", "s_cmp_gt_i32 %[iters], 0", "s_cbranch_scc1 L%=_ktile"]
     L.append("s_waitcnt vmcnt(0) lgkmcnt(0)")
     L += ["s_nop 7"] * 3   # last MFMAs -> accumulator reads by the epilogue
     return L
 
 
-def main():
-    here = os.path.dirname(os.path.abspath(__file__))
+LAYOUTS = (("NT", "kc", "kc"), ("NN", "kc", "mn"), ("TN", "mn", "mn"))
+
+
+def render():
+    """the text of gemm_loop.inc"""
     out = ["// Generated by gen_gemm_loop.py (the schedule is described there); do not edit.", ""]
-    for name, la, lb in (("NT", "kc", "kc"), ("NN", "kc", "mn"), ("TN", "mn", "mn")):
+    for name, la, lb in LAYOUTS:
         out.append(f"#define MTB_GEMM_LOOP_{name} \\")
         for line in loop(la, lb):
             out.append(f'  "{line}\\n" \\')
         out.append("")
     regs = ", ".join(f'"v{r}"' for r in range(128, 256))
     out.append(f"#define MTB_GEMM_LOOP_CLOBBERS {regs}")
+    return "\n".join(out) + "\n"
+
+
+def main():
+    here = os.path.dirname(os.path.abspath(__file__))
     with open(os.path.join(here, "gemm_loop.inc"), "w") as f:
-        f.write("\n".join(out) + "\n")
+        f.write(render())
 
 
 if __name__ == "__main__":
