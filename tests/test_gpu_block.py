@@ -67,6 +67,25 @@ def test_bf16_small_shapes(i):
     check_rank_vs_oracle(cfg, w, x, G)
 
 
+# Shapes that reach the hand-scheduled 256 x 256 GEMM (contractions that are
+# multiples of 128 and at least 1024 deep) with ragged edges: 4032 tokens
+# (fc1 forward, fc2 dgrad: token rows past the last full tile), and ragged
+# weight dimensions 2112 x 1344 for the weight gradients, whose contraction
+# (4096 tokens) is split four ways.
+SCHED_RAGGED = [
+    dict(batch=3, seq=1344, hidden=1280, q_heads=10, kv_heads=2, head_dim=128, ffn=3072, causal=True),
+    dict(batch=2, seq=2048, hidden=1344, q_heads=21, kv_heads=3, head_dim=64, ffn=2112, bias=True,
+         affine=True),
+]
+
+
+@pytest.mark.parametrize("i", range(len(SCHED_RAGGED)))
+def test_bf16_scheduled_gemm_ragged_shapes(i):
+    cfg = inputs.BlockConfig(f"bf16-sched-ragged-{i}", dtype="bf16", tp=1, seed=2100 + i, **SCHED_RAGGED[i])
+    w, x, G = _case(cfg)
+    check_rank_vs_oracle(cfg, w, x, G)
+
+
 def test_c2_rank_share():
     cfg = inputs.C2
     w, x, G = _case(cfg)
