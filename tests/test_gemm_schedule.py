@@ -14,7 +14,8 @@ that csrc/gen_gemm_loop.py writes to csrc/gemm_loop.inc).
    - a copy into a stage is issued only when every read of the stage's
      previous tile retired before a barrier (no wavefront still reads it);
    - the copies fetch k-tiles 0, 1, ..., KT-1 in order and then re-fetch the
-     last one; M0 is written, with a wait state, before every copy;
+     last one, for any KT (the body is entered at slot -KT mod 4); M0 is
+     written, with a wait state, before every copy;
    - wait counts fit their fields, LDS read offsets fit 16 bits, copy
      destinations stay inside the 128 KB of stages.
 """
@@ -54,7 +55,8 @@ class Wave:
     def __init__(self, layouts, KT):
         self.lay = layouts                 # {"a": "kc"|"mn", "b": ...}
         self.KT = KT
-        self.iters = KT // GEN.STAGES
+        self.first = -KT % GEN.STAGES     # the body slot k-tile 0 runs in
+        self.iters = (KT + self.first) // GEN.STAGES
         self.rem = KT - 1
         self.src = {(x, q): 0 for x in "AB" for q in range(4)}   # k-tile the copy offset points at
         self.copied = {(x, q): [] for x in "AB" for q in range(4)}
@@ -169,7 +171,7 @@ class Wave:
             line = lines[pc]
             pc += 1
             tag = self.step(line)
-            if tag == "branch":
+            if tag in ("branch", "jump"):
                 pc = labels[line.split()[-1]]
             self.prev = (self.prev + [tag or line.split()[0]])[-2:]
 
@@ -211,6 +213,10 @@ class Wave:
             self.copy(x, int(q))
         elif op == "s_cmp_gt_i32":
             self.scc = (self.rem if f[1] == "%[rem]" else self.iters) > 0
+        elif op == "s_cmp_eq_u32" and f[1] == "%[first]":
+            self.scc = self.first == int(f[2])
+        elif op == "s_branch":
+            return "jump"
         elif op == "s_cselect_b32":
             self.t[f[1][2:-1]] = 1 if self.scc else 0
         elif op == "s_sub_i32":
@@ -229,7 +235,7 @@ class Wave:
 
 
 @pytest.mark.parametrize("name,la,lb", GEN.LAYOUTS)
-@pytest.mark.parametrize("KT", [4, 8, 12, 32])
+@pytest.mark.parametrize("KT", [1, 2, 3, 4, 5, 6, 7, 8, 13, 32, 501])
 def test_schedule_symbolic_execution(name, la, lb, KT):
     lines = GEN.loop(la, lb)
     assert lines[0] == "s_nop 4" and lines[-3:] == ["s_nop 7"] * 3   # accumulator hazards

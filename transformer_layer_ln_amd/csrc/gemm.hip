@@ -597,7 +597,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(int M, i
 
 // 256 x 256 tile, 4 wavefronts (2 x 2) of 128 x 128 each, with the hand-scheduled
 // main loop of gemm_loop.inc (schedule and LDS layout: gen_gemm_loop.py).
-// Needs each split's contraction to be a multiple of 128 and every operand
+// Needs each split's contraction to be a multiple of 32 and every operand
 // byte offset below 2^32 (sched_ok).
 constexpr int SBK = 32, SSTAGES = 4;
 
@@ -673,7 +673,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_sched_kernel(int M, int N, i
   frag_bases(BKC, wn, B_OFF, fb);
 
   const int KT = kspan / SBK;
-  int rem = KT - 1, iters = KT / SSTAGES;
+  const int first = (SSTAGES - KT % SSTAGES) % SSTAGES;  // body slot of k-tile 0
+  int rem = KT - 1, iters = (KT + first) / SSTAGES;
   uint32_t ta, tb;
   f32x16 acc[4][4];
 #pragma unroll
@@ -691,7 +692,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_sched_kernel(int M, int N, i
     [voB0] "+v"(voB[0]), [voB1] "+v"(voB[1]), [voB2] "+v"(voB[2]), [voB3] "+v"(voB[3]),            \
     [rem] "+s"(rem), [iters] "+s"(iters), [ta] "=&s"(ta), [tb] "=&s"(tb)                           \
   : [ldsA] "s"(ldsA), [ldsB] "s"(ldsB), [sbA] "s"(sbA), [sbB] "s"(sbB), [ksA] "s"(ksA),            \
-    [ksB] "s"(ksB), [fa0] "v"(fa[0]), [fa1] "v"(fa[1]), [fa2] "v"(fa[2]), [fa3] "v"(fa[3]),        \
+    [ksB] "s"(ksB), [first] "s"(first), [fa0] "v"(fa[0]), [fa1] "v"(fa[1]), [fa2] "v"(fa[2]), [fa3] "v"(fa[3]),        \
     [fa4] "v"(fa[4]), [fa5] "v"(fa[5]), [fa6] "v"(fa[6]), [fa7] "v"(fa[7]), [fb0] "v"(fb[0]),      \
     [fb1] "v"(fb[1]), [fb2] "v"(fb[2]), [fb3] "v"(fb[3]), [fb4] "v"(fb[4]), [fb5] "v"(fb[5]),      \
     [fb6] "v"(fb[6]), [fb7] "v"(fb[7])                                                             \
@@ -796,16 +797,16 @@ struct Plan {
 // launch and the workspace query use. Candidates (relative per-tile rates
 // measured on MI355X over the block's GEMM shapes, times the fraction of the
 // chip their tile count fills): the scheduled 256x256 kernel (4 wavefronts,
-// gen_gemm_loop.py) when the contraction is a multiple of 128, 1.2-1.5x the
-// 2x4-wavefront 256x256 kernel; 256x192 (4x2 wavefronts) when N splits into
-// 192-wide tiles (plain store); 128x128 (2x2, two blocks per CU). Weight
-// gradients (both operands transposed in LDS) take the scheduled kernel with
-// the contraction split until the blocks fill 3/4 of the chip; without it,
-// 256x128 (4x2) when it fills the chip, else 128x128 (at two blocks per CU
-// those beat a partly filled 256x128 grid: 158 vs 175 us for the 1536 x 4096
-// x 8192 QKV weight gradient). Tiles for 6 wavefronts fill the chip better at
-// N = 1536 but leave two of a CU's four SIMDs with twice the work: measured
-// slower.
+// gen_gemm_loop.py) when the contraction is a multiple of 32 and at least 1024
+// deep, 1.2-1.5x the 2x4-wavefront 256x256 kernel; 256x192 (4x2 wavefronts)
+// when N splits into 192-wide tiles (plain store); 128x128 (2x2, two blocks
+// per CU). Weight gradients (both operands transposed in LDS) take the
+// scheduled kernel with the contraction split until the blocks fill 3/4 of
+// the chip; without it, 256x128 (4x2) when it fills the chip, else 128x128 (at
+// two blocks per CU those beat a partly filled 256x128 grid: 158 vs 175 us for
+// the 1536 x 4096 x 8192 QKV weight gradient). Tiles for 6 wavefronts fill the
+// chip better at N = 1536 but leave two of a CU's four SIMDs with twice the
+// work: measured slower.
 //
 // Split contraction (needs a workspace, `split_ok`; plain stores only): a
 // deep product whose tiles leave at least half of the chip's block slots idle
@@ -819,10 +820,10 @@ struct Plan {
 Plan plan(int M, int N, int K, bool a_kc, bool b_kc, int kind, bool split_ok) {
   auto tl = [&](int bm, int bn) { return (long)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
   auto depth_ok = [&](int s) { return K % (s * BK) == 0 && K / s >= 1024; };
-  auto sched_depth = [&](int s) { return K % (s * SSTAGES * SBK) == 0 && K / s >= 1024; };
+  auto sched_depth = [&](int s) { return K % (s * SBK) == 0 && K / s >= 1024; };
   const long t256 = tl(256, 256);
   if (!a_kc && !b_kc) {
-    if (K % (SSTAGES * SBK) == 0) {
+    if (K % SBK == 0) {
       int s = 1;
       if (split_ok && kind == EPI_STORE)
         while (s < 8 && t256 * s * 4 < 3L * kCUs && sched_depth(2 * s)) s *= 2;
@@ -846,7 +847,7 @@ Plan plan(int M, int N, int K, bool a_kc, bool b_kc, int kind, bool split_ok) {
   const double f128 = 0.85 * fill(t128, 2);
   // the scheduled kernel's fixed per-block costs (one wavefront per SIMD to hide the first copies
   // and the epilogue) outweigh its faster loop below 1024-deep contractions
-  const bool sk = K % (SSTAGES * SBK) == 0 && K >= 1024;
+  const bool sk = K % SBK == 0 && K >= 1024;
   if (K >= 512) {
     const double f256 = (sk ? 1.3 : 1.0) * fill(t256, 1);
     const double f192 = (a_kc && b_kc && kind == EPI_STORE && N % 192 == 0) ? 0.95 * fill(tl(256, 192), 1)
@@ -858,10 +859,10 @@ Plan plan(int M, int N, int K, bool a_kc, bool b_kc, int kind, bool split_ok) {
 }
 
 // The scheduled 256 x 256 kernel takes a problem when each split's
-// contraction is a multiple of 128 and every byte offset into an operand
-// fits in 32 bits.
+// contraction is a multiple of 32 and every byte offset into an operand fits
+// in 32 bits.
 bool sched_ok(int M, int N, int K, bool a_kc, int lda, bool b_kc, int ldb, int splits) {
-  if (K % splits != 0 || (K / splits) % (SSTAGES * SBK) != 0) return false;
+  if (K % splits != 0 || (K / splits) % SBK != 0) return false;
   auto fits = [&](bool kc, int rows, int ld) {
     const size_t last = kc ? (size_t)(rows - 1) * ld + K : (size_t)(K - 1) * ld + rows;
     return last * 2 < (size_t(1) << 32);

@@ -32,11 +32,15 @@ between tiles, so every read has a whole tile of MFMAs to land in. The loop
 body covers 4 tiles (one per stage, so that all LDS offsets are immediates).
 Copies past the last tile re-read the last tile (the source offset stops
 advancing), which keeps the wait counts uniform; those stages are never used.
+A contraction of KT 32-deep tiles that is not a multiple of 4 enters the body
+at slot (-KT mod 4) (one prologue per entry slot), so every k-tile count ends
+with the body's last slot.
 
 Operands of the asm block (names used below):
   c00..c33   accumulators ("+a", f32x16), cIJ = A fragment I x B fragment J
   voA0..3, voB0..3  per-lane byte offsets of this wavefront's 4 copy blocks
   rem        copies left before the source stops advancing; iters: loop count
+             (passes over the body, the first one entered at slot `first`)
   ta, tb     scratch SGPRs
   ldsA/ldsB  LDS byte address of this wavefront's first copy block in stage 0
   sbA/sbB    global base addresses; ksA/ksB: bytes per 32-deep k-tile
@@ -138,19 +142,29 @@ def loop(la, lb, reads_first=False, copies_step=0):
     nread = sum(4 if l == "kc" else 8 for l in (la, lb))   # LDS reads per 16-deep step
     wait_step = f"s_waitcnt lgkmcnt({min(nread, 15)})"
     L = ["s_nop 4"]   # accumulator initialisation (VALU/AGPR writes) -> MFMA
-    for st in range(STAGES - 1):
-        for u in copies(st):
-            L += u
-        L += advance()
-    L.append(f"s_waitcnt vmcnt({8 * (STAGES - 2)})")
-    L.append("s_barrier")
-    for kk in range(2):
-        for u in reads(la, 0, 0, 0, kk) + reads(lb, 1, 0, 0, kk):
-            L += u
+    # k-tile 0 runs in slot `first` of the 4-slot body (first = -KT mod 4), so
+    # that any number of k-tiles ends with the body's last slot: one prologue
+    # per entry slot
+    for f in range(1, STAGES):
+        L += [f"s_cmp_eq_u32 %[first], {f}", f"s_cbranch_scc1 L%=_pro{f}"]
+    for f in range(STAGES):
+        if f:
+            L.append(f"L%=_pro{f}:")
+        for t in range(STAGES - 1):
+            for u in copies((f + t) % STAGES):
+                L += u
+            L += advance()
+        L.append(f"s_waitcnt vmcnt({8 * (STAGES - 2)})")
+        L.append("s_barrier")
+        for kk in range(2):
+            for u in reads(la, 0, f & 1, f, kk) + reads(lb, 1, f & 1, f, kk):
+                L += u
+        L.append(f"s_branch L%=_slot{f}")
     L.append("L%=_ktile:")
     for u in range(STAGES):
         X, Y = u & 1, (u + 1) & 1
         nxt, dst = (u + 1) % STAGES, (u + STAGES - 1) % STAGES
+        L.append(f"L%=_slot{u}:")
         L.append(f"s_waitcnt vmcnt({8 * (STAGES - 3)})")
         L.append("s_barrier")
         L.append(wait_step)
