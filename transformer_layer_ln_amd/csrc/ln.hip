@@ -15,6 +15,20 @@ namespace {
 
 constexpr int kRowsPerBlock = 4;  // 4 wavefronts, one row each
 
+// 8 elements of a stream read once (nontemporal hint: no point keeping it in L2)
+template <typename T> MTB_DEV void ld8s(const T* p, float (&v)[8]);
+template <> MTB_DEV void ld8s<bf16_t>(const bf16_t* p, float (&v)[8]) {
+  const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { v[2 * i] = lo_f(q[i]); v[2 * i + 1] = hi_f(q[i]); }
+}
+template <> MTB_DEV void ld8s<float>(const float* p, float (&v)[8]) {
+  const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
+}
+
 // NC = number of 8-element chunks per lane (H <= 512 * NC)
 template <typename T, int NC>
 __global__ __launch_bounds__(256) void ln_fwd_kernel(int rows, int H, const T* __restrict__ x,
@@ -128,14 +142,14 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(int rows, int H, const T* _
     const int col = (c * 64 + lane) * 8;
     if (col < H) {
       float hv[8];
-      ld8(dy + base + col, gh[c]);
+      ld8s(dy + base + col, gh[c]);
       if constexpr (DY2) {
         float d2[8];
-        ld8(dy2 + base + col, d2);
+        ld8s(dy2 + base + col, d2);
 #pragma unroll
         for (int e = 0; e < 8; ++e) gh[c][e] += d2[e];
       }
-      ld8(hin + base + col, hv);
+      ld8s(hin + base + col, hv);
       if (g) {
         float gg[8];
         ld8(g + col, gg);
@@ -158,7 +172,7 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(int rows, int H, const T* _
     const int col = (c * 64 + lane) * 8;
     if (col < H) {
       float o[8], d0[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      if constexpr (DRES) ld8(dres + base + col, d0);
+      if constexpr (DRES) ld8s(dres + base + col, d0);
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = d0[e] + r * (gh[c][e] - mg - xh[c][e] * mgx);
       st8(dx + base + col, o);
