@@ -6,6 +6,8 @@
 // LayerNorm: [Lab06] sec. 2 steps (2) and (5) -- F.layer_norm over the hidden
 // dimension: per-token mean and biased variance, (x - mean) / sqrt(var + eps),
 // optional gain/shift.
+#include <algorithm>
+
 #include "common.h"
 #include "drop.h"
 #include "kernels.h"
@@ -29,7 +31,32 @@ template <> MTB_DEV void ld8s<float>(const float* p, float (&v)[8]) {
   for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
 }
 
-// NC = number of 8-element chunks per lane (H <= 512 * NC)
+// 8 elements of a row as loaded (bf16: one 16-byte word; fp32: two), unpacked later
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16_t> {
+  u32x4 q;
+  MTB_DEV void load(const bf16_t* p) { q = *reinterpret_cast<const u32x4*>(p); }
+  MTB_DEV void get(float (&v)[8]) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[2 * i] = lo_f(q[i]); v[2 * i + 1] = hi_f(q[i]); }
+  }
+};
+template <> struct Raw8<float> {
+  f32x4 a, b;
+  MTB_DEV void load(const float* p) {
+    a = *reinterpret_cast<const f32x4*>(p);
+    b = *reinterpret_cast<const f32x4*>(p + 4);
+  }
+  MTB_DEV void get(float (&v)[8]) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
+  }
+};
+
+// NC = number of 8-element chunks per lane (H <= 512 * NC). Each wavefront
+// walks rows row0, row0 + stride, ...; the next row's x (and residual) are
+// loaded before the current row is reduced and stored, so that the grid's
+// reads and writes overlap instead of running as one burst each.
 template <typename T, int NC>
 __global__ __launch_bounds__(256) void ln_fwd_kernel(int rows, int H, const T* __restrict__ x,
                                                      const T* __restrict__ resid,
@@ -40,81 +67,97 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(int rows, int H, const T* _
                                                      float* __restrict__ rstd_out, float eps,
                                                      Drop drop) {
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  const size_t base = (size_t)row * H;
-  float v[NC][8];
-  float s = 0.f;
+  const int row0 = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  const int stride = gridDim.x * kRowsPerBlock;
+  Raw8<T> xr[NC], rr[NC];
+  auto fetch = [&](int row) {
+    const size_t base = (size_t)row * H;
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int col = (c * 64 + lane) * 8;
-    if (col < H) {
-      ld8(x + base + col, v[c]);
-      if (resid || bias) {
-        // x + dropout(resid + bias)
-        float r[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (resid) ld8(resid + base + col, r);
-        if (bias) {
-          float bb[8];
-          ld8(bias + col, bb);
+    for (int c = 0; c < NC; ++c) {
+      const int col = (c * 64 + lane) * 8;
+      if (col < H) {
+        xr[c].load(x + base + col);
+        if (resid) rr[c].load(resid + base + col);
+      }
+    }
+  };
+  if (row0 < rows) fetch(row0);
+  for (int row = row0; row < rows; row += stride) {
+    const size_t base = (size_t)row * H;
+    float v[NC][8];
+    float s = 0.f;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) r[e] += bb[e];
+    for (int c = 0; c < NC; ++c) {
+      const int col = (c * 64 + lane) * 8;
+      if (col < H) {
+        xr[c].get(v[c]);
+        if (resid || bias) {
+          // x + dropout(resid + bias)
+          float r[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+          if (resid) rr[c].get(r);
+          if (bias) {
+            float bb[8];
+            ld8(bias + col, bb);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) r[e] += bb[e];
+          }
+          if (drop.thr) drop_apply8(drop, (uint64_t)base + col, r);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[c][e] += r[e];
+          // the stored residual stream and the statistics see the same values
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            T t;
+            st_f(&t, v[c][e]);
+            v[c][e] = ld_f(&t);
+          }
+          if (h_out) st8(h_out + base + col, v[c]);
         }
-        if (drop.thr) drop_apply8(drop, (uint64_t)base + col, r);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[c][e] += r[e];
-        // the stored residual stream and the statistics see the same values
+        for (int e = 0; e < 8; ++e) s += v[c][e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[c][e] = 0.f;
+      }
+    }
+    if (row + stride < rows) fetch(row + stride);
+    const float inv_h = 1.0f / (float)H;
+    const float mean = wave_sum(s) * inv_h;
+    float q = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int col = (c * 64 + lane) * 8;
+      if (col < H) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          T t;
-          st_f(&t, v[c][e]);
-          v[c][e] = ld_f(&t);
+          const float d = v[c][e] - mean;
+          q += d * d;
         }
-        if (h_out) st8(h_out + base + col, v[c]);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s += v[c][e];
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[c][e] = 0.f;
-    }
-  }
-  const float inv_h = 1.0f / (float)H;
-  const float mean = wave_sum(s) * inv_h;
-  float q = 0.f;
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int col = (c * 64 + lane) * 8;
-    if (col < H) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float d = v[c][e] - mean;
-        q += d * d;
       }
     }
-  }
-  const float var = wave_sum(q) * inv_h;
-  const float rstd = 1.0f / sqrtf(var + eps);
+    const float var = wave_sum(q) * inv_h;
+    const float rstd = 1.0f / sqrtf(var + eps);
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int col = (c * 64 + lane) * 8;
-    if (col < H) {
-      float o[8];
+    for (int c = 0; c < NC; ++c) {
+      const int col = (c * 64 + lane) * 8;
+      if (col < H) {
+        float o[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = (v[c][e] - mean) * rstd;
-      if (g) {
-        float gg[8], bb[8];
-        ld8(g + col, gg);
-        ld8(b + col, bb);
+        for (int e = 0; e < 8; ++e) o[e] = (v[c][e] - mean) * rstd;
+        if (g) {
+          float gg[8], bb[8];
+          ld8(g + col, gg);
+          ld8(b + col, bb);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = o[e] * gg[e] + bb[e];
+          for (int e = 0; e < 8; ++e) o[e] = o[e] * gg[e] + bb[e];
+        }
+        st8(y + base + col, o);
       }
-      st8(y + base + col, o);
     }
-  }
-  if (lane == 0) {
-    mu_out[row] = mean;
-    rstd_out[row] = rstd;
+    if (lane == 0) {
+      mu_out[row] = mean;
+      rstd_out[row] = rstd;
+    }
   }
 }
 
@@ -286,11 +329,15 @@ __global__ __launch_bounds__(256) void act_bwd_kernel(int act, size_t total, int
   }
 }
 
+// forward grid: at most LN_FWD_BLOCKS blocks (4 rows of each in flight), so
+// that large row counts give each wavefront several rows to pipeline
+constexpr int LN_FWD_BLOCKS = 512;
+
 template <typename T, int NC>
 hipError_t ln_fwd_t(int rows, int H, const void* x, const void* resid, const void* bias,
                     const void* g, const void* b, void* h_out, void* y, float* mu, float* rstd,
                     float eps, const Drop& drop, hipStream_t st) {
-  dim3 grid((rows + kRowsPerBlock - 1) / kRowsPerBlock);
+  dim3 grid(std::min((rows + kRowsPerBlock - 1) / kRowsPerBlock, LN_FWD_BLOCKS));
   hipLaunchKernelGGL((ln_fwd_kernel<T, NC>), grid, dim3(256), 0, st, rows, H, (const T*)x,
                      (const T*)resid, (const T*)bias, (const T*)g, (const T*)b, (T*)h_out, (T*)y,
                      mu, rstd, eps, drop);
