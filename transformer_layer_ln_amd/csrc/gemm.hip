@@ -1,15 +1,22 @@
 // GEMMs of the block: C[m][n] = sum_k A(m,k) B(n,k) with fused epilogues.
 //
-// bf16 path: gfx950 MFMA v_mfma_f32_32x32x16_bf16, a grid of 2x2, 2x4 or
-// 4x2 wavefronts per block, block tile BM x BN x 64, LDS double-buffered (one barrier per
-// k-step: the next tile is fetched into registers while the current one is
-// multiplied, then written to the other LDS buffer). A k-contiguous operand
-// sits in LDS as [row][k] with 16-byte chunks XOR-swizzled by row, so a
-// fragment is one ds_read_b128 per lane. An operand whose contraction index
-// is not the contiguous one (dgrad's weight, both wgrad operands) is copied
-// as it is, [k][row], and its fragments come from two LDS transpose reads
-// (ds_read_b64_tr_b16) per lane: no register transposes (measured 6 % faster
-// on the weight gradients than transposing in registers on the way to LDS).
+// bf16 path, gfx950 MFMA v_mfma_f32_32x32x16_bf16, two kernels:
+//  * gemm_bf16_sched_kernel (contractions >= 1024 deep, multiples of 32): a
+//    256 x 256 tile on 4 wavefronts of 128 x 128, its k-loop one hand-scheduled
+//    inline-assembly block (gemm_loop.inc, written by gen_gemm_loop.py, which
+//    describes the schedule): direct-to-LDS copies three 32-deep k-tiles
+//    ahead, fragments read a whole k-tile before their MFMAs;
+//  * gemm_bf16_kernel (the other shapes): a grid of 2x2, 2x4 or 4x2
+//    wavefronts per block, block tile BM x BN x 64, LDS double-buffered (one
+//    barrier per k-step: the next tile is fetched into registers while the
+//    current one is multiplied, then written to the other LDS buffer).
+// In both, a k-contiguous operand sits in LDS as [row][k] with 16-byte chunks
+// XOR-swizzled by row, so a fragment is one ds_read_b128 per lane. An operand
+// whose contraction index is not the contiguous one (dgrad's weight, both
+// wgrad operands) is copied as it is, [k][row], and its fragments come from
+// two LDS transpose reads (ds_read_b64_tr_b16) per lane: no register
+// transposes (measured 6 % faster on the weight gradients than transposing in
+// registers on the way to LDS).
 //
 // The MFMA is issued as (B-fragment, A-fragment), i.e. it computes C^T, so
 // that each lane ends up holding 4 consecutive n of one row m.
