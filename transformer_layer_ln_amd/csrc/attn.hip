@@ -73,13 +73,19 @@ MTB_DEV bf16x8 frag(const bf16_t* s, int row, int c) {
 }
 
 // linear workgroup id -> (tile along the sequence, batch*head). Causal
-// workloads put heavy tiles in the first half of the grid (heaviest first)
-// and light tiles in the second half (lightest first): the two workgroups a
-// CU holds together then carry about the same total work.
+// workloads order the tiles by their work. With two workgroups per CU
+// (paired), heavy tiles fill the first half of the grid (heaviest first) and
+// light tiles the second half (lightest first): the two workgroups a CU holds
+// together then carry about the same total work. With one workgroup per CU
+// the whole grid goes heaviest first, so that each CU that frees up takes the
+// heaviest tile left (longest-processing-time-first list scheduling: a
+// 64-tile sequence on 256 CUs finishes after 33 tile-units of work instead of
+// the 42 that the paired order gives there).
 // heavy_high: the heavy tiles are the high-numbered ones (queries at the end
 // see the most keys); otherwise the low-numbered ones (keys at the start are
 // seen by the most queries).
-MTB_DEV void tile_order(int L, int ntile, int nbh, bool causal, bool heavy_high, int& tile, int& bh) {
+MTB_DEV void tile_order(int L, int ntile, int nbh, bool causal, bool heavy_high, bool paired, int& tile,
+                        int& bh) {
   bh = L % nbh;
   const int j = L / nbh;
   int rank;  // 0 = heaviest
@@ -87,7 +93,7 @@ MTB_DEV void tile_order(int L, int ntile, int nbh, bool causal, bool heavy_high,
     tile = j;
     return;
   }
-  if (ntile % 2 == 0) {
+  if (paired && ntile % 2 == 0) {
     const int h = ntile / 2;
     rank = j < h ? j : ntile - 1 - (j - h);
   } else {
@@ -124,7 +130,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(int S, int nq, int nkv
   const int qh = wave & 1, kh = wave >> 1;
   const int ntile = S / 64, nbh = gridDim.x / ntile;
   int qb, bh;
-  tile_order(blockIdx.x, ntile, nbh, CAUSAL, true, qb, bh);
+  tile_order(blockIdx.x, ntile, nbh, CAUSAL, true, true, qb, bh);
   const int b = bh / nq, hq = bh % nq, hk = hq / (nq / nkv);
   const int q0 = qb * 64 + qh * 32;
   const int qi = q0 + (lane & 31);
@@ -300,6 +306,10 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(int rows, int S, int 
   }
 }
 
+// workgroups per CU: one at D = 128 (its LDS stages and registers fill a CU), else two
+template <int D>
+constexpr int dkdv_per_cu() { return D == 128 ? 1 : 2; }
+
 // dK, dV. Workgroup = 64 keys of one (batch, q head); wavefront w takes key
 // half w & 1 and query half w >> 1 of every 64-query tile. S = Q K^T puts a
 // key per lane, so P and dS feed dV^T += dO^T P^T and dK^T += Q^T dS^T
@@ -308,7 +318,7 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(int rows, int S, int 
 // copied global -> LDS directly, double-buffered: tile t+1 streams in while
 // tile t is used.
 template <int D, bool CAUSAL, bool DROP>
-__global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(
+__global__ __launch_bounds__(256, dkdv_per_cu<D>()) void attn_bwd_dkdv_kernel(
     int S, int nq, int nkv, int ldq, const bf16_t* __restrict__ qkv,
     const bf16_t* __restrict__ qkvT, const bf16_t* __restrict__ dO,
     const bf16_t* __restrict__ dOT, const float* __restrict__ lse,
@@ -322,7 +332,7 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(
   const int kh = wave & 1, qh = wave >> 1;
   const int ntile = S / 64, nbh = gridDim.x / ntile;
   int kb, bh;
-  tile_order(blockIdx.x, ntile, nbh, CAUSAL, false, kb, bh);
+  tile_order(blockIdx.x, ntile, nbh, CAUSAL, false, dkdv_per_cu<D>() == 2, kb, bh);
   const int b = bh / nq, hq = bh % nq;
   const int g = nq / nkv, hk = hq / g;
   const int k0 = kb * 64 + kh * 32;
@@ -560,7 +570,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
   const int qh = wave & 1, kh = wave >> 1;
   const int ntile = S / 64, nbh = gridDim.x / ntile;
   int qb, bh;
-  tile_order(blockIdx.x, ntile, nbh, CAUSAL, true, qb, bh);
+  tile_order(blockIdx.x, ntile, nbh, CAUSAL, true, true, qb, bh);
   const int b = bh / nq, hq = bh % nq, hk = hq / (nq / nkv);
   const int q0 = qb * 64 + qh * 32;
   const int qi = q0 + (lane & 31);
