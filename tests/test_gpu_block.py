@@ -68,14 +68,17 @@ def test_bf16_small_shapes(i):
 
 
 # Shapes that reach the hand-scheduled 256 x 256 GEMM (contractions that are
-# multiples of 128 and at least 1024 deep) with ragged edges: 4032 tokens
+# multiples of 32 and at least 1024 deep) with ragged edges: 4032 tokens
 # (fc1 forward, fc2 dgrad: token rows past the last full tile), and ragged
 # weight dimensions 2112 x 1344 for the weight gradients, whose contraction
-# (4096 tokens) is split four ways.
+# (4096 tokens) is split four ways; hidden 1984 (a 192-wide last tile), where
+# the QKV and projection weight gradients run as one grouped launch (1536 x
+# 1984 and 1984 x 512, each split four ways: 192 + 64 blocks).
 SCHED_RAGGED = [
     dict(batch=3, seq=1344, hidden=1280, q_heads=10, kv_heads=2, head_dim=128, ffn=3072, causal=True),
     dict(batch=2, seq=2048, hidden=1344, q_heads=21, kv_heads=3, head_dim=64, ffn=2112, bias=True,
          affine=True),
+    dict(batch=2, seq=2048, hidden=1984, q_heads=4, kv_heads=4, head_dim=128, ffn=576, causal=True),
 ]
 
 

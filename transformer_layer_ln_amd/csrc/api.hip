@@ -146,6 +146,20 @@ Saved saved_layout(const Dims& d) {
   return s;
 }
 
+// The QKV and projection weight gradients as one gemm_wgrad_pair (operands
+// may be null when only sizes are needed): dWqkv [Nqkv][H] = dqkv^T a and
+// dWo [H][nq d] = dA^T O, contractions over the tokens.
+GemmProb wgrad_qkv(const Dims& d, const void* dqkv, const void* a) {
+  GemmProb p{(int)d.Nqkv, (int)d.H, (int)d.T, dqkv, (int)d.Nqkv, a, (int)d.H, Epi()};
+  p.e.ldo = (int)d.H;
+  return p;
+}
+GemmProb wgrad_proj(const Dims& d, const void* dA, const void* O) {
+  GemmProb p{(int)d.H, (int)d.NO, (int)d.T, dA, (int)d.H, O, (int)d.NO, Epi()};
+  p.e.ldo = (int)d.NO;
+  return p;
+}
+
 struct Scratch {
   size_t dh, dr, gm, p, du, dm, dO, dOT, Dbuf, dqkv, part, red, ws, total;
 };
@@ -167,8 +181,8 @@ Scratch scratch_layout(const Dims& d) {
   int64_t nmax = d.H > d.Fu ? d.H : d.Fu;
   if (d.Nqkv > nmax) nmax = d.Nqkv;
   s.red = o; o += al((size_t)colsum_splits((int)d.T) * nmax * 4);
-  // split-contraction partial tiles (one GEMM at a time): the largest any
-  // GEMM of the block asks for
+  // split-contraction partial tiles (one GEMM, or one grouped pair, at a
+  // time): the largest any of them asks for
   const int dt = d.dt, T32 = (int)d.T, H = (int)d.H, Nq = (int)d.Nqkv, NO = (int)d.NO,
             F = (int)d.F, Fu = (int)d.Fu;
   const int act_f = d.act == MTB_ACT_GELU ? EPI_GELU : EPI_SWIGLU;
@@ -185,7 +199,8 @@ Scratch scratch_layout(const Dims& d) {
       gemm_ws_bytes(dt, H, F, T32, false, false, EPI_STORE),   // weight gradients
       gemm_ws_bytes(dt, Fu, H, T32, false, false, EPI_STORE),
       gemm_ws_bytes(dt, H, NO, T32, false, false, EPI_STORE),
-      gemm_ws_bytes(dt, Nq, H, T32, false, false, EPI_STORE)};
+      gemm_ws_bytes(dt, Nq, H, T32, false, false, EPI_STORE),
+      gemm_wgrad_pair_ws_bytes(dt, wgrad_qkv(d, nullptr, nullptr), wgrad_proj(d, nullptr, nullptr))};
   size_t ws = 0;
   for (size_t v : need) ws = v > ws ? v : ws;
   s.ws = o; o += al(ws);
@@ -586,7 +601,10 @@ mtb_status mtb_block_bwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
       e.out = dO; e.ldo = NO; e.outT = dOT; e.S = S; e.ws = ws;
       MTB_HIP(gemm(dt, T, NO, H, dA, H, true, w->w_o, NO, false, e, st));
     }
-    if (g.w_o) {
+    // the projection's weight gradient waits for the QKV one when both are
+    // requested: one grouped launch (gemm_wgrad_pair) after the attention
+    const bool wpair = g.w_o && g.w_qkv;
+    if (g.w_o && !wpair) {
       Epi e;
       e.out = g.w_o; e.ldo = NO; e.ws = ws;
       MTB_HIP(gemm(dt, H, NO, T, dA, H, false, O, NO, false, e, st));
@@ -595,7 +613,12 @@ mtb_status mtb_block_bwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
     // attention backward
     MTB_HIP(attn_bwd(dt, (int)d.B, S, (int)d.nq, (int)d.nkv, (int)d.d, d.causal, qkv, qkvT, O, dO,
                      dOT, lse, Dbuf, dqkv, part, st, d.dattn));
-    if (g.w_qkv) {
+    if (wpair) {
+      GemmProb pq = wgrad_qkv(d, dqkv, post ? x : a), po = wgrad_proj(d, dA, O);
+      pq.e.out = g.w_qkv;
+      po.e.out = g.w_o;
+      MTB_HIP(gemm_wgrad_pair(dt, pq, po, ws, st));
+    } else if (g.w_qkv) {
       Epi e;
       e.out = g.w_qkv; e.ldo = H; e.ws = ws;
       MTB_HIP(gemm(dt, Nq, H, T, dqkv, Nq, false, post ? x : a, H, false, e, st));

@@ -35,6 +35,7 @@
 //   forward   Y = X W^T         A = X [T][in],  B = W [out][in]     (k-contig both)
 //   dgrad     dX = dY W         A = dY [T][out], B = W [out][in]    (B transposed)
 //   wgrad     dW = dY^T X       A = dY [T][out], B = X [T][in]      (both transposed)
+#include <algorithm>
 #include <type_traits>
 
 #include "drop.h"
@@ -455,12 +456,12 @@ __global__ __launch_bounds__(NT) void splitk_epi_kernel(int M, int N, int splits
 struct BlockTile {
   int tm, tn, split, tiles_n;
 };
+// position of block `bid` of an `nb`-block grid when the grid is read XCD by XCD
+MTB_DEV int xcd_order(int bid, int nb) { return (nb & 7) == 0 ? (bid & 7) * (nb >> 3) + (bid >> 3) : bid; }
+// tile of the block at XCD-ordered position `bid` of one product
 template <int BM, int BN>
-MTB_DEV BlockTile block_tile(int M, int N) {
+MTB_DEV BlockTile tile_at(int M, int N, int bid) {
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  int bid = blockIdx.x;
-  const int nb = gridDim.x;
-  if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
   const int split = bid / (tiles_m * tiles_n);
   bid -= split * (tiles_m * tiles_n);
   constexpr int GROUP = 8;
@@ -468,6 +469,10 @@ MTB_DEV BlockTile block_tile(int M, int N) {
   const int first_m = (bid / per_group) * GROUP;
   const int gsz = min(tiles_m - first_m, GROUP);
   return {first_m + (bid % per_group) % gsz, (bid % per_group) / gsz, split, tiles_n};
+}
+template <int BM, int BN>
+MTB_DEV BlockTile block_tile(int M, int N) {
+  return tile_at<BM, BN>(M, N, xcd_order(blockIdx.x, gridDim.x));
 }
 
 // Epilogue. lane holds C[m][n..n+3] with m = (lane & 31), n = 8q + 4(lane >> 5)
@@ -608,18 +613,19 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(int M, i
 // byte offset below 2^32 (sched_ok).
 constexpr int SBK = 32, SSTAGES = 4;
 
+constexpr int SMEM_SCHED = SSTAGES * (256 + 256) * SBK;  // bf16 elements of LDS
+
+// One block's tile (bt) of the product: the k-loop and the epilogue. smem is
+// the block's SMEM_SCHED-element LDS array (1-KB aligned).
 template <bool AKC, bool BKC, int EPI>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_sched_kernel(int M, int N, int K,
-                                                                 const bf16_t* __restrict__ A, int lda,
-                                                                 const bf16_t* __restrict__ B, int ldb,
-                                                                 Epi ep, int ksplit) {
+MTB_DEV void sched_tile(bf16_t* smem, int M, int N, int K, const bf16_t* __restrict__ A, int lda,
+                        const bf16_t* __restrict__ B, int ldb, const Epi& ep, int ksplit,
+                        const BlockTile& bt) {
   constexpr int BM = 256, BN = 256;
   constexpr uint32_t B_OFF = BM * SBK * 2;  // operand B follows A inside a stage (bytes)
-  __shared__ __attribute__((aligned(1024))) bf16_t smem[SSTAGES * (BM + BN) * SBK];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const BlockTile bt = block_tile<BM, BN>(M, N);
   const int kspan = K / ksplit, kbeg = bt.split * kspan;
   const int m0 = bt.tm * BM, n0 = bt.tn * BN;
   const uint32_t lds = (uint32_t)(uintptr_t)smem;
@@ -720,6 +726,44 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_sched_kernel(int M, int N, i
   __syncthreads();
   gemm_epilogue<BM, BN, 2, 2, SSTAGES * (BM + BN) * SBK / 2, AKC, EPI>(acc, smem, ep, M, N, m0, n0, bt,
                                                                       wm, wn, lane, tid);
+}
+
+template <bool AKC, bool BKC, int EPI>
+__global__ __launch_bounds__(256, 1) void gemm_bf16_sched_kernel(int M, int N, int K,
+                                                                 const bf16_t* __restrict__ A, int lda,
+                                                                 const bf16_t* __restrict__ B, int ldb,
+                                                                 Epi ep, int ksplit) {
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[SMEM_SCHED];
+  sched_tile<AKC, BKC, EPI>(smem, M, N, K, A, lda, B, ldb, ep, ksplit, block_tile<256, 256>(M, N));
+}
+
+// One product of a grouped launch: its operands, split and block count.
+struct SchedProb {
+  int M, N, K;
+  const bf16_t* A;
+  int lda;
+  const bf16_t* B;
+  int ldb;
+  int ksplit, blocks;
+  Epi ep;
+};
+
+// Two independent products in one grid (same operand layouts and epilogue):
+// the first p0.blocks blocks in XCD order take p0, the rest p1, so that a
+// product whose tiles leave CUs idle shares the chip with another one.
+template <bool AKC, bool BKC, int EPI>
+__global__ __launch_bounds__(256, 1) void gemm_bf16_sched_pair_kernel(SchedProb p0, SchedProb p1) {
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[SMEM_SCHED];
+  const int r = xcd_order(blockIdx.x, gridDim.x);
+  const bool second = r >= p0.blocks;  // uniform over the block
+  const int M = second ? p1.M : p0.M, N = second ? p1.N : p0.N, K = second ? p1.K : p0.K;
+  const bf16_t* A = second ? p1.A : p0.A;
+  const bf16_t* B = second ? p1.B : p0.B;
+  const int lda = second ? p1.lda : p0.lda, ldb = second ? p1.ldb : p0.ldb;
+  const int ksplit = second ? p1.ksplit : p0.ksplit;
+  const Epi ep = second ? p1.ep : p0.ep;
+  sched_tile<AKC, BKC, EPI>(smem, M, N, K, A, lda, B, ldb, ep, ksplit,
+                            tile_at<256, 256>(M, N, second ? r - p0.blocks : r));
 }
 
 // ---------------------------------------------------------------------------
@@ -886,6 +930,52 @@ hipError_t launch_sched(int M, int N, int K, const void* A, int lda, const void*
   return hipGetLastError();
 }
 
+// Two weight gradients (both operands [K][rows], plain stores) in one grid:
+// p0 keeps the split plan() gives it alone (the scheduled kernel, split at
+// least two ways, its blocks leaving CUs idle); p1 takes the smallest split
+// of at least two whose parts are no deeper than p0's, and the pair is used
+// when the blocks of both fit the chip and a simple cost model -- per wave
+// of blocks, the k-tiles of one block plus 32 k-tiles of fixed (prologue and
+// epilogue) cost -- puts the pair below the two launches one after the
+// other. Both products then write fp32 partial tiles (p0's at ws, p1's
+// after them) that the split reduction sums.
+struct PairPlan {
+  bool ok = false;
+  int s0 = 1, s1 = 1;
+  size_t ws1 = 0;  // byte offset of p1's partial tiles in the workspace
+};
+PairPlan pair_plan(int M0, int N0, int K0, int lda0, int ldb0, int M1, int N1, int K1, int lda1,
+                   int ldb1) {
+  PairPlan pp;
+  if (M0 <= 0 || N0 <= 0 || K0 <= 0 || M1 <= 0 || N1 <= 0 || K1 <= 0) return pp;
+  const Plan a = plan(M0, N0, K0, false, false, EPI_STORE, true);
+  const Plan b = plan(M1, N1, K1, false, false, EPI_STORE, true);
+  if (a.tile != TSCHED || a.splits < 2) return pp;
+  auto tiles = [](int m, int n, int bm, int bn) { return (long)((m + bm - 1) / bm) * ((n + bn - 1) / bn); };
+  const long t0 = tiles(M0, N0, 256, 256), t1 = tiles(M1, N1, 256, 256);
+  const long blocks0 = t0 * a.splits;
+  int s1 = 2;
+  while (s1 < 8 && K1 / s1 > K0 / a.splits) s1 *= 2;
+  if (K1 % (s1 * SBK) != 0 || K1 / s1 < 1024 || blocks0 + t1 * s1 > kCUs) return pp;
+  if (!sched_ok(M0, N0, K0, false, lda0, false, ldb0, a.splits) ||
+      !sched_ok(M1, N1, K1, false, lda1, false, ldb1, s1))
+    return pp;
+  auto waves = [](long blocks, int per_cu) { return (blocks + (long)kCUs * per_cu - 1) / ((long)kCUs * per_cu); };
+  // p1 alone, on the tiles plan() gives it (k-tiles counted 32 deep whatever the kernel)
+  const int bm1 = b.tile == T128x128 ? 128 : 256;
+  const int bn1 = b.tile == T256x256 || b.tile == TSCHED ? 256 : b.tile == T256x192 ? 192 : 128;
+  const int per1 = b.tile == T128x128 ? 2 : 1;
+  const long alone = waves(blocks0, 1) * (K0 / a.splits / SBK + 32) +
+                     waves(tiles(M1, N1, bm1, bn1) * b.splits, per1) * (K1 / b.splits / SBK + 32);
+  const long paired = std::max(K0 / a.splits, K1 / s1) / SBK + 32;
+  if (paired >= alone) return pp;
+  pp.ok = true;
+  pp.s0 = a.splits;
+  pp.s1 = s1;
+  pp.ws1 = ((size_t)a.splits * M0 * N0 * 4 + 255) & ~(size_t)255;
+  return pp;
+}
+
 template <bool AKC, bool BKC, int EPI>
 hipError_t launch_bf16(int M, int N, int K, const void* A, int lda, const void* B, int ldb,
                        const Epi& e, hipStream_t st) {
@@ -959,6 +1049,54 @@ size_t gemm_ws_bytes(int dtype, int M, int N, int K, bool a_kc, bool b_kc, int k
   if (dtype == 0 || M <= 0 || N <= 0 || K <= 0) return 0;
   const Plan pl = plan(M, N, K, a_kc, b_kc, kind, true);
   return pl.splits > 1 ? (size_t)pl.splits * M * N * 4 : 0;
+}
+
+size_t gemm_wgrad_pair_ws_bytes(int dtype, const GemmProb& p0, const GemmProb& p1) {
+  if (dtype == 0) return 0;
+  const PairPlan pp = pair_plan(p0.M, p0.N, p0.K, p0.lda, p0.ldb, p1.M, p1.N, p1.K, p1.lda, p1.ldb);
+  if (pp.ok) return pp.ws1 + (size_t)pp.s1 * p1.M * p1.N * 4;
+  return std::max(gemm_ws_bytes(dtype, p0.M, p0.N, p0.K, false, false, EPI_STORE),
+                  gemm_ws_bytes(dtype, p1.M, p1.N, p1.K, false, false, EPI_STORE));
+}
+
+hipError_t gemm_wgrad_pair(int dtype, const GemmProb& p0, const GemmProb& p1, void* ws, hipStream_t st) {
+  const PairPlan pp = dtype == 0 || ws == nullptr
+                          ? PairPlan()
+                          : pair_plan(p0.M, p0.N, p0.K, p0.lda, p0.ldb, p1.M, p1.N, p1.K, p1.lda, p1.ldb);
+  if (!pp.ok) {
+    for (const GemmProb* q : {&p0, &p1}) {
+      Epi e = q->e;
+      e.ws = ws;
+      const hipError_t r = gemm(dtype, q->M, q->N, q->K, q->A, q->lda, false, q->B, q->ldb, false, e, st);
+      if (r != hipSuccess) return r;
+    }
+    return hipSuccess;
+  }
+  SchedProb q[2];
+  const GemmProb* src[2] = {&p0, &p1};
+  const int splits[2] = {pp.s0, pp.s1};
+  void* wsp[2] = {ws, (char*)ws + pp.ws1};
+  for (int i = 0; i < 2; ++i) {
+    const GemmProb& g = *src[i];
+    q[i].M = g.M; q[i].N = g.N; q[i].K = g.K;
+    q[i].A = (const bf16_t*)g.A; q[i].lda = g.lda;
+    q[i].B = (const bf16_t*)g.B; q[i].ldb = g.ldb;
+    q[i].ksplit = splits[i];
+    q[i].blocks = ((g.M + 255) / 256) * ((g.N + 255) / 256) * splits[i];
+    q[i].ep = Epi();
+    q[i].ep.ws = wsp[i];
+  }
+  hipLaunchKernelGGL((gemm_bf16_sched_pair_kernel<false, false, EPI_PARTIAL>),
+                     dim3((unsigned)(q[0].blocks + q[1].blocks)), dim3(256), 0, st, q[0], q[1]);
+  hipError_t r = hipGetLastError();
+  for (int i = 0; i < 2 && r == hipSuccess; ++i) {
+    const GemmProb& g = *src[i];
+    const size_t n8 = (size_t)g.M * g.N / 8;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, g.M, g.N,
+                       splits[i], (const float*)wsp[i], (bf16_t*)g.e.out, g.e.ldo);
+    r = hipGetLastError();
+  }
+  return r;
 }
 
 hipError_t gemm(int dtype, int M, int N, int K, const void* A, int lda, bool a_kc, const void* B,

@@ -68,6 +68,23 @@ hipError_t gemm(int dtype, int M, int N, int K, const void* A, int lda, bool a_k
 // copy) with too few tiles to fill the chip are split; the partial tiles are
 // summed in a fixed order.
 size_t gemm_ws_bytes(int dtype, int M, int N, int K, bool a_kc, bool b_kc, int kind);
+// One product for gemm_wgrad_pair: C[M][N] = sum_k A[k][M] B[k][N] (both
+// operands stored k-major, as weight gradients read activations), plain store
+// to e.out [M][e.ldo] (other Epi fields unused).
+struct GemmProb {
+  int M, N, K;
+  const void* A;
+  int lda;
+  const void* B;
+  int ldb;
+  Epi e;
+};
+// Two independent weight gradients. When the first one's tiles leave CUs idle
+// and the second fits beside it, both run in one grid of the scheduled kernel
+// (split contractions, summed in a fixed order); otherwise one after the
+// other, as gemm() runs them. ws: gemm_wgrad_pair_ws_bytes bytes.
+hipError_t gemm_wgrad_pair(int dtype, const GemmProb& p0, const GemmProb& p1, void* ws, hipStream_t st);
+size_t gemm_wgrad_pair_ws_bytes(int dtype, const GemmProb& p0, const GemmProb& p1);
 // Column-tile width the bf16 GEMM uses for this problem (the tiles_n of
 // EPI_XENT_STATS is ceil(N / it)).
 int gemm_tile_n(int M, int N, int K, bool a_kc, bool b_kc, int kind);
