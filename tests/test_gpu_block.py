@@ -73,12 +73,19 @@ def test_bf16_small_shapes(i):
 # weight dimensions 2112 x 1344 for the weight gradients, whose contraction
 # (4096 tokens) is split four ways; hidden 1984 (a 192-wide last tile), where
 # the QKV and projection weight gradients run as one grouped launch (1536 x
-# 1984 and 1984 x 512, each split four ways: 192 + 64 blocks).
+# 1984 and 1984 x 512, each split four ways: 192 + 64 blocks); 8064 tokens at
+# hidden 1984 with biases, where fc2 and the 512-deep projection forward add
+# their residual rows on the scheduled kernel past both ragged edges (a
+# 128-row last tile row, a 192-wide last tile column) and the grouped weight
+# gradients split 8064 tokens four ways (63 k-tiles each, entering the loop
+# body at its second slot).
 SCHED_RAGGED = [
     dict(batch=3, seq=1344, hidden=1280, q_heads=10, kv_heads=2, head_dim=128, ffn=3072, causal=True),
     dict(batch=2, seq=2048, hidden=1344, q_heads=21, kv_heads=3, head_dim=64, ffn=2112, bias=True,
          affine=True),
     dict(batch=2, seq=2048, hidden=1984, q_heads=4, kv_heads=4, head_dim=128, ffn=576, causal=True),
+    dict(batch=3, seq=2688, hidden=1984, q_heads=4, kv_heads=4, head_dim=128, ffn=576, causal=True,
+         bias=True),
 ]
 
 

@@ -203,6 +203,28 @@ struct Staged {
   MTB_DEV float get(int r, int n) const { return s[off(r, n)]; }
 };
 
+// The residual rows of one staged chunk (EPI_STORE with resid), loaded into
+// registers before the chunk is staged: one 16-byte load per row item of the
+// row phase below (same item order), all in flight at once. Loaded one item
+// at a time between the staged reads and the stores, the residual cost the
+// seq-2048 fc2 forward about 3x its HBM time (a load latency per item).
+template <int BN, int CR, int NT>
+struct ResidRows {
+  static constexpr int IPR = BN / 8, ITEMS = CR * IPR / NT;
+  static_assert(CR * IPR % NT == 0, "whole row items per thread");
+  u32x4 q[ITEMS];
+  MTB_DEV void load(const Epi& e, int M, int N, int mc, int n0, int tid) {
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+      const int it = tid + j * NT, r = it / IPR, nl = (it % IPR) * 8;
+      const int m = mc + r, n = n0 + nl;
+      q[j] = u32x4{0u, 0u, 0u, 0u};
+      if (m < M && n < N)
+        q[j] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(e.resid) + (size_t)m * e.ldr + n);
+    }
+  }
+};
+
 // Row phase of the epilogue for rows [0, CR) of the staged chunk whose first
 // row is global row mc: each work item is 8 consecutive columns of one row
 // (for SwiGLU, the 8 gate and the matching 8 up columns).
@@ -285,6 +307,31 @@ MTB_DEV void epi_rows(const Epi& e, const Staged<BN>& st, int M, int N, int mc, 
         out8(e.out, (size_t)m * e.ldo + n, v);
       }
     }
+  }
+}
+
+// Row phase of a plain store with the residual prefetched (pre): the same
+// items and arithmetic as epi_rows' EPI_STORE, item j of this thread adding
+// pre.q[j].
+template <int BN, int CR, int NT>
+MTB_DEV void epi_rows_resid(const Epi& e, const Staged<BN>& st, int M, int N, int mc, int n0, int tid,
+                            const ResidRows<BN, CR, NT>& pre) {
+  constexpr int IPR = BN / 8, ITEMS = CR * IPR / NT;
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j) {
+    const int it = tid + j * NT, r = it / IPR, nl = (it % IPR) * 8;
+    const int m = mc + r, n = n0 + nl;
+    if (m >= M || n >= N) continue;
+    float v[8];
+    st.get8(r, nl, v);
+    if (e.bias) add8(e.bias, n, v);
+    if (e.drop.thr) drop_apply8(e.drop, (uint64_t)m * N + n, v);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] += lo_f(pre.q[j][i]);
+      v[2 * i + 1] += hi_f(pre.q[j][i]);
+    }
+    out8(e.out, (size_t)m * e.ldo + n, v);
   }
 }
 
@@ -479,7 +526,7 @@ MTB_DEV BlockTile block_tile(int M, int N) {
 // inside each 32x32 fragment (register 4q + r -> column n + r). The tile goes
 // through LDS CR rows at a time, reusing the operand buffers (SMEM_F floats;
 // the caller has synchronised after the last operand read).
-template <int BM, int BN, int WGM, int WGN, int SMEM_F, bool AKC, int EPI>
+template <int BM, int BN, int WGM, int WGN, int SMEM_F, bool AKC, int EPI, bool RPRE = false>
 MTB_DEV void gemm_epilogue(const f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32], void* smem,
                            const Epi& ep, int M, int N, int m0, int n0, const BlockTile& bt,
                            int wm, int wn, int lane, int tid) {
@@ -491,6 +538,18 @@ MTB_DEV void gemm_epilogue(const f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32], vo
   constexpr bool COLS = EPI == EPI_STORE && AKC;
   static_assert(!COLS || CR % 64 == 0, "transposed copy needs whole 64-token groups per chunk");
   const Staged<BN> st{reinterpret_cast<float*>(smem)};
+  // RPRE (plain stores): a chunk's residual rows are all requested before any
+  // of its stores -- chunk 0's before the staging, chunk c + 1's right after
+  // chunk c's stores (vector memory operations complete in issue order, so a
+  // load issued after a store is waited for behind that store: one wait per
+  // chunk instead of one per row item). For kernels whose accumulators live
+  // in AGPRs; in the 2x4-wavefront kernel the extra registers spill.
+  constexpr bool PRE = RPRE && EPI == EPI_STORE;
+  ResidRows<BN, CR, NT> pre;
+  const bool has_pre = PRE && ep.resid != nullptr;
+  if constexpr (PRE) {
+    if (has_pre) pre.load(ep, M, N, m0, n0, tid);
+  }
 #pragma unroll 1
   for (int c0 = 0; c0 < BM; c0 += CR) {
     if (c0 > 0) __syncthreads();
@@ -515,10 +574,15 @@ MTB_DEV void gemm_epilogue(const f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32], vo
                               m0 + c0, n0, tid);
     else if constexpr (EPI == EPI_XENT_STATS)
       epi_xent_stats<BN, CR, NT>(ep, st, M, N, m0 + c0, n0, bt.tn, bt.tiles_n, tid);
+    else if (has_pre)
+      epi_rows_resid<BN, CR, NT>(ep, st, M, N, m0 + c0, n0, tid, pre);
     else
       epi_rows<EPI, BN, CR, NT>(ep, st, M, N, m0 + c0, n0, tid);
     if constexpr (COLS) {
       if (ep.outT) epi_cols<BN, CR, NT>(ep, st, M, N, m0 + c0, n0, tid);
+    }
+    if constexpr (PRE) {
+      if (has_pre && c0 + CR < BM) pre.load(ep, M, N, m0 + c0 + CR, n0, tid);
     }
   }
 }
@@ -724,8 +788,8 @@ MTB_DEV void sched_tile(bf16_t* smem, int M, int N, int K, const bf16_t* __restr
 #pragma clang diagnostic pop
 #undef MTB_LOOP_OPERANDS
   __syncthreads();
-  gemm_epilogue<BM, BN, 2, 2, SSTAGES * (BM + BN) * SBK / 2, AKC, EPI>(acc, smem, ep, M, N, m0, n0, bt,
-                                                                      wm, wn, lane, tid);
+  gemm_epilogue<BM, BN, 2, 2, SSTAGES * (BM + BN) * SBK / 2, AKC, EPI, true>(acc, smem, ep, M, N, m0, n0,
+                                                                            bt, wm, wn, lane, tid);
 }
 
 template <bool AKC, bool BKC, int EPI>
@@ -868,7 +932,7 @@ struct Plan {
 // partial-tile traffic. (At the seq-512 share, where every GEMM is 4096 x
 // <=1024 x <=4096, splitting down to 512-deep parts made the step slower,
 // 0.356 -> 0.401 ms: a block's fixed costs, not its k-loop, dominate there.)
-Plan plan(int M, int N, int K, bool a_kc, bool b_kc, int kind, bool split_ok) {
+Plan plan(int M, int N, int K, bool a_kc, bool b_kc, int kind, bool split_ok, bool resid = false) {
   auto tl = [&](int bm, int bn) { return (long)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
   auto depth_ok = [&](int s) { return K % (s * BK) == 0 && K / s >= 1024; };
   auto sched_depth = [&](int s) { return K % (s * SBK) == 0 && K / s >= 1024; };
@@ -897,8 +961,10 @@ Plan plan(int M, int N, int K, bool a_kc, bool b_kc, int kind, bool split_ok) {
   }
   const double f128 = 0.85 * fill(t128, 2);
   // the scheduled kernel's fixed per-block costs (one wavefront per SIMD to hide the first copies
-  // and the epilogue) outweigh its faster loop below 1024-deep contractions
-  const bool sk = K % SBK == 0 && K >= 1024;
+  // and the epilogue) outweigh its faster loop below 1024-deep contractions; with a residual to
+  // add, its prefetched residual rows make it the faster one from 512 deep (projection forward,
+  // 8192 x 4096 x 512: 70 against 77 us)
+  const bool sk = K % SBK == 0 && K >= (resid ? 512 : 1024);
   if (K >= 512) {
     const double f256 = (sk ? 1.3 : 1.0) * fill(t256, 1);
     const double f192 = (a_kc && b_kc && kind == EPI_STORE && N % 192 == 0) ? 0.95 * fill(tl(256, 192), 1)
@@ -980,7 +1046,7 @@ template <bool AKC, bool BKC, int EPI>
 hipError_t launch_bf16(int M, int N, int K, const void* A, int lda, const void* B, int ldb,
                        const Epi& e, hipStream_t st) {
   if (!AKC && e.outT) return hipErrorInvalidValue;  // the transposed copy is token-major only
-  const Plan pl = plan(M, N, K, AKC, BKC, EPI, e.ws != nullptr);
+  const Plan pl = plan(M, N, K, AKC, BKC, EPI, e.ws != nullptr, EPI == EPI_STORE && e.resid != nullptr);
   if (pl.tile == TSCHED) {
     // operands past the 32-bit offsets: the 2x4-wavefront kernel on the same tiles
     const bool ok = sched_ok(M, N, K, AKC, lda, BKC, ldb, pl.splits);
