@@ -203,24 +203,25 @@ struct Staged {
   MTB_DEV float get(int r, int n) const { return s[off(r, n)]; }
 };
 
-// The residual rows of one staged chunk (EPI_STORE with resid), loaded into
-// registers before the chunk is staged: one 16-byte load per row item of the
-// row phase below (same item order), all in flight at once. Loaded one item
-// at a time between the staged reads and the stores, the residual cost the
-// seq-2048 fc2 forward about 3x its HBM time (a load latency per item).
+// One bf16 operand of a staged chunk's row phase (the residual of EPI_STORE,
+// u of EPI_DGELU), loaded into registers before the chunk's stores: one
+// 16-byte load per row item of the row phase (same item order), all in
+// flight at once. Loaded one item at a time between the staged reads and the
+// stores, the residual cost the seq-2048 fc2 forward about 3x its HBM time (a
+// load latency per item).
 template <int BN, int CR, int NT>
-struct ResidRows {
+struct RowOperand {
   static constexpr int IPR = BN / 8, ITEMS = CR * IPR / NT;
   static_assert(CR * IPR % NT == 0, "whole row items per thread");
   u32x4 q[ITEMS];
-  MTB_DEV void load(const Epi& e, int M, int N, int mc, int n0, int tid) {
+  MTB_DEV void load(const void* src, int ld, int M, int N, int mc, int n0, int tid) {
 #pragma unroll
     for (int j = 0; j < ITEMS; ++j) {
       const int it = tid + j * NT, r = it / IPR, nl = (it % IPR) * 8;
       const int m = mc + r, n = n0 + nl;
       q[j] = u32x4{0u, 0u, 0u, 0u};
       if (m < M && n < N)
-        q[j] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(e.resid) + (size_t)m * e.ldr + n);
+        q[j] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(src) + (size_t)m * ld + n);
     }
   }
 };
@@ -310,12 +311,13 @@ MTB_DEV void epi_rows(const Epi& e, const Staged<BN>& st, int M, int N, int mc, 
   }
 }
 
-// Row phase of a plain store with the residual prefetched (pre): the same
-// items and arithmetic as epi_rows' EPI_STORE, item j of this thread adding
-// pre.q[j].
-template <int BN, int CR, int NT>
-MTB_DEV void epi_rows_resid(const Epi& e, const Staged<BN>& st, int M, int N, int mc, int n0, int tid,
-                            const ResidRows<BN, CR, NT>& pre) {
+// Row phase of a plain store (residual) or EPI_DGELU (u) with that operand
+// prefetched (pre): the same items and arithmetic as epi_rows, item j of this
+// thread taking pre.q[j].
+template <int EPI, int BN, int CR, int NT>
+MTB_DEV void epi_rows_pre(const Epi& e, const Staged<BN>& st, int M, int N, int mc, int n0, int tid,
+                          const RowOperand<BN, CR, NT>& pre) {
+  static_assert(EPI == EPI_STORE || EPI == EPI_DGELU, "prefetched row operand");
   constexpr int IPR = BN / 8, ITEMS = CR * IPR / NT;
 #pragma unroll
   for (int j = 0; j < ITEMS; ++j) {
@@ -324,12 +326,20 @@ MTB_DEV void epi_rows_resid(const Epi& e, const Staged<BN>& st, int M, int N, in
     if (m >= M || n >= N) continue;
     float v[8];
     st.get8(r, nl, v);
-    if (e.bias) add8(e.bias, n, v);
-    if (e.drop.thr) drop_apply8(e.drop, (uint64_t)m * N + n, v);
+    if constexpr (EPI == EPI_STORE) {
+      if (e.bias) add8(e.bias, n, v);
+      if (e.drop.thr) drop_apply8(e.drop, (uint64_t)m * N + n, v);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] += lo_f(pre.q[j][i]);
-      v[2 * i + 1] += hi_f(pre.q[j][i]);
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] += lo_f(pre.q[j][i]);
+        v[2 * i + 1] += hi_f(pre.q[j][i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] *= gelu_grad_f(lo_f(pre.q[j][i]));
+        v[2 * i + 1] *= gelu_grad_f(hi_f(pre.q[j][i]));
+      }
     }
     out8(e.out, (size_t)m * e.ldo + n, v);
   }
@@ -538,17 +548,24 @@ MTB_DEV void gemm_epilogue(const f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32], vo
   constexpr bool COLS = EPI == EPI_STORE && AKC;
   static_assert(!COLS || CR % 64 == 0, "transposed copy needs whole 64-token groups per chunk");
   const Staged<BN> st{reinterpret_cast<float*>(smem)};
-  // RPRE (plain stores): a chunk's residual rows are all requested before any
-  // of its stores -- chunk 0's before the staging, chunk c + 1's right after
-  // chunk c's stores (vector memory operations complete in issue order, so a
-  // load issued after a store is waited for behind that store: one wait per
-  // chunk instead of one per row item). For kernels whose accumulators live
-  // in AGPRs; in the 2x4-wavefront kernel the extra registers spill.
-  constexpr bool PRE = RPRE && EPI == EPI_STORE;
-  ResidRows<BN, CR, NT> pre;
-  const bool has_pre = PRE && ep.resid != nullptr;
+  // RPRE (plain stores with a residual, EPI_DGELU): a chunk's row operand is
+  // requested in full before any of its stores -- chunk 0's before the
+  // staging, chunk c + 1's right after chunk c's stores (vector memory
+  // operations complete in issue order, so a load issued after a store is
+  // waited for behind that store: one wait per chunk instead of one per row
+  // item). For kernels whose accumulators live in AGPRs; in the 2x4-wavefront
+  // kernel the extra registers spill.
+  constexpr bool PRE = RPRE && (EPI == EPI_STORE || EPI == EPI_DGELU);
+  RowOperand<BN, CR, NT> pre;
+  auto load_pre = [&](int mc) {
+    if constexpr (EPI == EPI_STORE)
+      pre.load(ep.resid, ep.ldr, M, N, mc, n0, tid);
+    else
+      pre.load(ep.aux, ep.ldaux, M, N, mc, n0, tid);
+  };
+  const bool has_pre = PRE && (EPI == EPI_STORE ? ep.resid : ep.aux) != nullptr;
   if constexpr (PRE) {
-    if (has_pre) pre.load(ep, M, N, m0, n0, tid);
+    if (has_pre) load_pre(m0);
   }
 #pragma unroll 1
   for (int c0 = 0; c0 < BM; c0 += CR) {
@@ -575,14 +592,14 @@ MTB_DEV void gemm_epilogue(const f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32], vo
     else if constexpr (EPI == EPI_XENT_STATS)
       epi_xent_stats<BN, CR, NT>(ep, st, M, N, m0 + c0, n0, bt.tn, bt.tiles_n, tid);
     else if (has_pre)
-      epi_rows_resid<BN, CR, NT>(ep, st, M, N, m0 + c0, n0, tid, pre);
+      epi_rows_pre<PRE ? EPI : EPI_STORE, BN, CR, NT>(ep, st, M, N, m0 + c0, n0, tid, pre);
     else
       epi_rows<EPI, BN, CR, NT>(ep, st, M, N, m0 + c0, n0, tid);
     if constexpr (COLS) {
       if (ep.outT) epi_cols<BN, CR, NT>(ep, st, M, N, m0 + c0, n0, tid);
     }
     if constexpr (PRE) {
-      if (has_pre && c0 + CR < BM) pre.load(ep, M, N, m0 + c0 + CR, n0, tid);
+      if (has_pre && c0 + CR < BM) load_pre(m0 + c0 + CR);
     }
   }
 }
