@@ -360,7 +360,7 @@ mtb_status mtb_vocab_embed_bwd(int64_t n_tokens, int64_t v_local, int64_t v_star
 #define MTB_TRACE_FC1_FWD 1   /* column-parallel fc1 GEMM + activation, forward */
 #define MTB_TRACE_ATTN_FWD 2  /* attention forward */
 #define MTB_TRACE_LN1_FWD 3   /* input LayerNorm forward */
-#define MTB_TRACE_FC2_WGRAD 4 /* fc2 weight-gradient GEMM */
+#define MTB_TRACE_FC2_WGRAD 4 /* fc2 weight-gradient GEMM (with fc1's when the two run as one launch) */
 /* Segments of MTB_PHASE_ALL calls (the attention / FFN / backward breakdown
  * of [Lab06] sec. 4): */
 #define MTB_TRACE_ATTN_SEG 5  /* forward LN1 .. projection (with the fused residual) */

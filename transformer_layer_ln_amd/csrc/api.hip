@@ -146,9 +146,9 @@ Saved saved_layout(const Dims& d) {
   return s;
 }
 
-// The QKV and projection weight gradients as one gemm_wgrad_pair (operands
-// may be null when only sizes are needed): dWqkv [Nqkv][H] = dqkv^T a and
-// dWo [H][nq d] = dA^T O, contractions over the tokens.
+// Weight gradients as gemm_wgrad_pair products (operands may be null when only
+// sizes are needed), contractions over the tokens: dWqkv [Nqkv][H] = dqkv^T a,
+// dWo [H][nq d] = dA^T O, dW2 [H][F] = G^T m, dW1 [Fu][H] = du^T c.
 GemmProb wgrad_qkv(const Dims& d, const void* dqkv, const void* a) {
   GemmProb p{(int)d.Nqkv, (int)d.H, (int)d.T, dqkv, (int)d.Nqkv, a, (int)d.H, Epi()};
   p.e.ldo = (int)d.H;
@@ -157,6 +157,16 @@ GemmProb wgrad_qkv(const Dims& d, const void* dqkv, const void* a) {
 GemmProb wgrad_proj(const Dims& d, const void* dA, const void* O) {
   GemmProb p{(int)d.H, (int)d.NO, (int)d.T, dA, (int)d.H, O, (int)d.NO, Epi()};
   p.e.ldo = (int)d.NO;
+  return p;
+}
+GemmProb wgrad_fc2(const Dims& d, const void* G, const void* m) {
+  GemmProb p{(int)d.H, (int)d.F, (int)d.T, G, (int)d.H, m, (int)d.F, Epi()};
+  p.e.ldo = (int)d.F;
+  return p;
+}
+GemmProb wgrad_fc1(const Dims& d, const void* du, const void* c) {
+  GemmProb p{(int)d.Fu, (int)d.H, (int)d.T, du, (int)d.Fu, c, (int)d.H, Epi()};
+  p.e.ldo = (int)d.H;
   return p;
 }
 
@@ -200,7 +210,8 @@ Scratch scratch_layout(const Dims& d) {
       gemm_ws_bytes(dt, Fu, H, T32, false, false, EPI_STORE),
       gemm_ws_bytes(dt, H, NO, T32, false, false, EPI_STORE),
       gemm_ws_bytes(dt, Nq, H, T32, false, false, EPI_STORE),
-      gemm_wgrad_pair_ws_bytes(dt, wgrad_qkv(d, nullptr, nullptr), wgrad_proj(d, nullptr, nullptr))};
+      gemm_wgrad_pair_ws_bytes(dt, wgrad_qkv(d, nullptr, nullptr), wgrad_proj(d, nullptr, nullptr)),
+      gemm_wgrad_pair_ws_bytes(dt, wgrad_fc2(d, nullptr, nullptr), wgrad_fc1(d, nullptr, nullptr))};
   size_t ws = 0;
   for (size_t v : need) ws = v > ws ? v : ws;
   s.ws = o; o += al(ws);
@@ -551,19 +562,26 @@ mtb_status mtb_block_bwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
       MTB_HIP(gemm(dt, T, F, H, Gm, H, true, w->w_fc2, F, false, e, st));
       MTB_HIP(act_bwd(dt, d.act, T, F, dm, u, du, st));
     }
-    if (g.w_fc2) {
+    // the two MLP weight gradients as one grouped launch when both are requested
+    if (g.w_fc2 && g.w_fc1) {
+      GemmProb p2 = wgrad_fc2(d, Gm, m), p1 = wgrad_fc1(d, du, c);
+      p2.e.out = g.w_fc2;
+      p1.e.out = g.w_fc1;
+      trace_begin(MTB_TRACE_FC2_WGRAD, st);
+      MTB_HIP(gemm_wgrad_pair(dt, p2, p1, ws, st));
+      trace_end(MTB_TRACE_FC2_WGRAD, st);
+    } else if (g.w_fc2) {
       Epi e;
       e.out = g.w_fc2; e.ldo = F; e.ws = ws;
       trace_begin(MTB_TRACE_FC2_WGRAD, st);
       MTB_HIP(gemm(dt, H, F, T, Gm, H, false, m, F, false, e, st));
       trace_end(MTB_TRACE_FC2_WGRAD, st);
-    }
-    if (g.b_fc2) MTB_HIP(colsum(dt, T, H, Gm, nullptr, H, nullptr, nullptr, nullptr, g.b_fc2, red, st));
-    if (g.w_fc1) {
+    } else if (g.w_fc1) {
       Epi e;
       e.out = g.w_fc1; e.ldo = H; e.ws = ws;
       MTB_HIP(gemm(dt, Fu, H, T, du, Fu, false, c, H, false, e, st));
     }
+    if (g.b_fc2) MTB_HIP(colsum(dt, T, H, Gm, nullptr, H, nullptr, nullptr, nullptr, g.b_fc2, red, st));
     if (g.b_fc1) MTB_HIP(colsum(dt, T, Fu, du, nullptr, Fu, nullptr, nullptr, nullptr, g.b_fc1, red, st));
     // fc1 input gradient: partial over ranks, summed at f1
     Epi e;

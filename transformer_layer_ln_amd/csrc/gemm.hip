@@ -1013,50 +1013,66 @@ hipError_t launch_sched(int M, int N, int K, const void* A, int lda, const void*
   return hipGetLastError();
 }
 
-// Two weight gradients (both operands [K][rows], plain stores) in one grid:
-// p0 keeps the split plan() gives it alone (the scheduled kernel, split at
-// least two ways, its blocks leaving CUs idle); p1 takes the smallest split
-// of at least two whose parts are no deeper than p0's, and the pair is used
-// when the blocks of both fit the chip and a simple cost model -- per wave
-// of blocks, the k-tiles of one block plus 32 k-tiles of fixed (prologue and
-// epilogue) cost -- puts the pair below the two launches one after the
-// other. Both products then write fp32 partial tiles (p0's at ws, p1's
-// after them) that the split reduction sums.
+// Two weight gradients (both operands [K][rows], plain stores) in one grid of
+// the scheduled kernel, in one of two forms:
+//  - split: both contractions split 2, 4 or 8 ways, or p0 keeps the split
+//    plan() gives it alone (its blocks leaving CUs idle) and p1 takes the
+//    smallest split of at least two whose parts are no deeper than p0's; both
+//    write fp32 partial tiles (p0's at ws, p1's after them) that the split
+//    reduction sums;
+//  - whole: neither is split, both products' tiles filling the chip together,
+//    stored directly.
+// A form is used when its blocks fill at least three quarters of the chip
+// without exceeding it and a simple cost model puts it below the two launches
+// one after the other: per wave of blocks, the
+// k-tiles of one block plus 32 k-tiles of fixed (prologue and epilogue) cost,
+// and 16 k-tiles per split reduction pass.
 struct PairPlan {
   bool ok = false;
   int s0 = 1, s1 = 1;
-  size_t ws1 = 0;  // byte offset of p1's partial tiles in the workspace
+  size_t ws1 = 0;  // split form: byte offset of p1's partial tiles in the workspace
 };
 PairPlan pair_plan(int M0, int N0, int K0, int lda0, int ldb0, int M1, int N1, int K1, int lda1,
                    int ldb1) {
-  PairPlan pp;
-  if (M0 <= 0 || N0 <= 0 || K0 <= 0 || M1 <= 0 || N1 <= 0 || K1 <= 0) return pp;
+  PairPlan best;
+  if (M0 <= 0 || N0 <= 0 || K0 <= 0 || M1 <= 0 || N1 <= 0 || K1 <= 0) return best;
+  auto tiles = [](int m, int n, int bm, int bn) { return (long)((m + bm - 1) / bm) * ((n + bn - 1) / bn); };
+  auto waves = [](long blocks, int per_cu) {
+    return (blocks + (long)kCUs * per_cu - 1) / ((long)kCUs * per_cu);
+  };
+  // one product alone, on the tiles plan() gives it (k-tiles counted 32 deep whatever the kernel)
+  auto alone = [&](const Plan& pl, int M, int N, int K) {
+    const int bm = pl.tile == T128x128 ? 128 : 256;
+    const int bn = pl.tile == T256x256 || pl.tile == TSCHED ? 256 : pl.tile == T256x192 ? 192 : 128;
+    const int per = pl.tile == T128x128 ? 2 : 1;
+    return waves(tiles(M, N, bm, bn) * pl.splits, per) * (K / pl.splits / SBK + 32) + (pl.splits > 1 ? 16 : 0);
+  };
   const Plan a = plan(M0, N0, K0, false, false, EPI_STORE, true);
   const Plan b = plan(M1, N1, K1, false, false, EPI_STORE, true);
-  if (a.tile != TSCHED || a.splits < 2) return pp;
-  auto tiles = [](int m, int n, int bm, int bn) { return (long)((m + bm - 1) / bm) * ((n + bn - 1) / bn); };
+  long best_cost = alone(a, M0, N0, K0) + alone(b, M1, N1, K1);
   const long t0 = tiles(M0, N0, 256, 256), t1 = tiles(M1, N1, 256, 256);
-  const long blocks0 = t0 * a.splits;
-  int s1 = 2;
-  while (s1 < 8 && K1 / s1 > K0 / a.splits) s1 *= 2;
-  if (K1 % (s1 * SBK) != 0 || K1 / s1 < 1024 || blocks0 + t1 * s1 > kCUs) return pp;
-  if (!sched_ok(M0, N0, K0, false, lda0, false, ldb0, a.splits) ||
-      !sched_ok(M1, N1, K1, false, lda1, false, ldb1, s1))
-    return pp;
-  auto waves = [](long blocks, int per_cu) { return (blocks + (long)kCUs * per_cu - 1) / ((long)kCUs * per_cu); };
-  // p1 alone, on the tiles plan() gives it (k-tiles counted 32 deep whatever the kernel)
-  const int bm1 = b.tile == T128x128 ? 128 : 256;
-  const int bn1 = b.tile == T256x256 || b.tile == TSCHED ? 256 : b.tile == T256x192 ? 192 : 128;
-  const int per1 = b.tile == T128x128 ? 2 : 1;
-  const long alone = waves(blocks0, 1) * (K0 / a.splits / SBK + 32) +
-                     waves(tiles(M1, N1, bm1, bn1) * b.splits, per1) * (K1 / b.splits / SBK + 32);
-  const long paired = std::max(K0 / a.splits, K1 / s1) / SBK + 32;
-  if (paired >= alone) return pp;
-  pp.ok = true;
-  pp.s0 = a.splits;
-  pp.s1 = s1;
-  pp.ws1 = ((size_t)a.splits * M0 * N0 * 4 + 255) & ~(size_t)255;
-  return pp;
+  auto consider = [&](int s0, int s1) {
+    if (K0 % (s0 * SBK) != 0 || K1 % (s1 * SBK) != 0 || K0 / s0 < 1024 || K1 / s1 < 1024) return;
+    // a pair is there to fill the chip: at most a quarter of its CUs idle
+    if (t0 * s0 + t1 * s1 > kCUs || 4 * (t0 * s0 + t1 * s1) < 3L * kCUs) return;
+    if (!sched_ok(M0, N0, K0, false, lda0, false, ldb0, s0) || !sched_ok(M1, N1, K1, false, lda1, false, ldb1, s1))
+      return;
+    const long c = std::max(K0 / s0, K1 / s1) / SBK + 32 + (s0 > 1 ? 32 : 0);
+    if (c >= best_cost) return;
+    best_cost = c;
+    best.ok = true;
+    best.s0 = s0;
+    best.s1 = s1;
+    best.ws1 = s0 > 1 ? ((size_t)s0 * M0 * N0 * 4 + 255) & ~(size_t)255 : 0;
+  };
+  consider(1, 1);
+  for (int sp = 2; sp <= 8; sp *= 2) consider(sp, sp);
+  if (a.tile == TSCHED && a.splits >= 2) {
+    int s1 = 2;
+    while (s1 < 8 && K1 / s1 > K0 / a.splits) s1 *= 2;
+    consider(a.splits, s1);
+  }
+  return best;
 }
 
 template <bool AKC, bool BKC, int EPI>
@@ -1137,7 +1153,7 @@ size_t gemm_ws_bytes(int dtype, int M, int N, int K, bool a_kc, bool b_kc, int k
 size_t gemm_wgrad_pair_ws_bytes(int dtype, const GemmProb& p0, const GemmProb& p1) {
   if (dtype == 0) return 0;
   const PairPlan pp = pair_plan(p0.M, p0.N, p0.K, p0.lda, p0.ldb, p1.M, p1.N, p1.K, p1.lda, p1.ldb);
-  if (pp.ok) return pp.ws1 + (size_t)pp.s1 * p1.M * p1.N * 4;
+  if (pp.ok) return pp.s0 > 1 ? pp.ws1 + (size_t)pp.s1 * p1.M * p1.N * 4 : 0;
   return std::max(gemm_ws_bytes(dtype, p0.M, p0.N, p0.K, false, false, EPI_STORE),
                   gemm_ws_bytes(dtype, p1.M, p1.N, p1.K, false, false, EPI_STORE));
 }
@@ -1167,10 +1183,19 @@ hipError_t gemm_wgrad_pair(int dtype, const GemmProb& p0, const GemmProb& p1, vo
     q[i].ksplit = splits[i];
     q[i].blocks = ((g.M + 255) / 256) * ((g.N + 255) / 256) * splits[i];
     q[i].ep = Epi();
-    q[i].ep.ws = wsp[i];
+    if (pp.s0 > 1) {
+      q[i].ep.ws = wsp[i];
+    } else {
+      q[i].ep.out = g.e.out;
+      q[i].ep.ldo = g.e.ldo;
+    }
   }
-  hipLaunchKernelGGL((gemm_bf16_sched_pair_kernel<false, false, EPI_PARTIAL>),
-                     dim3((unsigned)(q[0].blocks + q[1].blocks)), dim3(256), 0, st, q[0], q[1]);
+  const dim3 grid((unsigned)(q[0].blocks + q[1].blocks));
+  if (pp.s0 == 1) {
+    hipLaunchKernelGGL((gemm_bf16_sched_pair_kernel<false, false, EPI_STORE>), grid, dim3(256), 0, st, q[0], q[1]);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((gemm_bf16_sched_pair_kernel<false, false, EPI_PARTIAL>), grid, dim3(256), 0, st, q[0], q[1]);
   hipError_t r = hipGetLastError();
   for (int i = 0; i < 2 && r == hipSuccess; ++i) {
     const GemmProb& g = *src[i];

@@ -79,10 +79,11 @@ struct GemmProb {
   int ldb;
   Epi e;
 };
-// Two independent weight gradients. When the first one's tiles leave CUs idle
-// and the second fits beside it, both run in one grid of the scheduled kernel
-// (split contractions, summed in a fixed order); otherwise one after the
-// other, as gemm() runs them. ws: gemm_wgrad_pair_ws_bytes bytes.
+// Two independent weight gradients. When their tiles fit the chip together
+// -- split (partial tiles summed in a fixed order) beside a first one whose
+// tiles leave CUs idle, or both whole -- they run in one grid of the
+// scheduled kernel; otherwise one after the other, as gemm() runs them. ws:
+// gemm_wgrad_pair_ws_bytes bytes.
 hipError_t gemm_wgrad_pair(int dtype, const GemmProb& p0, const GemmProb& p1, void* ws, hipStream_t st);
 size_t gemm_wgrad_pair_ws_bytes(int dtype, const GemmProb& p0, const GemmProb& p1);
 // Column-tile width the bf16 GEMM uses for this problem (the tiles_n of
