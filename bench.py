@@ -439,7 +439,7 @@ def main():
     ms_eager, per_step_eager, wall, kern, graph = run_gpu(
         cfg, args.steps, args.warmup,
         trace_what=[mtb.TRACE_FC1_FWD, mtb.TRACE_LN1_FWD, mtb.TRACE_ATTN_FWD, mtb.TRACE_ATTN_SEG,
-                    mtb.TRACE_FFN_SEG, mtb.TRACE_BWD, mtb.TRACE_LN1_BWD],
+                    mtb.TRACE_FFN_SEG, mtb.TRACE_BWD, mtb.TRACE_LN1_BWD, mtb.TRACE_FC2_WGRAD],
         graph_steps=0 if args.eager else args.steps)
     ms, per_step = (ms_eager, per_step_eager) if graph is None else graph
     tflops = flops / (ms * 1e-3) / 1e12
@@ -458,6 +458,10 @@ def main():
     attn_ms = kern[mtb.TRACE_ATTN_FWD]
     lnb_bytes = T * H * 2 * 4 + T * 8          # read dy, x, dres, write dx (bf16), read mu/rstd
     lnb_ms = kern[mtb.TRACE_LN1_BWD]
+    # the fc2 and fc1 weight gradients, traced together (one grouped launch where
+    # their tiles fill the chip together, else one launch each)
+    wg_flops = 2.0 * T * H * F + 2.0 * T * Fu * H
+    wg_ms = kern[mtb.TRACE_FC2_WGRAD]
     xcfg = inputs.C5_XENT
     xent_ms = run_xent(xcfg, args.steps, args.warmup)
     xent_bytes = 6 * xcfg.n_tokens * xcfg.v_local   # X1 reads 2 B/logit, X3 reads 2 + writes 2
@@ -509,6 +513,13 @@ def main():
                 "achieved_GBs": round(ln_bytes / (ln_ms * 1e-3) / 1e9, 1), "peak_GBs": PEAK_HBM_GBS},
             "attn_fwd": {"bound": "mfma", "avg_ms": round(attn_ms, 5),
                          "achieved_TFLOPs": round(attn_flops / (attn_ms * 1e-3) / 1e12, 1)},
+            "mlp_wgrad": {"bound": "mfma",
+                          "what": ("fc2 and fc1 weight gradients (the step's longest launch when they "
+                                   "run as one grouped launch; fc2's left operand is the synthetic "
+                                   "loss's constant cotangent, which runs faster than varied data)"),
+                          "avg_ms": round(wg_ms, 5),
+                          "achieved_TFLOPs": round(wg_flops / (wg_ms * 1e-3) / 1e12, 1),
+                          "peak_TFLOPs": PEAK_BF16_TFLOPS},
             "ln1_bwd": None if cfg.norm == "post" else {
                 "bound": "hbm", "avg_ms": round(lnb_ms, 5),
                 "achieved_GBs": round(lnb_bytes / (lnb_ms * 1e-3) / 1e9, 1), "peak_GBs": PEAK_HBM_GBS},
