@@ -78,7 +78,9 @@ def test_bf16_small_shapes(i):
 # their residual rows on the scheduled kernel past both ragged edges (a
 # 128-row last tile row, a 192-wide last tile column) and the grouped weight
 # gradients split 8064 tokens four ways (63 k-tiles each, entering the loop
-# body at its second slot).
+# body at its second slot); SwiGLU at 4032 tokens, where the SwiGLU′ epilogue
+# of the fc2 data gradient takes its prefetched gate/up rows past the last
+# full tile row.
 SCHED_RAGGED = [
     dict(batch=3, seq=1344, hidden=1280, q_heads=10, kv_heads=2, head_dim=128, ffn=3072, causal=True),
     dict(batch=2, seq=2048, hidden=1344, q_heads=21, kv_heads=3, head_dim=64, ffn=2112, bias=True,
@@ -86,6 +88,8 @@ SCHED_RAGGED = [
     dict(batch=2, seq=2048, hidden=1984, q_heads=4, kv_heads=4, head_dim=128, ffn=576, causal=True),
     dict(batch=3, seq=2688, hidden=1984, q_heads=4, kv_heads=4, head_dim=128, ffn=576, causal=True,
          bias=True),
+    dict(batch=3, seq=1344, hidden=1280, q_heads=10, kv_heads=2, head_dim=128, ffn=3072, act="swiglu",
+         causal=True),
 ]
 
 

@@ -128,7 +128,13 @@ MTB_DEV float gelu_grad_f(float u) {
   const float cdf = 0.5f * (1.0f + erf_as(u * 0.70710678118654752f, e));
   return cdf + u * 0.39894228040143268f * e;
 }
-MTB_DEV float sigmoid_f(float u) { return 1.0f / (1.0f + expf(-u)); }
+// logistic sigmoid 1 / (1 + e^-u) from the hardware base-2 exponential and
+// reciprocal (a few instructions instead of the library exp and an IEEE
+// division, which made the SwiGLU epilogues VALU-bound); u -> -inf gives
+// rcp(inf) = 0, u -> +inf gives 1
+MTB_DEV float sigmoid_f(float u) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-u * 1.4426950408889634f));
+}
 
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
 // easy as 1, 2, 3", SC 2011): ten rounds; each multiplies counter words 0 and

@@ -311,6 +311,62 @@ MTB_DEV void epi_rows(const Epi& e, const Staged<BN>& st, int M, int N, int mc, 
   }
 }
 
+// EPI_DSWIGLU's saved gate and up pre-activations for half of a staged
+// chunk's row items (same item order as epi_rows), loaded before that half's
+// stores; the whole chunk's would take twice the registers.
+template <int BN, int CR, int NT>
+struct SwiRows {
+  static constexpr int IPR = BN / 8, ITEMS = CR * IPR / NT, HALF = ITEMS / 2;
+  static_assert(CR * IPR % NT == 0 && ITEMS % 2 == 0, "two halves of whole row items per thread");
+  u32x4 g[HALF], u[HALF];
+  MTB_DEV void load(const Epi& e, int M, int N, int mc, int n0, int tid, int half) {
+#pragma unroll
+    for (int j = 0; j < HALF; ++j) {
+      const int it = tid + (half * HALF + j) * NT, r = it / IPR, nl = (it % IPR) * 8;
+      const int m = mc + r, n = n0 + nl;
+      g[j] = u32x4{0u, 0u, 0u, 0u};
+      u[j] = g[j];
+      if (m < M && n < N) {
+        const bf16_t* q = reinterpret_cast<const bf16_t*>(e.aux) + (size_t)m * e.ldaux + (n >> 4) * 32 + (n & 15);
+        g[j] = *reinterpret_cast<const u32x4*>(q);
+        u[j] = *reinterpret_cast<const u32x4*>(q + 16);
+      }
+    }
+  }
+};
+
+// Row phase of EPI_DSWIGLU with the pre-activations prefetched: pre holds the
+// first half of the chunk's items on entry; the second half is requested
+// after the first half's stores.
+template <int BN, int CR, int NT>
+MTB_DEV void epi_rows_dswiglu_pre(const Epi& e, const Staged<BN>& st, int M, int N, int mc, int n0,
+                                  int tid, SwiRows<BN, CR, NT>& pre) {
+  constexpr int IPR = BN / 8, HALF = SwiRows<BN, CR, NT>::HALF;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (h == 1) pre.load(e, M, N, mc, n0, tid, 1);
+#pragma unroll
+    for (int j = 0; j < HALF; ++j) {
+      const int it = tid + (h * HALF + j) * NT, r = it / IPR, nl = (it % IPR) * 8;
+      const int m = mc + r, n = n0 + nl;
+      if (m >= M || n >= N) continue;
+      float v[8], dg[8], du[8];
+      st.get8(r, nl, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t gw = pre.g[j][i >> 1], uw = pre.u[j][i >> 1];
+        const float ug = (i & 1) ? hi_f(gw) : lo_f(gw), uu = (i & 1) ? hi_f(uw) : lo_f(uw);
+        const float sg = sigmoid_f(ug);
+        dg[i] = v[i] * uu * sg * (1.0f + ug * (1.0f - sg));
+        du[i] = v[i] * ug * sg;
+      }
+      const int gp = (n >> 4) * 32 + (n & 15);
+      out8(e.out, (size_t)m * e.ldo + gp, dg);
+      out8(e.out, (size_t)m * e.ldo + gp + 16, du);
+    }
+  }
+}
+
 // Row phase of a plain store (residual) or EPI_DGELU (u) with that operand
 // prefetched (pre): the same items and arithmetic as epi_rows, item j of this
 // thread taking pre.q[j].
@@ -548,7 +604,7 @@ MTB_DEV void gemm_epilogue(const f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32], vo
   constexpr bool COLS = EPI == EPI_STORE && AKC;
   static_assert(!COLS || CR % 64 == 0, "transposed copy needs whole 64-token groups per chunk");
   const Staged<BN> st{reinterpret_cast<float*>(smem)};
-  // RPRE (plain stores with a residual, EPI_DGELU): a chunk's row operand is
+  // RPRE (plain stores with a residual, EPI_DGELU, EPI_DSWIGLU): a chunk's row operand is
   // requested in full before any of its stores -- chunk 0's before the
   // staging, chunk c + 1's right after chunk c's stores (vector memory
   // operations complete in issue order, so a load issued after a store is
@@ -566,6 +622,13 @@ MTB_DEV void gemm_epilogue(const f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32], vo
   const bool has_pre = PRE && (EPI == EPI_STORE ? ep.resid : ep.aux) != nullptr;
   if constexpr (PRE) {
     if (has_pre) load_pre(m0);
+  }
+  // EPI_DSWIGLU: half a chunk of gate/up pre-activations at a time
+  constexpr bool PRE_SWI = RPRE && EPI == EPI_DSWIGLU;
+  SwiRows<BN, CR, NT> spre;
+  const bool has_swi = PRE_SWI && ep.aux != nullptr;
+  if constexpr (PRE_SWI) {
+    if (has_swi) spre.load(ep, M, N, m0, n0, tid, 0);
   }
 #pragma unroll 1
   for (int c0 = 0; c0 < BM; c0 += CR) {
@@ -593,6 +656,8 @@ MTB_DEV void gemm_epilogue(const f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32], vo
       epi_xent_stats<BN, CR, NT>(ep, st, M, N, m0 + c0, n0, bt.tn, bt.tiles_n, tid);
     else if (has_pre)
       epi_rows_pre<PRE ? EPI : EPI_STORE, BN, CR, NT>(ep, st, M, N, m0 + c0, n0, tid, pre);
+    else if (has_swi)
+      epi_rows_dswiglu_pre<BN, CR, NT>(ep, st, M, N, m0 + c0, n0, tid, spre);
     else
       epi_rows<EPI, BN, CR, NT>(ep, st, M, N, m0 + c0, n0, tid);
     if constexpr (COLS) {
@@ -600,6 +665,9 @@ MTB_DEV void gemm_epilogue(const f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32], vo
     }
     if constexpr (PRE) {
       if (has_pre && c0 + CR < BM) load_pre(m0 + c0 + CR);
+    }
+    if constexpr (PRE_SWI) {
+      if (has_swi && c0 + CR < BM) spre.load(ep, M, N, m0 + c0 + CR, n0, tid, 0);
     }
   }
 }
