@@ -604,13 +604,14 @@ MTB_DEV void gemm_epilogue(const f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32], vo
   constexpr bool COLS = EPI == EPI_STORE && AKC;
   static_assert(!COLS || CR % 64 == 0, "transposed copy needs whole 64-token groups per chunk");
   const Staged<BN> st{reinterpret_cast<float*>(smem)};
-  // RPRE (plain stores with a residual, EPI_DGELU, EPI_DSWIGLU): a chunk's row operand is
-  // requested in full before any of its stores -- chunk 0's before the
-  // staging, chunk c + 1's right after chunk c's stores (vector memory
-  // operations complete in issue order, so a load issued after a store is
-  // waited for behind that store: one wait per chunk instead of one per row
-  // item). For kernels whose accumulators live in AGPRs; in the 2x4-wavefront
-  // kernel the extra registers spill.
+  // RPRE (plain stores with a residual, EPI_DGELU, EPI_DSWIGLU): a chunk's
+  // row operand is requested in full before any of its stores -- chunk 0's
+  // before the staging, chunk c + 1's right after chunk c's stores (vector
+  // memory operations complete in issue order, so a load issued after a store
+  // is waited for behind that store: one wait per chunk instead of one per
+  // row item); EPI_DSWIGLU's two operands go half a chunk at a time (one wait
+  // per half). For kernels whose accumulators live in AGPRs; in the
+  // 2x4-wavefront kernel the extra registers spill.
   constexpr bool PRE = RPRE && (EPI == EPI_STORE || EPI == EPI_DGELU);
   RowOperand<BN, CR, NT> pre;
   auto load_pre = [&](int mc) {
@@ -1092,9 +1093,9 @@ hipError_t launch_sched(int M, int N, int K, const void* A, int lda, const void*
 //    stored directly.
 // A form is used when its blocks fill at least three quarters of the chip
 // without exceeding it and a simple cost model puts it below the two launches
-// one after the other: per wave of blocks, the
-// k-tiles of one block plus 32 k-tiles of fixed (prologue and epilogue) cost,
-// and 16 k-tiles per split reduction pass.
+// one after the other: per wave of blocks, the k-tiles of one block plus 32
+// k-tiles of fixed (prologue and epilogue) cost, and 16 k-tiles per split
+// reduction pass.
 struct PairPlan {
   bool ok = false;
   int s0 = 1, s1 = 1;
