@@ -134,11 +134,13 @@ def interleave(a, b):
     return out
 
 
-def loop(la, lb, reads_first=False, copies_step=0):
+def loop(la, lb, reads_first=False, copies_step=0, early=0):
     """the asm lines for operand layouts la, lb ("kc" / "mn"). The defaults are
     the schedule described above; reads_first issues a step's fragment reads
     right after its first MFMA instead of spreading them, copies_step = 1 moves
-    the copies into the second step (measurement variants)."""
+    the copies into the second step, early = n issues a tile's first n MFMAs
+    (whose fragments are already in registers) before its copy wait and
+    barrier (measurement variants)."""
     nread = sum(4 if l == "kc" else 8 for l in (la, lb))   # LDS reads per 16-deep step
     wait_step = f"s_waitcnt lgkmcnt({min(nread, 15)})"
     L = ["s_nop 4"]   # accumulator initialisation (VALU/AGPR writes) -> MFMA
@@ -165,13 +167,19 @@ def loop(la, lb, reads_first=False, copies_step=0):
         X, Y = u & 1, (u + 1) & 1
         nxt, dst = (u + 1) % STAGES, (u + STAGES - 1) % STAGES
         L.append(f"L%=_slot{u}:")
+        if early:
+            L.append(wait_step)
+            L += [mfma(X, 0, i, j) for i, j in pairs[:early]]
         L.append(f"s_waitcnt vmcnt({8 * (STAGES - 3)})")
         L.append("s_barrier")
-        L.append(wait_step)
+        if not early:
+            L.append(wait_step)
         for kk in range(2):
             r = reads(la, 0, Y, nxt, kk) + reads(lb, 1, Y, nxt, kk)
             c = copies(dst) + [advance()] if kk == copies_step else []
             m = [mfma(X, kk, i, j) for i, j in pairs]
+            if kk == 0 and early:
+                m = m[early:]
             if reads_first:
                 L += [m[0]] + [x for u in r for x in u] + spread(m[1:], c)
             else:
