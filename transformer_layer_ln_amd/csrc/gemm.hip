@@ -1183,8 +1183,11 @@ hipError_t launch_bf16(int M, int N, int K, const void* A, int lda, const void* 
     } else {
       r = launch_cfg<128, 128, 2, 2, 2, AKC, BKC, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, e, st, pl.splits);
       if (r != hipSuccess) return r;
-      const unsigned tiles = (unsigned)(((M + 127) / 128) * ((N + 127) / 128));
-      hipLaunchKernelGGL((splitk_epi_kernel<128, 128, 256, EPI>), dim3(tiles), dim3(256), 0, st, M, N,
+      // 64-row pieces: twice the workgroups of the GEMM's tiles, two per CU, so
+      // more of the partial-tile loads are in flight (15.0 -> 11.5 us for the
+      // 8192 x 512 projection dgrad)
+      const unsigned tiles = (unsigned)(((M + 63) / 64) * ((N + 127) / 128));
+      hipLaunchKernelGGL((splitk_epi_kernel<64, 128, 256, EPI>), dim3(tiles), dim3(256), 0, st, M, N,
                          pl.splits, (const float*)e.ws, e);
     }
     return hipGetLastError();
