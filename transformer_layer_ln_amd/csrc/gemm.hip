@@ -1016,11 +1016,20 @@ struct Plan {
 // fp32 partial tiles are summed in a fixed order by a second pass that also
 // runs the epilogue. Each extra split costs 8 bytes per output element of
 // partial-tile traffic. (At the seq-512 share, where every GEMM is 4096 x
-// <=1024 x <=4096, splitting down to 512-deep parts made the step slower,
-// 0.356 -> 0.401 ms: a block's fixed costs, not its k-loop, dominate there.)
+// <=1024 x <=4096, splitting every product down to 512-deep parts made the
+// step slower, 0.356 -> 0.401 ms: a block's fixed costs, not its k-loop,
+// dominate there; only the gradients that would leave at least half of the
+// chip idle go below 1024, see small_ok.)
 Plan plan(int M, int N, int K, bool a_kc, bool b_kc, int kind, bool split_ok, bool resid = false) {
   auto tl = [&](int bm, int bn) { return (long)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
   auto depth_ok = [&](int s) { return K % (s * BK) == 0 && K / s >= 1024; };
+  // parts down to 512 deep for weight and data gradients whose blocks would
+  // otherwise leave at least half of the chip's block slots idle (the
+  // seq-512 share's 4096-token products: its four weight gradients and the
+  // projection dgrad, step 0.354 -> 0.334 ms); forward products keep 1024
+  // (the QKV forward's extra pass for its transposed copy cost more than the
+  // split gained)
+  auto small_ok = [&](int s) { return K % (s * BK) == 0 && K / s >= 512; };
   auto sched_depth = [&](int s) { return K % (s * SBK) == 0 && K / s >= 1024; };
   const long t256 = tl(256, 256);
   if (!a_kc && !b_kc) {
@@ -1033,7 +1042,8 @@ Plan plan(int M, int N, int K, bool a_kc, bool b_kc, int kind, bool split_ok, bo
     const long t2 = tl(256, 128);
     if (split_ok && kind == EPI_STORE && t2 <= kCUs / 2 && K % BK == 0) {
       int s = 1;
-      while (s < 8 && t2 * s * 4 < 3L * kCUs && depth_ok(2 * s)) s *= 2;
+      while (s < 8 && t2 * s * 4 < 3L * kCUs && (depth_ok(2 * s) || (t2 * s * 2 <= kCUs && small_ok(2 * s))))
+        s *= 2;
       if (s > 1) return {T256x128, s};
     }
     if (K >= 1024 && t2 >= kCUs) return {T256x128, 1};
@@ -1042,7 +1052,8 @@ Plan plan(int M, int N, int K, bool a_kc, bool b_kc, int kind, bool split_ok, bo
   const long t128 = tl(128, 128);
   if (split_ok && a_kc && kind == EPI_STORE && t128 <= kCUs && t256 < kCUs && K % BK == 0) {
     int s = 1;
-    while (s < 4 && t128 * s < 2L * kCUs && depth_ok(2 * s)) s *= 2;
+    while (s < 4 && t128 * s < 2L * kCUs && (depth_ok(2 * s) || (!b_kc && t128 * s < kCUs && small_ok(2 * s))))
+      s *= 2;
     if (s > 1) return {T128x128, s};
   }
   const double f128 = 0.85 * fill(t128, 2);
