@@ -79,9 +79,9 @@ struct GemmProb {
   int ldb;
   Epi e;
 };
-// Two independent weight gradients. When their tiles fit the chip together
-// -- split (partial tiles summed in a fixed order) beside a first one whose
-// tiles leave CUs idle, or both whole -- they run in one grid of the
+// Two independent weight gradients. When their blocks fill the chip together
+// -- both contractions split (partial tiles summed in a fixed order), or both
+// whole -- and a per-wave cost model favours it, they run in one grid of the
 // scheduled kernel; otherwise one after the other, as gemm() runs them. ws:
 // gemm_wgrad_pair_ws_bytes bytes.
 hipError_t gemm_wgrad_pair(int dtype, const GemmProb& p0, const GemmProb& p1, void* ws, hipStream_t st);
