@@ -250,6 +250,21 @@ def test_schedule_symbolic_execution(name, la, lb, KT):
         assert tiles == list(range(KT)) + [KT - 1] * (n - KT), f"copy sequence of {key}: {tiles}"
 
 
+@pytest.mark.parametrize("name,la,lb", GEN.LAYOUTS)
+@pytest.mark.parametrize("variant", [dict(early=2), dict(reads_first=True), dict(copies_step=1)])
+def test_measurement_variants_are_valid_schedules(name, la, lb, variant):
+    """The generator's measurement variants (timed against the default in
+    alternating runs) obey the same waits, barriers and k-tile order."""
+    lines = GEN.loop(la, lb, **variant)
+    for KT in (1, 2, 3, 5, 13):
+        w = Wave({"a": la, "b": lb}, KT)
+        w.run(lines)
+        assert not w.lgkm and not w.vm
+        want = [(t, kk) for t in range(KT) for kk in (0, 1)]
+        for ij, got in w.acc.items():
+            assert got == want, f"{variant} KT {KT} accumulator c{ij[0]}{ij[1]}"
+
+
 def test_symbolic_execution_catches_a_short_wait():
     """The checker itself: dropping the wait before the second step's MFMAs
     (an MFMA would use fragments still in flight) must be reported."""
