@@ -251,7 +251,8 @@ def test_schedule_symbolic_execution(name, la, lb, KT):
 
 
 @pytest.mark.parametrize("name,la,lb", GEN.LAYOUTS)
-@pytest.mark.parametrize("variant", [dict(early=2), dict(reads_first=True), dict(copies_step=1)])
+@pytest.mark.parametrize("variant", [dict(early=2), dict(reads_first=True), dict(copies_step=1),
+                                     dict(order="col"), dict(order="snake")])
 def test_measurement_variants_are_valid_schedules(name, la, lb, variant):
     """The generator's measurement variants (timed against the default in
     alternating runs) obey the same waits, barriers and k-tile order."""

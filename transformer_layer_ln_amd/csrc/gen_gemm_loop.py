@@ -134,13 +134,22 @@ def interleave(a, b):
     return out
 
 
-def loop(la, lb, reads_first=False, copies_step=0, early=0):
+ORDERS = {
+    "row": [(i, j) for i in range(4) for j in range(4)],
+    "col": [(i, j) for j in range(4) for i in range(4)],
+    "snake": [(i, j if i % 2 == 0 else 3 - j) for i in range(4) for j in range(4)],
+}
+
+
+def loop(la, lb, reads_first=False, copies_step=0, early=0, order="row"):
     """the asm lines for operand layouts la, lb ("kc" / "mn"). The defaults are
     the schedule described above; reads_first issues a step's fragment reads
     right after its first MFMA instead of spreading them, copies_step = 1 moves
     the copies into the second step, early = n issues a tile's first n MFMAs
     (whose fragments are already in registers) before its copy wait and
-    barrier (measurement variants)."""
+    barrier, order picks the accumulators' MFMA order within a step
+    (measurement variants)."""
+    pairs = ORDERS[order]
     nread = sum(4 if l == "kc" else 8 for l in (la, lb))   # LDS reads per 16-deep step
     wait_step = f"s_waitcnt lgkmcnt({min(nread, 15)})"
     L = ["s_nop 4"]   # accumulator initialisation (VALU/AGPR writes) -> MFMA
