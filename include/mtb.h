@@ -30,9 +30,10 @@
  *   log-sum-exp and the cross-entropy statistics/loss are always fp32.
  * Streams: every kernel is enqueued on `hip_stream` (a hipStream_t; NULL =
  *   the default stream). Calls are asynchronous: no host synchronisation.
- *   Apart from a thread-local error message and the benchmark trace
- *   (mtb_trace_arm), the library holds no mutable global state, so calls on
- *   different streams with different buffers may run concurrently.
+ *   Apart from the thread-local error message and the thread-local
+ *   benchmark trace (mtb_trace_arm), the library holds no mutable global
+ *   state, so calls on different streams with different buffers may run
+ *   concurrently.
  * Errors: argument checks run before any launch; on failure nothing is
  *   launched and MTB_EINVAL (bad pointer, size or alignment) or
  *   MTB_EUNSUPPORTED (a valid shape the library has no kernel for) is
@@ -263,11 +264,14 @@ mtb_status mtb_block_bwd(const mtb_cfg *cfg, const mtb_weights *w, int32_t phase
  *     dlogits = (exp(z - M)/S - onehot(target)) * dloss[n]  (dloss != NULL).
  *   MTB_XENT_ALL: PARTIAL, then the hook's MAX of m, the local rescale
  *     s *= exp(m_r - M), the hook's SUMs of s and t, then FINISH.
- *     stats must hold 4n floats here (the last n keep the local max).
+ *     With a hook, stats must hold 4n floats (the last n keep this
+ *     shard's max between the MAX and the rescale); with NULL comm 3n.
+ *     (The [3][n] statistics layout is the same in every phase; the fourth
+ *     row exists only because the hook reduces in place.)
  * dlogits may alias logits (read-before-write per element). */
-#define MTB_XENT_ALL 0
-#define MTB_XENT_PARTIAL 1
-#define MTB_XENT_FINISH 2
+#define MTB_XENT_PARTIAL 0
+#define MTB_XENT_FINISH 1
+#define MTB_XENT_ALL 2
 mtb_status mtb_vocab_xent(int64_t n_tokens, int64_t v_local, int64_t v_start, int32_t dtype,
                           int32_t phase, const void *logits, const int64_t *target, float *stats,
                           float *loss, const float *dloss, void *dlogits, const mtb_comm *comm,
@@ -290,7 +294,8 @@ mtb_status mtb_vocab_xent_combine(int64_t n_tokens, int32_t n_shards, const floa
  * Forward: the logits are computed tile by tile and each tile is reduced in
  * the GEMM epilogue to per-token (max, sum exp, target logit); the
  * [n_tokens, v_local] logits are never stored. Then, exactly as
- * mtb_vocab_xent(MTB_XENT_ALL): stats [4][n_tokens] ends up holding the
+ * mtb_vocab_xent(MTB_XENT_ALL): stats [3][n_tokens] ([4][n_tokens] with a
+ * hook) ends up holding the
  * combined (M, S, T) over the shards (the hook's MAX, local rescale, SUM,
  * SUM; NULL comm: one shard), and loss[n] = log S + M - T if loss != NULL.
  *
@@ -350,8 +355,9 @@ mtb_status mtb_vocab_embed_bwd(int64_t n_tokens, int64_t v_local, int64_t v_star
                                int32_t dtype, const int64_t *ids, const void *dout, void *dtable,
                                void *workspace, void *hip_stream);
 
-/* Benchmark instrumentation (not for concurrent use; process-wide state).
- * While armed, every launch of the kernel class `what` records
+/* Benchmark instrumentation. The armed state is per host thread (like the
+ * error message): only calls made on the arming thread are traced, and
+ * other threads' calls are unaffected. While armed, every launch of the kernel class `what` records
  * begin_events[i] before it and end_events[i] after it on the launch's
  * stream, for i = 0, 1, ... up to n - 1 (later launches are not recorded).
  * The events are caller-created hipEvent_t handles. mtb_trace_disarm()

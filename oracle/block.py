@@ -414,6 +414,8 @@ def block_backward(G, cache):
 
 
 def block_loss_mean(out):
-    """The listing's loss: mean over every element of out ([Lab06] sec. 2 step (8));
-    its cotangent is 1 / numel everywhere."""
-    return out.mean()
+    """The listing's loss ([Lab06] sec. 2 step (8)): the mean over every
+    element of out. Returns (loss, dL/d out); the gradient of a mean is
+    1 / numel in every position, whatever out holds."""
+    out = np.asarray(out, np.float64)
+    return float(out.sum() / out.size), np.full(out.shape, 1.0 / out.size)

@@ -33,6 +33,18 @@ def rel_err(gpu, ref):
     return float(np.max(np.abs(gpu - ref)) / (den if den > 0 else 1.0))
 
 
+def elem_err(gpu, ref, floor=1e-3):
+    """Largest elementwise relative error, each element's |ref| floored at
+    floor * max|ref| (a plain elementwise ratio is undefined where ref is 0).
+    Logged beside rel_err, which is what the tolerance applies to: it shows
+    errors concentrated in the small entries of a tensor."""
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    m = np.max(np.abs(ref))
+    den = np.maximum(np.abs(ref), floor * (m if m > 0 else 1.0))
+    return float(np.max(np.abs(gpu - ref) / den))
+
+
 def zero_sum_err(gpu, terms):
     """Error of a gradient that is exactly zero in exact arithmetic (the key
     bias: softmax ignores a shift shared by a whole row of scores), measured
@@ -120,9 +132,13 @@ def check_rank_vs_oracle(cfg, w_split, x, G, tol=None, comm=None, label="", tp_r
     ref_out, cache = ob.block_forward(x, w_split, R=1, tp_rank=tp_rank, **oracle_kw(cfg))
     ref_dx, ref_g = ob.block_backward(G, cache)
     errs = {"out": rel_err(out, ref_out), "dx": rel_err(dx, ref_dx)}
+    elem = {"out": elem_err(out, ref_out), "dx": elem_err(dx, ref_dx)}
     for k in w_split:
         errs[k] = rel_err(grads[k], ref_g[k]) if k != "bk" else zero_sum_err(grads[k], ref_g["_dk_tokens"])
+        if k != "bk":
+            elem[k] = elem_err(grads[k], ref_g[k])
     say("   errors:", {k: f"{v:.2e}" for k, v in errs.items()})
+    say("   elementwise (floor 1e-3 max|ref|, logged only):", {k: f"{v:.2e}" for k, v in elem.items()})
     bad = {k: v for k, v in errs.items() if not v <= tol}
     assert not bad, f"above tolerance {tol}: {bad}"
     return errs

@@ -218,3 +218,40 @@ def test_lmhead_workspace_query():
     # the backward's bf16 [n, v_local] gradient of the logits dominates
     assert mtb.lmhead_xent_workspace_bytes(8192, 4096, 16032) == 8192 * 16032 * 2
     assert mtb.lmhead_xent_workspace_bytes(64, 4096, 8) == 64 * 8 * 2
+
+
+def header_constants():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    return {k: int(v) for k, v in re.findall(r"#define\s+(MTB_\w+)\s+(-?\d+)\b", text)}
+
+
+def test_constants_match_the_documented_numbering():
+    """The enumerations of the boundary: status codes, dtypes, activations,
+    reduction ops, block phases (ALL, then the three segments between the
+    reduction points) and the cross-entropy phases (0 = partial statistics,
+    1 = finish from combined statistics, 2 = all with the hook). The binding
+    uses the same numbers."""
+    c = header_constants()
+    want = {
+        "MTB_OK": 0, "MTB_EINVAL": 1, "MTB_EUNSUPPORTED": 2, "MTB_EHIP": 3, "MTB_ECOMM": 4,
+        "MTB_F32": 0, "MTB_BF16": 1, "MTB_ACT_GELU": 0, "MTB_ACT_SWIGLU": 1,
+        "MTB_OP_SUM": 0, "MTB_OP_MAX": 1,
+        "MTB_PHASE_ALL": 0, "MTB_PHASE_SEG0": 1, "MTB_PHASE_SEG1": 2, "MTB_PHASE_SEG2": 3,
+        "MTB_XENT_PARTIAL": 0, "MTB_XENT_FINISH": 1, "MTB_XENT_ALL": 2,
+    }
+    for k, v in want.items():
+        assert c[k] == v, (k, c[k], v)
+    binding = {"MTB_PHASE_ALL": mtb.PHASE_ALL, "MTB_PHASE_SEG0": mtb.PHASE_SEG0,
+               "MTB_PHASE_SEG1": mtb.PHASE_SEG1, "MTB_PHASE_SEG2": mtb.PHASE_SEG2,
+               "MTB_XENT_PARTIAL": mtb.XENT_PARTIAL, "MTB_XENT_FINISH": mtb.XENT_FINISH,
+               "MTB_XENT_ALL": mtb.XENT_ALL, "MTB_F32": mtb.F32, "MTB_BF16": mtb.BF16}
+    for k, v in binding.items():
+        assert c[k] == v, (k, c[k], v)
+
+
+def test_xent_rejects_phases_outside_the_numbering():
+    p = _FakePtr(0x100000)
+    for phase in (-1, 3):
+        st, msg = _status(mtb.vocab_xent, 8, 16, 0, mtb.BF16, phase, p, p, p, None, None, None,
+                          None, _S())
+        assert st == mtb.MTB_EINVAL and "phase" in msg

@@ -9,7 +9,8 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import TOL, host, oracle_kw, rel_err, run_rank, say, split_grads, tdtype, zero_sum_err
+from gpu_util import (TOL, check_rank_vs_oracle, host, oracle_kw, rel_err, run_rank, say, split_grads,
+                      tdtype, zero_sum_err)
 from oracle import block as ob
 from transformer_layer_ln_amd import inputs, mtb
 
@@ -160,39 +161,27 @@ class _Hook:
 
 
 def test_reduction_hook_called_at_the_two_points_each_way():
+    """MTB_PHASE_ALL with an (identity) hook runs the unfused LayerNorm / add
+    kernels after each reduction point: checked against the oracle itself."""
     cfg = inputs.BlockConfig("hook", batch=2, seq=128, hidden=256, q_heads=2, kv_heads=2,
                              head_dim=64, ffn=256, seed=2300)
     a = inputs.activations(cfg)
     w = inputs.shard_weights(cfg, 0)
     hook = _Hook()
-    say("[gpu] reduction hook, identity")
-    out_h, dx_h, g_h = run_rank(cfg, w, a["x"], a["g"], comm=hook.comm)
+    check_rank_vs_oracle(cfg, w, a["x"], a["g"], comm=hook.comm, label="hook, identity")
     T, H = cfg.tokens, cfg.hidden
     assert hook.calls == [(T * H, mtb.BF16, mtb.OP_SUM)] * 4
-    out, dx, g = run_rank(cfg, w, a["x"], a["g"])
-    # fused (no hook) and hooked paths round at different points; both are the block
-    assert rel_err(out_h, out) < 1e-2 and rel_err(dx_h, dx) < 1e-2
-    for k in g:
-        assert rel_err(g_h[k], g[k]) < 1e-2, k
 
 
-def test_reduction_hook_post_ln_matches_fused_path():
+def test_reduction_hook_post_ln_matches_oracle():
     cfg = inputs.BlockConfig("hook-post", batch=2, seq=128, hidden=256, q_heads=2, kv_heads=2,
                              head_dim=64, ffn=256, seed=2310, norm="post", affine=True, bias=True)
     a = inputs.activations(cfg)
     w = inputs.shard_weights(cfg, 0)
     hook = _Hook()
-    say("[gpu] reduction hook, identity, post-LN")
-    out_h, dx_h, g_h = run_rank(cfg, w, a["x"], a["g"], comm=hook.comm)
+    check_rank_vs_oracle(cfg, w, a["x"], a["g"], comm=hook.comm, label="hook, identity, post-LN")
     T, H = cfg.tokens, cfg.hidden
     assert hook.calls == [(T * H, mtb.BF16, mtb.OP_SUM)] * 4
-    out, dx, g = run_rank(cfg, w, a["x"], a["g"])
-    assert rel_err(out_h, out) < 1e-2 and rel_err(dx_h, dx) < 1e-2
-    for k in g:
-        if k == "bk":   # exactly zero in exact arithmetic: both are rounding noise
-            assert np.max(np.abs(g_h[k])) < 1e-2 * np.max(np.abs(g["bq"]))
-            continue
-        assert rel_err(g_h[k], g[k]) < 1e-2, k
 
 
 def test_reduction_hook_failure_is_reported():

@@ -282,6 +282,29 @@ def test_mean_loss_cotangent_leaves_layernorm_grad_zero_without_affine():
     assert np.max(np.abs(dx)) < 1e-15
 
 
+def test_mean_loss_value_and_gradient():
+    """block_loss_mean against what fixes it without retyping it: a brute
+    force Python sum over the elements divided by their count, the mean of a
+    constant tensor (that constant), and a central difference of the loss in
+    a few positions (the gradient 1/numel, the same everywhere)."""
+    rng = np.random.default_rng(31)
+    out = rng.normal(size=(2, 3, 5))
+    loss, g = ob.block_loss_mean(out)
+    total, count = 0.0, 0
+    for v in out.ravel().tolist():
+        total += v
+        count += 1
+    assert abs(loss - total / count) < 1e-14
+    assert abs(ob.block_loss_mean(np.full((4, 7), 2.5))[0] - 2.5) < 1e-15
+    assert g.shape == out.shape
+    h = 1e-6
+    for idx in [(0, 0, 0), (1, 2, 4), (0, 1, 3)]:
+        e = np.zeros_like(out)
+        e[idx] = h
+        fd = (ob.block_loss_mean(out + e)[0] - ob.block_loss_mean(out - e)[0]) / (2 * h)
+        assert abs(fd - g[idx]) < 1e-8 and abs(g[idx] - 1.0 / 30) < 1e-15
+
+
 def test_post_ln_closed_form_with_zero_projections():
     """Post-LN with Wo = W2 = 0 and no biases: out = LN(LN(x)) row by row.
     Written out: y = (x - mean) / sqrt(var + eps) has variance

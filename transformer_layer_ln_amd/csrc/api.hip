@@ -271,7 +271,7 @@ struct Trace {
   void* const* e = nullptr;
   int n = 0, i = 0;
 };
-Trace g_trace;
+thread_local Trace g_trace;  // per host thread, like the error message
 
 void trace_begin(int what, hipStream_t st) {
   if (g_trace.what == what && g_trace.i < g_trace.n) hipEventRecord((hipEvent_t)g_trace.b[g_trace.i], st);
@@ -681,7 +681,7 @@ mtb_status mtb_vocab_xent(int64_t n, int64_t v, int64_t v0, int32_t dtype, int32
   if (n <= 0 || v <= 0 || v0 < 0) return fail(MTB_EINVAL, "n_tokens, v_local must be > 0, v_start >= 0");
   if (n > 0x7fffffff) return fail(MTB_EUNSUPPORTED, "n_tokens beyond 2^31");
   if (dtype != MTB_F32 && dtype != MTB_BF16) return fail(MTB_EINVAL, "bad dtype %d", dtype);
-  if (phase < MTB_XENT_ALL || phase > MTB_XENT_FINISH) return fail(MTB_EINVAL, "bad phase %d", phase);
+  if (phase < MTB_XENT_PARTIAL || phase > MTB_XENT_ALL) return fail(MTB_EINVAL, "bad phase %d", phase);
   MTB_REQ_A(target, "target", 8);
   MTB_REQ_A(stats, "stats", 4);
   if (phase != MTB_XENT_FINISH || dlogits) MTB_REQ(logits, "logits");

@@ -20,7 +20,7 @@ ACT_GELU, ACT_SWIGLU = 0, 1
 NORM_PRE, NORM_POST = 0, 1
 OP_SUM, OP_MAX = 0, 1
 PHASE_ALL, PHASE_SEG0, PHASE_SEG1, PHASE_SEG2 = 0, 1, 2, 3
-XENT_ALL, XENT_PARTIAL, XENT_FINISH = 0, 1, 2
+XENT_PARTIAL, XENT_FINISH, XENT_ALL = 0, 1, 2
 
 WEIGHT_FIELDS = ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_o", "b_o",
                  "ln2_g", "ln2_b", "w_fc1", "b_fc1", "w_fc2", "b_fc2")
