@@ -355,6 +355,24 @@ mtb_status mtb_vocab_embed_bwd(int64_t n_tokens, int64_t v_local, int64_t v_star
                                int32_t dtype, const int64_t *ids, const void *dout, void *dtable,
                                void *workspace, void *hip_stream);
 
+/* The same backward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): no workspace argument; the per-row (count, first token) pairs
+ * live in a device array of the library, one per GPU, allocated with the
+ * library's code and held until the process ends (8 bytes per row,
+ * MTB_EMBED_NOALLOC_MAX_ROWS rows = 2 MiB). The call allocates nothing; the
+ * first call on a device looks the array's address up (hipGetSymbolAddress)
+ * with that device current. v_local above MTB_EMBED_NOALLOC_MAX_ROWS returns
+ * MTB_EUNSUPPORTED and launches nothing. Every call on one GPU uses the same
+ * array (the kernels reinitialise it each call): calls that may overlap on
+ * one GPU -- different streams, or different host threads -- race and give
+ * wrong results; serialise them. Output and arguments otherwise exactly as
+ * mtb_vocab_embed_bwd. */
+#define MTB_EMBED_NOALLOC_MAX_ROWS 262144
+mtb_status mtb_vocab_embed_bwd_noalloc(int64_t n_tokens, int64_t v_local, int64_t v_start,
+                                       int64_t hidden, int32_t dtype, const int64_t *ids,
+                                       const void *dout, void *dtable, void *hip_stream);
+
 /* Benchmark instrumentation. The armed state is per host thread (like the
  * error message): only calls made on the arming thread are traced, and
  * other threads' calls are unaffected. While armed, every launch of the kernel class `what` records

@@ -255,3 +255,13 @@ def test_xent_rejects_phases_outside_the_numbering():
         st, msg = _status(mtb.vocab_xent, 8, 16, 0, mtb.BF16, phase, p, p, p, None, None, None,
                           None, _S())
         assert st == mtb.MTB_EINVAL and "phase" in msg
+
+
+def test_noalloc_embedding_backward_rejects_shards_beyond_its_array():
+    """The allocation-free backward refuses a shard larger than its device
+    array before touching the device."""
+    p = _FakePtr(0x100000)
+    st, msg = _status(mtb.vocab_embed_bwd_noalloc, 8, mtb.EMBED_NOALLOC_MAX_ROWS + 1, 0, 64, mtb.BF16,
+                      p, p, p, _S())
+    assert st == mtb.MTB_EUNSUPPORTED and "no-alloc" in msg
+    assert header_constants()["MTB_EMBED_NOALLOC_MAX_ROWS"] == mtb.EMBED_NOALLOC_MAX_ROWS

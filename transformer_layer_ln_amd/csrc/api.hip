@@ -751,6 +751,23 @@ mtb_status mtb_vocab_embed_bwd(int64_t n, int64_t v, int64_t v0, int64_t h, int3
   return MTB_OK;
 }
 
+mtb_status mtb_vocab_embed_bwd_noalloc(int64_t n, int64_t v, int64_t v0, int64_t h, int32_t dtype,
+                                       const int64_t* ids, const void* dout, void* dtable,
+                                       void* hip_stream) {
+  mtb_status s = check_embed(n, v, v0, h, dtype);
+  if (s != MTB_OK) return s;
+  if (v > MTB_EMBED_NOALLOC_MAX_ROWS)
+    return fail(MTB_EUNSUPPORTED, "v_local %lld exceeds the no-alloc workspace (%d rows)", (long long)v,
+                (int)MTB_EMBED_NOALLOC_MAX_ROWS);
+  MTB_REQ_A(ids, "ids", 8);
+  MTB_REQ(dout, "dout");
+  MTB_REQ(dtable, "dtable");
+  void* ws = nullptr;
+  MTB_HIP(embed_scratch(&ws));
+  MTB_HIP(embed_bwd(dtype, n, v, v0, (int)h, ids, dout, dtable, ws, (hipStream_t)hip_stream));
+  return MTB_OK;
+}
+
 size_t mtb_lmhead_xent_workspace_bytes(int64_t n, int64_t h, int64_t v) {
   if (n <= 0 || h <= 0 || v <= 0 || n > 0x7fffffff || h > 0x7fffffff || v > 0x7fffffff) return 0;
   const size_t parts = (size_t)n * lmhead_tiles(n, h, v) * 3 * sizeof(float);

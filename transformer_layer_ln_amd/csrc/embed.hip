@@ -15,8 +15,11 @@
 // token order (wavefront ballots), adds their gradient rows in fp32 in that
 // order, stops when it has seen the row's count, and writes the row once --
 // zeros for a row no token selects.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
+#include "mtb.h"
 
 namespace mtb {
 namespace {
@@ -117,7 +120,36 @@ __global__ __launch_bounds__(256) void embed_bwd_kernel(int n, int64_t v0, int H
   }
 }
 
+// Device memory of the backward's per-row (count, first token) pairs for
+// callers that cannot allocate: one copy per GPU, held until the process
+// ends, shared by every call on that GPU (the last call's contents stay).
+__device__ __align__(256) int scratch[2 * MTB_EMBED_NOALLOC_MAX_ROWS];
+
+// Its device address on each GPU, looked up once per device with that device
+// current. The array's host-side name is not a device address: host code
+// uses only these pointers.
+std::mutex g_scratch_mu;
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices] = {};
+
 }  // namespace
+
+hipError_t embed_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t embed_fwd(int dtype, int64_t n, int64_t vl, int64_t v0, int H, const int64_t* ids,
                      const void* table, void* out, hipStream_t st) {

@@ -149,6 +149,9 @@ hipError_t lmhead_combine(int64_t n, int tiles, const float* parts, float* stats
 // Vocab-parallel embedding (one vocab shard [v0, v0 + vl) of the table).
 // Backward workspace: per table row, an int32 token count and first token.
 size_t embed_ws_bytes(int64_t vl);
+// the library's own backward workspace on the current device (a file-scope
+// device array of MTB_EMBED_NOALLOC_MAX_ROWS rows; see embed.hip)
+hipError_t embed_scratch(void** ptr);
 hipError_t embed_fwd(int dtype, int64_t n, int64_t vl, int64_t v0, int H, const int64_t* ids,
                      const void* table, void* out, hipStream_t st);
 hipError_t embed_bwd(int dtype, int64_t n, int64_t vl, int64_t v0, int H, const int64_t* ids,

@@ -29,7 +29,8 @@ WEIGHT_FIELDS = ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_o", "b_o",
 EXPORTS = ("mtb_block_saved_bytes", "mtb_block_scratch_bytes", "mtb_block_fwd", "mtb_block_bwd",
            "mtb_vocab_xent", "mtb_vocab_xent_combine", "mtb_lmhead_xent_workspace_bytes",
            "mtb_lmhead_xent_fwd", "mtb_lmhead_xent_bwd", "mtb_vocab_embed_fwd",
-           "mtb_vocab_embed_bwd_workspace_bytes", "mtb_vocab_embed_bwd", "mtb_trace_arm",
+           "mtb_vocab_embed_bwd_workspace_bytes", "mtb_vocab_embed_bwd",
+           "mtb_vocab_embed_bwd_noalloc", "mtb_trace_arm",
            "mtb_trace_disarm", "mtb_last_error")
 TRACE_NONE, TRACE_FC1_FWD, TRACE_ATTN_FWD, TRACE_LN1_FWD, TRACE_FC2_WGRAD = 0, 1, 2, 3, 4
 TRACE_ATTN_SEG, TRACE_FFN_SEG, TRACE_BWD, TRACE_LN1_BWD = 5, 6, 7, 8
@@ -111,6 +112,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mtb_vocab_embed_bwd.argtypes = [c_int64, c_int64, c_int64, c_int64, c_int32, c_void_p,
                                         c_void_p, c_void_p, c_void_p, c_void_p]
     lib.mtb_vocab_embed_bwd.restype = c_int32
+    lib.mtb_vocab_embed_bwd_noalloc.argtypes = [c_int64, c_int64, c_int64, c_int64, c_int32, c_void_p,
+                                                c_void_p, c_void_p, c_void_p]
+    lib.mtb_vocab_embed_bwd_noalloc.restype = c_int32
     lib.mtb_trace_arm.argtypes = [c_int32, c_void_p, c_void_p, c_int32]
     lib.mtb_trace_arm.restype = c_int32
     lib.mtb_trace_disarm.argtypes = []
@@ -239,6 +243,15 @@ def vocab_embed_bwd(n_tokens, v_local, v_start, hidden, dtype, ids, dout, dtable
                     stream=None):
     _check(load().mtb_vocab_embed_bwd(n_tokens, v_local, v_start, hidden, dtype, _ptr(ids),
                                       _ptr(dout), _ptr(dtable), _ptr(workspace), _stream(stream)))
+
+
+EMBED_NOALLOC_MAX_ROWS = 262144
+
+
+def vocab_embed_bwd_noalloc(n_tokens, v_local, v_start, hidden, dtype, ids, dout, dtable,
+                            stream=None):
+    _check(load().mtb_vocab_embed_bwd_noalloc(n_tokens, v_local, v_start, hidden, dtype, _ptr(ids),
+                                              _ptr(dout), _ptr(dtable), _stream(stream)))
 
 
 class Trace:
