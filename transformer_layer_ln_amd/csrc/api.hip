@@ -123,7 +123,7 @@ size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 // Post-LN: h = r1 = x + attn, c = LN1(r1) (the MLP input), a = r2 = c + mlp
 // (the second LayerNorm's input); mu/rstd 1 and 2 belong to LN1 and LN2.
 struct Saved {
-  size_t a, mu1, rs1, qkv, qkvT, O, lse, h, mu2, rs2, c, u, m, total;
+  size_t a, mu1, rs1, qkv, O, lse, h, mu2, rs2, c, u, m, total;
 };
 Saved saved_layout(const Dims& d) {
   Saved s;
@@ -133,7 +133,6 @@ Saved saved_layout(const Dims& d) {
   s.mu1 = o; o += al(T * 4);
   s.rs1 = o; o += al(T * 4);
   s.qkv = o; o += al(T * d.Nqkv * e);
-  s.qkvT = o; o += d.dt == MTB_BF16 ? al(T * d.Nqkv * e) : 0;
   s.O = o; o += al(T * d.NO * e);
   s.lse = o; o += al((size_t)d.B * d.nq * d.S * 4);
   s.h = o; o += al(T * d.H * e);
@@ -171,7 +170,7 @@ GemmProb wgrad_fc1(const Dims& d, const void* du, const void* c) {
 }
 
 struct Scratch {
-  size_t dh, dr, gm, p, du, dm, dO, dOT, Dbuf, dqkv, part, red, ws, total;
+  size_t dh, dr, gm, p, du, dm, dO, Dbuf, dqkv, part, red, ws, total;
 };
 Scratch scratch_layout(const Dims& d) {
   Scratch s;
@@ -184,7 +183,6 @@ Scratch scratch_layout(const Dims& d) {
   s.du = o; o += al(T * d.Fu * e);
   s.dm = o; o += d.dt == MTB_F32 ? al(T * d.F * e) : 0;
   s.dO = o; o += al(T * d.NO * e);
-  s.dOT = o; o += d.dt == MTB_BF16 ? al(T * d.NO * e) : 0;
   s.Dbuf = o; o += al((size_t)d.B * d.nq * d.S * 4);
   s.dqkv = o; o += al(T * d.Nqkv * e);
   s.part = o; o += (d.dt == MTB_BF16 && d.nq != d.nkv) ? al((size_t)d.B * d.nq * d.S * 2 * d.d * 4) : 0;
@@ -370,7 +368,7 @@ mtb_status mtb_block_fwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
   const bool bf = dt == MTB_BF16;
   const bool fused = phase == MTB_PHASE_ALL && !(comm && comm->allreduce);
   void* a = P(saved, L.a); float* mu1 = (float*)P(saved, L.mu1); float* rs1 = (float*)P(saved, L.rs1);
-  void* qkv = P(saved, L.qkv); void* qkvT = bf ? P(saved, L.qkvT) : nullptr;
+  void* qkv = P(saved, L.qkv);
   void* O = P(saved, L.O); float* lse = (float*)P(saved, L.lse);
   void* h = P(saved, L.h); float* mu2 = (float*)P(saved, L.mu2); float* rs2 = (float*)P(saved, L.rs2);
   void* c = P(saved, L.c); void* u = P(saved, L.u); void* m = P(saved, L.m);
@@ -393,14 +391,13 @@ mtb_status mtb_block_fwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
       MTB_HIP(ln_fwd(dt, T, H, x, nullptr, nullptr, w->ln1_g, w->ln1_b, nullptr, a, mu1, rs1, d.eps, st));
       trace_end(MTB_TRACE_LN1_FWD, st);
     }
-    // column-parallel QKV on LN1(x) (pre-LN) or x (post-LN); the bf16 path
-    // also keeps a per-batch transpose for attention
+    // column-parallel QKV on LN1(x) (pre-LN) or x (post-LN)
     Epi e;
-    e.out = qkv; e.ldo = Nq; e.bias = w->b_qkv; e.outT = qkvT; e.S = S; e.ws = ws;
+    e.out = qkv; e.ldo = Nq; e.bias = w->b_qkv; e.ws = ws;
     MTB_HIP(gemm(dt, T, Nq, H, post ? x : a, H, true, w->w_qkv, H, true, e, st));
     // per-head attention over the local heads
     trace_begin(MTB_TRACE_ATTN_FWD, st);
-    MTB_HIP(attn_fwd(dt, (int)d.B, S, (int)d.nq, (int)d.nkv, (int)d.d, d.causal, qkv, qkvT, O, lse, st,
+    MTB_HIP(attn_fwd(dt, (int)d.B, S, (int)d.nq, (int)d.nkv, (int)d.d, d.causal, qkv, O, lse, st,
                      d.dattn));
     trace_end(MTB_TRACE_ATTN_FWD, st);
     // row-parallel projection: a partial sum, reduced at g1
@@ -520,7 +517,7 @@ mtb_status mtb_block_bwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
   char* sv = (char*)saved;
   const void* a = sv + L.a; const float* mu1 = (const float*)(sv + L.mu1);
   const float* rs1 = (const float*)(sv + L.rs1);
-  const void* qkv = sv + L.qkv; const void* qkvT = bf ? sv + L.qkvT : nullptr;
+  const void* qkv = sv + L.qkv;
   const void* O = sv + L.O; const float* lse = (const float*)(sv + L.lse);
   const void* h = sv + L.h; const float* mu2 = (const float*)(sv + L.mu2);
   const float* rs2 = (const float*)(sv + L.rs2);
@@ -528,7 +525,7 @@ mtb_status mtb_block_bwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
   void* dh = P(scratch, Z.dh); void* p = P(scratch, Z.p); void* du = P(scratch, Z.du);
   void* dr = d.post ? P(scratch, Z.dr) : nullptr;
   void* gm = d.dh1.thr ? P(scratch, Z.gm) : nullptr;
-  void* dm = P(scratch, Z.dm); void* dO = P(scratch, Z.dO); void* dOT = bf ? P(scratch, Z.dOT) : nullptr;
+  void* dm = P(scratch, Z.dm); void* dO = P(scratch, Z.dO);
   float* Dbuf = (float*)P(scratch, Z.Dbuf); void* dqkv = P(scratch, Z.dqkv);
   float* part = (float*)P(scratch, Z.part); float* red = (float*)P(scratch, Z.red);
   void* ws = Z.total > Z.ws ? P(scratch, Z.ws) : nullptr;
@@ -616,7 +613,7 @@ mtb_status mtb_block_bwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
     // projection backward (row-parallel: g1's backward is the identity)
     {
       Epi e;
-      e.out = dO; e.ldo = NO; e.outT = dOT; e.S = S; e.ws = ws;
+      e.out = dO; e.ldo = NO; e.ws = ws;
       MTB_HIP(gemm(dt, T, NO, H, dA, H, true, w->w_o, NO, false, e, st));
     }
     // the projection's weight gradient waits for the QKV one when both are
@@ -629,8 +626,8 @@ mtb_status mtb_block_bwd(const mtb_cfg* cfg, const mtb_weights* w, int32_t phase
     }
     if (g.b_o) MTB_HIP(colsum(dt, T, H, dA, nullptr, H, nullptr, nullptr, nullptr, g.b_o, red, st));
     // attention backward
-    MTB_HIP(attn_bwd(dt, (int)d.B, S, (int)d.nq, (int)d.nkv, (int)d.d, d.causal, qkv, qkvT, O, dO,
-                     dOT, lse, Dbuf, dqkv, part, st, d.dattn));
+    MTB_HIP(attn_bwd(dt, (int)d.B, S, (int)d.nq, (int)d.nkv, (int)d.d, d.causal, qkv, O, dO, lse, Dbuf,
+                     dqkv, part, st, d.dattn));
     if (wpair) {
       GemmProb pq = wgrad_qkv(d, dqkv, post ? x : a), po = wgrad_proj(d, dA, O);
       pq.e.out = g.w_qkv;

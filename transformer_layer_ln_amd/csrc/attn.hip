@@ -7,10 +7,11 @@
 // (batch, head) with 4 wavefronts arranged 2 x 2: each wavefront takes 32 rows
 // of its own side and one 32-row half of the other side's tile, and the two
 // halves are combined through LDS at the end. That gives S/64 * B * heads
-// workgroups; causal grids pair heavy and light tiles. The other side's
-// tiles stream global -> LDS with direct-to-LDS loads, double-buffered (tile
-// t+1 is in flight while tile t is used); each wavefront reads a tile's
-// fragments in bulk ahead of the MFMAs that use them.
+// workgroups, two per CU; causal grids pair heavy and light tiles. The other
+// side's tiles stream global -> LDS with direct-to-LDS loads (forward and dQ
+// double-buffered: tile t+1 is in flight while tile t is used; dK/dV keeps
+// its K tile resident and single-buffers Q and dO, the CU's second
+// workgroup covering the copies).
 //  * forward: S^T = K Q^T puts one query per lane, so the online-softmax row
 //    max is 16 in-lane values plus one exchange with lane ^ 32, the running
 //    sum stays per lane until the end, and the O^T accumulator is rescaled
@@ -27,11 +28,12 @@
 //    the row sums are taken (the normaliser sees every key), and the
 //    backward uses the mask on P for dV and on dP = dO V^T for dS. D =
 //    rowsum(dO o O) is unchanged.
-// Layout inputs: qkv [T][Nqkv] token-major and its per-batch transpose
-// qkvT [B][Nqkv][S]; dO [T][nq*d] and dOT [B][nq*d][S]. In the transposed
-// copies the tokens of every 16 are stored in the order 0-3, 8-11, 4-7, 12-15,
-// so that an MFMA k-step's 16 keys -- the lane group g holds keys 4g..4g+3 and
-// 8+4g..8+4g+3 of its accumulator layout -- are one 16-byte chunk.
+// Layout inputs: qkv [T][Nqkv] and dO [T][nq*d], token-major. Every operand
+// tile is copied row-major into LDS; an operand that the MFMAs need
+// transposed (V^T, Q^T, dO^T, K^T) is read from that tile with the LDS
+// transpose read, in the key (or query) order of an accumulator's rows --
+// lane half g holds rows 4g..4g+3 and 8+4g..8+4g+3 of each 16 -- so that P
+// and dS feed the next products straight from registers.
 #include "common.h"
 #include "drop.h"
 #include "kernels.h"
@@ -43,34 +45,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
 
-MTB_DEV int swz(int row) { return (row ^ (row >> 3)) & 7; }
-
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// Direct-to-LDS copy of a ROWS x (CH 16-byte chunks) tile (row pitch ld
-// elements) into LDS [row][CH chunks] with the chunk index XOR-swizzled by
-// row, issued by the 4 wavefronts of the workgroup. Each load instruction
-// fills one contiguous KB of LDS (lane l -> bytes 16l..16l+15), so every
-// lane fetches the global chunk that belongs at its LDS position.
-template <int ROWS, int CH>
-MTB_DEV void dma_tile(bf16_t* lds, const bf16_t* __restrict__ g, size_t ld, int wave, int lane) {
-  constexpr int BLK = ROWS * CH / 64, PERW = BLK / 4, RPB = 64 / CH;
-  static_assert(BLK % 4 == 0, "tile must split over 4 wavefronts");
-#pragma unroll
-  for (int i = 0; i < PERW; ++i) {
-    const int b = wave * PERW + i;
-    const int row = b * RPB + lane / CH, pc = lane % CH;
-    const int c = pc ^ swz(row);
-    __builtin_amdgcn_global_load_lds((const void*)(g + (size_t)row * ld + c * 8),
-                                     (lds_ptr_t)(lds + b * 512), 16, 0, 0);
-  }
-}
-
-// fragment reads (lane: row = base + (lane & 31), 8 elements of chunk c + (lane >> 5))
-template <int W>
-MTB_DEV bf16x8 frag(const bf16_t* s, int row, int c) {
-  return *reinterpret_cast<const bf16x8*>(s + row * W + ((c ^ swz(row)) << 3));
-}
 
 // linear workgroup id -> (tile along the sequence, batch*head). Causal
 // workloads order the tiles by their work. With two workgroups per CU
@@ -114,17 +89,77 @@ MTB_DEV void pack_half(const float (&a)[16], bf16x8& p0, bf16x8& p1) {
   }
 }
 
+// LDS tiles of the K, V, Q and dO rows: [rows][D] bf16 row-major, 16-byte chunk c of row
+// r stored at chunk c ^ tswz(r). The swizzle is chosen so that both ways the
+// kernels read a tile are free of bank conflicts: direct fragment reads
+// (ds_read_b128; 16 lanes = 16 consecutive rows, one chunk: tswz is a
+// bijection on r mod 16) and transposed reads (ds_read_b64_tr_b16; 32 lanes
+// = 4 consecutive rows x 64 bytes: tswz puts those rows' 64-byte groups on
+// different banks).
+template <int D>
+MTB_DEV int tswz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+template <int D>
+MTB_DEV int toff(int r, int c) { return r * D + ((c ^ tswz<D>(r)) << 3); }
+
+// Direct-to-LDS copy of a ROWS x D tile (row pitch ld elements) into the
+// layout above, by the 4 wavefronts of the workgroup: each load instruction
+// fills one contiguous KB of LDS (lane l -> bytes 16l .. 16l + 15), so a lane
+// fetches the global chunk that belongs at its LDS position.
+template <int ROWS, int D>
+MTB_DEV void dma_rows(bf16_t* lds, const bf16_t* __restrict__ g, size_t ld, int wave, int lane) {
+  constexpr int CH = D / 8, RPB = 64 / CH, BLK = ROWS / RPB, PERW = BLK / 4;
+  static_assert(BLK % 4 == 0, "tile must split over 4 wavefronts");
+#pragma unroll
+  for (int i = 0; i < PERW; ++i) {
+    const int b = wave * PERW + i;
+    const int r = b * RPB + lane / CH, c = (lane % CH) ^ tswz<D>(r);
+    __builtin_amdgcn_global_load_lds((const void*)(g + (size_t)r * ld + c * 8), (lds_ptr_t)(lds + b * 512), 16,
+                                     0, 0);
+  }
+}
+
+// MFMA fragment of a tile read directly: rows r (the lane's row), 8 values of chunk c
+template <int D>
+MTB_DEV bf16x8 frag_d(const bf16_t* t, int r, int c) {
+  return *reinterpret_cast<const bf16x8*>(t + toff<D>(r, c));
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4* lds_i16x4_t;
+
+// MFMA fragment of the transpose of a tile: lane l gets column m0 + (l & 31)
+// at the 8 rows of k-step kk (rows 16 kk .. 16 kk + 15) that the lane's half
+// lg = l >> 5 holds, in the order of an accumulator's rows: 4 lg .. 4 lg + 3
+// and 8 + 4 lg .. 8 + 4 lg + 3 (so P or dS taken straight from an S
+// accumulator pairs with it). Two transpose reads of 4 rows each: within a
+// 16-lane group, lane i receives element i mod 4 of the 8 bytes that lanes
+// 4j + i / 4 address (rows +j).
+template <int D>
+MTB_DEV bf16x8 frag_t(const bf16_t* t, int kk, int m0, int lane) {
+  const int g = lane >> 4, sl = lane & 15, lg = lane >> 5;
+  const int col = m0 + 16 * (g & 1) + 4 * (sl & 3);
+  const int r0 = 16 * kk + 4 * lg + (sl >> 2);
+  const bf16_t* a0 = t + r0 * D + (((col >> 3) ^ tswz<D>(r0)) << 3) + (col & 7);
+  const bf16_t* a1 = t + (r0 + 8) * D + (((col >> 3) ^ tswz<D>(r0 + 8)) << 3) + (col & 7);
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t)a0);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t)a1);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // Forward. Workgroup = 64 queries of one (batch, q head); wavefront w takes
 // query half w & 1 and key half w >> 1 of every 64-key tile, keeps its own
 // online-softmax state, and the two key halves are merged at the end.
 template <int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(int S, int nq, int nkv, int ldq,
                                                           const bf16_t* __restrict__ qkv,
-                                                          const bf16_t* __restrict__ qkvT,
                                                           bf16_t* __restrict__ O,
                                                           float* __restrict__ lse, float sl2,
                                                           Drop drop) {
-  __shared__ __attribute__((aligned(1024))) bf16_t smem[4 * 64 * D];  // 2 stages of K, V^T
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[4 * 64 * D];  // 2 stages of K, V
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lg = lane >> 5;
   const int qh = wave & 1, kh = wave >> 1;
@@ -150,12 +185,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(int S, int nq, int nkv
   float m_i = kNegInf, l_i = 0.f;  // l_i: this lane's keys only, summed with lane ^ 32 at the end
 
   const bf16_t* kbase = qkv + tok0 * ldq + (size_t)(nq + hk) * D;
-  const bf16_t* vtbase = qkvT + ((size_t)b * ldq + (size_t)(nq + nkv + hk) * D) * S;
+  const bf16_t* vbase = qkv + tok0 * ldq + (size_t)(nq + nkv + hk) * D;
   const int ntk = CAUSAL ? qb + 1 : ntile;
   auto fetch = [&](int t) {
     bf16_t* st = smem + (t & 1) * 128 * D;
-    dma_tile<64, D / 8>(st, kbase + (size_t)t * 64 * ldq, ldq, wave, lane);
-    dma_tile<D, 8>(st + 64 * D, vtbase + t * 64, S, wave, lane);
+    dma_rows<64, D>(st, kbase + (size_t)t * 64 * ldq, ldq, wave, lane);
+    dma_rows<64, D>(st + 64 * D, vbase + (size_t)t * 64 * ldq, ldq, wave, lane);
   };
   fetch(0);
   __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
@@ -169,12 +204,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(int S, int nq, int nkv
     if (!CAUSAL || ks <= q0 + 31) {
       bf16x8 kf[D / 16], vt[D / 32][2];
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) kf[kk] = frag<D>(sK, kh * 32 + (lane & 31), 2 * kk + lg);
+      for (int kk = 0; kk < D / 16; ++kk) kf[kk] = frag_d<D>(sK, kh * 32 + (lane & 31), 2 * kk + lg);
 #pragma unroll
       for (int df = 0; df < D / 32; ++df) {
-        const int row = df * 32 + (lane & 31);
-        vt[df][0] = frag<64>(sV, row, 4 * kh + lg);
-        vt[df][1] = frag<64>(sV, row, 4 * kh + 2 + lg);
+        vt[df][0] = frag_t<D>(sV, 2 * kh, 32 * df, lane);
+        vt[df][1] = frag_t<D>(sV, 2 * kh + 1, 32 * df, lane);
       }
       f32x16 sa, sb;
 #pragma unroll
@@ -184,12 +218,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(int S, int nq, int nkv
         if (kk & 1) sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], sb, 0, 0, 0);
         else sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], sa, 0, 0, 0);
       }
-      // issue order: the K reads, then each S^T MFMA followed by one V^T read
+      // issue order: the K reads, then each S^T MFMA followed by one of the
+      // V^T transpose reads
       __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 0);
 #pragma unroll
       for (int i = 0; i < D / 16; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
       // s[j]: key ks + 8(j>>2) + 4lg + (j&3), query qi
       float s[16];
@@ -306,33 +341,33 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(int rows, int S, int 
   }
 }
 
-// workgroups per CU: one at D = 128 (its LDS stages and registers fill a CU), else two
-template <int D>
-constexpr int dkdv_per_cu() { return D == 128 ? 1 : 2; }
-
-// dK, dV. Workgroup = 64 keys of one (batch, q head); wavefront w takes key
+// dK, dV. Workgroup = 64 keys of one (batch, q head), two workgroups per CU
+// (each one's loads hidden behind the other's MFMAs); wavefront w takes key
 // half w & 1 and query half w >> 1 of every 64-query tile. S = Q K^T puts a
 // key per lane, so P and dS feed dV^T += dO^T P^T and dK^T += Q^T dS^T
-// straight from registers; the two query halves are summed at the end.
-// The Q, dO, Q^T, dO^T tiles and the tile's log-sum-exp and D values are
-// copied global -> LDS directly, double-buffered: tile t+1 streams in while
-// tile t is used.
+// straight from registers; dO^T and Q^T come from the row-major Q and dO
+// tiles by transpose reads. The K tile stays in LDS for the whole walk, the
+// wavefront's V rows in registers. The two query halves are summed at the
+// end.
 template <int D, bool CAUSAL, bool DROP>
-__global__ __launch_bounds__(256, dkdv_per_cu<D>()) void attn_bwd_dkdv_kernel(
-    int S, int nq, int nkv, int ldq, const bf16_t* __restrict__ qkv,
-    const bf16_t* __restrict__ qkvT, const bf16_t* __restrict__ dO,
-    const bf16_t* __restrict__ dOT, const float* __restrict__ lse,
-    const float* __restrict__ Dbuf, bf16_t* __restrict__ dqkv, float* __restrict__ part, float sl2,
-    float scale, Drop drop) {
-  constexpr int TILE = 64 * D;              // elements of one 64 x D (or D x 64) tile
-  constexpr int STAGE = 4 * TILE + 512;  // Q, dO, Q^T, dO^T, then lse and D (64 floats each), 1-KB aligned
-  __shared__ __attribute__((aligned(1024))) bf16_t smem[2 * STAGE];
+__global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(
+    int S, int nq, int nkv, int ldq, const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO,
+    const float* __restrict__ lse, const float* __restrict__ Dbuf, bf16_t* __restrict__ dqkv,
+    float* __restrict__ part, float sl2, float scale, Drop drop) {
+  constexpr int TILE = 64 * D;  // elements of one 64 x D tile
+  // K, then the streamed Q and dO tiles, then log-sum-exp and D (64 floats each)
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[3 * TILE + 256];
+  bf16_t* sK = smem;
+  bf16_t* sQ = smem + TILE;
+  bf16_t* sdO = smem + 2 * TILE;
+  const float* sL = reinterpret_cast<const float*>(smem + 3 * TILE);
+  const float* sD = sL + 64;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lg = lane >> 5;
   const int kh = wave & 1, qh = wave >> 1;
   const int ntile = S / 64, nbh = gridDim.x / ntile;
   int kb, bh;
-  tile_order(blockIdx.x, ntile, nbh, CAUSAL, false, dkdv_per_cu<D>() == 2, kb, bh);
+  tile_order(blockIdx.x, ntile, nbh, CAUSAL, false, true, kb, bh);
   const int b = bh / nq, hq = bh % nq;
   const int g = nq / nkv, hk = hq / g;
   const int k0 = kb * 64 + kh * 32;
@@ -340,14 +375,12 @@ __global__ __launch_bounds__(256, dkdv_per_cu<D>()) void attn_bwd_dkdv_kernel(
   const size_t tok0 = (size_t)b * S;
   const int ldo = nq * D;
 
-  bf16x8 kf[D / 16], vf[D / 16];
+  dma_rows<64, D>(sK, qkv + (tok0 + kb * 64) * ldq + (size_t)(nq + hk) * D, ldq, wave, lane);
+  bf16x8 vf[D / 16];
   {
-    const size_t kr = (tok0 + key) * ldq + 8 * lg;
+    const bf16_t* vp = qkv + (tok0 + key) * ldq + (size_t)(nq + nkv + hk) * D + 8 * lg;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      kf[kk] = *reinterpret_cast<const bf16x8*>(qkv + kr + (size_t)(nq + hk) * D + kk * 16);
-      vf[kk] = *reinterpret_cast<const bf16x8*>(qkv + kr + (size_t)(nq + nkv + hk) * D + kk * 16);
-    }
+    for (int kk = 0; kk < D / 16; ++kk) vf[kk] = *reinterpret_cast<const bf16x8*>(vp + kk * 16);
   }
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
@@ -356,76 +389,33 @@ __global__ __launch_bounds__(256, dkdv_per_cu<D>()) void attn_bwd_dkdv_kernel(
     for (int r = 0; r < 16; ++r) { dk[i][r] = 0.f; dv[i][r] = 0.f; }
 
   const bf16_t* qbase = qkv + tok0 * ldq + (size_t)hq * D;
-  const bf16_t* qtbase = qkvT + ((size_t)b * ldq + (size_t)hq * D) * S;
   const bf16_t* dobase = dO + tok0 * ldo + (size_t)hq * D;
-  const bf16_t* dotbase = dOT + ((size_t)b * ldo + (size_t)hq * D) * S;
   const float* lrow = lse + ((size_t)b * nq + hq) * S;
   const float* drow = Dbuf + ((size_t)b * nq + hq) * S;
+  const int krow = kh * 32 + (lane & 31);    // the lane's key row in sK
+  const int qrow = qh * 32 + (lane & 31);    // the lane's query row in sQ / sdO
 
-  auto fetch = [&](int qt) {
-    bf16_t* st = smem + (qt & 1) * STAGE;
+  for (int qt = CAUSAL ? kb : 0; qt < ntile; ++qt) {
     const int qt0 = qt * 64;
-    dma_tile<64, D / 8>(st, qbase + (size_t)qt0 * ldq, ldq, wave, lane);
-    dma_tile<64, D / 8>(st + TILE, dobase + (size_t)qt0 * ldo, ldo, wave, lane);
-    dma_tile<D, 8>(st + 2 * TILE, qtbase + qt0, S, wave, lane);
-    dma_tile<D, 8>(st + 3 * TILE, dotbase + qt0, S, wave, lane);
+    dma_rows<64, D>(sQ, qbase + (size_t)qt0 * ldq, ldq, wave, lane);
+    dma_rows<64, D>(sdO, dobase + (size_t)qt0 * ldo, ldo, wave, lane);
     if (wave == 0) {
-      __builtin_amdgcn_global_load_lds((const void*)(lrow + qt0 + lane), (lds_ptr_t)(st + 4 * TILE), 4, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(drow + qt0 + lane), (lds_ptr_t)(st + 4 * TILE + 128), 4, 0,
-                                       0);
+      __builtin_amdgcn_global_load_lds((const void*)(lrow + qt0 + lane), (lds_ptr_t)(smem + 3 * TILE), 4, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(drow + qt0 + lane), (lds_ptr_t)(smem + 3 * TILE + 128), 4,
+                                       0, 0);
     }
-  };
-
-  const int qfirst = CAUSAL ? kb : 0;
-  fetch(qfirst);
-  __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
-  __syncthreads();
-  for (int qt = qfirst; qt < ntile; ++qt) {
-    if (qt + 1 < ntile) fetch(qt + 1);   // into the stage every wave finished with last iteration
-    const bf16_t* st = smem + (qt & 1) * STAGE;
-    const bf16_t* sQ = st;
-    const bf16_t* sdO = st + TILE;
-    const bf16_t* sQT = st + 2 * TILE;
-    const bf16_t* sdOT = st + 3 * TILE;
-    const float* sL = reinterpret_cast<const float*>(st + 4 * TILE);
-    const float* sD = sL + 64;
-    const int qt0 = qt * 64;
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+    __syncthreads();
     const int qw0 = qt0 + qh * 32;
     if (!CAUSAL || qw0 + 31 >= k0) {
-      // all of this tile's Q / dO fragments first, so the LDS reads overlap
-      bf16x8 qa[D / 16], oa[D / 16];
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const int row = qh * 32 + (lane & 31);
-        qa[kk] = frag<D>(sQ, row, 2 * kk + lg);
-        oa[kk] = frag<D>(sdO, row, 2 * kk + lg);
-      }
       f32x16 s, dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kk], kf[kk], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[kk], vf[kk], dp, 0, 0, 0);
-      }
-      // the dO^T / Q^T fragments of the second pair of products, read under the first
-      bf16x8 ot[D / 32][2], qt2[D / 32][2];
-#pragma unroll
-      for (int df = 0; df < D / 32; ++df) {
-        const int row = df * 32 + (lane & 31);
-        ot[df][0] = frag<64>(sdOT, row, 4 * qh + lg);
-        ot[df][1] = frag<64>(sdOT, row, 4 * qh + 2 + lg);
-        qt2[df][0] = frag<64>(sQT, row, 4 * qh + lg);
-        qt2[df][1] = frag<64>(sQT, row, 4 * qh + 2 + lg);
-      }
-      // issue order: the Q / dO reads, then each S / dP MFMA followed by one
-      // of the dO^T / Q^T reads (the scheduler would otherwise sink every
-      // read next to its use)
-      __builtin_amdgcn_sched_group_barrier(0x100, D / 8, 0);
-#pragma unroll
-      for (int i = 0; i < D / 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_d<D>(sQ, qrow, 2 * kk + lg),
+                                                    frag_d<D>(sK, krow, 2 * kk + lg), s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_d<D>(sdO, qrow, 2 * kk + lg), vf[kk], dp, 0, 0, 0);
       }
       // element j: query qw0 + 8(j>>2) + 4lg + (j&3), key `key`
       float p[16], ds[16];
@@ -438,7 +428,7 @@ __global__ __launch_bounds__(256, dkdv_per_cu<D>()) void attn_bwd_dkdv_kernel(
         const int c = lane & 3;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int qq = qt0 + qh * 32 + 8 * i + 4 * lg + c;
+          const int qq = qw0 + 8 * i + 4 * lg + c;
           const u32x4 w = drop_words(drop, (((uint64_t)bh * S + qq) * S + (key & ~3)) >> 2);
           uint32_t v = (uint32_t)(w[0] >= drop.thr) | ((uint32_t)(w[1] >= drop.thr) << 1) |
                        ((uint32_t)(w[2] >= drop.thr) << 2) | ((uint32_t)(w[3] >= drop.thr) << 3);
@@ -473,53 +463,51 @@ __global__ __launch_bounds__(256, dkdv_per_cu<D>()) void attn_bwd_dkdv_kernel(
       pack_half(ds, d0, d1);
 #pragma unroll
       for (int df = 0; df < D / 32; ++df) {
-        dv[df] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ot[df][0], p0, dv[df], 0, 0, 0);
-        dv[df] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ot[df][1], p1, dv[df], 0, 0, 0);
-        dk[df] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt2[df][0], d0, dk[df], 0, 0, 0);
-        dk[df] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt2[df][1], d1, dk[df], 0, 0, 0);
+        dv[df] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_t<D>(sdO, 2 * qh, 32 * df, lane), p0, dv[df], 0, 0, 0);
+        dk[df] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_t<D>(sQ, 2 * qh, 32 * df, lane), d0, dk[df], 0, 0, 0);
+        dv[df] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_t<D>(sdO, 2 * qh + 1, 32 * df, lane), p1, dv[df], 0, 0,
+                                                         0);
+        dk[df] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_t<D>(sQ, 2 * qh + 1, 32 * df, lane), d1, dk[df], 0, 0,
+                                                         0);
       }
     }
-    // tile qt+1 landed, and every wave is done with stage qt & 1
-    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
-    __syncthreads();
+    __syncthreads();  // every wavefront is done with the tile before the next one lands
   }
   // sum the two query halves: qh = 1 hands its accumulators to qh = 0
+  // through LDS, dK first, then dV (each 2 x 64 x D floats: fits in the tiles)
   constexpr int NR = D / 2;
-  float* xo = reinterpret_cast<float*>(smem);  // [kh][dk|dv][NR][64]
-  if (qh == 1) {
+  float* xo = reinterpret_cast<float*>(smem);  // [kh][NR][64]
 #pragma unroll
-    for (int df = 0; df < D / 32; ++df)
+  for (int which = 0; which < 2; ++which) {
+    f32x16(&acc)[D / 32] = which == 0 ? dk : dv;
+    if (which == 1) __syncthreads();   // qh = 0 is done reading the dK half
+    if (qh == 1) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        xo[((kh * 2 + 0) * NR + df * 16 + r) * 64 + lane] = dk[df][r];
-        xo[((kh * 2 + 1) * NR + df * 16 + r) * 64 + lane] = dv[df][r];
-      }
-  }
-  __syncthreads();
-  if (qh == 1) return;
-  // dk[df][4i + r]: d = 32 df + 8i + 4lg + r for key `key`
+      for (int df = 0; df < D / 32; ++df)
 #pragma unroll
-  for (int df = 0; df < D / 32; ++df)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float a[4], c[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = df * 16 + 4 * i + r;
-        a[r] = (dk[df][4 * i + r] + xo[((kh * 2 + 0) * NR + j) * 64 + lane]) * scale;
-        c[r] = dv[df][4 * i + r] + xo[((kh * 2 + 1) * NR + j) * 64 + lane];
-      }
-      const int d = df * 32 + 8 * i + 4 * lg;
-      if (g == 1) {
-        st4(dqkv + (tok0 + key) * ldq + (size_t)(nq + hk) * D + d, a);
-        st4(dqkv + (tok0 + key) * ldq + (size_t)(nq + nkv + hk) * D + d, c);
-      } else {
-        float* pp = part + (((size_t)b * nq + hq) * S + key) * (2 * D);
-        st4(pp + d, a);
-        st4(pp + D + d, c);
-      }
+        for (int r = 0; r < 16; ++r) xo[(kh * NR + df * 16 + r) * 64 + lane] = acc[df][r];
     }
+    __syncthreads();
+    if (qh == 0) {
+      // acc[df][4i + r]: d = 32 df + 8i + 4lg + r for key `key`
+#pragma unroll
+      for (int df = 0; df < D / 32; ++df)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float a[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            a[r] = (acc[df][4 * i + r] + xo[(kh * NR + df * 16 + 4 * i + r) * 64 + lane]) * (which == 0 ? scale : 1.f);
+          const int d = df * 32 + 8 * i + 4 * lg;
+          if (g == 1)
+            st4(dqkv + (tok0 + key) * ldq + (size_t)(nq + which * nkv + hk) * D + d, a);
+          else
+            st4(part + (((size_t)b * nq + hq) * S + key) * (2 * D) + which * D + d, a);
+        }
+    }
+  }
 }
+
 
 // sum the g q-head contributions of each kv head (GQA) into dqkv
 template <int D>
@@ -550,21 +538,20 @@ __global__ __launch_bounds__(256) void attn_dkv_reduce_kernel(int B, int S, int 
   st8(dqkv + ((size_t)b * S + s) * ldq + col, acc);
 }
 
-// dQ. Workgroup = 64 queries of one (batch, q head); wavefront w takes query
-// half w & 1 and key half w >> 1 of every 64-key tile (S^T layout: a query
-// per lane); the key halves are summed at the end. K, V and K^T tiles are
-// copied global -> LDS directly into one buffer: two workgroups share a CU
-// and cover each other's loads (measured faster than double-buffering at one
-// workgroup per CU).
+// dQ. Workgroup = 64 queries of one (batch, q head), two workgroups per CU;
+// wavefront w takes query half w & 1 and key half w >> 1 of every 64-key tile
+// (S^T layout: a query per lane), its Q and dO rows in registers. The K and V
+// tiles stream global -> LDS double-buffered (tile t+1 in flight while tile
+// t is used); K^T comes from the K tile by transpose reads. The key halves
+// are summed at the end.
 template <int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
-    int S, int nq, int nkv, int ldq, const bf16_t* __restrict__ qkv,
-    const bf16_t* __restrict__ qkvT, const bf16_t* __restrict__ dO,
-    const float* __restrict__ lse, const float* __restrict__ Dbuf, bf16_t* __restrict__ dqkv,
-    float sl2, float scale, Drop drop) {
+    int S, int nq, int nkv, int ldq, const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO,
+    const float* __restrict__ lse, const float* __restrict__ Dbuf, bf16_t* __restrict__ dqkv, float sl2,
+    float scale, Drop drop) {
   constexpr int TILE = 64 * D;
-  constexpr int STAGE = 3 * TILE;  // K, V, K^T
-  __shared__ __attribute__((aligned(1024))) bf16_t smem[STAGE];
+  constexpr int STAGE = 2 * TILE;  // K, V
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[2 * STAGE];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lg = lane >> 5;
   const int qh = wave & 1, kh = wave >> 1;
@@ -576,6 +563,15 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
   const int qi = q0 + (lane & 31);
   const size_t tok0 = (size_t)b * S;
   const int ldo = nq * D;
+
+  const bf16_t* kbase = qkv + tok0 * ldq + (size_t)(nq + hk) * D;
+  const bf16_t* vbase = qkv + tok0 * ldq + (size_t)(nq + nkv + hk) * D;
+  auto fetch = [&](int t) {
+    bf16_t* st = smem + (t & 1) * STAGE;
+    dma_rows<64, D>(st, kbase + (size_t)t * 64 * ldq, ldq, wave, lane);
+    dma_rows<64, D>(st + TILE, vbase + (size_t)t * 64 * ldq, ldq, wave, lane);
+  };
+  fetch(0);
 
   bf16x8 qf[D / 16], of[D / 16];
   {
@@ -594,24 +590,15 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
   for (int i = 0; i < D / 32; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) dq[i][r] = 0.f;
+  const int krow = kh * 32 + (lane & 31);   // the lane's key row in the K / V tiles
 
-  const bf16_t* kbase = qkv + tok0 * ldq + (size_t)(nq + hk) * D;
-  const bf16_t* vbase = qkv + tok0 * ldq + (size_t)(nq + nkv + hk) * D;
-  const bf16_t* ktbase = qkvT + ((size_t)b * ldq + (size_t)(nq + hk) * D) * S;
   const int ntk = CAUSAL ? qb + 1 : ntile;
-  auto fetch = [&](int t) {
-    const int k0 = t * 64;
-    dma_tile<64, D / 8>(smem, kbase + (size_t)k0 * ldq, ldq, wave, lane);
-    dma_tile<64, D / 8>(smem + TILE, vbase + (size_t)k0 * ldq, ldq, wave, lane);
-    dma_tile<D, 8>(smem + 2 * TILE, ktbase + k0, S, wave, lane);
-  };
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+  __syncthreads();
   for (int t = 0; t < ntk; ++t) {
-    fetch(t);
-    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
-    __syncthreads();
-    const bf16_t* sK = smem;
+    if (t + 1 < ntk) fetch(t + 1);   // into the stage every wave finished with last iteration
+    const bf16_t* sK = smem + (t & 1) * STAGE;
     const bf16_t* sV = sK + TILE;
-    const bf16_t* sKT = sK + 2 * TILE;
     const int ks = t * 64 + kh * 32;
     if (!CAUSAL || ks <= q0 + 31) {
       f32x16 s, dp;
@@ -619,9 +606,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
       for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
-        const int row = kh * 32 + (lane & 31);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<D>(sK, row, 2 * kk + lg), qf[kk], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<D>(sV, row, 2 * kk + lg), of[kk], dp, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_d<D>(sK, krow, 2 * kk + lg), qf[kk], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_d<D>(sV, krow, 2 * kk + lg), of[kk], dp, 0, 0, 0);
       }
       // element j: key ks + 8(j>>2) + 4lg + (j&3), query qi
       float ds[16];
@@ -646,12 +632,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
       pack_half(ds, d0, d1);
 #pragma unroll
       for (int df = 0; df < D / 32; ++df) {
-        const int row = df * 32 + (lane & 31);
-        dq[df] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<64>(sKT, row, 4 * kh + lg), d0, dq[df], 0, 0, 0);
-        dq[df] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<64>(sKT, row, 4 * kh + 2 + lg), d1, dq[df], 0, 0, 0);
+        dq[df] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_t<D>(sK, 2 * kh, 32 * df, lane), d0, dq[df], 0, 0, 0);
+        dq[df] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_t<D>(sK, 2 * kh + 1, 32 * df, lane), d1, dq[df], 0, 0,
+                                                         0);
       }
     }
-    __syncthreads();  // every wave is done with the tile before the next one lands
+    // tile t+1 landed, and every wave is done with stage t & 1
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+    __syncthreads();
   }
   constexpr int NR = D / 2;
   float* xo = reinterpret_cast<float*>(smem);  // [qh][NR][64]
@@ -798,15 +786,14 @@ __global__ __launch_bounds__(128) void attn_bwd_dkdv_f32_kernel(
 }
 
 template <int D>
-hipError_t attn_fwd_bf16(int B, int S, int nq, int nkv, int causal, const void* qkv,
-                         const void* qkvT, void* O, float* lse, const Drop& drop,
-                         hipStream_t st) {
+hipError_t attn_fwd_bf16(int B, int S, int nq, int nkv, int causal, const void* qkv, void* O,
+                         float* lse, const Drop& drop, hipStream_t st) {
   const int ldq = (nq + 2 * nkv) * D;
   dim3 grid((S / 64) * B * nq);
   const float sl2 = kLog2e / sqrtf((float)D);
 #define MTB_FWD(C, DR)                                                                        \
   hipLaunchKernelGGL((attn_fwd_kernel<D, C, DR>), grid, dim3(256), 0, st, S, nq, nkv, ldq,    \
-                     (const bf16_t*)qkv, (const bf16_t*)qkvT, (bf16_t*)O, lse, sl2, drop)
+                     (const bf16_t*)qkv, (bf16_t*)O, lse, sl2, drop)
   if (causal) {
     if (drop.thr) MTB_FWD(true, true); else MTB_FWD(true, false);
   } else {
@@ -817,9 +804,8 @@ hipError_t attn_fwd_bf16(int B, int S, int nq, int nkv, int causal, const void* 
 }
 
 template <int D>
-hipError_t attn_bwd_bf16(int B, int S, int nq, int nkv, int causal, const void* qkv,
-                         const void* qkvT, const void* O, const void* dO, const void* dOT,
-                         const float* lse, float* Dbuf, void* dqkv, float* part,
+hipError_t attn_bwd_bf16(int B, int S, int nq, int nkv, int causal, const void* qkv, const void* O,
+                         const void* dO, const float* lse, float* Dbuf, void* dqkv, float* part,
                          const Drop& drop, hipStream_t st) {
   const int ldq = (nq + 2 * nkv) * D;
   const float sl2 = kLog2e / sqrtf((float)D), scale = 1.0f / sqrtf((float)D);
@@ -829,11 +815,11 @@ hipError_t attn_bwd_bf16(int B, int S, int nq, int nkv, int causal, const void* 
   dim3 grid((S / 64) * B * nq);
 #define MTB_BWD(C, DR)                                                                        \
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, C, DR>), grid, dim3(256), 0, st, S, nq, nkv,   \
-                     ldq, (const bf16_t*)qkv, (const bf16_t*)qkvT, (const bf16_t*)dO,        \
-                     (const bf16_t*)dOT, lse, Dbuf, (bf16_t*)dqkv, part, sl2, scale, drop);  \
+                     ldq, (const bf16_t*)qkv, (const bf16_t*)dO, lse, Dbuf, (bf16_t*)dqkv,   \
+                     part, sl2, scale, drop);                                                \
   hipLaunchKernelGGL((attn_bwd_dq_kernel<D, C, DR>), grid, dim3(256), 0, st, S, nq, nkv, ldq,\
-                     (const bf16_t*)qkv, (const bf16_t*)qkvT, (const bf16_t*)dO, lse, Dbuf,  \
-                     (bf16_t*)dqkv, sl2, scale, drop)
+                     (const bf16_t*)qkv, (const bf16_t*)dO, lse, Dbuf, (bf16_t*)dqkv, sl2,   \
+                     scale, drop)
   if (causal) {
     if (drop.thr) { MTB_BWD(true, true); } else { MTB_BWD(true, false); }
   } else {
@@ -881,10 +867,10 @@ hipError_t attn_bwd_f32(int B, int S, int nq, int nkv, int causal, const void* q
 }  // namespace
 
 hipError_t attn_fwd(int dtype, int B, int S, int nq, int nkv, int d, int causal, const void* qkv,
-                    const void* qkvT, void* O, float* lse, hipStream_t st, const Drop& drop) {
+                    void* O, float* lse, hipStream_t st, const Drop& drop) {
   if (dtype == 1) {
-    if (d == 64) return attn_fwd_bf16<64>(B, S, nq, nkv, causal, qkv, qkvT, O, lse, drop, st);
-    if (d == 128) return attn_fwd_bf16<128>(B, S, nq, nkv, causal, qkv, qkvT, O, lse, drop, st);
+    if (d == 64) return attn_fwd_bf16<64>(B, S, nq, nkv, causal, qkv, O, lse, drop, st);
+    if (d == 128) return attn_fwd_bf16<128>(B, S, nq, nkv, causal, qkv, O, lse, drop, st);
     return hipErrorInvalidValue;
   }
   if (d == 32) return attn_fwd_f32<32>(B, S, nq, nkv, causal, qkv, O, lse, drop, st);
@@ -894,16 +880,11 @@ hipError_t attn_fwd(int dtype, int B, int S, int nq, int nkv, int d, int causal,
 }
 
 hipError_t attn_bwd(int dtype, int B, int S, int nq, int nkv, int d, int causal, const void* qkv,
-                    const void* qkvT, const void* O, const void* dO, const void* dOT,
-                    const float* lse, float* Dbuf, void* dqkv, float* part, hipStream_t st,
-                    const Drop& drop) {
+                    const void* O, const void* dO, const float* lse, float* Dbuf, void* dqkv,
+                    float* part, hipStream_t st, const Drop& drop) {
   if (dtype == 1) {
-    if (d == 64)
-      return attn_bwd_bf16<64>(B, S, nq, nkv, causal, qkv, qkvT, O, dO, dOT, lse, Dbuf, dqkv, part,
-                               drop, st);
-    if (d == 128)
-      return attn_bwd_bf16<128>(B, S, nq, nkv, causal, qkv, qkvT, O, dO, dOT, lse, Dbuf, dqkv,
-                                part, drop, st);
+    if (d == 64) return attn_bwd_bf16<64>(B, S, nq, nkv, causal, qkv, O, dO, lse, Dbuf, dqkv, part, drop, st);
+    if (d == 128) return attn_bwd_bf16<128>(B, S, nq, nkv, causal, qkv, O, dO, lse, Dbuf, dqkv, part, drop, st);
     return hipErrorInvalidValue;
   }
   if (d == 32) return attn_bwd_f32<32>(B, S, nq, nkv, causal, qkv, O, dO, lse, Dbuf, dqkv, drop, st);

@@ -27,9 +27,7 @@
 // inputs, the stored outputs -- is 16 bytes per lane over whole rows. Storing
 // straight from the MFMA layout touches 32 rows per instruction with 16 bytes
 // each; on MI355X those partial-line writes reach HBM several times over
-// (measured 3.5x the output bytes for the two-output GELU epilogue). The
-// per-batch transposed copy that attention reads is written from the same
-// staged tile by columns, 128 contiguous bytes per output row.
+// (measured 3.5x the output bytes for the two-output GELU epilogue).
 //
 // Uses in the block ([TP-block] sec. 1-2; [MLM-notes] Column/RowParallelLinear):
 //   forward   Y = X W^T         A = X [T][in],  B = W [out][in]     (k-contig both)
@@ -484,43 +482,6 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(int M, int N, int sp
   st8(out + m * ldo + n, v);
 }
 
-// Column phase: the per-batch transposed copy outT[b][n][s] of the stored
-// values. Inside every 16 tokens the order is 0-3, 8-11, 4-7, 12-15 (bits 2
-// and 3 of the token index swapped), the key order the attention kernels'
-// MFMA operands consume. 8 lanes cover 64 consecutive positions (128 bytes)
-// of one output row; each lane writes 8 positions = tokens {4h..4h+3,
-// 8+4h..8+4h+3} of one 16-token block.
-template <int BN, int CR, int NT>
-MTB_DEV void epi_cols(const Epi& e, const Staged<BN>& st, int M, int N, int mc, int n0, int tid) {
-  static_assert(CR % 64 == 0, "whole 64-token groups per chunk");
-  for (int it = tid; it < BN * CR / 8; it += NT) {
-    const int l8 = it & 7, nl = (it >> 3) % BN, g = (it >> 3) / BN;
-    const int n = n0 + nl, blk = g * 64 + (l8 >> 1) * 16, h = l8 & 1;
-    const int m = mc + blk;  // first token of the 16-token block
-    if (m >= M || n >= N) continue;
-    float v[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[i] = st.get(blk + 4 * h + i, nl);
-      v[4 + i] = st.get(blk + 8 + 4 * h + i, nl);
-    }
-    if (e.bias) {
-      const float b = bf2f(reinterpret_cast<const bf16_t*>(e.bias)[n]);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] += b;
-    }
-    if (e.resid) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[i] += bf2f(reinterpret_cast<const bf16_t*>(e.resid)[(size_t)(m + 4 * h + i) * e.ldr + n]);
-        v[4 + i] += bf2f(reinterpret_cast<const bf16_t*>(e.resid)[(size_t)(m + 8 + 4 * h + i) * e.ldr + n]);
-      }
-    }
-    const int bb = m / e.S, s = m % e.S + 8 * h;
-    out8(e.outT, ((size_t)bb * N + n) * e.S + s, v);
-  }
-}
-
 // Epilogue of a split contraction with a fused epilogue: sums the fp32
 // partial tiles of ws [splits][M][N] in split order into the staged tile, then
 // runs the same row (and column) phases as the GEMM kernel. One block per
@@ -555,9 +516,6 @@ __global__ __launch_bounds__(NT) void splitk_epi_kernel(int M, int N, int splits
     }
     __syncthreads();
     epi_rows<EPI, BN, CR, NT>(ep, st, M, N, m0 + c0, n0, tid);
-    if constexpr (EPI == EPI_STORE) {
-      if (ep.outT) epi_cols<BN, CR, NT>(ep, st, M, N, m0 + c0, n0, tid);
-    }
   }
 }
 
@@ -600,9 +558,6 @@ MTB_DEV void gemm_epilogue(const f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32], vo
   constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32;
   constexpr int CR = stage_rows(BM, WM, SMEM_F / BN, BM);
   static_assert(CR >= WM && BM % CR == 0 && CR * BN <= SMEM_F, "staging chunk");
-  // the per-batch transposed copy (token-major left operand only) needs whole 64-token groups
-  constexpr bool COLS = EPI == EPI_STORE && AKC;
-  static_assert(!COLS || CR % 64 == 0, "transposed copy needs whole 64-token groups per chunk");
   const Staged<BN> st{reinterpret_cast<float*>(smem)};
   // RPRE (plain stores with a residual, EPI_DGELU, EPI_DSWIGLU): a chunk's
   // row operand is requested in full before any of its stores -- chunk 0's
@@ -661,9 +616,6 @@ MTB_DEV void gemm_epilogue(const f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32], vo
       epi_rows_dswiglu_pre<BN, CR, NT>(ep, st, M, N, m0 + c0, n0, tid, spre);
     else
       epi_rows<EPI, BN, CR, NT>(ep, st, M, N, m0 + c0, n0, tid);
-    if constexpr (COLS) {
-      if (ep.outT) epi_cols<BN, CR, NT>(ep, st, M, N, m0 + c0, n0, tid);
-    }
     if constexpr (PRE) {
       if (has_pre && c0 + CR < BM) load_pre(m0 + c0 + CR);
     }
@@ -1158,7 +1110,6 @@ PairPlan pair_plan(int M0, int N0, int K0, int lda0, int ldb0, int M1, int N1, i
 template <bool AKC, bool BKC, int EPI>
 hipError_t launch_bf16(int M, int N, int K, const void* A, int lda, const void* B, int ldb,
                        const Epi& e, hipStream_t st) {
-  if (!AKC && e.outT) return hipErrorInvalidValue;  // the transposed copy is token-major only
   const Plan pl = plan(M, N, K, AKC, BKC, EPI, e.ws != nullptr, EPI == EPI_STORE && e.resid != nullptr);
   if (pl.tile == TSCHED) {
     // operands past the 32-bit offsets: the 2x4-wavefront kernel on the same tiles

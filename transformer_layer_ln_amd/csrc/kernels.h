@@ -20,7 +20,7 @@ struct Drop {
 
 // GEMM epilogues. The product is C[m][n] = sum_k A(m,k) B(n,k).
 enum EpiKind {
-  EPI_STORE = 0,    // out = C (+bias[n]) (+resid[m][n]); optional per-batch transpose outT
+  EPI_STORE = 0,    // out = C (+bias[n]) (+resid[m][n])
   EPI_GELU = 1,     // u = C (+bias): out = u, out2 = GELU(u)
   EPI_SWIGLU = 2,   // u = C (+bias) over interleaved gate/up columns: out = u [M][2F],
                     // out2[m][f] = silu(gate) * up  [M][F]
@@ -52,9 +52,6 @@ struct Epi {
   const float* rowscale = nullptr;  // EPI_XENT_GRAD: [M] loss cotangent
   Drop drop;                   // EPI_STORE: out = resid + dropout(C + bias), element index
                                // m * N + n (the [T][H] hidden state)
-  void* outT = nullptr;        // [M/S][N][S]: per-batch transpose (tokens contiguous, bits 2
-                               // and 3 of the token index swapped: see gemm.hip)
-  int S = 1;
 };
 
 // C = A . B^T-style product with operand majorness:
@@ -64,9 +61,8 @@ hipError_t gemm(int dtype, int M, int N, int K, const void* A, int lda, bool a_k
                 const void* B, int ldb, bool b_kc, const Epi& e, hipStream_t st);
 // Bytes of Epi::ws that gemm() uses to split the contraction of this product
 // over several workgroups per output tile (0: it does not split). Plain-store
-// products (weight gradients; token-major products, also with the transposed
-// copy) with too few tiles to fill the chip are split; the partial tiles are
-// summed in a fixed order.
+// products (weight gradients; token-major products) with too few tiles to
+// fill the chip are split; the partial tiles are summed in a fixed order.
 size_t gemm_ws_bytes(int dtype, int M, int N, int K, bool a_kc, bool b_kc, int kind);
 // One product for gemm_wgrad_pair: C[M][N] = sum_k A[k][M] B[k][N] (both
 // operands stored k-major, as weight gradients read activations), plain store
@@ -120,17 +116,14 @@ hipError_t act_bwd(int dtype, int act, int rows, int F, const void* dm, const vo
                    hipStream_t st);
 
 // Attention. qkv [T][Nqkv] token-major ([Q heads | K heads | V heads]);
-// qkvT [B][Nqkv][S] (bf16 path only; tokens in the within-16 order the GEMM
-// epilogue writes); O [T][nq*d]; lse [B][nq][S] (natural log).
+// O [T][nq*d]; lse [B][nq][S] (natural log).
 hipError_t attn_fwd(int dtype, int B, int S, int nq, int nkv, int d, int causal, const void* qkv,
-                    const void* qkvT, void* O, float* lse, hipStream_t st,
-                    const Drop& drop = Drop());
-// dO [T][nq*d], dOT [B][nq*d][S] (bf16 only); Dbuf [B][nq][S] fp32 scratch;
-// dqkv [T][Nqkv] output; part: fp32 scratch of B*nq*S*2*d floats (GQA, bf16).
+                    void* O, float* lse, hipStream_t st, const Drop& drop = Drop());
+// dO [T][nq*d]; Dbuf [B][nq][S] fp32 scratch; dqkv [T][Nqkv] output; part:
+// fp32 scratch of B*nq*S*2*d floats (GQA, bf16).
 hipError_t attn_bwd(int dtype, int B, int S, int nq, int nkv, int d, int causal, const void* qkv,
-                    const void* qkvT, const void* O, const void* dO, const void* dOT,
-                    const float* lse, float* Dbuf, void* dqkv, float* part, hipStream_t st,
-                    const Drop& drop = Drop());
+                    const void* O, const void* dO, const float* lse, float* Dbuf, void* dqkv,
+                    float* part, hipStream_t st, const Drop& drop = Drop());
 
 // Vocab-sharded cross-entropy.
 hipError_t xent_partial(int dtype, int64_t n, int64_t v, int64_t v0, const void* z,
