@@ -14,10 +14,11 @@ that csrc/gen_gemm_loop.py writes to csrc/gemm_loop.inc).
    - a copy into a stage is issued only when every read of the stage's
      previous tile retired before a barrier (no wavefront still reads it);
    - the copies fetch k-tiles 0, 1, ..., KT-1 in order and then re-fetch the
-     last one, for any KT (the body is entered at slot -KT mod 4); M0 is
+     last one, for any KT (the body is entered at slot -KT mod SLOTS); M0 is
      written, with a wait state, before every copy;
    - wait counts fit their fields, LDS read offsets fit 16 bits, copy
-     destinations stay inside the 128 KB of stages.
+     destinations stay inside their operand's part of a stage.
+   This for every tile shape the generator builds (256 x 256, 256 x 192).
 """
 import importlib.util
 import os
@@ -50,16 +51,19 @@ class ScheduleError(AssertionError):
 
 
 class Wave:
-    """Symbolic state of one wavefront running the loop for KT k-tiles."""
+    """Symbolic state of one wavefront running the loop of shape `sh` for KT k-tiles."""
 
-    def __init__(self, layouts, KT):
+    def __init__(self, layouts, KT, sh=GEN.S256):
         self.lay = layouts                 # {"a": "kc"|"mn", "b": ...}
+        self.sh = sh
         self.KT = KT
-        self.first = -KT % GEN.STAGES     # the body slot k-tile 0 runs in
-        self.iters = (KT + self.first) // GEN.STAGES
+        self.first = -KT % sh.slots       # the body slot k-tile 0 runs in
+        self.iters = (KT + self.first) // sh.slots
         self.rem = KT - 1
-        self.src = {(x, q): 0 for x in "AB" for q in range(4)}   # k-tile the copy offset points at
-        self.copied = {(x, q): [] for x in "AB" for q in range(4)}
+        self.nq = {"A": sh.qa, "B": sh.qb}
+        keys = [(x, q) for x in "AB" for q in range(self.nq[x])]
+        self.src = {k: 0 for k in keys}   # k-tile the copy offset points at
+        self.copied = {k: [] for k in keys}
         self.t = {"ta": None, "tb": None}
         self.scc = None
         self.m0 = None
@@ -67,11 +71,12 @@ class Wave:
         self.vm = []         # outstanding copies: (stage, x, q)
         self.regs = {}       # first VGPR of a 2-register half -> (content, landed)
         self.epoch = 0       # barriers passed
-        self.visible = {s: None for s in range(GEN.STAGES)}       # k-tile readable in a stage
-        self.blocks = {s: {} for s in range(GEN.STAGES)}          # (x, q) -> [tile, complete]
-        self.reads_done = {s: [] for s in range(GEN.STAGES)}      # epochs of retired reads
-        self.reads_open = {s: 0 for s in range(GEN.STAGES)}
-        self.acc = {(i, j): [] for i in range(4) for j in range(4)}
+        S = sh.stages
+        self.visible = {s: None for s in range(S)}       # k-tile readable in a stage
+        self.blocks = {s: {} for s in range(S)}          # (x, q) -> [tile, complete]
+        self.reads_done = {s: [] for s in range(S)}      # epochs of retired reads
+        self.reads_open = {s: 0 for s in range(S)}
+        self.acc = {(i, j): [] for i in range(sh.fm) for j in range(sh.fn)}
         self.prev = []       # the last two instructions (M0 hazard check)
 
     def fail(self, msg):
@@ -95,33 +100,47 @@ class Wave:
         self.epoch += 1
         for s, blk in self.blocks.items():
             tiles = {t for t, _ in blk.values()}
-            if len(blk) == 8 and len(tiles) == 1 and all(c for _, c in blk.values()):
+            if len(blk) == self.sh.cpt and len(tiles) == 1 and all(c for _, c in blk.values()):
                 self.visible[s] = tiles.pop()
 
     # --- instructions
     def ds_read(self, kind, reg, base, off):
+        sh = self.sh
+        SB = sh.stage_bytes
         if off > 65535:
             self.fail(f"LDS read offset {off} does not fit 16 bits")
         x, n = base[0], int(base[1:])
         op = "ab".index(x)
-        hi = n // 2 if self.lay[x] == "kc" else n // 4
-        stage = 2 * hi + off // STAGE
+        F = sh.nfrag(op)
         if self.lay[x] == "kc":
             if kind != "ds_read_b128":
                 self.fail("k-contiguous operand read with " + kind)
-            kk, idx, half = n % 2, (off % STAGE) // 2048, None
+            st, kk = n // 2, n % 2
+            stage = 2 * st + off // SB
+            idx, half = (off % SB) // 2048, None
+            if (off % SB) % 2048:
+                self.fail(f"read offset {off} is not a fragment start")
             regs = [reg, reg + 2]
         else:
             if kind != "ds_read_b64_tr_b16":
                 self.fail("transposed operand read with " + kind)
-            idx, kk, half = n % 4, (off % STAGE) // 8192, (off % 8192) // 2048
+            rb = sh.rows(op) * 2
+            st, idx = n // F, n % F
+            stage = 2 * st + off // SB
+            rem = off % SB
+            kk, half = rem // (16 * rb), (rem % (16 * rb)) // (4 * rb)
+            if rem % (4 * rb) or kk > 1 or half > 1:
+                self.fail(f"transpose read offset {off} is not a fragment half")
             regs = [reg] if half == 0 else [reg - 2]
+        if stage >= sh.stages or idx >= F:
+            self.fail(f"read of stage {stage} fragment {idx}: outside the tile")
         tile = self.visible[stage]
         if tile is None:
             self.fail(f"read of stage {stage} before its copy completed behind a barrier")
         r0 = regs[0]
-        exp = GEN.freg((r0 - 128) // 64, kk, op, idx)
-        if r0 != exp:
+        buf = (r0 - sh.frag_lo) // sh.per_buf
+        exp = sh.freg(buf, kk, op, idx)
+        if r0 != exp or r0 < sh.frag_lo or r0 + 4 > sh.frag_hi:
             self.fail(f"fragment (kk {kk}, op {x}, {idx}) read into v{r0}, expected v{exp}")
         content = (tile, kk, op, idx)
         dest = regs if half is None else [reg]
@@ -131,12 +150,16 @@ class Wave:
         self.reads_open[stage] += 1
 
     def copy(self, x, q):
+        sh = self.sh
+        SB = sh.stage_bytes
         if len(self.prev) < 2 or self.prev[-1] != "s_nop" or self.prev[-2] != "m0":
             self.fail("copy not preceded by an M0 write and one wait state")
         mx, moff = self.m0
-        stage, mq = moff // STAGE, (moff % STAGE) // 1024
-        # the last wavefront's block ends at M0 + its 3 * 4 KB + 1 KB
-        if mx != x or mq != q or moff % 1024 or moff + (GEN.B_OFFSET if x == "B" else 0) + 3 * 4096 + 1024 > GEN.STAGES * STAGE:
+        stage, mq = moff // SB, (moff % SB) // 1024
+        # the last wavefront's block ends at M0 + its 3 Q KB + 1 KB, inside the operand's region
+        region = sh.a_bytes if x == "A" else sh.b_bytes
+        if mx != x or mq != q or moff % 1024 or q >= self.nq[x] or stage >= sh.stages or \
+                (moff % SB) + 3 * self.nq[x] * 1024 + 1024 > region:
             self.fail(f"M0 {self.m0} does not address block {q} of operand {x}")
         if self.reads_open[stage] or any(e >= self.epoch for e in self.reads_done[stage]):
             self.fail(f"copy into stage {stage} while a read of its previous tile may be in flight")
@@ -234,20 +257,43 @@ class Wave:
         return None
 
 
-@pytest.mark.parametrize("name,la,lb", GEN.LAYOUTS)
-@pytest.mark.parametrize("KT", [1, 2, 3, 4, 5, 6, 7, 8, 13, 32, 501])
-def test_schedule_symbolic_execution(name, la, lb, KT):
-    lines = GEN.loop(la, lb)
+def _check_run(la, lb, KT, sh=GEN.S256, **variant):
+    lines = GEN.loop(la, lb, sh=sh, **variant)
     assert lines[0] == "s_nop 4" and lines[-3:] == ["s_nop 7"] * 3   # accumulator hazards
-    w = Wave({"a": la, "b": lb}, KT)
+    w = Wave({"a": la, "b": lb}, KT, sh)
     w.run(lines)
     assert not w.lgkm and not w.vm, "memory operations outstanding at the end"
     want = [(t, kk) for t in range(KT) for kk in (0, 1)]
     for ij, got in w.acc.items():
-        assert got == want, f"accumulator c{ij[0]}{ij[1]}"
+        assert got == want, f"{sh.name} {variant} KT {KT} accumulator c{ij[0]}{ij[1]}"
     for key, tiles in w.copied.items():
         n = len(tiles)
         assert tiles == list(range(KT)) + [KT - 1] * (n - KT), f"copy sequence of {key}: {tiles}"
+    return w
+
+
+@pytest.mark.parametrize("name,la,lb", GEN.LAYOUTS)
+@pytest.mark.parametrize("KT", [1, 2, 3, 4, 5, 6, 7, 8, 13, 32, 501])
+def test_schedule_symbolic_execution(name, la, lb, KT):
+    _check_run(la, lb, KT)
+
+
+@pytest.mark.parametrize("shape", [s.name for s in GEN.SHAPES if s is not GEN.S256])
+@pytest.mark.parametrize("KT", [1, 2, 3, 4, 5, 6, 7, 8, 11, 13, 32, 128])
+def test_other_shapes_symbolic_execution(shape, KT):
+    """The 256 x 192 loop, for every layout built."""
+    sh = next(s for s in GEN.SHAPES if s.name == shape)
+    for name, la, lb in GEN.SHAPE_LAYOUTS[shape]:
+        _check_run(la, lb, KT, sh)
+
+
+def test_shapes_fit_their_registers_and_lds():
+    """Fragment registers inside the clobbered range, stages inside a CU's
+    160 KB of LDS, copy blocks whole."""
+    for sh in GEN.SHAPES:
+        assert sh.stages * sh.stage_bytes <= 160 * 1024, sh.name
+        assert sh.a_bytes % 4096 == 0 and sh.b_bytes % 4096 == 0, sh.name
+        assert sh.frag_lo >= 0 and sh.frag_hi <= 256
 
 
 @pytest.mark.parametrize("name,la,lb", GEN.LAYOUTS)
@@ -256,14 +302,8 @@ def test_schedule_symbolic_execution(name, la, lb, KT):
 def test_measurement_variants_are_valid_schedules(name, la, lb, variant):
     """The generator's measurement variants (timed against the default in
     alternating runs) obey the same waits, barriers and k-tile order."""
-    lines = GEN.loop(la, lb, **variant)
     for KT in (1, 2, 3, 5, 13):
-        w = Wave({"a": la, "b": lb}, KT)
-        w.run(lines)
-        assert not w.lgkm and not w.vm
-        want = [(t, kk) for t in range(KT) for kk in (0, 1)]
-        for ij, got in w.acc.items():
-            assert got == want, f"{variant} KT {KT} accumulator c{ij[0]}{ij[1]}"
+        _check_run(la, lb, KT, **variant)
 
 
 def test_symbolic_execution_catches_a_short_wait():

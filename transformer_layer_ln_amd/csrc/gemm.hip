@@ -709,21 +709,37 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(int M, i
                                                             lane, tid);
 }
 
-// 256 x 256 tile, 4 wavefronts (2 x 2) of 128 x 128 each, with the hand-scheduled
-// main loop of gemm_loop.inc (schedule and LDS layout: gen_gemm_loop.py).
+// Hand-scheduled tiles: 4 wavefronts (2 x 2), each with FM x FN 32x32
+// accumulators, the k-loop one inline-assembly block of gemm_loop.inc
+// (schedules and LDS layout: gen_gemm_loop.py). Shapes:
+//   SH256: 256 x 256, 4 stages, one block per CU;
+//   SH192: 256 x 192, 4 stages, one block per CU (1536-wide products: 256
+//          tiles on 256 CUs instead of 192).
 // Needs each split's contraction to be a multiple of 32 and every operand
 // byte offset below 2^32 (sched_ok).
-constexpr int SBK = 32, SSTAGES = 4;
-
-constexpr int SMEM_SCHED = SSTAGES * (256 + 256) * SBK;  // bf16 elements of LDS
+constexpr int SBK = 32;
+enum SchedShape { SH256 = 0, SH192 = 1 };
+template <int SH>
+struct Sched {
+  static constexpr int FM = 4, FN = SH == SH256 ? 4 : 3;
+  static constexpr int BM = 64 * FM, BN = 64 * FN;
+  static constexpr int STAGES = 4;
+  static constexpr int SLOTS = STAGES;                 // loop body slots (gen_gemm_loop.py)
+  static constexpr int PER_CU = 1;
+  static constexpr int QA = BM / 64, QB = BN / 64;     // copy blocks per wavefront and k-tile
+  static constexpr uint32_t STAGE_BYTES = (BM + BN) * SBK * 2;
+  static constexpr int SETS = (STAGES + 1) / 2;       // fragment base sets (stages 2i, 2i+1)
+  static constexpr int SMEM = STAGES * (BM + BN) * SBK;  // bf16 elements of LDS
+};
 
 // One block's tile (bt) of the product: the k-loop and the epilogue. smem is
-// the block's SMEM_SCHED-element LDS array (1-KB aligned).
-template <bool AKC, bool BKC, int EPI>
+// the block's Sched<SH>::SMEM-element LDS array (1-KB aligned).
+template <int SH, bool AKC, bool BKC, int EPI>
 MTB_DEV void sched_tile(bf16_t* smem, int M, int N, int K, const bf16_t* __restrict__ A, int lda,
                         const bf16_t* __restrict__ B, int ldb, const Epi& ep, int ksplit,
                         const BlockTile& bt) {
-  constexpr int BM = 256, BN = 256;
+  using G = Sched<SH>;
+  constexpr int BM = G::BM, BN = G::BN, FM = G::FM, FN = G::FN;
   constexpr uint32_t B_OFF = BM * SBK * 2;  // operand B follows A inside a stage (bytes)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -732,72 +748,85 @@ MTB_DEV void sched_tile(bf16_t* smem, int M, int N, int K, const bf16_t* __restr
   const int m0 = bt.tm * BM, n0 = bt.tn * BN;
   const uint32_t lds = (uint32_t)(uintptr_t)smem;
 
-  // Copies: this wavefront's blocks 4 wave + q (q = 0..3) of 1 KB per operand
-  // and k-tile; lane l writes bytes [16 l, 16 l + 16) of its block.
+  // Copies: this wavefront's blocks Q wave + q (q < Q) of 1 KB per operand and
+  // k-tile; lane l writes bytes [16 l, 16 l + 16) of its block.
   // k-contiguous: block = 16 rows x 64 bytes; row r's chunk c sits at c ^ ((r >> 2) & 3).
-  // otherwise:    block = 2 k-rows x 512 bytes; k-row k's chunk c sits at c ^ ((k & 3) << 2).
-  auto copy_off = [&](bool kc, int q, int row0, int rows, int ld) -> uint32_t {
-    const int b = 4 * wave + q;
+  // otherwise:    block = 1024 / (2 ROWS) k-rows of 2 ROWS bytes; k-row k's chunk c sits at
+  //               c ^ ((k & 3) << 2).
+  auto copy_off = [&](bool kc, int b, int row0, int rows, int ld, int ROWS) -> uint32_t {
     if (kc) {
       const int r = 16 * b + (lane >> 2), c = (lane & 3) ^ ((r >> 2) & 3);
       return ((uint32_t)min(row0 + r, rows - 1) * (uint32_t)ld + c * 8) * 2u;
     }
-    const int k = 2 * b + (lane >> 5), c = (lane & 31) ^ ((k & 3) << 2);
+    const int cpr = ROWS / 8, kpb = 64 / cpr;   // chunks per k-row, k-rows per block
+    const int k = kpb * b + lane / cpr, c = (lane % cpr) ^ ((k & 3) << 2);
     return ((uint32_t)k * (uint32_t)ld + (uint32_t)min(row0 + c * 8, rows - 8)) * 2u;
   };
-  uint32_t voA[4], voB[4];
+  uint32_t voA[G::QA], voB[G::QB];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    voA[q] = copy_off(AKC, q, m0, M, lda);
-    voB[q] = copy_off(BKC, q, n0, N, ldb);
-  }
+  for (int q = 0; q < G::QA; ++q) voA[q] = copy_off(AKC, G::QA * wave + q, m0, M, lda, BM);
+#pragma unroll
+  for (int q = 0; q < G::QB; ++q) voB[q] = copy_off(BKC, G::QB * wave + q, n0, N, ldb, BN);
   const uint64_t sbA = (uint64_t)(A + (AKC ? (size_t)kbeg : (size_t)kbeg * lda));
   const uint64_t sbB = (uint64_t)(B + (BKC ? (size_t)kbeg : (size_t)kbeg * ldb));
   const uint32_t ksA = AKC ? SBK * 2 : SBK * 2 * (uint32_t)lda;
   const uint32_t ksB = BKC ? SBK * 2 : SBK * 2 * (uint32_t)ldb;
-  const uint32_t ldsA = __builtin_amdgcn_readfirstlane(lds + wave * 4096);
-  const uint32_t ldsB = __builtin_amdgcn_readfirstlane(lds + B_OFF + wave * 4096);
+  const uint32_t ldsA = __builtin_amdgcn_readfirstlane(lds + wave * G::QA * 1024);
+  const uint32_t ldsB = __builtin_amdgcn_readfirstlane(lds + B_OFF + wave * G::QB * 1024);
 
-  // Fragment base addresses (stages 2 and 3 from the second set, 64 KB on,
-  // past the reach of the 16-bit read offset).
-  // k-contiguous: f[2 hi + kk] for step kk (fragment i is 2 KB further);
-  // otherwise: f[4 hi + i] for fragment i (step kk is 8 KB further).
-  auto frag_bases = [&](bool kc, int w, uint32_t off, uint32_t (&f)[8]) {
+  // Fragment base addresses; set i (stages 2i, 2i+1) 2 i STAGE_BYTES further,
+  // so that every read offset fits the 16-bit immediate.
+  // k-contiguous: f[2 set + kk] for step kk (fragment i is 2 KB further);
+  // otherwise: f[F set + i] for fragment i (step kk is 32 ROWS bytes further).
+  constexpr int NA = G::SETS * (AKC ? 2 : FM), NB = G::SETS * (BKC ? 2 : FN);
+  auto frag_bases = [&](bool kc, int w, uint32_t off, int F, int ROWS, uint32_t* f) {
     if (kc) {
-      const int r = w * 128 + (lane & 31);
+      const int r = w * 32 * F + (lane & 31);
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const int c = 2 * kk + (lane >> 5);
-        f[kk] = lds + off + r * 64 + ((c ^ ((r >> 2) & 3)) << 4);
-        f[2 + kk] = f[kk] + 65536;
-        f[4 + kk] = f[kk];
-        f[6 + kk] = f[2 + kk];
+        const uint32_t b0 = lds + off + r * 64 + ((c ^ ((r >> 2) & 3)) << 4);
+#pragma unroll
+        for (int st = 0; st < G::SETS; ++st) f[2 * st + kk] = b0 + st * 2 * G::STAGE_BYTES;
       }
     } else {
       const int g = lane >> 4, sl = lane & 15, k = 8 * (g >> 1) + (sl >> 2);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = w * 128 + 32 * i + 16 * (g & 1) + 4 * (sl & 3);
-        f[i] = lds + off + (k * 256 + ((m >> 3) ^ ((k & 3) << 2)) * 8 + (m & 7)) * 2;
-        f[4 + i] = f[i] + 65536;
+      for (int i = 0; i < F; ++i) {
+        const int m = w * 32 * F + 32 * i + 16 * (g & 1) + 4 * (sl & 3);
+        const uint32_t b0 = lds + off + (k * ROWS + ((m >> 3) ^ ((k & 3) << 2)) * 8 + (m & 7)) * 2;
+#pragma unroll
+        for (int st = 0; st < G::SETS; ++st) f[F * st + i] = b0 + st * 2 * G::STAGE_BYTES;
       }
     }
   };
-  uint32_t fa[8], fb[8];
-  frag_bases(AKC, wm, 0, fa);
-  frag_bases(BKC, wn, B_OFF, fb);
+  uint32_t fa[NA], fb[NB];
+  frag_bases(AKC, wm, 0, FM, BM, fa);
+  frag_bases(BKC, wn, B_OFF, FN, BN, fb);
 
   const int KT = kspan / SBK;
-  const int first = (SSTAGES - KT % SSTAGES) % SSTAGES;  // body slot of k-tile 0
-  int rem = KT - 1, iters = (KT + first) / SSTAGES;
+  const int first = (G::SLOTS - KT % G::SLOTS) % G::SLOTS;  // body slot of k-tile 0
+  int rem = KT - 1, iters = (KT + first) / G::SLOTS;
   uint32_t ta, tb;
-  f32x16 acc[4][4];
+  f32x16 acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+#define MTB_ACC_ROW(I)                                                                             \
+  [c##I##0] "+a"(acc[I][0]), [c##I##1] "+a"(acc[I][1])
+#define MTB_LOOP_COMMON                                                                            \
+    [rem] "+s"(rem), [iters] "+s"(iters), [ta] "=&s"(ta), [tb] "=&s"(tb)                           \
+  : [ldsA] "s"(ldsA), [ldsB] "s"(ldsB), [sbA] "s"(sbA), [sbB] "s"(sbB), [ksA] "s"(ksA),            \
+    [ksB] "s"(ksB), [first] "s"(first)
+  // The loop writes M0 (the LDS address of its copies) before every use; no
+  // code around it keeps a value in M0, so its clobber is declared without
+  // the compiler's warning about reserved registers.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  if constexpr (SH == SH256) {
 #define MTB_LOOP_OPERANDS                                                                          \
   : [c00] "+a"(acc[0][0]), [c01] "+a"(acc[0][1]), [c02] "+a"(acc[0][2]), [c03] "+a"(acc[0][3]),    \
     [c10] "+a"(acc[1][0]), [c11] "+a"(acc[1][1]), [c12] "+a"(acc[1][2]), [c13] "+a"(acc[1][3]),    \
@@ -805,38 +834,50 @@ MTB_DEV void sched_tile(bf16_t* smem, int M, int N, int K, const bf16_t* __restr
     [c30] "+a"(acc[3][0]), [c31] "+a"(acc[3][1]), [c32] "+a"(acc[3][2]), [c33] "+a"(acc[3][3]),    \
     [voA0] "+v"(voA[0]), [voA1] "+v"(voA[1]), [voA2] "+v"(voA[2]), [voA3] "+v"(voA[3]),            \
     [voB0] "+v"(voB[0]), [voB1] "+v"(voB[1]), [voB2] "+v"(voB[2]), [voB3] "+v"(voB[3]),            \
-    [rem] "+s"(rem), [iters] "+s"(iters), [ta] "=&s"(ta), [tb] "=&s"(tb)                           \
-  : [ldsA] "s"(ldsA), [ldsB] "s"(ldsB), [sbA] "s"(sbA), [sbB] "s"(sbB), [ksA] "s"(ksA),            \
-    [ksB] "s"(ksB), [first] "s"(first), [fa0] "v"(fa[0]), [fa1] "v"(fa[1]), [fa2] "v"(fa[2]), [fa3] "v"(fa[3]),        \
-    [fa4] "v"(fa[4]), [fa5] "v"(fa[5]), [fa6] "v"(fa[6]), [fa7] "v"(fa[7]), [fb0] "v"(fb[0]),      \
-    [fb1] "v"(fb[1]), [fb2] "v"(fb[2]), [fb3] "v"(fb[3]), [fb4] "v"(fb[4]), [fb5] "v"(fb[5]),      \
-    [fb6] "v"(fb[6]), [fb7] "v"(fb[7])                                                             \
+    MTB_LOOP_COMMON,                                                                               \
+    [fa0] "v"(fa[0]), [fa1] "v"(fa[1]), [fa2] "v"(fa[2]), [fa3] "v"(fa[3]),                        \
+    [fa4] "v"(fa[NA > 4 ? 4 : 0]), [fa5] "v"(fa[NA > 5 ? 5 : 0]), [fa6] "v"(fa[NA > 6 ? 6 : 0]),   \
+    [fa7] "v"(fa[NA > 7 ? 7 : 0]),                                                                 \
+    [fb0] "v"(fb[0]), [fb1] "v"(fb[1]), [fb2] "v"(fb[2]), [fb3] "v"(fb[3]),                        \
+    [fb4] "v"(fb[NB > 4 ? 4 : 0]), [fb5] "v"(fb[NB > 5 ? 5 : 0]), [fb6] "v"(fb[NB > 6 ? 6 : 0]),   \
+    [fb7] "v"(fb[NB > 7 ? 7 : 0])                                                                  \
   : "memory", "m0", "scc", MTB_GEMM_LOOP_CLOBBERS
-  // The loop writes M0 (the LDS address of its copies) before every use; no
-  // code around it keeps a value in M0, so its clobber is declared without
-  // the compiler's warning about reserved registers.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-  if constexpr (AKC && BKC)
-    asm volatile(MTB_GEMM_LOOP_NT MTB_LOOP_OPERANDS);
-  else if constexpr (AKC)
-    asm volatile(MTB_GEMM_LOOP_NN MTB_LOOP_OPERANDS);
-  else
-    asm volatile(MTB_GEMM_LOOP_TN MTB_LOOP_OPERANDS);
-#pragma clang diagnostic pop
+    if constexpr (AKC && BKC)
+      asm volatile(MTB_GEMM_LOOP_NT MTB_LOOP_OPERANDS);
+    else if constexpr (AKC)
+      asm volatile(MTB_GEMM_LOOP_NN MTB_LOOP_OPERANDS);
+    else
+      asm volatile(MTB_GEMM_LOOP_TN MTB_LOOP_OPERANDS);
 #undef MTB_LOOP_OPERANDS
+  } else if constexpr (SH == SH192) {
+    static_assert(AKC && BKC, "the 256 x 192 tile is built for k-contiguous operands only");
+    asm volatile(MTB_GEMM_LOOP_NT_192
+                 : [c00] "+a"(acc[0][0]), [c01] "+a"(acc[0][1]), [c02] "+a"(acc[0][2]),
+                   [c10] "+a"(acc[1][0]), [c11] "+a"(acc[1][1]), [c12] "+a"(acc[1][2]),
+                   [c20] "+a"(acc[2][0]), [c21] "+a"(acc[2][1]), [c22] "+a"(acc[2][2]),
+                   [c30] "+a"(acc[3][0]), [c31] "+a"(acc[3][1]), [c32] "+a"(acc[3][2]),
+                   [voA0] "+v"(voA[0]), [voA1] "+v"(voA[1]), [voA2] "+v"(voA[2]), [voA3] "+v"(voA[3]),
+                   [voB0] "+v"(voB[0]), [voB1] "+v"(voB[1]), [voB2] "+v"(voB[2]),
+                   MTB_LOOP_COMMON,
+                   [fa0] "v"(fa[0]), [fa1] "v"(fa[1]), [fa2] "v"(fa[2]), [fa3] "v"(fa[3]),
+                   [fb0] "v"(fb[0]), [fb1] "v"(fb[1]), [fb2] "v"(fb[2]), [fb3] "v"(fb[3])
+                 : "memory", "m0", "scc", MTB_GEMM_LOOP_CLOBBERS_192);
+  }
+#pragma clang diagnostic pop
+#undef MTB_LOOP_COMMON
+#undef MTB_ACC_ROW
   __syncthreads();
-  gemm_epilogue<BM, BN, 2, 2, SSTAGES * (BM + BN) * SBK / 2, AKC, EPI, true>(acc, smem, ep, M, N, m0, n0,
-                                                                            bt, wm, wn, lane, tid);
+  gemm_epilogue<BM, BN, 2, 2, G::SMEM / 2, AKC, EPI, true>(acc, smem, ep, M, N, m0, n0, bt, wm, wn, lane,
+                                                           tid);
 }
 
-template <bool AKC, bool BKC, int EPI>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_sched_kernel(int M, int N, int K,
-                                                                 const bf16_t* __restrict__ A, int lda,
-                                                                 const bf16_t* __restrict__ B, int ldb,
-                                                                 Epi ep, int ksplit) {
-  __shared__ __attribute__((aligned(1024))) bf16_t smem[SMEM_SCHED];
-  sched_tile<AKC, BKC, EPI>(smem, M, N, K, A, lda, B, ldb, ep, ksplit, block_tile<256, 256>(M, N));
+template <int SH, bool AKC, bool BKC, int EPI>
+__global__ __launch_bounds__(256, Sched<SH>::PER_CU) void gemm_bf16_sched_kernel(
+    int M, int N, int K, const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ B, int ldb,
+    Epi ep, int ksplit) {
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[Sched<SH>::SMEM];
+  sched_tile<SH, AKC, BKC, EPI>(smem, M, N, K, A, lda, B, ldb, ep, ksplit,
+                                block_tile<Sched<SH>::BM, Sched<SH>::BN>(M, N));
 }
 
 // One product of a grouped launch: its operands, split and block count.
@@ -855,7 +896,7 @@ struct SchedProb {
 // product whose tiles leave CUs idle shares the chip with another one.
 template <bool AKC, bool BKC, int EPI>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_sched_pair_kernel(SchedProb p0, SchedProb p1) {
-  __shared__ __attribute__((aligned(1024))) bf16_t smem[SMEM_SCHED];
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[Sched<SH256>::SMEM];
   const int r = xcd_order(blockIdx.x, gridDim.x);
   const bool second = r >= p0.blocks;  // uniform over the block
   const int M = second ? p1.M : p0.M, N = second ? p1.N : p0.N, K = second ? p1.K : p0.K;
@@ -864,8 +905,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_sched_pair_kernel(SchedProb 
   const int lda = second ? p1.lda : p0.lda, ldb = second ? p1.ldb : p0.ldb;
   const int ksplit = second ? p1.ksplit : p0.ksplit;
   const Epi ep = second ? p1.ep : p0.ep;
-  sched_tile<AKC, BKC, EPI>(smem, M, N, K, A, lda, B, ldb, ep, ksplit,
-                            tile_at<256, 256>(M, N, second ? r - p0.blocks : r));
+  sched_tile<SH256, AKC, BKC, EPI>(smem, M, N, K, A, lda, B, ldb, ep, ksplit,
+                                   tile_at<256, 256>(M, N, second ? r - p0.blocks : r));
 }
 
 // ---------------------------------------------------------------------------
@@ -940,7 +981,7 @@ double fill(long tiles, int per_cu) {
   return (double)tiles / (double)(waves * slots);
 }
 
-enum Tile { T256x256, T256x192, T256x128, T128x128, TSCHED };
+enum Tile { T256x256, T256x192, T256x128, T128x128, TSCHED, TSCHED192 };
 struct Plan {
   Tile tile;
   int splits;  // > 1: the contraction is split over that many blocks per tile
@@ -1002,6 +1043,16 @@ Plan plan(int M, int N, int K, bool a_kc, bool b_kc, int kind, bool split_ok, bo
     return {T128x128, 1};
   }
   const long t128 = tl(128, 128);
+  // token-major plain stores whose 256 x 256 tiles leave at least half of the
+  // chip idle and whose contraction is deep (the 8192 x 512 x 4096 projection
+  // data gradient: 64 tiles): the scheduled kernel on the contraction split
+  // 2-4 ways into parts at least 1024 deep, then one pass that sums the
+  // partial tiles and runs the epilogue
+  if (split_ok && a_kc && kind == EPI_STORE && 2 * t256 <= kCUs && K % SBK == 0) {
+    int s = 1;
+    while (s < 4 && t256 * s * 2 <= kCUs && sched_depth(2 * s)) s *= 2;
+    if (s > 1) return {TSCHED, s};
+  }
   if (split_ok && a_kc && kind == EPI_STORE && t128 <= kCUs && t256 < kCUs && K % BK == 0) {
     int s = 1;
     while (s < 4 && t128 * s < 2L * kCUs && (depth_ok(2 * s) || (!b_kc && t128 * s < kCUs && small_ok(2 * s))))
@@ -1016,9 +1067,15 @@ Plan plan(int M, int N, int K, bool a_kc, bool b_kc, int kind, bool split_ok, bo
   const bool sk = K % SBK == 0 && K >= (resid ? 512 : 1024);
   if (K >= 512) {
     const double f256 = (sk ? 1.3 : 1.0) * fill(t256, 1);
-    const double f192 = (a_kc && b_kc && kind == EPI_STORE && N % 192 == 0) ? 0.95 * fill(tl(256, 192), 1)
-                                                                            : 0.0;
-    if (f192 > f256 && f192 > f128) return {T256x192, 1};
+    // 256 x 192 tiles: plain stores (the 2x4-wavefront kernel) or any epilogue (the scheduled one)
+    const double f192 = (a_kc && b_kc && N % 192 == 0 && (sk || kind == EPI_STORE))
+                            ? (sk ? 1.3 : 0.95) * fill(tl(256, 192), 1) : 0.0;
+    if (f192 > f256 && f192 > f128) {
+      // the scheduled 256 x 192 tile where it fills more of the chip than the 256 x 256 one
+      // (the 8192 x 1536 QKV forward: 256 tiles instead of 192)
+      if (sk) return {TSCHED192, 1};
+      return {T256x192, 1};
+    }
     if (f256 >= f128) return {sk ? TSCHED : T256x256, 1};
   }
   return {T128x128, 1};
@@ -1036,11 +1093,12 @@ bool sched_ok(int M, int N, int K, bool a_kc, int lda, bool b_kc, int ldb, int s
   return M >= 8 && N >= 8 && fits(a_kc, M, lda) && fits(b_kc, N, ldb);
 }
 
-template <bool AKC, bool BKC, int EPI>
+template <int SH, bool AKC, bool BKC, int EPI>
 hipError_t launch_sched(int M, int N, int K, const void* A, int lda, const void* B, int ldb,
                         const Epi& e, hipStream_t st, int ksplit = 1) {
-  const int tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  hipLaunchKernelGGL((gemm_bf16_sched_kernel<AKC, BKC, EPI>), dim3(tiles * ksplit), dim3(256), 0, st,
+  constexpr int BM = Sched<SH>::BM, BN = Sched<SH>::BN;
+  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_bf16_sched_kernel<SH, AKC, BKC, EPI>), dim3(tiles * ksplit), dim3(256), 0, st,
                      M, N, K, (const bf16_t*)A, lda, (const bf16_t*)B, ldb, e, ksplit);
   return hipGetLastError();
 }
@@ -1075,7 +1133,7 @@ PairPlan pair_plan(int M0, int N0, int K0, int lda0, int ldb0, int M1, int N1, i
   // one product alone, on the tiles plan() gives it (k-tiles counted 32 deep whatever the kernel)
   auto alone = [&](const Plan& pl, int M, int N, int K) {
     const int bm = pl.tile == T128x128 ? 128 : 256;
-    const int bn = pl.tile == T256x256 || pl.tile == TSCHED ? 256 : pl.tile == T256x192 ? 192 : 128;
+    const int bn = pl.tile == T256x256 || pl.tile == TSCHED ? 256 : pl.tile == T256x192 || pl.tile == TSCHED192 ? 192 : 128;
     const int per = pl.tile == T128x128 ? 2 : 1;
     return waves(tiles(M, N, bm, bn) * pl.splits, per) * (K / pl.splits / SBK + 32) + (pl.splits > 1 ? 16 : 0);
   };
@@ -1111,13 +1169,21 @@ template <bool AKC, bool BKC, int EPI>
 hipError_t launch_bf16(int M, int N, int K, const void* A, int lda, const void* B, int ldb,
                        const Epi& e, hipStream_t st) {
   const Plan pl = plan(M, N, K, AKC, BKC, EPI, e.ws != nullptr, EPI == EPI_STORE && e.resid != nullptr);
+  if (pl.tile == TSCHED192) {
+    if constexpr (AKC && BKC) {
+      if (sched_ok(M, N, K, AKC, lda, BKC, ldb, 1))
+        return launch_sched<SH192, AKC, BKC, EPI>(M, N, K, A, lda, B, ldb, e, st);
+      if constexpr (EPI == EPI_STORE) return launch_cfg<256, 192, 4, 2, 1, AKC, BKC, EPI>(M, N, K, A, lda, B, ldb, e, st);
+    }
+    return launch_cfg<256, 256, 2, 4, 1, AKC, BKC, EPI>(M, N, K, A, lda, B, ldb, e, st);
+  }
   if (pl.tile == TSCHED) {
     // operands past the 32-bit offsets: the 2x4-wavefront kernel on the same tiles
     const bool ok = sched_ok(M, N, K, AKC, lda, BKC, ldb, pl.splits);
     if constexpr (!AKC && !BKC && EPI == EPI_STORE) {
       if (pl.splits > 1) {
         const hipError_t r =
-            ok ? launch_sched<AKC, BKC, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, e, st, pl.splits)
+            ok ? launch_sched<SH256, AKC, BKC, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, e, st, pl.splits)
                : launch_cfg<256, 256, 2, 4, 1, AKC, BKC, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, e, st,
                                                                        pl.splits);
         if (r != hipSuccess) return r;
@@ -1127,8 +1193,22 @@ hipError_t launch_bf16(int M, int N, int K, const void* A, int lda, const void* 
         return hipGetLastError();
       }
     }
-    if (pl.splits > 1) return hipErrorInvalidValue;  // only weight gradients split on these tiles
-    return ok ? launch_sched<AKC, BKC, EPI>(M, N, K, A, lda, B, ldb, e, st)
+    if (pl.splits > 1) {
+      // token-major plain stores: partial tiles, then the split epilogue pass
+      if constexpr (AKC && EPI == EPI_STORE) {
+        const hipError_t r =
+            ok ? launch_sched<SH256, AKC, BKC, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, e, st, pl.splits)
+               : launch_cfg<256, 256, 2, 4, 1, AKC, BKC, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, e, st,
+                                                                       pl.splits);
+        if (r != hipSuccess) return r;
+        const unsigned tiles = (unsigned)(((M + 63) / 64) * ((N + 127) / 128));
+        hipLaunchKernelGGL((splitk_epi_kernel<64, 128, 256, EPI>), dim3(tiles), dim3(256), 0, st, M, N,
+                           pl.splits, (const float*)e.ws, e);
+        return hipGetLastError();
+      }
+      return hipErrorInvalidValue;
+    }
+    return ok ? launch_sched<SH256, AKC, BKC, EPI>(M, N, K, A, lda, B, ldb, e, st)
               : launch_cfg<256, 256, 2, 4, 1, AKC, BKC, EPI>(M, N, K, A, lda, B, ldb, e, st);
   }
   if (pl.splits > 1) {
@@ -1173,7 +1253,8 @@ int gemm_tile_n(int M, int N, int K, bool a_kc, bool b_kc, int kind) {
   switch (plan(M, N, K, a_kc, b_kc, kind, false).tile) {
     case T256x256:
     case TSCHED: return 256;
-    case T256x192: return 192;
+    case T256x192:
+    case TSCHED192: return 192;
     default: return 128;
   }
 }
