@@ -8,8 +8,11 @@
 // instead of re-reading the logits; the three reductions are the same.
 // The backward is shard-local: dz = (exp(z - M)/S - onehot) * dloss.
 //
-// One 256-thread workgroup per token row; 16-byte vector loads when the
-// shard width is a multiple of 8 (a scalar loop covers any width).
+// One wavefront per token row, 4 rows per workgroup; 16-byte vector loads
+// when the shard width is a multiple of 8 (a scalar loop covers any width).
+// Each lane first requests kUnroll chunks of its row (unconditional loads,
+// clamped to the row), then reduces them; the row's statistics merge with
+// wavefront shuffles only.
 #include "common.h"
 #include "kernels.h"
 
@@ -17,6 +20,7 @@ namespace mtb {
 namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kLog2e = 1.4426950408889634f;
 
 MTB_DEV void ms_merge(float& m, float& s, float m2, float s2) {
   const float M = fmaxf(m, m2);
@@ -25,57 +29,97 @@ MTB_DEV void ms_merge(float& m, float& s, float m2, float s2) {
   m = M;
 }
 
-// block-wide merge of (m, s); result valid in thread 0
-MTB_DEV void block_ms(float& m, float& s) {
-  __shared__ float sm[4], ss[4];
+constexpr int kUnroll = 8;   // 8-element chunks a thread has in flight
+
+// 8 elements as loaded (bf16: one 16-byte word; fp32: two), unpacked later
+template <typename T> struct Raw8;
+// (loads with the nontemporal hint: the logits are streamed once per pass)
+template <> struct Raw8<bf16_t> {
+  u32x4 q;
+  MTB_DEV void load(const bf16_t* p) { q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)); }
+  MTB_DEV void get(float (&v)[8]) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[2 * i] = lo_f(q[i]); v[2 * i + 1] = hi_f(q[i]); }
+  }
+};
+template <> struct Raw8<float> {
+  f32x4 a, b;
+  MTB_DEV void load(const float* p) {
+    a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4));
+  }
+  MTB_DEV void get(float (&v)[8]) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
+  }
+};
+
+// wavefront-wide merge of (m, s) (every lane ends with the result)
+MTB_DEV void wave_ms(float& m, float& s) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
     ms_merge(m, s, m2, s2);
   }
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) { sm[w] = m; ss[w] = s; }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int i = 1; i < 4; ++i) ms_merge(m, s, sm[i], ss[i]);
-  }
 }
 
+// One wavefront per token row (4 rows per workgroup): no block-wide
+// reduction, and the target logit is requested before the row's chunks.
 template <typename T, bool VEC>
 __global__ __launch_bounds__(256) void xent_partial_kernel(int64_t n, int64_t v, int64_t v0,
                                                            const T* __restrict__ z,
                                                            const int64_t* __restrict__ tgt,
                                                            float* __restrict__ stats,
                                                            float* __restrict__ mloc) {
-  const int64_t row = blockIdx.x;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= n) return;
   const T* zr = z + row * v;
+  const int64_t lt = tgt[row] - v0;
+  const float t = (lt >= 0 && lt < v) ? ld_f(zr + lt) : 0.f;
   float m = kNegInf, s = 0.f;
   if (VEC) {
-    for (int64_t c = threadIdx.x; c < v / 8; c += 256) {
-      float x[8];
-      ld8(zr + c * 8, x);
-      float cm = x[0];
+    const int64_t nch = v / 8;
+    for (int64_t base = lane; base < nch; base += 64 * kUnroll) {
+      Raw8<T> raw[kUnroll];
 #pragma unroll
-      for (int e = 1; e < 8; ++e) cm = fmaxf(cm, x[e]);
+      for (int u = 0; u < kUnroll; ++u) raw[u].load(zr + min(base + (int64_t)u * 64, nch - 1) * 8);
+      float x[kUnroll][8];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) raw[u].get(x[u]);
+      // the arithmetic is most of the pass's time: exp(x - M) as
+      // exp2(x log2 e - M log2 e), one fma + one v_exp per logit; a batch
+      // wholly inside the row runs without per-chunk guards
+      const bool whole = base + (int64_t)(kUnroll - 1) * 64 < nch;
+      float cm = kNegInf;
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+        if (whole || base + (int64_t)u * 64 < nch) {
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) cm = fmaxf(cm, fmaxf(x[u][e], x[u][e + 1]));
+        }
       const float M = fmaxf(m, cm);
+      const float Ml = M * kLog2e;
       float acc = (m == kNegInf) ? 0.f : s * exp_fast(m - M);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc += exp_fast(x[e] - M);
+      for (int u = 0; u < kUnroll; ++u)
+        if (whole || base + (int64_t)u * 64 < nch) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc += __builtin_amdgcn_exp2f(fmaf(x[u][e], kLog2e, -Ml));
+        }
       m = M;
       s = acc;
     }
   } else {
-    for (int64_t j = threadIdx.x; j < v; j += 256) {
+    for (int64_t j = lane; j < v; j += 64) {
       const float x = ld_f(zr + j);
       const float M = fmaxf(m, x);
       s = ((m == kNegInf) ? 0.f : s * exp_fast(m - M)) + exp_fast(x - M);
       m = M;
     }
   }
-  block_ms(m, s);
-  if (threadIdx.x == 0) {
-    const int64_t lt = tgt[row] - v0;
-    const float t = (lt >= 0 && lt < v) ? ld_f(zr + lt) : 0.f;
+  wave_ms(m, s);
+  if (lane == 0) {
     stats[row] = m;
     stats[n + row] = s;
     stats[2 * n + row] = t;
@@ -118,27 +162,40 @@ __global__ __launch_bounds__(256) void xent_finish_kernel(int64_t n, int64_t v, 
                                                           float* __restrict__ loss,
                                                           const float* __restrict__ dloss,
                                                           T* __restrict__ dz) {
-  const int64_t row = blockIdx.x;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= n) return;
   const float M = stats[row], S = stats[n + row];
-  if (loss && threadIdx.x == 0) loss[row] = __logf(S) + M - stats[2 * n + row];
+  if (loss && lane == 0) loss[row] = __logf(S) + M - stats[2 * n + row];
   if (!dz) return;
-  const float sc = dloss[row] / S;
+  const float dl = dloss[row];
+  const float sc = dl / S, Ml = M * kLog2e;
   const int64_t lt = tgt[row] - v0;
   const T* zr = z + row * v;
   T* dr = dz + row * v;
   if (VEC) {
-    for (int64_t c = threadIdx.x; c < v / 8; c += 256) {
-      float x[8];
-      ld8(zr + c * 8, x);
+    const int64_t nch = v / 8;
+    for (int64_t base = lane; base < nch; base += 64 * kUnroll) {
+      Raw8<T> raw[kUnroll];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = exp_fast(x[e] - M) * sc;
-      if (lt >= c * 8 && lt < c * 8 + 8) x[lt - c * 8] -= dloss[row];
-      st8(dr + c * 8, x);
+      for (int u = 0; u < kUnroll; ++u) raw[u].load(zr + min(base + (int64_t)u * 64, nch - 1) * 8);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t c = base + (int64_t)u * 64;
+        if (c < nch) {
+          float x[8];
+          raw[u].get(x);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = __builtin_amdgcn_exp2f(fmaf(x[e], kLog2e, -Ml)) * sc;
+          if (lt >= c * 8 && lt < c * 8 + 8) x[lt - c * 8] -= dl;
+          st8(dr + c * 8, x);
+        }
+      }
     }
   } else {
-    for (int64_t j = threadIdx.x; j < v; j += 256) {
+    for (int64_t j = lane; j < v; j += 64) {
       float x = exp_fast(ld_f(zr + j) - M) * sc;
-      if (j == lt) x -= dloss[row];
+      if (j == lt) x -= dl;
       st_f(dr + j, x);
     }
   }
@@ -177,24 +234,26 @@ __global__ __launch_bounds__(256) void lmhead_combine_kernel(int64_t n, int tile
 template <typename T>
 hipError_t partial_t(int64_t n, int64_t v, int64_t v0, const void* z, const int64_t* tgt,
                      float* stats, float* mloc, hipStream_t st) {
+  const dim3 grid((unsigned)((n + 3) / 4));
   if (v % 8 == 0)
-    hipLaunchKernelGGL((xent_partial_kernel<T, true>), dim3((unsigned)n), dim3(256), 0, st, n, v,
-                       v0, (const T*)z, tgt, stats, mloc);
+    hipLaunchKernelGGL((xent_partial_kernel<T, true>), grid, dim3(256), 0, st, n, v, v0, (const T*)z,
+                       tgt, stats, mloc);
   else
-    hipLaunchKernelGGL((xent_partial_kernel<T, false>), dim3((unsigned)n), dim3(256), 0, st, n, v,
-                       v0, (const T*)z, tgt, stats, mloc);
+    hipLaunchKernelGGL((xent_partial_kernel<T, false>), grid, dim3(256), 0, st, n, v, v0, (const T*)z,
+                       tgt, stats, mloc);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t finish_t(int64_t n, int64_t v, int64_t v0, const void* z, const int64_t* tgt,
                     const float* stats, float* loss, const float* dloss, void* dz, hipStream_t st) {
+  const dim3 grid((unsigned)((n + 3) / 4));
   if (v % 8 == 0)
-    hipLaunchKernelGGL((xent_finish_kernel<T, true>), dim3((unsigned)n), dim3(dz ? 256 : 64), 0, st,
-                       n, v, v0, (const T*)z, tgt, stats, loss, dloss, (T*)dz);
+    hipLaunchKernelGGL((xent_finish_kernel<T, true>), grid, dim3(256), 0, st, n, v, v0, (const T*)z, tgt,
+                       stats, loss, dloss, (T*)dz);
   else
-    hipLaunchKernelGGL((xent_finish_kernel<T, false>), dim3((unsigned)n), dim3(dz ? 256 : 64), 0,
-                       st, n, v, v0, (const T*)z, tgt, stats, loss, dloss, (T*)dz);
+    hipLaunchKernelGGL((xent_finish_kernel<T, false>), grid, dim3(256), 0, st, n, v, v0, (const T*)z, tgt,
+                       stats, loss, dloss, (T*)dz);
   return hipGetLastError();
 }
 
