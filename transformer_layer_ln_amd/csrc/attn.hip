@@ -44,8 +44,10 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
+// forward: how far (log2 units) a row's scores may exceed the reference max
+// before it is moved
+constexpr float kLazy = 8.0f;
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // linear workgroup id -> (tile along the sequence, batch*head). Causal
 // workloads order the tiles by their work. With two workgroups per CU
@@ -104,22 +106,57 @@ MTB_DEV int tswz(int r) {
 template <int D>
 MTB_DEV int toff(int r, int c) { return r * D + ((c ^ tswz<D>(r)) << 3); }
 
+// Direct-to-LDS loads: lane l fills LDS bytes [BYTES l, BYTES (l + 1)) from
+// `lds` (wavefront-uniform) with the bytes at sbase + voff (sbase uniform).
+// They are issued from inline assembly: a copy the compiler sees is an LDS
+// store in flight, and it then waits for the copy to land (vmcnt(0)) before
+// the next LDS read of any address, so the copy of the next tile would not
+// overlap the work on the current one. Every kernel here waits for its
+// copies itself (vmcnt(0) and a barrier) before it reads the stage they
+// fill, and the copies write only a stage no wavefront reads until then.
+// Fragments loaded from global memory ahead of a loop are settled (settle())
+// before it, so that no compiler-placed wait inside the loop counts these
+// copies. The address registers are read at issue. M0 is written before
+// every use; no compiled code around these keeps a value in M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+MTB_DEV void lds_load16(uint32_t voff, const void* sbase, const void* lds) {
+  const uint32_t a = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               : : "v"(voff), "s"(sbase), "s"(a) : "memory", "m0");
+}
+MTB_DEV void lds_load4(uint32_t voff, const void* sbase, const void* lds) {
+  const uint32_t a = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               : : "v"(voff), "s"(sbase), "s"(a) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // Direct-to-LDS copy of a ROWS x D tile (row pitch ld elements) into the
 // layout above, by the 4 wavefronts of the workgroup: each load instruction
 // fills one contiguous KB of LDS (lane l -> bytes 16l .. 16l + 15), so a lane
-// fetches the global chunk that belongs at its LDS position.
+// fetches the global chunk that belongs at its LDS position. The per-lane
+// byte offsets from the tile's first row are fixed for a given pitch and
+// computed once; each copy passes only the tile's (uniform) first row.
 template <int ROWS, int D>
-MTB_DEV void dma_rows(bf16_t* lds, const bf16_t* __restrict__ g, size_t ld, int wave, int lane) {
-  constexpr int CH = D / 8, RPB = 64 / CH, BLK = ROWS / RPB, PERW = BLK / 4;
+struct RowCopy {
+  static constexpr int CH = D / 8, RPB = 64 / CH, BLK = ROWS / RPB, PERW = BLK / 4;
   static_assert(BLK % 4 == 0, "tile must split over 4 wavefronts");
+  uint32_t off[PERW];
+  int wave;
+  MTB_DEV RowCopy(int ld, int wave_, int lane) : wave(wave_) {
 #pragma unroll
-  for (int i = 0; i < PERW; ++i) {
-    const int b = wave * PERW + i;
-    const int r = b * RPB + lane / CH, c = (lane % CH) ^ tswz<D>(r);
-    __builtin_amdgcn_global_load_lds((const void*)(g + (size_t)r * ld + c * 8), (lds_ptr_t)(lds + b * 512), 16,
-                                     0, 0);
+    for (int i = 0; i < PERW; ++i) {
+      const int b = wave * PERW + i;
+      const int r = b * RPB + lane / CH, c = (lane % CH) ^ tswz<D>(r);
+      off[i] = ((uint32_t)r * (uint32_t)ld + (uint32_t)c * 8u) * 2u;
+    }
   }
-}
+  MTB_DEV void operator()(bf16_t* lds, const bf16_t* g) const {
+#pragma unroll
+    for (int i = 0; i < PERW; ++i) lds_load16(off[i], g, lds + (wave * PERW + i) * 512);
+  }
+};
 
 // MFMA fragment of a tile read directly: rows r (the lane's row), 8 values of chunk c
 template <int D>
@@ -150,6 +187,16 @@ MTB_DEV bf16x8 frag_t(const bf16_t* t, int kk, int m0, int lane) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// Pins fragments loaded from global memory before a loop: their loads
+// complete here, not at their first use inside the loop, where the wait for
+// them would also count the tile copies in flight (which the compiler does
+// not see) and stall on those.
+template <int N>
+MTB_DEV void settle(bf16x8 (&f)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(f[i]));
+}
+
 // Forward. Workgroup = 64 queries of one (batch, q head); wavefront w takes
 // query half w & 1 and key half w >> 1 of every 64-key tile, keeps its own
 // online-softmax state, and the two key halves are merged at the end.
@@ -177,6 +224,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(int S, int nq, int nkv
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qp + kk * 16);
   }
+  settle(qf);
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i)
@@ -187,10 +235,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(int S, int nq, int nkv
   const bf16_t* kbase = qkv + tok0 * ldq + (size_t)(nq + hk) * D;
   const bf16_t* vbase = qkv + tok0 * ldq + (size_t)(nq + nkv + hk) * D;
   const int ntk = CAUSAL ? qb + 1 : ntile;
+  const RowCopy<64, D> copy(ldq, wave, lane);
   auto fetch = [&](int t) {
     bf16_t* st = smem + (t & 1) * 128 * D;
-    dma_rows<64, D>(st, kbase + (size_t)t * 64 * ldq, ldq, wave, lane);
-    dma_rows<64, D>(st + 64 * D, vbase + (size_t)t * 64 * ldq, ldq, wave, lane);
+    copy(st, kbase + (size_t)t * 64 * ldq);
+    copy(st + 64 * D, vbase + (size_t)t * 64 * ldq);
   };
   fetch(0);
   __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
@@ -210,14 +259,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(int S, int nq, int nkv
         vt[df][0] = frag_t<D>(sV, 2 * kh, 32 * df, lane);
         vt[df][1] = frag_t<D>(sV, 2 * kh + 1, 32 * df, lane);
       }
-      f32x16 sa, sb;
+      f32x16 sacc;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) { sa[r] = 0.f; sb[r] = 0.f; }
+      for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        if (kk & 1) sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], sb, 0, 0, 0);
-        else sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], sa, 0, 0, 0);
-      }
+      for (int kk = 0; kk < D / 16; ++kk) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], sacc, 0, 0, 0);
       // issue order: the K reads, then each S^T MFMA followed by one of the
       // V^T transpose reads
       __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 0);
@@ -229,7 +275,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(int S, int nq, int nkv
       // s[j]: key ks + 8(j>>2) + 4lg + (j&3), query qi
       float s[16];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) s[j] = sa[j] + sb[j];
+      for (int j = 0; j < 16; ++j) s[j] = sacc[j];
       if (CAUSAL && ks + 31 > q0) {
 #pragma unroll
         for (int j = 0; j < 16; ++j)
@@ -239,9 +285,23 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(int S, int nq, int nkv
 #pragma unroll
       for (int j = 1; j < 16; ++j) mx = fmaxf(mx, s[j]);
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mnew = fmaxf(m_i, mx * sl2);
-      const float mref = mnew == kNegInf ? 0.f : mnew;
-      const float alpha = exp2_fast(m_i - mref);
+      const float mt = mx * sl2;  // the tile's row max, log2 units
+      // Lazy reference max: m_i moves (and O^T and l_i are rescaled) only when
+      // some row's tile max exceeds it by more than kLazy; otherwise the
+      // probabilities are taken against the old m_i and stay below 2^kLazy.
+      // O^T and l_i always share m_i, so O = O^T / l is unchanged.
+      float alpha = 1.0f;
+      if (__any(mt > m_i + kLazy)) {
+        if (mt > m_i) {
+          alpha = exp2_fast(m_i - mt);  // 0 while m_i is still -inf
+          m_i = mt;
+        }
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+      }
+      const float mref = m_i == kNegInf ? 0.f : m_i;  // a row with no key seen yet: every p is 0
       float ls = 0.f;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
@@ -249,7 +309,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(int S, int nq, int nkv
         ls += s[j];
       }
       l_i = l_i * alpha + ls;
-      m_i = mnew;
       if constexpr (DROP) {
         const uint64_t row = ((uint64_t)bh * S + qi) * S;
 #pragma unroll
@@ -259,12 +318,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(int S, int nq, int nkv
 #pragma unroll
           for (int r = 0; r < 4; ++r) s[4 * i + r] *= km[r];
         }
-      }
-      if (__any(alpha != 1.0f)) {
-#pragma unroll
-        for (int i = 0; i < D / 32; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
       }
       bf16x8 p0, p1;
       pack_half(s, p0, p1);
@@ -375,13 +428,15 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(
   const size_t tok0 = (size_t)b * S;
   const int ldo = nq * D;
 
-  dma_rows<64, D>(sK, qkv + (tok0 + kb * 64) * ldq + (size_t)(nq + hk) * D, ldq, wave, lane);
+  const RowCopy<64, D> copy_q(ldq, wave, lane), copy_o(nq * D, wave, lane);
+  copy_q(sK, qkv + (tok0 + kb * 64) * ldq + (size_t)(nq + hk) * D);
   bf16x8 vf[D / 16];
   {
     const bf16_t* vp = qkv + (tok0 + key) * ldq + (size_t)(nq + nkv + hk) * D + 8 * lg;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) vf[kk] = *reinterpret_cast<const bf16x8*>(vp + kk * 16);
   }
+  settle(vf);
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i)
@@ -397,12 +452,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(
 
   for (int qt = CAUSAL ? kb : 0; qt < ntile; ++qt) {
     const int qt0 = qt * 64;
-    dma_rows<64, D>(sQ, qbase + (size_t)qt0 * ldq, ldq, wave, lane);
-    dma_rows<64, D>(sdO, dobase + (size_t)qt0 * ldo, ldo, wave, lane);
+    copy_q(sQ, qbase + (size_t)qt0 * ldq);
+    copy_o(sdO, dobase + (size_t)qt0 * ldo);
     if (wave == 0) {
-      __builtin_amdgcn_global_load_lds((const void*)(lrow + qt0 + lane), (lds_ptr_t)(smem + 3 * TILE), 4, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(drow + qt0 + lane), (lds_ptr_t)(smem + 3 * TILE + 128), 4,
-                                       0, 0);
+      lds_load4(4u * lane, lrow + qt0, smem + 3 * TILE);
+      lds_load4(4u * lane, drow + qt0, smem + 3 * TILE + 128);
     }
     __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
     __syncthreads();
@@ -566,10 +620,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
 
   const bf16_t* kbase = qkv + tok0 * ldq + (size_t)(nq + hk) * D;
   const bf16_t* vbase = qkv + tok0 * ldq + (size_t)(nq + nkv + hk) * D;
+  const RowCopy<64, D> copy(ldq, wave, lane);
   auto fetch = [&](int t) {
     bf16_t* st = smem + (t & 1) * STAGE;
-    dma_rows<64, D>(st, kbase + (size_t)t * 64 * ldq, ldq, wave, lane);
-    dma_rows<64, D>(st + TILE, vbase + (size_t)t * 64 * ldq, ldq, wave, lane);
+    copy(st, kbase + (size_t)t * 64 * ldq);
+    copy(st + TILE, vbase + (size_t)t * 64 * ldq);
   };
   fetch(0);
 
@@ -583,8 +638,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
       of[kk] = *reinterpret_cast<const bf16x8*>(gp + kk * 16);
     }
   }
-  const float Lq = lse[((size_t)b * nq + hq) * S + qi] * kLog2e;
-  const float Dq = Dbuf[((size_t)b * nq + hq) * S + qi];
+  settle(qf);
+  settle(of);
+  float Lq = lse[((size_t)b * nq + hq) * S + qi] * kLog2e;
+  float Dq = Dbuf[((size_t)b * nq + hq) * S + qi];
+  asm volatile("" : "+v"(Lq), "+v"(Dq));
   f32x16 dq[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i)
