@@ -6,19 +6,24 @@ that csrc/gen_gemm_loop.py writes to csrc/gemm_loop.inc).
    wavefronts of a block run the same stream, so what holds for one holds for
    all) over several contraction lengths, per operand layout, checks:
    - every MFMA multiplies an A and a B fragment of the same k-tile and
-     16-deep step, both landed (their LDS reads retired by an s_waitcnt), and
-     every accumulator sums each (k-tile, step) exactly once, in order;
+     16-deep step, both landed (their LDS reads, or their direct global loads,
+     retired by an s_waitcnt), and every accumulator sums each (k-tile, step)
+     exactly once, in order;
    - an LDS read sees a stage only when the stage's last copy completed on
      every lane (vmcnt) before a barrier, and reads the fragment its
      destination registers are meant for;
    - a copy into a stage is issued only when every read of the stage's
      previous tile retired before a barrier (no wavefront still reads it);
-   - the copies fetch k-tiles 0, 1, ..., KT-1 in order and then re-fetch the
-     last one, for any KT (the body is entered at slot -KT mod SLOTS); M0 is
-     written, with a wait state, before every copy;
+   - the copies (and the direct loads, both steps of each) fetch k-tiles 0,
+     1, ..., KT-1 in order and then re-fetch the last one, for any KT (the
+     body is entered at slot -KT mod SLOTS); M0 is written, with a wait
+     state, before every copy; direct loads write only the direct operand's
+     fragment registers;
    - wait counts fit their fields, LDS read offsets fit 16 bits, copy
      destinations stay inside their operand's part of a stage.
-   This for every tile shape the generator builds (256 x 256, 256 x 192).
+   This for every tile shape the generator builds (256 x 256, 256 x 192),
+   with the direct operand each layout takes and with both operands through
+   LDS.
 """
 import importlib.util
 import os
@@ -38,7 +43,6 @@ def _gen():
 
 
 GEN = _gen()
-STAGE = GEN.STAGE_BYTES
 
 
 def test_committed_include_matches_generator():
@@ -51,10 +55,12 @@ class ScheduleError(AssertionError):
 
 
 class Wave:
-    """Symbolic state of one wavefront running the loop of shape `sh` for KT k-tiles."""
+    """Symbolic state of one wavefront running the loop of shape `sh` (the
+    variant for these layouts, with its direct operand) for KT k-tiles."""
 
-    def __init__(self, layouts, KT, sh=GEN.S256):
+    def __init__(self, layouts, KT, sh=GEN.S256, direct=None):
         self.lay = layouts                 # {"a": "kc"|"mn", "b": ...}
+        sh = GEN.shape_for(sh, layouts["a"], layouts["b"], direct)
         self.sh = sh
         self.KT = KT
         self.first = -KT % sh.slots       # the body slot k-tile 0 runs in
@@ -62,13 +68,16 @@ class Wave:
         self.rem = KT - 1
         self.nq = {"A": sh.qa, "B": sh.qb}
         keys = [(x, q) for x in "AB" for q in range(self.nq[x])]
-        self.src = {k: 0 for k in keys}   # k-tile the copy offset points at
+        if sh.direct:
+            x = sh.direct.upper()
+            keys += [(x, i) for i in range(sh.nfrag("AB".index(x)))]
+        self.src = {k: 0 for k in keys}   # k-tile the copy / direct offset points at
         self.copied = {k: [] for k in keys}
         self.t = {"ta": None, "tb": None}
         self.scc = None
         self.m0 = None
         self.lgkm = []       # outstanding LDS reads, oldest first: (regs, content, stage)
-        self.vm = []         # outstanding copies: (stage, x, q)
+        self.vm = []         # outstanding copies (stage, x, q) and direct loads ("direct", regs)
         self.regs = {}       # first VGPR of a 2-register half -> (content, landed)
         self.epoch = 0       # barriers passed
         S = sh.stages
@@ -93,14 +102,20 @@ class Wave:
 
     def retire_vm(self, n):
         while len(self.vm) > n:
-            stage, x, q = self.vm.pop(0)
-            self.blocks[stage][(x, q)][1] = True
+            item = self.vm.pop(0)
+            if item[0] == "direct":
+                for r in item[1]:
+                    content, _ = self.regs[r]
+                    self.regs[r] = (content, True)
+            else:
+                stage, x, q = item
+                self.blocks[stage][(x, q)][1] = True
 
     def barrier(self):
         self.epoch += 1
         for s, blk in self.blocks.items():
             tiles = {t for t, _ in blk.values()}
-            if len(blk) == self.sh.cpt and len(tiles) == 1 and all(c for _, c in blk.values()):
+            if len(blk) == self.sh.ncopy and len(tiles) == 1 and all(c for _, c in blk.values()):
                 self.visible[s] = tiles.pop()
 
     # --- instructions
@@ -138,10 +153,11 @@ class Wave:
         if tile is None:
             self.fail(f"read of stage {stage} before its copy completed behind a barrier")
         r0 = regs[0]
-        buf = (r0 - sh.frag_lo) // sh.per_buf
-        exp = sh.freg(buf, kk, op, idx)
-        if r0 != exp or r0 < sh.frag_lo or r0 + 4 > sh.frag_hi:
-            self.fail(f"fragment (kk {kk}, op {x}, {idx}) read into v{r0}, expected v{exp}")
+        if sh.is_direct(op):
+            self.fail(f"LDS read of the direct operand {x}")
+        exp = [sh.freg(b, kk, op, idx) for b in range(2)]
+        if r0 not in exp or r0 < sh.frag_lo or r0 + 4 > sh.frag_hi:
+            self.fail(f"fragment (kk {kk}, op {x}, {idx}) read into v{r0}, expected one of {exp}")
         content = (tile, kk, op, idx)
         dest = regs if half is None else [reg]
         for r in dest:
@@ -170,12 +186,30 @@ class Wave:
         self.blocks[stage][(x, q)] = [tile, False]
         self.vm.append((stage, x, q))
 
+    def direct_load(self, reg, x, i, off):
+        sh = self.sh
+        op = "AB".index(x)
+        if not sh.is_direct(op) or i >= sh.nfrag(op) or off not in (0, 32):
+            self.fail(f"direct load of {x}{i} offset {off}: not a direct fragment")
+        kk = off // 32
+        lo = sh.freg(0, 0, op, 0)
+        hi = sh.freg(sh.nbuf[op] - 1, 1, op, sh.nfrag(op) - 1) + 4
+        if reg < lo or reg + 4 > hi or (reg - sh.freg(0, kk, op, i)) % (8 * sh.nfrag(op)):
+            self.fail(f"direct load of {x}{i} step {kk} into v{reg}: not one of its register sets")
+        tile = self.src[(x, i)]
+        self.copied[(x, i)].append(tile)
+        content = (tile, kk, op, i)
+        dest = [reg, reg + 2]
+        for r in dest:
+            self.regs[r] = (content, False)
+        self.vm.append(("direct", dest))
+
     def mfma(self, i, j, rb, ra):
         ca, cb = [], []
         for r, out in ((ra, ca), (rb, cb)):
             for h in (r, r + 2):
                 if h not in self.regs or not self.regs[h][1]:
-                    self.fail(f"MFMA c{i}{j} reads v{h} before its LDS read retired")
+                    self.fail(f"MFMA c{i}{j} reads v{h} before its LDS read or direct load retired")
                 out.append(self.regs[h][0])
         if ca[0] != ca[1] or cb[0] != cb[1]:
             self.fail(f"MFMA c{i}{j}: fragment halves from different reads {ca} {cb}")
@@ -234,6 +268,12 @@ class Wave:
         elif op == "global_load_lds_dwordx4":
             x, q = re.match(r"%\[vo([AB])(\d)\]", f[1]).groups()
             self.copy(x, int(q))
+        elif op == "global_load_dwordx4":
+            reg = int(re.match(r"v\[(\d+):", f[1]).group(1))
+            x, i = re.match(r"%\[vo([AB])(\d)\]", f[2]).groups()
+            if f[3] != f"%[sb{x}]":
+                self.fail("direct load from another operand's base: " + line)
+            self.direct_load(reg, x, int(i), int(f[4].split(":")[1]))
         elif op == "s_cmp_gt_i32":
             self.scc = (self.rem if f[1] == "%[rem]" else self.iters) > 0
         elif op == "s_cmp_eq_u32" and f[1] == "%[first]":
@@ -260,13 +300,15 @@ class Wave:
 def _check_run(la, lb, KT, sh=GEN.S256, **variant):
     lines = GEN.loop(la, lb, sh=sh, **variant)
     assert lines[0] == "s_nop 4" and lines[-3:] == ["s_nop 7"] * 3   # accumulator hazards
-    w = Wave({"a": la, "b": lb}, KT, sh)
+    w = Wave({"a": la, "b": lb}, KT, sh, variant.get("direct"))
     w.run(lines)
     assert not w.lgkm and not w.vm, "memory operations outstanding at the end"
     want = [(t, kk) for t in range(KT) for kk in (0, 1)]
     for ij, got in w.acc.items():
         assert got == want, f"{sh.name} {variant} KT {KT} accumulator c{ij[0]}{ij[1]}"
     for key, tiles in w.copied.items():
+        if w.sh.direct and key[0] == w.sh.direct.upper():
+            tiles = tiles[::2]     # each tile's two steps load the same k-tile
         n = len(tiles)
         assert tiles == list(range(KT)) + [KT - 1] * (n - KT), f"copy sequence of {key}: {tiles}"
     return w
@@ -276,6 +318,14 @@ def _check_run(la, lb, KT, sh=GEN.S256, **variant):
 @pytest.mark.parametrize("KT", [1, 2, 3, 4, 5, 6, 7, 8, 13, 32, 501])
 def test_schedule_symbolic_execution(name, la, lb, KT):
     _check_run(la, lb, KT)
+
+
+@pytest.mark.parametrize("name,la,lb", GEN.LAYOUTS[:2])
+@pytest.mark.parametrize("KT", [1, 2, 3, 5, 8, 13])
+def test_schedule_with_direct_operand(name, la, lb, KT):
+    """The measurement variant that loads the k-contiguous operand straight
+    into registers obeys the same waits and k-tile order."""
+    _check_run(la, lb, KT, direct="auto")
 
 
 @pytest.mark.parametrize("shape", [s.name for s in GEN.SHAPES if s is not GEN.S256])
@@ -288,12 +338,17 @@ def test_other_shapes_symbolic_execution(shape, KT):
 
 
 def test_shapes_fit_their_registers_and_lds():
-    """Fragment registers inside the clobbered range, stages inside a CU's
-    160 KB of LDS, copy blocks whole."""
+    """Fragment registers inside the clobbered range (and at least 64 VGPRs
+    left to the compiled code around the loop), stages inside a CU's 160 KB
+    of LDS, copy blocks whole, wait counts inside their fields."""
     for sh in GEN.SHAPES:
-        assert sh.stages * sh.stage_bytes <= 160 * 1024, sh.name
-        assert sh.a_bytes % 4096 == 0 and sh.b_bytes % 4096 == 0, sh.name
-        assert sh.frag_lo >= 0 and sh.frag_hi <= 256
+        for name, la, lb in GEN.SHAPE_LAYOUTS[sh.name]:
+            for d in (None, "auto"):
+                v = GEN.shape_for(sh, la, lb, d)
+                assert v.stages * v.stage_bytes <= 160 * 1024, (sh.name, name)
+                assert v.a_bytes % 4096 == 0 and v.b_bytes % 4096 == 0, (sh.name, name)
+                assert 64 <= v.frag_lo and v.frag_hi <= 256, (sh.name, name, d)
+                assert v.cpt * (v.stages - 2) <= 63, (sh.name, name, d)
 
 
 @pytest.mark.parametrize("name,la,lb", GEN.LAYOUTS)
@@ -313,8 +368,23 @@ def test_symbolic_execution_catches_a_short_wait():
     lines = GEN.loop(la, lb)
     waits = [k for k, l in enumerate(lines) if l.startswith("s_waitcnt lgkmcnt")]
     bad = lines[:waits[2]] + lines[waits[2] + 1:]
-    with pytest.raises(ScheduleError, match="before its LDS read retired"):
+    with pytest.raises(ScheduleError, match="before its LDS read"):
         Wave({"a": la, "b": lb}, 8).run(bad)
+
+
+@pytest.mark.parametrize("name,la,lb", GEN.LAYOUTS[:2])
+def test_symbolic_execution_catches_a_short_direct_wait(name, la, lb):
+    """The checker itself: a body wait that lets one more tile of memory
+    operations stay in flight (the direct fragments of the tile about to run
+    would not have landed) must be reported."""
+    sh = GEN.shape_for(GEN.S256, la, lb, "auto")
+    lines = GEN.loop(la, lb, direct="auto")
+    body = lines.index("L%=_ktile:")
+    good = f"s_waitcnt vmcnt({sh.cpt * (sh.stages - 3)})"
+    bad = lines[:body] + [f"s_waitcnt vmcnt({sh.cpt * (sh.stages - 2)})" if l == good else l
+                          for l in lines[body:]]
+    with pytest.raises(ScheduleError):
+        Wave({"a": la, "b": lb}, 8, direct="auto").run(bad)
 
 
 def test_symbolic_execution_catches_an_early_copy():
@@ -328,3 +398,153 @@ def test_symbolic_execution_catches_an_early_copy():
     bad = lines[:k] + lines[k + 1:]
     with pytest.raises(ScheduleError):
         Wave({"a": la, "b": lb}, 8).run(bad)
+
+
+class Wave64(Wave):
+    """Symbolic state of one wavefront running the 64-deep loop (gen_gemm_loop.loop64)."""
+
+    def __init__(self, layouts, KT, sh=GEN.S256_64):
+        self.lay = layouts
+        self.sh = sh
+        self.KT = KT
+        self.first = -KT % sh.slots
+        self.iters = (KT + self.first) // sh.slots
+        self.rem = KT - 1
+        self.nq = {"A": sh.qa, "B": sh.qb}
+        keys = [(x, q) for x in "AB" for q in range(self.nq[x])]
+        self.src = {k: 0 for k in keys}
+        self.copied = {k: [] for k in keys}
+        self.t = {"ta": None, "tb": None}
+        self.scc = None
+        self.m0 = None
+        self.lgkm = []
+        self.vm = []
+        self.regs = {}
+        self.epoch = 0
+        S = sh.stages
+        self.visible = {s: None for s in range(S)}
+        self.blocks = {s: {} for s in range(S)}
+        self.reads_done = {s: [] for s in range(S)}
+        self.reads_open = {s: 0 for s in range(S)}
+        self.acc = {(i, j): [] for i in range(sh.fm) for j in range(sh.fn)}
+        self.prev = []
+
+    def barrier(self):
+        self.epoch += 1
+        for s, blk in self.blocks.items():
+            tiles = {t for t, _ in blk.values()}
+            if len(blk) == self.sh.cpt and len(tiles) == 1 and all(c for _, c in blk.values()):
+                self.visible[s] = tiles.pop()
+
+    def ds_read(self, kind, reg, base, off):
+        sh = self.sh
+        if off > 65535:
+            self.fail(f"LDS read offset {off} does not fit 16 bits")
+        x, n = base[0], int(base[1:])
+        op = "ab".index(x)
+        F = sh.nfrag(op)
+        if self.lay[x] == "kc":
+            if kind != "ds_read_b128":
+                self.fail("k-contiguous operand read with " + kind)
+            stage, step = n // sh.steps, n % sh.steps
+            idx, half = off // 4096, None
+            if off % 4096:
+                self.fail(f"read offset {off} is not a fragment start")
+            regs = [reg, reg + 2]
+        else:
+            if kind != "ds_read_b64_tr_b16":
+                self.fail("transposed operand read with " + kind)
+            rb = sh.rows(op) * 2
+            stage, idx = n // F, n % F
+            step, half = off // (16 * rb), (off % (16 * rb)) // (4 * rb)
+            if off % (4 * rb) or step >= sh.steps or half > 1:
+                self.fail(f"transpose read offset {off} is not a fragment half")
+            regs = [reg] if half == 0 else [reg - 2]
+        if stage >= sh.stages or idx >= F:
+            self.fail(f"read of stage {stage} fragment {idx}: outside the tile")
+        tile = self.visible[stage]
+        if tile is None:
+            self.fail(f"read of stage {stage} before its copy completed behind a barrier")
+        r0 = regs[0]
+        exp = [sh.freg(b, op, idx) for b in range(sh.nbuf)]
+        if r0 not in exp:
+            self.fail(f"fragment (step {step}, op {x}, {idx}) read into v{r0}, expected one of {exp}")
+        content = (tile, step, op, idx)
+        dest = regs if half is None else [reg]
+        for r in dest:
+            self.regs[r] = (content, False)
+        self.lgkm.append((dest, content, stage))
+        self.reads_open[stage] += 1
+
+
+def _check_run64(la, lb, KT, sh=GEN.S256_64):
+    """Symbolic run of loop64 (the shape's own read-ahead) for KT 64-deep tiles."""
+    lines = GEN.loop64(la, lb, sh=sh)
+    assert lines[0] == "s_nop 4" and lines[-3:] == ["s_nop 7"] * 3
+    w = Wave64({"a": la, "b": lb}, KT, sh)
+    w.run(lines)
+    assert not w.lgkm and not w.vm, "memory operations outstanding at the end"
+    want = [(t, s) for t in range(KT) for s in range(sh.steps)]
+    for ij, got in w.acc.items():
+        assert got == want, f"64-deep {sh.name} KT {KT} accumulator c{ij[0]}{ij[1]}"
+    for key, tiles in w.copied.items():
+        n = len(tiles)
+        assert tiles == list(range(KT)) + [KT - 1] * (n - KT), f"copy sequence of {key}: {tiles}"
+    return w
+
+
+@pytest.mark.parametrize("name,la,lb", GEN.LAYOUTS)
+@pytest.mark.parametrize("KT", [1, 2, 3, 4, 5, 8, 13, 64, 251])
+def test_schedule64_symbolic_execution(name, la, lb, KT):
+    """The 64-deep loop (KT 64-deep tiles) for every layout, 256 x 256."""
+    _check_run64(la, lb, KT)
+
+
+@pytest.mark.parametrize("KT", [1, 2, 3, 4, 7, 24])
+def test_schedule64_other_shapes(KT):
+    for sh in GEN.SHAPES64:
+        for name, la, lb in GEN.SHAPE_LAYOUTS[sh.name]:
+            _check_run64(la, lb, KT, sh)
+
+
+@pytest.mark.parametrize("ra", [1, 2])
+@pytest.mark.parametrize("name,la,lb", GEN.LAYOUTS)
+def test_schedule64_read_ahead_variants(ra, name, la, lb):
+    """Both read-ahead depths of the 64-deep loop (one step: two register
+    sets; two steps: four)."""
+    sh = GEN.Shape64("256", 4, 4, ra=ra)
+    for KT in (1, 2, 3, 6, 11):
+        _check_run64(la, lb, KT, sh)
+
+
+def test_shapes64_fit():
+    """Two 64-deep stages in a CU's LDS (no more than four 32-deep ones, the
+    epilogue's staging area), wait counts and read offsets in their fields."""
+    for sh in GEN.SHAPES64:
+        assert sh.stages * sh.stage_bytes <= 160 * 1024 and sh.frag_lo >= 64
+        assert sh.cpt <= 63
+        assert sh.read_offset("kc", 0, 3, sh.fm - 1) < 65536
+        assert sh.read_offset("mn", 1, 3, sh.fn - 1, 1) < 65536
+
+
+def test_schedule64_catches_a_missing_barrier():
+    """Dropping the barrier of step 3 (copies into a stage other wavefronts may
+    still read, reads of a stage whose copy has not landed everywhere) must be
+    reported."""
+    la, lb = "kc", "kc"
+    lines = GEN.loop64(la, lb)
+    k = lines.index("s_barrier", lines.index("L%=_ktile:"))
+    bad = lines[:k] + lines[k + 1:]
+    with pytest.raises(ScheduleError):
+        Wave64({"a": la, "b": lb}, 8).run(bad)
+
+
+def test_schedule64_catches_a_short_wait():
+    """A step wait that leaves the step's fragment reads in flight must be reported."""
+    la, lb = "kc", "mn"
+    lines = GEN.loop64(la, lb)
+    body = lines.index("L%=_ktile:")
+    k = next(i for i in range(body, len(lines)) if lines[i].startswith("s_waitcnt lgkmcnt"))
+    bad = lines[:k] + lines[k + 1:]
+    with pytest.raises(ScheduleError, match="before its LDS read"):
+        Wave64({"a": la, "b": lb}, 8).run(bad)

@@ -841,13 +841,13 @@ MTB_DEV void sched_tile(bf16_t* smem, int M, int N, int K, const bf16_t* __restr
     [fb0] "v"(fb[0]), [fb1] "v"(fb[1]), [fb2] "v"(fb[2]), [fb3] "v"(fb[3]),                        \
     [fb4] "v"(fb[NB > 4 ? 4 : 0]), [fb5] "v"(fb[NB > 5 ? 5 : 0]), [fb6] "v"(fb[NB > 6 ? 6 : 0]),   \
     [fb7] "v"(fb[NB > 7 ? 7 : 0])                                                                  \
-  : "memory", "m0", "scc", MTB_GEMM_LOOP_CLOBBERS
+  : "memory", "m0", "scc"
     if constexpr (AKC && BKC)
-      asm volatile(MTB_GEMM_LOOP_NT MTB_LOOP_OPERANDS);
+      asm volatile(MTB_GEMM_LOOP_NT MTB_LOOP_OPERANDS, MTB_GEMM_LOOP_CLOBBERS_NT);
     else if constexpr (AKC)
-      asm volatile(MTB_GEMM_LOOP_NN MTB_LOOP_OPERANDS);
+      asm volatile(MTB_GEMM_LOOP_NN MTB_LOOP_OPERANDS, MTB_GEMM_LOOP_CLOBBERS_NN);
     else
-      asm volatile(MTB_GEMM_LOOP_TN MTB_LOOP_OPERANDS);
+      asm volatile(MTB_GEMM_LOOP_TN MTB_LOOP_OPERANDS, MTB_GEMM_LOOP_CLOBBERS_TN);
 #undef MTB_LOOP_OPERANDS
   } else if constexpr (SH == SH192) {
     static_assert(AKC && BKC, "the 256 x 192 tile is built for k-contiguous operands only");
@@ -861,7 +861,7 @@ MTB_DEV void sched_tile(bf16_t* smem, int M, int N, int K, const bf16_t* __restr
                    MTB_LOOP_COMMON,
                    [fa0] "v"(fa[0]), [fa1] "v"(fa[1]), [fa2] "v"(fa[2]), [fa3] "v"(fa[3]),
                    [fb0] "v"(fb[0]), [fb1] "v"(fb[1]), [fb2] "v"(fb[2]), [fb3] "v"(fb[3])
-                 : "memory", "m0", "scc", MTB_GEMM_LOOP_CLOBBERS_192);
+                 : "memory", "m0", "scc", MTB_GEMM_LOOP_CLOBBERS_NT_192);
   }
 #pragma clang diagnostic pop
 #undef MTB_LOOP_COMMON
