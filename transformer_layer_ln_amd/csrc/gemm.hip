@@ -2,7 +2,8 @@
 //
 // bf16 path, gfx950 MFMA v_mfma_f32_32x32x16_bf16, two kernels:
 //  * gemm_bf16_sched_kernel (contractions >= 1024 deep, multiples of 32): a
-//    256 x 256 tile on 4 wavefronts of 128 x 128, its k-loop one hand-scheduled
+//    256 x 256 tile on 8 wavefronts of 128 x 64 (two per SIMD; a 256 x 192
+//    tile on 4 wavefronts for 1536-wide products), its k-loop one hand-scheduled
 //    inline-assembly block (gemm_loop.inc, written by gen_gemm_loop.py, which
 //    describes the schedule): direct-to-LDS copies three 32-deep k-tiles
 //    ahead, fragments read a whole k-tile before their MFMAs;
@@ -605,17 +606,22 @@ MTB_DEV void gemm_epilogue(const f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32], vo
       }
     }
     __syncthreads();
+    // the row items' LDS and global addresses are the same for every chunk;
+    // hidden behind this copy of tid they are recomputed per chunk instead of
+    // held (or spilled) across the loop
+    int t = tid;
+    asm volatile("" : "+v"(t));
     if constexpr (EPI == EPI_PARTIAL)
       epi_partial<BN, CR, NT>(reinterpret_cast<float*>(ep.ws) + (size_t)bt.split * M * N, st, M, N,
-                              m0 + c0, n0, tid);
+                              m0 + c0, n0, t);
     else if constexpr (EPI == EPI_XENT_STATS)
-      epi_xent_stats<BN, CR, NT>(ep, st, M, N, m0 + c0, n0, bt.tn, bt.tiles_n, tid);
+      epi_xent_stats<BN, CR, NT>(ep, st, M, N, m0 + c0, n0, bt.tn, bt.tiles_n, t);
     else if (has_pre)
-      epi_rows_pre<PRE ? EPI : EPI_STORE, BN, CR, NT>(ep, st, M, N, m0 + c0, n0, tid, pre);
+      epi_rows_pre<PRE ? EPI : EPI_STORE, BN, CR, NT>(ep, st, M, N, m0 + c0, n0, t, pre);
     else if (has_swi)
-      epi_rows_dswiglu_pre<BN, CR, NT>(ep, st, M, N, m0 + c0, n0, tid, spre);
+      epi_rows_dswiglu_pre<BN, CR, NT>(ep, st, M, N, m0 + c0, n0, t, spre);
     else
-      epi_rows<EPI, BN, CR, NT>(ep, st, M, N, m0 + c0, n0, tid);
+      epi_rows<EPI, BN, CR, NT>(ep, st, M, N, m0 + c0, n0, t);
     if constexpr (PRE) {
       if (has_pre && c0 + CR < BM) load_pre(m0 + c0 + CR);
     }
@@ -709,28 +715,39 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(int M, i
                                                             lane, tid);
 }
 
-// Hand-scheduled tiles: 4 wavefronts (2 x 2), each with FM x FN 32x32
+// Hand-scheduled tiles: 2 x WGN wavefronts, each with FM x FN 32x32
 // accumulators, the k-loop one inline-assembly block of gemm_loop.inc
-// (schedules and LDS layout: gen_gemm_loop.py). Shapes:
-//   SH256: 256 x 256, 4 stages, one block per CU;
-//   SH192: 256 x 192, 4 stages, one block per CU (1536-wide products: 256
-//          tiles on 256 CUs instead of 192).
+// (schedules and LDS layout: gen_gemm_loop.py). Shapes, all with 4 stages and
+// one block per CU:
+//   SH256:   256 x 256 on 4 wavefronts (2 x 2) of 128 x 128;
+//   SH192:   256 x 192 on 4 wavefronts of 128 x 96 (1536-wide products: 256
+//            tiles on 256 CUs instead of 192);
+//   SH256W8: 256 x 256 on 8 wavefronts (2 x 4) of 128 x 64, two per SIMD, so
+//            that one wavefront's MFMAs run while the other waits on its
+//            copies, fragment reads or the barrier.
 // Needs each split's contraction to be a multiple of 32 and every operand
 // byte offset below 2^32 (sched_ok).
 constexpr int SBK = 32;
-enum SchedShape { SH256 = 0, SH192 = 1 };
+enum SchedShape { SH256 = 0, SH192 = 1, SH256W8 = 2 };
 template <int SH>
 struct Sched {
-  static constexpr int FM = 4, FN = SH == SH256 ? 4 : 3;
-  static constexpr int BM = 64 * FM, BN = 64 * FN;
+  static constexpr int WAVES = SH == SH256W8 ? 8 : 4, WGN = WAVES / 2;
+  static constexpr int FM = 4, FN = SH == SH256 ? 4 : SH == SH192 ? 3 : 2;
+  static constexpr int BM = 64 * FM, BN = 32 * WGN * FN;
   static constexpr int STAGES = 4;
   static constexpr int SLOTS = STAGES;                 // loop body slots (gen_gemm_loop.py)
   static constexpr int PER_CU = 1;
-  static constexpr int QA = BM / 64, QB = BN / 64;     // copy blocks per wavefront and k-tile
+  static constexpr int QA = BM / 16 / WAVES, QB = BN / 16 / WAVES;  // copy blocks per wavefront and k-tile
   static constexpr uint32_t STAGE_BYTES = (BM + BN) * SBK * 2;
   static constexpr int SETS = (STAGES + 1) / 2;       // fragment base sets (stages 2i, 2i+1)
   static constexpr int SMEM = STAGES * (BM + BN) * SBK;  // bf16 elements of LDS
 };
+
+// the 256 x 256 shape every scheduled launch of that tile uses: two
+// wavefronts per SIMD measured 4-7 % faster than one on the block's products
+// with k-contiguous operands (fc1 forward 134 -> 129 us, fc1 dgrad 116 -> 110
+// us) and the same on the weight gradients
+constexpr int kShMain = SH256W8;
 
 // One block's tile (bt) of the product: the k-loop and the epilogue. smem is
 // the block's Sched<SH>::SMEM-element LDS array (1-KB aligned).
@@ -743,7 +760,7 @@ MTB_DEV void sched_tile(bf16_t* smem, int M, int N, int K, const bf16_t* __restr
   constexpr uint32_t B_OFF = BM * SBK * 2;  // operand B follows A inside a stage (bytes)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / G::WGN, wn = wave % G::WGN;
   const int kspan = K / ksplit, kbeg = bt.split * kspan;
   const int m0 = bt.tm * BM, n0 = bt.tn * BN;
   const uint32_t lds = (uint32_t)(uintptr_t)smem;
@@ -862,17 +879,35 @@ MTB_DEV void sched_tile(bf16_t* smem, int M, int N, int K, const bf16_t* __restr
                    [fa0] "v"(fa[0]), [fa1] "v"(fa[1]), [fa2] "v"(fa[2]), [fa3] "v"(fa[3]),
                    [fb0] "v"(fb[0]), [fb1] "v"(fb[1]), [fb2] "v"(fb[2]), [fb3] "v"(fb[3])
                  : "memory", "m0", "scc", MTB_GEMM_LOOP_CLOBBERS_NT_192);
+  } else if constexpr (SH == SH256W8) {
+#define MTB_LOOP_OPERANDS                                                                          \
+  : [c00] "+a"(acc[0][0]), [c01] "+a"(acc[0][1]), [c10] "+a"(acc[1][0]), [c11] "+a"(acc[1][1]),    \
+    [c20] "+a"(acc[2][0]), [c21] "+a"(acc[2][1]), [c30] "+a"(acc[3][0]), [c31] "+a"(acc[3][1]),    \
+    [voA0] "+v"(voA[0]), [voA1] "+v"(voA[1]), [voB0] "+v"(voB[0]), [voB1] "+v"(voB[1]),            \
+    MTB_LOOP_COMMON,                                                                               \
+    [fa0] "v"(fa[0]), [fa1] "v"(fa[1]), [fa2] "v"(fa[2]), [fa3] "v"(fa[3]),                        \
+    [fa4] "v"(fa[NA > 4 ? 4 : 0]), [fa5] "v"(fa[NA > 5 ? 5 : 0]), [fa6] "v"(fa[NA > 6 ? 6 : 0]),   \
+    [fa7] "v"(fa[NA > 7 ? 7 : 0]),                                                                 \
+    [fb0] "v"(fb[0]), [fb1] "v"(fb[1]), [fb2] "v"(fb[2]), [fb3] "v"(fb[3])                         \
+  : "memory", "m0", "scc"
+    if constexpr (AKC && BKC)
+      asm volatile(MTB_GEMM_LOOP_NT_W8 MTB_LOOP_OPERANDS, MTB_GEMM_LOOP_CLOBBERS_NT_W8);
+    else if constexpr (AKC)
+      asm volatile(MTB_GEMM_LOOP_NN_W8 MTB_LOOP_OPERANDS, MTB_GEMM_LOOP_CLOBBERS_NN_W8);
+    else
+      asm volatile(MTB_GEMM_LOOP_TN_W8 MTB_LOOP_OPERANDS, MTB_GEMM_LOOP_CLOBBERS_TN_W8);
+#undef MTB_LOOP_OPERANDS
   }
 #pragma clang diagnostic pop
 #undef MTB_LOOP_COMMON
 #undef MTB_ACC_ROW
   __syncthreads();
-  gemm_epilogue<BM, BN, 2, 2, G::SMEM / 2, AKC, EPI, true>(acc, smem, ep, M, N, m0, n0, bt, wm, wn, lane,
-                                                           tid);
+  gemm_epilogue<BM, BN, 2, G::WGN, G::SMEM / 2, AKC, EPI, true>(acc, smem, ep, M, N, m0, n0, bt, wm, wn,
+                                                                lane, tid);
 }
 
 template <int SH, bool AKC, bool BKC, int EPI>
-__global__ __launch_bounds__(256, Sched<SH>::PER_CU) void gemm_bf16_sched_kernel(
+__global__ __launch_bounds__(64 * Sched<SH>::WAVES, Sched<SH>::PER_CU) void gemm_bf16_sched_kernel(
     int M, int N, int K, const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ B, int ldb,
     Epi ep, int ksplit) {
   __shared__ __attribute__((aligned(1024))) bf16_t smem[Sched<SH>::SMEM];
@@ -895,8 +930,9 @@ struct SchedProb {
 // the first p0.blocks blocks in XCD order take p0, the rest p1, so that a
 // product whose tiles leave CUs idle shares the chip with another one.
 template <bool AKC, bool BKC, int EPI>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_sched_pair_kernel(SchedProb p0, SchedProb p1) {
-  __shared__ __attribute__((aligned(1024))) bf16_t smem[Sched<SH256>::SMEM];
+__global__ __launch_bounds__(64 * Sched<kShMain>::WAVES, 1) void gemm_bf16_sched_pair_kernel(SchedProb p0,
+                                                                                             SchedProb p1) {
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[Sched<kShMain>::SMEM];
   const int r = xcd_order(blockIdx.x, gridDim.x);
   const bool second = r >= p0.blocks;  // uniform over the block
   const int M = second ? p1.M : p0.M, N = second ? p1.N : p0.N, K = second ? p1.K : p0.K;
@@ -905,8 +941,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_sched_pair_kernel(SchedProb 
   const int lda = second ? p1.lda : p0.lda, ldb = second ? p1.ldb : p0.ldb;
   const int ksplit = second ? p1.ksplit : p0.ksplit;
   const Epi ep = second ? p1.ep : p0.ep;
-  sched_tile<SH256, AKC, BKC, EPI>(smem, M, N, K, A, lda, B, ldb, ep, ksplit,
-                                   tile_at<256, 256>(M, N, second ? r - p0.blocks : r));
+  sched_tile<kShMain, AKC, BKC, EPI>(smem, M, N, K, A, lda, B, ldb, ep, ksplit,
+                                     tile_at<256, 256>(M, N, second ? r - p0.blocks : r));
 }
 
 // ---------------------------------------------------------------------------
@@ -990,7 +1026,7 @@ struct Plan {
 // Tile shape and contraction split per problem, the one decision both the
 // launch and the workspace query use. Candidates (relative per-tile rates
 // measured on MI355X over the block's GEMM shapes, times the fraction of the
-// chip their tile count fills): the scheduled 256x256 kernel (4 wavefronts,
+// chip their tile count fills): the scheduled 256x256 kernel (8 wavefronts,
 // gen_gemm_loop.py) when the contraction is a multiple of 32 and at least 1024
 // deep, 1.2-1.5x the 2x4-wavefront 256x256 kernel; 256x192 (4x2 wavefronts)
 // when N splits into 192-wide tiles (plain store); 128x128 (2x2, two blocks
@@ -1060,8 +1096,8 @@ Plan plan(int M, int N, int K, bool a_kc, bool b_kc, int kind, bool split_ok, bo
     if (s > 1) return {T128x128, s};
   }
   const double f128 = 0.85 * fill(t128, 2);
-  // the scheduled kernel's fixed per-block costs (one wavefront per SIMD to hide the first copies
-  // and the epilogue) outweigh its faster loop below 1024-deep contractions; with a residual to
+  // the scheduled kernel's fixed per-block costs (one block per CU to hide the first copies and
+  // the epilogue) outweigh its faster loop below 1024-deep contractions; with a residual to
   // add, its prefetched residual rows make it the faster one from 512 deep (projection forward,
   // 8192 x 4096 x 512: 70 against 77 us)
   const bool sk = K % SBK == 0 && K >= (resid ? 512 : 1024);
@@ -1098,7 +1134,8 @@ hipError_t launch_sched(int M, int N, int K, const void* A, int lda, const void*
                         const Epi& e, hipStream_t st, int ksplit = 1) {
   constexpr int BM = Sched<SH>::BM, BN = Sched<SH>::BN;
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_bf16_sched_kernel<SH, AKC, BKC, EPI>), dim3(tiles * ksplit), dim3(256), 0, st,
+  hipLaunchKernelGGL((gemm_bf16_sched_kernel<SH, AKC, BKC, EPI>), dim3(tiles * ksplit),
+                     dim3(64 * Sched<SH>::WAVES), 0, st,
                      M, N, K, (const bf16_t*)A, lda, (const bf16_t*)B, ldb, e, ksplit);
   return hipGetLastError();
 }
@@ -1183,7 +1220,7 @@ hipError_t launch_bf16(int M, int N, int K, const void* A, int lda, const void* 
     if constexpr (!AKC && !BKC && EPI == EPI_STORE) {
       if (pl.splits > 1) {
         const hipError_t r =
-            ok ? launch_sched<SH256, AKC, BKC, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, e, st, pl.splits)
+            ok ? launch_sched<kShMain, AKC, BKC, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, e, st, pl.splits)
                : launch_cfg<256, 256, 2, 4, 1, AKC, BKC, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, e, st,
                                                                        pl.splits);
         if (r != hipSuccess) return r;
@@ -1197,7 +1234,7 @@ hipError_t launch_bf16(int M, int N, int K, const void* A, int lda, const void* 
       // token-major plain stores: partial tiles, then the split epilogue pass
       if constexpr (AKC && EPI == EPI_STORE) {
         const hipError_t r =
-            ok ? launch_sched<SH256, AKC, BKC, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, e, st, pl.splits)
+            ok ? launch_sched<kShMain, AKC, BKC, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, e, st, pl.splits)
                : launch_cfg<256, 256, 2, 4, 1, AKC, BKC, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, e, st,
                                                                        pl.splits);
         if (r != hipSuccess) return r;
@@ -1208,7 +1245,7 @@ hipError_t launch_bf16(int M, int N, int K, const void* A, int lda, const void* 
       }
       return hipErrorInvalidValue;
     }
-    return ok ? launch_sched<SH256, AKC, BKC, EPI>(M, N, K, A, lda, B, ldb, e, st)
+    return ok ? launch_sched<kShMain, AKC, BKC, EPI>(M, N, K, A, lda, B, ldb, e, st)
               : launch_cfg<256, 256, 2, 4, 1, AKC, BKC, EPI>(M, N, K, A, lda, B, ldb, e, st);
   }
   if (pl.splits > 1) {
@@ -1307,10 +1344,12 @@ hipError_t gemm_wgrad_pair(int dtype, const GemmProb& p0, const GemmProb& p1, vo
   }
   const dim3 grid((unsigned)(q[0].blocks + q[1].blocks));
   if (pp.s0 == 1) {
-    hipLaunchKernelGGL((gemm_bf16_sched_pair_kernel<false, false, EPI_STORE>), grid, dim3(256), 0, st, q[0], q[1]);
+    hipLaunchKernelGGL((gemm_bf16_sched_pair_kernel<false, false, EPI_STORE>), grid,
+                       dim3(64 * Sched<kShMain>::WAVES), 0, st, q[0], q[1]);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((gemm_bf16_sched_pair_kernel<false, false, EPI_PARTIAL>), grid, dim3(256), 0, st, q[0], q[1]);
+  hipLaunchKernelGGL((gemm_bf16_sched_pair_kernel<false, false, EPI_PARTIAL>), grid,
+                     dim3(64 * Sched<kShMain>::WAVES), 0, st, q[0], q[1]);
   hipError_t r = hipGetLastError();
   for (int i = 0; i < 2 && r == hipSuccess; ++i) {
     const GemmProb& g = *src[i];
