@@ -4,14 +4,16 @@
 // its local heads with no communication; GQA: q head i reads kv head i / g).
 //
 // bf16 path (gfx950 MFMA 32x32x16). Every kernel works on 64-row tiles of one
-// (batch, head) with 4 wavefronts arranged 2 x 2: each wavefront takes 32 rows
-// of its own side and one 32-row half of the other side's tile, and the two
-// halves are combined through LDS at the end. That gives S/64 * B * heads
-// workgroups, two per CU; causal grids pair heavy and light tiles. The other
-// side's tiles stream global -> LDS with direct-to-LDS loads (forward and dQ
+// (batch, head) with groups of 4 wavefronts arranged 2 x 2: each wavefront
+// takes 32 rows of its own side and one 32-row half of the other side's tile,
+// and the two halves are combined through LDS at the end. That gives S/64 * B
+// * heads workgroups: two of one group per CU (causal forward grids pair heavy
+// and light tiles), or, for the causal backward, one of two groups per CU that
+// split the tile's range of the other side between them. The other side's
+// tiles stream global -> LDS with direct-to-LDS loads (forward and dQ
 // double-buffered: tile t+1 is in flight while tile t is used; dK/dV keeps
-// its K tile resident and single-buffers Q and dO, the CU's second
-// workgroup covering the copies).
+// its K tile resident and single-buffers Q and dO, the CU's other wavefronts
+// covering the copies).
 //  * forward: S^T = K Q^T puts one query per lane, so the online-softmax row
 //    max is 16 in-lane values plus one exchange with lane ^ 32, the running
 //    sum stays per lane until the end, and the O^T accumulator is rescaled
@@ -78,6 +80,20 @@ MTB_DEV void tile_order(int L, int ntile, int nbh, bool causal, bool heavy_high,
   }
   tile = heavy_high ? ntile - 1 - rank : rank;
 }
+
+// The causal backward kernels run bwd_groups(true) = 2 groups of 4 wavefronts
+// per workgroup (one workgroup per CU), the two groups splitting the
+// workgroup's triangular range of tiles in halves and summing their partial
+// results through LDS at the end; the grid goes heaviest tile first. Each
+// group then carries half of its tile's work and both groups run to about the
+// same length, where two separate workgroups per CU, one heavy and one light,
+// left the heavy one to finish alone on a CU whose other slot had emptied.
+// Measured on the seq-4096 causal GQA share: dK/dV 133 -> 111 us, dQ 89 -> 79
+// us; on the seq-2048 causal share dK/dV 76 -> 71 us, dQ unchanged. The
+// forward keeps two workgroups per CU: its per-workgroup fixed work (the Q
+// fragments, the merge and the O stores) is larger, and two groups made it
+// slower (seq-2048 causal 39 -> 43 us).
+__host__ __device__ constexpr int bwd_groups(bool causal) { return causal ? 2 : 1; }
 
 // two 16-row k-steps of a 32x32 accumulator as bf16 B operands:
 // step 0 = rows {4lg..4lg+3, 8+4lg..}, step 1 = rows {16+4lg.., 24+4lg..}
@@ -394,33 +410,36 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(int rows, int S, int 
   }
 }
 
-// dK, dV. Workgroup = 64 keys of one (batch, q head), two workgroups per CU
-// (each one's loads hidden behind the other's MFMAs); wavefront w takes key
-// half w & 1 and query half w >> 1 of every 64-query tile. S = Q K^T puts a
-// key per lane, so P and dS feed dV^T += dO^T P^T and dK^T += Q^T dS^T
-// straight from registers; dO^T and Q^T come from the row-major Q and dO
-// tiles by transpose reads. The K tile stays in LDS for the whole walk, the
-// wavefront's V rows in registers. The two query halves are summed at the
-// end.
+
+// dK, dV. Workgroup = 64 keys of one (batch, q head); non-causal: two
+// workgroups per CU (each one's loads hidden behind the other's MFMAs).
+// Wavefront w of a group takes key half w & 1 and query half w >> 1 of every
+// 64-query tile. S = Q K^T puts a key per lane, so P and dS feed
+// dV^T += dO^T P^T and dK^T += Q^T dS^T straight from registers; dO^T and
+// Q^T come from the row-major Q and dO tiles by transpose reads. The K tile
+// stays in LDS for the whole walk, the wavefront's V rows in registers. The
+// groups' and then the two query halves' sums are added at the end.
 template <int D, bool CAUSAL, bool DROP>
-__global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(
+__global__ __launch_bounds__(256 * bwd_groups(CAUSAL), 2 / bwd_groups(CAUSAL)) void attn_bwd_dkdv_kernel(
     int S, int nq, int nkv, int ldq, const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO,
     const float* __restrict__ lse, const float* __restrict__ Dbuf, bf16_t* __restrict__ dqkv,
     float* __restrict__ part, float sl2, float scale, Drop drop) {
-  constexpr int TILE = 64 * D;  // elements of one 64 x D tile
-  // K, then the streamed Q and dO tiles, then log-sum-exp and D (64 floats each)
-  __shared__ __attribute__((aligned(1024))) bf16_t smem[3 * TILE + 256];
-  bf16_t* sK = smem;
-  bf16_t* sQ = smem + TILE;
-  bf16_t* sdO = smem + 2 * TILE;
-  const float* sL = reinterpret_cast<const float*>(smem + 3 * TILE);
-  const float* sD = sL + 64;
+  constexpr int G = bwd_groups(CAUSAL);
+  constexpr int TILE = 64 * D;         // elements of one 64 x D tile
+  constexpr int GRP = 2 * TILE + 256;  // one group's Q and dO tiles, log-sum-exp and D (64 floats each)
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[TILE + G * GRP];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lg = lane >> 5;
-  const int kh = wave & 1, qh = wave >> 1;
+  const int grp = wave >> 2, w4 = wave & 3;  // grp: 0 for every wavefront when G = 1
+  const int kh = w4 & 1, qh = w4 >> 1;
+  bf16_t* sK = smem;
+  bf16_t* sQ = smem + TILE + grp * GRP;
+  bf16_t* sdO = sQ + TILE;
+  const float* sL = reinterpret_cast<const float*>(sQ + 2 * TILE);
+  const float* sD = sL + 64;
   const int ntile = S / 64, nbh = gridDim.x / ntile;
   int kb, bh;
-  tile_order(blockIdx.x, ntile, nbh, CAUSAL, false, true, kb, bh);
+  tile_order(blockIdx.x, ntile, nbh, CAUSAL, false, G == 1, kb, bh);
   const int b = bh / nq, hq = bh % nq;
   const int g = nq / nkv, hk = hq / g;
   const int k0 = kb * 64 + kh * 32;
@@ -428,8 +447,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(
   const size_t tok0 = (size_t)b * S;
   const int ldo = nq * D;
 
-  const RowCopy<64, D> copy_q(ldq, wave, lane), copy_o(nq * D, wave, lane);
-  copy_q(sK, qkv + (tok0 + kb * 64) * ldq + (size_t)(nq + hk) * D);
+  const RowCopy<64, D> copy_q(ldq, w4, lane), copy_o(nq * D, w4, lane);
+  if (grp == 0) copy_q(sK, qkv + (tok0 + kb * 64) * ldq + (size_t)(nq + hk) * D);
   bf16x8 vf[D / 16];
   {
     const bf16_t* vp = qkv + (tok0 + key) * ldq + (size_t)(nq + nkv + hk) * D + 8 * lg;
@@ -450,18 +469,26 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(
   const int krow = kh * 32 + (lane & 31);    // the lane's key row in sK
   const int qrow = qh * 32 + (lane & 31);    // the lane's query row in sQ / sdO
 
-  for (int qt = CAUSAL ? kb : 0; qt < ntile; ++qt) {
+  // this group's query tiles: [q_beg, q_end) of the tile's range, in `iters`
+  // passes that every group makes (the barriers are the workgroup's)
+  const int q_first = CAUSAL ? kb : 0, iters = (ntile - q_first + G - 1) / G;
+  const int q_beg = q_first + grp * iters, q_end = min(ntile, q_beg + iters);
+  for (int it = 0; it < iters; ++it) {
+    const int qt = q_beg + it;
+    const bool live = qt < q_end;   // uniform over the group
     const int qt0 = qt * 64;
-    copy_q(sQ, qbase + (size_t)qt0 * ldq);
-    copy_o(sdO, dobase + (size_t)qt0 * ldo);
-    if (wave == 0) {
-      lds_load4(4u * lane, lrow + qt0, smem + 3 * TILE);
-      lds_load4(4u * lane, drow + qt0, smem + 3 * TILE + 128);
+    if (live) {
+      copy_q(sQ, qbase + (size_t)qt0 * ldq);
+      copy_o(sdO, dobase + (size_t)qt0 * ldo);
+      if (w4 == 0) {
+        lds_load4(4u * lane, lrow + qt0, sQ + 2 * TILE);
+        lds_load4(4u * lane, drow + qt0, sQ + 2 * TILE + 128);
+      }
     }
     __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
     __syncthreads();
     const int qw0 = qt0 + qh * 32;
-    if (!CAUSAL || qw0 + 31 >= k0) {
+    if (live && (!CAUSAL || qw0 + 31 >= k0)) {
       f32x16 s, dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
@@ -527,22 +554,39 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(
     }
     __syncthreads();  // every wavefront is done with the tile before the next one lands
   }
-  // sum the two query halves: qh = 1 hands its accumulators to qh = 0
-  // through LDS, dK first, then dV (each 2 x 64 x D floats: fits in the tiles)
+  // sum the groups (group 1 hands its accumulators to group 0 through LDS:
+  // 4 x 64 x D floats), then the two query halves (qh = 1 to qh = 0: 2 x 64 x
+  // D floats), dK first, then dV; both fit in the tiles
   constexpr int NR = D / 2;
-  float* xo = reinterpret_cast<float*>(smem);  // [kh][NR][64]
+  float* xo = reinterpret_cast<float*>(smem);  // [kh][NR][64], or [w4][NR][64] for the groups
 #pragma unroll
   for (int which = 0; which < 2; ++which) {
     f32x16(&acc)[D / 32] = which == 0 ? dk : dv;
-    if (which == 1) __syncthreads();   // qh = 0 is done reading the dK half
-    if (qh == 1) {
+    if constexpr (G == 2) {
+      __syncthreads();   // nobody reads xo (or the tiles) any more
+      if (grp == 1) {
+#pragma unroll
+        for (int df = 0; df < D / 32; ++df)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) xo[(w4 * NR + df * 16 + r) * 64 + lane] = acc[df][r];
+      }
+      __syncthreads();
+      if (grp == 0) {
+#pragma unroll
+        for (int df = 0; df < D / 32; ++df)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[df][r] += xo[(w4 * NR + df * 16 + r) * 64 + lane];
+      }
+    }
+    if (G == 2 || which == 1) __syncthreads();   // xo's readers are done
+    if (grp == 0 && qh == 1) {
 #pragma unroll
       for (int df = 0; df < D / 32; ++df)
 #pragma unroll
         for (int r = 0; r < 16; ++r) xo[(kh * NR + df * 16 + r) * 64 + lane] = acc[df][r];
     }
     __syncthreads();
-    if (qh == 0) {
+    if (grp == 0 && qh == 0) {
       // acc[df][4i + r]: d = 32 df + 8i + 4lg + r for key `key`
 #pragma unroll
       for (int df = 0; df < D / 32; ++df)
@@ -592,26 +636,30 @@ __global__ __launch_bounds__(256) void attn_dkv_reduce_kernel(int B, int S, int 
   st8(dqkv + ((size_t)b * S + s) * ldq + col, acc);
 }
 
-// dQ. Workgroup = 64 queries of one (batch, q head), two workgroups per CU;
-// wavefront w takes query half w & 1 and key half w >> 1 of every 64-key tile
-// (S^T layout: a query per lane), its Q and dO rows in registers. The K and V
-// tiles stream global -> LDS double-buffered (tile t+1 in flight while tile
-// t is used); K^T comes from the K tile by transpose reads. The key halves
-// are summed at the end.
+// dQ. Workgroup = 64 queries of one (batch, q head); non-causal: two
+// workgroups per CU. Wavefront w of a group takes query half w & 1 and key
+// half w >> 1 of every 64-key tile (S^T layout: a query per lane), its Q and
+// dO rows in registers. The K and V tiles stream global -> LDS
+// double-buffered (tile t+1 in flight while tile t is used); K^T comes from
+// the K tile by transpose reads. The groups' and then the key halves' sums
+// are added at the end.
 template <int D, bool CAUSAL, bool DROP>
-__global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
+__global__ __launch_bounds__(256 * bwd_groups(CAUSAL), 2 / bwd_groups(CAUSAL)) void attn_bwd_dq_kernel(
     int S, int nq, int nkv, int ldq, const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO,
     const float* __restrict__ lse, const float* __restrict__ Dbuf, bf16_t* __restrict__ dqkv, float sl2,
     float scale, Drop drop) {
+  constexpr int G = bwd_groups(CAUSAL);
   constexpr int TILE = 64 * D;
   constexpr int STAGE = 2 * TILE;  // K, V
-  __shared__ __attribute__((aligned(1024))) bf16_t smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[G * 2 * STAGE];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lg = lane >> 5;
-  const int qh = wave & 1, kh = wave >> 1;
+  const int grp = G == 1 ? 0 : wave >> 2, w4 = wave & 3;
+  const int qh = w4 & 1, kh = w4 >> 1;
+  bf16_t* gsm = smem + grp * 2 * STAGE;  // this group's two stages
   const int ntile = S / 64, nbh = gridDim.x / ntile;
   int qb, bh;
-  tile_order(blockIdx.x, ntile, nbh, CAUSAL, true, true, qb, bh);
+  tile_order(blockIdx.x, ntile, nbh, CAUSAL, true, G == 1, qb, bh);
   const int b = bh / nq, hq = bh % nq, hk = hq / (nq / nkv);
   const int q0 = qb * 64 + qh * 32;
   const int qi = q0 + (lane & 31);
@@ -620,13 +668,17 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
 
   const bf16_t* kbase = qkv + tok0 * ldq + (size_t)(nq + hk) * D;
   const bf16_t* vbase = qkv + tok0 * ldq + (size_t)(nq + nkv + hk) * D;
-  const RowCopy<64, D> copy(ldq, wave, lane);
-  auto fetch = [&](int t) {
-    bf16_t* st = smem + (t & 1) * STAGE;
-    copy(st, kbase + (size_t)t * 64 * ldq);
-    copy(st + TILE, vbase + (size_t)t * 64 * ldq);
+  // this group's key tiles: [k_beg, k_end), in `iters` passes that every
+  // group makes (the barriers are the workgroup's)
+  const int ntk = CAUSAL ? qb + 1 : ntile, iters = (ntk + G - 1) / G;
+  const int k_beg = grp * iters, k_end = min(ntk, k_beg + iters);
+  const RowCopy<64, D> copy(ldq, w4, lane);
+  auto fetch = [&](int t) {   // pass t's tiles into stage t & 1
+    bf16_t* st = gsm + (t & 1) * STAGE;
+    copy(st, kbase + (size_t)(k_beg + t) * 64 * ldq);
+    copy(st + TILE, vbase + (size_t)(k_beg + t) * 64 * ldq);
   };
-  fetch(0);
+  if (k_beg < k_end) fetch(0);
 
   bf16x8 qf[D / 16], of[D / 16];
   {
@@ -650,15 +702,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     for (int r = 0; r < 16; ++r) dq[i][r] = 0.f;
   const int krow = kh * 32 + (lane & 31);   // the lane's key row in the K / V tiles
 
-  const int ntk = CAUSAL ? qb + 1 : ntile;
   __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
   __syncthreads();
-  for (int t = 0; t < ntk; ++t) {
-    if (t + 1 < ntk) fetch(t + 1);   // into the stage every wave finished with last iteration
-    const bf16_t* sK = smem + (t & 1) * STAGE;
+  for (int t = 0; t < iters; ++t) {
+    if (k_beg + t + 1 < k_end) fetch(t + 1);   // into the stage every wave finished with last pass
+    const bf16_t* sK = gsm + (t & 1) * STAGE;
     const bf16_t* sV = sK + TILE;
-    const int ks = t * 64 + kh * 32;
-    if (!CAUSAL || ks <= q0 + 31) {
+    const int ks = (k_beg + t) * 64 + kh * 32;
+    if (k_beg + t < k_end && (!CAUSAL || ks <= q0 + 31)) {
       f32x16 s, dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
@@ -700,15 +751,32 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     __syncthreads();
   }
   constexpr int NR = D / 2;
-  float* xo = reinterpret_cast<float*>(smem);  // [qh][NR][64]
-  if (kh == 1) {
+  float* xo = reinterpret_cast<float*>(smem);  // [qh][NR][64], or [w4][NR][64] for the groups
+  if constexpr (G == 2) {
+    // group 1 hands its accumulators to group 0 (4 x 64 x D floats)
+    if (grp == 1) {
+#pragma unroll
+      for (int df = 0; df < D / 32; ++df)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xo[(w4 * NR + df * 16 + r) * 64 + lane] = dq[df][r];
+    }
+    __syncthreads();
+    if (grp == 0) {
+#pragma unroll
+      for (int df = 0; df < D / 32; ++df)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dq[df][r] += xo[(w4 * NR + df * 16 + r) * 64 + lane];
+    }
+    __syncthreads();   // group 0 is done reading xo
+  }
+  if (grp == 0 && kh == 1) {
 #pragma unroll
     for (int df = 0; df < D / 32; ++df)
 #pragma unroll
       for (int r = 0; r < 16; ++r) xo[(qh * NR + df * 16 + r) * 64 + lane] = dq[df][r];
   }
   __syncthreads();
-  if (kh == 1) return;
+  if (grp == 1 || kh == 1) return;
   bf16_t* op = dqkv + (tok0 + qi) * ldq + (size_t)hq * D;
 #pragma unroll
   for (int df = 0; df < D / 32; ++df)
@@ -850,8 +918,8 @@ hipError_t attn_fwd_bf16(int B, int S, int nq, int nkv, int causal, const void* 
   dim3 grid((S / 64) * B * nq);
   const float sl2 = kLog2e / sqrtf((float)D);
 #define MTB_FWD(C, DR)                                                                        \
-  hipLaunchKernelGGL((attn_fwd_kernel<D, C, DR>), grid, dim3(256), 0, st, S, nq, nkv, ldq,    \
-                     (const bf16_t*)qkv, (bf16_t*)O, lse, sl2, drop)
+  hipLaunchKernelGGL((attn_fwd_kernel<D, C, DR>), grid, dim3(256), 0, st, S, nq, nkv,          \
+                     ldq, (const bf16_t*)qkv, (bf16_t*)O, lse, sl2, drop)
   if (causal) {
     if (drop.thr) MTB_FWD(true, true); else MTB_FWD(true, false);
   } else {
@@ -872,12 +940,12 @@ hipError_t attn_bwd_bf16(int B, int S, int nq, int nkv, int causal, const void* 
                      dim3(256), 0, st, rows, S, nq, (const bf16_t*)O, (const bf16_t*)dO, Dbuf);
   dim3 grid((S / 64) * B * nq);
 #define MTB_BWD(C, DR)                                                                        \
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, C, DR>), grid, dim3(256), 0, st, S, nq, nkv,   \
-                     ldq, (const bf16_t*)qkv, (const bf16_t*)dO, lse, Dbuf, (bf16_t*)dqkv,   \
-                     part, sl2, scale, drop);                                                \
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<D, C, DR>), grid, dim3(256), 0, st, S, nq, nkv, ldq,\
-                     (const bf16_t*)qkv, (const bf16_t*)dO, lse, Dbuf, (bf16_t*)dqkv, sl2,   \
-                     scale, drop)
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, C, DR>), grid, dim3(256 * bwd_groups(C)), 0, st, S, nq, \
+                     nkv, ldq, (const bf16_t*)qkv, (const bf16_t*)dO, lse, Dbuf,             \
+                     (bf16_t*)dqkv, part, sl2, scale, drop);                                 \
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<D, C, DR>), grid, dim3(256 * bwd_groups(C)), 0, st, S, nq, \
+                     nkv, ldq, (const bf16_t*)qkv, (const bf16_t*)dO, lse, Dbuf,             \
+                     (bf16_t*)dqkv, sl2, scale, drop)
   if (causal) {
     if (drop.thr) { MTB_BWD(true, true); } else { MTB_BWD(true, false); }
   } else {
