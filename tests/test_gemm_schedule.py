@@ -331,7 +331,7 @@ def test_schedule_with_direct_operand(name, la, lb, KT):
 @pytest.mark.parametrize("shape", [s.name for s in GEN.SHAPES if s is not GEN.S256])
 @pytest.mark.parametrize("KT", [1, 2, 3, 4, 5, 6, 7, 8, 11, 13, 32, 128])
 def test_other_shapes_symbolic_execution(shape, KT):
-    """The 256 x 192 and 8-wavefront 256 x 256 loops, for every layout built."""
+    """The 256 x 192, 8-wavefront 256 x 256 and 128 x 128 loops, for every layout built."""
     sh = next(s for s in GEN.SHAPES if s.name == shape)
     for name, la, lb in GEN.SHAPE_LAYOUTS[shape]:
         _check_run(la, lb, KT, sh)
@@ -341,16 +341,17 @@ def test_shapes_fit_their_registers_and_lds():
     """Fragment registers inside the clobbered range (and a quarter of the
     wavefront's VGPRs left to the compiled code around the loop: 64 of 256
     with one wavefront per SIMD, 32 of 128 with two), stages inside a CU's
-    160 KB of LDS, copy blocks whole, wait counts inside their fields. The
-    direct-operand variants exist for the one-wavefront-per-SIMD shapes."""
+    160 KB of LDS (per block, times the blocks a CU holds), copy blocks
+    whole, wait counts inside their fields. The direct-operand variants
+    exist for the one-wavefront-per-SIMD shapes."""
     for sh in GEN.SHAPES:
         for name, la, lb in GEN.SHAPE_LAYOUTS[sh.name]:
-            for d in (None, "auto") if sh.waves == 4 else (None,):
+            for d in (None, "auto") if sh.waves * sh.per_cu == 4 else (None,):
                 v = GEN.shape_for(sh, la, lb, d)
-                assert v.stages * v.stage_bytes <= 160 * 1024, (sh.name, name)
+                assert v.stages * v.stage_bytes * v.per_cu <= 160 * 1024, (sh.name, name)
                 assert v.a_bytes % 4096 == 0 and v.b_bytes % 4096 == 0, (sh.name, name)
                 assert v.frag_top // 4 <= v.frag_lo and v.frag_hi <= v.frag_top, (sh.name, name, d)
-                assert v.frag_top == 256 // (v.waves // 4), (sh.name, name, d)
+                assert v.frag_top == 256 * 4 // (v.waves * v.per_cu), (sh.name, name, d)
                 assert v.cpt * (v.stages - 2) <= 63, (sh.name, name, d)
 
 

@@ -724,19 +724,22 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(int M, i
 //            tiles on 256 CUs instead of 192);
 //   SH256W8: 256 x 256 on 8 wavefronts (2 x 4) of 128 x 64, two per SIMD, so
 //            that one wavefront's MFMAs run while the other waits on its
-//            copies, fragment reads or the barrier.
+//            copies, fragment reads or the barrier;
+//   SH128:   128 x 128 on 4 wavefronts of 64 x 64, two blocks per CU (64 KB
+//            of LDS each): for products whose larger tiles leave CUs idle,
+//            one block's first copies and epilogue overlap the other's loop.
 // Needs each split's contraction to be a multiple of 32 and every operand
 // byte offset below 2^32 (sched_ok).
 constexpr int SBK = 32;
-enum SchedShape { SH256 = 0, SH192 = 1, SH256W8 = 2 };
+enum SchedShape { SH256 = 0, SH192 = 1, SH256W8 = 2, SH128 = 3 };
 template <int SH>
 struct Sched {
   static constexpr int WAVES = SH == SH256W8 ? 8 : 4, WGN = WAVES / 2;
-  static constexpr int FM = 4, FN = SH == SH256 ? 4 : SH == SH192 ? 3 : 2;
+  static constexpr int FM = SH == SH128 ? 2 : 4, FN = SH == SH256 ? 4 : SH == SH192 ? 3 : 2;
   static constexpr int BM = 64 * FM, BN = 32 * WGN * FN;
   static constexpr int STAGES = 4;
   static constexpr int SLOTS = STAGES;                 // loop body slots (gen_gemm_loop.py)
-  static constexpr int PER_CU = 1;
+  static constexpr int PER_CU = SH == SH128 ? 2 : 1;
   static constexpr int QA = BM / 16 / WAVES, QB = BN / 16 / WAVES;  // copy blocks per wavefront and k-tile
   static constexpr uint32_t STAGE_BYTES = (BM + BN) * SBK * 2;
   static constexpr int SETS = (STAGES + 1) / 2;       // fragment base sets (stages 2i, 2i+1)
@@ -897,6 +900,21 @@ MTB_DEV void sched_tile(bf16_t* smem, int M, int N, int K, const bf16_t* __restr
     else
       asm volatile(MTB_GEMM_LOOP_TN_W8 MTB_LOOP_OPERANDS, MTB_GEMM_LOOP_CLOBBERS_TN_W8);
 #undef MTB_LOOP_OPERANDS
+  } else if constexpr (SH == SH128) {
+#define MTB_LOOP_OPERANDS                                                                          \
+  : [c00] "+a"(acc[0][0]), [c01] "+a"(acc[0][1]), [c10] "+a"(acc[1][0]), [c11] "+a"(acc[1][1]),    \
+    [voA0] "+v"(voA[0]), [voA1] "+v"(voA[1]), [voB0] "+v"(voB[0]), [voB1] "+v"(voB[1]),            \
+    MTB_LOOP_COMMON,                                                                               \
+    [fa0] "v"(fa[0]), [fa1] "v"(fa[1]), [fa2] "v"(fa[2]), [fa3] "v"(fa[3]),                        \
+    [fb0] "v"(fb[0]), [fb1] "v"(fb[1]), [fb2] "v"(fb[2]), [fb3] "v"(fb[3])                         \
+  : "memory", "m0", "scc"
+    if constexpr (AKC && BKC)
+      asm volatile(MTB_GEMM_LOOP_NT_128 MTB_LOOP_OPERANDS, MTB_GEMM_LOOP_CLOBBERS_NT_128);
+    else if constexpr (AKC)
+      asm volatile(MTB_GEMM_LOOP_NN_128 MTB_LOOP_OPERANDS, MTB_GEMM_LOOP_CLOBBERS_NN_128);
+    else
+      asm volatile(MTB_GEMM_LOOP_TN_128 MTB_LOOP_OPERANDS, MTB_GEMM_LOOP_CLOBBERS_TN_128);
+#undef MTB_LOOP_OPERANDS
   }
 #pragma clang diagnostic pop
 #undef MTB_LOOP_COMMON
@@ -929,10 +947,10 @@ struct SchedProb {
 // Two independent products in one grid (same operand layouts and epilogue):
 // the first p0.blocks blocks in XCD order take p0, the rest p1, so that a
 // product whose tiles leave CUs idle shares the chip with another one.
-template <bool AKC, bool BKC, int EPI>
-__global__ __launch_bounds__(64 * Sched<kShMain>::WAVES, 1) void gemm_bf16_sched_pair_kernel(SchedProb p0,
-                                                                                             SchedProb p1) {
-  __shared__ __attribute__((aligned(1024))) bf16_t smem[Sched<kShMain>::SMEM];
+template <int SH, bool AKC, bool BKC, int EPI>
+__global__ __launch_bounds__(64 * Sched<SH>::WAVES, Sched<SH>::PER_CU) void gemm_bf16_sched_pair_kernel(
+    SchedProb p0, SchedProb p1) {
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[Sched<SH>::SMEM];
   const int r = xcd_order(blockIdx.x, gridDim.x);
   const bool second = r >= p0.blocks;  // uniform over the block
   const int M = second ? p1.M : p0.M, N = second ? p1.N : p0.N, K = second ? p1.K : p0.K;
@@ -941,8 +959,8 @@ __global__ __launch_bounds__(64 * Sched<kShMain>::WAVES, 1) void gemm_bf16_sched
   const int lda = second ? p1.lda : p0.lda, ldb = second ? p1.ldb : p0.ldb;
   const int ksplit = second ? p1.ksplit : p0.ksplit;
   const Epi ep = second ? p1.ep : p0.ep;
-  sched_tile<kShMain, AKC, BKC, EPI>(smem, M, N, K, A, lda, B, ldb, ep, ksplit,
-                                     tile_at<256, 256>(M, N, second ? r - p0.blocks : r));
+  sched_tile<SH, AKC, BKC, EPI>(smem, M, N, K, A, lda, B, ldb, ep, ksplit,
+                                tile_at<Sched<SH>::BM, Sched<SH>::BN>(M, N, second ? r - p0.blocks : r));
 }
 
 // ---------------------------------------------------------------------------
@@ -1095,7 +1113,14 @@ Plan plan(int M, int N, int K, bool a_kc, bool b_kc, int kind, bool split_ok, bo
       s *= 2;
     if (s > 1) return {T128x128, s};
   }
-  const double f128 = 0.85 * fill(t128, 2);
+  // 128 x 128 tiles: the scheduled kernel (two blocks per CU) where the
+  // contraction is a multiple of 32, else the 2x2-wavefront kernel. Where
+  // both tiles fill the chip, the 256 x 256 one is faster (8192 x 4096 x 768:
+  // 76 against 87 us); where the larger tiles leave CUs idle, the scheduled
+  // 128 x 128 one wins (the seq-512 share's 4096-token products: 17.7 -> 13.2
+  // us, 26.4 -> 19.9 us with the GELU' epilogue, its QKV forward 24.6 us on
+  // 64 tiles of 256 x 192 -> 192 tiles of 128 x 128)
+  const double f128 = (K % SBK == 0 ? 0.95 : 0.85) * fill(t128, 2);
   // the scheduled kernel's fixed per-block costs (one block per CU to hide the first copies and
   // the epilogue) outweigh its faster loop below 1024-deep contractions; with a residual to
   // add, its prefetched residual rows make it the faster one from 512 deep (projection forward,
@@ -1156,6 +1181,7 @@ hipError_t launch_sched(int M, int N, int K, const void* A, int lda, const void*
 // reduction pass.
 struct PairPlan {
   bool ok = false;
+  bool small = false;  // 128 x 128 tiles (two blocks per CU) instead of 256 x 256
   int s0 = 1, s1 = 1;
   size_t ws1 = 0;  // split form: byte offset of p1's partial tiles in the workspace
 };
@@ -1198,6 +1224,29 @@ PairPlan pair_plan(int M0, int N0, int K0, int lda0, int ldb0, int M1, int N1, i
     int s1 = 2;
     while (s1 < 8 && K1 / s1 > K0 / a.splits) s1 *= 2;
     consider(a.splits, s1);
+  }
+  // Products too small for the 256 x 256 pair (the seq-512 share's 1024-wide
+  // weight gradients): the 128 x 128 scheduled tiles, two blocks per CU, both
+  // contractions split the same way into parts at least 512 deep, with at
+  // least one block for every CU and at most two. In the cost units above a
+  // 128 x 128 k-tile counts 1/3 of a 256 x 256 one (a quarter of its work at
+  // a lower rate), per block a CU holds.
+  if (!best.ok) {
+    const long u0 = tiles(M0, N0, 128, 128), u1 = tiles(M1, N1, 128, 128);
+    for (int sp = 1; sp <= 8; sp *= 2) {
+      if (K0 % (sp * SBK) != 0 || K1 % (sp * SBK) != 0 || K0 / sp < 512 || K1 / sp < 512) continue;
+      const long blocks = (u0 + u1) * sp;
+      if (blocks < kCUs || blocks > 2L * kCUs) continue;
+      if (!sched_ok(M0, N0, K0, false, lda0, false, ldb0, sp) || !sched_ok(M1, N1, K1, false, lda1, false, ldb1, sp))
+        continue;
+      const long per_cu = (blocks + kCUs - 1) / kCUs;
+      const long c = std::max(K0, K1) / sp / SBK * per_cu / 3 + 16 + (sp > 1 ? 16 : 0);
+      if (c >= best_cost) continue;
+      best_cost = c;
+      best.ok = best.small = true;
+      best.s0 = best.s1 = sp;
+      best.ws1 = sp > 1 ? ((size_t)sp * M0 * N0 * 4 + 255) & ~(size_t)255 : 0;
+    }
   }
   return best;
 }
@@ -1260,7 +1309,10 @@ hipError_t launch_bf16(int M, int N, int K, const void* A, int lda, const void* 
       hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st,
                          M, N, pl.splits, (const float*)e.ws, (bf16_t*)e.out, e.ldo);
     } else {
-      r = launch_cfg<128, 128, 2, 2, 2, AKC, BKC, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, e, st, pl.splits);
+      r = (K / pl.splits) % SBK == 0 && sched_ok(M, N, K, AKC, lda, BKC, ldb, pl.splits)
+              ? launch_sched<SH128, AKC, BKC, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, e, st, pl.splits)
+              : launch_cfg<128, 128, 2, 2, 2, AKC, BKC, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, e, st,
+                                                                      pl.splits);
       if (r != hipSuccess) return r;
       // 64-row pieces: twice the workgroups of the GEMM's tiles, two per CU, so
       // more of the partial-tile loads are in flight (15.0 -> 11.5 us for the
@@ -1281,6 +1333,8 @@ hipError_t launch_bf16(int M, int N, int K, const void* A, int lda, const void* 
     if (pl.tile == T256x256)
       return launch_cfg<256, 256, 2, 4, 1, AKC, BKC, EPI>(M, N, K, A, lda, B, ldb, e, st);
   }
+  if (K % SBK == 0 && sched_ok(M, N, K, AKC, lda, BKC, ldb, 1))
+    return launch_sched<SH128, AKC, BKC, EPI>(M, N, K, A, lda, B, ldb, e, st);
   return launch_cfg<128, 128, 2, 2, 2, AKC, BKC, EPI>(M, N, K, A, lda, B, ldb, e, st);
 }
 
@@ -1333,7 +1387,8 @@ hipError_t gemm_wgrad_pair(int dtype, const GemmProb& p0, const GemmProb& p1, vo
     q[i].A = (const bf16_t*)g.A; q[i].lda = g.lda;
     q[i].B = (const bf16_t*)g.B; q[i].ldb = g.ldb;
     q[i].ksplit = splits[i];
-    q[i].blocks = ((g.M + 255) / 256) * ((g.N + 255) / 256) * splits[i];
+    const int tm = pp.small ? 128 : 256;
+    q[i].blocks = ((g.M + tm - 1) / tm) * ((g.N + tm - 1) / tm) * splits[i];
     q[i].ep = Epi();
     if (pp.s0 > 1) {
       q[i].ep.ws = wsp[i];
@@ -1343,13 +1398,22 @@ hipError_t gemm_wgrad_pair(int dtype, const GemmProb& p0, const GemmProb& p1, vo
     }
   }
   const dim3 grid((unsigned)(q[0].blocks + q[1].blocks));
+  const dim3 block(64 * (pp.small ? Sched<SH128>::WAVES : Sched<kShMain>::WAVES));
   if (pp.s0 == 1) {
-    hipLaunchKernelGGL((gemm_bf16_sched_pair_kernel<false, false, EPI_STORE>), grid,
-                       dim3(64 * Sched<kShMain>::WAVES), 0, st, q[0], q[1]);
+    if (pp.small)
+      hipLaunchKernelGGL((gemm_bf16_sched_pair_kernel<SH128, false, false, EPI_STORE>), grid, block, 0, st,
+                         q[0], q[1]);
+    else
+      hipLaunchKernelGGL((gemm_bf16_sched_pair_kernel<kShMain, false, false, EPI_STORE>), grid, block, 0, st,
+                         q[0], q[1]);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((gemm_bf16_sched_pair_kernel<false, false, EPI_PARTIAL>), grid,
-                     dim3(64 * Sched<kShMain>::WAVES), 0, st, q[0], q[1]);
+  if (pp.small)
+    hipLaunchKernelGGL((gemm_bf16_sched_pair_kernel<SH128, false, false, EPI_PARTIAL>), grid, block, 0, st,
+                       q[0], q[1]);
+  else
+    hipLaunchKernelGGL((gemm_bf16_sched_pair_kernel<kShMain, false, false, EPI_PARTIAL>), grid, block, 0, st,
+                       q[0], q[1]);
   hipError_t r = hipGetLastError();
   for (int i = 0; i < 2 && r == hipSuccess; ++i) {
     const GemmProb& g = *src[i];

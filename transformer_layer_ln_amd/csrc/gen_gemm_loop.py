@@ -96,10 +96,10 @@ class Shape:
     wavefront per SIMD; 128 with two, whose accumulators take the other 128
     of the SIMD's registers per lane)."""
 
-    def __init__(self, name, fm, fn, stages, direct=None, frag_top=256, waves=4):
+    def __init__(self, name, fm, fn, stages, direct=None, frag_top=256, waves=4, per_cu=1):
         self.name, self.fm, self.fn, self.stages = name, fm, fn, stages
         self.direct = direct
-        self.waves, self.frag_top = waves, frag_top
+        self.waves, self.frag_top, self.per_cu = waves, frag_top, per_cu
         self.bm, self.bn = 64 * fm, 32 * (waves // 2) * fn
         self.a_bytes = 0 if direct == "a" else self.bm * KT_BYTES
         self.b_bytes = 0 if direct == "b" else self.bn * KT_BYTES
@@ -156,19 +156,24 @@ class Shape:
 
 
 # the kernels' shapes: 256 x 256, 256 x 192 for the 1536-wide products (256
-# tiles instead of 192 on 256 CUs), and 256 x 256 on 8 wavefronts (two per
-# SIMD, 128 x 64 each)
+# tiles instead of 192 on 256 CUs), 256 x 256 on 8 wavefronts (two per SIMD,
+# 128 x 64 each), and 128 x 128 on 4 wavefronts of 64 x 64 with two blocks per
+# CU (64 KB of LDS each), for products too small to fill the chip with the
+# larger tiles, where one block's first copies and epilogue overlap the other
+# block's loop
 S256 = Shape("256", 4, 4, 4)
 S192 = Shape("192", 4, 3, 4)
 S256W8 = Shape("w8", 4, 2, 4, frag_top=128, waves=8)
-SHAPES = (S256, S192, S256W8)
+S128 = Shape("128", 2, 2, 4, frag_top=128, per_cu=2)
+SHAPES = (S256, S192, S256W8, S128)
 
 
 def shape_for(sh, la, lb, direct=None):
     """the variant of sh that a loop over layouts (la, lb) runs (direct="auto":
     with the operand direct_for picks loaded straight into registers)"""
     d = direct_for(la, lb) if direct == "auto" else direct
-    return Shape(sh.name, sh.fm, sh.fn, sh.stages, d, frag_top=sh.frag_top, waves=sh.waves)
+    return Shape(sh.name, sh.fm, sh.fn, sh.stages, d, frag_top=sh.frag_top, waves=sh.waves,
+                 per_cu=sh.per_cu)
 
 
 def reads(sh, layout, op, buf, stage, kk):
@@ -492,7 +497,7 @@ def loop64(la, lb, sh=S256_64, order="row"):
 LAYOUTS = (("NT", "kc", "kc"), ("NN", "kc", "mn"), ("TN", "mn", "mn"))
 # which layouts each shape is built for: 256 x 192 only for the 1536-wide
 # forward products (both operands k-contiguous)
-SHAPE_LAYOUTS = {"256": LAYOUTS, "192": LAYOUTS[:1], "w8": LAYOUTS}
+SHAPE_LAYOUTS = {"256": LAYOUTS, "192": LAYOUTS[:1], "w8": LAYOUTS, "128": LAYOUTS}
 
 
 def render():
