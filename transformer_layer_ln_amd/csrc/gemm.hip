@@ -465,10 +465,9 @@ MTB_DEV void epi_partial(float* ws, const Staged<BN>& st, int M, int N, int mc, 
 
 // out[m][n] = sum over s = 0 .. splits-1 of ws[s][m][n], rounded once; 8
 // elements per thread (N % 8 == 0)
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(int M, int N, int splits,
-                                                            const float* __restrict__ ws,
-                                                            bf16_t* __restrict__ out, int ldo) {
-  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 8;
+MTB_DEV void splitk_reduce_at(size_t blk, int M, int N, int splits, const float* __restrict__ ws,
+                              bf16_t* __restrict__ out, int ldo) {
+  const size_t i = (blk * 256 + threadIdx.x) * 8;
   const size_t MN = (size_t)M * N;
   if (i >= MN) return;
   float v[8];
@@ -481,6 +480,25 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(int M, int N, int sp
   }
   const size_t m = i / N, n = i % N;
   st8(out + m * ldo + n, v);
+}
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(int M, int N, int splits,
+                                                            const float* __restrict__ ws,
+                                                            bf16_t* __restrict__ out, int ldo) {
+  splitk_reduce_at(blockIdx.x, M, N, splits, ws, out, ldo);
+}
+// The split sums of two products in one launch: blocks [0, blocks0) take the
+// first, the rest the second (a launch of its own costs more than the few MB
+// of a small product's partials take to read).
+struct SplitSum {
+  int M, N, splits;
+  const float* ws;
+  bf16_t* out;
+  int ldo;
+};
+__global__ __launch_bounds__(256) void splitk_reduce_pair_kernel(SplitSum a, SplitSum b, int blocks0) {
+  const bool second = (int)blockIdx.x >= blocks0;
+  const SplitSum& p = second ? b : a;
+  splitk_reduce_at(second ? blockIdx.x - blocks0 : blockIdx.x, p.M, p.N, p.splits, p.ws, p.out, p.ldo);
 }
 
 // Epilogue of a split contraction with a fused epilogue: sums the fp32
@@ -1415,14 +1433,17 @@ hipError_t gemm_wgrad_pair(int dtype, const GemmProb& p0, const GemmProb& p1, vo
     hipLaunchKernelGGL((gemm_bf16_sched_pair_kernel<kShMain, false, false, EPI_PARTIAL>), grid, block, 0, st,
                        q[0], q[1]);
   hipError_t r = hipGetLastError();
-  for (int i = 0; i < 2 && r == hipSuccess; ++i) {
+  if (r != hipSuccess) return r;
+  SplitSum sum[2];
+  unsigned nblk[2];
+  for (int i = 0; i < 2; ++i) {
     const GemmProb& g = *src[i];
-    const size_t n8 = (size_t)g.M * g.N / 8;
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, g.M, g.N,
-                       splits[i], (const float*)wsp[i], (bf16_t*)g.e.out, g.e.ldo);
-    r = hipGetLastError();
+    sum[i] = {g.M, g.N, splits[i], (const float*)wsp[i], (bf16_t*)g.e.out, g.e.ldo};
+    nblk[i] = (unsigned)(((size_t)g.M * g.N / 8 + 255) / 256);
   }
-  return r;
+  hipLaunchKernelGGL(splitk_reduce_pair_kernel, dim3(nblk[0] + nblk[1]), dim3(256), 0, st, sum[0], sum[1],
+                     (int)nblk[0]);
+  return hipGetLastError();
 }
 
 hipError_t gemm(int dtype, int M, int N, int K, const void* A, int lda, bool a_kc, const void* B,
