@@ -81,19 +81,22 @@ MTB_DEV void tile_order(int L, int ntile, int nbh, bool causal, bool heavy_high,
   tile = heavy_high ? ntile - 1 - rank : rank;
 }
 
-// The causal backward kernels run bwd_groups(true) = 2 groups of 4 wavefronts
-// per workgroup (one workgroup per CU), the two groups splitting the
-// workgroup's triangular range of tiles in halves and summing their partial
-// results through LDS at the end; the grid goes heaviest tile first. Each
+// The backward kernels run G = 2 groups of 4 wavefronts per workgroup (one
+// workgroup per CU) for causal grids and for grids with no more workgroups
+// than CUs, G = 1 (two workgroups per CU) otherwise. The two groups split the
+// workgroup's range of tiles in halves and sum their partial results through
+// LDS at the end; causal grids go heaviest tile first. For causal grids each
 // group then carries half of its tile's work and both groups run to about the
 // same length, where two separate workgroups per CU, one heavy and one light,
-// left the heavy one to finish alone on a CU whose other slot had emptied.
-// Measured on the seq-4096 causal GQA share: dK/dV 133 -> 111 us, dQ 89 -> 79
-// us; on the seq-2048 causal share dK/dV 76 -> 71 us, dQ unchanged. The
-// forward keeps two workgroups per CU: its per-workgroup fixed work (the Q
-// fragments, the merge and the O stores) is larger, and two groups made it
-// slower (seq-2048 causal 39 -> 43 us).
-__host__ __device__ constexpr int bwd_groups(bool causal) { return causal ? 2 : 1; }
+// left the heavy one to finish alone on a CU whose other slot had emptied:
+// measured on the seq-4096 causal GQA share, dK/dV 133 -> 111 us, dQ 89 -> 79
+// us; on the seq-2048 causal share dK/dV 76 -> 71 us, dQ unchanged. A grid
+// of at most one workgroup per CU (the seq-512 share: 256) otherwise leaves
+// one wavefront per SIMD. The forward keeps two workgroups per CU: its
+// per-workgroup fixed work (the Q fragments, the merge and the O stores) is
+// larger, and two groups made it slower (seq-2048 causal 39 -> 43 us).
+constexpr int kAttnCUs = 256;
+inline int bwd_groups(bool causal, long workgroups) { return causal || workgroups <= kAttnCUs ? 2 : 1; }
 
 // two 16-row k-steps of a 32x32 accumulator as bf16 B operands:
 // step 0 = rows {4lg..4lg+3, 8+4lg..}, step 1 = rows {16+4lg.., 24+4lg..}
@@ -419,12 +422,11 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(int rows, int S, int 
 // Q^T come from the row-major Q and dO tiles by transpose reads. The K tile
 // stays in LDS for the whole walk, the wavefront's V rows in registers. The
 // groups' and then the two query halves' sums are added at the end.
-template <int D, bool CAUSAL, bool DROP>
-__global__ __launch_bounds__(256 * bwd_groups(CAUSAL), 2 / bwd_groups(CAUSAL)) void attn_bwd_dkdv_kernel(
+template <int D, bool CAUSAL, bool DROP, int G>
+__global__ __launch_bounds__(256 * G, 2 / G) void attn_bwd_dkdv_kernel(
     int S, int nq, int nkv, int ldq, const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO,
     const float* __restrict__ lse, const float* __restrict__ Dbuf, bf16_t* __restrict__ dqkv,
     float* __restrict__ part, float sl2, float scale, Drop drop) {
-  constexpr int G = bwd_groups(CAUSAL);
   constexpr int TILE = 64 * D;         // elements of one 64 x D tile
   constexpr int GRP = 2 * TILE + 256;  // one group's Q and dO tiles, log-sum-exp and D (64 floats each)
   __shared__ __attribute__((aligned(1024))) bf16_t smem[TILE + G * GRP];
@@ -643,12 +645,11 @@ __global__ __launch_bounds__(256) void attn_dkv_reduce_kernel(int B, int S, int 
 // double-buffered (tile t+1 in flight while tile t is used); K^T comes from
 // the K tile by transpose reads. The groups' and then the key halves' sums
 // are added at the end.
-template <int D, bool CAUSAL, bool DROP>
-__global__ __launch_bounds__(256 * bwd_groups(CAUSAL), 2 / bwd_groups(CAUSAL)) void attn_bwd_dq_kernel(
+template <int D, bool CAUSAL, bool DROP, int G>
+__global__ __launch_bounds__(256 * G, 2 / G) void attn_bwd_dq_kernel(
     int S, int nq, int nkv, int ldq, const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO,
     const float* __restrict__ lse, const float* __restrict__ Dbuf, bf16_t* __restrict__ dqkv, float sl2,
     float scale, Drop drop) {
-  constexpr int G = bwd_groups(CAUSAL);
   constexpr int TILE = 64 * D;
   constexpr int STAGE = 2 * TILE;  // K, V
   __shared__ __attribute__((aligned(1024))) bf16_t smem[G * 2 * STAGE];
@@ -939,17 +940,20 @@ hipError_t attn_bwd_bf16(int B, int S, int nq, int nkv, int causal, const void* 
   hipLaunchKernelGGL((attn_bwd_pre_kernel<bf16_t, D>), dim3((rows * (D / 8) + 255) / 256),
                      dim3(256), 0, st, rows, S, nq, (const bf16_t*)O, (const bf16_t*)dO, Dbuf);
   dim3 grid((S / 64) * B * nq);
-#define MTB_BWD(C, DR)                                                                        \
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, C, DR>), grid, dim3(256 * bwd_groups(C)), 0, st, S, nq, \
-                     nkv, ldq, (const bf16_t*)qkv, (const bf16_t*)dO, lse, Dbuf,             \
-                     (bf16_t*)dqkv, part, sl2, scale, drop);                                 \
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<D, C, DR>), grid, dim3(256 * bwd_groups(C)), 0, st, S, nq, \
-                     nkv, ldq, (const bf16_t*)qkv, (const bf16_t*)dO, lse, Dbuf,             \
-                     (bf16_t*)dqkv, sl2, scale, drop)
+  const int G = bwd_groups(causal != 0, (long)grid.x);
+#define MTB_BWD(C, DR, G)                                                                     \
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, C, DR, G>), grid, dim3(256 * G), 0, st, S, nq, nkv, \
+                     ldq, (const bf16_t*)qkv, (const bf16_t*)dO, lse, Dbuf, (bf16_t*)dqkv,   \
+                     part, sl2, scale, drop);                                                \
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<D, C, DR, G>), grid, dim3(256 * G), 0, st, S, nq, nkv, \
+                     ldq, (const bf16_t*)qkv, (const bf16_t*)dO, lse, Dbuf, (bf16_t*)dqkv,   \
+                     sl2, scale, drop)
   if (causal) {
-    if (drop.thr) { MTB_BWD(true, true); } else { MTB_BWD(true, false); }
+    if (drop.thr) { MTB_BWD(true, true, 2); } else { MTB_BWD(true, false, 2); }
+  } else if (G == 2) {
+    if (drop.thr) { MTB_BWD(false, true, 2); } else { MTB_BWD(false, false, 2); }
   } else {
-    if (drop.thr) { MTB_BWD(false, true); } else { MTB_BWD(false, false); }
+    if (drop.thr) { MTB_BWD(false, true, 1); } else { MTB_BWD(false, false, 1); }
   }
 #undef MTB_BWD
   if (nq != nkv) {
