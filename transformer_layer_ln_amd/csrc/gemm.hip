@@ -1243,13 +1243,15 @@ PairPlan pair_plan(int M0, int N0, int K0, int lda0, int ldb0, int M1, int N1, i
     while (s1 < 8 && K1 / s1 > K0 / a.splits) s1 *= 2;
     consider(a.splits, s1);
   }
-  // Products too small for the 256 x 256 pair (the seq-512 share's 1024-wide
-  // weight gradients): the 128 x 128 scheduled tiles, two blocks per CU, both
-  // contractions split the same way into parts at least 512 deep, with at
-  // least one block for every CU and at most two. In the cost units above a
-  // 128 x 128 k-tile counts 1/3 of a 256 x 256 one (a quarter of its work at
-  // a lower rate), per block a CU holds.
-  if (!best.ok) {
+  // Products too small for the scheduled 256 x 256 tiles, alone or paired
+  // (the seq-512 share's 1024-wide weight gradients): the 128 x 128
+  // scheduled tiles, two blocks per CU, both contractions split the same way
+  // into parts at least 512 deep, with at least one block for every CU and at
+  // most two. In the cost units above a 128 x 128 k-tile counts 1/3 of a 256
+  // x 256 one (a quarter of its work at a lower rate), per block a CU holds.
+  // Products that run on the 256 x 256 tiles alone stay there (the seq-4096
+  // share's QKV and projection weight gradients: 13 us faster alone).
+  if (!best.ok && a.tile != TSCHED && b.tile != TSCHED) {
     const long u0 = tiles(M0, N0, 128, 128), u1 = tiles(M1, N1, 128, 128);
     for (int sp = 1; sp <= 8; sp *= 2) {
       if (K0 % (sp * SBK) != 0 || K1 % (sp * SBK) != 0 || K0 / sp < 512 || K1 / sp < 512) continue;
