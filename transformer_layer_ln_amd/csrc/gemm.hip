@@ -1120,9 +1120,12 @@ Plan plan(int M, int N, int K, bool a_kc, bool b_kc, int kind, bool split_ok, bo
   // data gradient: 64 tiles): the scheduled kernel on the contraction split
   // 2-4 ways into parts at least 1024 deep, then one pass that sums the
   // partial tiles and runs the epilogue
-  // (not where the scheduled 128 x 128 tiles alone give every CU a block:
-  // the 8192 x 512 x 4096 projection dgrad, 49 + 13 -> 59 us)
-  const bool fill128 = K % SBK == 0 && t128 >= kCUs;
+  // (not where the 256 x 256 tiles fill at most a quarter of the chip and
+  // the scheduled 128 x 128 tiles alone give every CU a block: the 8192 x
+  // 512 x 4096 projection dgrad, split 4 ways 49 + 13 -> 59 us; the 8192 x
+  // 768 x 4096 QKV forward of the seq-4096 share stays split two ways, 63 +
+  // 12 against 78 us)
+  const bool fill128 = K % SBK == 0 && t128 >= kCUs && 4 * t256 <= kCUs;
   if (split_ok && a_kc && kind == EPI_STORE && 2 * t256 <= kCUs && K % SBK == 0 && !fill128) {
     int s = 1;
     while (s < 4 && t256 * s * 2 <= kCUs && sched_depth(2 * s)) s *= 2;
