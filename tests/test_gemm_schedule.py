@@ -525,7 +525,8 @@ def test_shapes64_fit():
     """Two 64-deep stages in a CU's LDS (no more than four 32-deep ones, the
     epilogue's staging area), wait counts and read offsets in their fields."""
     for sh in GEN.SHAPES64:
-        assert sh.stages * sh.stage_bytes <= 160 * 1024 and sh.frag_lo >= 64
+        assert sh.stages * sh.stage_bytes <= 160 * 1024 and sh.frag_lo >= sh.frag_top // 4
+        assert sh.frag_top == 256 * 4 // sh.waves
         assert sh.cpt <= 63
         assert sh.read_offset("kc", 0, 3, sh.fm - 1) < 65536
         assert sh.read_offset("mn", 1, 3, sh.fn - 1, 1) < 65536

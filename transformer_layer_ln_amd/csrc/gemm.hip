@@ -770,22 +770,15 @@ struct Sched {
 // us) and the same on the weight gradients
 constexpr int kShMain = SH256W8;
 
-// One block's tile (bt) of the product: the k-loop and the epilogue. smem is
-// the block's Sched<SH>::SMEM-element LDS array (1-KB aligned).
-template <int SH, bool AKC, bool BKC, int EPI>
-MTB_DEV void sched_tile(bf16_t* smem, int M, int N, int K, const bf16_t* __restrict__ A, int lda,
-                        const bf16_t* __restrict__ B, int ldb, const Epi& ep, int ksplit,
-                        const BlockTile& bt) {
+// The 32-deep loop: copies and fragment bases for the layout of
+// gen_gemm_loop.py's Shape (4 stages), then its asm block.
+template <int SH, bool AKC, bool BKC>
+MTB_DEV void sched_loop32(f32x16 (&acc)[Sched<SH>::FM][Sched<SH>::FN], uint32_t lds, int M, int N,
+                          const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ B, int ldb,
+                          int kbeg, int kspan, int m0, int n0, int wave, int wm, int wn, int lane) {
   using G = Sched<SH>;
   constexpr int BM = G::BM, BN = G::BN, FM = G::FM, FN = G::FN;
   constexpr uint32_t B_OFF = BM * SBK * 2;  // operand B follows A inside a stage (bytes)
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / G::WGN, wn = wave % G::WGN;
-  const int kspan = K / ksplit, kbeg = bt.split * kspan;
-  const int m0 = bt.tm * BM, n0 = bt.tn * BN;
-  const uint32_t lds = (uint32_t)(uintptr_t)smem;
-
   // Copies: this wavefront's blocks Q wave + q (q < Q) of 1 KB per operand and
   // k-tile; lane l writes bytes [16 l, 16 l + 16) of its block.
   // k-contiguous: block = 16 rows x 64 bytes; row r's chunk c sits at c ^ ((r >> 2) & 3).
@@ -846,13 +839,6 @@ MTB_DEV void sched_tile(bf16_t* smem, int M, int N, int K, const bf16_t* __restr
   const int first = (G::SLOTS - KT % G::SLOTS) % G::SLOTS;  // body slot of k-tile 0
   int rem = KT - 1, iters = (KT + first) / G::SLOTS;
   uint32_t ta, tb;
-  f32x16 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 #define MTB_ACC_ROW(I)                                                                             \
   [c##I##0] "+a"(acc[I][0]), [c##I##1] "+a"(acc[I][1])
 #define MTB_LOOP_COMMON                                                                            \
@@ -937,6 +923,139 @@ MTB_DEV void sched_tile(bf16_t* smem, int M, int N, int K, const bf16_t* __restr
 #pragma clang diagnostic pop
 #undef MTB_LOOP_COMMON
 #undef MTB_ACC_ROW
+}
+
+// The 64-deep loop of the 8-wavefront tile (contractions that are a multiple
+// of 64): two stages of [A BM x 64 | B BN x 64] in the same LDS as four
+// 32-deep ones, so that a k-contiguous operand's copies move whole 128-byte
+// lines (8 rows x 128 bytes per instruction) and the L2 serves half the
+// requests of the 32-deep loop's 64-byte ones; copies and fragment bases for
+// gen_gemm_loop.py's Shape64, then its asm block.
+template <int SH, bool AKC, bool BKC>
+MTB_DEV void sched_loop64(f32x16 (&acc)[Sched<SH>::FM][Sched<SH>::FN], uint32_t lds, int M, int N,
+                          const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ B, int ldb,
+                          int kbeg, int kspan, int m0, int n0, int wave, int wm, int wn, int lane) {
+  static_assert(SH == SH256W8, "the 64-deep loop is built for the 8-wavefront tile");
+  using G = Sched<SH>;
+  constexpr int BM = G::BM, BN = G::BN, FM = G::FM, FN = G::FN;
+  constexpr uint32_t ST = (BM + BN) * 128, B_OFF = BM * 128;   // stage and operand-B offsets (bytes)
+  constexpr int QA = BM * 128 / 1024 / G::WAVES, QB = BN * 128 / 1024 / G::WAVES;
+  // Copies: this wavefront's blocks Q wave + q (q < Q) of 1 KB per operand and
+  // k-tile; lane l writes bytes [16 l, 16 l + 16) of its block.
+  // k-contiguous: block = 8 rows x 128 bytes (whole cache lines); row r's
+  //               chunk j sits at j ^ ((r >> 1) & 7).
+  // otherwise:    block = 1024 / (2 ROWS) k-rows of 2 ROWS bytes; k-row k's chunk c sits at
+  //               c ^ ((k & 3) << 2).
+  auto copy_off = [&](bool kc, int b, int row0, int rows, int ld, int ROWS) -> uint32_t {
+    if (kc) {
+      const int r = 8 * b + (lane >> 3), j = (lane & 7) ^ ((r >> 1) & 7);
+      return ((uint32_t)min(row0 + r, rows - 1) * (uint32_t)ld + j * 8) * 2u;
+    }
+    const int cpr = ROWS / 8, kpb = 64 / cpr;
+    const int k = kpb * b + lane / cpr, c = (lane % cpr) ^ ((k & 3) << 2);
+    return ((uint32_t)k * (uint32_t)ld + (uint32_t)min(row0 + c * 8, rows - 8)) * 2u;
+  };
+  uint32_t voA[QA], voB[QB];
+#pragma unroll
+  for (int q = 0; q < QA; ++q) voA[q] = copy_off(AKC, QA * wave + q, m0, M, lda, BM);
+#pragma unroll
+  for (int q = 0; q < QB; ++q) voB[q] = copy_off(BKC, QB * wave + q, n0, N, ldb, BN);
+  const uint64_t sbA = (uint64_t)(A + (AKC ? (size_t)kbeg : (size_t)kbeg * lda));
+  const uint64_t sbB = (uint64_t)(B + (BKC ? (size_t)kbeg : (size_t)kbeg * ldb));
+  const uint32_t ksA = AKC ? 128u : 128u * (uint32_t)lda;
+  const uint32_t ksB = BKC ? 128u : 128u * (uint32_t)ldb;
+  const uint32_t ldsA = __builtin_amdgcn_readfirstlane(lds + wave * QA * 1024);
+  const uint32_t ldsB = __builtin_amdgcn_readfirstlane(lds + B_OFF + wave * QB * 1024);
+
+  // Fragment base addresses, one per stage and: step s (k-contiguous; its
+  // fragment i is 32 rows = 4 KB further) or fragment i (otherwise; step s
+  // is 16 k-rows further, a fragment's second half 4 k-rows).
+  constexpr int NA = 2 * (AKC ? 4 : FM), NB = 2 * (BKC ? 4 : FN);
+  auto frag_bases = [&](bool kc, int w, uint32_t off, int F, int ROWS, uint32_t* f) {
+    if (kc) {
+      const int r = w * 32 * F + (lane & 31);
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int j = 2 * q + (lane >> 5);
+          f[4 * st + q] = lds + off + st * ST + r * 128 + ((j ^ ((r >> 1) & 7)) << 4);
+        }
+    } else {
+      const int g = lane >> 4, sl = lane & 15, k = 8 * (g >> 1) + (sl >> 2);
+#pragma unroll
+      for (int i = 0; i < F; ++i) {
+        const int m = w * 32 * F + 32 * i + 16 * (g & 1) + 4 * (sl & 3);
+        const uint32_t b0 = lds + off + (k * ROWS + ((m >> 3) ^ ((k & 3) << 2)) * 8 + (m & 7)) * 2;
+#pragma unroll
+        for (int st = 0; st < 2; ++st) f[F * st + i] = b0 + st * ST;
+      }
+    }
+  };
+  uint32_t fa[NA], fb[NB];
+  frag_bases(AKC, wm, 0, FM, BM, fa);
+  frag_bases(BKC, wn, B_OFF, FN, BN, fb);
+
+  const int KT = kspan / 64;
+  const int first = KT & 1;  // body slot of k-tile 0 (-KT mod 2)
+  int rem = KT - 1, iters = (KT + first) / 2;
+  uint32_t ta, tb;
+  static_assert(NA == 8 && (NB == 8 || NB == 4), "two stages of 4 steps or of 2-4 fragments");
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+#define MTB_LOOP_OPERANDS                                                                          \
+  : [c00] "+a"(acc[0][0]), [c01] "+a"(acc[0][1]), [c10] "+a"(acc[1][0]), [c11] "+a"(acc[1][1]),    \
+    [c20] "+a"(acc[2][0]), [c21] "+a"(acc[2][1]), [c30] "+a"(acc[3][0]), [c31] "+a"(acc[3][1]),    \
+    [voA0] "+v"(voA[0]), [voA1] "+v"(voA[1]), [voA2] "+v"(voA[2]), [voA3] "+v"(voA[3]),            \
+    [voB0] "+v"(voB[0]), [voB1] "+v"(voB[1]), [voB2] "+v"(voB[2]), [voB3] "+v"(voB[3]),            \
+    [rem] "+s"(rem), [iters] "+s"(iters), [ta] "=&s"(ta), [tb] "=&s"(tb)                           \
+  : [ldsA] "s"(ldsA), [ldsB] "s"(ldsB), [sbA] "s"(sbA), [sbB] "s"(sbB), [ksA] "s"(ksA),            \
+    [ksB] "s"(ksB), [first] "s"(first),                                                            \
+    [fa0] "v"(fa[0]), [fa1] "v"(fa[1]), [fa2] "v"(fa[2]), [fa3] "v"(fa[3]),                        \
+    [fa4] "v"(fa[4]), [fa5] "v"(fa[5]), [fa6] "v"(fa[6]), [fa7] "v"(fa[7]),                        \
+    [fb0] "v"(fb[0]), [fb1] "v"(fb[1]), [fb2] "v"(fb[2]), [fb3] "v"(fb[3]),                        \
+    [fb4] "v"(fb[NB > 4 ? 4 : 0]), [fb5] "v"(fb[NB > 5 ? 5 : 0]), [fb6] "v"(fb[NB > 6 ? 6 : 0]),   \
+    [fb7] "v"(fb[NB > 7 ? 7 : 0])                                                                  \
+  : "memory", "m0", "scc"
+  static_assert(AKC && BKC, "the 64-deep loop is built for k-contiguous operands");
+  asm volatile(MTB_GEMM_LOOP64_NT_W8 MTB_LOOP_OPERANDS, MTB_GEMM_LOOP_CLOBBERS64_NT_W8);
+#undef MTB_LOOP_OPERANDS
+#pragma clang diagnostic pop
+}
+
+// One block's tile (bt) of the product: the k-loop and the epilogue. smem is
+// the block's Sched<SH>::SMEM-element LDS array (1-KB aligned).
+template <int SH, bool AKC, bool BKC, int EPI>
+MTB_DEV void sched_tile(bf16_t* smem, int M, int N, int K, const bf16_t* __restrict__ A, int lda,
+                        const bf16_t* __restrict__ B, int ldb, const Epi& ep, int ksplit,
+                        const BlockTile& bt) {
+  using G = Sched<SH>;
+  constexpr int BM = G::BM, BN = G::BN, FM = G::FM, FN = G::FN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / G::WGN, wn = wave % G::WGN;
+  const int kspan = K / ksplit, kbeg = bt.split * kspan;
+  const int m0 = bt.tm * BM, n0 = bt.tn * BN;
+  const uint32_t lds = (uint32_t)(uintptr_t)smem;
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  // the 64-deep loop where both operands are k-contiguous (both then copy
+  // whole lines: fc1 forward 116.6 -> 109.0 us in a standalone run); with a
+  // transposed operand, whose copies are whole lines in either loop, it was
+  // 2-8 % slower (fc1 dgrad 119 -> 122 us, a weight gradient 130 -> 140 us)
+  bool done = false;
+  if constexpr (SH == SH256W8 && AKC && BKC) {
+    if (kspan % 64 == 0) {
+      sched_loop64<SH, AKC, BKC>(acc, lds, M, N, A, lda, B, ldb, kbeg, kspan, m0, n0, wave, wm, wn, lane);
+      done = true;
+    }
+  }
+  if (!done) sched_loop32<SH, AKC, BKC>(acc, lds, M, N, A, lda, B, ldb, kbeg, kspan, m0, n0, wave, wm, wn, lane);
   __syncthreads();
   gemm_epilogue<BM, BN, 2, G::WGN, G::SMEM / 2, AKC, EPI, true>(acc, smem, ep, M, N, m0, n0, bt, wm, wn,
                                                                 lane, tid);

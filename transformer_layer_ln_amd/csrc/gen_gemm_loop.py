@@ -366,20 +366,22 @@ def loop(la, lb, reads_first=False, copies_step=0, early=0, order="row", sh=S256
 # KT64 tiles enters the two-slot body at slot (-KT64 mod 2).
 
 class Shape64:
-    """The 64-deep variant of a block tile of 2 x 2 wavefronts with FM x FN
-    accumulators; fragment reads run ra steps ahead of their MFMAs (nbuf
-    register sets)."""
+    """The 64-deep variant of a block tile of 2 x (waves / 2) wavefronts with
+    FM x FN accumulators; fragment reads run ra steps ahead of their MFMAs
+    (nbuf register sets)."""
 
-    def __init__(self, name, fm, fn, ra=1, frag_top=256):
+    def __init__(self, name, fm, fn, ra=1, frag_top=256, waves=4):
         self.name, self.fm, self.fn = name, fm, fn
         self.direct = None                # both operands through LDS
-        self.bm, self.bn = 64 * fm, 64 * fn
+        self.waves, self.frag_top, self.per_cu = waves, frag_top, 1
+        self.bm, self.bn = 64 * fm, 32 * (waves // 2) * fn
         self.stages, self.steps, self.slots = 2, 4, 2
         self.a_bytes, self.b_bytes = self.bm * 128, self.bn * 128
         self.stage_bytes = self.a_bytes + self.b_bytes
         self.b_offset = self.a_bytes
         # copy blocks (1 KB) per wavefront and k-tile
-        self.qa, self.qb = self.bm // 32, self.bn // 32
+        self.qa, self.qb = self.a_bytes // 1024 // waves, self.b_bytes // 1024 // waves
+        assert self.qa * 1024 * waves == self.a_bytes and self.qb * 1024 * waves == self.b_bytes
         self.cpt = self.qa + self.qb
         assert ra in (1, 2)
         self.ra = ra
@@ -417,7 +419,8 @@ class Shape64:
 
 S256_64 = Shape64("256", 4, 4, ra=2)
 S192_64 = Shape64("192", 4, 3, ra=2)
-SHAPES64 = (S256_64, S192_64)
+S256W8_64 = Shape64("w8", 4, 2, ra=1, frag_top=128, waves=8)
+SHAPES64 = (S256_64, S192_64, S256W8_64)
 
 
 def reads64(sh, layout, op, buf, stage, step):
@@ -510,7 +513,7 @@ def render():
             out.append(f'  "{line}\\n" \\')
         out.append("")
         regs = ", ".join(f'"v{r}"' for r in range(lo, hi))
-        out.append(f"#define {name.replace('_LOOP', '_LOOP_CLOBBERS')} {regs}")
+        out.append(f"#define {name.replace('_LOOP', '_LOOP_CLOBBERS', 1)} {regs}")
         out.append("")
 
     for sh in SHAPES:
@@ -518,6 +521,11 @@ def render():
         for name, la, lb in SHAPE_LAYOUTS[sh.name]:
             v = shape_for(sh, la, lb)
             block(f"MTB_GEMM_LOOP_{name}{suffix}", loop(la, lb, sh=sh), v.frag_lo, v.frag_hi)
+    # the 64-deep loop of the 8-wavefront 256 x 256 tile (contractions that are a
+    # multiple of 64, both operands k-contiguous)
+    for name, la, lb in LAYOUTS[:1]:
+        block(f"MTB_GEMM_LOOP64_{name}_W8", loop64(la, lb, sh=S256W8_64), S256W8_64.frag_lo,
+              S256W8_64.frag_hi)
     return "\n".join(out)
 
 
