@@ -339,15 +339,18 @@ def loop(la, lb, reads_first=False, copies_step=0, early=0, order="row", sh=S256
 
 
 # ---------------------------------------------------------------------------
-# 64-deep k-tiles (loop64), a measurement variant (not built into the
-# kernels): a 32-deep tile of a k-contiguous operand is 64 bytes of each row,
-# so its copies (16 rows x 64 bytes per instruction) ask the L2 for half cache
-# lines; a 64-deep tile copies whole 128-byte lines (8 rows x 128 bytes per
-# instruction) and halves the requests. Measured against the 32-deep loop it
-# was no faster for the 8192 x 2048 x 4096 product with both operands
-# k-contiguous and 3-12 % slower for the others (one tile of copy lead in two
-# stages, reads one step ahead); reading two steps ahead shortens the copy
-# lead to three steps and was slower still. Two stages of [A BM x 64 | B BN x
+# 64-deep k-tiles (loop64): a 32-deep tile of a k-contiguous operand is 64
+# bytes of each row, so its copies (16 rows x 64 bytes per instruction) ask
+# the L2 for half cache lines; a 64-deep tile copies whole 128-byte lines (8
+# rows x 128 bytes per instruction) and halves the requests. Built for the
+# 8-wavefront 256 x 256 tile with both operands k-contiguous (S256W8_64,
+# reads one step ahead): 6-7 % faster than its 32-deep loop there, where the
+# L2's request rate limits the copies; with a transposed operand (whose
+# copies move whole lines in either loop) 2-8 % slower, and reading two steps
+# ahead was no faster. On the 4-wavefront tiles (S256_64, S192_64, kept as
+# measurement variants) it was no faster for the 8192 x 2048 x 4096 product
+# and 3-12 % slower for the others: one wavefront per SIMD stalls on the
+# step waits before the request rate matters. Two stages of [A BM x 64 | B BN x
 # 64] (the same LDS as four 32-deep stages), four 16-deep steps per tile:
 #   - a k-contiguous operand sits as [row][64 k], 16-byte chunk j of row r at
 #     chunk j ^ ((r >> 1) & 7) (conflict-free for 128-bit reads: 16 rows of
