@@ -745,16 +745,22 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_bf16_kernel(int M, i
 //            copies, fragment reads or the barrier;
 //   SH128:   128 x 128 on 4 wavefronts of 64 x 64, two blocks per CU (64 KB
 //            of LDS each): for products whose larger tiles leave CUs idle,
-//            one block's first copies and epilogue overlap the other's loop.
+//            one block's first copies and epilogue overlap the other's loop;
+//   SH192W8: 256 x 192 on 8 wavefronts (4 x 2) of 64 x 96, k-contiguous
+//            operands and contractions that are a multiple of 64 only (the
+//            64-deep loop: its B tile's 24 copy blocks split over 8
+//            wavefronts, the 32-deep tile's 12 do not).
 // Needs each split's contraction to be a multiple of 32 and every operand
 // byte offset below 2^32 (sched_ok).
 constexpr int SBK = 32;
-enum SchedShape { SH256 = 0, SH192 = 1, SH256W8 = 2, SH128 = 3 };
+enum SchedShape { SH256 = 0, SH192 = 1, SH256W8 = 2, SH128 = 3, SH192W8 = 4 };
 template <int SH>
 struct Sched {
-  static constexpr int WAVES = SH == SH256W8 ? 8 : 4, WGN = WAVES / 2;
-  static constexpr int FM = SH == SH128 ? 2 : 4, FN = SH == SH256 ? 4 : SH == SH192 ? 3 : 2;
-  static constexpr int BM = 64 * FM, BN = 32 * WGN * FN;
+  static constexpr int WAVES = SH == SH256W8 || SH == SH192W8 ? 8 : 4;
+  static constexpr int WGN = SH == SH192W8 ? 2 : WAVES / 2, WGM = WAVES / WGN;  // wavefront grid
+  static constexpr int FM = SH == SH128 || SH == SH192W8 ? 2 : 4;
+  static constexpr int FN = SH == SH256 ? 4 : SH == SH192 || SH == SH192W8 ? 3 : 2;
+  static constexpr int BM = 32 * WGM * FM, BN = 32 * WGN * FN;
   static constexpr int STAGES = 4;
   static constexpr int SLOTS = STAGES;                 // loop body slots (gen_gemm_loop.py)
   static constexpr int PER_CU = SH == SH128 ? 2 : 1;
@@ -935,7 +941,7 @@ template <int SH, bool AKC, bool BKC>
 MTB_DEV void sched_loop64(f32x16 (&acc)[Sched<SH>::FM][Sched<SH>::FN], uint32_t lds, int M, int N,
                           const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ B, int ldb,
                           int kbeg, int kspan, int m0, int n0, int wave, int wm, int wn, int lane) {
-  static_assert(SH == SH256W8, "the 64-deep loop is built for the 8-wavefront tile");
+  static_assert(SH == SH256W8 || SH == SH192W8, "the 64-deep loop is built for the 8-wavefront tiles");
   using G = Sched<SH>;
   constexpr int BM = G::BM, BN = G::BN, FM = G::FM, FN = G::FN;
   constexpr uint32_t ST = (BM + BN) * 128, B_OFF = BM * 128;   // stage and operand-B offsets (bytes)
@@ -1000,26 +1006,33 @@ MTB_DEV void sched_loop64(f32x16 (&acc)[Sched<SH>::FM][Sched<SH>::FN], uint32_t 
   const int first = KT & 1;  // body slot of k-tile 0 (-KT mod 2)
   int rem = KT - 1, iters = (KT + first) / 2;
   uint32_t ta, tb;
-  static_assert(NA == 8 && (NB == 8 || NB == 4), "two stages of 4 steps or of 2-4 fragments");
+  static_assert(AKC && BKC && NA == 8 && NB == 8, "the 64-deep loop is built for k-contiguous operands");
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-#define MTB_LOOP_OPERANDS                                                                          \
-  : [c00] "+a"(acc[0][0]), [c01] "+a"(acc[0][1]), [c10] "+a"(acc[1][0]), [c11] "+a"(acc[1][1]),    \
-    [c20] "+a"(acc[2][0]), [c21] "+a"(acc[2][1]), [c30] "+a"(acc[3][0]), [c31] "+a"(acc[3][1]),    \
-    [voA0] "+v"(voA[0]), [voA1] "+v"(voA[1]), [voA2] "+v"(voA[2]), [voA3] "+v"(voA[3]),            \
-    [voB0] "+v"(voB[0]), [voB1] "+v"(voB[1]), [voB2] "+v"(voB[2]), [voB3] "+v"(voB[3]),            \
+#define MTB_LOOP_COMMON                                                                            \
     [rem] "+s"(rem), [iters] "+s"(iters), [ta] "=&s"(ta), [tb] "=&s"(tb)                           \
   : [ldsA] "s"(ldsA), [ldsB] "s"(ldsB), [sbA] "s"(sbA), [sbB] "s"(sbB), [ksA] "s"(ksA),            \
     [ksB] "s"(ksB), [first] "s"(first),                                                            \
     [fa0] "v"(fa[0]), [fa1] "v"(fa[1]), [fa2] "v"(fa[2]), [fa3] "v"(fa[3]),                        \
     [fa4] "v"(fa[4]), [fa5] "v"(fa[5]), [fa6] "v"(fa[6]), [fa7] "v"(fa[7]),                        \
     [fb0] "v"(fb[0]), [fb1] "v"(fb[1]), [fb2] "v"(fb[2]), [fb3] "v"(fb[3]),                        \
-    [fb4] "v"(fb[NB > 4 ? 4 : 0]), [fb5] "v"(fb[NB > 5 ? 5 : 0]), [fb6] "v"(fb[NB > 6 ? 6 : 0]),   \
-    [fb7] "v"(fb[NB > 7 ? 7 : 0])                                                                  \
+    [fb4] "v"(fb[4]), [fb5] "v"(fb[5]), [fb6] "v"(fb[6]), [fb7] "v"(fb[7])                         \
   : "memory", "m0", "scc"
-  static_assert(AKC && BKC, "the 64-deep loop is built for k-contiguous operands");
-  asm volatile(MTB_GEMM_LOOP64_NT_W8 MTB_LOOP_OPERANDS, MTB_GEMM_LOOP_CLOBBERS64_NT_W8);
-#undef MTB_LOOP_OPERANDS
+  if constexpr (SH == SH256W8)
+    asm volatile(MTB_GEMM_LOOP64_NT_W8
+                 : [c00] "+a"(acc[0][0]), [c01] "+a"(acc[0][1]), [c10] "+a"(acc[1][0]), [c11] "+a"(acc[1][1]),
+                   [c20] "+a"(acc[2][0]), [c21] "+a"(acc[2][1]), [c30] "+a"(acc[3][0]), [c31] "+a"(acc[3][1]),
+                   [voA0] "+v"(voA[0]), [voA1] "+v"(voA[1]), [voA2] "+v"(voA[2]), [voA3] "+v"(voA[3]),
+                   [voB0] "+v"(voB[0]), [voB1] "+v"(voB[1]), [voB2] "+v"(voB[2]), [voB3] "+v"(voB[3]),
+                   MTB_LOOP_COMMON, MTB_GEMM_LOOP_CLOBBERS64_NT_W8);
+  else
+    asm volatile(MTB_GEMM_LOOP64_NT_192W8
+                 : [c00] "+a"(acc[0][0]), [c01] "+a"(acc[0][1]), [c02] "+a"(acc[0][2]),
+                   [c10] "+a"(acc[1][0]), [c11] "+a"(acc[1][1]), [c12] "+a"(acc[1][2]),
+                   [voA0] "+v"(voA[0]), [voA1] "+v"(voA[1]), [voA2] "+v"(voA[2]), [voA3] "+v"(voA[3]),
+                   [voB0] "+v"(voB[0]), [voB1] "+v"(voB[1]), [voB2] "+v"(voB[2]),
+                   MTB_LOOP_COMMON, MTB_GEMM_LOOP_CLOBBERS64_NT_192W8);
+#undef MTB_LOOP_COMMON
 #pragma clang diagnostic pop
 }
 
@@ -1048,17 +1061,23 @@ MTB_DEV void sched_tile(bf16_t* smem, int M, int N, int K, const bf16_t* __restr
   // whole lines: fc1 forward 116.6 -> 109.0 us in a standalone run); with a
   // transposed operand, whose copies are whole lines in either loop, it was
   // 2-8 % slower (fc1 dgrad 119 -> 122 us, a weight gradient 130 -> 140 us)
-  bool done = false;
-  if constexpr (SH == SH256W8 && AKC && BKC) {
-    if (kspan % 64 == 0) {
-      sched_loop64<SH, AKC, BKC>(acc, lds, M, N, A, lda, B, ldb, kbeg, kspan, m0, n0, wave, wm, wn, lane);
-      done = true;
+  if constexpr (SH == SH192W8) {
+    // launched only for contractions that are a multiple of 64 (launch_bf16)
+    sched_loop64<SH, AKC, BKC>(acc, lds, M, N, A, lda, B, ldb, kbeg, kspan, m0, n0, wave, wm, wn, lane);
+  } else {
+    bool done = false;
+    if constexpr (SH == SH256W8 && AKC && BKC) {
+      if (kspan % 64 == 0) {
+        sched_loop64<SH, AKC, BKC>(acc, lds, M, N, A, lda, B, ldb, kbeg, kspan, m0, n0, wave, wm, wn, lane);
+        done = true;
+      }
     }
+    if (!done)
+      sched_loop32<SH, AKC, BKC>(acc, lds, M, N, A, lda, B, ldb, kbeg, kspan, m0, n0, wave, wm, wn, lane);
   }
-  if (!done) sched_loop32<SH, AKC, BKC>(acc, lds, M, N, A, lda, B, ldb, kbeg, kspan, m0, n0, wave, wm, wn, lane);
   __syncthreads();
-  gemm_epilogue<BM, BN, 2, G::WGN, G::SMEM / 2, AKC, EPI, true>(acc, smem, ep, M, N, m0, n0, bt, wm, wn,
-                                                                lane, tid);
+  gemm_epilogue<BM, BN, G::WGM, G::WGN, G::SMEM / 2, AKC, EPI, true>(acc, smem, ep, M, N, m0, n0, bt, wm,
+                                                                     wn, lane, tid);
 }
 
 template <int SH, bool AKC, bool BKC, int EPI>
@@ -1403,7 +1422,8 @@ hipError_t launch_bf16(int M, int N, int K, const void* A, int lda, const void* 
   if (pl.tile == TSCHED192) {
     if constexpr (AKC && BKC) {
       if (sched_ok(M, N, K, AKC, lda, BKC, ldb, 1))
-        return launch_sched<SH192, AKC, BKC, EPI>(M, N, K, A, lda, B, ldb, e, st);
+        return K % 64 == 0 ? launch_sched<SH192W8, AKC, BKC, EPI>(M, N, K, A, lda, B, ldb, e, st)
+                           : launch_sched<SH192, AKC, BKC, EPI>(M, N, K, A, lda, B, ldb, e, st);
       if constexpr (EPI == EPI_STORE) return launch_cfg<256, 192, 4, 2, 1, AKC, BKC, EPI>(M, N, K, A, lda, B, ldb, e, st);
     }
     return launch_cfg<256, 256, 2, 4, 1, AKC, BKC, EPI>(M, N, K, A, lda, B, ldb, e, st);

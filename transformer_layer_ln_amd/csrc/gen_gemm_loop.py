@@ -369,15 +369,15 @@ def loop(la, lb, reads_first=False, copies_step=0, early=0, order="row", sh=S256
 # KT64 tiles enters the two-slot body at slot (-KT64 mod 2).
 
 class Shape64:
-    """The 64-deep variant of a block tile of 2 x (waves / 2) wavefronts with
-    FM x FN accumulators; fragment reads run ra steps ahead of their MFMAs
-    (nbuf register sets)."""
+    """The 64-deep variant of a block tile of wr x (waves / wr) wavefronts
+    with FM x FN accumulators; fragment reads run ra steps ahead of their
+    MFMAs (nbuf register sets)."""
 
-    def __init__(self, name, fm, fn, ra=1, frag_top=256, waves=4):
+    def __init__(self, name, fm, fn, ra=1, frag_top=256, waves=4, wr=2):
         self.name, self.fm, self.fn = name, fm, fn
         self.direct = None                # both operands through LDS
         self.waves, self.frag_top, self.per_cu = waves, frag_top, 1
-        self.bm, self.bn = 64 * fm, 32 * (waves // 2) * fn
+        self.bm, self.bn = 32 * wr * fm, 32 * (waves // wr) * fn
         self.stages, self.steps, self.slots = 2, 4, 2
         self.a_bytes, self.b_bytes = self.bm * 128, self.bn * 128
         self.stage_bytes = self.a_bytes + self.b_bytes
@@ -423,7 +423,11 @@ class Shape64:
 S256_64 = Shape64("256", 4, 4, ra=2)
 S192_64 = Shape64("192", 4, 3, ra=2)
 S256W8_64 = Shape64("w8", 4, 2, ra=1, frag_top=128, waves=8)
-SHAPES64 = (S256_64, S192_64, S256W8_64)
+# 256 x 192 on 8 wavefronts (4 x 2, 64 x 96 each): its B tile is 24 copy
+# blocks of 8 rows, three per wavefront (the 32-deep tile's 12 blocks of 16
+# rows do not split over 8)
+S192W8_64 = Shape64("192w8", 2, 3, ra=1, frag_top=128, waves=8, wr=4)
+SHAPES64 = (S256_64, S192_64, S256W8_64, S192W8_64)
 
 
 def reads64(sh, layout, op, buf, stage, step):
@@ -503,7 +507,7 @@ def loop64(la, lb, sh=S256_64, order="row"):
 LAYOUTS = (("NT", "kc", "kc"), ("NN", "kc", "mn"), ("TN", "mn", "mn"))
 # which layouts each shape is built for: 256 x 192 only for the 1536-wide
 # forward products (both operands k-contiguous)
-SHAPE_LAYOUTS = {"256": LAYOUTS, "192": LAYOUTS[:1], "w8": LAYOUTS, "128": LAYOUTS}
+SHAPE_LAYOUTS = {"256": LAYOUTS, "192": LAYOUTS[:1], "w8": LAYOUTS, "128": LAYOUTS, "192w8": LAYOUTS[:1]}
 
 
 def render():
@@ -526,9 +530,9 @@ def render():
             block(f"MTB_GEMM_LOOP_{name}{suffix}", loop(la, lb, sh=sh), v.frag_lo, v.frag_hi)
     # the 64-deep loop of the 8-wavefront 256 x 256 tile (contractions that are a
     # multiple of 64, both operands k-contiguous)
-    for name, la, lb in LAYOUTS[:1]:
-        block(f"MTB_GEMM_LOOP64_{name}_W8", loop64(la, lb, sh=S256W8_64), S256W8_64.frag_lo,
-              S256W8_64.frag_hi)
+    for sh in (S256W8_64, S192W8_64):
+        name, la, lb = LAYOUTS[0]
+        block(f"MTB_GEMM_LOOP64_{name}_{sh.name.upper()}", loop64(la, lb, sh=sh), sh.frag_lo, sh.frag_hi)
     return "\n".join(out)
 
 
