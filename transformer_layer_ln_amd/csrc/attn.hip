@@ -420,8 +420,12 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(int rows, int S, int 
 // 64-query tile. S = Q K^T puts a key per lane, so P and dS feed
 // dV^T += dO^T P^T and dK^T += Q^T dS^T straight from registers; dO^T and
 // Q^T come from the row-major Q and dO tiles by transpose reads. The K tile
-// stays in LDS for the whole walk, the wavefront's V rows in registers. The
-// groups' and then the two query halves' sums are added at the end.
+// stays in LDS for the whole walk, the wavefront's V rows in registers. With
+// two workgroups per CU a group's Q and dO tiles are single-buffered (80 KB
+// of LDS per workgroup allows no more; the other workgroup covers the copy);
+// with two groups in one workgroup, whose barriers are shared, they are
+// double-buffered (tile t+1 in flight while tile t is used). The groups' and
+// then the two query halves' sums are added at the end.
 template <int D, bool CAUSAL, bool DROP, int G>
 __global__ __launch_bounds__(256 * G, 2 / G) void attn_bwd_dkdv_kernel(
     int S, int nq, int nkv, int ldq, const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO,
@@ -429,16 +433,14 @@ __global__ __launch_bounds__(256 * G, 2 / G) void attn_bwd_dkdv_kernel(
     float* __restrict__ part, float sl2, float scale, Drop drop) {
   constexpr int TILE = 64 * D;         // elements of one 64 x D tile
   constexpr int GRP = 2 * TILE + 256;  // one group's Q and dO tiles, log-sum-exp and D (64 floats each)
-  __shared__ __attribute__((aligned(1024))) bf16_t smem[TILE + G * GRP];
+  constexpr int NBUF = G == 2 ? 2 : 1; // Q / dO buffers per group
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[TILE + G * NBUF * GRP];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lg = lane >> 5;
   const int grp = wave >> 2, w4 = wave & 3;  // grp: 0 for every wavefront when G = 1
   const int kh = w4 & 1, qh = w4 >> 1;
   bf16_t* sK = smem;
-  bf16_t* sQ = smem + TILE + grp * GRP;
-  bf16_t* sdO = sQ + TILE;
-  const float* sL = reinterpret_cast<const float*>(sQ + 2 * TILE);
-  const float* sD = sL + 64;
+  bf16_t* const gbuf = smem + TILE + grp * NBUF * GRP;  // this group's buffers
   const int ntile = S / 64, nbh = gridDim.x / ntile;
   int kb, bh;
   tile_order(blockIdx.x, ntile, nbh, CAUSAL, false, G == 1, kb, bh);
@@ -475,20 +477,36 @@ __global__ __launch_bounds__(256 * G, 2 / G) void attn_bwd_dkdv_kernel(
   // passes that every group makes (the barriers are the workgroup's)
   const int q_first = CAUSAL ? kb : 0, iters = (ntile - q_first + G - 1) / G;
   const int q_beg = q_first + grp * iters, q_end = min(ntile, q_beg + iters);
+  auto fetch = [&](int qt, bf16_t* buf) {   // query tile qt's Q, dO, log-sum-exp and D rows
+    const int qt0 = qt * 64;
+    copy_q(buf, qbase + (size_t)qt0 * ldq);
+    copy_o(buf + TILE, dobase + (size_t)qt0 * ldo);
+    if (w4 == 0) {
+      lds_load4(4u * lane, lrow + qt0, buf + 2 * TILE);
+      lds_load4(4u * lane, drow + qt0, buf + 2 * TILE + 128);
+    }
+  };
+  if constexpr (NBUF == 2) {
+    if (q_beg < q_end) fetch(q_beg, gbuf);
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+    __syncthreads();
+  }
   for (int it = 0; it < iters; ++it) {
     const int qt = q_beg + it;
     const bool live = qt < q_end;   // uniform over the group
     const int qt0 = qt * 64;
-    if (live) {
-      copy_q(sQ, qbase + (size_t)qt0 * ldq);
-      copy_o(sdO, dobase + (size_t)qt0 * ldo);
-      if (w4 == 0) {
-        lds_load4(4u * lane, lrow + qt0, sQ + 2 * TILE);
-        lds_load4(4u * lane, drow + qt0, sQ + 2 * TILE + 128);
-      }
+    bf16_t* sQ = gbuf + (NBUF == 2 ? (it & 1) * GRP : 0);
+    if constexpr (NBUF == 2) {
+      // into the buffer every wavefront finished with in the last pass
+      if (qt + 1 < q_end) fetch(qt + 1, gbuf + ((it + 1) & 1) * GRP);
+    } else {
+      if (live) fetch(qt, sQ);
+      __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+      __syncthreads();
     }
-    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
-    __syncthreads();
+    const bf16_t* sdO = sQ + TILE;
+    const float* sL = reinterpret_cast<const float*>(sQ + 2 * TILE);
+    const float* sD = sL + 64;
     const int qw0 = qt0 + qh * 32;
     if (live && (!CAUSAL || qw0 + 31 >= k0)) {
       f32x16 s, dp;
@@ -554,7 +572,10 @@ __global__ __launch_bounds__(256 * G, 2 / G) void attn_bwd_dkdv_kernel(
                                                          0);
       }
     }
-    __syncthreads();  // every wavefront is done with the tile before the next one lands
+    // every wavefront is done with the tile before the next one lands there
+    // (double-buffered: and tile t+1 has landed)
+    if constexpr (NBUF == 2) __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+    __syncthreads();
   }
   // sum the groups (group 1 hands its accumulators to group 0 through LDS:
   // 4 x 64 x D floats), then the two query halves (qh = 1 to qh = 0: 2 x 64 x
