@@ -1223,7 +1223,7 @@ struct Plan {
 // step slower, 0.356 -> 0.401 ms: a block's fixed costs, not its k-loop,
 // dominate there; only the gradients that would leave at least half of the
 // chip idle go below 1024, see small_ok.)
-Plan plan(int M, int N, int K, bool a_kc, bool b_kc, int kind, bool split_ok, bool resid = false) {
+Plan plan(int M, int N, int K, bool a_kc, bool b_kc, int kind, bool split_ok) {
   auto tl = [&](int bm, int bn) { return (long)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
   auto depth_ok = [&](int s) { return K % (s * BK) == 0 && K / s >= 1024; };
   // parts down to 512 deep for weight and data gradients whose blocks would
@@ -1283,11 +1283,10 @@ Plan plan(int M, int N, int K, bool a_kc, bool b_kc, int kind, bool split_ok, bo
   // us, 26.4 -> 19.9 us with the GELU' epilogue, its QKV forward 24.6 us on
   // 64 tiles of 256 x 192 -> 192 tiles of 128 x 128)
   const double f128 = (K % SBK == 0 ? 0.95 : 0.85) * fill(t128, 2);
-  // the scheduled kernel's fixed per-block costs (one block per CU to hide the first copies and
-  // the epilogue) outweigh its faster loop below 1024-deep contractions; with a residual to
-  // add, its prefetched residual rows make it the faster one from 512 deep (projection forward,
-  // 8192 x 4096 x 512: 70 against 77 us)
-  const bool sk = K % SBK == 0 && K >= (resid ? 512 : 1024);
+  // the scheduled kernel from 512-deep contractions: on the 8-wavefront tile
+  // it is the faster one there too (8192 x 4096 x 768 with a transposed
+  // weight: 71 -> 55 us; 8192 x 4096 x 512, k-contiguous: 53 -> 43 us)
+  const bool sk = K % SBK == 0 && K >= 512;
   if (K >= 512) {
     const double f256 = (sk ? 1.3 : 1.0) * fill(t256, 1);
     // 256 x 192 tiles: plain stores (the 2x4-wavefront kernel) or any epilogue (the scheduled one)
@@ -1418,7 +1417,7 @@ PairPlan pair_plan(int M0, int N0, int K0, int lda0, int ldb0, int M1, int N1, i
 template <bool AKC, bool BKC, int EPI>
 hipError_t launch_bf16(int M, int N, int K, const void* A, int lda, const void* B, int ldb,
                        const Epi& e, hipStream_t st) {
-  const Plan pl = plan(M, N, K, AKC, BKC, EPI, e.ws != nullptr, EPI == EPI_STORE && e.resid != nullptr);
+  const Plan pl = plan(M, N, K, AKC, BKC, EPI, e.ws != nullptr);
   if (pl.tile == TSCHED192) {
     if constexpr (AKC && BKC) {
       if (sched_ok(M, N, K, AKC, lda, BKC, ldb, 1))
