@@ -1414,9 +1414,49 @@ PairPlan pair_plan(int M0, int N0, int K0, int lda0, int ldb0, int M1, int N1, i
   return best;
 }
 
+// Column split of a forward product with an activation epilogue whose 256 x
+// 256 tiles leave the last wave of blocks part-empty: the first n1 columns
+// (a multiple of 256) on 256 x 256 tiles and the rest on 256 x 192 tiles,
+// each part in whole waves, the 192-wide one three quarters as long (the
+// seq-4096 share's SwiGLU fc1 forward, 8192 x 3584: 448 tiles in two waves,
+// the second three quarters full -> 256 + 256 tiles). Returns n1, or 0 for
+// no split.
+int col_split_192(int M, int N, int K) {
+  if (K % 64 != 0) return 0;
+  const long rows = (M + 255) / 256;
+  auto waves = [](long t) { return (t + kCUs - 1) / kCUs; };
+  double best_c = (double)waves(rows * ((N + 255) / 256)) - 0.125;   // a gain of an eighth of a wave at least
+  int best = 0;
+  for (int n2 = 192; n2 < N; n2 += 192) {
+    const int n1 = N - n2;
+    if (n1 % 256 != 0) continue;
+    const double c = (double)waves(rows * (n1 / 256)) + 0.75 * (double)waves(rows * (n2 / 192));
+    if (c < best_c) {
+      best_c = c;
+      best = n1;
+    }
+  }
+  return best;
+}
+
 template <bool AKC, bool BKC, int EPI>
 hipError_t launch_bf16(int M, int N, int K, const void* A, int lda, const void* B, int ldb,
                        const Epi& e, hipStream_t st) {
+  if constexpr (AKC && BKC && (EPI == EPI_SWIGLU || EPI == EPI_GELU)) {
+    const int n1 = col_split_192(M, N, K);
+    if (n1 > 0 && sched_ok(M, n1, K, AKC, lda, BKC, ldb, 1) && sched_ok(M, N - n1, K, AKC, lda, BKC, ldb, 1)) {
+      const hipError_t r = launch_sched<kShMain, AKC, BKC, EPI>(M, n1, K, A, lda, B, ldb, e, st);
+      if (r != hipSuccess) return r;
+      // the second part's columns: SwiGLU's activation output holds half as
+      // many (gate/up pairs of 16-column blocks; n1 is a multiple of 32)
+      Epi e2 = e;
+      e2.out = static_cast<bf16_t*>(e.out) + n1;
+      e2.out2 = static_cast<bf16_t*>(e.out2) + (EPI == EPI_SWIGLU ? n1 / 2 : n1);
+      if (e.bias) e2.bias = static_cast<const bf16_t*>(e.bias) + n1;
+      return launch_sched<SH192W8, AKC, BKC, EPI>(M, N - n1, K, A, lda,
+                                                  static_cast<const bf16_t*>(B) + (size_t)n1 * ldb, ldb, e2, st);
+    }
+  }
   const Plan pl = plan(M, N, K, AKC, BKC, EPI, e.ws != nullptr);
   if (pl.tile == TSCHED192) {
     if constexpr (AKC && BKC) {
