@@ -1267,6 +1267,15 @@ Plan plan(int M, int N, int K, bool a_kc, bool b_kc, int kind, bool split_ok) {
   if (split_ok && a_kc && kind == EPI_STORE && 2 * t256 <= kCUs && K % SBK == 0 && !fill128) {
     int s = 1;
     while (s < 4 && t256 * s * 2 <= kCUs && sched_depth(2 * s)) s *= 2;
+    // the 8-wavefront 256 x 192 tile where its split blocks fill more of the
+    // chip (the seq-4096 share's 8192 x 768 x 4096 QKV forward: 96 tiles x 2
+    // = 192 blocks -> 128 x 2 = 256; 67.0 -> 62.2 us standalone)
+    if (b_kc && N % 192 == 0) {
+      const long t192 = tl(256, 192);
+      int s2 = 1;
+      while (s2 < 4 && t192 * s2 * 2 <= kCUs && K % (2 * s2 * 64) == 0 && K / (2 * s2) >= 1024) s2 *= 2;
+      if (s2 > 1 && t192 * s2 > t256 * s) return {TSCHED192, s2};
+    }
     if (s > 1) return {TSCHED, s};
   }
   if (split_ok && a_kc && kind == EPI_STORE && t128 <= kCUs && t256 < kCUs && K % BK == 0 && !fill128) {
@@ -1459,6 +1468,17 @@ hipError_t launch_bf16(int M, int N, int K, const void* A, int lda, const void* 
   }
   const Plan pl = plan(M, N, K, AKC, BKC, EPI, e.ws != nullptr);
   if (pl.tile == TSCHED192) {
+    if constexpr (AKC && BKC && EPI == EPI_STORE) {
+      if (pl.splits > 1) {   // partial tiles (contraction parts multiples of 64), then the split epilogue pass
+        if (!sched_ok(M, N, K, AKC, lda, BKC, ldb, pl.splits)) return hipErrorInvalidValue;
+        const hipError_t r = launch_sched<SH192W8, AKC, BKC, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, e, st, pl.splits);
+        if (r != hipSuccess) return r;
+        const unsigned tiles = (unsigned)(((M + 63) / 64) * ((N + 127) / 128));
+        hipLaunchKernelGGL((splitk_epi_kernel<64, 128, 256, EPI>), dim3(tiles), dim3(256), 0, st, M, N,
+                           pl.splits, (const float*)e.ws, e);
+        return hipGetLastError();
+      }
+    }
     if constexpr (AKC && BKC) {
       if (sched_ok(M, N, K, AKC, lda, BKC, ldb, 1))
         return K % 64 == 0 ? launch_sched<SH192W8, AKC, BKC, EPI>(M, N, K, A, lda, B, ldb, e, st)
