@@ -1041,7 +1041,7 @@ MTB_DEV void sched_loop64(f32x16 (&acc)[Sched<SH>::FM][Sched<SH>::FN], uint32_t 
 template <int SH, bool AKC, bool BKC, int EPI>
 MTB_DEV void sched_tile(bf16_t* smem, int M, int N, int K, const bf16_t* __restrict__ A, int lda,
                         const bf16_t* __restrict__ B, int ldb, const Epi& ep, int ksplit,
-                        const BlockTile& bt) {
+                        const BlockTile& bt, bool prefetch_b = false) {
   using G = Sched<SH>;
   constexpr int BM = G::BM, BN = G::BN, FM = G::FM, FN = G::FN;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1050,6 +1050,29 @@ MTB_DEV void sched_tile(bf16_t* smem, int M, int N, int K, const bf16_t* __restr
   const int kspan = K / ksplit, kbeg = bt.split * kspan;
   const int m0 = bt.tm * BM, n0 = bt.tn * BN;
   const uint32_t lds = (uint32_t)(uintptr_t)smem;
+  // B operand prefetch for a small B (at most 8 MB: a weight matrix that
+  // many blocks share, such as the 4096 x 512 projection's): the grid's
+  // blocks each touch one slice of B's bytes (one 4-byte load per 128-byte
+  // line, at most two per thread), so that the infinity cache holds B before
+  // the k-loop's copies ask for it -- the step last read that weight long
+  // ago, and when every block misses on the same cold lines each k-tile's
+  // copy waits out the HBM latency (projection dgrad 60 -> 44 us). The loads
+  // join the k-loop's first copy wait (vector memory operations complete in
+  // issue order); their values are only kept alive. A large B (16 MB
+  // weights, the weight gradients' activations) was slower with it.
+  uint32_t pf0 = 0, pf1 = 0;
+  if (prefetch_b) {
+    constexpr int NT = 64 * G::WAVES;
+    const size_t bytes = 2 * (BKC ? (size_t)(N - 1) * ldb + K : (size_t)(K - 1) * ldb + N);
+    if (bytes <= ((size_t)8 << 20) && K >= 2048) {
+      const size_t per = ((bytes + gridDim.x - 1) / gridDim.x + 127) & ~(size_t)127;
+      const size_t lo = (size_t)blockIdx.x * per, hi = min(bytes, lo + per);
+      const char* bb = reinterpret_cast<const char*>(B);
+      const size_t o0 = lo + (size_t)tid * 128, o1 = o0 + (size_t)NT * 128;
+      if (o0 + 4 <= hi) pf0 = *reinterpret_cast<const uint32_t*>(bb + o0);
+      if (o1 + 4 <= hi) pf1 = *reinterpret_cast<const uint32_t*>(bb + o1);
+    }
+  }
   f32x16 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -1075,6 +1098,7 @@ MTB_DEV void sched_tile(bf16_t* smem, int M, int N, int K, const bf16_t* __restr
     if (!done)
       sched_loop32<SH, AKC, BKC>(acc, lds, M, N, A, lda, B, ldb, kbeg, kspan, m0, n0, wave, wm, wn, lane);
   }
+  asm volatile("" : : "v"(pf0), "v"(pf1));
   __syncthreads();
   gemm_epilogue<BM, BN, G::WGM, G::WGN, G::SMEM / 2, AKC, EPI, true>(acc, smem, ep, M, N, m0, n0, bt, wm,
                                                                      wn, lane, tid);
@@ -1086,7 +1110,7 @@ __global__ __launch_bounds__(64 * Sched<SH>::WAVES, Sched<SH>::PER_CU) void gemm
     Epi ep, int ksplit) {
   __shared__ __attribute__((aligned(1024))) bf16_t smem[Sched<SH>::SMEM];
   sched_tile<SH, AKC, BKC, EPI>(smem, M, N, K, A, lda, B, ldb, ep, ksplit,
-                                block_tile<Sched<SH>::BM, Sched<SH>::BN>(M, N));
+                                block_tile<Sched<SH>::BM, Sched<SH>::BN>(M, N), true);
 }
 
 // One product of a grouped launch: its operands, split and block count.
