@@ -665,12 +665,14 @@ __global__ __launch_bounds__(256) void attn_dkv_reduce_kernel(int B, int S, int 
 // dO rows in registers. The K and V tiles stream global -> LDS
 // double-buffered (tile t+1 in flight while tile t is used); K^T comes from
 // the K tile by transpose reads. The groups' and then the key halves' sums
-// are added at the end.
+// are added at the end. Each query's D = rowsum(dO o O) is formed here from
+// the dO rows in registers and the O rows, and written to Dbuf for the dK/dV
+// kernel, which runs after this one.
 template <int D, bool CAUSAL, bool DROP, int G>
 __global__ __launch_bounds__(256 * G, 2 / G) void attn_bwd_dq_kernel(
-    int S, int nq, int nkv, int ldq, const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO,
-    const float* __restrict__ lse, const float* __restrict__ Dbuf, bf16_t* __restrict__ dqkv, float sl2,
-    float scale, Drop drop) {
+    int S, int nq, int nkv, int ldq, const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ O,
+    const bf16_t* __restrict__ dO, const float* __restrict__ lse, float* __restrict__ Dbuf,
+    bf16_t* __restrict__ dqkv, float sl2, float scale, Drop drop) {
   constexpr int TILE = 64 * D;
   constexpr int STAGE = 2 * TILE;  // K, V
   __shared__ __attribute__((aligned(1024))) bf16_t smem[G * 2 * STAGE];
@@ -703,19 +705,29 @@ __global__ __launch_bounds__(256 * G, 2 / G) void attn_bwd_dq_kernel(
   if (k_beg < k_end) fetch(0);
 
   bf16x8 qf[D / 16], of[D / 16];
+  float Dq = 0.f;
   {
     const bf16_t* qp = qkv + (tok0 + qi) * ldq + hq * D + 8 * lg;
     const bf16_t* gp = dO + (tok0 + qi) * ldo + hq * D + 8 * lg;
+    const bf16_t* op = O + (tok0 + qi) * ldo + hq * D + 8 * lg;
+    bf16x8 orow[D / 16];
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       qf[kk] = *reinterpret_cast<const bf16x8*>(qp + kk * 16);
       of[kk] = *reinterpret_cast<const bf16x8*>(gp + kk * 16);
+      orow[kk] = *reinterpret_cast<const bf16x8*>(op + kk * 16);
     }
+    // D over the lane's half of the row's columns, then the other half's (lane ^ 32)
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Dq = fmaf((float)of[kk][e], (float)orow[kk][e], Dq);
+    Dq += __shfl_xor(Dq, 32, 64);
   }
   settle(qf);
   settle(of);
   float Lq = lse[((size_t)b * nq + hq) * S + qi] * kLog2e;
-  float Dq = Dbuf[((size_t)b * nq + hq) * S + qi];
+  if (grp == 0 && kh == 0 && lg == 0) Dbuf[((size_t)b * nq + hq) * S + qi] = Dq;
   asm volatile("" : "+v"(Lq), "+v"(Dq));
   f32x16 dq[D / 32];
 #pragma unroll
@@ -957,18 +969,16 @@ hipError_t attn_bwd_bf16(int B, int S, int nq, int nkv, int causal, const void* 
                          const Drop& drop, hipStream_t st) {
   const int ldq = (nq + 2 * nkv) * D;
   const float sl2 = kLog2e / sqrtf((float)D), scale = 1.0f / sqrtf((float)D);
-  const int rows = B * S * nq;
-  hipLaunchKernelGGL((attn_bwd_pre_kernel<bf16_t, D>), dim3((rows * (D / 8) + 255) / 256),
-                     dim3(256), 0, st, rows, S, nq, (const bf16_t*)O, (const bf16_t*)dO, Dbuf);
+  // dQ first: it also writes D = rowsum(dO o O) per query for dK/dV
   dim3 grid((S / 64) * B * nq);
   const int G = bwd_groups(causal != 0, (long)grid.x);
 #define MTB_BWD(C, DR, G)                                                                     \
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<D, C, DR, G>), grid, dim3(256 * G), 0, st, S, nq, nkv, \
+                     ldq, (const bf16_t*)qkv, (const bf16_t*)O, (const bf16_t*)dO, lse, Dbuf,  \
+                     (bf16_t*)dqkv, sl2, scale, drop);                                         \
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, C, DR, G>), grid, dim3(256 * G), 0, st, S, nq, nkv, \
                      ldq, (const bf16_t*)qkv, (const bf16_t*)dO, lse, Dbuf, (bf16_t*)dqkv,   \
-                     part, sl2, scale, drop);                                                \
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<D, C, DR, G>), grid, dim3(256 * G), 0, st, S, nq, nkv, \
-                     ldq, (const bf16_t*)qkv, (const bf16_t*)dO, lse, Dbuf, (bf16_t*)dqkv,   \
-                     sl2, scale, drop)
+                     part, sl2, scale, drop)
   if (causal) {
     if (drop.thr) { MTB_BWD(true, true, 2); } else { MTB_BWD(true, false, 2); }
   } else if (G == 2) {
