@@ -424,7 +424,8 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(int rows, int S, int 
 // two workgroups per CU a group's Q and dO tiles are single-buffered (80 KB
 // of LDS per workgroup allows no more; the other workgroup covers the copy);
 // with two groups in one workgroup, whose barriers are shared, they are
-// double-buffered (tile t+1 in flight while tile t is used). The groups' and
+// double-buffered (tile t+1 in flight while tile t is used), except with
+// dropout. The groups' and
 // then the two query halves' sums are added at the end.
 template <int D, bool CAUSAL, bool DROP, int G>
 __global__ __launch_bounds__(256 * G, 2 / G) void attn_bwd_dkdv_kernel(
@@ -433,7 +434,10 @@ __global__ __launch_bounds__(256 * G, 2 / G) void attn_bwd_dkdv_kernel(
     float* __restrict__ part, float sl2, float scale, Drop drop) {
   constexpr int TILE = 64 * D;         // elements of one 64 x D tile
   constexpr int GRP = 2 * TILE + 256;  // one group's Q and dO tiles, log-sum-exp and D (64 floats each)
-  constexpr int NBUF = G == 2 ? 2 : 1; // Q / dO buffers per group
+  // Q / dO buffers per group (with dropout the second buffer's address
+  // arithmetic spills registers: single-buffered there, 133 -> 127 us at
+  // the seq-2048 causal share)
+  constexpr int NBUF = G == 2 && !DROP ? 2 : 1;
   __shared__ __attribute__((aligned(1024))) bf16_t smem[TILE + G * NBUF * GRP];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lg = lane >> 5;
