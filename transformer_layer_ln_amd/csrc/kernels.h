@@ -119,8 +119,9 @@ hipError_t act_bwd(int dtype, int act, int rows, int F, const void* dm, const vo
 // O [T][nq*d]; lse [B][nq][S] (natural log).
 hipError_t attn_fwd(int dtype, int B, int S, int nq, int nkv, int d, int causal, const void* qkv,
                     void* O, float* lse, hipStream_t st, const Drop& drop = Drop());
-// dO [T][nq*d]; Dbuf [B][nq][S] fp32 scratch; dqkv [T][Nqkv] output; part:
-// fp32 scratch of B*nq*S*2*d floats (GQA, bf16).
+// dO [T][nq*d]; Dbuf [B][nq][S] fp32 scratch (rowsum(dO o O) per query, formed
+// inside the backward); dqkv [T][Nqkv] output; part: fp32 scratch of
+// B*nq*S*2*d floats (GQA, bf16).
 hipError_t attn_bwd(int dtype, int B, int S, int nq, int nkv, int d, int causal, const void* qkv,
                     const void* O, const void* dO, const float* lse, float* Dbuf, void* dqkv,
                     float* part, hipStream_t st, const Drop& drop = Drop());
