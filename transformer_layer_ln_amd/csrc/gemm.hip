@@ -1051,7 +1051,8 @@ MTB_DEV void sched_tile(bf16_t* smem, int M, int N, int K, const bf16_t* __restr
   const int m0 = bt.tm * BM, n0 = bt.tn * BN;
   const uint32_t lds = (uint32_t)(uintptr_t)smem;
   // B operand prefetch for a small B (at most 8 MB: a weight matrix that
-  // many blocks share, such as the 4096 x 512 projection's): the grid's
+  // many blocks share, such as the 4096 x 512 projection's) read by a deep
+  // contraction or by two waves of blocks: the grid's
   // blocks each touch one slice of B's bytes (one 4-byte load per 128-byte
   // line, at most two per thread), so that the infinity cache holds B before
   // the k-loop's copies ask for it -- the step last read that weight long
@@ -1064,7 +1065,7 @@ MTB_DEV void sched_tile(bf16_t* smem, int M, int N, int K, const bf16_t* __restr
   if (prefetch_b) {
     constexpr int NT = 64 * G::WAVES;
     const size_t bytes = 2 * (BKC ? (size_t)(N - 1) * ldb + K : (size_t)(K - 1) * ldb + N);
-    if (bytes <= ((size_t)8 << 20) && K >= 2048) {
+    if (bytes <= ((size_t)8 << 20) && (K >= 2048 || gridDim.x >= 512)) {
       const size_t per = ((bytes + gridDim.x - 1) / gridDim.x + 127) & ~(size_t)127;
       const size_t lo = (size_t)blockIdx.x * per, hi = min(bytes, lo + per);
       const char* bb = reinterpret_cast<const char*>(B);
