@@ -82,7 +82,9 @@ def test_bf16_small_shapes(i):
 # gradients split 8064 tokens four ways (63 k-tiles each, entering the loop
 # body at its second slot); SwiGLU at 4032 tokens, where the SwiGLU′ epilogue
 # of the fc2 data gradient takes its prefetched gate/up rows past the last
-# full tile row.
+# full tile row. 8064 tokens with a 3584-wide GELU fc1 (448 tiles of 256 x
+# 256) split its columns into 2048 on 256 x 256 tiles and 1536 on 256 x 192
+# tiles, past a ragged last tile row.
 SCHED_RAGGED = [
     dict(batch=3, seq=1344, hidden=1280, q_heads=10, kv_heads=2, head_dim=128, ffn=3072, causal=True),
     dict(batch=2, seq=2048, hidden=1344, q_heads=21, kv_heads=3, head_dim=64, ffn=2112, bias=True,
@@ -92,6 +94,7 @@ SCHED_RAGGED = [
          bias=True),
     dict(batch=3, seq=1344, hidden=1280, q_heads=10, kv_heads=2, head_dim=128, ffn=3072, act="swiglu",
          causal=True),
+    dict(batch=3, seq=2688, hidden=256, q_heads=2, kv_heads=2, head_dim=128, ffn=3584, causal=True, bias=True),
 ]
 
 
